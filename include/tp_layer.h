@@ -1,0 +1,152 @@
+/*
+ * tp_layer.h -- C ABI of one tensor-parallel rank's share of a Megatron-style
+ * Transformer layer (MLP block + causal self-attention block), forward and
+ * backward, for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the tensor-parallel split of the Megatron-LM deep dive
+ * (charles2530.github.io): "MLP: column parallel then row parallel" (Fig. 3a),
+ * "Attention: split Q/K/V by head" (Fig. 3b) and the f / g operators (Fig. 4);
+ * and the MT-NLG 530B deep dive (zzszmyf.github.io), section 2.4 (column and
+ * row parallel linear layers).
+ *
+ * The caller passes ONE rank's shards; the library computes that rank's share
+ * and never communicates. The g all-reduce of the forward pass and the f
+ * all-reduce of the backward pass are left to the caller; on one device they
+ * are emulated with tp_sum_partials over the ranks' partial outputs.
+ *
+ * Conventions (all calls):
+ *   - Notation per rank r of p = tp_size: T = batch*seq tokens (row t =
+ *     batch_index*seq + position), h = hidden, h_l = h/p, n_l = n_heads/p local
+ *     heads of width d = head_dim, f_l = ffn/p.
+ *   - Every matrix is row-major and contiguous. Every pointer is a device
+ *     pointer, 16-byte aligned, except the tp_shape pointer (host memory) and
+ *     tp_sum_partials' array of part pointers (a host array of device pointers).
+ *   - Tensors are stored in shape->dtype (fp32 or bf16); products accumulate in
+ *     fp32. lse is always fp32. bf16 results are rounded to nearest even once.
+ *   - The caller allocates and owns every buffer, including the workspace
+ *     (size from tp_*_workspace_bytes). The library never allocates, frees or
+ *     synchronizes: work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     null stream) and the call returns.
+ *   - Outputs (weight gradients included) are overwritten, never accumulated.
+ *     Outputs must not alias inputs or each other.
+ *   - Error behaviour: a non-zero return means nothing was enqueued, except
+ *     TP_ERR_HIP (a launch failed part way; the outputs are undefined). The
+ *     message is available from tp_last_error() on the calling thread.
+ *     Device-side faults surface at the caller's next synchronization.
+ *     No C++ exception crosses this interface.
+ *   - Empty batches (batch == 0 or seq == 0) are valid: token-shaped outputs
+ *     are empty and weight / bias gradients are written as zeros.
+ */
+#ifndef TP_LAYER_H
+#define TP_LAYER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TP_OK = 0,
+  TP_ERR_NULL = -1,         /* a required pointer is NULL                       */
+  TP_ERR_SHAPE = -2,        /* negative size, or a size limit exceeded          */
+  TP_ERR_DIVISIBILITY = -3, /* n_heads or ffn not divisible by tp_size, or
+                               n_heads*head_dim != hidden                       */
+  TP_ERR_RANK = -4,         /* tp_rank outside [0, tp_size) or tp_size < 1      */
+  TP_ERR_DTYPE = -5,        /* dtype not TP_FP32 / TP_BF16                      */
+  TP_ERR_HEADDIM = -6,      /* head_dim outside the supported set               */
+  TP_ERR_WORKSPACE = -7,    /* workspace NULL or smaller than required          */
+  TP_ERR_ALIGN = -8,        /* pointer not 16-byte aligned, or (bf16) a weight
+                               dimension not a multiple of 8                    */
+  TP_ERR_HIP = -9           /* a HIP launch or query failed                     */
+} tp_status;
+
+typedef enum { TP_FP32 = 0, TP_BF16 = 1 } tp_dtype;
+
+/* Full (unsharded) layer sizes plus the pages' (rank, degree) pair. */
+typedef struct {
+  int32_t batch, seq, hidden, ffn, n_heads, head_dim;
+  int32_t tp_rank, tp_size; /* 0 <= tp_rank < tp_size                           */
+  int32_t dtype;            /* tp_dtype: storage type; accumulation is fp32     */
+  int32_t causal;           /* must be 1: left-to-right (autoregressive) mask,
+                               key j attends to query i iff j <= i              */
+  int32_t alibi;            /* 0/1: add -m_k*(i-j) to the scaled score of global
+                               head k (1-based), m_k = 2^(-8k/n_heads)
+                               (Megatron-DeepSpeed blog, section 4.3)           */
+} tp_shape;
+
+/* Supported sizes. head_dim: 8..256 and a multiple of 8 (bf16 also requires
+ * hidden, ffn/p and h/p to be multiples of 8); seq <= 65536; every matrix
+ * dimension < 2^31 elements per row and T*max(h, 3h_l, f_l) < 2^40. */
+
+/* Workspace bytes the calls below need for this shape (0 on an invalid shape).
+ * Host-only; no HIP call. */
+size_t tp_mlp_workspace_bytes(const tp_shape* shape);
+size_t tp_attn_workspace_bytes(const tp_shape* shape);
+
+/* MLP forward (Megatron-LM deep dive, Fig. 3a; Megatron-DeepSpeed blog 2.1):
+ *   pre_i = X A_i + b1_i         X [T,h] (replicated input), A_i [h,f_l]
+ *                                (column shard), b1_i [f_l]
+ *   y_i   = GeLU(pre_i)          tanh form: 0.5 x (1 + tanh(sqrt(2/pi)(x + 0.044715 x^3)))
+ *   Z_i   = y_i B_i              B_i [f_l,h] (row shard); Z_i [T,h] is this
+ *                                rank's PARTIAL sum; b2 is not added (the caller
+ *                                adds it once after the sum over ranks).
+ * Outputs pre_i, y_i [T,f_l] are saved for the backward pass. */
+tp_status tp_mlp_fwd(const tp_shape* shape, const void* X, const void* A_i, const void* b1_i,
+                     const void* B_i, void* pre_i, void* y_i, void* Z_i, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* MLP backward: gradients of <Z_i + b2, dZ> with dZ [T,h] replicated (g's
+ * backward is the identity):
+ *   dPre = (dZ B_i^T) * GeLU'(pre_i)
+ *   dB_i = y_i^T dZ [f_l,h];  dA_i = X^T dPre [h,f_l];  db1_i = sum_t dPre [f_l]
+ *   dX_i = dPre A_i^T [T,h]   this rank's PARTIAL input gradient (f's backward
+ *                             sums it over ranks)
+ *   db2  = sum_t dZ [h]       replicated bias; written only if db2_or_null != NULL */
+tp_status tp_mlp_bwd(const tp_shape* shape, const void* X, const void* A_i, const void* B_i,
+                     const void* pre_i, const void* y_i, const void* dZ, void* dX_i, void* dA_i,
+                     void* db1_i, void* dB_i, void* db2_or_null, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Attention forward (Megatron-LM deep dive, Fig. 3b):
+ *   qkv_i = X Wqkv_i + bqkv_i    Wqkv_i [h,3h_l] = [Wq_i | Wk_i | Wv_i] (the
+ *                                columns of this rank's heads), bqkv_i [3h_l];
+ *                                local head l uses columns l*d..l*d+d-1 of each
+ *                                third; rank r owns global heads r*n_l..r*n_l+n_l-1
+ *   per batch element and local head: S = q k^T / sqrt(d) (+ ALiBi), causal
+ *   mask, row softmax, ctx = softmax(S) v; lse = log-sum-exp of each row of S
+ *   O_i = ctx_i Wo_i             Wo_i [h_l,h] (row shard); O_i [T,h] is this
+ *                                rank's PARTIAL sum; bo is not added.
+ * Saved for backward: qkv_i [T,3h_l], ctx_i [T,h_l] (heads side by side),
+ * lse_i [batch, n_l, seq] fp32. */
+tp_status tp_attn_fwd(const tp_shape* shape, const void* X, const void* Wqkv_i, const void* bqkv_i,
+                      const void* Wo_i, void* qkv_i, void* ctx_i, float* lse_i, void* O_i,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Attention backward: gradients of <O_i + bo, dO>, dO [T,h] replicated.
+ *   dC = dO Wo_i^T;  dWo_i = ctx_i^T dO [h_l,h]
+ *   per head: dV = P^T dC, dP = dC V^T, dS = P*(dP - rowsum(dC*ctx)),
+ *             dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d)   (P recomputed from lse)
+ *   dWqkv_i = X^T dqkv [h,3h_l];  dbqkv_i = sum_t dqkv [3h_l]
+ *   dX_i = dqkv Wqkv_i^T [T,h]   PARTIAL input gradient
+ *   dbo = sum_t dO [h]           replicated bias; written only if dbo_or_null != NULL */
+tp_status tp_attn_bwd(const tp_shape* shape, const void* X, const void* Wqkv_i, const void* Wo_i,
+                      const void* qkv_i, const void* ctx_i, const float* lse_i, const void* dO,
+                      void* dX_i, void* dWqkv_i, void* dbqkv_i, void* dWo_i, void* dbo_or_null,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* The f / g all-reduce emulated on one device (Megatron-LM deep dive, Fig. 4):
+ *   out [T,h] = sum_{k < n_parts} parts[k] + bias   (fp32 accumulation, rounded
+ * once). parts is a HOST array of n_parts (1..64) device pointers to [T,h]
+ * tensors in shape->dtype; bias_or_null [h] may be NULL. out may alias parts[0]. */
+tp_status tp_sum_partials(const tp_shape* shape, const void* const* parts, int32_t n_parts,
+                          const void* bias_or_null, void* out, void* stream);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* tp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TP_LAYER_H */

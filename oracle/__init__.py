@@ -20,5 +20,6 @@ function here is "parity unpinned".
 """
 from .tp_layer import (  # noqa: F401
     GELU_C, gelu, gelu_grad, column_shard, row_shard, qkv_weight_shard, qkv_bias_shard,
-    layer_weight_shapes, mlp_fwd, mlp_bwd, alibi_slope, attn_fwd, attn_bwd, sum_partials,
+    layer_weight_shapes, mlp_fwd, mlp_bwd, alibi_slope, attn_core_fwd, attn_core_bwd, attn_fwd,
+    attn_bwd, sum_partials,
 )

@@ -139,26 +139,60 @@ def _softmax_rows(S):
     return E / den, (mx + np.log(den))[:, 0]
 
 
-def attn_fwd(X, Wqkv_r, bqkv_r, Wo_r, *, batch, seq, n_heads, tp_size, tp_rank,
-             causal=True, alibi=False):
-    """Returns qkv_r [T, 3h_l], ctx_r [T, h_l], lse_r [batch, n_l, seq], O_r [T, h] (partial)."""
-    T = batch * seq
-    h_l = Wqkv_r.shape[1] // 3
-    n_l = n_heads // tp_size
-    d = h_l // n_l
-    qkv = X @ Wqkv_r + bqkv_r
-    ctx = np.zeros((T, h_l))
-    lse = np.zeros((batch, n_l, seq))
+def attn_core_fwd(qkv, *, batch, seq, n_local, head_dim, head0, n_heads, causal=True, alibi=False):
+    """Per batch element and local head l (global head k = head0 + l + 1):
+    ctx = softmax(q k^T / sqrt(d) + bias) v, lse = log-sum-exp of each score row.
+    qkv [T, 3h_l] -> ctx [T, h_l], lse [batch, n_local, seq]."""
+    h_l = n_local * head_dim
+    ctx = np.zeros((batch * seq, h_l))
+    lse = np.zeros((batch, n_local, seq))
     for bi in range(batch):
         rows = slice(bi * seq, (bi + 1) * seq)
-        for l in range(n_l):
-            cq, ck, cv = _head_cols(l, d, h_l)
-            k_glob = tp_rank * n_l + l + 1
-            slope = alibi_slope(k_glob, n_heads) if alibi else None
-            S = _scores(qkv[rows, cq], qkv[rows, ck], d, causal, slope)
+        for l in range(n_local):
+            cq, ck, cv = _head_cols(l, head_dim, h_l)
+            slope = alibi_slope(head0 + l + 1, n_heads) if alibi else None
+            S = _scores(qkv[rows, cq], qkv[rows, ck], head_dim, causal, slope)
             P, lse_h = _softmax_rows(S)
             ctx[rows, cq] = P @ qkv[rows, cv]
             lse[bi, l] = lse_h
+    return ctx, lse
+
+
+def attn_core_bwd(qkv, dctx, *, batch, seq, n_local, head_dim, head0, n_heads, causal=True, alibi=False):
+    """Gradient of <ctx, dctx> with respect to qkv, per head:
+    dv = P^T dc, dP = dc v^T, dS = P * (dP - rowsum(P * dP)),
+    dq = dS k / sqrt(d), dk = dS^T q / sqrt(d)."""
+    h_l = n_local * head_dim
+    dqkv = np.zeros_like(qkv)
+    for bi in range(batch):
+        rows = slice(bi * seq, (bi + 1) * seq)
+        for l in range(n_local):
+            cq, ck, cv = _head_cols(l, head_dim, h_l)
+            slope = alibi_slope(head0 + l + 1, n_heads) if alibi else None
+            q, k, v = qkv[rows, cq], qkv[rows, ck], qkv[rows, cv]
+            P, _ = _softmax_rows(_scores(q, k, head_dim, causal, slope))
+            dc = dctx[rows, cq]
+            dP = dc @ v.T
+            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            dqkv[rows, cq] = (dS @ k) / math.sqrt(head_dim)
+            dqkv[rows, ck] = (dS.T @ q) / math.sqrt(head_dim)
+            dqkv[rows, cv] = P.T @ dc
+    return dqkv
+
+
+def _core_kw(Wqkv_r, batch, seq, n_heads, tp_size, tp_rank, causal, alibi):
+    h_l = Wqkv_r.shape[1] // 3
+    n_l = n_heads // tp_size
+    return dict(batch=batch, seq=seq, n_local=n_l, head_dim=h_l // n_l, head0=tp_rank * n_l,
+                n_heads=n_heads, causal=causal, alibi=alibi)
+
+
+def attn_fwd(X, Wqkv_r, bqkv_r, Wo_r, *, batch, seq, n_heads, tp_size, tp_rank,
+             causal=True, alibi=False):
+    """Returns qkv_r [T, 3h_l], ctx_r [T, h_l], lse_r [batch, n_l, seq], O_r [T, h] (partial)."""
+    kw = _core_kw(Wqkv_r, batch, seq, n_heads, tp_size, tp_rank, causal, alibi)
+    qkv = X @ Wqkv_r + bqkv_r
+    ctx, lse = attn_core_fwd(qkv, **kw)
     O_r = ctx @ Wo_r
     return qkv, ctx, lse, O_r
 
@@ -167,30 +201,11 @@ def attn_bwd(X, Wqkv_r, bqkv_r, Wo_r, dO, *, batch, seq, n_heads, tp_size, tp_ra
              causal=True, alibi=False):
     """Gradients of <O_r + bo, dO>. Recomputes the forward from X.
     Returns dX_r (partial), dWqkv_r, dbqkv_r, dWo_r, dbo (replicated, once)."""
-    T = batch * seq
-    h_l = Wqkv_r.shape[1] // 3
-    n_l = n_heads // tp_size
-    d = h_l // n_l
+    kw = _core_kw(Wqkv_r, batch, seq, n_heads, tp_size, tp_rank, causal, alibi)
     qkv = X @ Wqkv_r + bqkv_r
-    ctx = np.zeros((T, h_l))
-    dqkv = np.zeros_like(qkv)
+    ctx, _ = attn_core_fwd(qkv, **kw)
     dC = dO @ Wo_r.T
-    for bi in range(batch):
-        rows = slice(bi * seq, (bi + 1) * seq)
-        for l in range(n_l):
-            cq, ck, cv = _head_cols(l, d, h_l)
-            k_glob = tp_rank * n_l + l + 1
-            slope = alibi_slope(k_glob, n_heads) if alibi else None
-            q, k, v = qkv[rows, cq], qkv[rows, ck], qkv[rows, cv]
-            P, _ = _softmax_rows(_scores(q, k, d, causal, slope))
-            ctx[rows, cq] = P @ v
-            dc = dC[rows, cq]
-            dv = P.T @ dc
-            dP = dc @ v.T
-            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
-            dqkv[rows, cq] = (dS @ k) / math.sqrt(d)
-            dqkv[rows, ck] = (dS.T @ q) / math.sqrt(d)
-            dqkv[rows, cv] = dv
+    dqkv = attn_core_bwd(qkv, dC, **kw)
     dWo_r = ctx.T @ dO
     dbo = dO.sum(axis=0)
     dWqkv_r = X.T @ dqkv

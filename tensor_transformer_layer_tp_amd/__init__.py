@@ -1,0 +1,170 @@
+"""One tensor-parallel rank's share of a Megatron-style Transformer layer on
+AMD Instinct MI355X (gfx950): Python binding of the C ABI in include/tp_layer.h.
+
+This module only marshals arguments: every step of the computation runs in the
+HIP library lib/libtp_layer.so (build it with
+`python -m tensor_transformer_layer_tp_amd.build`). Importing this module does
+not need a GPU; calling a compute entry point does. If the library is missing,
+every call raises -- there is no fallback.
+
+Tensors are passed as torch tensors (their data_ptr is used), plain integer
+device addresses, or None for the optional outputs. `stream` defaults to
+torch's current stream on the current device.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+__all__ = [
+    "TpShape", "TPError", "TP_FP32", "TP_BF16", "STATUS", "library_path", "load_library",
+    "exported_symbols", "tp_mlp_workspace_bytes", "tp_attn_workspace_bytes", "tp_mlp_fwd",
+    "tp_mlp_bwd", "tp_attn_fwd", "tp_attn_bwd", "tp_sum_partials", "tp_last_error",
+]
+
+TP_FP32, TP_BF16 = 0, 1
+STATUS = {
+    0: "TP_OK", -1: "TP_ERR_NULL", -2: "TP_ERR_SHAPE", -3: "TP_ERR_DIVISIBILITY", -4: "TP_ERR_RANK",
+    -5: "TP_ERR_DTYPE", -6: "TP_ERR_HEADDIM", -7: "TP_ERR_WORKSPACE", -8: "TP_ERR_ALIGN", -9: "TP_ERR_HIP",
+}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_HEADER = os.path.join(os.path.dirname(_HERE), "include", "tp_layer.h")
+
+
+def library_path() -> str:
+    return os.environ.get("TP_LAYER_LIB", os.path.join(_HERE, "lib", "libtp_layer.so"))
+
+
+class TPError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+
+
+class TpShape(ctypes.Structure):
+    """Mirror of tp_shape: full (unsharded) sizes plus (tp_rank, tp_size)."""
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "seq", "hidden", "ffn", "n_heads", "head_dim", "tp_rank", "tp_size", "dtype", "causal", "alibi")]
+
+    @classmethod
+    def make(cls, *, batch, seq, hidden, ffn, n_heads, head_dim, tp_rank=0, tp_size=1, dtype=TP_BF16,
+             causal=1, alibi=0) -> "TpShape":
+        if isinstance(dtype, str):
+            dtype = {"fp32": TP_FP32, "bf16": TP_BF16}[dtype]
+        return cls(batch, seq, hidden, ffn, n_heads, head_dim, tp_rank, tp_size, dtype, int(causal), int(alibi))
+
+
+_lib = None
+_vp, _sz, _st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+_SIGS = {
+    "tp_mlp_workspace_bytes": (_sz, [ctypes.POINTER(TpShape)]),
+    "tp_attn_workspace_bytes": (_sz, [ctypes.POINTER(TpShape)]),
+    "tp_mlp_fwd": (_st, [ctypes.POINTER(TpShape)] + [_vp] * 7 + [_vp, _sz, _vp]),
+    "tp_mlp_bwd": (_st, [ctypes.POINTER(TpShape)] + [_vp] * 11 + [_vp, _sz, _vp]),
+    "tp_attn_fwd": (_st, [ctypes.POINTER(TpShape)] + [_vp] * 8 + [_vp, _sz, _vp]),
+    "tp_attn_bwd": (_st, [ctypes.POINTER(TpShape)] + [_vp] * 12 + [_vp, _sz, _vp]),
+    "tp_sum_partials": (_st, [ctypes.POINTER(TpShape), ctypes.POINTER(_vp), ctypes.c_int32, _vp, _vp, _vp]),
+    "tp_last_error": (ctypes.c_char_p, []),
+}
+
+
+def load_library() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"HIP library {path} is missing: build it with "
+                               "`python -m tensor_transformer_layer_tp_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def exported_symbols() -> list[str]:
+    """Names of the functions include/tp_layer.h declares."""
+    with open(_HEADER) as fh:
+        text = fh.read()
+    return re.findall(r"^\s*(?:size_t|tp_status|const char\*)\s+(tp_\w+)\s*\(", text, flags=re.M)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t or None
+    return t.data_ptr() or None
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ws(ws):
+    if ws is None:
+        return None, 0
+    if isinstance(ws, tuple):
+        return ws
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def _check(status: int):
+    if status != 0:
+        raise TPError(status, tp_last_error())
+
+
+def tp_last_error() -> str:
+    return load_library().tp_last_error().decode()
+
+
+def tp_mlp_workspace_bytes(shape: TpShape) -> int:
+    return load_library().tp_mlp_workspace_bytes(ctypes.byref(shape))
+
+
+def tp_attn_workspace_bytes(shape: TpShape) -> int:
+    return load_library().tp_attn_workspace_bytes(ctypes.byref(shape))
+
+
+def tp_mlp_fwd(shape, X, A_i, b1_i, B_i, pre_i, y_i, Z_i, workspace=None, stream=None):
+    w, wn = _ws(workspace)
+    _check(load_library().tp_mlp_fwd(ctypes.byref(shape), _ptr(X), _ptr(A_i), _ptr(b1_i), _ptr(B_i), _ptr(pre_i),
+                                     _ptr(y_i), _ptr(Z_i), w, wn, _stream(stream)))
+
+
+def tp_mlp_bwd(shape, X, A_i, B_i, pre_i, y_i, dZ, dX_i, dA_i, db1_i, dB_i, db2_or_null=None, workspace=None,
+               stream=None):
+    w, wn = _ws(workspace)
+    _check(load_library().tp_mlp_bwd(ctypes.byref(shape), _ptr(X), _ptr(A_i), _ptr(B_i), _ptr(pre_i), _ptr(y_i),
+                                     _ptr(dZ), _ptr(dX_i), _ptr(dA_i), _ptr(db1_i), _ptr(dB_i), _ptr(db2_or_null),
+                                     w, wn, _stream(stream)))
+
+
+def tp_attn_fwd(shape, X, Wqkv_i, bqkv_i, Wo_i, qkv_i, ctx_i, lse_i, O_i, workspace=None, stream=None):
+    w, wn = _ws(workspace)
+    _check(load_library().tp_attn_fwd(ctypes.byref(shape), _ptr(X), _ptr(Wqkv_i), _ptr(bqkv_i), _ptr(Wo_i),
+                                      _ptr(qkv_i), _ptr(ctx_i), _ptr(lse_i), _ptr(O_i), w, wn, _stream(stream)))
+
+
+def tp_attn_bwd(shape, X, Wqkv_i, Wo_i, qkv_i, ctx_i, lse_i, dO, dX_i, dWqkv_i, dbqkv_i, dWo_i, dbo_or_null=None,
+                workspace=None, stream=None):
+    w, wn = _ws(workspace)
+    _check(load_library().tp_attn_bwd(ctypes.byref(shape), _ptr(X), _ptr(Wqkv_i), _ptr(Wo_i), _ptr(qkv_i),
+                                      _ptr(ctx_i), _ptr(lse_i), _ptr(dO), _ptr(dX_i), _ptr(dWqkv_i), _ptr(dbqkv_i),
+                                      _ptr(dWo_i), _ptr(dbo_or_null), w, wn, _stream(stream)))
+
+
+def tp_sum_partials(shape, parts, bias_or_null, out, stream=None):
+    arr = (_vp * len(parts))(*[_ptr(p) for p in parts])
+    _check(load_library().tp_sum_partials(ctypes.byref(shape), arr, len(parts), _ptr(bias_or_null), _ptr(out),
+                                          _stream(stream)))

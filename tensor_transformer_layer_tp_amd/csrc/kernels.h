@@ -1,0 +1,71 @@
+// Host-side launchers of the layer-shard kernels (internal C++ interface used
+// by the C ABI in tp_layer.cpp). Every launcher enqueues on `stream` and
+// returns the launch status; none allocates or synchronizes.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tpk {
+
+enum DType : int { DT_F32 = 0, DT_BF16 = 1 };
+
+// Epilogues applied to an fp32 accumulator element C[m][n] before it is stored.
+enum Epi : int {
+  EPI_STORE = 0,      // out = acc
+  EPI_BIAS_GELU = 1,  // pre = acc + bias[n]; out2 = gelu(pre); out = pre
+  EPI_DGELU = 2,      // out = acc * gelu'(aux[m][n])
+  EPI_BIAS = 3,       // out = acc + bias[n]
+};
+
+// C[M,N] = op(A) op(B) with fp32 accumulation, then an epilogue.
+//   A: a_kmajor ? A[m*lda + k] : A[k*lda + m]
+//   B: b_kmajor ? B[n*ldb + k] : B[k*ldb + n]
+// epi: one of Epi (C2 receives gelu(pre) for EPI_BIAS_GELU).
+struct GemmDesc {
+  int M = 0, N = 0, K = 0;
+  const void* A = nullptr; long lda = 0; bool a_kmajor = true;
+  const void* B = nullptr; long ldb = 0; bool b_kmajor = false;
+  int epi = 0;
+  void* C = nullptr; long ldc = 0;
+  void* C2 = nullptr; long ldc2 = 0;
+  const void* bias = nullptr;
+  const void* aux = nullptr; long ldaux = 0;
+};
+
+// Workspace bytes gemm_launch needs for this problem (host only).
+size_t gemm_workspace_bytes(int dtype, int M, int N, int K);
+hipError_t gemm_launch(int dtype, const GemmDesc& g, void* ws, size_t ws_bytes, hipStream_t stream);
+
+// Attention on the packed per-rank qkv [T, 3*h_l] = [Q | K | V].
+struct AttnDesc {
+  int batch = 0, seq = 0, n_local = 0, head_dim = 0;
+  int head0 = 0;       // 0-based global index of local head 0 (rank * n_local)
+  int n_heads = 1;     // global head count (ALiBi slopes)
+  int alibi = 0;
+  const void* qkv = nullptr;  // [T, 3*h_l]
+  void* ctx = nullptr;        // [T, h_l]
+  float* lse = nullptr;       // [batch, n_local, seq]
+  // backward only
+  const void* dctx = nullptr;  // [T, h_l]
+  float* delta = nullptr;      // [batch, n_local, seq] scratch: rowsum(dctx * ctx)
+  void* dqkv = nullptr;        // [T, 3*h_l]
+};
+bool attn_mfma_supported(int dtype, int head_dim);
+hipError_t attn_fwd_launch(int dtype, const AttnDesc& a, hipStream_t stream);
+hipError_t attn_bwd_launch(int dtype, const AttnDesc& a, hipStream_t stream);
+
+// out[n] = sum_m X[m*ld + n] for n < N (fp32 accumulation, fixed order).
+size_t colsum_workspace_bytes(int M, int N);
+hipError_t colsum_launch(int dtype, const void* X, int M, int N, long ld, void* out, float* ws,
+                         hipStream_t stream);
+
+// out[i] = sum_k parts[k][i] + bias[i % cols] over count elements.
+hipError_t sum_partials_launch(int dtype, const void* const* parts, int n_parts, const void* bias,
+                               void* out, long long count, int cols, hipStream_t stream);
+
+// Fill rows x cols (leading dimension ld) of dtype elements with zero.
+hipError_t zero_launch(int dtype, void* p, long long rows, long long cols, long long ld,
+                       hipStream_t stream);
+
+}  // namespace tpk

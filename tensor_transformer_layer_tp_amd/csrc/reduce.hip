@@ -1,0 +1,134 @@
+// Bandwidth-bound helpers: column sums (bias gradients), the emulated f / g
+// sum over ranks' partials, and zero fill.
+#include "common.h"
+#include "kernels.h"
+
+namespace tpk {
+namespace {
+
+constexpr int CB = 256;  // columns per workgroup (one per thread)
+
+// part[y][n] = sum of X[r][n] over the y-th run of rows.
+template <typename T>
+__global__ __launch_bounds__(CB) void colsum_part_kernel(const T* X, int M, int N, long ld, int rows_per,
+                                                         float* part) {
+  const int n = blockIdx.x * CB + threadIdx.x;
+  if (n >= N) return;
+  const int r0 = blockIdx.y * rows_per;
+  const int r1 = min(M, r0 + rows_per);
+  float s = 0.f;
+  for (int r = r0; r < r1; ++r) s += to_f(X[(long)r * ld + n]);
+  part[(long)blockIdx.y * N + n] = s;
+}
+
+template <typename T>
+__global__ __launch_bounds__(CB) void colsum_final_kernel(const float* part, int R, int N, T* out) {
+  const int n = blockIdx.x * CB + threadIdx.x;
+  if (n >= N) return;
+  float s = 0.f;
+  for (int r = 0; r < R; ++r) s += part[(long)r * N + n];
+  out[n] = from_f<T>(s);
+}
+
+void colsum_split(int M, int N, int& R, int& rows_per) {
+  const int cblocks = (N + CB - 1) / CB;
+  R = (1024 + cblocks - 1) / cblocks;  // aim for ~1024 workgroups
+  const int rmax = (M + 31) / 32;      // at least 32 rows per run
+  if (R > rmax) R = rmax;
+  if (R < 1) R = 1;
+  rows_per = (M + R - 1) / R;
+  if (rows_per < 1) rows_per = 1;
+  R = (M + rows_per - 1) / rows_per;
+  if (R < 1) R = 1;
+}
+
+struct Parts {
+  const void* p[64];
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void sum_partials_kernel(Parts parts, int n_parts, const T* bias, T* out,
+                                                           long long count, int cols) {
+  const long long stride = (long long)gridDim.x * 256;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < count; i += stride) {
+    float s = 0.f;
+    for (int k = 0; k < n_parts; ++k) s += to_f(((const T*)parts.p[k])[i]);
+    if (bias) s += to_f(bias[i % cols]);
+    out[i] = from_f<T>(s);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void zero_kernel(T* p, long long rows, long long cols, long long ld) {
+  const long long count = rows * cols;
+  const long long stride = (long long)gridDim.x * 256;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < count; i += stride) {
+    const long long r = i / cols, c = i - r * cols;
+    p[r * ld + c] = from_f<T>(0.f);
+  }
+}
+
+unsigned grid_for(long long count) {
+  long long g = (count + 255) / 256;
+  if (g > 65536) g = 65536;
+  if (g < 1) g = 1;
+  return (unsigned)g;
+}
+
+}  // namespace
+
+size_t colsum_workspace_bytes(int M, int N) {
+  int R, rows_per;
+  colsum_split(M, N, R, rows_per);
+  return (size_t)R * N * sizeof(float);
+}
+
+hipError_t colsum_launch(int dtype, const void* X, int M, int N, long ld, void* out, float* ws,
+                         hipStream_t stream) {
+  if (N <= 0) return hipSuccess;
+  int R, rows_per;
+  colsum_split(M, N, R, rows_per);
+  const unsigned cblocks = (N + CB - 1) / CB;
+  if (M > 0) {
+    if (dtype == DT_BF16)
+      hipLaunchKernelGGL(colsum_part_kernel<bf16>, dim3(cblocks, R), dim3(CB), 0, stream, (const bf16*)X, M, N, ld,
+                         rows_per, ws);
+    else
+      hipLaunchKernelGGL(colsum_part_kernel<float>, dim3(cblocks, R), dim3(CB), 0, stream, (const float*)X, M, N, ld,
+                         rows_per, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else {
+    R = 0;  // no rows: the sum is zero
+  }
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(colsum_final_kernel<bf16>, dim3(cblocks), dim3(CB), 0, stream, ws, R, N, (bf16*)out);
+  else
+    hipLaunchKernelGGL(colsum_final_kernel<float>, dim3(cblocks), dim3(CB), 0, stream, ws, R, N, (float*)out);
+  return hipGetLastError();
+}
+
+hipError_t sum_partials_launch(int dtype, const void* const* parts, int n_parts, const void* bias, void* out,
+                               long long count, int cols, hipStream_t stream) {
+  if (count <= 0) return hipSuccess;
+  Parts ps{};
+  for (int k = 0; k < n_parts; ++k) ps.p[k] = parts[k];
+  const unsigned g = grid_for(count);
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(sum_partials_kernel<bf16>, dim3(g), dim3(256), 0, stream, ps, n_parts, (const bf16*)bias,
+                       (bf16*)out, count, cols);
+  else
+    hipLaunchKernelGGL(sum_partials_kernel<float>, dim3(g), dim3(256), 0, stream, ps, n_parts, (const float*)bias,
+                       (float*)out, count, cols);
+  return hipGetLastError();
+}
+
+hipError_t zero_launch(int dtype, void* p, long long rows, long long cols, long long ld, hipStream_t stream) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  const unsigned g = grid_for(rows * cols);
+  if (dtype == DT_BF16) hipLaunchKernelGGL(zero_kernel<bf16>, dim3(g), dim3(256), 0, stream, (bf16*)p, rows, cols, ld);
+  else hipLaunchKernelGGL(zero_kernel<float>, dim3(g), dim3(256), 0, stream, (float*)p, rows, cols, ld);
+  return hipGetLastError();
+}
+
+}  // namespace tpk

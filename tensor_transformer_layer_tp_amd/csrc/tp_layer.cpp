@@ -1,0 +1,372 @@
+// C ABI of the tensor-parallel layer shard: argument validation, workspace
+// planning and the launch sequence of each operation on the caller's stream.
+// See include/tp_layer.h for the contract of every entry point.
+#include "../../include/tp_layer.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kernels.h"
+
+using namespace tpk;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tp_status fail(tp_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+tp_status hip_fail(hipError_t e, const char* where) {
+  return fail(TP_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr long long kMaxElems = 1LL << 30;  // per tensor (32-bit byte offsets)
+constexpr int kMaxDim = 1 << 22;
+
+struct Dims {
+  long long T, h, hl, fl, nl, d;
+  int dtype;
+  size_t esz;
+};
+
+tp_status check_shape(const tp_shape* s, Dims& dm) {
+  if (!s) return fail(TP_ERR_NULL, "shape is NULL");
+  if (s->tp_size < 1 || s->tp_rank < 0 || s->tp_rank >= s->tp_size)
+    return fail(TP_ERR_RANK, "tp_rank %d outside [0, tp_size=%d)", s->tp_rank, s->tp_size);
+  if (s->dtype != TP_FP32 && s->dtype != TP_BF16) return fail(TP_ERR_DTYPE, "dtype %d is not TP_FP32/TP_BF16", s->dtype);
+  if (s->batch < 0 || s->seq < 0 || s->hidden <= 0 || s->ffn <= 0 || s->n_heads <= 0 || s->head_dim <= 0)
+    return fail(TP_ERR_SHAPE, "sizes must be positive (batch, seq may be 0)");
+  if (s->batch > 65535 || s->seq > 65536 || s->hidden > kMaxDim || s->ffn > kMaxDim)
+    return fail(TP_ERR_SHAPE, "size limit exceeded (batch <= 65535, seq <= 65536, hidden/ffn <= 2^22)");
+  if (s->causal != 1) return fail(TP_ERR_SHAPE, "only the causal (left-to-right) mask is supported");
+  if (s->alibi != 0 && s->alibi != 1) return fail(TP_ERR_SHAPE, "alibi must be 0 or 1");
+  if (s->n_heads % s->tp_size != 0) return fail(TP_ERR_DIVISIBILITY, "n_heads %d not divisible by tp_size %d", s->n_heads, s->tp_size);
+  if (s->ffn % s->tp_size != 0) return fail(TP_ERR_DIVISIBILITY, "ffn %d not divisible by tp_size %d", s->ffn, s->tp_size);
+  if ((long long)s->n_heads * s->head_dim != s->hidden)
+    return fail(TP_ERR_DIVISIBILITY, "n_heads*head_dim = %lld != hidden %d", (long long)s->n_heads * s->head_dim, s->hidden);
+  if (s->head_dim < 8 || s->head_dim > 256 || s->head_dim % 8 != 0)
+    return fail(TP_ERR_HEADDIM, "head_dim %d not a multiple of 8 in [8, 256]", s->head_dim);
+  dm.T = (long long)s->batch * s->seq;
+  dm.h = s->hidden;
+  dm.nl = s->n_heads / s->tp_size;
+  dm.d = s->head_dim;
+  dm.hl = dm.nl * dm.d;
+  dm.fl = s->ffn / s->tp_size;
+  dm.dtype = s->dtype;
+  dm.esz = s->dtype == TP_BF16 ? 2 : 4;
+  if (s->dtype == TP_BF16 && (dm.h % 8 || dm.fl % 8 || dm.hl % 8))
+    return fail(TP_ERR_ALIGN, "bf16 needs hidden, ffn/tp and hidden/tp to be multiples of 8");
+  const long long big[] = {dm.T * dm.h, dm.T * dm.fl, dm.T * 3 * dm.hl, dm.h * dm.fl, dm.h * 3 * dm.hl};
+  for (long long v : big)
+    if (v >= kMaxElems) return fail(TP_ERR_SHAPE, "a tensor of this shape has >= 2^30 elements");
+  if (dm.T >= kMaxDim) return fail(TP_ERR_SHAPE, "batch*seq must be < 2^22");
+  return TP_OK;
+}
+
+// Required pointer: non-NULL unless its tensor is empty; 16-byte aligned.
+tp_status check_ptr(const void* p, const char* name, bool empty_ok) {
+  if (!p) {
+    if (empty_ok) return TP_OK;
+    return fail(TP_ERR_NULL, "%s is NULL", name);
+  }
+  if (((uintptr_t)p) & 15u) return fail(TP_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return TP_OK;
+}
+
+#define TP_CHECK(expr)                 \
+  do {                                 \
+    tp_status _st = (expr);            \
+    if (_st != TP_OK) return _st;      \
+  } while (0)
+
+#define TP_HIP(expr, where)                         \
+  do {                                              \
+    hipError_t _e = (expr);                         \
+    if (_e != hipSuccess) return hip_fail(_e, where); \
+  } while (0)
+
+// Bump allocation inside the caller's workspace (256-byte aligned pieces).
+struct Bump {
+  char* base;
+  size_t off = 0;
+  explicit Bump(void* b) : base((char*)b) {}
+  void* take(size_t bytes) {
+    off = (off + 255) & ~(size_t)255;
+    void* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+size_t max3(size_t a, size_t b, size_t c) { return a > b ? (a > c ? a : c) : (b > c ? b : c); }
+
+struct MlpPlan {
+  void *dpre, *gemm_ws, *col_ws;
+  size_t gemm_bytes, col_bytes, total;
+};
+
+MlpPlan plan_mlp(const Dims& dm, void* ws, bool bwd) {
+  Bump bp(ws);
+  MlpPlan pl{};
+  const int dt = dm.dtype;
+  if (bwd) pl.dpre = bp.take((size_t)(dm.T * dm.fl) * dm.esz);
+  size_t g = gemm_workspace_bytes(dt, (int)dm.T, (int)dm.fl, (int)dm.h);
+  g = max3(g, gemm_workspace_bytes(dt, (int)dm.T, (int)dm.h, (int)dm.fl), 0);
+  if (bwd) {
+    g = max3(g, gemm_workspace_bytes(dt, (int)dm.fl, (int)dm.h, (int)dm.T),
+             gemm_workspace_bytes(dt, (int)dm.h, (int)dm.fl, (int)dm.T));
+    pl.col_bytes = colsum_workspace_bytes((int)dm.T, (int)(dm.fl > dm.h ? dm.fl : dm.h));
+    pl.col_ws = bp.take(pl.col_bytes);
+  }
+  pl.gemm_bytes = g;
+  pl.gemm_ws = bp.take(g);
+  pl.total = bp.off;
+  return pl;
+}
+
+struct AttnPlan {
+  void *dctx, *dqkv, *delta, *gemm_ws, *col_ws;
+  size_t gemm_bytes, col_bytes, total;
+};
+
+AttnPlan plan_attn(const Dims& dm, void* ws, bool bwd) {
+  Bump bp(ws);
+  AttnPlan pl{};
+  const int dt = dm.dtype;
+  const long long B = dm.T;
+  size_t g = max3(gemm_workspace_bytes(dt, (int)B, (int)(3 * dm.hl), (int)dm.h),
+                  gemm_workspace_bytes(dt, (int)B, (int)dm.h, (int)dm.hl), 0);
+  if (bwd) {
+    pl.dctx = bp.take((size_t)(dm.T * dm.hl) * dm.esz);
+    pl.dqkv = bp.take((size_t)(dm.T * 3 * dm.hl) * dm.esz);
+    pl.delta = bp.take((size_t)(dm.T * dm.nl) * sizeof(float));
+    g = max3(g, gemm_workspace_bytes(dt, (int)B, (int)dm.hl, (int)dm.h),
+             gemm_workspace_bytes(dt, (int)dm.hl, (int)dm.h, (int)B));
+    g = max3(g, gemm_workspace_bytes(dt, (int)dm.h, (int)(3 * dm.hl), (int)B), 0);
+    pl.col_bytes = colsum_workspace_bytes((int)dm.T, (int)(3 * dm.hl > dm.h ? 3 * dm.hl : dm.h));
+    pl.col_ws = bp.take(pl.col_bytes);
+  }
+  pl.gemm_bytes = g;
+  pl.gemm_ws = bp.take(g);
+  pl.total = bp.off;
+  return pl;
+}
+
+tp_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return TP_OK;
+  if (!ws) return fail(TP_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+  if (have < need) return fail(TP_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", have, need);
+  if (((uintptr_t)ws) & 255u) return fail(TP_ERR_ALIGN, "workspace is not 256-byte aligned");
+  return TP_OK;
+}
+
+GemmDesc gd(int M, int N, int K, const void* A, long lda, bool ak, const void* B, long ldb, bool bk, int epi,
+            void* C, long ldc) {
+  GemmDesc g;
+  g.M = M; g.N = N; g.K = K;
+  g.A = A; g.lda = lda; g.a_kmajor = ak;
+  g.B = B; g.ldb = ldb; g.b_kmajor = bk;
+  g.epi = epi;
+  g.C = C; g.ldc = ldc;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tp_last_error(void) { return g_last_error.c_str(); }
+
+size_t tp_mlp_workspace_bytes(const tp_shape* shape) {
+  Dims dm;
+  if (check_shape(shape, dm) != TP_OK) return 0;
+  const MlpPlan a = plan_mlp(dm, nullptr, false), b = plan_mlp(dm, nullptr, true);
+  return a.total > b.total ? a.total : b.total;
+}
+
+size_t tp_attn_workspace_bytes(const tp_shape* shape) {
+  Dims dm;
+  if (check_shape(shape, dm) != TP_OK) return 0;
+  const AttnPlan a = plan_attn(dm, nullptr, false), b = plan_attn(dm, nullptr, true);
+  return a.total > b.total ? a.total : b.total;
+}
+
+tp_status tp_mlp_fwd(const tp_shape* shape, const void* X, const void* A_i, const void* b1_i, const void* B_i,
+                     void* pre_i, void* y_i, void* Z_i, void* workspace, size_t workspace_bytes, void* stream) {
+  Dims dm;
+  TP_CHECK(check_shape(shape, dm));
+  const bool e = dm.T == 0;
+  TP_CHECK(check_ptr(X, "X", e));
+  TP_CHECK(check_ptr(A_i, "A_i", false));
+  TP_CHECK(check_ptr(b1_i, "b1_i", false));
+  TP_CHECK(check_ptr(B_i, "B_i", false));
+  TP_CHECK(check_ptr(pre_i, "pre_i", e));
+  TP_CHECK(check_ptr(y_i, "y_i", e));
+  TP_CHECK(check_ptr(Z_i, "Z_i", e));
+  const MlpPlan need = plan_mlp(dm, nullptr, false);
+  TP_CHECK(check_ws(workspace, workspace_bytes, need.total));
+  if (e) return TP_OK;
+  const MlpPlan pl = plan_mlp(dm, workspace, false);
+  hipStream_t st = (hipStream_t)stream;
+  const int dt = dm.dtype;
+  GemmDesc g1 = gd((int)dm.T, (int)dm.fl, (int)dm.h, X, dm.h, true, A_i, dm.fl, false, EPI_BIAS_GELU, pre_i, dm.fl);
+  g1.C2 = y_i; g1.ldc2 = dm.fl; g1.bias = b1_i;
+  TP_HIP(gemm_launch(dt, g1, pl.gemm_ws, pl.gemm_bytes, st), "mlp GEMM1 (X A_i + b1_i, GeLU)");
+  GemmDesc g2 = gd((int)dm.T, (int)dm.h, (int)dm.fl, y_i, dm.fl, true, B_i, dm.h, false, EPI_STORE, Z_i, dm.h);
+  TP_HIP(gemm_launch(dt, g2, pl.gemm_ws, pl.gemm_bytes, st), "mlp GEMM2 (y_i B_i)");
+  return TP_OK;
+}
+
+tp_status tp_mlp_bwd(const tp_shape* shape, const void* X, const void* A_i, const void* B_i, const void* pre_i,
+                     const void* y_i, const void* dZ, void* dX_i, void* dA_i, void* db1_i, void* dB_i,
+                     void* db2_or_null, void* workspace, size_t workspace_bytes, void* stream) {
+  Dims dm;
+  TP_CHECK(check_shape(shape, dm));
+  const bool e = dm.T == 0;
+  TP_CHECK(check_ptr(X, "X", e));
+  TP_CHECK(check_ptr(A_i, "A_i", false));
+  TP_CHECK(check_ptr(B_i, "B_i", false));
+  TP_CHECK(check_ptr(pre_i, "pre_i", e));
+  TP_CHECK(check_ptr(y_i, "y_i", e));
+  TP_CHECK(check_ptr(dZ, "dZ", e));
+  TP_CHECK(check_ptr(dX_i, "dX_i", e));
+  TP_CHECK(check_ptr(dA_i, "dA_i", false));
+  TP_CHECK(check_ptr(db1_i, "db1_i", false));
+  TP_CHECK(check_ptr(dB_i, "dB_i", false));
+  TP_CHECK(check_ptr(db2_or_null, "db2", true));
+  const MlpPlan need = plan_mlp(dm, nullptr, true);
+  TP_CHECK(check_ws(workspace, workspace_bytes, need.total));
+  const MlpPlan pl = plan_mlp(dm, workspace, true);
+  hipStream_t st = (hipStream_t)stream;
+  const int dt = dm.dtype;
+  const int T = (int)dm.T, h = (int)dm.h, fl = (int)dm.fl;
+  if (T > 0) {
+    GemmDesc g = gd(T, fl, h, dZ, h, true, B_i, h, true, EPI_DGELU, pl.dpre, fl);
+    g.aux = pre_i; g.ldaux = fl;
+    TP_HIP(gemm_launch(dt, g, pl.gemm_ws, pl.gemm_bytes, st), "mlp dgrad (dZ B_i^T * GeLU'(pre_i))");
+  }
+  // weight gradients (K = T; T == 0 gives zeros)
+  TP_HIP(gemm_launch(dt, gd(fl, h, T, y_i, fl, false, dZ, h, false, EPI_STORE, dB_i, h), pl.gemm_ws, pl.gemm_bytes, st),
+         "mlp wgrad dB_i = y_i^T dZ");
+  TP_HIP(gemm_launch(dt, gd(h, fl, T, X, h, false, pl.dpre, fl, false, EPI_STORE, dA_i, fl), pl.gemm_ws, pl.gemm_bytes, st),
+         "mlp wgrad dA_i = X^T dPre");
+  TP_HIP(colsum_launch(dt, pl.dpre, T, fl, fl, db1_i, (float*)pl.col_ws, st), "mlp db1_i");
+  if (T > 0)
+    TP_HIP(gemm_launch(dt, gd(T, h, fl, pl.dpre, fl, true, A_i, fl, true, EPI_STORE, dX_i, h), pl.gemm_ws, pl.gemm_bytes, st),
+           "mlp dgrad dX_i = dPre A_i^T");
+  if (db2_or_null) TP_HIP(colsum_launch(dt, dZ, T, h, h, db2_or_null, (float*)pl.col_ws, st), "mlp db2");
+  return TP_OK;
+}
+
+tp_status tp_attn_fwd(const tp_shape* shape, const void* X, const void* Wqkv_i, const void* bqkv_i, const void* Wo_i,
+                      void* qkv_i, void* ctx_i, float* lse_i, void* O_i, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  Dims dm;
+  TP_CHECK(check_shape(shape, dm));
+  const bool e = dm.T == 0;
+  TP_CHECK(check_ptr(X, "X", e));
+  TP_CHECK(check_ptr(Wqkv_i, "Wqkv_i", false));
+  TP_CHECK(check_ptr(bqkv_i, "bqkv_i", false));
+  TP_CHECK(check_ptr(Wo_i, "Wo_i", false));
+  TP_CHECK(check_ptr(qkv_i, "qkv_i", e));
+  TP_CHECK(check_ptr(ctx_i, "ctx_i", e));
+  TP_CHECK(check_ptr(lse_i, "lse_i", e));
+  TP_CHECK(check_ptr(O_i, "O_i", e));
+  const AttnPlan need = plan_attn(dm, nullptr, false);
+  TP_CHECK(check_ws(workspace, workspace_bytes, need.total));
+  if (e) return TP_OK;
+  const AttnPlan pl = plan_attn(dm, workspace, false);
+  hipStream_t st = (hipStream_t)stream;
+  const int dt = dm.dtype;
+  const int T = (int)dm.T, h = (int)dm.h, hl = (int)dm.hl;
+  GemmDesc g = gd(T, 3 * hl, h, X, h, true, Wqkv_i, 3 * hl, false, EPI_BIAS, qkv_i, 3 * hl);
+  g.bias = bqkv_i;
+  TP_HIP(gemm_launch(dt, g, pl.gemm_ws, pl.gemm_bytes, st), "attn QKV projection");
+  AttnDesc a;
+  a.batch = shape->batch; a.seq = shape->seq; a.n_local = (int)dm.nl; a.head_dim = (int)dm.d;
+  a.head0 = shape->tp_rank * (int)dm.nl; a.n_heads = shape->n_heads; a.alibi = shape->alibi;
+  a.qkv = qkv_i; a.ctx = ctx_i; a.lse = lse_i;
+  TP_HIP(attn_fwd_launch(dt, a, st), "attn forward");
+  TP_HIP(gemm_launch(dt, gd(T, h, hl, ctx_i, hl, true, Wo_i, h, false, EPI_STORE, O_i, h), pl.gemm_ws, pl.gemm_bytes, st),
+         "attn output projection");
+  return TP_OK;
+}
+
+tp_status tp_attn_bwd(const tp_shape* shape, const void* X, const void* Wqkv_i, const void* Wo_i, const void* qkv_i,
+                      const void* ctx_i, const float* lse_i, const void* dO, void* dX_i, void* dWqkv_i, void* dbqkv_i,
+                      void* dWo_i, void* dbo_or_null, void* workspace, size_t workspace_bytes, void* stream) {
+  Dims dm;
+  TP_CHECK(check_shape(shape, dm));
+  const bool e = dm.T == 0;
+  TP_CHECK(check_ptr(X, "X", e));
+  TP_CHECK(check_ptr(Wqkv_i, "Wqkv_i", false));
+  TP_CHECK(check_ptr(Wo_i, "Wo_i", false));
+  TP_CHECK(check_ptr(qkv_i, "qkv_i", e));
+  TP_CHECK(check_ptr(ctx_i, "ctx_i", e));
+  TP_CHECK(check_ptr(lse_i, "lse_i", e));
+  TP_CHECK(check_ptr(dO, "dO", e));
+  TP_CHECK(check_ptr(dX_i, "dX_i", e));
+  TP_CHECK(check_ptr(dWqkv_i, "dWqkv_i", false));
+  TP_CHECK(check_ptr(dbqkv_i, "dbqkv_i", false));
+  TP_CHECK(check_ptr(dWo_i, "dWo_i", false));
+  TP_CHECK(check_ptr(dbo_or_null, "dbo", true));
+  const AttnPlan need = plan_attn(dm, nullptr, true);
+  TP_CHECK(check_ws(workspace, workspace_bytes, need.total));
+  const AttnPlan pl = plan_attn(dm, workspace, true);
+  hipStream_t st = (hipStream_t)stream;
+  const int dt = dm.dtype;
+  const int T = (int)dm.T, h = (int)dm.h, hl = (int)dm.hl;
+  if (T > 0)
+    TP_HIP(gemm_launch(dt, gd(T, hl, h, dO, h, true, Wo_i, h, true, EPI_STORE, pl.dctx, hl), pl.gemm_ws, pl.gemm_bytes, st),
+           "attn dgrad dC = dO Wo_i^T");
+  TP_HIP(gemm_launch(dt, gd(hl, h, T, ctx_i, hl, false, dO, h, false, EPI_STORE, dWo_i, h), pl.gemm_ws, pl.gemm_bytes, st),
+         "attn wgrad dWo_i = ctx_i^T dO");
+  if (dbo_or_null) TP_HIP(colsum_launch(dt, dO, T, h, h, dbo_or_null, (float*)pl.col_ws, st), "attn dbo");
+  if (T > 0) {
+    AttnDesc a;
+    a.batch = shape->batch; a.seq = shape->seq; a.n_local = (int)dm.nl; a.head_dim = (int)dm.d;
+    a.head0 = shape->tp_rank * (int)dm.nl; a.n_heads = shape->n_heads; a.alibi = shape->alibi;
+    a.qkv = qkv_i; a.ctx = (void*)ctx_i; a.lse = (float*)lse_i;
+    a.dctx = pl.dctx; a.delta = (float*)pl.delta; a.dqkv = pl.dqkv;
+    TP_HIP(attn_bwd_launch(dt, a, st), "attn backward");
+  }
+  TP_HIP(gemm_launch(dt, gd(h, 3 * hl, T, X, h, false, pl.dqkv, 3 * hl, false, EPI_STORE, dWqkv_i, 3 * hl), pl.gemm_ws,
+                     pl.gemm_bytes, st),
+         "attn wgrad dWqkv_i = X^T dqkv");
+  TP_HIP(colsum_launch(dt, pl.dqkv, T, 3 * hl, 3 * hl, dbqkv_i, (float*)pl.col_ws, st), "attn dbqkv_i");
+  if (T > 0)
+    TP_HIP(gemm_launch(dt, gd(T, h, 3 * hl, pl.dqkv, 3 * hl, true, Wqkv_i, 3 * hl, true, EPI_STORE, dX_i, h), pl.gemm_ws,
+                       pl.gemm_bytes, st),
+           "attn dgrad dX_i = dqkv Wqkv_i^T");
+  return TP_OK;
+}
+
+tp_status tp_sum_partials(const tp_shape* shape, const void* const* parts, int32_t n_parts, const void* bias_or_null,
+                          void* out, void* stream) {
+  Dims dm;
+  TP_CHECK(check_shape(shape, dm));
+  const bool e = dm.T == 0;
+  if (!parts) return fail(TP_ERR_NULL, "parts is NULL");
+  if (n_parts < 1 || n_parts > 64) return fail(TP_ERR_SHAPE, "n_parts %d outside [1, 64]", n_parts);
+  for (int k = 0; k < n_parts; ++k) TP_CHECK(check_ptr(parts[k], "parts[k]", e));
+  TP_CHECK(check_ptr(bias_or_null, "bias", true));
+  TP_CHECK(check_ptr(out, "out", e));
+  if (e) return TP_OK;
+  TP_HIP(sum_partials_launch(dm.dtype, parts, n_parts, bias_or_null, out, dm.T * dm.h, (int)dm.h, (hipStream_t)stream),
+         "sum of partials");
+  return TP_OK;
+}
+
+}  // extern "C"

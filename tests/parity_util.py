@@ -1,0 +1,76 @@
+"""Comparison helpers shared by the GPU parity tests (HIP path vs fp64 oracle)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+# Relative Frobenius bound per storage type; the element-wise bound catches a
+# localized error (a wrong tile) that a norm over millions of elements hides.
+FRO_TOL = {"fp32": 1e-5, "bf16": 1e-2}
+ELEM_TOL = {"fp32": (2e-5, 1e-5), "bf16": (0.08, 0.02)}  # (x rms(ref), x |ref|)
+
+
+def f64(t) -> np.ndarray:
+    if isinstance(t, np.ndarray):
+        return t.astype(np.float64)
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def compare(name: str, gpu, ref, dtype: str, report: dict | None = None):
+    g, r = f64(gpu), f64(ref)
+    assert g.shape == r.shape, (name, g.shape, r.shape)
+    assert np.all(np.isfinite(g)), f"{name}: non-finite values in the HIP output"
+    nr = np.linalg.norm(r)
+    err = np.linalg.norm(g - r) / (nr if nr > 0 else 1.0)
+    if report is not None:
+        report[name] = err
+    assert err <= FRO_TOL[dtype], f"{name}: relative Frobenius error {err:.3e} > {FRO_TOL[dtype]:.0e}"
+    if r.size:
+        a, b = ELEM_TOL[dtype]
+        rms = np.sqrt(np.mean(r * r))
+        bad = np.abs(g - r) > a * rms + b * np.abs(r)
+        if np.any(bad):
+            idx = np.argwhere(bad)[0]
+            raise AssertionError(f"{name}: {int(bad.sum())} elements out of bound, first at {tuple(idx)}: "
+                                 f"gpu {g[tuple(idx)]:.6g} ref {r[tuple(idx)]:.6g} rms {rms:.3g}")
+    return err
+
+
+def oracle_rank(w, inp: dict, rank: int, alibi=None) -> dict:
+    """Full oracle for one rank's shard (small shapes)."""
+    a = {k: f64(v) for k, v in inp.items()}
+    alibi = w.alibi if alibi is None else alibi
+    kw = dict(batch=w.batch, seq=w.seq, n_heads=w.n_heads, tp_size=w.tp_size, tp_rank=rank, alibi=alibi)
+    qkv, ctx, lse, O = oracle.attn_fwd(a["X_attn"], a["Wqkv"], a["bqkv"], a["Wo"], **kw)
+    dXa, dWqkv, dbqkv, dWo, dbo = oracle.attn_bwd(a["X_attn"], a["Wqkv"], a["bqkv"], a["Wo"], a["dO"], **kw)
+    pre, y, Z = oracle.mlp_fwd(a["X_mlp"], a["A"], a["b1"], a["B"])
+    dXm, dA, db1, dB, db2 = oracle.mlp_bwd(a["X_mlp"], a["A"], a["B"], pre, y, a["dZ"])
+    return dict(qkv=qkv, ctx=ctx, lse=lse, O=O, pre=pre, y=y, Z=Z, dX_mlp=dXm, dA=dA, db1=db1, dB=dB, db2=db2,
+                dX_attn=dXa, dWqkv=dWqkv, dbqkv=dbqkv, dWo=dWo, dbo=dbo)
+
+
+def shape_of(w, rank: int, **kw):
+    import tensor_transformer_layer_tp_amd as tp
+    return tp.TpShape.make(batch=w.batch, seq=w.seq, hidden=w.hidden, ffn=w.ffn, n_heads=w.n_heads,
+                           head_dim=w.head_dim, tp_rank=rank, tp_size=w.tp_size, dtype=w.dtype,
+                           alibi=int(kw.get("alibi", w.alibi)))
+
+
+def shard_of_full(full: dict, rank: int, tp: int) -> dict:
+    """One rank's inputs sliced from the unsharded draw (column / row / head split)."""
+    out = {}
+    for k, v in full.items():
+        n = v.numpy() if v.dtype != torch.bfloat16 else v.view(torch.int16).numpy()
+        if k == "Wqkv" or k == "bqkv":
+            s = oracle.qkv_weight_shard(n, rank, tp)
+        elif k in ("A", "b1"):
+            s = oracle.column_shard(n, rank, tp)
+        elif k in ("Wo", "B"):
+            s = oracle.row_shard(n, rank, tp)
+        else:
+            s = n
+        t = torch.from_numpy(np.ascontiguousarray(s))
+        out[k] = t.view(torch.bfloat16) if v.dtype == torch.bfloat16 else t
+    return out

@@ -1,0 +1,113 @@
+"""Host-side checks of the C-ABI library: it loads without a GPU, exports every
+function the header declares, sizes workspaces, and rejects invalid arguments
+before touching the device (every call here returns before any HIP call)."""
+import ctypes
+import subprocess
+
+import pytest
+
+import tensor_transformer_layer_tp_amd as tp
+
+FAKE = 0x10000  # 16-byte aligned non-null address; never dereferenced by these calls
+
+
+def shape(**kw):
+    base = dict(batch=2, seq=32, hidden=64, ffn=256, n_heads=4, head_dim=16, tp_rank=0, tp_size=2, dtype=tp.TP_FP32)
+    base.update(kw)
+    return tp.TpShape.make(**base)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = tp.load_library()
+    names = tp.exported_symbols()
+    assert set(names) == {"tp_mlp_workspace_bytes", "tp_attn_workspace_bytes", "tp_mlp_fwd", "tp_mlp_bwd",
+                          "tp_attn_fwd", "tp_attn_bwd", "tp_sum_partials", "tp_last_error"}
+    for n in names:
+        assert isinstance(getattr(lib, n), ctypes._CFuncPtr), n
+    out = subprocess.run(["nm", "-D", "--defined-only", tp.library_path()], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(names) <= exported
+
+
+def test_workspace_sizes():
+    assert tp.tp_mlp_workspace_bytes(shape()) > 0
+    assert tp.tp_attn_workspace_bytes(shape()) > 0
+    big = shape(batch=1, seq=2048, hidden=20480, ffn=81920, n_heads=128, head_dim=160, tp_size=8, dtype=tp.TP_BF16)
+    # dPre [T, f_l] bf16 alone is 2048*10240*2 bytes
+    assert tp.tp_mlp_workspace_bytes(big) >= 2048 * 10240 * 2
+    # dctx + dqkv + delta
+    assert tp.tp_attn_workspace_bytes(big) >= 2048 * 2560 * 2 * 4 + 2048 * 16 * 4
+    assert tp.tp_mlp_workspace_bytes(shape(tp_rank=2)) == 0  # invalid shape -> 0
+
+
+def _mlp_fwd(s, ws=(FAKE, 1 << 40), **override):
+    args = dict(X=FAKE, A_i=FAKE, b1_i=FAKE, B_i=FAKE, pre_i=FAKE, y_i=FAKE, Z_i=FAKE)
+    args.update(override)
+    tp.tp_mlp_fwd(s, workspace=ws, stream=0, **args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(tp_rank=2), "TP_ERR_RANK"),
+    (dict(tp_rank=-1), "TP_ERR_RANK"),
+    (dict(tp_size=0, tp_rank=0), "TP_ERR_RANK"),
+    (dict(n_heads=4, tp_size=3), "TP_ERR_DIVISIBILITY"),
+    (dict(ffn=255), "TP_ERR_DIVISIBILITY"),
+    (dict(head_dim=8), "TP_ERR_DIVISIBILITY"),
+    (dict(hidden=60, n_heads=6, head_dim=10, ffn=240), "TP_ERR_HEADDIM"),
+    (dict(dtype=7), "TP_ERR_DTYPE"),
+    (dict(causal=0), "TP_ERR_SHAPE"),
+    (dict(batch=-1), "TP_ERR_SHAPE"),
+    (dict(hidden=72, n_heads=4, head_dim=18, ffn=256, dtype=tp.TP_BF16), "TP_ERR_HEADDIM"),
+    (dict(hidden=96, n_heads=4, head_dim=24, ffn=264, tp_size=2, dtype=tp.TP_BF16), "TP_ERR_ALIGN"),
+])
+def test_shape_validation(kw, status):
+    with pytest.raises(tp.TPError) as ei:
+        _mlp_fwd(shape(**kw))
+    assert ei.value.name == status, str(ei.value)
+    assert tp.tp_last_error() != ""
+
+
+def test_pointer_validation():
+    with pytest.raises(tp.TPError) as ei:
+        _mlp_fwd(shape(), X=None)
+    assert ei.value.name == "TP_ERR_NULL"
+    with pytest.raises(tp.TPError) as ei:
+        _mlp_fwd(shape(), A_i=FAKE + 2)
+    assert ei.value.name == "TP_ERR_ALIGN"
+    s = shape(dtype=tp.TP_BF16, hidden=512, ffn=2048, n_heads=4, head_dim=128)
+    need = tp.tp_mlp_workspace_bytes(s)
+    assert need > 0
+    with pytest.raises(tp.TPError) as ei:
+        _mlp_fwd(s, ws=(FAKE, 16))
+    assert ei.value.name == "TP_ERR_WORKSPACE"
+    with pytest.raises(tp.TPError) as ei:
+        _mlp_fwd(s, ws=(None, 0))
+    assert ei.value.name == "TP_ERR_WORKSPACE"
+    with pytest.raises(tp.TPError) as ei:
+        _mlp_fwd(s, ws=(FAKE + 16, need))
+    assert ei.value.name == "TP_ERR_ALIGN"
+
+
+def test_every_entry_point_validates():
+    s = shape(tp_rank=5)
+    with pytest.raises(tp.TPError):
+        tp.tp_mlp_bwd(s, *([FAKE] * 10), workspace=(FAKE, 1 << 40), stream=0)
+    with pytest.raises(tp.TPError):
+        tp.tp_attn_fwd(s, *([FAKE] * 8), workspace=(FAKE, 1 << 40), stream=0)
+    with pytest.raises(tp.TPError):
+        tp.tp_attn_bwd(s, *([FAKE] * 11), workspace=(FAKE, 1 << 40), stream=0)
+    with pytest.raises(tp.TPError):
+        tp.tp_sum_partials(s, [FAKE, FAKE], None, FAKE, stream=0)
+    with pytest.raises(tp.TPError) as ei:
+        tp.tp_sum_partials(shape(), [], None, FAKE, stream=0)
+    assert ei.value.name == "TP_ERR_SHAPE"
+    with pytest.raises(tp.TPError) as ei:
+        tp.tp_attn_bwd(shape(), *([FAKE] * 7), None, FAKE, FAKE, FAKE, workspace=(FAKE, 1 << 40), stream=0)
+    assert ei.value.name == "TP_ERR_NULL"
+
+
+def test_empty_batch_needs_no_token_pointers():
+    # batch 0: token-shaped pointers may be NULL; the forward enqueues nothing
+    s = shape(batch=0)
+    tp.tp_mlp_fwd(s, None, FAKE, FAKE, FAKE, None, None, None, workspace=(FAKE, 1 << 40), stream=0)
+    tp.tp_attn_fwd(s, None, FAKE, FAKE, FAKE, None, None, None, None, workspace=(FAKE, 1 << 40), stream=0)
