@@ -1,0 +1,245 @@
+"""Benchmark: one tensor-parallel rank's layer shard, forward + backward, on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is the whole path on one micro-batch: tp_attn_fwd, tp_mlp_fwd,
+tp_mlp_bwd, tp_attn_bwd (the twelve products, the attention kernels and the
+bias-gradient sums), inputs resident in HBM. Throughput is algorithmic flops
+per second:
+    F = 3 * [2 T h (4 h_l + 2 f_l) + 2 b n_l d s (s + 1)]
+(causal attention counts the j <= i triangle; the backward pass is twice the
+forward; recomputation and elementwise work are not credited).
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak (published)
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def layer_flops(w, n_l=None, f_l=None) -> float:
+    n_l = w.heads_local if n_l is None else n_l
+    f_l = w.ffn_local if f_l is None else f_l
+    h_l = n_l * w.head_dim
+    T, h, b, s, d = w.tokens, w.hidden, w.batch, w.seq, w.head_dim
+    return 3.0 * (2.0 * T * h * (4 * h_l + 2 * f_l) + 2.0 * b * n_l * d * s * (s + 1))
+
+
+def step_flops(w) -> dict:
+    """Algorithmic flops of each timed step (per launch sequence)."""
+    T, h, hl, fl = w.tokens, w.hidden, w.h_local, w.ffn_local
+    att = 2.0 * w.batch * w.heads_local * w.head_dim * w.seq * (w.seq + 1)
+    g = lambda m, n, k: 2.0 * m * n * k  # noqa: E731
+    return {
+        "qkv_proj": g(T, 3 * hl, h), "attn_fwd": att, "out_proj": g(T, h, hl), "fc1": g(T, fl, h),
+        "fc2": g(T, h, fl), "fc2_dgrad": g(T, fl, h), "fc2_wgrad": g(fl, h, T), "fc1_wgrad": g(h, fl, T),
+        "fc1_dgrad": g(T, h, fl), "out_dgrad": g(T, hl, h), "out_wgrad": g(hl, h, T), "attn_bwd": 2 * att,
+        "qkv_wgrad": g(h, 3 * hl, T), "qkv_dgrad": g(T, h, 3 * hl), "bias_grads": 0.0,
+    }
+
+
+# Kernel names per step (as the trace shows them) for the roofline record.
+KERNEL_OF_STEP = {
+    "qkv_proj": "gemm_qkv_proj", "out_proj": "gemm_out_proj", "fc1": "gemm_fc1_bias_gelu", "fc2": "gemm_fc2",
+    "fc2_dgrad": "gemm_fc2_dgrad_gelu", "fc2_wgrad": "gemm_fc2_wgrad", "fc1_wgrad": "gemm_fc1_wgrad",
+    "fc1_dgrad": "gemm_fc1_dgrad", "out_dgrad": "gemm_out_dgrad", "out_wgrad": "gemm_out_wgrad",
+    "qkv_wgrad": "gemm_qkv_wgrad", "qkv_dgrad": "gemm_qkv_dgrad",
+}
+
+
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm_mfma.hip", "common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "tensor_transformer_layer_tp_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken on
+    the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_b = re.search(r"traffic_bytes_per_launch\s*=\s*([0-9.eE+]+)", text)
+    m_h = re.search(r"source_sha256_16\s*=\s*([0-9a-f]+)", text)
+    if not (m_b and m_h) or m_h.group(1) != gemm_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(w, inp, target_s: float) -> dict:
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload:
+    a sub-shard of this rank (its first n_sub heads and first f_sub FFN
+    columns; a column block of a column-parallel shard is itself a shard), on
+    the same tokens. Rate = algorithmic flops of the sample / wall time."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    f64 = lambda t: t.double().numpy()  # noqa: E731
+    X_attn, X_mlp, dO, dZ = f64(inp["X_attn"]), f64(inp["X_mlp"]), f64(inp["dO"]), f64(inp["dZ"])
+    n_l, f_l, d = w.heads_local, w.ffn_local, w.head_dim
+    h_l = n_l * d
+
+    def run(n_sub: int, f_sub: int) -> float:
+        cols = np.concatenate([np.arange(k * h_l, k * h_l + n_sub * d) for k in range(3)])
+        Wqkv = f64(inp["Wqkv"][:, cols])
+        bqkv = f64(inp["bqkv"][cols])
+        Wo = f64(inp["Wo"][:n_sub * d])
+        A, b1, B = f64(inp["A"][:, :f_sub]), f64(inp["b1"][:f_sub]), f64(inp["B"][:f_sub])
+        kw = dict(batch=w.batch, seq=w.seq, n_heads=w.n_heads, tp_size=w.n_heads // n_sub, tp_rank=0,
+                  alibi=w.alibi)
+        t0 = time.perf_counter()
+        oracle.attn_fwd(X_attn, Wqkv, bqkv, Wo, **kw)
+        oracle.attn_bwd(X_attn, Wqkv, bqkv, Wo, dO, **kw)
+        pre, y, _ = oracle.mlp_fwd(X_mlp, A, b1, B)
+        oracle.mlp_bwd(X_mlp, A, B, pre, y, dZ)
+        return time.perf_counter() - t0
+
+    k = n_l  # start at 1/n_l of the shard (one head, f_l/n_l FFN columns)
+    while True:
+        n_sub, f_sub = max(1, n_l // k), max(8, f_l // k)
+        t = run(n_sub, f_sub)
+        log(f"cpu baseline: {n_sub}/{n_l} heads, {f_sub}/{f_l} ffn columns: {t:.2f} s")
+        if t >= target_s / 3 or k == 1 or t * 2 > target_s:
+            break
+        grow = max(2, 2 ** int(math.log2(max(1.0, target_s / max(t, 1e-3)))))
+        k = max(1, k // grow)
+        while n_l % k:
+            k -= 1
+    fl = layer_flops(w, n_l=n_sub, f_l=f_sub)
+    return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, fwd+bwd of a sub-shard of rank 0: {n_sub} of {n_l} heads and "
+                      f"{f_sub} of {f_l} FFN columns on all {w.tokens} tokens ({fl:.3e} algorithmic flops "
+                      f"in {t:.2f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mtnlg_530b_tp8")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-target-s", type=float, default=15.0)
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {a.gpus} requested): this build runs one tensor-parallel "
+              "rank's shard on one device; multi-GPU runs are not part of it.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import tensor_transformer_layer_tp_amd as tp
+    from tensor_transformer_layer_tp_amd.shard import INPUTS, LayerShard
+
+    w = synth.WORKLOADS[a.workload]
+    if w.dtype != "bf16":
+        raise SystemExit("the benchmark runs the bf16 workloads")
+    tp.load_library()
+    log(f"workload {w.name}: drawing seeded inputs")
+    inp = synth.draw_shard(w, seed=0)
+    shape = tp.TpShape.make(batch=w.batch, seq=w.seq, hidden=w.hidden, ffn=w.ffn, n_heads=w.n_heads,
+                            head_dim=w.head_dim, tp_rank=0, tp_size=w.tp_size, dtype=w.dtype, alibi=int(w.alibi))
+    dev = {k: inp[k].cuda() for k in INPUTS}
+    ls = LayerShard(shape, dev)
+    torch.cuda.synchronize()
+    log(f"warmup {a.warmup} steps")
+    for _ in range(a.warmup):
+        ls.step()
+    torch.cuda.synchronize()
+
+    # per-step breakdown (separate pass, every step bracketed by events)
+    sf = step_flops(w)
+    tp.tp_profile_enable(sum(1 << v for v in tp.STEPS.values()))
+    nb = 3
+    for _ in range(nb):
+        ls.step()
+    torch.cuda.synchronize()
+    breakdown = {}
+    for name, sid in tp.STEPS.items():
+        n, ms = tp.tp_profile_collect(sid)
+        if n:
+            breakdown[name] = ms / nb
+    tp.tp_profile_enable(0)
+    tot = sum(breakdown.values())
+    for name, ms in sorted(breakdown.items(), key=lambda kv: -kv[1]):
+        tf = sf[name] / (ms / 1e3) / 1e12 if ms > 0 else 0.0
+        log(f"  {name:11s} {ms:8.3f} ms  {100 * ms / tot:5.1f}%  {tf:7.1f} TFLOP/s  {100 * tf / PEAK_BF16_TFLOPS:5.1f}% peak")
+    gemm_steps = {k: v for k, v in breakdown.items() if k in KERNEL_OF_STEP}
+    dom = max(gemm_steps, key=gemm_steps.get)
+
+    # timed region; the dominant kernel's launches are bracketed by events on the same stream
+    log(f"timing {a.steps} steps (dominant kernel: {KERNEL_OF_STEP[dom]})")
+    tp.tp_profile_enable(1 << tp.STEPS[dom])
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(a.steps):
+        ls.step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = e0.elapsed_time(e1) / a.steps
+    n_dom, ms_dom = tp.tp_profile_collect(tp.STEPS[dom])
+    tp.tp_profile_enable(0)
+    avg_dom_ms = ms_dom / max(n_dom, 1)
+    F = layer_flops(w)
+    value = F / (ms_step / 1e3) / 1e12
+    log(f"{ms_step:.3f} ms/step, {value:.1f} TFLOP/s ({100 * value / PEAK_BF16_TFLOPS:.1f}% of peak); "
+        f"host wall {wall:.3f} s for {a.steps} steps")
+    achieved = sf[dom] / (avg_dom_ms / 1e3) / 1e12
+    kernel = KERNEL_OF_STEP[dom]
+    traffic = stored_traffic(kernel, w.name)
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": kernel,
+            "flops_per_launch": sf[dom], "avg_launch_ms": round(avg_dom_ms, 4), "launches": n_dom}
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle on a bounded sample)")
+        cpu = cpu_baseline(w, inp, a.cpu_target_s)
+
+    out = {
+        "metric": "layer-shard fwd+bwd TFLOP/s (bf16) on 1 MI355X; % of MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) activations and gradients, N(0,0.02) weights)",
+        "pct_of_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq, "hidden": w.hidden,
+                   "heads": f"{w.heads_local} of {w.n_heads}", "head_dim": w.head_dim,
+                   "ffn_shard": f"{w.ffn_local} of {w.ffn}", "tp_rank": 0, "tp_size": w.tp_size,
+                   "alibi": w.alibi, "flops_per_step": F},
+        "breakdown_ms": {k: round(v, 4) for k, v in breakdown.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

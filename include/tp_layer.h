@@ -76,9 +76,11 @@ typedef struct {
                                (Megatron-DeepSpeed blog, section 4.3)           */
 } tp_shape;
 
-/* Supported sizes. head_dim: 8..256 and a multiple of 8 (bf16 also requires
- * hidden, ffn/p and h/p to be multiples of 8); seq <= 65536; every matrix
- * dimension < 2^31 elements per row and T*max(h, 3h_l, f_l) < 2^40. */
+/* Supported sizes (else TP_ERR_SHAPE / TP_ERR_HEADDIM / TP_ERR_ALIGN):
+ * head_dim a multiple of 8 in [8, 256]; batch <= 65535, seq <= 65536,
+ * batch*seq < 2^22, hidden and ffn <= 2^22; every tensor (X, pre_i, qkv_i,
+ * A_i, Wqkv_i, ...) below 2^30 elements; bf16 also needs hidden, ffn/p and
+ * hidden/p to be multiples of 8. */
 
 /* Workspace bytes the calls below need for this shape (0 on an invalid shape).
  * Host-only; no HIP call. */
@@ -110,7 +112,8 @@ tp_status tp_mlp_bwd(const tp_shape* shape, const void* X, const void* A_i, cons
                      size_t workspace_bytes, void* stream);
 
 /* Attention forward (Megatron-LM deep dive, Fig. 3b):
- *   qkv_i = X Wqkv_i + bqkv_i    Wqkv_i [h,3h_l] = [Wq_i | Wk_i | Wv_i] (the
+ *   qkv_i = X Wqkv_i + bqkv_i    (fp32 for both storage types, see below)
+ *                                Wqkv_i [h,3h_l] = [Wq_i | Wk_i | Wv_i] (the
  *                                columns of this rank's heads), bqkv_i [3h_l];
  *                                local head l uses columns l*d..l*d+d-1 of each
  *                                third; rank r owns global heads r*n_l..r*n_l+n_l-1
@@ -118,10 +121,13 @@ tp_status tp_mlp_bwd(const tp_shape* shape, const void* X, const void* A_i, cons
  *   mask, row softmax, ctx = softmax(S) v; lse = log-sum-exp of each row of S
  *   O_i = ctx_i Wo_i             Wo_i [h_l,h] (row shard); O_i [T,h] is this
  *                                rank's PARTIAL sum; bo is not added.
- * Saved for backward: qkv_i [T,3h_l], ctx_i [T,h_l] (heads side by side),
- * lse_i [batch, n_l, seq] fp32. */
+ * Saved for backward: qkv_i [T,3h_l] fp32, ctx_i [T,h_l] (heads side by
+ * side), lse_i [batch, n_l, seq] fp32. qkv_i is kept in fp32 because the
+ * scores q.k/sqrt(d) can be large and nearly tied (rows sharper than bf16 can
+ * resolve); the bf16 path forms them from q and k split into bf16 high and
+ * low parts (three matrix-core products), accurate to about 2^-16. */
 tp_status tp_attn_fwd(const tp_shape* shape, const void* X, const void* Wqkv_i, const void* bqkv_i,
-                      const void* Wo_i, void* qkv_i, void* ctx_i, float* lse_i, void* O_i,
+                      const void* Wo_i, float* qkv_i, void* ctx_i, float* lse_i, void* O_i,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Attention backward: gradients of <O_i + bo, dO>, dO [T,h] replicated.
@@ -132,7 +138,7 @@ tp_status tp_attn_fwd(const tp_shape* shape, const void* X, const void* Wqkv_i, 
  *   dX_i = dqkv Wqkv_i^T [T,h]   PARTIAL input gradient
  *   dbo = sum_t dO [h]           replicated bias; written only if dbo_or_null != NULL */
 tp_status tp_attn_bwd(const tp_shape* shape, const void* X, const void* Wqkv_i, const void* Wo_i,
-                      const void* qkv_i, const void* ctx_i, const float* lse_i, const void* dO,
+                      const float* qkv_i, const void* ctx_i, const float* lse_i, const void* dO,
                       void* dX_i, void* dWqkv_i, void* dbqkv_i, void* dWo_i, void* dbo_or_null,
                       void* workspace, size_t workspace_bytes, void* stream);
 
@@ -142,6 +148,36 @@ tp_status tp_attn_bwd(const tp_shape* shape, const void* X, const void* Wqkv_i, 
  * tensors in shape->dtype; bias_or_null [h] may be NULL. out may alias parts[0]. */
 tp_status tp_sum_partials(const tp_shape* shape, const void* const* parts, int32_t n_parts,
                           const void* bias_or_null, void* out, void* stream);
+
+/* Steps of the path, for per-step timing. The id doubles as the bit position
+ * in tp_profile_enable's mask. */
+enum {
+  TP_STEP_QKV_PROJ = 1,   /* qkv_i = X Wqkv_i + bqkv_i                       */
+  TP_STEP_ATTN_FWD = 2,   /* per-head causal attention, forward              */
+  TP_STEP_OUT_PROJ = 3,   /* O_i = ctx_i Wo_i                                */
+  TP_STEP_FC1 = 4,        /* pre_i = X A_i + b1_i, y_i = GeLU(pre_i)         */
+  TP_STEP_FC2 = 5,        /* Z_i = y_i B_i                                   */
+  TP_STEP_FC2_DGRAD = 6,  /* dPre = (dZ B_i^T) * GeLU'(pre_i)                */
+  TP_STEP_FC2_WGRAD = 7,  /* dB_i = y_i^T dZ                                 */
+  TP_STEP_FC1_WGRAD = 8,  /* dA_i = X^T dPre                                 */
+  TP_STEP_FC1_DGRAD = 9,  /* dX_i = dPre A_i^T                               */
+  TP_STEP_OUT_DGRAD = 10, /* dC = dO Wo_i^T                                  */
+  TP_STEP_OUT_WGRAD = 11, /* dWo_i = ctx_i^T dO                              */
+  TP_STEP_ATTN_BWD = 12,  /* per-head causal attention, backward             */
+  TP_STEP_QKV_WGRAD = 13, /* dWqkv_i = X^T dqkv                              */
+  TP_STEP_QKV_DGRAD = 14, /* dX_i = dqkv Wqkv_i^T                            */
+  TP_STEP_BIAS_GRADS = 15 /* column sums db1_i, db2, dbo, dbqkv_i            */
+};
+
+/* Measurement aid (no passage of the pages; for benchmarks): while bit k of
+ * step_mask is set, every launch sequence of step k is bracketed by a pair of
+ * hipEvents recorded on the caller's stream (the events are created on first
+ * use and pooled). tp_profile_enable discards what was recorded and sets the
+ * mask (0 turns timing off). tp_profile_collect waits for the recorded events
+ * of one step, returns how many launch sequences were recorded and their total
+ * GPU time in ms, and forgets them. Not for use under stream capture. */
+tp_status tp_profile_enable(uint32_t step_mask);
+tp_status tp_profile_collect(int32_t step, int32_t* launches, double* total_ms);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* tp_last_error(void);

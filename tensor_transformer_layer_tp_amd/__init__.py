@@ -20,7 +20,8 @@ import re
 __all__ = [
     "TpShape", "TPError", "TP_FP32", "TP_BF16", "STATUS", "library_path", "load_library",
     "exported_symbols", "tp_mlp_workspace_bytes", "tp_attn_workspace_bytes", "tp_mlp_fwd",
-    "tp_mlp_bwd", "tp_attn_fwd", "tp_attn_bwd", "tp_sum_partials", "tp_last_error",
+    "tp_mlp_bwd", "tp_attn_fwd", "tp_attn_bwd", "tp_sum_partials", "tp_last_error", "tp_profile_enable",
+    "tp_profile_collect", "STEPS",
 ]
 
 TP_FP32, TP_BF16 = 0, 1
@@ -67,7 +68,16 @@ _SIGS = {
     "tp_attn_fwd": (_st, [ctypes.POINTER(TpShape)] + [_vp] * 8 + [_vp, _sz, _vp]),
     "tp_attn_bwd": (_st, [ctypes.POINTER(TpShape)] + [_vp] * 12 + [_vp, _sz, _vp]),
     "tp_sum_partials": (_st, [ctypes.POINTER(TpShape), ctypes.POINTER(_vp), ctypes.c_int32, _vp, _vp, _vp]),
+    "tp_profile_enable": (_st, [ctypes.c_uint32]),
+    "tp_profile_collect": (_st, [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)]),
     "tp_last_error": (ctypes.c_char_p, []),
+}
+
+# Step ids of tp_profile_enable / tp_profile_collect (TP_STEP_* in the header).
+STEPS = {
+    "qkv_proj": 1, "attn_fwd": 2, "out_proj": 3, "fc1": 4, "fc2": 5, "fc2_dgrad": 6, "fc2_wgrad": 7,
+    "fc1_wgrad": 8, "fc1_dgrad": 9, "out_dgrad": 10, "out_wgrad": 11, "attn_bwd": 12, "qkv_wgrad": 13,
+    "qkv_dgrad": 14, "bias_grads": 15,
 }
 
 
@@ -162,6 +172,17 @@ def tp_attn_bwd(shape, X, Wqkv_i, Wo_i, qkv_i, ctx_i, lse_i, dO, dX_i, dWqkv_i, 
     _check(load_library().tp_attn_bwd(ctypes.byref(shape), _ptr(X), _ptr(Wqkv_i), _ptr(Wo_i), _ptr(qkv_i),
                                       _ptr(ctx_i), _ptr(lse_i), _ptr(dO), _ptr(dX_i), _ptr(dWqkv_i), _ptr(dbqkv_i),
                                       _ptr(dWo_i), _ptr(dbo_or_null), w, wn, _stream(stream)))
+
+
+def tp_profile_enable(step_mask: int):
+    _check(load_library().tp_profile_enable(step_mask))
+
+
+def tp_profile_collect(step: int):
+    """-> (launch sequences recorded, total GPU ms) for one step id."""
+    n, ms = ctypes.c_int32(), ctypes.c_double()
+    _check(load_library().tp_profile_collect(step, ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value
 
 
 def tp_sum_partials(shape, parts, bias_or_null, out, stream=None):

@@ -1,9 +1,15 @@
 // Flash-style causal attention for bf16 on CDNA4 matrix cores
 // (v_mfma_f32_32x32x16_bf16), head widths D in {64, 96, 128, 160}.
 //
-// Layout: per rank, qkv [T, 3*h_l] = [Q | K | V]; local head l uses columns
-// l*D.. of each third; row t = b*seq + position. ctx [T, h_l], lse
+// Layout: per rank, qkv [T, 3*h_l] = [Q | K | V] in fp32; local head l uses
+// columns l*D.. of each third; row t = b*seq + position. ctx [T, h_l] bf16, lse
 // [batch, n_local, seq] (natural log, fp32).
+//
+// Precision: scores are formed from q and k split into bf16 high and low parts,
+// S = q_hi k_hi + q_hi k_lo + q_lo k_hi (three products, error ~2^-16 |q||k|),
+// because rows of large, nearly tied scores amplify bf16 rounding of q and k
+// far beyond the rounding of the output. V, P, dS and dctx enter the products
+// as bf16 (their rounding is not amplified).
 //
 // Forward (one workgroup = 4 waves = 128 queries of one head; each wave owns 32
 // queries): per 64-key tile, K is staged in LDS row-major and V transposed; a
@@ -28,7 +34,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 struct MP {
   int batch, seq, n_local, h_l, head0, n_heads, alibi;
   long ld;             // 3*h_l
-  const bf16* qkv;
+  const float* qkv;
   bf16* ctx;
   float* lse;
   const bf16* dctx;
@@ -45,10 +51,30 @@ __device__ __forceinline__ float alibi_slope_log2(const MP& p, int l) {
   return p.alibi ? exp2f(-8.0f * (float)(p.head0 + l + 1) / (float)p.n_heads) * kLog2e : 0.0f;
 }
 
+// 8 consecutive elements as packed bf16 (one 16-byte LDS chunk).
+__device__ __forceinline__ u32x4 load8(const bf16* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ u32x4 load8(const float* p) {
+  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+  bf16x8 v;
+  v[0] = (bf16)a[0]; v[1] = (bf16)a[1]; v[2] = (bf16)a[2]; v[3] = (bf16)a[3];
+  v[4] = (bf16)b[0]; v[5] = (bf16)b[1]; v[6] = (bf16)b[2]; v[7] = (bf16)b[3];
+  return __builtin_bit_cast(u32x4, v);
+}
+// 8 consecutive fp32 elements split into bf16 high and low parts.
+__device__ __forceinline__ void load8_split(const float* p, bf16x8& hi, bf16x8& lo) {
+  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    hi[e] = (bf16)x[e];
+    lo[e] = (bf16)(x[e] - (float)hi[e]);
+  }
+}
+
 // Tile rows [row0, row0+64) of a [seq, *] slab, row-major in LDS with row
 // stride D+8 (the padding spreads rows over the banks). Rows >= seq are zero.
-template <int D>
-__device__ __forceinline__ void stage_rows(bf16* s, const bf16* src, long ld, long grow0, int row0, int seq) {
+template <int D, typename S>
+__device__ __forceinline__ void stage_rows(bf16* s, const S* src, long ld, long grow0, int row0, int seq) {
   constexpr int CPR = D / 8;
 #pragma unroll
   for (int it = 0; it < D / 32; ++it) {
@@ -56,8 +82,24 @@ __device__ __forceinline__ void stage_rows(bf16* s, const bf16* src, long ld, lo
     const int r = id / CPR, c = id - r * CPR;
     const int pos = row0 + r;
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (pos < seq) v = *(const u32x4*)(src + (grow0 + pos) * ld + 8 * c);
+    if (pos < seq) v = load8(src + (grow0 + pos) * ld + 8 * c);
     *(u32x4*)(s + r * (D + 8) + 8 * c) = v;
+  }
+}
+// Same, fp32 source split into high and low bf16 tiles.
+template <int D>
+__device__ __forceinline__ void stage_rows_split(bf16* shi, bf16* slo, const float* src, long ld, long grow0,
+                                                 int row0, int seq) {
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int it = 0; it < D / 32; ++it) {
+    const int id = threadIdx.x + 256 * it;
+    const int r = id / CPR, c = id - r * CPR;
+    const int pos = row0 + r;
+    bf16x8 hi = bf16x8{}, lo = bf16x8{};
+    if (pos < seq) load8_split(src + (grow0 + pos) * ld + 8 * c, hi, lo);
+    *(bf16x8*)(shi + r * (D + 8) + 8 * c) = hi;
+    *(bf16x8*)(slo + r * (D + 8) + 8 * c) = lo;
   }
 }
 
@@ -65,8 +107,8 @@ __device__ __forceinline__ void stage_rows(bf16* s, const bf16* src, long ld, lo
 // the accumulator key order (inside each group of 16: position 8g + 4a + r for
 // tile row 8a + 4g + r), 16-byte chunks XOR-swizzled by swz(d). Each of the
 // first D threads transposes one 8x8 block in registers.
-template <int D>
-__device__ __forceinline__ void stage_trans(bf16* s, const bf16* src, long ld, long grow0, int row0, int seq) {
+template <int D, typename S>
+__device__ __forceinline__ void stage_trans(bf16* s, const S* src, long ld, long grow0, int row0, int seq) {
   const int id = threadIdx.x;
   if (id >= D) return;
   const int rb8 = id & 7, cb8 = id >> 3;
@@ -74,7 +116,7 @@ __device__ __forceinline__ void stage_trans(bf16* s, const bf16* src, long ld, l
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int pos = row0 + 8 * rb8 + j;
-    r[j] = pos < seq ? *(const u32x4*)(src + (grow0 + pos) * ld + 8 * cb8) : u32x4{0u, 0u, 0u, 0u};
+    r[j] = pos < seq ? load8(src + (grow0 + pos) * ld + 8 * cb8) : u32x4{0u, 0u, 0u, 0u};
   }
   const int c16 = rb8 >> 1, a = rb8 & 1;
 #pragma unroll
@@ -109,6 +151,7 @@ template <int D>
 __global__ __launch_bounds__(256) void fwd_mfma(MP p) {
   constexpr int NC = D / 16, NB = D / 32;
   __shared__ __attribute__((aligned(16))) bf16 sK[64 * (D + 8)];
+  __shared__ __attribute__((aligned(16))) bf16 sKl[64 * (D + 8)];
   __shared__ __attribute__((aligned(16))) bf16 sVt[D * 64];
   const int head = blockIdx.x;
   const int b = head / p.n_local, l = head - b * p.n_local;
@@ -116,16 +159,17 @@ __global__ __launch_bounds__(256) void fwd_mfma(MP p) {
   const int qt = nqt - 1 - blockIdx.y;  // heaviest (longest causal prefix) first
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const long grow0 = (long)b * p.seq;
-  const bf16* Qg = p.qkv + (long)l * D;
-  const bf16* Kg = p.qkv + p.h_l + (long)l * D;
-  const bf16* Vg = p.qkv + 2L * p.h_l + (long)l * D;
+  const float* Qg = p.qkv + (long)l * D;
+  const float* Kg = p.qkv + p.h_l + (long)l * D;
+  const float* Vg = p.qkv + 2L * p.h_l + (long)l * D;
   const int q0w = qt * 128 + 32 * w;
   const int myq = q0w + l32;
-  bf16x8 qf[NC];
+  bf16x8 qf[NC], qfl[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    if (myq < p.seq) qf[c] = *(const bf16x8*)(Qg + (grow0 + myq) * p.ld + 16 * c + 8 * g);
-    else qf[c] = bf16x8{};
+    qf[c] = bf16x8{};
+    qfl[c] = bf16x8{};
+    if (myq < p.seq) load8_split(Qg + (grow0 + myq) * p.ld + 16 * c + 8 * g, qf[c], qfl[c]);
   }
   f32x16 o[NB];
 #pragma unroll
@@ -137,7 +181,7 @@ __global__ __launch_bounds__(256) void fwd_mfma(MP p) {
   for (int kt = 0; kt < nkt; ++kt) {
     const int kv0 = kt * 64;
     __syncthreads();
-    stage_rows<D>(sK, Kg, p.ld, grow0, kv0, p.seq);
+    stage_rows_split<D>(sK, sKl, Kg, p.ld, grow0, kv0, p.seq);
     stage_trans<D>(sVt, Vg, p.ld, grow0, kv0, p.seq);
     __syncthreads();
 #pragma unroll
@@ -147,8 +191,11 @@ __global__ __launch_bounds__(256) void fwd_mfma(MP p) {
       f32x16 s = f32x16{};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const bf16x8 kf = *(const bf16x8*)(sK + (32 * sb + l32) * (D + 8) + 16 * c + 8 * g);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s, 0, 0, 0);
+        const int off = (32 * sb + l32) * (D + 8) + 16 * c + 8 * g;
+        const bf16x8 kh = *(const bf16x8*)(sK + off), kl = *(const bf16x8*)(sKl + off);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qf[c], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qfl[c], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qf[c], s, 0, 0, 0);
       }
       // s[q]: key k0 + 8(q>>2) + 4g + (q&3), query myq
       const bool need_mask = (k0 + 31 > q0w) || (k0 + 32 > p.seq);
@@ -206,6 +253,7 @@ template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dkdv_mfma(MP p) {
   constexpr int NC = D / 16, NB = D / 32;
   __shared__ __attribute__((aligned(16))) bf16 sQ[64 * (D + 8)];
+  __shared__ __attribute__((aligned(16))) bf16 sQl[64 * (D + 8)];
   __shared__ __attribute__((aligned(16))) bf16 sC[64 * (D + 8)];
   __shared__ __attribute__((aligned(16))) bf16 sQt[D * 64];
   __shared__ __attribute__((aligned(16))) bf16 sCt[D * 64];
@@ -216,21 +264,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int kvt = blockIdx.y;  // 128-key tile; tile 0 sees the most queries
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const long grow0 = (long)b * p.seq;
-  const bf16* Qg = p.qkv + (long)l * D;
-  const bf16* Kg = p.qkv + p.h_l + (long)l * D;
-  const bf16* Vg = p.qkv + 2L * p.h_l + (long)l * D;
+  const float* Qg = p.qkv + (long)l * D;
+  const float* Kg = p.qkv + p.h_l + (long)l * D;
+  const float* Vg = p.qkv + 2L * p.h_l + (long)l * D;
   const bf16* Cg = p.dctx + (long)l * D;
   const int k0w = kvt * 128 + 32 * w;
   const int myk = k0w + l32;
-  bf16x8 kf[NC], vf[NC];
+  bf16x8 kf[NC], kfl[NC], vf[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
+    kf[c] = bf16x8{};
+    kfl[c] = bf16x8{};
+    vf[c] = bf16x8{};
     if (myk < p.seq) {
-      kf[c] = *(const bf16x8*)(Kg + (grow0 + myk) * p.ld + 16 * c + 8 * g);
-      vf[c] = *(const bf16x8*)(Vg + (grow0 + myk) * p.ld + 16 * c + 8 * g);
-    } else {
-      kf[c] = bf16x8{};
-      vf[c] = bf16x8{};
+      load8_split(Kg + (grow0 + myk) * p.ld + 16 * c + 8 * g, kf[c], kfl[c]);
+      vf[c] = __builtin_bit_cast(bf16x8, load8(Vg + (grow0 + myk) * p.ld + 16 * c + 8 * g));
     }
   }
   f32x16 dv[NB], dk[NB];
@@ -241,7 +289,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int qt = (kvt * 128) / 64; qt < nqt; ++qt) {
     const int q0 = qt * 64;
     __syncthreads();
-    stage_rows<D>(sQ, Qg, p.ld, grow0, q0, p.seq);
+    stage_rows_split<D>(sQ, sQl, Qg, p.ld, grow0, q0, p.seq);
     stage_rows<D>(sC, Cg, p.h_l, grow0, q0, p.seq);
     stage_trans<D>(sQt, Qg, p.ld, grow0, q0, p.seq);
     stage_trans<D>(sCt, Cg, p.h_l, grow0, q0, p.seq);
@@ -260,7 +308,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const int off = (32 * qs + l32) * (D + 8) + 16 * c + 8 * g;
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(sQ + off), kf[c], s, 0, 0, 0);
+        const bf16x8 qh = *(const bf16x8*)(sQ + off), ql = *(const bf16x8*)(sQl + off);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql, kf[c], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, kfl[c], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, kf[c], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(sC + off), vf[c], dp, 0, 0, 0);
       }
       // s[q], dp[q]: query qs0 + 8(q>>2) + 4g + (q&3), key myk
@@ -315,6 +366,7 @@ template <int D>
 __global__ __launch_bounds__(256) void dq_mfma(MP p) {
   constexpr int NC = D / 16, NB = D / 32;
   __shared__ __attribute__((aligned(16))) bf16 sK[64 * (D + 8)];
+  __shared__ __attribute__((aligned(16))) bf16 sKl[64 * (D + 8)];
   __shared__ __attribute__((aligned(16))) bf16 sV[64 * (D + 8)];
   __shared__ __attribute__((aligned(16))) bf16 sKt[D * 64];
   const int head = blockIdx.x;
@@ -323,21 +375,21 @@ __global__ __launch_bounds__(256) void dq_mfma(MP p) {
   const int qt = nqt - 1 - blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const long grow0 = (long)b * p.seq;
-  const bf16* Qg = p.qkv + (long)l * D;
-  const bf16* Kg = p.qkv + p.h_l + (long)l * D;
-  const bf16* Vg = p.qkv + 2L * p.h_l + (long)l * D;
+  const float* Qg = p.qkv + (long)l * D;
+  const float* Kg = p.qkv + p.h_l + (long)l * D;
+  const float* Vg = p.qkv + 2L * p.h_l + (long)l * D;
   const bf16* Cg = p.dctx + (long)l * D;
   const int q0w = qt * 128 + 32 * w;
   const int myq = q0w + l32;
-  bf16x8 qf[NC], cf[NC];
+  bf16x8 qf[NC], qfl[NC], cf[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
+    qf[c] = bf16x8{};
+    qfl[c] = bf16x8{};
+    cf[c] = bf16x8{};
     if (myq < p.seq) {
-      qf[c] = *(const bf16x8*)(Qg + (grow0 + myq) * p.ld + 16 * c + 8 * g);
+      load8_split(Qg + (grow0 + myq) * p.ld + 16 * c + 8 * g, qf[c], qfl[c]);
       cf[c] = *(const bf16x8*)(Cg + (grow0 + myq) * p.h_l + 16 * c + 8 * g);
-    } else {
-      qf[c] = bf16x8{};
-      cf[c] = bf16x8{};
     }
   }
   const float L = myq < p.seq ? p.lse[(long)head * p.seq + myq] * kLog2e : 0.f;
@@ -351,7 +403,7 @@ __global__ __launch_bounds__(256) void dq_mfma(MP p) {
   for (int kt = 0; kt < nkt; ++kt) {
     const int kv0 = kt * 64;
     __syncthreads();
-    stage_rows<D>(sK, Kg, p.ld, grow0, kv0, p.seq);
+    stage_rows_split<D>(sK, sKl, Kg, p.ld, grow0, kv0, p.seq);
     stage_rows<D>(sV, Vg, p.ld, grow0, kv0, p.seq);
     stage_trans<D>(sKt, Kg, p.ld, grow0, kv0, p.seq);
     __syncthreads();
@@ -363,7 +415,10 @@ __global__ __launch_bounds__(256) void dq_mfma(MP p) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const int off = (32 * sb + l32) * (D + 8) + 16 * c + 8 * g;
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(sK + off), qf[c], s, 0, 0, 0);
+        const bf16x8 kh = *(const bf16x8*)(sK + off), kl = *(const bf16x8*)(sKl + off);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qf[c], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qfl[c], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qf[c], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(sV + off), cf[c], dp, 0, 0, 0);
       }
       // s[q]: key k0 + 8(q>>2) + 4g + (q&3), query myq
@@ -404,7 +459,7 @@ MP make_mp(const AttnDesc& a) {
   p.batch = a.batch; p.seq = a.seq; p.n_local = a.n_local;
   p.h_l = a.n_local * a.head_dim; p.head0 = a.head0; p.n_heads = a.n_heads; p.alibi = a.alibi;
   p.ld = 3L * p.h_l;
-  p.qkv = (const bf16*)a.qkv; p.ctx = (bf16*)a.ctx; p.lse = a.lse;
+  p.qkv = a.qkv; p.ctx = (bf16*)a.ctx; p.lse = a.lse;
   p.dctx = (const bf16*)a.dctx; p.delta = a.delta; p.dqkv = (bf16*)a.dqkv;
   p.scale = 1.0f / sqrtf((float)a.head_dim);
   p.scale_log2 = p.scale * kLog2e;

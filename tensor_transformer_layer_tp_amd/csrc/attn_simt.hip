@@ -1,6 +1,7 @@
 // Per-head causal attention on the vector ALUs: the path for fp32 storage and
 // for head widths the matrix-core kernels do not instantiate. One workgroup per
-// (query or key row, local head, batch element); keys are visited 128 at a time
+// (query or key row, local head, batch element); qkv is fp32, ctx / dctx /
+// dqkv use the storage type T. Keys are visited 128 at a time
 // with a running max / sum (online softmax), so memory stays O(d) per row.
 // Also: delta = rowsum(dctx * ctx), the softmax-backward row term, for both paths.
 #include <math.h>
@@ -36,7 +37,7 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 
 struct SP {
   int batch, seq, n_local, d, h_l, head0, n_heads, alibi;
-  const void* qkv; void* ctx; float* lse; const void* dctx; const float* delta; void* dqkv;
+  const float* qkv; void* ctx; float* lse; const void* dctx; const float* delta; void* dqkv;
 };
 
 __device__ __forceinline__ float slope_of(const SP& p, int l) {
@@ -52,11 +53,11 @@ __global__ __launch_bounds__(NT) void fwd_kernel(SP p) {
   const int i = blockIdx.x, l = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int d = p.d;
   const long ld = 3L * p.h_l;
-  const T* qkv = (const T*)p.qkv;
+  const float* qkv = p.qkv;
   const long row0 = (long)b * p.seq;
-  const T* q = qkv + (row0 + i) * ld + (long)l * d;
-  const T* kb = qkv + row0 * ld + p.h_l + (long)l * d;
-  const T* vb = qkv + row0 * ld + 2L * p.h_l + (long)l * d;
+  const float* q = qkv + (row0 + i) * ld + (long)l * d;
+  const float* kb = qkv + row0 * ld + p.h_l + (long)l * d;
+  const float* vb = qkv + row0 * ld + 2L * p.h_l + (long)l * d;
   const float scale = 1.0f / sqrtf((float)d), slope = slope_of(p, l);
   for (int dd = tid; dd < d; dd += NT) sq[dd] = to_f(q[dd]) * scale;
   __syncthreads();
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(NT) void fwd_kernel(SP p) {
     const int j = j0 + tid;
     float s = -INFINITY;
     if (j <= i) {
-      const T* kj = kb + (long)j * ld;
+      const float* kj = kb + (long)j * ld;
       float dot = 0.f;
       for (int dd = 0; dd < d; ++dd) dot = fmaf(sq[dd], to_f(kj[dd]), dot);
       s = dot - slope * (float)(i - j);
@@ -106,13 +107,13 @@ __global__ __launch_bounds__(NT) void dq_kernel(SP p) {
   const int i = blockIdx.x, l = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int d = p.d;
   const long ld = 3L * p.h_l;
-  const T* qkv = (const T*)p.qkv;
+  const float* qkv = p.qkv;
   const long row0 = (long)b * p.seq;
   const float scale = 1.0f / sqrtf((float)d), slope = slope_of(p, l);
-  const T* q = qkv + (row0 + i) * ld + (long)l * d;
+  const float* q = qkv + (row0 + i) * ld + (long)l * d;
   const T* dc = (const T*)p.dctx + (row0 + i) * p.h_l + (long)l * d;
-  const T* kb = qkv + row0 * ld + p.h_l + (long)l * d;
-  const T* vb = qkv + row0 * ld + 2L * p.h_l + (long)l * d;
+  const float* kb = qkv + row0 * ld + p.h_l + (long)l * d;
+  const float* vb = qkv + row0 * ld + 2L * p.h_l + (long)l * d;
   for (int dd = tid; dd < d; dd += NT) { sq[dd] = to_f(q[dd]) * scale; sdc[dd] = to_f(dc[dd]); }
   __syncthreads();
   const long hr = ((long)b * p.n_local + l) * p.seq + i;
@@ -122,8 +123,8 @@ __global__ __launch_bounds__(NT) void dq_kernel(SP p) {
     const int j = j0 + tid;
     float ds = 0.f;
     if (j <= i) {
-      const T* kj = kb + (long)j * ld;
-      const T* vj = vb + (long)j * ld;
+      const float* kj = kb + (long)j * ld;
+      const float* vj = vb + (long)j * ld;
       float s = 0.f, dp = 0.f;
       for (int dd = 0; dd < d; ++dd) {
         s = fmaf(sq[dd], to_f(kj[dd]), s);
@@ -154,12 +155,12 @@ __global__ __launch_bounds__(NT) void dkdv_kernel(SP p) {
   const int j = blockIdx.x, l = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int d = p.d;
   const long ld = 3L * p.h_l;
-  const T* qkv = (const T*)p.qkv;
+  const float* qkv = p.qkv;
   const long row0 = (long)b * p.seq;
   const float scale = 1.0f / sqrtf((float)d), slope = slope_of(p, l);
-  const T* kj = qkv + (row0 + j) * ld + p.h_l + (long)l * d;
-  const T* vj = qkv + (row0 + j) * ld + 2L * p.h_l + (long)l * d;
-  const T* qb = qkv + row0 * ld + (long)l * d;
+  const float* kj = qkv + (row0 + j) * ld + p.h_l + (long)l * d;
+  const float* vj = qkv + (row0 + j) * ld + 2L * p.h_l + (long)l * d;
+  const float* qb = qkv + row0 * ld + (long)l * d;
   const T* dcb = (const T*)p.dctx + row0 * p.h_l + (long)l * d;
   for (int dd = tid; dd < d; dd += NT) { sk[dd] = to_f(kj[dd]) * scale; sv[dd] = to_f(vj[dd]); }
   __syncthreads();
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(NT) void dkdv_kernel(SP p) {
     const int i = i0 + tid;
     float pij = 0.f, ds = 0.f;
     if (i < p.seq) {
-      const T* qi = qb + (long)i * ld;
+      const float* qi = qb + (long)i * ld;
       const T* dci = dcb + (long)i * p.h_l;
       float s = 0.f, dp = 0.f;
       for (int dd = 0; dd < d; ++dd) {
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(NT) void dkdv_kernel(SP p) {
     const int cnt = min(NT, p.seq - i0);
     for (int ii = 0; ii < cnt; ++ii) {
       const float pp = spp[ii], dd_ = sds[ii];
-      const T* qi = qb + (long)(i0 + ii) * ld;
+      const float* qi = qb + (long)(i0 + ii) * ld;
       const T* dci = dcb + (long)(i0 + ii) * p.h_l;
       if (tid < d) { v0 = fmaf(pp, to_f(dci[tid]), v0); k0 = fmaf(dd_, to_f(qi[tid]), k0); }
       if (tid + NT < d) { v1 = fmaf(pp, to_f(dci[tid + NT]), v1); k1 = fmaf(dd_, to_f(qi[tid + NT]), k1); }

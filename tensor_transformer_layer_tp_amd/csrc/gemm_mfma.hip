@@ -1,5 +1,5 @@
 // bf16 GEMM on CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16), fp32 accumulation,
-// with the layer's fused epilogues (bias, bias+GeLU, GeLU' scaling).
+// with the layer's fused epilogues (bias, bias+GeLU, GeLU' scaling, fp32 out).
 //
 // Tiling: a 256x256 output tile per workgroup of 4 waves (2x2), each wave a
 // 128x128 sub-tile = 4x4 MFMA blocks of 32x32 (256 fp32 accumulators per lane).
@@ -244,7 +244,7 @@ __device__ __forceinline__ void epilogue(const KParams& p, int tm, int tn, const
         const int n = tn * BN + wn * 128 + j * 32 + q4 * 8 + (lane >> 5) * 4;
         if (n >= p.N) continue;
         float v[4] = {acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]};
-        if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) {
+        if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_F32) {
           bf16x4 bb = *(const bf16x4*)(p.bias + n);
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] += (float)bb[e];
@@ -253,6 +253,10 @@ __device__ __forceinline__ void epilogue(const KParams& p, int tm, int tn, const
           bf16x4 pa = *(const bf16x4*)(p.aux + (long)m * p.ldaux + n);
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f((float)pa[e]);
+        }
+        if (EPI == EPI_BIAS_F32) {
+          *(f32x4*)((float*)p.C + (long)m * p.ldc + n) = f32x4{v[0], v[1], v[2], v[3]};
+          continue;
         }
         store_bf16x4(p.C + (long)m * p.ldc + n, v);
         if (EPI == EPI_BIAS_GELU) {
@@ -297,10 +301,7 @@ __device__ __forceinline__ void store_partial(float* slot, const f32x16 (&acc)[4
 // then its run of stream-K iterations (whole tiles in the run are stored
 // directly, partial tiles go to the workspace).
 template <bool AK, bool BKM, int EPI>
-__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_bf16_kernel(KParams p) {
-  __shared__ __attribute__((aligned(16))) bf16 sA[2 * STAGE];
-  __shared__ __attribute__((aligned(16))) bf16 sB[2 * STAGE];
+__device__ __forceinline__ void gemm_body(const KParams& p, bf16* sA, bf16* sB) {
   const int lw = logical_wg(blockIdx.x, p.grid);
   const bool in_sk = p.sk_total > 0 && lw < p.sk_grid;
   long long base = 0, rem = 0, s = 0, e = 0;
@@ -349,7 +350,7 @@ void gemm_bf16_kernel(KParams p) {
 // One workgroup per stream-K tile: sum the contributors' partials in
 // contributor order and apply the epilogue.
 template <int EPI>
-__global__ __launch_bounds__(NTHR) void gemm_sk_fixup_kernel(KParams p, int first_tile) {
+__device__ __forceinline__ void fixup_body(const KParams& p, int first_tile) {
   const int t = first_tile + blockIdx.x;
   const long long base = p.sk_total / p.sk_grid, rem = p.sk_total % p.sk_grid;
   const long long t0 = (long long)t * p.iters - p.sk_begin;
@@ -382,6 +383,40 @@ __global__ __launch_bounds__(NTHR) void gemm_sk_fixup_kernel(KParams p, int firs
   tile_coords(p, t, tm, tn);
   epilogue<EPI>(p, tm, tn, acc);
 }
+
+}  // namespace
+
+// One kernel (and its stream-K fix-up kernel) per product of the layer, so
+// that a trace attributes time to each step by name.
+#define TP_GEMM_KERNELS(NAME, AKV, BKV, EV)                                           \
+  __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))     \
+  void NAME(KParams p) {                                                            \
+    __shared__ __attribute__((aligned(16))) bf16 sA[2 * STAGE];                     \
+    __shared__ __attribute__((aligned(16))) bf16 sB[2 * STAGE];                     \
+    gemm_body<AKV, BKV, EV>(p, sA, sB);                                             \
+  }                                                                                 \
+  __global__ __launch_bounds__(NTHR) void NAME##_fixup(KParams p, int first_tile) { \
+    fixup_body<EV>(p, first_tile);                                                  \
+  }
+
+// forward products: A k-inner (activations), B k-outer (weights)
+TP_GEMM_KERNELS(gemm_qkv_proj, true, false, EPI_BIAS_F32)
+TP_GEMM_KERNELS(gemm_out_proj, true, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_fc1_bias_gelu, true, false, EPI_BIAS_GELU)
+TP_GEMM_KERNELS(gemm_fc2, true, false, EPI_STORE)
+// input gradients: both k-inner (weights read transposed)
+TP_GEMM_KERNELS(gemm_fc2_dgrad_gelu, true, true, EPI_DGELU)
+TP_GEMM_KERNELS(gemm_fc1_dgrad, true, true, EPI_STORE)
+TP_GEMM_KERNELS(gemm_out_dgrad, true, true, EPI_STORE)
+TP_GEMM_KERNELS(gemm_qkv_dgrad, true, true, EPI_STORE)
+// weight gradients: both k-outer (K = tokens)
+TP_GEMM_KERNELS(gemm_fc2_wgrad, false, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_fc1_wgrad, false, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_out_wgrad, false, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_qkv_wgrad, false, false, EPI_STORE)
+#undef TP_GEMM_KERNELS
+
+namespace {
 
 struct Plan {
   int grid, dp_rounds, sk_grid, sk_first_tile, sk_tiles;
@@ -456,24 +491,36 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
   dim3 grid(pl.grid), block(NTHR);
   const int first = pl.sk_first_tile, nsk = pl.sk_tiles;
   const bool sk = pl.sk_total > 0;
-#define TP_GEMM_CASE(AKV, BKV, EV)                                                                  \
-  if (g.a_kmajor == AKV && g.b_kmajor == BKV && g.epi == EV) {                                      \
-    hipLaunchKernelGGL((gemm_bf16_kernel<AKV, BKV, EV>), grid, block, 0, stream, p);                \
-    hipError_t e1 = hipGetLastError();                                                              \
-    if (e1 != hipSuccess || !sk) return e1;                                                         \
-    hipLaunchKernelGGL((gemm_sk_fixup_kernel<EV>), dim3(nsk), block, 0, stream, p, first);          \
-    return hipGetLastError();                                                                       \
+  typedef void (*MainK)(KParams);
+  typedef void (*FixK)(KParams, int);
+  MainK mk = nullptr;
+  FixK fk = nullptr;
+  bool ak = true, bk = false;
+  int ep = EPI_STORE;
+#define TP_ROLE(R, NAME, AKV, BKV, EV) \
+  case R: mk = NAME; fk = NAME##_fixup; ak = AKV; bk = BKV; ep = EV; break;
+  switch (g.role) {
+    TP_ROLE(GR_QKV_PROJ, gemm_qkv_proj, true, false, EPI_BIAS_F32)
+    TP_ROLE(GR_OUT_PROJ, gemm_out_proj, true, false, EPI_STORE)
+    TP_ROLE(GR_FC1, gemm_fc1_bias_gelu, true, false, EPI_BIAS_GELU)
+    TP_ROLE(GR_FC2, gemm_fc2, true, false, EPI_STORE)
+    TP_ROLE(GR_FC2_DGRAD, gemm_fc2_dgrad_gelu, true, true, EPI_DGELU)
+    TP_ROLE(GR_FC1_DGRAD, gemm_fc1_dgrad, true, true, EPI_STORE)
+    TP_ROLE(GR_OUT_DGRAD, gemm_out_dgrad, true, true, EPI_STORE)
+    TP_ROLE(GR_QKV_DGRAD, gemm_qkv_dgrad, true, true, EPI_STORE)
+    TP_ROLE(GR_FC2_WGRAD, gemm_fc2_wgrad, false, false, EPI_STORE)
+    TP_ROLE(GR_FC1_WGRAD, gemm_fc1_wgrad, false, false, EPI_STORE)
+    TP_ROLE(GR_OUT_WGRAD, gemm_out_wgrad, false, false, EPI_STORE)
+    TP_ROLE(GR_QKV_WGRAD, gemm_qkv_wgrad, false, false, EPI_STORE)
+    default: return hipErrorInvalidValue;
   }
-  // the products this layer uses: forward (A k-inner, B k-outer), input
-  // gradients (both k-inner), weight gradients (both k-outer)
-  TP_GEMM_CASE(true, false, EPI_STORE)
-  TP_GEMM_CASE(true, false, EPI_BIAS)
-  TP_GEMM_CASE(true, false, EPI_BIAS_GELU)
-  TP_GEMM_CASE(true, true, EPI_STORE)
-  TP_GEMM_CASE(true, true, EPI_DGELU)
-  TP_GEMM_CASE(false, false, EPI_STORE)
-#undef TP_GEMM_CASE
-  return hipErrorInvalidValue;
+#undef TP_ROLE
+  if (g.a_kmajor != ak || g.b_kmajor != bk || g.epi != ep) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mk, grid, block, 0, stream, p);
+  hipError_t e1 = hipGetLastError();
+  if (e1 != hipSuccess || !sk) return e1;
+  hipLaunchKernelGGL(fk, dim3(nsk), block, 0, stream, p, first);
+  return hipGetLastError();
 }
 
 }  // namespace tpk

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(SParams p) {
       const int n = n0 + tx * 4 + j;
       if (n >= p.N) continue;
       float v = acc[i][j];
-      if (p.epi == EPI_BIAS || p.epi == EPI_BIAS_GELU) v += p.bias[n];
+      if (p.epi == EPI_BIAS || p.epi == EPI_BIAS_GELU || p.epi == EPI_BIAS_F32) v += p.bias[n];
       if (p.epi == EPI_DGELU) v *= gelu_grad_f(p.aux[(long)m * p.ldaux + n]);
       p.C[(long)m * p.ldc + n] = v;
       if (p.epi == EPI_BIAS_GELU) p.C2[(long)m * p.ldc2 + n] = gelu_f(v);

@@ -16,6 +16,14 @@ enum Epi : int {
   EPI_BIAS_GELU = 1,  // pre = acc + bias[n]; out2 = gelu(pre); out = pre
   EPI_DGELU = 2,      // out = acc * gelu'(aux[m][n])
   EPI_BIAS = 3,       // out = acc + bias[n]
+  EPI_BIAS_F32 = 4,   // out (fp32) = acc + bias[n]
+};
+
+// The layer's products; the numbers match the TP_STEP_* ids of the C ABI.
+enum GemmRole : int {
+  GR_QKV_PROJ = 1, GR_OUT_PROJ = 3, GR_FC1 = 4, GR_FC2 = 5, GR_FC2_DGRAD = 6, GR_FC2_WGRAD = 7,
+  GR_FC1_WGRAD = 8, GR_FC1_DGRAD = 9, GR_OUT_DGRAD = 10, GR_OUT_WGRAD = 11, GR_QKV_WGRAD = 13,
+  GR_QKV_DGRAD = 14,
 };
 
 // C[M,N] = op(A) op(B) with fp32 accumulation, then an epilogue.
@@ -23,6 +31,7 @@ enum Epi : int {
 //   B: b_kmajor ? B[n*ldb + k] : B[k*ldb + n]
 // epi: one of Epi (C2 receives gelu(pre) for EPI_BIAS_GELU).
 struct GemmDesc {
+  int role = 0;  // GemmRole (selects the bf16 kernel; the fp32 path ignores it)
   int M = 0, N = 0, K = 0;
   const void* A = nullptr; long lda = 0; bool a_kmajor = true;
   const void* B = nullptr; long ldb = 0; bool b_kmajor = false;
@@ -38,12 +47,14 @@ size_t gemm_workspace_bytes(int dtype, int M, int N, int K);
 hipError_t gemm_launch(int dtype, const GemmDesc& g, void* ws, size_t ws_bytes, hipStream_t stream);
 
 // Attention on the packed per-rank qkv [T, 3*h_l] = [Q | K | V].
+// qkv is fp32 for both storage types (scores are formed from split-bf16
+// q and k on the matrix cores); ctx, dctx and dqkv use the storage type.
 struct AttnDesc {
   int batch = 0, seq = 0, n_local = 0, head_dim = 0;
   int head0 = 0;       // 0-based global index of local head 0 (rank * n_local)
   int n_heads = 1;     // global head count (ALiBi slopes)
   int alibi = 0;
-  const void* qkv = nullptr;  // [T, 3*h_l]
+  const float* qkv = nullptr;  // [T, 3*h_l] fp32
   void* ctx = nullptr;        // [T, h_l]
   float* lse = nullptr;       // [batch, n_local, seq]
   // backward only

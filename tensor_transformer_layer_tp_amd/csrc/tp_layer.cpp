@@ -8,7 +8,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "kernels.h"
 
@@ -31,6 +33,62 @@ tp_status fail(tp_status st, const char* fmt, ...) {
 tp_status hip_fail(hipError_t e, const char* where) {
   return fail(TP_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
+
+// ---- per-step timing (tp_profile_enable / tp_profile_collect) -----------------
+// While a step's bit is set, every launch sequence of that step is bracketed by
+// a pair of hipEvents recorded on the caller's stream. Event pairs are pooled
+// per device and reused after collection.
+struct EvPair {
+  hipEvent_t a, b;
+  int dev;
+};
+struct Rec {
+  int step;
+  EvPair ev;
+};
+std::mutex g_prof_mu;
+uint32_t g_prof_mask = 0;
+std::vector<Rec> g_prof_recs;
+std::vector<EvPair> g_prof_pool;
+
+class StepTimer {
+ public:
+  StepTimer(int step, hipStream_t st) : step_(step), st_(st) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!(g_prof_mask & (1u << step))) return;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return;
+    for (size_t i = 0; i < g_prof_pool.size(); ++i)
+      if (g_prof_pool[i].dev == dev) {
+        ev_ = g_prof_pool[i];
+        g_prof_pool.erase(g_prof_pool.begin() + i);
+        active_ = true;
+        break;
+      }
+    if (!active_) {
+      if (hipEventCreate(&ev_.a) != hipSuccess) return;
+      if (hipEventCreate(&ev_.b) != hipSuccess) { (void)hipEventDestroy(ev_.a); return; }
+      ev_.dev = dev;
+      active_ = true;
+    }
+    if (hipEventRecord(ev_.a, st_) != hipSuccess) {
+      g_prof_pool.push_back(ev_);
+      active_ = false;
+    }
+  }
+  ~StepTimer() {
+    if (!active_) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (hipEventRecord(ev_.b, st_) == hipSuccess) g_prof_recs.push_back(Rec{step_, ev_});
+    else g_prof_pool.push_back(ev_);
+  }
+
+ private:
+  int step_;
+  hipStream_t st_;
+  EvPair ev_{};
+  bool active_ = false;
+};
 
 constexpr long long kMaxElems = 1LL << 30;  // per tensor (32-bit byte offsets)
 constexpr int kMaxDim = 1 << 22;
@@ -93,6 +151,14 @@ tp_status check_ptr(const void* p, const char* name, bool empty_ok) {
 
 #define TP_HIP(expr, where)                         \
   do {                                              \
+    hipError_t _e = (expr);                         \
+    if (_e != hipSuccess) return hip_fail(_e, where); \
+  } while (0)
+
+// TP_HIP for one step of the path, timed when profiling selects it.
+#define TP_STEP(step, expr, where)                  \
+  do {                                              \
+    StepTimer _t((step), st);                       \
     hipError_t _e = (expr);                         \
     if (_e != hipSuccess) return hip_fail(_e, where); \
   } while (0)
@@ -172,9 +238,10 @@ tp_status check_ws(void* ws, size_t have, size_t need) {
   return TP_OK;
 }
 
-GemmDesc gd(int M, int N, int K, const void* A, long lda, bool ak, const void* B, long ldb, bool bk, int epi,
-            void* C, long ldc) {
+GemmDesc gd(int role, int M, int N, int K, const void* A, long lda, bool ak, const void* B, long ldb, bool bk,
+            int epi, void* C, long ldc) {
   GemmDesc g;
+  g.role = role;
   g.M = M; g.N = N; g.K = K;
   g.A = A; g.lda = lda; g.a_kmajor = ak;
   g.B = B; g.ldb = ldb; g.b_kmajor = bk;
@@ -221,11 +288,11 @@ tp_status tp_mlp_fwd(const tp_shape* shape, const void* X, const void* A_i, cons
   const MlpPlan pl = plan_mlp(dm, workspace, false);
   hipStream_t st = (hipStream_t)stream;
   const int dt = dm.dtype;
-  GemmDesc g1 = gd((int)dm.T, (int)dm.fl, (int)dm.h, X, dm.h, true, A_i, dm.fl, false, EPI_BIAS_GELU, pre_i, dm.fl);
+  GemmDesc g1 = gd(GR_FC1, (int)dm.T, (int)dm.fl, (int)dm.h, X, dm.h, true, A_i, dm.fl, false, EPI_BIAS_GELU, pre_i, dm.fl);
   g1.C2 = y_i; g1.ldc2 = dm.fl; g1.bias = b1_i;
-  TP_HIP(gemm_launch(dt, g1, pl.gemm_ws, pl.gemm_bytes, st), "mlp GEMM1 (X A_i + b1_i, GeLU)");
-  GemmDesc g2 = gd((int)dm.T, (int)dm.h, (int)dm.fl, y_i, dm.fl, true, B_i, dm.h, false, EPI_STORE, Z_i, dm.h);
-  TP_HIP(gemm_launch(dt, g2, pl.gemm_ws, pl.gemm_bytes, st), "mlp GEMM2 (y_i B_i)");
+  TP_STEP(TP_STEP_FC1, gemm_launch(dt, g1, pl.gemm_ws, pl.gemm_bytes, st), "mlp GEMM1 (X A_i + b1_i, GeLU)");
+  GemmDesc g2 = gd(GR_FC2, (int)dm.T, (int)dm.h, (int)dm.fl, y_i, dm.fl, true, B_i, dm.h, false, EPI_STORE, Z_i, dm.h);
+  TP_STEP(TP_STEP_FC2, gemm_launch(dt, g2, pl.gemm_ws, pl.gemm_bytes, st), "mlp GEMM2 (y_i B_i)");
   return TP_OK;
 }
 
@@ -253,25 +320,25 @@ tp_status tp_mlp_bwd(const tp_shape* shape, const void* X, const void* A_i, cons
   const int dt = dm.dtype;
   const int T = (int)dm.T, h = (int)dm.h, fl = (int)dm.fl;
   if (T > 0) {
-    GemmDesc g = gd(T, fl, h, dZ, h, true, B_i, h, true, EPI_DGELU, pl.dpre, fl);
+    GemmDesc g = gd(GR_FC2_DGRAD, T, fl, h, dZ, h, true, B_i, h, true, EPI_DGELU, pl.dpre, fl);
     g.aux = pre_i; g.ldaux = fl;
-    TP_HIP(gemm_launch(dt, g, pl.gemm_ws, pl.gemm_bytes, st), "mlp dgrad (dZ B_i^T * GeLU'(pre_i))");
+    TP_STEP(TP_STEP_FC2_DGRAD, gemm_launch(dt, g, pl.gemm_ws, pl.gemm_bytes, st), "mlp dgrad (dZ B_i^T * GeLU'(pre_i))");
   }
   // weight gradients (K = T; T == 0 gives zeros)
-  TP_HIP(gemm_launch(dt, gd(fl, h, T, y_i, fl, false, dZ, h, false, EPI_STORE, dB_i, h), pl.gemm_ws, pl.gemm_bytes, st),
+  TP_STEP(TP_STEP_FC2_WGRAD, gemm_launch(dt, gd(GR_FC2_WGRAD, fl, h, T, y_i, fl, false, dZ, h, false, EPI_STORE, dB_i, h), pl.gemm_ws, pl.gemm_bytes, st),
          "mlp wgrad dB_i = y_i^T dZ");
-  TP_HIP(gemm_launch(dt, gd(h, fl, T, X, h, false, pl.dpre, fl, false, EPI_STORE, dA_i, fl), pl.gemm_ws, pl.gemm_bytes, st),
+  TP_STEP(TP_STEP_FC1_WGRAD, gemm_launch(dt, gd(GR_FC1_WGRAD, h, fl, T, X, h, false, pl.dpre, fl, false, EPI_STORE, dA_i, fl), pl.gemm_ws, pl.gemm_bytes, st),
          "mlp wgrad dA_i = X^T dPre");
-  TP_HIP(colsum_launch(dt, pl.dpre, T, fl, fl, db1_i, (float*)pl.col_ws, st), "mlp db1_i");
+  TP_STEP(TP_STEP_BIAS_GRADS, colsum_launch(dt, pl.dpre, T, fl, fl, db1_i, (float*)pl.col_ws, st), "mlp db1_i");
   if (T > 0)
-    TP_HIP(gemm_launch(dt, gd(T, h, fl, pl.dpre, fl, true, A_i, fl, true, EPI_STORE, dX_i, h), pl.gemm_ws, pl.gemm_bytes, st),
+    TP_STEP(TP_STEP_FC1_DGRAD, gemm_launch(dt, gd(GR_FC1_DGRAD, T, h, fl, pl.dpre, fl, true, A_i, fl, true, EPI_STORE, dX_i, h), pl.gemm_ws, pl.gemm_bytes, st),
            "mlp dgrad dX_i = dPre A_i^T");
-  if (db2_or_null) TP_HIP(colsum_launch(dt, dZ, T, h, h, db2_or_null, (float*)pl.col_ws, st), "mlp db2");
+  if (db2_or_null) TP_STEP(TP_STEP_BIAS_GRADS, colsum_launch(dt, dZ, T, h, h, db2_or_null, (float*)pl.col_ws, st), "mlp db2");
   return TP_OK;
 }
 
 tp_status tp_attn_fwd(const tp_shape* shape, const void* X, const void* Wqkv_i, const void* bqkv_i, const void* Wo_i,
-                      void* qkv_i, void* ctx_i, float* lse_i, void* O_i, void* workspace, size_t workspace_bytes,
+                      float* qkv_i, void* ctx_i, float* lse_i, void* O_i, void* workspace, size_t workspace_bytes,
                       void* stream) {
   Dims dm;
   TP_CHECK(check_shape(shape, dm));
@@ -291,20 +358,20 @@ tp_status tp_attn_fwd(const tp_shape* shape, const void* X, const void* Wqkv_i, 
   hipStream_t st = (hipStream_t)stream;
   const int dt = dm.dtype;
   const int T = (int)dm.T, h = (int)dm.h, hl = (int)dm.hl;
-  GemmDesc g = gd(T, 3 * hl, h, X, h, true, Wqkv_i, 3 * hl, false, EPI_BIAS, qkv_i, 3 * hl);
+  GemmDesc g = gd(GR_QKV_PROJ, T, 3 * hl, h, X, h, true, Wqkv_i, 3 * hl, false, EPI_BIAS_F32, qkv_i, 3 * hl);
   g.bias = bqkv_i;
-  TP_HIP(gemm_launch(dt, g, pl.gemm_ws, pl.gemm_bytes, st), "attn QKV projection");
+  TP_STEP(TP_STEP_QKV_PROJ, gemm_launch(dt, g, pl.gemm_ws, pl.gemm_bytes, st), "attn QKV projection");
   AttnDesc a;
   a.batch = shape->batch; a.seq = shape->seq; a.n_local = (int)dm.nl; a.head_dim = (int)dm.d;
   a.head0 = shape->tp_rank * (int)dm.nl; a.n_heads = shape->n_heads; a.alibi = shape->alibi;
   a.qkv = qkv_i; a.ctx = ctx_i; a.lse = lse_i;
-  TP_HIP(attn_fwd_launch(dt, a, st), "attn forward");
-  TP_HIP(gemm_launch(dt, gd(T, h, hl, ctx_i, hl, true, Wo_i, h, false, EPI_STORE, O_i, h), pl.gemm_ws, pl.gemm_bytes, st),
+  TP_STEP(TP_STEP_ATTN_FWD, attn_fwd_launch(dt, a, st), "attn forward");
+  TP_STEP(TP_STEP_OUT_PROJ, gemm_launch(dt, gd(GR_OUT_PROJ, T, h, hl, ctx_i, hl, true, Wo_i, h, false, EPI_STORE, O_i, h), pl.gemm_ws, pl.gemm_bytes, st),
          "attn output projection");
   return TP_OK;
 }
 
-tp_status tp_attn_bwd(const tp_shape* shape, const void* X, const void* Wqkv_i, const void* Wo_i, const void* qkv_i,
+tp_status tp_attn_bwd(const tp_shape* shape, const void* X, const void* Wqkv_i, const void* Wo_i, const float* qkv_i,
                       const void* ctx_i, const float* lse_i, const void* dO, void* dX_i, void* dWqkv_i, void* dbqkv_i,
                       void* dWo_i, void* dbo_or_null, void* workspace, size_t workspace_bytes, void* stream) {
   Dims dm;
@@ -329,25 +396,25 @@ tp_status tp_attn_bwd(const tp_shape* shape, const void* X, const void* Wqkv_i, 
   const int dt = dm.dtype;
   const int T = (int)dm.T, h = (int)dm.h, hl = (int)dm.hl;
   if (T > 0)
-    TP_HIP(gemm_launch(dt, gd(T, hl, h, dO, h, true, Wo_i, h, true, EPI_STORE, pl.dctx, hl), pl.gemm_ws, pl.gemm_bytes, st),
+    TP_STEP(TP_STEP_OUT_DGRAD, gemm_launch(dt, gd(GR_OUT_DGRAD, T, hl, h, dO, h, true, Wo_i, h, true, EPI_STORE, pl.dctx, hl), pl.gemm_ws, pl.gemm_bytes, st),
            "attn dgrad dC = dO Wo_i^T");
-  TP_HIP(gemm_launch(dt, gd(hl, h, T, ctx_i, hl, false, dO, h, false, EPI_STORE, dWo_i, h), pl.gemm_ws, pl.gemm_bytes, st),
+  TP_STEP(TP_STEP_OUT_WGRAD, gemm_launch(dt, gd(GR_OUT_WGRAD, hl, h, T, ctx_i, hl, false, dO, h, false, EPI_STORE, dWo_i, h), pl.gemm_ws, pl.gemm_bytes, st),
          "attn wgrad dWo_i = ctx_i^T dO");
-  if (dbo_or_null) TP_HIP(colsum_launch(dt, dO, T, h, h, dbo_or_null, (float*)pl.col_ws, st), "attn dbo");
+  if (dbo_or_null) TP_STEP(TP_STEP_BIAS_GRADS, colsum_launch(dt, dO, T, h, h, dbo_or_null, (float*)pl.col_ws, st), "attn dbo");
   if (T > 0) {
     AttnDesc a;
     a.batch = shape->batch; a.seq = shape->seq; a.n_local = (int)dm.nl; a.head_dim = (int)dm.d;
     a.head0 = shape->tp_rank * (int)dm.nl; a.n_heads = shape->n_heads; a.alibi = shape->alibi;
     a.qkv = qkv_i; a.ctx = (void*)ctx_i; a.lse = (float*)lse_i;
     a.dctx = pl.dctx; a.delta = (float*)pl.delta; a.dqkv = pl.dqkv;
-    TP_HIP(attn_bwd_launch(dt, a, st), "attn backward");
+    TP_STEP(TP_STEP_ATTN_BWD, attn_bwd_launch(dt, a, st), "attn backward");
   }
-  TP_HIP(gemm_launch(dt, gd(h, 3 * hl, T, X, h, false, pl.dqkv, 3 * hl, false, EPI_STORE, dWqkv_i, 3 * hl), pl.gemm_ws,
+  TP_STEP(TP_STEP_QKV_WGRAD, gemm_launch(dt, gd(GR_QKV_WGRAD, h, 3 * hl, T, X, h, false, pl.dqkv, 3 * hl, false, EPI_STORE, dWqkv_i, 3 * hl), pl.gemm_ws,
                      pl.gemm_bytes, st),
          "attn wgrad dWqkv_i = X^T dqkv");
-  TP_HIP(colsum_launch(dt, pl.dqkv, T, 3 * hl, 3 * hl, dbqkv_i, (float*)pl.col_ws, st), "attn dbqkv_i");
+  TP_STEP(TP_STEP_BIAS_GRADS, colsum_launch(dt, pl.dqkv, T, 3 * hl, 3 * hl, dbqkv_i, (float*)pl.col_ws, st), "attn dbqkv_i");
   if (T > 0)
-    TP_HIP(gemm_launch(dt, gd(T, h, 3 * hl, pl.dqkv, 3 * hl, true, Wqkv_i, 3 * hl, true, EPI_STORE, dX_i, h), pl.gemm_ws,
+    TP_STEP(TP_STEP_QKV_DGRAD, gemm_launch(dt, gd(GR_QKV_DGRAD, T, h, 3 * hl, pl.dqkv, 3 * hl, true, Wqkv_i, 3 * hl, true, EPI_STORE, dX_i, h), pl.gemm_ws,
                        pl.gemm_bytes, st),
            "attn dgrad dX_i = dqkv Wqkv_i^T");
   return TP_OK;
@@ -366,6 +433,42 @@ tp_status tp_sum_partials(const tp_shape* shape, const void* const* parts, int32
   if (e) return TP_OK;
   TP_HIP(sum_partials_launch(dm.dtype, parts, n_parts, bias_or_null, out, dm.T * dm.h, (int)dm.h, (hipStream_t)stream),
          "sum of partials");
+  return TP_OK;
+}
+
+tp_status tp_profile_enable(uint32_t step_mask) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (const Rec& r : g_prof_recs) g_prof_pool.push_back(r.ev);
+  g_prof_recs.clear();
+  g_prof_mask = step_mask;
+  return TP_OK;
+}
+
+tp_status tp_profile_collect(int32_t step, int32_t* launches, double* total_ms) {
+  if (!launches || !total_ms) return fail(TP_ERR_NULL, "launches / total_ms is NULL");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  int n = 0;
+  double tot = 0.0;
+  std::vector<Rec> keep;
+  for (const Rec& r : g_prof_recs) {
+    if (r.step != step) {
+      keep.push_back(r);
+      continue;
+    }
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.ev.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.ev.a, r.ev.b);
+    if (e != hipSuccess) {
+      g_prof_recs.clear();
+      return hip_fail(e, "tp_profile_collect");
+    }
+    tot += ms;
+    ++n;
+    g_prof_pool.push_back(r.ev);
+  }
+  g_prof_recs.swap(keep);
+  *launches = n;
+  *total_ms = tot;
   return TP_OK;
 }
 

@@ -41,7 +41,7 @@ class LayerShard:
             return t
 
         self.out = {
-            "qkv": buf(T, 3 * hl), "ctx": buf(T, hl), "lse": buf(shape.batch, nl, shape.seq, dtype=torch.float32),
+            "qkv": buf(T, 3 * hl, dtype=torch.float32), "ctx": buf(T, hl), "lse": buf(shape.batch, nl, shape.seq, dtype=torch.float32),
             "O": buf(T, h), "pre": buf(T, fl), "y": buf(T, fl), "Z": buf(T, h),
             "dX_mlp": buf(T, h), "dA": buf(h, fl), "db1": buf(fl), "dB": buf(fl, h),
             "dX_attn": buf(T, h), "dWqkv": buf(h, 3 * hl), "dbqkv": buf(3 * hl), "dWo": buf(hl, h),

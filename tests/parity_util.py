@@ -6,10 +6,16 @@ import torch
 
 import oracle
 
-# Relative Frobenius bound per storage type; the element-wise bound catches a
-# localized error (a wrong tile) that a norm over millions of elements hides.
+# Relative Frobenius bound per storage type (the stated bar); the element-wise
+# bound catches a localized error (a wrong tile errs by ~rms) that a norm over
+# millions of elements hides. Outputs downstream of the softmax get a wider
+# element band: with bf16 storage of qkv, near-tied large scores move the
+# softmax weights by more than the rounding of any one element (sharp rows at
+# the 530B-like shape: score gaps of ~0.1 at |score| ~ 20).
 FRO_TOL = {"fp32": 1e-5, "bf16": 1e-2}
 ELEM_TOL = {"fp32": (2e-5, 1e-5), "bf16": (0.08, 0.02)}  # (x rms(ref), x |ref|)
+ELEM_TOL_SOFTMAX = {"fp32": (2e-5, 1e-5), "bf16": (0.3, 0.05)}
+SOFTMAX_DOWNSTREAM = ("ctx", "lse", "O", "dX_attn", "dWqkv", "dbqkv", "dWo")
 
 
 def f64(t) -> np.ndarray:
@@ -18,7 +24,7 @@ def f64(t) -> np.ndarray:
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def compare(name: str, gpu, ref, dtype: str, report: dict | None = None):
+def compare(name: str, gpu, ref, dtype: str, report: dict | None = None, verbose: bool = True):
     g, r = f64(gpu), f64(ref)
     assert g.shape == r.shape, (name, g.shape, r.shape)
     assert np.all(np.isfinite(g)), f"{name}: non-finite values in the HIP output"
@@ -26,10 +32,14 @@ def compare(name: str, gpu, ref, dtype: str, report: dict | None = None):
     err = np.linalg.norm(g - r) / (nr if nr > 0 else 1.0)
     if report is not None:
         report[name] = err
+    soft = name.split("[")[0].split("(")[-1].rstrip(")") in SOFTMAX_DOWNSTREAM
+    a, b = (ELEM_TOL_SOFTMAX if soft else ELEM_TOL)[dtype]
+    rms = np.sqrt(np.mean(r * r)) if r.size else 0.0
+    worst = float(np.max(np.abs(g - r) / (a * rms + b * np.abs(r) + 1e-300))) if r.size else 0.0
+    if verbose:
+        print(f"    {name:14s} rel_fro {err:.3e} (bar {FRO_TOL[dtype]:.0e})  worst element / band {worst:.3f}", flush=True)
     assert err <= FRO_TOL[dtype], f"{name}: relative Frobenius error {err:.3e} > {FRO_TOL[dtype]:.0e}"
     if r.size:
-        a, b = ELEM_TOL[dtype]
-        rms = np.sqrt(np.mean(r * r))
         bad = np.abs(g - r) > a * rms + b * np.abs(r)
         if np.any(bad):
             idx = np.argwhere(bad)[0]

@@ -21,7 +21,8 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = tp.load_library()
     names = tp.exported_symbols()
     assert set(names) == {"tp_mlp_workspace_bytes", "tp_attn_workspace_bytes", "tp_mlp_fwd", "tp_mlp_bwd",
-                          "tp_attn_fwd", "tp_attn_bwd", "tp_sum_partials", "tp_last_error"}
+                          "tp_attn_fwd", "tp_attn_bwd", "tp_sum_partials", "tp_last_error", "tp_profile_enable",
+                          "tp_profile_collect"}
     for n in names:
         assert isinstance(getattr(lib, n), ctypes._CFuncPtr), n
     out = subprocess.run(["nm", "-D", "--defined-only", tp.library_path()], capture_output=True, text=True).stdout
@@ -104,6 +105,14 @@ def test_every_entry_point_validates():
     with pytest.raises(tp.TPError) as ei:
         tp.tp_attn_bwd(shape(), *([FAKE] * 7), None, FAKE, FAKE, FAKE, workspace=(FAKE, 1 << 40), stream=0)
     assert ei.value.name == "TP_ERR_NULL"
+
+
+def test_profile_mask_without_gpu():
+    # enabling / disabling records nothing by itself; collecting an empty step is a no-op
+    tp.tp_profile_enable(1 << tp.STEPS["fc1"])
+    tp.tp_profile_enable(0)
+    assert tp.tp_profile_collect(tp.STEPS["fc1"]) == (0, 0.0)
+    assert set(tp.STEPS.values()) == set(range(1, 16))
 
 
 def test_empty_batch_needs_no_token_pointers():
