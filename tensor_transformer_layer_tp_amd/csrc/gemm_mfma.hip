@@ -2,18 +2,27 @@
 // with the layer's fused epilogues (bias, bias+GeLU, GeLU' scaling, fp32 out).
 //
 // Tiling: a 256x256 output tile per workgroup of 4 waves (2x2), each wave a
-// 128x128 sub-tile = 4x4 MFMA blocks of 32x32 (256 fp32 accumulators per lane).
-// K advances 64 at a time through two LDS stages (2 x 64 KiB): the next k-slab
-// is fetched into registers while the current one feeds the MFMAs, then written
-// to the other stage, one barrier per k-step.
+// 128x128 sub-tile = 4x4 MFMA blocks of 32x32 (256 fp32 accumulators per lane,
+// held in AGPRs). K advances 64 at a time through two LDS stages (2 x 64 KiB).
 //
-// LDS layout: both operands are kept "k-inner": row r (an m or n index) holds
-// its 64 k-values as eight 16-byte chunks; chunk c is stored at c ^ swz(r),
-// swz(r) = (r ^ (r >> 3)) & 7, so the MFMA fragment reads (32 rows, one chunk)
-// and the transposed writes (rows 8a+i for a run of a) hit distinct banks.
-// Operands that are k-outer in memory (the weight of a forward product, both
-// operands of a weight gradient) are transposed in registers, 8x8 bf16 blocks,
-// on their way to LDS.
+// Global -> LDS: buffer loads that write LDS directly (16 bytes per lane; one
+// instruction fills 1 KiB in lane order), so no VGPRs stage the tiles. Each
+// lane picks the global address whose data belongs at its LDS slot, which is
+// how the swizzles below are applied. Loads of k-step t+1 are issued right
+// after the barrier of step t and complete while step t's MFMAs run.
+//
+// LDS layouts (bf16):
+//  * k-inner operand (memory holds rows with k contiguous: activations of a
+//    forward product, both operands of an input gradient): [256 rows][64 k],
+//    16-byte chunk c of row r stored at c ^ swz(r), swz(r) = (r ^ (r>>3)) & 7;
+//    an MFMA fragment is one ds_read_b128 per lane.
+//  * k-outer operand (memory holds k-rows with the m/n index contiguous: the
+//    weight of a forward product, both operands of a weight gradient): kept in
+//    memory order, [64 k][256 cols], chunk c of k-row q at c ^ 4(q & 3); an
+//    MFMA fragment is two ds_read_b64_tr_b16 per lane (the transposing LDS
+//    read of gfx950: lane 4r+c of each 16-lane group fetches 4 columns of
+//    k-row r, and lane i receives column i of the 4 rows).
+// Both layouts make the fragment reads bank-conflict free.
 //
 // Scheduling: data-parallel tiles, plus stream-K for the last partial wave when
 // whole waves would leave many CUs idle: the leftover tiles' k-iterations are
@@ -65,18 +74,9 @@ __device__ __forceinline__ void tile_coords(const KParams& p, int t, int& tm, in
   tn = r / gm;
 }
 
-// ---- global -> registers (buffer loads, 32-bit offsets) -------------------
-// A tile's operand panel is addressed through a buffer resource whose base is
-// the panel's first row (k-inner) or first column (k-outer); loads whose
-// offset is at or past num_records return zero, which covers ragged M/N edges
-// and the k tail.
-struct Panel {
-  const bf16* base;  // workgroup-uniform
-  uint32_t nrec;     // workgroup-uniform buffer size in bytes
-  uint32_t kstep;    // workgroup-uniform bytes the panel advances per k-step
-  uint32_t voff[8];  // per-thread byte offsets of its 8 loads (nrec = invalid)
-  int kvalid_from;   // k-inner: this thread's k offset inside the slab (8*chunk)
-};
+// ---- global -> LDS (buffer loads writing LDS) ------------------------------
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ const bf16* uni_ptr(const bf16* p) {
@@ -84,141 +84,188 @@ __device__ __forceinline__ const bf16* uni_ptr(const bf16* p) {
   return (const bf16*)(((uint64_t)uni((uint32_t)(v >> 32)) << 32) | uni((uint32_t)v));
 }
 
-// k-inner operand X[r*ld + k], rows r0g.. of `rows`: thread owns chunk (tid&7)
-// of rows (tid>>3)+32i.
-__device__ __forceinline__ Panel panel_kinner(const bf16* X, long ld, int rows, int r0g) {
+// One operand panel of a tile: a buffer resource based at the panel's first
+// row (k-inner) or first column (k-outer), and this lane's byte offsets for its
+// 8 load instructions (nrec = out of range: the load writes zeros).
+struct Panel {
+  const bf16* base;  // workgroup-uniform
+  uint32_t nrec;     // workgroup-uniform buffer size in bytes
+  uint32_t kstep;    // workgroup-uniform bytes the panel advances per k-step
+  uint32_t voff[8];
+};
+
+// k-inner X[r*ld + k], rows r0g.. of `rows`. Instruction i of wave w fills LDS
+// block 8w+i = rows 64w+8i .. +7; lane l lands in row 64w+8i+(l>>3), physical
+// chunk l&7, so it loads logical chunk (l&7) ^ swz(row) = (l&7) ^ (l>>3) ^ i.
+__device__ __forceinline__ Panel panel_kinner(const bf16* X, long ld, int rows, int r0g, int wave, int lane) {
   Panel pn;
-  const int tid = threadIdx.x, c = tid & 7, rr = tid >> 3;
   int nrows = rows - r0g;
   nrows = nrows < 256 ? nrows : 256;
   pn.base = uni_ptr(X + (long)r0g * ld);
   pn.nrec = uni((uint32_t)((long)nrows * ld * 2));
+  pn.kstep = BKK * 2;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    int r = rr + 32 * i;
+    const int r = 64 * wave + 8 * i + (lane >> 3);
+    const int c = (lane & 7) ^ (lane >> 3) ^ i;
     pn.voff[i] = r < nrows ? (uint32_t)(((long)r * ld + 8 * c) * 2) : pn.nrec;
   }
-  pn.kstep = BKK * 2;
-  pn.kvalid_from = 8 * c;
   return pn;
 }
-// k-outer operand X[k*ld + r]: thread owns the 8x8 block (k-block tid>>5, r-block tid&31).
-__device__ __forceinline__ Panel panel_kouter(const bf16* X, long ld, int rows, int K, int r0g) {
+// k-outer X[k*ld + r], columns r0g.. of `rows`. Instruction i of wave w fills
+// LDS block 8w+i = k-rows 16w+2i, +1; lane l lands in k-row 16w+2i+(l>>5),
+// physical chunk l&31, so it loads logical chunk (l&31) ^ 4(krow&3). Rows at
+// or past K fall beyond nrec and load zeros.
+__device__ __forceinline__ Panel panel_kouter(const bf16* X, long ld, int rows, int K, int r0g, int wave,
+                                              int lane) {
   Panel pn;
-  const int tid = threadIdx.x, kb = tid >> 5, rb = tid & 31;
   pn.base = uni_ptr(X + r0g);
   pn.nrec = uni((uint32_t)(((long)K * ld - r0g) * 2));
-  const bool colok = r0g + 8 * rb < rows;
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    pn.voff[j] = colok ? (uint32_t)(((long)(8 * kb + j) * ld + 8 * rb) * 2) : pn.nrec;
   pn.kstep = uni((uint32_t)(BKK * ld * 2));
-  pn.kvalid_from = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int kr = 16 * wave + 2 * i + (lane >> 5);
+    const int c = (lane & 31) ^ (4 * (kr & 3));
+    pn.voff[i] = (r0g + 8 * c < rows) ? (uint32_t)(((long)kr * ld + 8 * c) * 2) : pn.nrec;
+  }
   return pn;
 }
 
+// Issue the 8 loads of one operand for k-step kt into LDS stage `dst`.
 template <bool KIN>
-__device__ __forceinline__ void load_panel(const Panel& pn, int kt, int K, u32x4 (&reg)[8]) {
+__device__ __forceinline__ void issue_panel(const Panel& pn, int kt, int K, bf16* dst, int wave, int lane) {
   const int soff = (int)uni((uint32_t)kt * pn.kstep);
   __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)pn.base, (short)0, (int)pn.nrec, 0x00020000);
-  if (KIN) {
-    const bool kok = kt * BKK + pn.kvalid_from < K;
+  // k tail (k-inner only): chunks at or past K must read zeros, not the next row
+  const bool tail = KIN && (kt + 1) * BKK > K;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) reg[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, kok ? pn.voff[i] : pn.nrec, soff, 0);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) reg[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, pn.voff[i], soff, 0);
+  for (int i = 0; i < 8; ++i) {
+    uint32_t vo = pn.voff[i];
+    if (tail) {
+      const int c = (lane & 7) ^ (lane >> 3) ^ i;
+      if (kt * BKK + 8 * c >= K) vo = pn.nrec;
+    }
+    bf16* blk = dst + (8 * wave + i) * 512;  // 1 KiB block, wave-uniform
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)blk, 16, vo, soff, 0, 0);
   }
 }
 
-// ---- registers -> LDS ----------------------------------------------------
-// k-inner: row r = rr + 32i, swz(r) = (rr&7) ^ (rr>>3) ^ 4(i&1).
-__device__ __forceinline__ void store_kinner(bf16* s, const u32x4 (&reg)[8]) {
-  const int tid = threadIdx.x;
-  const int c = tid & 7, rr = tid >> 3;
-  const int s0 = (rr & 7) ^ (rr >> 3);
-  bf16* b0 = s + rr * BKK + ((c ^ s0) << 3);
-  bf16* b1 = s + rr * BKK + ((c ^ s0 ^ 4) << 3);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) *(u32x4*)(((i & 1) ? b1 : b0) + i * 32 * BKK) = reg[i];
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ---- fragment reads ------------------------------------------------------------
+// k-inner: 32-row block i of this wave's 128 rows; lane owns row base+32i+(l&31)
+// and k = 16kk + 8(l>>5) .. +7.
+__device__ __forceinline__ bf16x8 frag_kin(const bf16* s, int rowbase, int s1, int g, int kk, int i) {
+  const int e = (2 * kk) ^ g ^ s1 ^ (4 * (i & 1));
+  return *(const bf16x8*)(s + rowbase + i * 32 * BKK + (e << 3));
 }
-// k-outer: transpose the 8x8 block in registers. reg[j] is k-row j holding
-// r = 8rb+0..7 as 4 dwords; output row r = 8rb+i takes element i of each reg[j].
-__device__ __forceinline__ void store_kouter(bf16* s, const u32x4 (&reg)[8]) {
-  const int tid = threadIdx.x;
-  const int kb = tid >> 5, rb = tid & 31;
-  const int t = kb ^ (rb & 7);
-  bf16* base = s + rb * 8 * BKK;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int d = i >> 1;
-    u32x4 o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t lo = reg[2 * q][d], hi = reg[2 * q + 1][d];
-      o[q] = (i & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-    }
-    *(u32x4*)(base + i * BKK + ((t ^ i) << 3)) = o;
-  }
+// k-outer: per-lane byte offset of 32-column block jb inside a stage (see the
+// layout note): k-row 8v + (j>>2) (+16kk + 4t), chunk ((col>>3) ^ 4(j>>2)),
+// half (j&1); j = l&15, h = (l>>4)&1, v = l>>5, col = base + 32jb + 16h + 4(j&3).
+__device__ __forceinline__ int kout_lane_off(int colbase, int jb, int lane) {
+  const int j = lane & 15, h = (lane >> 4) & 1, v = lane >> 5;
+  const int col = colbase + 32 * jb + 16 * h + 4 * (j & 3);
+  const int chunk = (col >> 3) ^ (4 * (j >> 2));
+  return (8 * v + (j >> 2)) * 512 + chunk * 16 + 8 * (j & 1);
 }
-template <bool KIN>
-__device__ __forceinline__ void store_op(bf16* s, const u32x4 (&reg)[8]) {
-  if (KIN) store_kinner(s, reg);
-  else store_kouter(s, reg);
+__device__ __forceinline__ bf16x8 frag_kout(const bf16* s, int lane_off, int kk) {
+  const char* b = (const char*)s + lane_off + kk * 16 * 512;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(b));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(b + 4 * 512));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 // ---- main loop over k-iterations [kb, ke) of one tile -------------------------
+// One k-step: wait for this wave's loads into the current stage, barrier (all
+// loads landed; everyone finished reading the other stage), issue the next
+// k-step's loads into the other stage, then 4 x 16 MFMAs from the current
+// stage with the next sub-step's fragments read ahead. The stage pointers are
+// __restrict__: the two stages never overlap, and the no-alias information
+// lets the compiler's wait-count pass leave the in-flight LDS writes (other
+// stage) outstanding while the fragment reads (this stage) proceed.
+template <bool AK, bool BKM>
+__device__ __forceinline__ void kstep(const KParams& p, const Panel& pa, const Panel& pb, int kt, int ke,
+                                      const bf16* __restrict__ a, const bf16* __restrict__ b,
+                                      bf16* __restrict__ na, bf16* __restrict__ nb, int wave, int lane,
+                                      int rowA, int rowB, const int (&offA)[4], const int (&offB)[4], int s1, int g,
+                                      f32x16 (&acc)[4][4]) {
+  wait_vmem();
+  __syncthreads();
+  // Next k-step's loads, unconditionally so that the whole step is one
+  // scheduling region: past the last k-step of the tile they read either zeros
+  // (k beyond K is out of the buffer's range) or in-range data nobody uses.
+  issue_panel<AK>(pa, kt + 1, p.K, na, wave, lane);
+  issue_panel<BKM>(pb, kt + 1, p.K, nb, wave, lane);
+  bf16x8 af[2][4], bfg[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    af[0][i] = AK ? frag_kin(a, rowA, s1, g, 0, i) : frag_kout(a, offA[i], 0);
+    bfg[0][i] = BKM ? frag_kin(b, rowB, s1, g, 0, i) : frag_kout(b, offB[i], 0);
+  }
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int c = kk & 1, n = c ^ 1;
+    if (kk < 3) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        af[n][i] = AK ? frag_kin(a, rowA, s1, g, kk + 1, i) : frag_kout(a, offA[i], kk + 1);
+        bfg[n][i] = BKM ? frag_kin(b, rowB, s1, g, kk + 1, i) : frag_kout(b, offB[i], kk + 1);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        // operands swapped: D[n][m], so each lane ends up owning one m and
+        // runs of 4 consecutive n (vector stores in the epilogue)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[c][j], af[c][i], acc[i][j], 0, 0, 0);
+  }
+  // Instruction order for the step: the first sub-step's fragment reads, then
+  // each MFMA followed by one read of the next sub-step's fragments and (in
+  // the first sub-step) one of the 16 loads of the next k-step.
+  constexpr int R = (AK ? 4 : 8) + (BKM ? 4 : 8);  // LDS reads per sub-step
+  __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (kk < 3 && m < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (kk == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+}
+
 template <bool AK, bool BKM>
 __device__ __forceinline__ void mainloop(const KParams& p, int tm, int tn, int kb, int ke,
-                                         f32x16 (&acc)[4][4], bf16* sA, bf16* sB) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+                                         f32x16 (&acc)[4][4], bf16* sA0, bf16* sA1, bf16* sB0, bf16* sB1) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = (int)uni((uint32_t)(tid >> 6));
   const int wm = wave >> 1, wn = wave & 1;
   const int g = lane >> 5, l32 = lane & 31;
   const int s1 = (l32 & 7) ^ (l32 >> 3);
-  const bf16* fa = sA + (wm * 128 + l32) * BKK;
-  const bf16* fb = sB + (wn * 128 + l32) * BKK;
   Panel pa, pb;
-  if (AK) pa = panel_kinner(p.A, p.lda, p.M, tm * BM);
-  else pa = panel_kouter(p.A, p.lda, p.M, p.K, tm * BM);
-  if (BKM) pb = panel_kinner(p.B, p.ldb, p.N, tn * BN);
-  else pb = panel_kouter(p.B, p.ldb, p.N, p.K, tn * BN);
-  u32x4 ra[8], rb[8];
-  load_panel<AK>(pa, kb, p.K, ra);
-  load_panel<BKM>(pb, kb, p.K, rb);
-  store_op<AK>(sA, ra);
-  store_op<BKM>(sB, rb);
-  __syncthreads();
-  for (int kt = kb; kt < ke; ++kt) {
-    const int cur = (kt - kb) & 1;
-    const bool more = kt + 1 < ke;
-    if (more) {
-      load_panel<AK>(pa, kt + 1, p.K, ra);
-      load_panel<BKM>(pb, kt + 1, p.K, rb);
-    }
-    const bf16* a = fa + cur * STAGE;
-    const bf16* b = fb + cur * STAGE;
+  if (AK) pa = panel_kinner(p.A, p.lda, p.M, tm * BM, wave, lane);
+  else pa = panel_kouter(p.A, p.lda, p.M, p.K, tm * BM, wave, lane);
+  if (BKM) pb = panel_kinner(p.B, p.ldb, p.N, tn * BN, wave, lane);
+  else pb = panel_kouter(p.B, p.ldb, p.N, p.K, tn * BN, wave, lane);
+  const int rowA = (wm * 128 + l32) * BKK, rowB = (wn * 128 + l32) * BKK;
+  int offA[4], offB[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int e = (2 * kk) ^ g ^ s1;
-      bf16x8 af[4], bfg[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)(a + i * 32 * BKK + ((e ^ (4 * (i & 1))) << 3));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bfg[j] = *(const bf16x8*)(b + j * 32 * BKK + ((e ^ (4 * (j & 1))) << 3));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          // operands swapped: D[n][m], so each lane ends up owning one m and
-          // runs of 4 consecutive n (vector stores in the epilogue)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[j], af[i], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      store_op<AK>(sA + (cur ^ 1) * STAGE, ra);
-      store_op<BKM>(sB + (cur ^ 1) * STAGE, rb);
-    }
-    __syncthreads();
+  for (int j = 0; j < 4; ++j) {
+    offA[j] = AK ? 0 : kout_lane_off(wm * 128, j, lane);
+    offB[j] = BKM ? 0 : kout_lane_off(wn * 128, j, lane);
   }
+  issue_panel<AK>(pa, kb, p.K, sA0, wave, lane);
+  issue_panel<BKM>(pb, kb, p.K, sB0, wave, lane);
+  for (int kt = kb; kt < ke; ++kt) {
+    const bool odd = (kt - kb) & 1;
+    kstep<AK, BKM>(p, pa, pb, kt, ke, odd ? sA1 : sA0, odd ? sB1 : sB0, odd ? sA0 : sA1, odd ? sB0 : sB1, wave,
+                   lane, rowA, rowB, offA, offB, s1, g, acc);
+  }
+  wait_vmem();      // the last step's read-ahead loads have landed
+  __syncthreads();  // LDS is reused by the next work item
 }
 
 // ---- epilogue ---------------------------------------------------------------
@@ -301,7 +348,7 @@ __device__ __forceinline__ void store_partial(float* slot, const f32x16 (&acc)[4
 // then its run of stream-K iterations (whole tiles in the run are stored
 // directly, partial tiles go to the workspace).
 template <bool AK, bool BKM, int EPI>
-__device__ __forceinline__ void gemm_body(const KParams& p, bf16* sA, bf16* sB) {
+__device__ __forceinline__ void gemm_body(const KParams& p, bf16* sA0, bf16* sA1, bf16* sB0, bf16* sB1) {
   const int lw = logical_wg(blockIdx.x, p.grid);
   const bool in_sk = p.sk_total > 0 && lw < p.sk_grid;
   long long base = 0, rem = 0, s = 0, e = 0;
@@ -336,7 +383,7 @@ __device__ __forceinline__ void gemm_body(const KParams& p, bf16* sA, bf16* sB) 
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-    mainloop<AK, BKM>(p, tm, tn, kb, ke, acc, sA, sB);
+    mainloop<AK, BKM>(p, tm, tn, kb, ke, acc, sA0, sA1, sB0, sB1);
     if (kb == 0 && ke == p.iters) {
       epilogue<EPI>(p, tm, tn, acc);
     } else {
@@ -391,9 +438,11 @@ __device__ __forceinline__ void fixup_body(const KParams& p, int first_tile) {
 #define TP_GEMM_KERNELS(NAME, AKV, BKV, EV)                                           \
   __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))     \
   void NAME(KParams p) {                                                            \
-    __shared__ __attribute__((aligned(16))) bf16 sA[2 * STAGE];                     \
-    __shared__ __attribute__((aligned(16))) bf16 sB[2 * STAGE];                     \
-    gemm_body<AKV, BKV, EV>(p, sA, sB);                                             \
+    __shared__ __attribute__((aligned(16))) bf16 sA0[STAGE];                        \
+    __shared__ __attribute__((aligned(16))) bf16 sA1[STAGE];                        \
+    __shared__ __attribute__((aligned(16))) bf16 sB0[STAGE];                        \
+    __shared__ __attribute__((aligned(16))) bf16 sB1[STAGE];                        \
+    gemm_body<AKV, BKV, EV>(p, sA0, sA1, sB0, sB1);                                 \
   }                                                                                 \
   __global__ __launch_bounds__(NTHR) void NAME##_fixup(KParams p, int first_tile) { \
     fixup_body<EV>(p, first_tile);                                                  \
