@@ -143,6 +143,8 @@ def main():
     ap.add_argument("--workload", default="mtnlg_530b_tp8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-target-s", type=float, default=15.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run device-to-device copies of this many MiB (calibrates byte counters)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {a.gpus} requested): this build runs one tensor-parallel "
@@ -150,6 +152,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if a.copy_probe_mib:
+        n = a.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {n} bytes x5")
+        return
 
     import synth
     import tensor_transformer_layer_tp_amd as tp

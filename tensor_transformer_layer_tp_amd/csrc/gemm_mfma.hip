@@ -92,6 +92,7 @@ struct Panel {
   uint32_t nrec;     // workgroup-uniform buffer size in bytes
   uint32_t kstep;    // workgroup-uniform bytes the panel advances per k-step
   uint32_t voff[8];
+  int prow;          // k-inner: valid rows of the panel (L2 prefetch)
 };
 
 // k-inner X[r*ld + k], rows r0g.. of `rows`. Instruction i of wave w fills LDS
@@ -104,6 +105,7 @@ __device__ __forceinline__ Panel panel_kinner(const bf16* X, long ld, int rows, 
   pn.base = uni_ptr(X + (long)r0g * ld);
   pn.nrec = uni((uint32_t)((long)nrows * ld * 2));
   pn.kstep = BKK * 2;
+  pn.prow = nrows;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = 64 * wave + 8 * i + (lane >> 3);
@@ -122,6 +124,7 @@ __device__ __forceinline__ Panel panel_kouter(const bf16* X, long ld, int rows, 
   pn.base = uni_ptr(X + r0g);
   pn.nrec = uni((uint32_t)(((long)K * ld - r0g) * 2));
   pn.kstep = uni((uint32_t)(BKK * ld * 2));
+  pn.prow = 256;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int kr = 16 * wave + 2 * i + (lane >> 5);
@@ -151,6 +154,32 @@ __device__ __forceinline__ void issue_panel(const Panel& pn, int kt, int K, bf16
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+#ifndef TP_GEMM_PF_DIST
+#define TP_GEMM_PF_DIST 0
+#endif
+// L2 prefetch distance in k-steps (0: off).
+constexpr int PF_DIST = TP_GEMM_PF_DIST;
+// All but the most recent loads (this wave's L2 prefetches, if any) have landed.
+__device__ __forceinline__ void wait_vmem_but_prefetch() {
+  if (PF_DIST > 0) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// L2 prefetch of k-step kt of a panel, PF_DIST steps ahead of its LDS loads:
+// every thread touches one 128-byte line (k-inner: row tid; k-outer: k-row
+// tid/4, quarter tid%4) with a 4-byte load into a scratch LDS word, so no
+// VGPR is written. Past the tile's last k-step it reads nothing (offset nrec).
+template <bool KIN>
+__device__ __forceinline__ void prefetch_panel(const Panel& pn, int kt, int ke, long ld, int* __restrict__ scratch,
+                                               int tid) {
+  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)pn.base, (short)0, (int)pn.nrec, 0x00020000);
+  const int soff = (int)uni((uint32_t)kt * pn.kstep);
+  uint32_t vo;
+  if (KIN) vo = tid < pn.prow ? (uint32_t)((long)tid * ld * 2) : pn.nrec;
+  else vo = (uint32_t)(((long)(tid >> 2) * ld + 64 * (tid & 3)) * 2);
+  if (kt >= ke) vo = pn.nrec;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)scratch, 4, vo, soff, 0, 0);
+}
 
 // ---- fragment reads ------------------------------------------------------------
 // k-inner: 32-row block i of this wave's 128 rows; lane owns row base+32i+(l&31)
@@ -190,8 +219,8 @@ __device__ __forceinline__ void kstep(const KParams& p, const Panel& pa, const P
                                       const bf16* __restrict__ a, const bf16* __restrict__ b,
                                       bf16* __restrict__ na, bf16* __restrict__ nb, int wave, int lane,
                                       int rowA, int rowB, const int (&offA)[4], const int (&offB)[4], int s1, int g,
-                                      f32x16 (&acc)[4][4]) {
-  wait_vmem();
+                                      f32x16 (&acc)[4][4], int* __restrict__ pfs) {
+  wait_vmem_but_prefetch();
   __syncthreads();
   // Next k-step's loads, unconditionally so that the whole step is one
   // scheduling region: past the last k-step of the tile they read either zeros
@@ -235,11 +264,19 @@ __device__ __forceinline__ void kstep(const KParams& p, const Panel& pa, const P
       if (kk < 3 && m < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       if (kk == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
+  // The L2 prefetches go last, after a scheduling fence, so that they are the
+  // two youngest loads when the next step waits for this step's LDS loads.
+  if (PF_DIST > 0) {
+    __builtin_amdgcn_sched_barrier(0);
+    prefetch_panel<AK>(pa, kt + PF_DIST, ke, p.lda, pfs, threadIdx.x);
+    prefetch_panel<BKM>(pb, kt + PF_DIST, ke, p.ldb, pfs, threadIdx.x);
+  }
 }
 
 template <bool AK, bool BKM>
 __device__ __forceinline__ void mainloop(const KParams& p, int tm, int tn, int kb, int ke,
-                                         f32x16 (&acc)[4][4], bf16* sA0, bf16* sA1, bf16* sB0, bf16* sB1) {
+                                         f32x16 (&acc)[4][4], bf16* sA0, bf16* sA1, bf16* sB0, bf16* sB1,
+                                         int* pfs) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = (int)uni((uint32_t)(tid >> 6));
   const int wm = wave >> 1, wn = wave & 1;
@@ -259,10 +296,17 @@ __device__ __forceinline__ void mainloop(const KParams& p, int tm, int tn, int k
   }
   issue_panel<AK>(pa, kb, p.K, sA0, wave, lane);
   issue_panel<BKM>(pb, kb, p.K, sB0, wave, lane);
+  // steps kb+1 .. kb+PF_DIST-1 are prefetched here, the rest one per step; the
+  // last two loads issued are always prefetches (see wait_vmem_but_prefetch)
+#pragma unroll
+  for (int d = 1; d < PF_DIST; ++d) {
+    prefetch_panel<AK>(pa, kb + d, ke, p.lda, pfs, tid);
+    prefetch_panel<BKM>(pb, kb + d, ke, p.ldb, pfs, tid);
+  }
   for (int kt = kb; kt < ke; ++kt) {
     const bool odd = (kt - kb) & 1;
     kstep<AK, BKM>(p, pa, pb, kt, ke, odd ? sA1 : sA0, odd ? sB1 : sB0, odd ? sA0 : sA1, odd ? sB0 : sB1, wave,
-                   lane, rowA, rowB, offA, offB, s1, g, acc);
+                   lane, rowA, rowB, offA, offB, s1, g, acc, pfs);
   }
   wait_vmem();      // the last step's read-ahead loads have landed
   __syncthreads();  // LDS is reused by the next work item
@@ -276,21 +320,21 @@ __device__ __forceinline__ void store_bf16x4(bf16* dst, const float (&v)[4]) {
   *(bf16x4*)dst = o;
 }
 
+// Row block i (rows 32i..32i+31 of each wave's 128) of a tile.
 template <int EPI>
-__device__ __forceinline__ void epilogue(const KParams& p, int tm, int tn, const f32x16 (&acc)[4][4]) {
+__device__ __forceinline__ void epilogue_rows(const KParams& p, int tm, int tn, int i, const f32x16 (&acc)[4]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  {
     const int m = tm * BM + wm * 128 + i * 32 + (lane & 31);
-    if (m >= p.M) continue;
+    if (m >= p.M) return;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int n = tn * BN + wn * 128 + j * 32 + q4 * 8 + (lane >> 5) * 4;
         if (n >= p.N) continue;
-        float v[4] = {acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]};
+        float v[4] = {acc[j][4 * q4], acc[j][4 * q4 + 1], acc[j][4 * q4 + 2], acc[j][4 * q4 + 3]};
         if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_F32) {
           bf16x4 bb = *(const bf16x4*)(p.bias + n);
 #pragma unroll
@@ -315,6 +359,12 @@ __device__ __forceinline__ void epilogue(const KParams& p, int tm, int tn, const
       }
     }
   }
+}
+
+template <int EPI>
+__device__ __forceinline__ void epilogue(const KParams& p, int tm, int tn, const f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) epilogue_rows<EPI>(p, tm, tn, i, acc[i]);
 }
 
 // ---- stream-K bookkeeping -----------------------------------------------------
@@ -348,7 +398,7 @@ __device__ __forceinline__ void store_partial(float* slot, const f32x16 (&acc)[4
 // then its run of stream-K iterations (whole tiles in the run are stored
 // directly, partial tiles go to the workspace).
 template <bool AK, bool BKM, int EPI>
-__device__ __forceinline__ void gemm_body(const KParams& p, bf16* sA0, bf16* sA1, bf16* sB0, bf16* sB1) {
+__device__ __forceinline__ void gemm_body(const KParams& p, bf16* sA0, bf16* sA1, bf16* sB0, bf16* sB1, int* pfs) {
   const int lw = logical_wg(blockIdx.x, p.grid);
   const bool in_sk = p.sk_total > 0 && lw < p.sk_grid;
   long long base = 0, rem = 0, s = 0, e = 0;
@@ -383,7 +433,7 @@ __device__ __forceinline__ void gemm_body(const KParams& p, bf16* sA0, bf16* sA1
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-    mainloop<AK, BKM>(p, tm, tn, kb, ke, acc, sA0, sA1, sB0, sB1);
+    mainloop<AK, BKM>(p, tm, tn, kb, ke, acc, sA0, sA1, sB0, sB1, pfs);
     if (kb == 0 && ke == p.iters) {
       epilogue<EPI>(p, tm, tn, acc);
     } else {
@@ -394,41 +444,38 @@ __device__ __forceinline__ void gemm_body(const KParams& p, bf16* sA0, bf16* sA1
   }
 }
 
-// One workgroup per stream-K tile: sum the contributors' partials in
-// contributor order and apply the epilogue.
+// Stream-K fix-up: sum each split tile's partials in contributor order and
+// apply the epilogue.
 template <int EPI>
 __device__ __forceinline__ void fixup_body(const KParams& p, int first_tile) {
-  const int t = first_tile + blockIdx.x;
+  // four workgroups per tile, one per row block i of the waves' sub-tiles
+  const int t = first_tile + blockIdx.x / 4, i = blockIdx.x % 4;
   const long long base = p.sk_total / p.sk_grid, rem = p.sk_total % p.sk_grid;
   const long long t0 = (long long)t * p.iters - p.sk_begin;
   const long long c0 = sk_owner(t0, base, rem), c1 = sk_owner(t0 + p.iters - 1, base, rem);
   if (c0 == c1) return;  // one workgroup covered the whole tile and stored it
   const int tid = threadIdx.x;
-  f32x16 acc[4][4];
+  f32x16 acc[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  for (int j = 0; j < 4; ++j) acc[j] = f32x16{};
   for (long long c = c0; c <= c1; ++c) {
     const int slot = (int)(2 * c + (sk_start(c, base, rem) >= t0 ? 0 : 1));
     const float* src = p.partials + (long)slot * BM * BN;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int f4 = (i * 4 + j) * 4 + q4;
-          f32x4 v = *(const f32x4*)(src + ((long)f4 * NTHR + tid) * 4);
-          acc[i][j][4 * q4] += v[0];
-          acc[i][j][4 * q4 + 1] += v[1];
-          acc[i][j][4 * q4 + 2] += v[2];
-          acc[i][j][4 * q4 + 3] += v[3];
-        }
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int f4 = (i * 4 + j) * 4 + q4;
+        f32x4 v = *(const f32x4*)(src + ((long)f4 * NTHR + tid) * 4);
+        acc[j][4 * q4] += v[0];
+        acc[j][4 * q4 + 1] += v[1];
+        acc[j][4 * q4 + 2] += v[2];
+        acc[j][4 * q4 + 3] += v[3];
+      }
   }
   int tm, tn;
   tile_coords(p, t, tm, tn);
-  epilogue<EPI>(p, tm, tn, acc);
+  epilogue_rows<EPI>(p, tm, tn, i, acc);
 }
 
 }  // namespace
@@ -442,7 +489,8 @@ __device__ __forceinline__ void fixup_body(const KParams& p, int first_tile) {
     __shared__ __attribute__((aligned(16))) bf16 sA1[STAGE];                        \
     __shared__ __attribute__((aligned(16))) bf16 sB0[STAGE];                        \
     __shared__ __attribute__((aligned(16))) bf16 sB1[STAGE];                        \
-    gemm_body<AKV, BKV, EV>(p, sA0, sA1, sB0, sB1);                                 \
+    __shared__ __attribute__((aligned(16))) int pfs[64];                            \
+    gemm_body<AKV, BKV, EV>(p, sA0, sA1, sB0, sB1, pfs);                            \
   }                                                                                 \
   __global__ __launch_bounds__(NTHR) void NAME##_fixup(KParams p, int first_tile) { \
     fixup_body<EV>(p, first_tile);                                                  \
@@ -568,7 +616,7 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
   hipLaunchKernelGGL(mk, grid, block, 0, stream, p);
   hipError_t e1 = hipGetLastError();
   if (e1 != hipSuccess || !sk) return e1;
-  hipLaunchKernelGGL(fk, dim3(nsk), block, 0, stream, p, first);
+  hipLaunchKernelGGL(fk, dim3(4 * nsk), block, 0, stream, p, first);
   return hipGetLastError();
 }
 
