@@ -2,6 +2,8 @@
 
     python -m tensor_transformer_layer_tp_amd.profsum stats  <dir>            # per-kernel durations
     python -m tensor_transformer_layer_tp_amd.profsum counters <dir> [filter] # per-kernel counter means
+    python -m tensor_transformer_layer_tp_amd.profsum traffic <fetch_dir> <write_dir> \
+        <copy_fetch_dir> <copy_write_dir> <copy_bytes> <kernel>                # HBM bytes per launch
 
 <dir> is a rocprofv3 output directory written with --output-format csv. The
 counter summary averages every counter over the dispatches of each kernel
@@ -26,8 +28,8 @@ def _rows(d: str, suffix: str):
 
 
 def short(name: str) -> str:
-    n = name.split("(")[0]
-    return n.replace("tpk::", "").replace("(anonymous namespace)::", "").replace("void ", "")
+    n = name.replace("void ", "").replace("(anonymous namespace)::", "").replace("tpk::", "")
+    return n.split("(")[0]
 
 
 def stats(d: str) -> str:
@@ -53,6 +55,41 @@ def counters(d: str, filt: str = "") -> str:
     return "\n".join(out)
 
 
+def _mean(d: str, counter: str, kernel: str) -> float:
+    v = [float(r["Counter_Value"]) for r in _rows(d, "counter_collection.csv")
+         if r["Counter_Name"] == counter and short(r["Kernel_Name"]) == kernel]
+    if not v:
+        raise SystemExit(f"no {counter} rows for {kernel} under {d}")
+    return sum(v) / len(v)
+
+
+def traffic(fetch_dir: str, write_dir: str, copyf_dir: str, copyw_dir: str, copy_bytes: int, kernel: str) -> str:
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of `kernel`, each scaled by
+    the factor that makes a device copy of copy_bytes read and write exactly
+    copy_bytes."""
+    cf = copy_bytes / (_mean(copyf_dir, "FETCH_SIZE", "__amd_rocclr_copyBuffer") * 1024)
+    cw = copy_bytes / (_mean(copyw_dir, "WRITE_SIZE", "__amd_rocclr_copyBuffer") * 1024)
+    f = _mean(fetch_dir, "FETCH_SIZE", kernel) * 1024 * cf
+    w = _mean(write_dir, "WRITE_SIZE", kernel) * 1024 * cw
+    here = os.path.dirname(os.path.abspath(__file__))
+    sys.path.insert(0, os.path.dirname(here))
+    import bench  # noqa: E402  (source hash of the GEMM kernels)
+    return "\n".join([
+        f"calibration: copy of {copy_bytes} bytes -> FETCH_SIZE x {cf:.4f}, WRITE_SIZE x {cw:.4f}",
+        f"fetch_bytes_per_launch = {f:.6e}",
+        f"write_bytes_per_launch = {w:.6e}",
+        f"traffic_bytes_per_launch = {f + w:.6e}",
+        f"source_sha256_16 = {bench.gemm_source_hash()}",
+    ])
+
+
 if __name__ == "__main__":
     mode, d = sys.argv[1], sys.argv[2]
-    print(stats(d) if mode == "stats" else counters(d, sys.argv[3] if len(sys.argv) > 3 else ""))
+    if mode == "stats":
+        print(stats(d))
+    elif mode == "counters":
+        print(counters(d, sys.argv[3] if len(sys.argv) > 3 else ""))
+    elif mode == "traffic":
+        print(traffic(d, sys.argv[3], sys.argv[4], sys.argv[5], int(sys.argv[6]), sys.argv[7]))
+    else:
+        raise SystemExit(f"unknown mode {mode}")
