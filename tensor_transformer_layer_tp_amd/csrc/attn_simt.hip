@@ -200,20 +200,45 @@ __global__ __launch_bounds__(NT) void dkdv_kernel(SP p) {
 }
 
 // delta[b][l][i] = sum_dd dctx[t][l*d+dd] * ctx[t][l*d+dd], t = b*seq + i.
+// delta[b][l][i] = sum_d dctx[t][l*D + d] * ctx[t][l*D + d], t = b*seq + i.
+// One 32-lane half-wave per (token, head) row: lane c reads 8 adjacent
+// elements (16-byte loads of both tensors), then a fixed butterfly of
+// shuffles sums the D/8 (<= 32) lane products.
 template <typename T>
 __global__ __launch_bounds__(256) void delta_kernel(const T* dctx, const T* ctx, float* delta, int batch,
                                                     int seq, int n_local, int d, int h_l) {
-  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  const long row = ((long)blockIdx.x * 256 + threadIdx.x) >> 5;
   const long total = (long)batch * seq * n_local;
-  if (idx >= total) return;
-  const int l = (int)(idx % n_local);
-  const long t = idx / n_local;
-  const int b = (int)(t / seq), i = (int)(t % seq);
-  const T* x = dctx + t * h_l + (long)l * d;
-  const T* y = ctx + t * h_l + (long)l * d;
+  const int c = threadIdx.x & 31;
   float s = 0.f;
-  for (int dd = 0; dd < d; ++dd) s = fmaf(to_f(x[dd]), to_f(y[dd]), s);
-  delta[((long)b * n_local + l) * seq + i] = s;
+  int l = 0;
+  long t = 0;
+  if (row < total) {
+    l = (int)(row % n_local);
+    t = row / n_local;
+    if (8 * c < d) {
+      const T* x = dctx + t * h_l + (long)l * d + 8 * c;
+      const T* y = ctx + t * h_l + (long)l * d + 8 * c;
+      if constexpr (sizeof(T) == 2) {
+        const bf16x8 a = *(const bf16x8*)x, b = *(const bf16x8*)y;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s = fmaf((float)a[e], (float)b[e], s);
+      } else {
+        const f32x4 a0 = *(const f32x4*)x, a1 = *(const f32x4*)(x + 4);
+        const f32x4 b0 = *(const f32x4*)y, b1 = *(const f32x4*)(y + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s = fmaf(a0[e], b0[e], s);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s = fmaf(a1[e], b1[e], s);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) s += __shfl_xor(s, off, 32);
+  if (row < total && c == 0) {
+    const int b = (int)(t / seq), i = (int)(t % seq);
+    delta[((long)b * n_local + l) * seq + i] = s;
+  }
 }
 
 SP make_sp(const AttnDesc& a) {
@@ -229,7 +254,7 @@ SP make_sp(const AttnDesc& a) {
 hipError_t delta_launch(int dtype, const AttnDesc& a, hipStream_t stream) {
   const long total = (long)a.batch * a.seq * a.n_local;
   if (total == 0) return hipSuccess;
-  dim3 grid((unsigned)((total + 255) / 256));
+  dim3 grid((unsigned)((total + 7) / 8));  // 8 rows per 256-thread workgroup
   const int h_l = a.n_local * a.head_dim;
   if (dtype == DT_BF16)
     hipLaunchKernelGGL(delta_kernel<bf16>, grid, dim3(256), 0, stream, (const bf16*)a.dctx, (const bf16*)a.ctx,
