@@ -1,24 +1,34 @@
 // Flash-style causal attention for bf16 on CDNA4 matrix cores
 // (v_mfma_f32_32x32x16_bf16), head widths D in {64, 96, 128, 160}.
 //
-// Layout: per rank, qkv [T, 3*h_l] = [Q | K | V] in fp32; local head l uses
-// columns l*D.. of each third; row t = b*seq + position. ctx [T, h_l] bf16, lse
-// [batch, n_local, seq] (natural log, fp32).
+// Inputs: per rank, qkv [T, 3*h_l] = [Q | K | V] in fp32; local head l uses
+// columns l*D.. of each third; row t = b*seq + position. A split kernel first
+// writes five bf16 arrays [T, h_l] to the workspace: q_hi, q_lo, k_hi, k_lo,
+// v (x = hi + lo to ~2^-16 relative). Outputs: ctx [T, h_l] bf16, lse
+// [batch, n_local, seq] fp32 (natural log); backward dqkv [T, 3*h_l] bf16.
 //
-// Precision: scores are formed from q and k split into bf16 high and low parts,
-// S = q_hi k_hi + q_hi k_lo + q_lo k_hi (three products, error ~2^-16 |q||k|),
-// because rows of large, nearly tied scores amplify bf16 rounding of q and k
-// far beyond the rounding of the output. V, P, dS and dctx enter the products
-// as bf16 (their rounding is not amplified).
+// Precision: scores are S = q_hi k_hi + q_hi k_lo + q_lo k_hi (three
+// products), because rows of large, nearly tied scores amplify bf16 rounding
+// of q and k far beyond the rounding of the output. V, P, dS and dctx enter
+// the products as bf16 (their rounding is not amplified).
 //
-// Forward (one workgroup = 4 waves = 128 queries of one head; each wave owns 32
-// queries): per 64-key tile, K is staged in LDS row-major and V transposed; a
-// wave computes S^T = K Q^T for 32 keys x its 32 queries, so each lane holds one
-// query column and the softmax statistics (max, sum) are per lane, combined
-// with the partner lane 32 away. P^T stays in registers and is fed straight
-// back as the B operand of ctx^T += V^T P^T: the keys a lane holds in the S^T
-// accumulator form, chunk by chunk, a fixed permutation of 16 consecutive keys,
-// and the transposed V tile is stored in LDS in that same key order.
+// Tiles of 64 rows x D columns are staged in LDS by buffer loads that write
+// LDS directly, double-buffered (the next tile's loads are in flight while
+// the current tile is used), in a chunk-major layout: [D/8 chunks][64 rows]
+// [8 bf16], row r of chunk c stored at slot r ^ 4(c & 3). A tile is read two
+// ways, both free of bank conflicts by that swizzle:
+//  * as rows (MFMA A operand "rows x D"): one ds_read_b128 per lane, lanes
+//    0..31 read 32 consecutive rows of one chunk;
+//  * transposed (A operand "D x rows"): two ds_read_b64_tr_b16 per lane, the
+//    gfx950 transposing read, each giving a lane 4 consecutive rows of its
+//    column. The row order within 16-row groups follows the key/query order
+//    the score accumulators produce, so P (or dS) is fed from registers as the
+//    B operand without any shuffle.
+//
+// Forward (workgroup = 4 waves = 128 queries of one head, each wave 32): per
+// 64-key tile, S^T = K Q^T for 32 keys x the wave's 32 queries, so each lane
+// holds one query column and the softmax statistics (max, sum) are per lane,
+// combined with the partner lane 32 away; ctx^T += V^T P^T.
 //
 // Backward: dK/dV per 32-key wave (workgroup = 128 keys, looping over 64-query
 // tiles), dQ per 32-query wave (looping over 64-key tiles); both recompute P
@@ -30,114 +40,86 @@ namespace tpk {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int TROWS = 64;  // rows per staged tile
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(3))) i16x4* lds_i16x4;
 
 struct MP {
   int batch, seq, n_local, h_l, head0, n_heads, alibi;
-  long ld;             // 3*h_l
-  const float* qkv;
+  long T;
+  const bf16* qh; const bf16* ql; const bf16* kh; const bf16* kl; const bf16* vh;  // [T, h_l] each
   bf16* ctx;
   float* lse;
-  const bf16* dctx;
-  const float* delta;
-  bf16* dqkv;
+  const bf16* dctx;    // [T, h_l]
+  const float* delta;  // [batch, n_local, seq]
+  bf16* dqkv;          // [T, 3*h_l]
   float scale_log2;    // log2(e) / sqrt(D)
   float scale;         // 1 / sqrt(D)
 };
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ const void* uni_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  return (const void*)(((uint64_t)uni((uint32_t)(v >> 32)) << 32) | uni((uint32_t)v));
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t nrec) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)uni_ptr(base), (short)0, (int)uni(nrec), 0x00020000);
+}
 
 __device__ __forceinline__ float alibi_slope_log2(const MP& p, int l) {
   // global head k = head0 + l + 1 (1-based): slope 2^(-8k/n_heads), in log2 units
   return p.alibi ? exp2f(-8.0f * (float)(p.head0 + l + 1) / (float)p.n_heads) * kLog2e : 0.0f;
 }
 
-// 8 consecutive elements as packed bf16 (one 16-byte LDS chunk).
-__device__ __forceinline__ u32x4 load8(const bf16* p) { return *(const u32x4*)p; }
-__device__ __forceinline__ u32x4 load8(const float* p) {
-  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
-  bf16x8 v;
-  v[0] = (bf16)a[0]; v[1] = (bf16)a[1]; v[2] = (bf16)a[2]; v[3] = (bf16)a[3];
-  v[4] = (bf16)b[0]; v[5] = (bf16)b[1]; v[6] = (bf16)b[2]; v[7] = (bf16)b[3];
-  return __builtin_bit_cast(u32x4, v);
-}
-// 8 consecutive fp32 elements split into bf16 high and low parts.
-__device__ __forceinline__ void load8_split(const float* p, bf16x8& hi, bf16x8& lo) {
-  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
-  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    hi[e] = (bf16)x[e];
-    lo[e] = (bf16)(x[e] - (float)hi[e]);
-  }
-}
+// Byte offset of (row, chunk) in a chunk-major tile.
+__device__ __forceinline__ int cm_off(int row, int chunk) { return (chunk << 10) + ((row ^ ((chunk & 3) << 2)) << 4); }
 
-// Tile rows [row0, row0+64) of a [seq, *] slab, row-major in LDS with row
-// stride D+8 (the padding spreads rows over the banks). Rows >= seq are zero.
-template <int D, typename S>
-__device__ __forceinline__ void stage_rows(bf16* s, const S* src, long ld, long grow0, int row0, int seq) {
-  constexpr int CPR = D / 8;
-#pragma unroll
-  for (int it = 0; it < D / 32; ++it) {
-    const int id = threadIdx.x + 256 * it;
-    const int r = id / CPR, c = id - r * CPR;
-    const int pos = row0 + r;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (pos < seq) v = load8(src + (grow0 + pos) * ld + 8 * c);
-    *(u32x4*)(s + r * (D + 8) + 8 * c) = v;
-  }
-}
-// Same, fp32 source split into high and low bf16 tiles.
+// Stage rows [row0, row0 + 64) of columns [col0, col0 + D) of a [T, h_l] bf16
+// array into a chunk-major tile. Wave w loads chunks w, w+4, ...; lane i of a
+// chunk's load lands in slot i, i.e. row i ^ 4(c & 3). Rows at or past seq
+// read zeros (offset beyond the buffer).
 template <int D>
-__device__ __forceinline__ void stage_rows_split(bf16* shi, bf16* slo, const float* src, long ld, long grow0,
-                                                 int row0, int seq) {
-  constexpr int CPR = D / 8;
+__device__ __forceinline__ void dma_tile(const bf16* arr, uint32_t nrec, char* tile, long grow0, int col0, int row0,
+                                         int seq, int h_l, int w, int lane) {
+  const __amdgpu_buffer_rsrc_t rs = rsrc(arr, nrec);
 #pragma unroll
-  for (int it = 0; it < D / 32; ++it) {
-    const int id = threadIdx.x + 256 * it;
-    const int r = id / CPR, c = id - r * CPR;
-    const int pos = row0 + r;
-    bf16x8 hi = bf16x8{}, lo = bf16x8{};
-    if (pos < seq) load8_split(src + (grow0 + pos) * ld + 8 * c, hi, lo);
-    *(bf16x8*)(shi + r * (D + 8) + 8 * c) = hi;
-    *(bf16x8*)(slo + r * (D + 8) + 8 * c) = lo;
+  for (int j = 0; j < D / 32; ++j) {
+    const int c = w + 4 * j;
+    const int pos = row0 + (lane ^ (w << 2));  // (c & 3) == w
+    const uint32_t vo = pos < seq ? (uint32_t)(((grow0 + pos) * h_l + col0 + 8 * c) * 2) : nrec;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(tile + (c << 10)), 16, vo, 0, 0, 0);
   }
 }
 
-// The same 64 rows transposed: LDS [D][64], row d holds the 64 tile rows in
-// the accumulator key order (inside each group of 16: position 8g + 4a + r for
-// tile row 8a + 4g + r), 16-byte chunks XOR-swizzled by swz(d). Each of the
-// first D threads transposes one 8x8 block in registers.
-template <int D, typename S>
-__device__ __forceinline__ void stage_trans(bf16* s, const S* src, long ld, long grow0, int row0, int seq) {
-  const int id = threadIdx.x;
-  if (id >= D) return;
-  const int rb8 = id & 7, cb8 = id >> 3;
-  u32x4 r[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int pos = row0 + 8 * rb8 + j;
-    r[j] = pos < seq ? load8(src + (grow0 + pos) * ld + 8 * cb8) : u32x4{0u, 0u, 0u, 0u};
-  }
-  const int c16 = rb8 >> 1, a = rb8 & 1;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int dw = i >> 1;
-    uint32_t o[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = r[2 * q][dw], hi = r[2 * q + 1][dw];
-      o[q] = (i & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-    }
-    const int d = 8 * cb8 + i, sw = swz(d);
-    bf16* rowp = s + d * 64;
-    *(u32x2*)(rowp + (((2 * c16) ^ sw) << 3) + 4 * a) = u32x2{o[0], o[1]};
-    *(u32x2*)(rowp + (((2 * c16 + 1) ^ sw) << 3) + 4 * a) = u32x2{o[2], o[3]};
-  }
+// Row fragment: row `row` of the tile, 8 columns of chunk `chunk`.
+__device__ __forceinline__ bf16x8 frag_row(const char* tile, int row, int chunk) {
+  return *(const bf16x8*)(tile + cm_off(row, chunk));
 }
 
-// A-operand fragment from a transposed tile: row d, 16-row chunk kc of the tile.
-__device__ __forceinline__ bf16x8 frag_trans(const bf16* s, int d, int kc, int g) {
-  return *(const bf16x8*)(s + d * 64 + (((2 * kc + g) ^ swz(d)) << 3));
+// Transposed fragment: lane l gets column 32db + (l & 31) of rows
+// 16kc + 4g + {0..3} and 16kc + 8 + 4g + {0..3} (g = l >> 5). In each 16-lane
+// group, lane 4r + c fetches 4 columns of one of those rows; the per-lane
+// byte offsets (relative to chunk 4db, row 16kc) are tr_offsets' a and b.
+struct TrOff {
+  int a, b;
+};
+__device__ __forceinline__ TrOff tr_offsets(int lane) {
+  const int G = lane >> 4, r = (lane >> 2) & 3, c = lane & 3, g = lane >> 5;
+  const int x = 2 * (G & 1) + (c >> 1);  // chunk within the 4-chunk (32-column) block
+  TrOff o;
+  o.a = (x << 10) + (((4 * g + r) ^ (x << 2)) << 4) + 8 * (c & 1);
+  o.b = (x << 10) + (((8 + 4 * g + r) ^ (x << 2)) << 4) + 8 * (c & 1);
+  return o;
+}
+__device__ __forceinline__ bf16x8 frag_tr(const char* tile, int db, int kc, const TrOff& o) {
+  const char* b = tile + (db << 12) + (kc << 8);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(b + o.a));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(b + o.b));
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 __device__ __forceinline__ bf16x8 pack8(const float* x) {
@@ -147,94 +129,133 @@ __device__ __forceinline__ bf16x8 pack8(const float* x) {
   return v;
 }
 
+__device__ __forceinline__ bf16x8 ld8(const bf16* p) { return *(const bf16x8*)p; }
+
+// This wave's loads into LDS have landed, then the workgroup barrier: after it
+// every wave's loads have landed. (The barrier's own fence does not wait for
+// loads that write LDS directly.)
+__device__ __forceinline__ void loads_landed_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+// ---- forward ---------------------------------------------------------------------
+template <int D>
+struct FwdState {
+  bf16x8 qf[D / 16], qfl[D / 16];
+  f32x16 o[D / 32];
+  float m_run, l_run;
+};
+
+// One 64-key tile from stage `cur` (K hi, K lo, V at 0, TB, 2TB); the loads
+// of the next tile go to `nxt` first.
+template <int D>
+__device__ __forceinline__ void fwd_tile(const MP& p, const char* __restrict__ cur, char* __restrict__ nxt,
+                                         bool issue, int kv0, int l, long grow0, int w, int lane, int q0w, int myq,
+                                         float slope2, const TrOff& tro, FwdState<D>& st) {
+  constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
+  const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
+  if (issue) {
+    dma_tile<D>(p.kh, nrec, nxt, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
+    dma_tile<D>(p.kl, nrec, nxt + TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
+    dma_tile<D>(p.vh, nrec, nxt + 2 * TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
+  }
+  const int g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    const int k0 = kv0 + 32 * sb;
+    if (k0 > q0w + 31 || k0 >= p.seq) continue;  // wave-uniform: all masked
+    f32x16 sa = f32x16{}, sc = f32x16{};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const bf16x8 kh = frag_row(cur, 32 * sb + l32, 2 * c + g);
+      const bf16x8 kl = frag_row(cur + TB, 32 * sb + l32, 2 * c + g);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, st.qf[c], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, st.qfl[c], sc, 0, 0, 0);
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, st.qf[c], sa, 0, 0, 0);
+    }
+    // s[q]: key k0 + 8(q>>2) + 4g + (q&3), query myq
+    const bool need_mask = (k0 + 31 > q0w) || (k0 + 32 > p.seq);
+    float x[16];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int key = k0 + 8 * (q >> 2) + 4 * g + (q & 3);
+      float v = (sc[q] + sa[q]) * p.scale_log2 - slope2 * (float)(myq - key);
+      if (need_mask && (key > myq || key >= p.seq)) v = -INFINITY;
+      x[q] = v;
+      mloc = fmaxf(mloc, v);
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const float m_new = fmaxf(st.m_run, mloc);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    float lloc = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      x[q] = exp2f(x[q] - m_use);
+      lloc += x[q];
+    }
+    lloc += __shfl_xor(lloc, 32);
+    const float corr = exp2f(st.m_run - m_use);
+    st.l_run = st.l_run * corr + lloc;
+    st.m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < NB; ++db) st.o[db] *= corr;
+    const bf16x8 pf0 = pack8(x), pf1 = pack8(x + 8);
+    const char* vt = cur + 2 * TB;
+#pragma unroll
+    for (int db = 0; db < NB; ++db) {
+      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(vt, db, 2 * sb, tro), pf0, st.o[db], 0, 0, 0);
+      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(vt, db, 2 * sb + 1, tro), pf1, st.o[db], 0, 0, 0);
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void fwd_mfma(MP p) {
-  constexpr int NC = D / 16, NB = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16 sK[64 * (D + 8)];
-  __shared__ __attribute__((aligned(16))) bf16 sKl[64 * (D + 8)];
-  __shared__ __attribute__((aligned(16))) bf16 sVt[D * 64];
+  constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
+  __shared__ __attribute__((aligned(16))) char st0[3 * TB];
+  __shared__ __attribute__((aligned(16))) char st1[3 * TB];
   const int head = blockIdx.x;
   const int b = head / p.n_local, l = head - b * p.n_local;
   const int nqt = (p.seq + 127) / 128;
   const int qt = nqt - 1 - blockIdx.y;  // heaviest (longest causal prefix) first
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = (int)uni((uint32_t)(tid >> 6));
   const long grow0 = (long)b * p.seq;
-  const float* Qg = p.qkv + (long)l * D;
-  const float* Kg = p.qkv + p.h_l + (long)l * D;
-  const float* Vg = p.qkv + 2L * p.h_l + (long)l * D;
   const int q0w = qt * 128 + 32 * w;
   const int myq = q0w + l32;
-  bf16x8 qf[NC], qfl[NC];
+  const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
+  const int kv_end = min(p.seq, qt * 128 + 128);
+  const int nkt = (kv_end + TROWS - 1) / TROWS;
+  dma_tile<D>(p.kh, nrec, st0, grow0, l * D, 0, p.seq, p.h_l, w, lane);
+  dma_tile<D>(p.kl, nrec, st0 + TB, grow0, l * D, 0, p.seq, p.h_l, w, lane);
+  dma_tile<D>(p.vh, nrec, st0 + 2 * TB, grow0, l * D, 0, p.seq, p.h_l, w, lane);
+  FwdState<D> st;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    qf[c] = bf16x8{};
-    qfl[c] = bf16x8{};
-    if (myq < p.seq) load8_split(Qg + (grow0 + myq) * p.ld + 16 * c + 8 * g, qf[c], qfl[c]);
-  }
-  f32x16 o[NB];
-#pragma unroll
-  for (int db = 0; db < NB; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-  const float slope2 = alibi_slope_log2(p, l);
-  const int kv_end = min(p.seq, qt * 128 + 128);
-  const int nkt = (kv_end + 63) / 64;
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int kv0 = kt * 64;
-    __syncthreads();
-    stage_rows_split<D>(sK, sKl, Kg, p.ld, grow0, kv0, p.seq);
-    stage_trans<D>(sVt, Vg, p.ld, grow0, kv0, p.seq);
-    __syncthreads();
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const int k0 = kv0 + 32 * sb;
-      if (k0 > q0w + 31 || k0 >= p.seq) continue;  // wave-uniform: all masked
-      f32x16 s = f32x16{};
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int off = (32 * sb + l32) * (D + 8) + 16 * c + 8 * g;
-        const bf16x8 kh = *(const bf16x8*)(sK + off), kl = *(const bf16x8*)(sKl + off);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qf[c], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qfl[c], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qf[c], s, 0, 0, 0);
-      }
-      // s[q]: key k0 + 8(q>>2) + 4g + (q&3), query myq
-      const bool need_mask = (k0 + 31 > q0w) || (k0 + 32 > p.seq);
-      float x[16];
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int key = k0 + 8 * (q >> 2) + 4 * g + (q & 3);
-        float v = s[q] * p.scale_log2 - slope2 * (float)(myq - key);
-        if (need_mask && (key > myq || key >= p.seq)) v = -INFINITY;
-        x[q] = v;
-        mloc = fmaxf(mloc, v);
-      }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const float m_new = fmaxf(m_run, mloc);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      float lloc = 0.f;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        x[q] = exp2f(x[q] - m_use);
-        lloc += x[q];
-      }
-      lloc += __shfl_xor(lloc, 32);
-      const float corr = exp2f(m_run - m_use);
-      l_run = l_run * corr + lloc;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < NB; ++db) o[db] *= corr;
-      const bf16x8 pf0 = pack8(x), pf1 = pack8(x + 8);
-#pragma unroll
-      for (int db = 0; db < NB; ++db) {
-        const int d = 32 * db + l32;
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_trans(sVt, d, 2 * sb, g), pf0, o[db], 0, 0, 0);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_trans(sVt, d, 2 * sb + 1, g), pf1, o[db], 0, 0, 0);
-      }
+    st.qf[c] = bf16x8{};
+    st.qfl[c] = bf16x8{};
+    if (myq < p.seq) {
+      const long off = (grow0 + myq) * p.h_l + (long)l * D + 16 * c + 8 * g;
+      st.qf[c] = ld8(p.qh + off);
+      st.qfl[c] = ld8(p.ql + off);
     }
   }
+#pragma unroll
+  for (int db = 0; db < NB; ++db) st.o[db] = f32x16{};
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
+  const float slope2 = alibi_slope_log2(p, l);
+  const TrOff tro = tr_offsets(lane);
+  for (int kt = 0; kt < nkt; ++kt) {
+    loads_landed_barrier();  // tile kt is in LDS; tile kt-1 is no longer read
+    const bool odd = kt & 1;
+    fwd_tile<D>(p, odd ? st1 : st0, odd ? st0 : st1, kt + 1 < nkt, kt * TROWS, l, grow0, w, lane, q0w, myq, slope2,
+                tro, st);
+  }
   if (myq < p.seq) {
-    const float inv = 1.0f / l_run;
+    const float inv = 1.0f / st.l_run;
     bf16* dst = p.ctx + (grow0 + myq) * p.h_l + (long)l * D;
 #pragma unroll
     for (int db = 0; db < NB; ++db)
@@ -242,110 +263,143 @@ __global__ __launch_bounds__(256) void fwd_mfma(MP p) {
       for (int q4 = 0; q4 < 4; ++q4) {
         bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (bf16)(o[db][4 * q4 + e] * inv);
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)(st.o[db][4 * q4 + e] * inv);
         *(bf16x4*)(dst + 32 * db + 8 * q4 + 4 * g) = v;
       }
-    if (g == 0) p.lse[(long)head * p.seq + myq] = (m_run + __log2f(l_run)) * (1.0f / kLog2e);
+    if (g == 0) p.lse[(long)head * p.seq + myq] = (st.m_run + __log2f(st.l_run)) * (1.0f / kLog2e);
+  }
+}
+
+// ---- backward: dK, dV ---------------------------------------------------------------
+template <int D>
+struct KvState {
+  bf16x8 kf[D / 16], kfl[D / 16], vf[D / 16];
+  f32x16 dv[D / 32], dk[D / 32];
+};
+
+// lse and delta of a 64-query tile: 64 floats each, after the three tiles.
+__device__ __forceinline__ void dma_stats(const MP& p, char* stage_stats, int head, int q0, int w, int lane) {
+  if (w >= 2) return;
+  const float* base = (w == 0 ? (const float*)p.lse : p.delta) + (long)head * p.seq;
+  const uint32_t nrec = (uint32_t)(p.seq * 4);
+  const __amdgpu_buffer_rsrc_t rs = rsrc(base, nrec);
+  const uint32_t vo = q0 + lane < p.seq ? (uint32_t)((q0 + lane) * 4) : nrec;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(stage_stats + 256 * w), 4, vo, 0, 0, 0);
+}
+
+// One 64-query tile from stage `cur` (Q hi, Q lo, dctx, then lse, delta).
+template <int D>
+__device__ __forceinline__ void dkdv_tile(const MP& p, const char* __restrict__ cur, char* __restrict__ nxt,
+                                          bool issue, int q0, int head, int l, long grow0, int w, int lane, int k0w,
+                                          int myk, float slope2, const TrOff& tro, KvState<D>& st) {
+  constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
+  const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
+  if (issue) {
+    const int qn = q0 + TROWS;
+    dma_tile<D>(p.qh, nrec, nxt, grow0, l * D, qn, p.seq, p.h_l, w, lane);
+    dma_tile<D>(p.ql, nrec, nxt + TB, grow0, l * D, qn, p.seq, p.h_l, w, lane);
+    dma_tile<D>(p.dctx, nrec, nxt + 2 * TB, grow0, l * D, qn, p.seq, p.h_l, w, lane);
+    dma_stats(p, nxt + 3 * TB, head, qn, w, lane);
+  }
+  if (k0w >= p.seq) return;
+  const int g = lane >> 5, l32 = lane & 31;
+  const float* sL = (const float*)(cur + 3 * TB);
+  const float* sDl = sL + 64;
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    const int qs0 = q0 + 32 * qs;
+    if (qs0 + 31 < k0w || qs0 >= p.seq) continue;  // wave-uniform: all masked
+    f32x16 sa = f32x16{}, sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int row = 32 * qs + l32, ch = 2 * c + g;
+      const bf16x8 qh = frag_row(cur, row, ch), ql = frag_row(cur + TB, row, ch);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql, st.kf[c], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, st.kfl[c], sc, 0, 0, 0);
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, st.kf[c], sa, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(cur + 2 * TB, row, ch), st.vf[c], dp, 0, 0, 0);
+    }
+    // s[q], dp[q]: query qs0 + 8(q>>2) + 4g + (q&3), key myk
+    const bool need_mask = (qs0 < k0w + 31) || (qs0 + 32 > p.seq);
+    float pv[16], dsv[16];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 L = *(const f32x4*)(sL + 32 * qs + 8 * q4 + 4 * g);
+      const f32x4 Dl = *(const f32x4*)(sDl + 32 * qs + 8 * q4 + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int q = 4 * q4 + e;
+        const int query = qs0 + 8 * q4 + 4 * g + e;
+        float pp = exp2f((sc[q] + sa[q]) * p.scale_log2 - slope2 * (float)(query - myk) - L[e] * kLog2e);
+        if (need_mask && (query < myk || query >= p.seq)) pp = 0.f;
+        pv[q] = pp;
+        dsv[q] = pp * (dp[q] - Dl[e]);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bf16x8 pf = pack8(pv + 8 * h), df = pack8(dsv + 8 * h);
+#pragma unroll
+      for (int db = 0; db < NB; ++db) {
+        st.dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(cur + 2 * TB, db, 2 * qs + h, tro), pf,
+                                                            st.dv[db], 0, 0, 0);
+        st.dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(cur, db, 2 * qs + h, tro), df, st.dk[db], 0,
+                                                            0, 0);
+      }
+    }
   }
 }
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dkdv_mfma(MP p) {
-  constexpr int NC = D / 16, NB = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16 sQ[64 * (D + 8)];
-  __shared__ __attribute__((aligned(16))) bf16 sQl[64 * (D + 8)];
-  __shared__ __attribute__((aligned(16))) bf16 sC[64 * (D + 8)];
-  __shared__ __attribute__((aligned(16))) bf16 sQt[D * 64];
-  __shared__ __attribute__((aligned(16))) bf16 sCt[D * 64];
-  __shared__ __attribute__((aligned(16))) float sL[64];
-  __shared__ __attribute__((aligned(16))) float sDl[64];
+  constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2, SB = 3 * TB + 512;
+  __shared__ __attribute__((aligned(16))) char st0[SB];
+  __shared__ __attribute__((aligned(16))) char st1[SB];
   const int head = blockIdx.x;
   const int b = head / p.n_local, l = head - b * p.n_local;
   const int kvt = blockIdx.y;  // 128-key tile; tile 0 sees the most queries
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = (int)uni((uint32_t)(tid >> 6));
   const long grow0 = (long)b * p.seq;
-  const float* Qg = p.qkv + (long)l * D;
-  const float* Kg = p.qkv + p.h_l + (long)l * D;
-  const float* Vg = p.qkv + 2L * p.h_l + (long)l * D;
-  const bf16* Cg = p.dctx + (long)l * D;
   const int k0w = kvt * 128 + 32 * w;
   const int myk = k0w + l32;
-  bf16x8 kf[NC], kfl[NC], vf[NC];
+  const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
+  const int nqt = (p.seq + TROWS - 1) / TROWS;
+  const int qt0 = (kvt * 128) / TROWS;
+  dma_tile<D>(p.qh, nrec, st0, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, lane);
+  dma_tile<D>(p.ql, nrec, st0 + TB, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, lane);
+  dma_tile<D>(p.dctx, nrec, st0 + 2 * TB, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, lane);
+  dma_stats(p, st0 + 3 * TB, head, qt0 * TROWS, w, lane);
+  KvState<D> st;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    kf[c] = bf16x8{};
-    kfl[c] = bf16x8{};
-    vf[c] = bf16x8{};
+    st.kf[c] = bf16x8{};
+    st.kfl[c] = bf16x8{};
+    st.vf[c] = bf16x8{};
     if (myk < p.seq) {
-      load8_split(Kg + (grow0 + myk) * p.ld + 16 * c + 8 * g, kf[c], kfl[c]);
-      vf[c] = __builtin_bit_cast(bf16x8, load8(Vg + (grow0 + myk) * p.ld + 16 * c + 8 * g));
+      const long off = (grow0 + myk) * p.h_l + (long)l * D + 16 * c + 8 * g;
+      st.kf[c] = ld8(p.kh + off);
+      st.kfl[c] = ld8(p.kl + off);
+      st.vf[c] = ld8(p.vh + off);
     }
   }
-  f32x16 dv[NB], dk[NB];
 #pragma unroll
-  for (int db = 0; db < NB; ++db) { dv[db] = f32x16{}; dk[db] = f32x16{}; }
+  for (int db = 0; db < NB; ++db) {
+    st.dv[db] = f32x16{};
+    st.dk[db] = f32x16{};
+  }
   const float slope2 = alibi_slope_log2(p, l);
-  const int nqt = (p.seq + 63) / 64;
-  for (int qt = (kvt * 128) / 64; qt < nqt; ++qt) {
-    const int q0 = qt * 64;
-    __syncthreads();
-    stage_rows_split<D>(sQ, sQl, Qg, p.ld, grow0, q0, p.seq);
-    stage_rows<D>(sC, Cg, p.h_l, grow0, q0, p.seq);
-    stage_trans<D>(sQt, Qg, p.ld, grow0, q0, p.seq);
-    stage_trans<D>(sCt, Cg, p.h_l, grow0, q0, p.seq);
-    if (tid < 64) {
-      const int pos = q0 + tid;
-      sL[tid] = pos < p.seq ? p.lse[(long)head * p.seq + pos] * kLog2e : 0.f;
-      sDl[tid] = pos < p.seq ? p.delta[(long)head * p.seq + pos] : 0.f;
-    }
-    __syncthreads();
-    if (k0w >= p.seq) continue;
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      const int qs0 = q0 + 32 * qs;
-      if (qs0 + 31 < k0w || qs0 >= p.seq) continue;  // wave-uniform: all masked
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int off = (32 * qs + l32) * (D + 8) + 16 * c + 8 * g;
-        const bf16x8 qh = *(const bf16x8*)(sQ + off), ql = *(const bf16x8*)(sQl + off);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql, kf[c], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, kfl[c], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, kf[c], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(sC + off), vf[c], dp, 0, 0, 0);
-      }
-      // s[q], dp[q]: query qs0 + 8(q>>2) + 4g + (q&3), key myk
-      const bool need_mask = (qs0 < k0w + 31) || (qs0 + 32 > p.seq);
-      float pv[16], dsv[16];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 L = *(const f32x4*)(sL + 32 * qs + 8 * q4 + 4 * g);
-        const f32x4 Dl = *(const f32x4*)(sDl + 32 * qs + 8 * q4 + 4 * g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int q = 4 * q4 + e;
-          const int query = qs0 + 8 * q4 + 4 * g + e;
-          float pp = exp2f(s[q] * p.scale_log2 - slope2 * (float)(query - myk) - L[e]);
-          if (need_mask && (query < myk || query >= p.seq)) pp = 0.f;
-          pv[q] = pp;
-          dsv[q] = pp * (dp[q] - Dl[e]);
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const bf16x8 pf = pack8(pv + 8 * h), df = pack8(dsv + 8 * h);
-#pragma unroll
-        for (int db = 0; db < NB; ++db) {
-          const int d = 32 * db + l32;
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_trans(sCt, d, 2 * qs + h, g), pf, dv[db], 0, 0, 0);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_trans(sQt, d, 2 * qs + h, g), df, dk[db], 0, 0, 0);
-        }
-      }
-    }
+  const TrOff tro = tr_offsets(lane);
+  for (int qt = qt0; qt < nqt; ++qt) {
+    loads_landed_barrier();
+    const bool odd = (qt - qt0) & 1;
+    dkdv_tile<D>(p, odd ? st1 : st0, odd ? st0 : st1, qt + 1 < nqt, qt * TROWS, head, l, grow0, w, lane, k0w, myk,
+                 slope2, tro, st);
   }
   if (myk < p.seq) {
-    bf16* dK = p.dqkv + (grow0 + myk) * p.ld + p.h_l + (long)l * D;
-    bf16* dV = p.dqkv + (grow0 + myk) * p.ld + 2L * p.h_l + (long)l * D;
+    const long ld3 = 3L * p.h_l;
+    bf16* dK = p.dqkv + (grow0 + myk) * ld3 + p.h_l + (long)l * D;
+    bf16* dV = p.dqkv + (grow0 + myk) * ld3 + 2L * p.h_l + (long)l * D;
 #pragma unroll
     for (int db = 0; db < NB; ++db)
 #pragma unroll
@@ -353,8 +407,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         bf16x4 a, c;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          a[e] = (bf16)(dk[db][4 * q4 + e] * p.scale);
-          c[e] = (bf16)dv[db][4 * q4 + e];
+          a[e] = (bf16)(st.dk[db][4 * q4 + e] * p.scale);
+          c[e] = (bf16)st.dv[db][4 * q4 + e];
         }
         *(bf16x4*)(dK + 32 * db + 8 * q4 + 4 * g) = a;
         *(bf16x4*)(dV + 32 * db + 8 * q4 + 4 * g) = c;
@@ -362,104 +416,164 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
+// ---- backward: dQ ----------------------------------------------------------------
+template <int D>
+struct QState {
+  bf16x8 qf[D / 16], qfl[D / 16], cf[D / 16];
+  f32x16 dq[D / 32];
+  float L, Dl;
+};
+
+// One 64-key tile from stage `cur` (K hi, K lo, V).
+template <int D>
+__device__ __forceinline__ void dq_tile(const MP& p, const char* __restrict__ cur, char* __restrict__ nxt, bool issue,
+                                        int kv0, int l, long grow0, int w, int lane, int q0w, int myq, float slope2,
+                                        const TrOff& tro, QState<D>& st) {
+  constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
+  const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
+  if (issue) {
+    dma_tile<D>(p.kh, nrec, nxt, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
+    dma_tile<D>(p.kl, nrec, nxt + TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
+    dma_tile<D>(p.vh, nrec, nxt + 2 * TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
+  }
+  const int g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    const int k0 = kv0 + 32 * sb;
+    if (k0 > q0w + 31 || k0 >= p.seq) continue;
+    f32x16 sa = f32x16{}, sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int row = 32 * sb + l32, ch = 2 * c + g;
+      const bf16x8 kh = frag_row(cur, row, ch), kl = frag_row(cur + TB, row, ch);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, st.qf[c], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, st.qfl[c], sc, 0, 0, 0);
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, st.qf[c], sa, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(cur + 2 * TB, row, ch), st.cf[c], dp, 0, 0, 0);
+    }
+    // s[q]: key k0 + 8(q>>2) + 4g + (q&3), query myq
+    const bool need_mask = (k0 + 31 > q0w) || (k0 + 32 > p.seq);
+    float ds[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int key = k0 + 8 * (q >> 2) + 4 * g + (q & 3);
+      float pp = exp2f((sc[q] + sa[q]) * p.scale_log2 - slope2 * (float)(myq - key) - st.L);
+      if (need_mask && (key > myq || key >= p.seq)) pp = 0.f;
+      ds[q] = pp * (dp[q] - st.Dl);
+    }
+    const bf16x8 df0 = pack8(ds), df1 = pack8(ds + 8);
+#pragma unroll
+    for (int db = 0; db < NB; ++db) {
+      st.dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(cur, db, 2 * sb, tro), df0, st.dq[db], 0, 0, 0);
+      st.dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(cur, db, 2 * sb + 1, tro), df1, st.dq[db], 0, 0, 0);
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void dq_mfma(MP p) {
-  constexpr int NC = D / 16, NB = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16 sK[64 * (D + 8)];
-  __shared__ __attribute__((aligned(16))) bf16 sKl[64 * (D + 8)];
-  __shared__ __attribute__((aligned(16))) bf16 sV[64 * (D + 8)];
-  __shared__ __attribute__((aligned(16))) bf16 sKt[D * 64];
+  constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
+  __shared__ __attribute__((aligned(16))) char st0[3 * TB];
+  __shared__ __attribute__((aligned(16))) char st1[3 * TB];
   const int head = blockIdx.x;
   const int b = head / p.n_local, l = head - b * p.n_local;
   const int nqt = (p.seq + 127) / 128;
   const int qt = nqt - 1 - blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = (int)uni((uint32_t)(tid >> 6));
   const long grow0 = (long)b * p.seq;
-  const float* Qg = p.qkv + (long)l * D;
-  const float* Kg = p.qkv + p.h_l + (long)l * D;
-  const float* Vg = p.qkv + 2L * p.h_l + (long)l * D;
-  const bf16* Cg = p.dctx + (long)l * D;
   const int q0w = qt * 128 + 32 * w;
   const int myq = q0w + l32;
-  bf16x8 qf[NC], qfl[NC], cf[NC];
+  const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
+  const int kv_end = min(p.seq, qt * 128 + 128);
+  const int nkt = (kv_end + TROWS - 1) / TROWS;
+  dma_tile<D>(p.kh, nrec, st0, grow0, l * D, 0, p.seq, p.h_l, w, lane);
+  dma_tile<D>(p.kl, nrec, st0 + TB, grow0, l * D, 0, p.seq, p.h_l, w, lane);
+  dma_tile<D>(p.vh, nrec, st0 + 2 * TB, grow0, l * D, 0, p.seq, p.h_l, w, lane);
+  QState<D> st;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    qf[c] = bf16x8{};
-    qfl[c] = bf16x8{};
-    cf[c] = bf16x8{};
+    st.qf[c] = bf16x8{};
+    st.qfl[c] = bf16x8{};
+    st.cf[c] = bf16x8{};
     if (myq < p.seq) {
-      load8_split(Qg + (grow0 + myq) * p.ld + 16 * c + 8 * g, qf[c], qfl[c]);
-      cf[c] = *(const bf16x8*)(Cg + (grow0 + myq) * p.h_l + 16 * c + 8 * g);
+      const long off = (grow0 + myq) * p.h_l + (long)l * D + 16 * c + 8 * g;
+      st.qf[c] = ld8(p.qh + off);
+      st.qfl[c] = ld8(p.ql + off);
+      st.cf[c] = ld8(p.dctx + off);
     }
   }
-  const float L = myq < p.seq ? p.lse[(long)head * p.seq + myq] * kLog2e : 0.f;
-  const float Dl = myq < p.seq ? p.delta[(long)head * p.seq + myq] : 0.f;
-  f32x16 dq[NB];
+  st.L = myq < p.seq ? p.lse[(long)head * p.seq + myq] * kLog2e : 0.f;
+  st.Dl = myq < p.seq ? p.delta[(long)head * p.seq + myq] : 0.f;
 #pragma unroll
-  for (int db = 0; db < NB; ++db) dq[db] = f32x16{};
+  for (int db = 0; db < NB; ++db) st.dq[db] = f32x16{};
   const float slope2 = alibi_slope_log2(p, l);
-  const int kv_end = min(p.seq, qt * 128 + 128);
-  const int nkt = (kv_end + 63) / 64;
+  const TrOff tro = tr_offsets(lane);
   for (int kt = 0; kt < nkt; ++kt) {
-    const int kv0 = kt * 64;
-    __syncthreads();
-    stage_rows_split<D>(sK, sKl, Kg, p.ld, grow0, kv0, p.seq);
-    stage_rows<D>(sV, Vg, p.ld, grow0, kv0, p.seq);
-    stage_trans<D>(sKt, Kg, p.ld, grow0, kv0, p.seq);
-    __syncthreads();
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const int k0 = kv0 + 32 * sb;
-      if (k0 > q0w + 31 || k0 >= p.seq) continue;
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int off = (32 * sb + l32) * (D + 8) + 16 * c + 8 * g;
-        const bf16x8 kh = *(const bf16x8*)(sK + off), kl = *(const bf16x8*)(sKl + off);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qf[c], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qfl[c], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qf[c], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(sV + off), cf[c], dp, 0, 0, 0);
-      }
-      // s[q]: key k0 + 8(q>>2) + 4g + (q&3), query myq
-      const bool need_mask = (k0 + 31 > q0w) || (k0 + 32 > p.seq);
-      float ds[16];
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int key = k0 + 8 * (q >> 2) + 4 * g + (q & 3);
-        float pp = exp2f(s[q] * p.scale_log2 - slope2 * (float)(myq - key) - L);
-        if (need_mask && (key > myq || key >= p.seq)) pp = 0.f;
-        ds[q] = pp * (dp[q] - Dl);
-      }
-      const bf16x8 df0 = pack8(ds), df1 = pack8(ds + 8);
-#pragma unroll
-      for (int db = 0; db < NB; ++db) {
-        const int d = 32 * db + l32;
-        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_trans(sKt, d, 2 * sb, g), df0, dq[db], 0, 0, 0);
-        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_trans(sKt, d, 2 * sb + 1, g), df1, dq[db], 0, 0, 0);
-      }
-    }
+    loads_landed_barrier();
+    const bool odd = kt & 1;
+    dq_tile<D>(p, odd ? st1 : st0, odd ? st0 : st1, kt + 1 < nkt, kt * TROWS, l, grow0, w, lane, q0w, myq, slope2, tro,
+               st);
   }
   if (myq < p.seq) {
-    bf16* dQ = p.dqkv + (grow0 + myq) * p.ld + (long)l * D;
+    bf16* dQ = p.dqkv + (grow0 + myq) * (3L * p.h_l) + (long)l * D;
 #pragma unroll
     for (int db = 0; db < NB; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         bf16x4 a;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a[e] = (bf16)(dq[db][4 * q4 + e] * p.scale);
+        for (int e = 0; e < 4; ++e) a[e] = (bf16)(st.dq[db][4 * q4 + e] * p.scale);
         *(bf16x4*)(dQ + 32 * db + 8 * q4 + 4 * g) = a;
       }
   }
+}
+
+// ---- q/k/v split ------------------------------------------------------------------
+// out = [q_hi | q_lo | k_hi | k_lo | v] as five [T, h_l] bf16 arrays; hi is the
+// round-to-nearest bf16 of x, lo that of x - hi.
+__global__ __launch_bounds__(256) void split_qkv_kernel(const float* qkv, bf16* out, long T, int h_l) {
+  const long n8 = T * 3L * h_l / 8;
+  const long plane = T * (long)h_l;
+  const long stride = (long)gridDim.x * 256;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
+    const long e0 = 8 * i;
+    const long t = e0 / (3L * h_l);
+    const int col = (int)(e0 - t * 3L * h_l);
+    const int part = col / h_l, c = col - part * h_l;
+    const f32x4 a = *(const f32x4*)(qkv + e0), b = *(const f32x4*)(qkv + e0 + 4);
+    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    bf16x8 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      hi[e] = (bf16)x[e];
+      lo[e] = (bf16)(x[e] - (float)hi[e]);
+    }
+    *(bf16x8*)(out + 2 * part * plane + t * h_l + c) = hi;
+    if (part < 2) *(bf16x8*)(out + (2 * part + 1) * plane + t * h_l + c) = lo;
+  }
+}
+
+hipError_t split_launch(const AttnDesc& a, hipStream_t stream) {
+  const long T = (long)a.batch * a.seq;
+  const int h_l = a.n_local * a.head_dim;
+  const long n8 = T * 3L * h_l / 8;
+  long grid = (n8 + 255) / 256;
+  if (grid > 8192) grid = 8192;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(split_qkv_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a.qkv, (bf16*)a.split, T, h_l);
+  return hipGetLastError();
 }
 
 MP make_mp(const AttnDesc& a) {
   MP p{};
   p.batch = a.batch; p.seq = a.seq; p.n_local = a.n_local;
   p.h_l = a.n_local * a.head_dim; p.head0 = a.head0; p.n_heads = a.n_heads; p.alibi = a.alibi;
-  p.ld = 3L * p.h_l;
-  p.qkv = a.qkv; p.ctx = (bf16*)a.ctx; p.lse = a.lse;
+  p.T = (long)a.batch * a.seq;
+  const bf16* sp = (const bf16*)a.split;
+  const long plane = p.T * p.h_l;
+  p.qh = sp; p.ql = sp + plane; p.kh = sp + 2 * plane; p.kl = sp + 3 * plane; p.vh = sp + 4 * plane;
+  p.ctx = (bf16*)a.ctx; p.lse = a.lse;
   p.dctx = (const bf16*)a.dctx; p.delta = a.delta; p.dqkv = (bf16*)a.dqkv;
   p.scale = 1.0f / sqrtf((float)a.head_dim);
   p.scale_log2 = p.scale * kLog2e;
@@ -488,7 +602,13 @@ bool attn_mfma_supported(int dtype, int head_dim) {
   return dtype == DT_BF16 && (head_dim == 64 || head_dim == 96 || head_dim == 128 || head_dim == 160);
 }
 
+size_t attn_split_bytes(int dtype, int head_dim, long long T, long long h_l) {
+  return attn_mfma_supported(dtype, head_dim) ? (size_t)(5 * T * h_l * 2) : 0;
+}
+
 hipError_t attn_mfma_fwd(const AttnDesc& a, hipStream_t stream) {
+  hipError_t e = split_launch(a, stream);
+  if (e != hipSuccess) return e;
   const MP p = make_mp(a);
   switch (a.head_dim) {
     case 64: return fwd_d<64>(p, stream);
@@ -500,6 +620,8 @@ hipError_t attn_mfma_fwd(const AttnDesc& a, hipStream_t stream) {
 }
 
 hipError_t attn_mfma_bwd(const AttnDesc& a, hipStream_t stream) {
+  hipError_t e = split_launch(a, stream);
+  if (e != hipSuccess) return e;
   const MP p = make_mp(a);
   switch (a.head_dim) {
     case 64: return bwd_d<64>(p, stream);

@@ -61,8 +61,12 @@ struct AttnDesc {
   const void* dctx = nullptr;  // [T, h_l]
   float* delta = nullptr;      // [batch, n_local, seq] scratch: rowsum(dctx * ctx)
   void* dqkv = nullptr;        // [T, 3*h_l]
+  // matrix-core path only: workspace for q/k/v split into bf16 hi/lo parts,
+  // attn_split_bytes() bytes (5 arrays [T, h_l] bf16)
+  void* split = nullptr;
 };
 bool attn_mfma_supported(int dtype, int head_dim);
+size_t attn_split_bytes(int dtype, int head_dim, long long T, long long h_l);
 hipError_t attn_fwd_launch(int dtype, const AttnDesc& a, hipStream_t stream);
 hipError_t attn_bwd_launch(int dtype, const AttnDesc& a, hipStream_t stream);
 

@@ -203,7 +203,7 @@ MlpPlan plan_mlp(const Dims& dm, void* ws, bool bwd) {
 }
 
 struct AttnPlan {
-  void *dctx, *dqkv, *delta, *gemm_ws, *col_ws;
+  void *dctx, *dqkv, *delta, *gemm_ws, *col_ws, *split;
   size_t gemm_bytes, col_bytes, total;
 };
 
@@ -212,6 +212,8 @@ AttnPlan plan_attn(const Dims& dm, void* ws, bool bwd) {
   AttnPlan pl{};
   const int dt = dm.dtype;
   const long long B = dm.T;
+  const size_t split = attn_split_bytes(dt, (int)dm.d, dm.T, dm.hl);
+  pl.split = split ? bp.take(split) : nullptr;
   size_t g = max3(gemm_workspace_bytes(dt, (int)B, (int)(3 * dm.hl), (int)dm.h),
                   gemm_workspace_bytes(dt, (int)B, (int)dm.h, (int)dm.hl), 0);
   if (bwd) {
@@ -364,7 +366,7 @@ tp_status tp_attn_fwd(const tp_shape* shape, const void* X, const void* Wqkv_i, 
   AttnDesc a;
   a.batch = shape->batch; a.seq = shape->seq; a.n_local = (int)dm.nl; a.head_dim = (int)dm.d;
   a.head0 = shape->tp_rank * (int)dm.nl; a.n_heads = shape->n_heads; a.alibi = shape->alibi;
-  a.qkv = qkv_i; a.ctx = ctx_i; a.lse = lse_i;
+  a.qkv = qkv_i; a.ctx = ctx_i; a.lse = lse_i; a.split = pl.split;
   TP_STEP(TP_STEP_ATTN_FWD, attn_fwd_launch(dt, a, st), "attn forward");
   TP_STEP(TP_STEP_OUT_PROJ, gemm_launch(dt, gd(GR_OUT_PROJ, T, h, hl, ctx_i, hl, true, Wo_i, h, false, EPI_STORE, O_i, h), pl.gemm_ws, pl.gemm_bytes, st),
          "attn output projection");
@@ -406,7 +408,7 @@ tp_status tp_attn_bwd(const tp_shape* shape, const void* X, const void* Wqkv_i, 
     a.batch = shape->batch; a.seq = shape->seq; a.n_local = (int)dm.nl; a.head_dim = (int)dm.d;
     a.head0 = shape->tp_rank * (int)dm.nl; a.n_heads = shape->n_heads; a.alibi = shape->alibi;
     a.qkv = qkv_i; a.ctx = (void*)ctx_i; a.lse = (float*)lse_i;
-    a.dctx = pl.dctx; a.delta = (float*)pl.delta; a.dqkv = pl.dqkv;
+    a.dctx = pl.dctx; a.delta = (float*)pl.delta; a.dqkv = pl.dqkv; a.split = pl.split;
     TP_STEP(TP_STEP_ATTN_BWD, attn_bwd_launch(dt, a, st), "attn backward");
   }
   TP_STEP(TP_STEP_QKV_WGRAD, gemm_launch(dt, gd(GR_QKV_WGRAD, h, 3 * hl, T, X, h, false, pl.dqkv, 3 * hl, false, EPI_STORE, dWqkv_i, 3 * hl), pl.gemm_ws,
