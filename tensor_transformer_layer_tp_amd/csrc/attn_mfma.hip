@@ -74,8 +74,6 @@ __device__ __forceinline__ float alibi_slope_log2(const MP& p, int l) {
   return p.alibi ? exp2f(-8.0f * (float)(p.head0 + l + 1) / (float)p.n_heads) * kLog2e : 0.0f;
 }
 
-// Byte offset of (row, chunk) in a chunk-major tile.
-__device__ __forceinline__ int cm_off(int row, int chunk) { return (chunk << 10) + ((row ^ ((chunk & 3) << 2)) << 4); }
 
 // Stage rows [row0, row0 + 64) of columns [col0, col0 + D) of a [T, h_l] bf16
 // array into a chunk-major tile. Wave w loads chunks w, w+4, ...; lane i of a
@@ -94,10 +92,27 @@ __device__ __forceinline__ void dma_tile(const bf16* arr, uint32_t nrec, char* t
   }
 }
 
-// Row fragment: row `row` of the tile, 8 columns of chunk `chunk`.
-__device__ __forceinline__ bf16x8 frag_row(const char* tile, int row, int chunk) {
-  return *(const bf16x8*)(tile + cm_off(row, chunk));
+// Row fragment for MFMA operand "rows x D": lane l reads row 32blk + (l & 31),
+// columns 16c + 8(l >> 5) .. +7, i.e. chunk 2c + g. The swizzle term
+// 4((2c + g) & 3) only depends on the parity of c, so two per-lane offsets
+// (c even, c odd) plus compile-time constants address every fragment.
+struct RowOff {
+  int e, o;
+};
+__device__ __forceinline__ RowOff row_offsets(int lane) {
+  const int g = lane >> 5, l32 = lane & 31;
+  RowOff r;
+  r.e = (g << 10) + ((l32 ^ (g << 2)) << 4);
+  r.o = (g << 10) + ((l32 ^ ((2 + g) << 2)) << 4);
+  return r;
 }
+__device__ __forceinline__ bf16x8 frag_row(const char* tile, int blk, int c, const RowOff& ro) {
+  return *(const bf16x8*)(tile + ((c & 1) ? ro.o : ro.e) + (c << 11) + (blk << 9));
+}
+
+// 2^x by the hardware instruction (inputs here are <= 2^8 or far below 0;
+// results below the normal range flush to 0, which softmax weights tolerate).
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Transposed fragment: lane l gets column 32db + (l & 31) of rows
 // 16kc + 4g + {0..3} and 16kc + 8 + 4g + {0..3} (g = l >> 5). In each 16-lane
@@ -147,12 +162,37 @@ struct FwdState {
   float m_run, l_run;
 };
 
+// Scores of one 32-key block in log2 units, masked to -inf where the key is
+// after the query or past the sequence (MASK: only blocks on the diagonal or
+// at the end need it).
+template <bool MASK, bool AL>
+__device__ __forceinline__ float fwd_scores(const f32x16& sa, const f32x16& sc, float (&x)[16], float scale_log2,
+                                            float slope2, int k0, int g, int myq, int seq) {
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int key = k0 + 8 * (q >> 2) + 4 * g + (q & 3);
+    float v = (sc[q] + sa[q]) * scale_log2;
+    if (AL) v -= slope2 * (float)(myq - key);
+    if (MASK && (key > myq || key >= seq)) v = -INFINITY;
+    x[q] = v;
+    mloc = fmaxf(mloc, v);
+  }
+  return mloc;
+}
+
+// Running softmax with a lazily moved reference: the reference max m_run only
+// moves when a row's max exceeds it by more than 2^8, so weights stay below
+// 2^8 (exact in fp32, in range for bf16) and the output accumulator is
+// rescaled only when some row of the wave moves its reference.
+constexpr float kLazy = 8.0f;
+
 // One 64-key tile from stage `cur` (K hi, K lo, V at 0, TB, 2TB); the loads
 // of the next tile go to `nxt` first.
-template <int D>
+template <int D, bool AL>
 __device__ __forceinline__ void fwd_tile(const MP& p, const char* __restrict__ cur, char* __restrict__ nxt,
                                          bool issue, int kv0, int l, long grow0, int w, int lane, int q0w, int myq,
-                                         float slope2, const TrOff& tro, FwdState<D>& st) {
+                                         float slope2, const TrOff& tro, const RowOff& ro, FwdState<D>& st) {
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
   const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
   if (issue) {
@@ -160,7 +200,7 @@ __device__ __forceinline__ void fwd_tile(const MP& p, const char* __restrict__ c
     dma_tile<D>(p.kl, nrec, nxt + TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
     dma_tile<D>(p.vh, nrec, nxt + 2 * TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
   }
-  const int g = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 5;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
     const int k0 = kv0 + 32 * sb;
@@ -168,39 +208,37 @@ __device__ __forceinline__ void fwd_tile(const MP& p, const char* __restrict__ c
     f32x16 sa = f32x16{}, sc = f32x16{};
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const bf16x8 kh = frag_row(cur, 32 * sb + l32, 2 * c + g);
-      const bf16x8 kl = frag_row(cur + TB, 32 * sb + l32, 2 * c + g);
+      const bf16x8 kh = frag_row(cur, sb, c, ro);
+      const bf16x8 kl = frag_row(cur + TB, sb, c, ro);
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, st.qf[c], sc, 0, 0, 0);
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, st.qfl[c], sc, 0, 0, 0);
       sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, st.qf[c], sa, 0, 0, 0);
     }
     // s[q]: key k0 + 8(q>>2) + 4g + (q&3), query myq
-    const bool need_mask = (k0 + 31 > q0w) || (k0 + 32 > p.seq);
     float x[16];
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int key = k0 + 8 * (q >> 2) + 4 * g + (q & 3);
-      float v = (sc[q] + sa[q]) * p.scale_log2 - slope2 * (float)(myq - key);
-      if (need_mask && (key > myq || key >= p.seq)) v = -INFINITY;
-      x[q] = v;
-      mloc = fmaxf(mloc, v);
-    }
+    float mloc;
+    if ((k0 + 31 > q0w) || (k0 + 32 > p.seq))
+      mloc = fwd_scores<true, AL>(sa, sc, x, p.scale_log2, slope2, k0, g, myq, p.seq);
+    else
+      mloc = fwd_scores<false, AL>(sa, sc, x, p.scale_log2, slope2, k0, g, myq, p.seq);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(st.m_run, mloc);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const bool move = mloc > st.m_run + kLazy;  // also true on a row's first unmasked keys
+    if (__ballot(move)) {                        // wave-uniform
+      const float m_new = move ? mloc : st.m_run;
+      const float corr = move ? fexp2(st.m_run - m_new) : 1.0f;
+      st.l_run *= corr;
+      st.m_run = m_new;
+#pragma unroll
+      for (int db = 0; db < NB; ++db) st.o[db] *= corr;
+    }
+    const float m_use = (st.m_run == -INFINITY) ? 0.f : st.m_run;
     float lloc = 0.f;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      x[q] = exp2f(x[q] - m_use);
+      x[q] = fexp2(x[q] - m_use);
       lloc += x[q];
     }
-    lloc += __shfl_xor(lloc, 32);
-    const float corr = exp2f(st.m_run - m_use);
-    st.l_run = st.l_run * corr + lloc;
-    st.m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < NB; ++db) st.o[db] *= corr;
+    st.l_run += lloc + __shfl_xor(lloc, 32);
     const bf16x8 pf0 = pack8(x), pf1 = pack8(x + 8);
     const char* vt = cur + 2 * TB;
 #pragma unroll
@@ -211,7 +249,7 @@ __device__ __forceinline__ void fwd_tile(const MP& p, const char* __restrict__ c
   }
 }
 
-template <int D>
+template <int D, bool AL>
 __global__ __launch_bounds__(256) void fwd_mfma(MP p) {
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
   __shared__ __attribute__((aligned(16))) char st0[3 * TB];
@@ -248,11 +286,12 @@ __global__ __launch_bounds__(256) void fwd_mfma(MP p) {
   st.l_run = 0.f;
   const float slope2 = alibi_slope_log2(p, l);
   const TrOff tro = tr_offsets(lane);
+  const RowOff ro = row_offsets(lane);
   for (int kt = 0; kt < nkt; ++kt) {
     loads_landed_barrier();  // tile kt is in LDS; tile kt-1 is no longer read
     const bool odd = kt & 1;
-    fwd_tile<D>(p, odd ? st1 : st0, odd ? st0 : st1, kt + 1 < nkt, kt * TROWS, l, grow0, w, lane, q0w, myq, slope2,
-                tro, st);
+    fwd_tile<D, AL>(p, odd ? st1 : st0, odd ? st0 : st1, kt + 1 < nkt, kt * TROWS, l, grow0, w, lane, q0w, myq,
+                    slope2, tro, ro, st);
   }
   if (myq < p.seq) {
     const float inv = 1.0f / st.l_run;
@@ -287,11 +326,35 @@ __device__ __forceinline__ void dma_stats(const MP& p, char* stage_stats, int he
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(stage_stats + 256 * w), 4, vo, 0, 0, 0);
 }
 
+// P and dS of one 32-query block for this lane's key (MASK as in fwd_scores).
+template <bool MASK, bool AL>
+__device__ __forceinline__ void kv_probs(const f32x16& sa, const f32x16& sc, const f32x16& dp, const float* sL,
+                                         const float* sDl, float (&pv)[16], float (&dsv)[16], float scale_log2,
+                                         float slope2, int qs0, int g, int myk, int seq) {
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const f32x4 L = *(const f32x4*)(sL + 8 * q4 + 4 * g);
+    const f32x4 Dl = *(const f32x4*)(sDl + 8 * q4 + 4 * g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int q = 4 * q4 + e;
+      const int query = qs0 + 8 * q4 + 4 * g + e;
+      float v = (sc[q] + sa[q]) * scale_log2 - L[e] * kLog2e;
+      if (AL) v -= slope2 * (float)(query - myk);
+      float pp = fexp2(v);
+      if (MASK && (query < myk || query >= seq)) pp = 0.f;
+      pv[q] = pp;
+      dsv[q] = pp * (dp[q] - Dl[e]);
+    }
+  }
+}
+
 // One 64-query tile from stage `cur` (Q hi, Q lo, dctx, then lse, delta).
-template <int D>
+template <int D, bool AL>
 __device__ __forceinline__ void dkdv_tile(const MP& p, const char* __restrict__ cur, char* __restrict__ nxt,
                                           bool issue, int q0, int head, int l, long grow0, int w, int lane, int k0w,
-                                          int myk, float slope2, const TrOff& tro, KvState<D>& st) {
+                                          int myk, float slope2, const TrOff& tro, const RowOff& ro,
+                                          KvState<D>& st) {
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
   const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
   if (issue) {
@@ -302,7 +365,7 @@ __device__ __forceinline__ void dkdv_tile(const MP& p, const char* __restrict__ 
     dma_stats(p, nxt + 3 * TB, head, qn, w, lane);
   }
   if (k0w >= p.seq) return;
-  const int g = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 5;
   const float* sL = (const float*)(cur + 3 * TB);
   const float* sDl = sL + 64;
 #pragma unroll
@@ -312,30 +375,18 @@ __device__ __forceinline__ void dkdv_tile(const MP& p, const char* __restrict__ 
     f32x16 sa = f32x16{}, sc = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const int row = 32 * qs + l32, ch = 2 * c + g;
-      const bf16x8 qh = frag_row(cur, row, ch), ql = frag_row(cur + TB, row, ch);
+      const bf16x8 qh = frag_row(cur, qs, c, ro), ql = frag_row(cur + TB, qs, c, ro);
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql, st.kf[c], sc, 0, 0, 0);
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, st.kfl[c], sc, 0, 0, 0);
       sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, st.kf[c], sa, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(cur + 2 * TB, row, ch), st.vf[c], dp, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(cur + 2 * TB, qs, c, ro), st.vf[c], dp, 0, 0, 0);
     }
     // s[q], dp[q]: query qs0 + 8(q>>2) + 4g + (q&3), key myk
-    const bool need_mask = (qs0 < k0w + 31) || (qs0 + 32 > p.seq);
     float pv[16], dsv[16];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4 L = *(const f32x4*)(sL + 32 * qs + 8 * q4 + 4 * g);
-      const f32x4 Dl = *(const f32x4*)(sDl + 32 * qs + 8 * q4 + 4 * g);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int q = 4 * q4 + e;
-        const int query = qs0 + 8 * q4 + 4 * g + e;
-        float pp = exp2f((sc[q] + sa[q]) * p.scale_log2 - slope2 * (float)(query - myk) - L[e] * kLog2e);
-        if (need_mask && (query < myk || query >= p.seq)) pp = 0.f;
-        pv[q] = pp;
-        dsv[q] = pp * (dp[q] - Dl[e]);
-      }
-    }
+    if ((qs0 < k0w + 31) || (qs0 + 32 > p.seq))
+      kv_probs<true, AL>(sa, sc, dp, sL + 32 * qs, sDl + 32 * qs, pv, dsv, p.scale_log2, slope2, qs0, g, myk, p.seq);
+    else
+      kv_probs<false, AL>(sa, sc, dp, sL + 32 * qs, sDl + 32 * qs, pv, dsv, p.scale_log2, slope2, qs0, g, myk, p.seq);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const bf16x8 pf = pack8(pv + 8 * h), df = pack8(dsv + 8 * h);
@@ -350,7 +401,7 @@ __device__ __forceinline__ void dkdv_tile(const MP& p, const char* __restrict__ 
   }
 }
 
-template <int D>
+template <int D, bool AL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dkdv_mfma(MP p) {
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2, SB = 3 * TB + 512;
   __shared__ __attribute__((aligned(16))) char st0[SB];
@@ -390,11 +441,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   const float slope2 = alibi_slope_log2(p, l);
   const TrOff tro = tr_offsets(lane);
+  const RowOff ro = row_offsets(lane);
   for (int qt = qt0; qt < nqt; ++qt) {
     loads_landed_barrier();
     const bool odd = (qt - qt0) & 1;
-    dkdv_tile<D>(p, odd ? st1 : st0, odd ? st0 : st1, qt + 1 < nqt, qt * TROWS, head, l, grow0, w, lane, k0w, myk,
-                 slope2, tro, st);
+    dkdv_tile<D, AL>(p, odd ? st1 : st0, odd ? st0 : st1, qt + 1 < nqt, qt * TROWS, head, l, grow0, w, lane, k0w,
+                     myk, slope2, tro, ro, st);
   }
   if (myk < p.seq) {
     const long ld3 = 3L * p.h_l;
@@ -424,11 +476,27 @@ struct QState {
   float L, Dl;
 };
 
+// dS of one 32-key block for this lane's query (MASK as in fwd_scores).
+template <bool MASK, bool AL>
+__device__ __forceinline__ void q_dscores(const f32x16& sa, const f32x16& sc, const f32x16& dp, float (&ds)[16],
+                                          float scale_log2, float slope2, float L, float Dl, int k0, int g, int myq,
+                                          int seq) {
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int key = k0 + 8 * (q >> 2) + 4 * g + (q & 3);
+    float v = (sc[q] + sa[q]) * scale_log2 - L;
+    if (AL) v -= slope2 * (float)(myq - key);
+    float pp = fexp2(v);
+    if (MASK && (key > myq || key >= seq)) pp = 0.f;
+    ds[q] = pp * (dp[q] - Dl);
+  }
+}
+
 // One 64-key tile from stage `cur` (K hi, K lo, V).
-template <int D>
+template <int D, bool AL>
 __device__ __forceinline__ void dq_tile(const MP& p, const char* __restrict__ cur, char* __restrict__ nxt, bool issue,
                                         int kv0, int l, long grow0, int w, int lane, int q0w, int myq, float slope2,
-                                        const TrOff& tro, QState<D>& st) {
+                                        const TrOff& tro, const RowOff& ro, QState<D>& st) {
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
   const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
   if (issue) {
@@ -436,7 +504,7 @@ __device__ __forceinline__ void dq_tile(const MP& p, const char* __restrict__ cu
     dma_tile<D>(p.kl, nrec, nxt + TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
     dma_tile<D>(p.vh, nrec, nxt + 2 * TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
   }
-  const int g = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 5;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
     const int k0 = kv0 + 32 * sb;
@@ -444,23 +512,18 @@ __device__ __forceinline__ void dq_tile(const MP& p, const char* __restrict__ cu
     f32x16 sa = f32x16{}, sc = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const int row = 32 * sb + l32, ch = 2 * c + g;
-      const bf16x8 kh = frag_row(cur, row, ch), kl = frag_row(cur + TB, row, ch);
+      const bf16x8 kh = frag_row(cur, sb, c, ro), kl = frag_row(cur + TB, sb, c, ro);
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, st.qf[c], sc, 0, 0, 0);
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, st.qfl[c], sc, 0, 0, 0);
       sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, st.qf[c], sa, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(cur + 2 * TB, row, ch), st.cf[c], dp, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(cur + 2 * TB, sb, c, ro), st.cf[c], dp, 0, 0, 0);
     }
     // s[q]: key k0 + 8(q>>2) + 4g + (q&3), query myq
-    const bool need_mask = (k0 + 31 > q0w) || (k0 + 32 > p.seq);
     float ds[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int key = k0 + 8 * (q >> 2) + 4 * g + (q & 3);
-      float pp = exp2f((sc[q] + sa[q]) * p.scale_log2 - slope2 * (float)(myq - key) - st.L);
-      if (need_mask && (key > myq || key >= p.seq)) pp = 0.f;
-      ds[q] = pp * (dp[q] - st.Dl);
-    }
+    if ((k0 + 31 > q0w) || (k0 + 32 > p.seq))
+      q_dscores<true, AL>(sa, sc, dp, ds, p.scale_log2, slope2, st.L, st.Dl, k0, g, myq, p.seq);
+    else
+      q_dscores<false, AL>(sa, sc, dp, ds, p.scale_log2, slope2, st.L, st.Dl, k0, g, myq, p.seq);
     const bf16x8 df0 = pack8(ds), df1 = pack8(ds + 8);
 #pragma unroll
     for (int db = 0; db < NB; ++db) {
@@ -470,7 +533,7 @@ __device__ __forceinline__ void dq_tile(const MP& p, const char* __restrict__ cu
   }
 }
 
-template <int D>
+template <int D, bool AL>
 __global__ __launch_bounds__(256) void dq_mfma(MP p) {
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
   __shared__ __attribute__((aligned(16))) char st0[3 * TB];
@@ -509,11 +572,12 @@ __global__ __launch_bounds__(256) void dq_mfma(MP p) {
   for (int db = 0; db < NB; ++db) st.dq[db] = f32x16{};
   const float slope2 = alibi_slope_log2(p, l);
   const TrOff tro = tr_offsets(lane);
+  const RowOff ro = row_offsets(lane);
   for (int kt = 0; kt < nkt; ++kt) {
     loads_landed_barrier();
     const bool odd = kt & 1;
-    dq_tile<D>(p, odd ? st1 : st0, odd ? st0 : st1, kt + 1 < nkt, kt * TROWS, l, grow0, w, lane, q0w, myq, slope2, tro,
-               st);
+    dq_tile<D, AL>(p, odd ? st1 : st0, odd ? st0 : st1, kt + 1 < nkt, kt * TROWS, l, grow0, w, lane, q0w, myq, slope2,
+                   tro, ro, st);
   }
   if (myq < p.seq) {
     bf16* dQ = p.dqkv + (grow0 + myq) * (3L * p.h_l) + (long)l * D;
@@ -583,16 +647,19 @@ MP make_mp(const AttnDesc& a) {
 template <int D>
 hipError_t fwd_d(const MP& p, hipStream_t stream) {
   dim3 grid(p.batch * p.n_local, (p.seq + 127) / 128);
-  hipLaunchKernelGGL(fwd_mfma<D>, grid, dim3(256), 0, stream, p);
+  if (p.alibi) hipLaunchKernelGGL((fwd_mfma<D, true>), grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((fwd_mfma<D, false>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 template <int D>
 hipError_t bwd_d(const MP& p, hipStream_t stream) {
   dim3 grid(p.batch * p.n_local, (p.seq + 127) / 128);
-  hipLaunchKernelGGL(dkdv_mfma<D>, grid, dim3(256), 0, stream, p);
+  if (p.alibi) hipLaunchKernelGGL((dkdv_mfma<D, true>), grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((dkdv_mfma<D, false>), grid, dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dq_mfma<D>, grid, dim3(256), 0, stream, p);
+  if (p.alibi) hipLaunchKernelGGL((dq_mfma<D, true>), grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((dq_mfma<D, false>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
