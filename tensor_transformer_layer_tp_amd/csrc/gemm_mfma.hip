@@ -1,9 +1,12 @@
 // bf16 GEMM on CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16), fp32 accumulation,
 // with the layer's fused epilogues (bias, bias+GeLU, GeLU' scaling, fp32 out).
 //
-// Tiling: a 256x256 output tile per workgroup of 4 waves (2x2), each wave a
-// 128x128 sub-tile = 4x4 MFMA blocks of 32x32 (256 fp32 accumulators per lane,
-// held in AGPRs). K advances 64 at a time through two LDS stages (2 x 64 KiB).
+// Tiling: a 256x256 output tile per workgroup. With 4 waves (2x2) each wave
+// owns a 128x128 sub-tile = 4x4 MFMA blocks of 32x32 (256 fp32 accumulators
+// per lane, one wave per SIMD); with 8 waves (2x4) each owns 128x64 (128
+// accumulators, two waves per SIMD, so one wave's barrier and load waits are
+// covered by the other's MFMAs, and twice as many loads are in flight per CU).
+// K advances 64 at a time through two LDS stages (2 x 64 KiB).
 //
 // Global -> LDS: buffer loads that write LDS directly (16 bytes per lane; one
 // instruction fills 1 KiB in lane order), so no VGPRs stage the tiles. Each
@@ -35,7 +38,18 @@
 namespace tpk {
 namespace {
 
-constexpr int BM = 256, BN = 256, BKK = 64, NTHR = 256;
+constexpr int BM = 256, BN = 256, BKK = 64;
+// Wave layout of a workgroup of NW waves (4: one per SIMD, 8: two per SIMD):
+// 2 waves along m (128 rows each) x NW/2 along n.
+template <int NW>
+struct WC {
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static constexpr int NTHR = 64 * NW;
+  static constexpr int WNG = NW / 2;      // waves along n
+  static constexpr int WNW = BN / WNG;    // columns per wave
+  static constexpr int NJ = WNW / 32;     // 32-column MFMA blocks per wave
+  static constexpr int NLI = 32 / NW;     // loads per operand per wave per k-step
+};
 constexpr int STAGE = BM * BKK;  // bf16 elements per operand per stage
 constexpr int GMAX = 256;        // largest persistent grid (workspace sizing)
 constexpr int GROUP_M = 8;       // tiles along M per raster group
@@ -87,99 +101,78 @@ __device__ __forceinline__ const bf16* uni_ptr(const bf16* p) {
 // One operand panel of a tile: a buffer resource based at the panel's first
 // row (k-inner) or first column (k-outer), and this lane's byte offsets for its
 // 8 load instructions (nrec = out of range: the load writes zeros).
+template <int NW>
 struct Panel {
   const bf16* base;  // workgroup-uniform
   uint32_t nrec;     // workgroup-uniform buffer size in bytes
   uint32_t kstep;    // workgroup-uniform bytes the panel advances per k-step
-  uint32_t voff[8];
-  int prow;          // k-inner: valid rows of the panel (L2 prefetch)
+  uint32_t voff[WC<NW>::NLI];
 };
 
-// k-inner X[r*ld + k], rows r0g.. of `rows`. Instruction i of wave w fills LDS
-// block 8w+i = rows 64w+8i .. +7; lane l lands in row 64w+8i+(l>>3), physical
-// chunk l&7, so it loads logical chunk (l&7) ^ swz(row) = (l&7) ^ (l>>3) ^ i.
-__device__ __forceinline__ Panel panel_kinner(const bf16* X, long ld, int rows, int r0g, int wave, int lane) {
-  Panel pn;
+// k-inner X[r*ld + k], rows r0g.. of `rows`. Load i of wave w fills LDS block
+// b = NLI*w + i = rows 8b .. 8b+7; lane l lands in row 8b+(l>>3), physical
+// chunk l&7, so it loads logical chunk (l&7) ^ swz(row) = (l&7) ^ (l>>3) ^ (b&7).
+template <int NW>
+__device__ __forceinline__ Panel<NW> panel_kinner(const bf16* X, long ld, int rows, int r0g, int wave, int lane) {
+  constexpr int NLI = WC<NW>::NLI;
+  Panel<NW> pn;
   int nrows = rows - r0g;
   nrows = nrows < 256 ? nrows : 256;
   pn.base = uni_ptr(X + (long)r0g * ld);
   pn.nrec = uni((uint32_t)((long)nrows * ld * 2));
   pn.kstep = BKK * 2;
-  pn.prow = nrows;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 64 * wave + 8 * i + (lane >> 3);
-    const int c = (lane & 7) ^ (lane >> 3) ^ i;
+  for (int i = 0; i < NLI; ++i) {
+    const int b = NLI * wave + i;
+    const int r = 8 * b + (lane >> 3);
+    const int c = (lane & 7) ^ (lane >> 3) ^ (b & 7);
     pn.voff[i] = r < nrows ? (uint32_t)(((long)r * ld + 8 * c) * 2) : pn.nrec;
   }
   return pn;
 }
-// k-outer X[k*ld + r], columns r0g.. of `rows`. Instruction i of wave w fills
-// LDS block 8w+i = k-rows 16w+2i, +1; lane l lands in k-row 16w+2i+(l>>5),
+// k-outer X[k*ld + r], columns r0g.. of `rows`. Load i of wave w fills LDS
+// block b = NLI*w + i = k-rows 2b, 2b+1; lane l lands in k-row 2b+(l>>5),
 // physical chunk l&31, so it loads logical chunk (l&31) ^ 4(krow&3). Rows at
 // or past K fall beyond nrec and load zeros.
-__device__ __forceinline__ Panel panel_kouter(const bf16* X, long ld, int rows, int K, int r0g, int wave,
-                                              int lane) {
-  Panel pn;
+template <int NW>
+__device__ __forceinline__ Panel<NW> panel_kouter(const bf16* X, long ld, int rows, int K, int r0g, int wave,
+                                                  int lane) {
+  constexpr int NLI = WC<NW>::NLI;
+  Panel<NW> pn;
   pn.base = uni_ptr(X + r0g);
   pn.nrec = uni((uint32_t)(((long)K * ld - r0g) * 2));
   pn.kstep = uni((uint32_t)(BKK * ld * 2));
-  pn.prow = 256;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int kr = 16 * wave + 2 * i + (lane >> 5);
+  for (int i = 0; i < NLI; ++i) {
+    const int kr = 2 * (NLI * wave + i) + (lane >> 5);
     const int c = (lane & 31) ^ (4 * (kr & 3));
     pn.voff[i] = (r0g + 8 * c < rows) ? (uint32_t)(((long)kr * ld + 8 * c) * 2) : pn.nrec;
   }
   return pn;
 }
 
-// Issue the 8 loads of one operand for k-step kt into LDS stage `dst`.
-template <bool KIN>
-__device__ __forceinline__ void issue_panel(const Panel& pn, int kt, int K, bf16* dst, int wave, int lane) {
+// Issue the NLI loads of one operand for k-step kt into LDS stage `dst`.
+template <int NW, bool KIN>
+__device__ __forceinline__ void issue_panel(const Panel<NW>& pn, int kt, int K, bf16* dst, int wave, int lane) {
+  constexpr int NLI = WC<NW>::NLI;
   const int soff = (int)uni((uint32_t)kt * pn.kstep);
   __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)pn.base, (short)0, (int)pn.nrec, 0x00020000);
   // k tail (k-inner only): chunks at or past K must read zeros, not the next row
   const bool tail = KIN && (kt + 1) * BKK > K;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NLI; ++i) {
+    const int b = NLI * wave + i;
     uint32_t vo = pn.voff[i];
     if (tail) {
-      const int c = (lane & 7) ^ (lane >> 3) ^ i;
+      const int c = (lane & 7) ^ (lane >> 3) ^ (b & 7);
       if (kt * BKK + 8 * c >= K) vo = pn.nrec;
     }
-    bf16* blk = dst + (8 * wave + i) * 512;  // 1 KiB block, wave-uniform
+    bf16* blk = dst + b * 512;  // 1 KiB block, wave-uniform
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)blk, 16, vo, soff, 0, 0);
   }
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-#ifndef TP_GEMM_PF_DIST
-#define TP_GEMM_PF_DIST 0
-#endif
-// L2 prefetch distance in k-steps (0: off).
-constexpr int PF_DIST = TP_GEMM_PF_DIST;
-// All but the most recent loads (this wave's L2 prefetches, if any) have landed.
-__device__ __forceinline__ void wait_vmem_but_prefetch() {
-  if (PF_DIST > 0) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
-// L2 prefetch of k-step kt of a panel, PF_DIST steps ahead of its LDS loads:
-// every thread touches one 128-byte line (k-inner: row tid; k-outer: k-row
-// tid/4, quarter tid%4) with a 4-byte load into a scratch LDS word, so no
-// VGPR is written. Past the tile's last k-step it reads nothing (offset nrec).
-template <bool KIN>
-__device__ __forceinline__ void prefetch_panel(const Panel& pn, int kt, int ke, long ld, int* __restrict__ scratch,
-                                               int tid) {
-  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)pn.base, (short)0, (int)pn.nrec, 0x00020000);
-  const int soff = (int)uni((uint32_t)kt * pn.kstep);
-  uint32_t vo;
-  if (KIN) vo = tid < pn.prow ? (uint32_t)((long)tid * ld * 2) : pn.nrec;
-  else vo = (uint32_t)(((long)(tid >> 2) * ld + 64 * (tid & 3)) * 2);
-  if (kt >= ke) vo = pn.nrec;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)scratch, 4, vo, soff, 0, 0);
-}
 
 // ---- fragment reads ------------------------------------------------------------
 // k-inner: 32-row block i of this wave's 128 rows; lane owns row base+32i+(l&31)
@@ -209,29 +202,32 @@ __device__ __forceinline__ bf16x8 frag_kout(const bf16* s, int lane_off, int kk)
 // ---- main loop over k-iterations [kb, ke) of one tile -------------------------
 // One k-step: wait for this wave's loads into the current stage, barrier (all
 // loads landed; everyone finished reading the other stage), issue the next
-// k-step's loads into the other stage, then 4 x 16 MFMAs from the current
-// stage with the next sub-step's fragments read ahead. The stage pointers are
-// __restrict__: the two stages never overlap, and the no-alias information
-// lets the compiler's wait-count pass leave the in-flight LDS writes (other
-// stage) outstanding while the fragment reads (this stage) proceed.
-template <bool AK, bool BKM>
-__device__ __forceinline__ void kstep(const KParams& p, const Panel& pa, const Panel& pb, int kt, int ke,
+// k-step's loads into the other stage, then 4 sub-steps of 4 x NJ MFMAs from
+// the current stage with the next sub-step's fragments read ahead. The stage
+// pointers are __restrict__: the two stages never overlap, and the no-alias
+// information lets the compiler's wait-count pass leave the in-flight LDS
+// writes (other stage) outstanding while the fragment reads (this stage)
+// proceed.
+template <int NW, bool AK, bool BKM>
+__device__ __forceinline__ void kstep(const KParams& p, const Panel<NW>& pa, const Panel<NW>& pb, int kt,
                                       const bf16* __restrict__ a, const bf16* __restrict__ b,
-                                      bf16* __restrict__ na, bf16* __restrict__ nb, int wave, int lane,
-                                      int rowA, int rowB, const int (&offA)[4], const int (&offB)[4], int s1, int g,
-                                      f32x16 (&acc)[4][4], int* __restrict__ pfs) {
-  wait_vmem_but_prefetch();
+                                      bf16* __restrict__ na, bf16* __restrict__ nb, int wave, int lane, int rowA,
+                                      int rowB, const int (&offA)[4], const int (&offB)[WC<NW>::NJ], int s1, int g,
+                                      f32x16 (&acc)[4][WC<NW>::NJ]) {
+  constexpr int NJ = WC<NW>::NJ, NLI = WC<NW>::NLI;
+  wait_vmem();
   __syncthreads();
   // Next k-step's loads, unconditionally so that the whole step is one
   // scheduling region: past the last k-step of the tile they read either zeros
   // (k beyond K is out of the buffer's range) or in-range data nobody uses.
-  issue_panel<AK>(pa, kt + 1, p.K, na, wave, lane);
-  issue_panel<BKM>(pb, kt + 1, p.K, nb, wave, lane);
-  bf16x8 af[2][4], bfg[2][4];
+  issue_panel<NW, AK>(pa, kt + 1, p.K, na, wave, lane);
+  issue_panel<NW, BKM>(pb, kt + 1, p.K, nb, wave, lane);
+  // fragments read in the order a0, b0, a1, b1, ...
+  bf16x8 af[2][4], bfg[2][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     af[0][i] = AK ? frag_kin(a, rowA, s1, g, 0, i) : frag_kout(a, offA[i], 0);
-    bfg[0][i] = BKM ? frag_kin(b, rowB, s1, g, 0, i) : frag_kout(b, offB[i], 0);
+    if (i < NJ) bfg[0][i] = BKM ? frag_kin(b, rowB, s1, g, 0, i) : frag_kout(b, offB[i], 0);
   }
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -240,73 +236,65 @@ __device__ __forceinline__ void kstep(const KParams& p, const Panel& pa, const P
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         af[n][i] = AK ? frag_kin(a, rowA, s1, g, kk + 1, i) : frag_kout(a, offA[i], kk + 1);
-        bfg[n][i] = BKM ? frag_kin(b, rowB, s1, g, kk + 1, i) : frag_kout(b, offB[i], kk + 1);
+        if (i < NJ) bfg[n][i] = BKM ? frag_kin(b, rowB, s1, g, kk + 1, i) : frag_kout(b, offB[i], kk + 1);
       }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
         // operands swapped: D[n][m], so each lane ends up owning one m and
         // runs of 4 consecutive n (vector stores in the epilogue)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[c][j], af[c][i], acc[i][j], 0, 0, 0);
   }
   // Instruction order for the step: the first sub-step's fragment reads, then
-  // each MFMA followed by one read of the next sub-step's fragments and (in
-  // the first sub-step) one of the 16 loads of the next k-step.
-  constexpr int R = (AK ? 4 : 8) + (BKM ? 4 : 8);  // LDS reads per sub-step
+  // the MFMAs with the next sub-step's fragment reads spread evenly between
+  // them and (in the first sub-step) the next k-step's 2*NLI loads.
+  constexpr int R = (AK ? 4 : 8) + (BKM ? NJ : 2 * NJ);  // LDS reads per sub-step
+  constexpr int NM = 4 * NJ;                              // MFMAs per sub-step
   __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
+    for (int m = 0; m < NM; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (kk < 3 && m < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (kk == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      const int nr = (R * (m + 1)) / NM - (R * m) / NM;
+      if (kk < 3)
+#pragma unroll
+        for (int t = 0; t < nr; ++t) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      const int nv = (2 * NLI * (m + 1)) / NM - (2 * NLI * m) / NM;
+      if (kk == 0)
+#pragma unroll
+        for (int t = 0; t < nv; ++t) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
-  // The L2 prefetches go last, after a scheduling fence, so that they are the
-  // two youngest loads when the next step waits for this step's LDS loads.
-  if (PF_DIST > 0) {
-    __builtin_amdgcn_sched_barrier(0);
-    prefetch_panel<AK>(pa, kt + PF_DIST, ke, p.lda, pfs, threadIdx.x);
-    prefetch_panel<BKM>(pb, kt + PF_DIST, ke, p.ldb, pfs, threadIdx.x);
-  }
 }
 
-template <bool AK, bool BKM>
+template <int NW, bool AK, bool BKM>
 __device__ __forceinline__ void mainloop(const KParams& p, int tm, int tn, int kb, int ke,
-                                         f32x16 (&acc)[4][4], bf16* sA0, bf16* sA1, bf16* sB0, bf16* sB1,
-                                         int* pfs) {
+                                         f32x16 (&acc)[4][WC<NW>::NJ], bf16* sA0, bf16* sA1, bf16* sB0, bf16* sB1) {
+  constexpr int NJ = WC<NW>::NJ, WNG = WC<NW>::WNG, WNW = WC<NW>::WNW;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = (int)uni((uint32_t)(tid >> 6));
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WNG, wn = wave % WNG;
   const int g = lane >> 5, l32 = lane & 31;
   const int s1 = (l32 & 7) ^ (l32 >> 3);
-  Panel pa, pb;
-  if (AK) pa = panel_kinner(p.A, p.lda, p.M, tm * BM, wave, lane);
-  else pa = panel_kouter(p.A, p.lda, p.M, p.K, tm * BM, wave, lane);
-  if (BKM) pb = panel_kinner(p.B, p.ldb, p.N, tn * BN, wave, lane);
-  else pb = panel_kouter(p.B, p.ldb, p.N, p.K, tn * BN, wave, lane);
-  const int rowA = (wm * 128 + l32) * BKK, rowB = (wn * 128 + l32) * BKK;
-  int offA[4], offB[4];
+  Panel<NW> pa, pb;
+  if (AK) pa = panel_kinner<NW>(p.A, p.lda, p.M, tm * BM, wave, lane);
+  else pa = panel_kouter<NW>(p.A, p.lda, p.M, p.K, tm * BM, wave, lane);
+  if (BKM) pb = panel_kinner<NW>(p.B, p.ldb, p.N, tn * BN, wave, lane);
+  else pb = panel_kouter<NW>(p.B, p.ldb, p.N, p.K, tn * BN, wave, lane);
+  const int rowA = (wm * 128 + l32) * BKK, rowB = (wn * WNW + l32) * BKK;
+  int offA[4], offB[NJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    offA[j] = AK ? 0 : kout_lane_off(wm * 128, j, lane);
-    offB[j] = BKM ? 0 : kout_lane_off(wn * 128, j, lane);
-  }
-  issue_panel<AK>(pa, kb, p.K, sA0, wave, lane);
-  issue_panel<BKM>(pb, kb, p.K, sB0, wave, lane);
-  // steps kb+1 .. kb+PF_DIST-1 are prefetched here, the rest one per step; the
-  // last two loads issued are always prefetches (see wait_vmem_but_prefetch)
+  for (int i = 0; i < 4; ++i) offA[i] = AK ? 0 : kout_lane_off(wm * 128, i, lane);
 #pragma unroll
-  for (int d = 1; d < PF_DIST; ++d) {
-    prefetch_panel<AK>(pa, kb + d, ke, p.lda, pfs, tid);
-    prefetch_panel<BKM>(pb, kb + d, ke, p.ldb, pfs, tid);
-  }
+  for (int j = 0; j < NJ; ++j) offB[j] = BKM ? 0 : kout_lane_off(wn * WNW, j, lane);
+  issue_panel<NW, AK>(pa, kb, p.K, sA0, wave, lane);
+  issue_panel<NW, BKM>(pb, kb, p.K, sB0, wave, lane);
   for (int kt = kb; kt < ke; ++kt) {
     const bool odd = (kt - kb) & 1;
-    kstep<AK, BKM>(p, pa, pb, kt, ke, odd ? sA1 : sA0, odd ? sB1 : sB0, odd ? sA0 : sA1, odd ? sB0 : sB1, wave,
-                   lane, rowA, rowB, offA, offB, s1, g, acc, pfs);
+    kstep<NW, AK, BKM>(p, pa, pb, kt, odd ? sA1 : sA0, odd ? sB1 : sB0, odd ? sA0 : sA1, odd ? sB0 : sB1, wave, lane,
+                   rowA, rowB, offA, offB, s1, g, acc);
   }
   wait_vmem();      // the last step's read-ahead loads have landed
   __syncthreads();  // LDS is reused by the next work item
@@ -321,18 +309,20 @@ __device__ __forceinline__ void store_bf16x4(bf16* dst, const float (&v)[4]) {
 }
 
 // Row block i (rows 32i..32i+31 of each wave's 128) of a tile.
-template <int EPI>
-__device__ __forceinline__ void epilogue_rows(const KParams& p, int tm, int tn, int i, const f32x16 (&acc)[4]) {
+template <int NW, int EPI>
+__device__ __forceinline__ void epilogue_rows(const KParams& p, int tm, int tn, int i,
+                                              const f32x16 (&acc)[WC<NW>::NJ]) {
+  constexpr int NJ = WC<NW>::NJ, WNG = WC<NW>::WNG, WNW = WC<NW>::WNW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WNG, wn = wave % WNG;
   {
     const int m = tm * BM + wm * 128 + i * 32 + (lane & 31);
     if (m >= p.M) return;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int n = tn * BN + wn * 128 + j * 32 + q4 * 8 + (lane >> 5) * 4;
+        const int n = tn * BN + wn * WNW + j * 32 + q4 * 8 + (lane >> 5) * 4;
         if (n >= p.N) continue;
         float v[4] = {acc[j][4 * q4], acc[j][4 * q4 + 1], acc[j][4 * q4 + 2], acc[j][4 * q4 + 3]};
         if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_F32) {
@@ -361,10 +351,10 @@ __device__ __forceinline__ void epilogue_rows(const KParams& p, int tm, int tn, 
   }
 }
 
-template <int EPI>
-__device__ __forceinline__ void epilogue(const KParams& p, int tm, int tn, const f32x16 (&acc)[4][4]) {
+template <int NW, int EPI>
+__device__ __forceinline__ void epilogue(const KParams& p, int tm, int tn, const f32x16 (&acc)[4][WC<NW>::NJ]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) epilogue_rows<EPI>(p, tm, tn, i, acc[i]);
+  for (int i = 0; i < 4; ++i) epilogue_rows<NW, EPI>(p, tm, tn, i, acc[i]);
 }
 
 // ---- stream-K bookkeeping -----------------------------------------------------
@@ -379,16 +369,19 @@ __device__ __forceinline__ long long sk_owner(long long x, long long base, long 
 }
 
 // Partial tiles are stored in accumulator order: float4 f4 of thread tid at
-// (f4*256 + tid)*4, so each store/load instruction covers 4 KiB contiguously.
-__device__ __forceinline__ void store_partial(float* slot, const f32x16 (&acc)[4][4]) {
+// (f4*NTHR + tid)*4, so each store/load instruction covers NTHR*16 bytes
+// contiguously.
+template <int NW>
+__device__ __forceinline__ void store_partial(float* slot, const f32x16 (&acc)[4][WC<NW>::NJ]) {
+  constexpr int NJ = WC<NW>::NJ, NTHR = WC<NW>::NTHR;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int f4 = (i * 4 + j) * 4 + q4;
+        const int f4 = (i * NJ + j) * 4 + q4;
         f32x4 v = {acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]};
         *(f32x4*)(slot + ((long)f4 * NTHR + tid) * 4) = v;
       }
@@ -397,8 +390,9 @@ __device__ __forceinline__ void store_partial(float* slot, const f32x16 (&acc)[4
 // One loop over this workgroup's work items: first its data-parallel tiles,
 // then its run of stream-K iterations (whole tiles in the run are stored
 // directly, partial tiles go to the workspace).
-template <bool AK, bool BKM, int EPI>
-__device__ __forceinline__ void gemm_body(const KParams& p, bf16* sA0, bf16* sA1, bf16* sB0, bf16* sB1, int* pfs) {
+template <int NW, bool AK, bool BKM, int EPI>
+__device__ __forceinline__ void gemm_body(const KParams& p, bf16* sA0, bf16* sA1, bf16* sB0, bf16* sB1) {
+  constexpr int NJ = WC<NW>::NJ;
   const int lw = logical_wg(blockIdx.x, p.grid);
   const bool in_sk = p.sk_total > 0 && lw < p.sk_grid;
   long long base = 0, rem = 0, s = 0, e = 0;
@@ -428,26 +422,27 @@ __device__ __forceinline__ void gemm_body(const KParams& p, bf16* sA0, bf16* sA1
     }
     int tm, tn;
     tile_coords(p, t, tm, tn);
-    f32x16 acc[4][4];
+    f32x16 acc[4][NJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-    mainloop<AK, BKM>(p, tm, tn, kb, ke, acc, sA0, sA1, sB0, sB1, pfs);
+      for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
+    mainloop<NW, AK, BKM>(p, tm, tn, kb, ke, acc, sA0, sA1, sB0, sB1);
     if (kb == 0 && ke == p.iters) {
-      epilogue<EPI>(p, tm, tn, acc);
+      epilogue<NW, EPI>(p, tm, tn, acc);
     } else {
       const long long t0 = (long long)t * p.iters - p.sk_begin;  // tile start, SK-relative
       const int slot = 2 * lw + (s >= t0 ? 0 : 1);
-      store_partial(p.partials + (long)slot * BM * BN, acc);
+      store_partial<NW>(p.partials + (long)slot * BM * BN, acc);
     }
   }
 }
 
 // Stream-K fix-up: sum each split tile's partials in contributor order and
 // apply the epilogue.
-template <int EPI>
+template <int NW, int EPI>
 __device__ __forceinline__ void fixup_body(const KParams& p, int first_tile) {
+  constexpr int NJ = WC<NW>::NJ, NTHR = WC<NW>::NTHR;
   // four workgroups per tile, one per row block i of the waves' sub-tiles
   const int t = first_tile + blockIdx.x / 4, i = blockIdx.x % 4;
   const long long base = p.sk_total / p.sk_grid, rem = p.sk_total % p.sk_grid;
@@ -455,17 +450,17 @@ __device__ __forceinline__ void fixup_body(const KParams& p, int first_tile) {
   const long long c0 = sk_owner(t0, base, rem), c1 = sk_owner(t0 + p.iters - 1, base, rem);
   if (c0 == c1) return;  // one workgroup covered the whole tile and stored it
   const int tid = threadIdx.x;
-  f32x16 acc[4];
+  f32x16 acc[NJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = f32x16{};
+  for (int j = 0; j < NJ; ++j) acc[j] = f32x16{};
   for (long long c = c0; c <= c1; ++c) {
     const int slot = (int)(2 * c + (sk_start(c, base, rem) >= t0 ? 0 : 1));
     const float* src = p.partials + (long)slot * BM * BN;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int f4 = (i * 4 + j) * 4 + q4;
+        const int f4 = (i * NJ + j) * 4 + q4;
         f32x4 v = *(const f32x4*)(src + ((long)f4 * NTHR + tid) * 4);
         acc[j][4 * q4] += v[0];
         acc[j][4 * q4 + 1] += v[1];
@@ -475,42 +470,44 @@ __device__ __forceinline__ void fixup_body(const KParams& p, int first_tile) {
   }
   int tm, tn;
   tile_coords(p, t, tm, tn);
-  epilogue_rows<EPI>(p, tm, tn, i, acc);
+  epilogue_rows<NW, EPI>(p, tm, tn, i, acc);
 }
 
 }  // namespace
 
 // One kernel (and its stream-K fix-up kernel) per product of the layer, so
 // that a trace attributes time to each step by name.
-#define TP_GEMM_KERNELS(NAME, AKV, BKV, EV)                                           \
-  __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))     \
-  void NAME(KParams p) {                                                            \
-    __shared__ __attribute__((aligned(16))) bf16 sA0[STAGE];                        \
-    __shared__ __attribute__((aligned(16))) bf16 sA1[STAGE];                        \
-    __shared__ __attribute__((aligned(16))) bf16 sB0[STAGE];                        \
-    __shared__ __attribute__((aligned(16))) bf16 sB1[STAGE];                        \
-    __shared__ __attribute__((aligned(16))) int pfs[64];                            \
-    gemm_body<AKV, BKV, EV>(p, sA0, sA1, sB0, sB1, pfs);                            \
-  }                                                                                 \
-  __global__ __launch_bounds__(NTHR) void NAME##_fixup(KParams p, int first_tile) { \
-    fixup_body<EV>(p, first_tile);                                                  \
+#define TP_GEMM_KERNELS(NAME, NWV, AKV, BKV, EV)                                      \
+  __global__ __launch_bounds__(64 * NWV)                                              \
+  __attribute__((amdgpu_waves_per_eu(NWV / 4, NWV / 4))) void NAME(KParams p) {       \
+    __shared__ __attribute__((aligned(16))) bf16 sA0[STAGE];                          \
+    __shared__ __attribute__((aligned(16))) bf16 sA1[STAGE];                          \
+    __shared__ __attribute__((aligned(16))) bf16 sB0[STAGE];                          \
+    __shared__ __attribute__((aligned(16))) bf16 sB1[STAGE];                          \
+    gemm_body<NWV, AKV, BKV, EV>(p, sA0, sA1, sB0, sB1);                              \
+  }                                                                                   \
+  __global__ __launch_bounds__(64 * NWV) void NAME##_fixup(KParams p, int first_tile) { \
+    fixup_body<NWV, EV>(p, first_tile);                                               \
   }
 
+// Products with a k-inner A (activations of the forward products, input
+// gradients) run 8 waves per workgroup (two per SIMD); the weight gradients
+// (both operands read through transposing LDS loads) run 4.
 // forward products: A k-inner (activations), B k-outer (weights)
-TP_GEMM_KERNELS(gemm_qkv_proj, true, false, EPI_BIAS_F32)
-TP_GEMM_KERNELS(gemm_out_proj, true, false, EPI_STORE)
-TP_GEMM_KERNELS(gemm_fc1_bias_gelu, true, false, EPI_BIAS_GELU)
-TP_GEMM_KERNELS(gemm_fc2, true, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_qkv_proj, 8, true, false, EPI_BIAS_F32)
+TP_GEMM_KERNELS(gemm_out_proj, 8, true, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_fc1_bias_gelu, 8, true, false, EPI_BIAS_GELU)
+TP_GEMM_KERNELS(gemm_fc2, 8, true, false, EPI_STORE)
 // input gradients: both k-inner (weights read transposed)
-TP_GEMM_KERNELS(gemm_fc2_dgrad_gelu, true, true, EPI_DGELU)
-TP_GEMM_KERNELS(gemm_fc1_dgrad, true, true, EPI_STORE)
-TP_GEMM_KERNELS(gemm_out_dgrad, true, true, EPI_STORE)
-TP_GEMM_KERNELS(gemm_qkv_dgrad, true, true, EPI_STORE)
+TP_GEMM_KERNELS(gemm_fc2_dgrad_gelu, 8, true, true, EPI_DGELU)
+TP_GEMM_KERNELS(gemm_fc1_dgrad, 8, true, true, EPI_STORE)
+TP_GEMM_KERNELS(gemm_out_dgrad, 8, true, true, EPI_STORE)
+TP_GEMM_KERNELS(gemm_qkv_dgrad, 8, true, true, EPI_STORE)
 // weight gradients: both k-outer (K = tokens)
-TP_GEMM_KERNELS(gemm_fc2_wgrad, false, false, EPI_STORE)
-TP_GEMM_KERNELS(gemm_fc1_wgrad, false, false, EPI_STORE)
-TP_GEMM_KERNELS(gemm_out_wgrad, false, false, EPI_STORE)
-TP_GEMM_KERNELS(gemm_qkv_wgrad, false, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_fc2_wgrad, 4, false, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_fc1_wgrad, 4, false, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_out_wgrad, 4, false, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_qkv_wgrad, 4, false, false, EPI_STORE)
 #undef TP_GEMM_KERNELS
 
 namespace {
@@ -585,7 +582,7 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
   }
   p.grid = pl.grid; p.dp_rounds = pl.dp_rounds; p.sk_grid = pl.sk_grid;
   p.sk_begin = pl.sk_begin; p.sk_total = pl.sk_total;
-  dim3 grid(pl.grid), block(NTHR);
+  dim3 grid(pl.grid);
   const int first = pl.sk_first_tile, nsk = pl.sk_tiles;
   const bool sk = pl.sk_total > 0;
   typedef void (*MainK)(KParams);
@@ -593,26 +590,27 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
   MainK mk = nullptr;
   FixK fk = nullptr;
   bool ak = true, bk = false;
-  int ep = EPI_STORE;
-#define TP_ROLE(R, NAME, AKV, BKV, EV) \
-  case R: mk = NAME; fk = NAME##_fixup; ak = AKV; bk = BKV; ep = EV; break;
+  int ep = EPI_STORE, nw = 4;
+#define TP_ROLE(R, NAME, NWV, AKV, BKV, EV) \
+  case R: mk = NAME; fk = NAME##_fixup; nw = NWV; ak = AKV; bk = BKV; ep = EV; break;
   switch (g.role) {
-    TP_ROLE(GR_QKV_PROJ, gemm_qkv_proj, true, false, EPI_BIAS_F32)
-    TP_ROLE(GR_OUT_PROJ, gemm_out_proj, true, false, EPI_STORE)
-    TP_ROLE(GR_FC1, gemm_fc1_bias_gelu, true, false, EPI_BIAS_GELU)
-    TP_ROLE(GR_FC2, gemm_fc2, true, false, EPI_STORE)
-    TP_ROLE(GR_FC2_DGRAD, gemm_fc2_dgrad_gelu, true, true, EPI_DGELU)
-    TP_ROLE(GR_FC1_DGRAD, gemm_fc1_dgrad, true, true, EPI_STORE)
-    TP_ROLE(GR_OUT_DGRAD, gemm_out_dgrad, true, true, EPI_STORE)
-    TP_ROLE(GR_QKV_DGRAD, gemm_qkv_dgrad, true, true, EPI_STORE)
-    TP_ROLE(GR_FC2_WGRAD, gemm_fc2_wgrad, false, false, EPI_STORE)
-    TP_ROLE(GR_FC1_WGRAD, gemm_fc1_wgrad, false, false, EPI_STORE)
-    TP_ROLE(GR_OUT_WGRAD, gemm_out_wgrad, false, false, EPI_STORE)
-    TP_ROLE(GR_QKV_WGRAD, gemm_qkv_wgrad, false, false, EPI_STORE)
+    TP_ROLE(GR_QKV_PROJ, gemm_qkv_proj, 8, true, false, EPI_BIAS_F32)
+    TP_ROLE(GR_OUT_PROJ, gemm_out_proj, 8, true, false, EPI_STORE)
+    TP_ROLE(GR_FC1, gemm_fc1_bias_gelu, 8, true, false, EPI_BIAS_GELU)
+    TP_ROLE(GR_FC2, gemm_fc2, 8, true, false, EPI_STORE)
+    TP_ROLE(GR_FC2_DGRAD, gemm_fc2_dgrad_gelu, 8, true, true, EPI_DGELU)
+    TP_ROLE(GR_FC1_DGRAD, gemm_fc1_dgrad, 8, true, true, EPI_STORE)
+    TP_ROLE(GR_OUT_DGRAD, gemm_out_dgrad, 8, true, true, EPI_STORE)
+    TP_ROLE(GR_QKV_DGRAD, gemm_qkv_dgrad, 8, true, true, EPI_STORE)
+    TP_ROLE(GR_FC2_WGRAD, gemm_fc2_wgrad, 4, false, false, EPI_STORE)
+    TP_ROLE(GR_FC1_WGRAD, gemm_fc1_wgrad, 4, false, false, EPI_STORE)
+    TP_ROLE(GR_OUT_WGRAD, gemm_out_wgrad, 4, false, false, EPI_STORE)
+    TP_ROLE(GR_QKV_WGRAD, gemm_qkv_wgrad, 4, false, false, EPI_STORE)
     default: return hipErrorInvalidValue;
   }
 #undef TP_ROLE
   if (g.a_kmajor != ak || g.b_kmajor != bk || g.epi != ep) return hipErrorInvalidValue;
+  const dim3 block(64 * nw);
   hipLaunchKernelGGL(mk, grid, block, 0, stream, p);
   hipError_t e1 = hipGetLastError();
   if (e1 != hipSuccess || !sk) return e1;
