@@ -69,7 +69,8 @@ struct KParams {
   bf16* C2; long ldc2;
   const bf16* bias;
   const bf16* aux; long ldaux;
-  float* partials;    // [2*sk_grid][BM*BN]
+  float* partials;    // [2*sk_grid][BM*BN] (split-K: [splits*tiles][BM*BN])
+  int splits;         // > 1: split-K mode, workgroup (s, t) takes k-range s of tile t
 };
 
 __device__ __forceinline__ int logical_wg(int w, int g) {
@@ -394,6 +395,24 @@ template <int NW, bool AK, bool BKM, int EPI>
 __device__ __forceinline__ void gemm_body(const KParams& p, bf16* sA0, bf16* sA1, bf16* sB0, bf16* sB1) {
   constexpr int NJ = WC<NW>::NJ;
   const int lw = logical_wg(blockIdx.x, p.grid);
+  if (p.splits > 1) {
+    // Split-K for problems with few tiles: consecutive workgroups (one XCD)
+    // take the same k-range of neighbouring tiles, so they share panels in L2.
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int t = lw % tiles, sidx = lw / tiles;
+    const int kb = (int)((long long)sidx * p.iters / p.splits);
+    const int ke = (int)((long long)(sidx + 1) * p.iters / p.splits);
+    int tm, tn;
+    tile_coords(p, t, tm, tn);
+    f32x16 acc[4][NJ];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
+    mainloop<NW, AK, BKM>(p, tm, tn, kb, ke, acc, sA0, sA1, sB0, sB1);
+    store_partial<NW>(p.partials + (long)lw * BM * BN, acc);
+    return;
+  }
   const bool in_sk = p.sk_total > 0 && lw < p.sk_grid;
   long long base = 0, rem = 0, s = 0, e = 0;
   if (in_sk) {
@@ -445,11 +464,35 @@ __device__ __forceinline__ void fixup_body(const KParams& p, int first_tile) {
   constexpr int NJ = WC<NW>::NJ, NTHR = WC<NW>::NTHR;
   // four workgroups per tile, one per row block i of the waves' sub-tiles
   const int t = first_tile + blockIdx.x / 4, i = blockIdx.x % 4;
+  const int tid = threadIdx.x;
+  if (p.splits > 1) {  // split-K: the tile's partials are slots t, t + tiles, ...
+    const int tiles = p.tiles_m * p.tiles_n;
+    f32x16 acc[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[j] = f32x16{};
+    for (int sidx = 0; sidx < p.splits; ++sidx) {
+      const float* src = p.partials + (long)(sidx * tiles + t) * BM * BN;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int f4 = (i * NJ + j) * 4 + q4;
+          f32x4 v = *(const f32x4*)(src + ((long)f4 * NTHR + tid) * 4);
+          acc[j][4 * q4] += v[0];
+          acc[j][4 * q4 + 1] += v[1];
+          acc[j][4 * q4 + 2] += v[2];
+          acc[j][4 * q4 + 3] += v[3];
+        }
+    }
+    int tm, tn;
+    tile_coords(p, t, tm, tn);
+    epilogue_rows<NW, EPI>(p, tm, tn, i, acc);
+    return;
+  }
   const long long base = p.sk_total / p.sk_grid, rem = p.sk_total % p.sk_grid;
   const long long t0 = (long long)t * p.iters - p.sk_begin;
   const long long c0 = sk_owner(t0, base, rem), c1 = sk_owner(t0 + p.iters - 1, base, rem);
   if (c0 == c1) return;  // one workgroup covered the whole tile and stored it
-  const int tid = threadIdx.x;
   f32x16 acc[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) acc[j] = f32x16{};
@@ -515,11 +558,22 @@ namespace {
 struct Plan {
   int grid, dp_rounds, sk_grid, sk_first_tile, sk_tiles;
   long long sk_begin, sk_total;
+  int splits;
 };
 
 Plan make_plan(int tiles, int iters, int ncu) {
   Plan pl{};
   ncu = ncu < GMAX ? ncu : GMAX;
+  pl.splits = 1;
+  if (2 * tiles <= ncu && iters >= 16) {
+    // few tiles: split K evenly (at least 8 k-steps per piece)
+    int sp = ncu / tiles;
+    if (sp > iters / 8) sp = iters / 8;
+    pl.splits = sp;
+    pl.grid = tiles * sp;
+    pl.sk_tiles = tiles;  // every tile is finished by the fix-up kernel
+    return pl;
+  }
   const int waves = (tiles + ncu - 1) / ncu;
   const double eff_dp = (double)tiles / ((double)waves * ncu);
   if (iters < 8 || eff_dp >= 0.9) {
@@ -574,17 +628,19 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
   p.bias = (const bf16*)g.bias;
   p.aux = (const bf16*)g.aux; p.ldaux = g.ldaux;
   p.partials = (float*)ws;
+  p.splits = 1;
   const int tiles = p.tiles_m * p.tiles_n;
   Plan pl = make_plan(tiles, p.iters, device_cus());
-  if (pl.sk_total > 0) {
-    const size_t need = (size_t)2 * pl.sk_grid * BM * BN * sizeof(float);
-    if (ws == nullptr || ws_bytes < need) pl = Plan{tiles, 1, 0, 0, 0, 0, 0};  // data-parallel only
+  if (pl.sk_total > 0 || pl.splits > 1) {
+    const size_t slots = pl.splits > 1 ? (size_t)pl.splits * tiles : (size_t)2 * pl.sk_grid;
+    if (ws == nullptr || ws_bytes < slots * BM * BN * sizeof(float))
+      pl = Plan{tiles, 1, 0, 0, 0, 0, 0, 1};  // data-parallel only
   }
   p.grid = pl.grid; p.dp_rounds = pl.dp_rounds; p.sk_grid = pl.sk_grid;
-  p.sk_begin = pl.sk_begin; p.sk_total = pl.sk_total;
+  p.sk_begin = pl.sk_begin; p.sk_total = pl.sk_total; p.splits = pl.splits;
   dim3 grid(pl.grid);
   const int first = pl.sk_first_tile, nsk = pl.sk_tiles;
-  const bool sk = pl.sk_total > 0;
+  const bool sk = pl.sk_total > 0 || pl.splits > 1;
   typedef void (*MainK)(KParams);
   typedef void (*FixK)(KParams, int);
   MainK mk = nullptr;
