@@ -69,8 +69,11 @@ struct KParams {
   bf16* C2; long ldc2;
   const bf16* bias;
   const bf16* aux; long ldaux;
-  float* partials;    // [2*sk_grid][BM*BN] (split-K: [splits*tiles][BM*BN])
-  int splits;         // > 1: split-K mode, workgroup (s, t) takes k-range s of tile t
+  float* partials;    // [2*sk_grid][BM*BN] (split tail: [splits*split_tiles][BM*BN])
+  // Split tail (splits > 1, instead of stream-K): after the data-parallel
+  // rounds, workgroup lw < splits*split_tiles takes k-range lw / split_tiles of
+  // tile split_first + lw % split_tiles.
+  int splits, split_first, split_tiles;
 };
 
 __device__ __forceinline__ int logical_wg(int w, int g) {
@@ -396,10 +399,23 @@ __device__ __forceinline__ void gemm_body(const KParams& p, bf16* sA0, bf16* sA1
   constexpr int NJ = WC<NW>::NJ;
   const int lw = logical_wg(blockIdx.x, p.grid);
   if (p.splits > 1) {
-    // Split-K for problems with few tiles: consecutive workgroups (one XCD)
-    // take the same k-range of neighbouring tiles, so they share panels in L2.
-    const int tiles = p.tiles_m * p.tiles_n;
-    const int t = lw % tiles, sidx = lw / tiles;
+    // data-parallel rounds, then the split tail: consecutive workgroups (one
+    // XCD) take the same k-range of neighbouring tiles, so they share panels
+    // in L2
+    for (int r = 0; r < p.dp_rounds; ++r) {
+      const int t = r * p.grid + lw;
+      int tm, tn;
+      tile_coords(p, t, tm, tn);
+      f32x16 acc[4][NJ];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
+      mainloop<NW, AK, BKM>(p, tm, tn, 0, p.iters, acc, sA0, sA1, sB0, sB1);
+      epilogue<NW, EPI>(p, tm, tn, acc);
+    }
+    if (lw >= p.splits * p.split_tiles) return;
+    const int t = p.split_first + lw % p.split_tiles, sidx = lw / p.split_tiles;
     const int kb = (int)((long long)sidx * p.iters / p.splits);
     const int ke = (int)((long long)(sidx + 1) * p.iters / p.splits);
     int tm, tn;
@@ -465,13 +481,12 @@ __device__ __forceinline__ void fixup_body(const KParams& p, int first_tile) {
   // four workgroups per tile, one per row block i of the waves' sub-tiles
   const int t = first_tile + blockIdx.x / 4, i = blockIdx.x % 4;
   const int tid = threadIdx.x;
-  if (p.splits > 1) {  // split-K: the tile's partials are slots t, t + tiles, ...
-    const int tiles = p.tiles_m * p.tiles_n;
+  if (p.splits > 1) {  // split tail: tile t's partials are slots (t - first) + s*split_tiles
     f32x16 acc[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[j] = f32x16{};
     for (int sidx = 0; sidx < p.splits; ++sidx) {
-      const float* src = p.partials + (long)(sidx * tiles + t) * BM * BN;
+      const float* src = p.partials + (long)(sidx * p.split_tiles + t - p.split_first) * BM * BN;
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -561,24 +576,33 @@ struct Plan {
   int splits;
 };
 
+// Data-parallel rounds of ncu tiles; the remaining R tiles, if a partial
+// round would leave many CUs idle, are either split evenly in K over
+// S = ncu / R workgroups each (when that keeps >= 90% of the CUs busy and
+// >= 8 k-steps per piece: better L2 reuse) or dealt out stream-K.
 Plan make_plan(int tiles, int iters, int ncu) {
   Plan pl{};
   ncu = ncu < GMAX ? ncu : GMAX;
   pl.splits = 1;
-  if (2 * tiles <= ncu && iters >= 16) {
-    // few tiles: split K evenly (at least 8 k-steps per piece)
-    int sp = ncu / tiles;
-    if (sp > iters / 8) sp = iters / 8;
-    pl.splits = sp;
-    pl.grid = tiles * sp;
-    pl.sk_tiles = tiles;  // every tile is finished by the fix-up kernel
-    return pl;
-  }
   const int waves = (tiles + ncu - 1) / ncu;
   const double eff_dp = (double)tiles / ((double)waves * ncu);
   if (iters < 8 || eff_dp >= 0.9) {
     pl.grid = tiles; pl.dp_rounds = 1;
     return pl;
+  }
+  const int full0 = tiles / ncu, rem0 = tiles - full0 * ncu;
+  if (rem0 > 0 && iters >= 16) {
+    int sp = ncu / rem0;
+    if (sp > iters / 8) sp = iters / 8;
+    const double eff_tail = (double)(sp * rem0) / ncu;
+    if (sp >= 2 && eff_tail >= 0.9) {
+      pl.splits = sp;
+      pl.dp_rounds = full0;
+      pl.grid = full0 > 0 ? ncu : rem0 * sp;
+      pl.sk_first_tile = full0 * ncu;  // first split tile (fix-up launch)
+      pl.sk_tiles = rem0;
+      return pl;
+    }
   }
   const int full = tiles / ncu;
   pl.grid = ncu;
@@ -632,12 +656,13 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
   const int tiles = p.tiles_m * p.tiles_n;
   Plan pl = make_plan(tiles, p.iters, device_cus());
   if (pl.sk_total > 0 || pl.splits > 1) {
-    const size_t slots = pl.splits > 1 ? (size_t)pl.splits * tiles : (size_t)2 * pl.sk_grid;
+    const size_t slots = pl.splits > 1 ? (size_t)pl.splits * pl.sk_tiles : (size_t)2 * pl.sk_grid;
     if (ws == nullptr || ws_bytes < slots * BM * BN * sizeof(float))
       pl = Plan{tiles, 1, 0, 0, 0, 0, 0, 1};  // data-parallel only
   }
   p.grid = pl.grid; p.dp_rounds = pl.dp_rounds; p.sk_grid = pl.sk_grid;
   p.sk_begin = pl.sk_begin; p.sk_total = pl.sk_total; p.splits = pl.splits;
+  p.split_first = pl.sk_first_tile; p.split_tiles = pl.sk_tiles;
   dim3 grid(pl.grid);
   const int first = pl.sk_first_tile, nsk = pl.sk_tiles;
   const bool sk = pl.sk_total > 0 || pl.splits > 1;
