@@ -25,10 +25,11 @@
 //    the score accumulators produce, so P (or dS) is fed from registers as the
 //    B operand without any shuffle.
 //
-// Forward (workgroup = 4 waves = 128 queries of one head, each wave 32): per
-// 64-key tile, S^T = K Q^T for 32 keys x the wave's 32 queries, so each lane
-// holds one query column and the softmax statistics (max, sum) are per lane,
-// combined with the partner lane 32 away; ctx^T += V^T P^T.
+// Forward (workgroup = 8 waves = 128 queries of one head; a pair of waves
+// shares 32 queries and splits every 64-key tile into its two 32-key halves):
+// S^T = K Q^T for 32 keys x the wave's 32 queries, so each lane holds one
+// query column and the softmax statistics (max, sum) are per lane, combined
+// with the partner lane 32 away; ctx^T += V^T P^T; the pair merges at the end.
 //
 // Backward: dK/dV per 32-key wave (workgroup = 128 keys, looping over 64-query
 // tiles), dQ per 32-query wave (looping over 64-key tiles); both recompute P
@@ -76,17 +77,20 @@ __device__ __forceinline__ float alibi_slope_log2(const MP& p, int l) {
 
 
 // Stage rows [row0, row0 + 64) of columns [col0, col0 + D) of a [T, h_l] bf16
-// array into a chunk-major tile. Wave w loads chunks w, w+4, ...; lane i of a
-// chunk's load lands in slot i, i.e. row i ^ 4(c & 3). Rows at or past seq
-// read zeros (offset beyond the buffer).
-template <int D>
+// array into a chunk-major tile. With NW waves, wave w loads the chunks c with
+// c = w (mod 4), every (NW/4)-th of them starting at c = (w & 3) + 4(w >> 2);
+// lane i of a chunk's load lands in slot i, i.e. row i ^ 4(c & 3). Rows at or
+// past seq read zeros (offset beyond the buffer).
+template <int D, int NW = 4>
 __device__ __forceinline__ void dma_tile(const bf16* arr, uint32_t nrec, char* tile, long grow0, int col0, int row0,
                                          int seq, int h_l, int w, int lane) {
   const __amdgpu_buffer_rsrc_t rs = rsrc(arr, nrec);
+  const int w4 = NW == 4 ? w : (w & 3);
+  const int j0 = NW == 4 ? 0 : (w >> 2);
 #pragma unroll
-  for (int j = 0; j < D / 32; ++j) {
-    const int c = w + 4 * j;
-    const int pos = row0 + (lane ^ (w << 2));  // (c & 3) == w
+  for (int j = j0; j < D / 32; j += NW / 4) {
+    const int c = w4 + 4 * j;
+    const int pos = row0 + (lane ^ (w4 << 2));  // (c & 3) == w4
     const uint32_t vo = pos < seq ? (uint32_t)(((grow0 + pos) * h_l + col0 + 8 * c) * 2) : nrec;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(tile + (c << 10)), 16, vo, 0, 0, 0);
   }
@@ -187,88 +191,86 @@ __device__ __forceinline__ float fwd_scores(const f32x16& sa, const f32x16& sc, 
 // rescaled only when some row of the wave moves its reference.
 constexpr float kLazy = 8.0f;
 
-// One 64-key tile from stage `cur` (K hi, K lo, V at 0, TB, 2TB); the loads
-// of the next tile go to `nxt` first.
+// One 32-key block (keys k0 .. k0 + 31, block sb of the 64-key tile in `cur`:
+// K hi, K lo, V at 0, TB, 2TB) for this wave's 32 queries.
 template <int D, bool AL>
-__device__ __forceinline__ void fwd_tile(const MP& p, const char* __restrict__ cur, char* __restrict__ nxt,
-                                         bool issue, int kv0, int l, long grow0, int w, int lane, int q0w, int myq,
-                                         float slope2, const TrOff& tro, const RowOff& ro, FwdState<D>& st) {
+__device__ __forceinline__ void fwd_block(const MP& p, const char* __restrict__ cur, int k0, int sb, int g,
+                                          int q0w, int myq, float slope2, const TrOff& tro, const RowOff& ro,
+                                          FwdState<D>& st) {
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
-  const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
-  if (issue) {
-    dma_tile<D>(p.kh, nrec, nxt, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
-    dma_tile<D>(p.kl, nrec, nxt + TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
-    dma_tile<D>(p.vh, nrec, nxt + 2 * TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
+  f32x16 sa = f32x16{}, sc = f32x16{};
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const bf16x8 kh = frag_row(cur, sb, c, ro);
+    const bf16x8 kl = frag_row(cur + TB, sb, c, ro);
+    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, st.qf[c], sc, 0, 0, 0);
+    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, st.qfl[c], sc, 0, 0, 0);
+    sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, st.qf[c], sa, 0, 0, 0);
   }
-  const int g = lane >> 5;
+  // s[q]: key k0 + 8(q>>2) + 4g + (q&3), query myq
+  float x[16];
+  float mloc;
+  if ((k0 + 31 > q0w) || (k0 + 32 > p.seq))
+    mloc = fwd_scores<true, AL>(sa, sc, x, p.scale_log2, slope2, k0, g, myq, p.seq);
+  else
+    mloc = fwd_scores<false, AL>(sa, sc, x, p.scale_log2, slope2, k0, g, myq, p.seq);
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  const bool move = mloc > st.m_run + kLazy;  // also true on a row's first unmasked keys
+  if (__ballot(move)) {                        // wave-uniform
+    const float m_new = move ? mloc : st.m_run;
+    const float corr = move ? fexp2(st.m_run - m_new) : 1.0f;
+    st.l_run *= corr;
+    st.m_run = m_new;
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
-    const int k0 = kv0 + 32 * sb;
-    if (k0 > q0w + 31 || k0 >= p.seq) continue;  // wave-uniform: all masked
-    f32x16 sa = f32x16{}, sc = f32x16{};
+    for (int db = 0; db < NB; ++db) st.o[db] *= corr;
+  }
+  const float m_use = (st.m_run == -INFINITY) ? 0.f : st.m_run;
+  float lloc = 0.f;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const bf16x8 kh = frag_row(cur, sb, c, ro);
-      const bf16x8 kl = frag_row(cur + TB, sb, c, ro);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, st.qf[c], sc, 0, 0, 0);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, st.qfl[c], sc, 0, 0, 0);
-      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, st.qf[c], sa, 0, 0, 0);
-    }
-    // s[q]: key k0 + 8(q>>2) + 4g + (q&3), query myq
-    float x[16];
-    float mloc;
-    if ((k0 + 31 > q0w) || (k0 + 32 > p.seq))
-      mloc = fwd_scores<true, AL>(sa, sc, x, p.scale_log2, slope2, k0, g, myq, p.seq);
-    else
-      mloc = fwd_scores<false, AL>(sa, sc, x, p.scale_log2, slope2, k0, g, myq, p.seq);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const bool move = mloc > st.m_run + kLazy;  // also true on a row's first unmasked keys
-    if (__ballot(move)) {                        // wave-uniform
-      const float m_new = move ? mloc : st.m_run;
-      const float corr = move ? fexp2(st.m_run - m_new) : 1.0f;
-      st.l_run *= corr;
-      st.m_run = m_new;
+  for (int q = 0; q < 16; ++q) {
+    x[q] = fexp2(x[q] - m_use);
+    lloc += x[q];
+  }
+  st.l_run += lloc + __shfl_xor(lloc, 32);
+  const bf16x8 pf0 = pack8(x), pf1 = pack8(x + 8);
+  const char* vt = cur + 2 * TB;
 #pragma unroll
-      for (int db = 0; db < NB; ++db) st.o[db] *= corr;
-    }
-    const float m_use = (st.m_run == -INFINITY) ? 0.f : st.m_run;
-    float lloc = 0.f;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      x[q] = fexp2(x[q] - m_use);
-      lloc += x[q];
-    }
-    st.l_run += lloc + __shfl_xor(lloc, 32);
-    const bf16x8 pf0 = pack8(x), pf1 = pack8(x + 8);
-    const char* vt = cur + 2 * TB;
-#pragma unroll
-    for (int db = 0; db < NB; ++db) {
-      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(vt, db, 2 * sb, tro), pf0, st.o[db], 0, 0, 0);
-      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(vt, db, 2 * sb + 1, tro), pf1, st.o[db], 0, 0, 0);
-    }
+  for (int db = 0; db < NB; ++db) {
+    st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(vt, db, 2 * sb, tro), pf0, st.o[db], 0, 0, 0);
+    st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(vt, db, 2 * sb + 1, tro), pf1, st.o[db], 0, 0, 0);
   }
 }
 
+// Forward workgroup: 8 waves, two per SIMD. Wave w takes queries
+// q0 + 32(w & 3) .. +31 and, of every 64-key tile, the 32-key half w >> 2, so
+// the two waves of a pair see disjoint key sets with the same queries; each
+// keeps its own running (max reference, sum, output), and the pair merges
+// through LDS at the end. Two waves per SIMD let one wave's softmax
+// arithmetic overlap the other's matrix products.
+constexpr int FWD_WAVES = 8;
+
 template <int D, bool AL>
-__global__ __launch_bounds__(256) void fwd_mfma(MP p) {
+__global__ __launch_bounds__(64 * FWD_WAVES) void fwd_mfma(MP p) {
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
-  __shared__ __attribute__((aligned(16))) char st0[3 * TB];
-  __shared__ __attribute__((aligned(16))) char st1[3 * TB];
+  constexpr int NX = NB * 16 + 2;  // floats a wave hands to its partner, per lane
+  static_assert(4 * NX * 64 * 4 <= 6 * TB, "merge buffer exceeds the tile stages");
+  __shared__ __attribute__((aligned(16))) char stage[6 * TB];
   const int head = blockIdx.x;
   const int b = head / p.n_local, l = head - b * p.n_local;
   const int nqt = (p.seq + 127) / 128;
   const int qt = nqt - 1 - blockIdx.y;  // heaviest (longest causal prefix) first
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = (int)uni((uint32_t)(tid >> 6));
+  const int qw = w & 3, kh = w >> 2;
   const long grow0 = (long)b * p.seq;
-  const int q0w = qt * 128 + 32 * w;
+  const int q0w = qt * 128 + 32 * qw;
   const int myq = q0w + l32;
   const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
   const int kv_end = min(p.seq, qt * 128 + 128);
   const int nkt = (kv_end + TROWS - 1) / TROWS;
-  dma_tile<D>(p.kh, nrec, st0, grow0, l * D, 0, p.seq, p.h_l, w, lane);
-  dma_tile<D>(p.kl, nrec, st0 + TB, grow0, l * D, 0, p.seq, p.h_l, w, lane);
-  dma_tile<D>(p.vh, nrec, st0 + 2 * TB, grow0, l * D, 0, p.seq, p.h_l, w, lane);
+  dma_tile<D, FWD_WAVES>(p.kh, nrec, stage, grow0, l * D, 0, p.seq, p.h_l, w, lane);
+  dma_tile<D, FWD_WAVES>(p.kl, nrec, stage + TB, grow0, l * D, 0, p.seq, p.h_l, w, lane);
+  dma_tile<D, FWD_WAVES>(p.vh, nrec, stage + 2 * TB, grow0, l * D, 0, p.seq, p.h_l, w, lane);
   FwdState<D> st;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -290,23 +292,52 @@ __global__ __launch_bounds__(256) void fwd_mfma(MP p) {
   for (int kt = 0; kt < nkt; ++kt) {
     loads_landed_barrier();  // tile kt is in LDS; tile kt-1 is no longer read
     const bool odd = kt & 1;
-    fwd_tile<D, AL>(p, odd ? st1 : st0, odd ? st0 : st1, kt + 1 < nkt, kt * TROWS, l, grow0, w, lane, q0w, myq,
-                    slope2, tro, ro, st);
+    const char* cur = odd ? stage + 3 * TB : stage;
+    char* nxt = odd ? stage : stage + 3 * TB;
+    const int kv0 = kt * TROWS;
+    if (kt + 1 < nkt) {
+      dma_tile<D, FWD_WAVES>(p.kh, nrec, nxt, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
+      dma_tile<D, FWD_WAVES>(p.kl, nrec, nxt + TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
+      dma_tile<D, FWD_WAVES>(p.vh, nrec, nxt + 2 * TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
+    }
+    const int k0 = kv0 + 32 * kh;
+    if (k0 <= q0w + 31 && k0 < p.seq)  // wave-uniform; otherwise every key is masked
+      fwd_block<D, AL>(p, cur, k0, kh, g, q0w, myq, slope2, tro, ro, st);
   }
-  if (myq < p.seq) {
-    const float inv = 1.0f / st.l_run;
-    bf16* dst = p.ctx + (grow0 + myq) * p.h_l + (long)l * D;
+  // Pair merge. The last tile issued no loads, so after this barrier no wave
+  // reads or writes the stages any more.
+  __syncthreads();
+  float* xs = (float*)stage + qw * NX * 64 + lane;
+  if (kh) {
 #pragma unroll
     for (int db = 0; db < NB; ++db)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (bf16)(st.o[db][4 * q4 + e] * inv);
-        *(bf16x4*)(dst + 32 * db + 8 * q4 + 4 * g) = v;
-      }
-    if (g == 0) p.lse[(long)head * p.seq + myq] = (st.m_run + __log2f(st.l_run)) * (1.0f / kLog2e);
+      for (int i = 0; i < 16; ++i) xs[(16 * db + i) * 64] = st.o[db][i];
+    xs[NB * 16 * 64] = st.m_run;
+    xs[(NB * 16 + 1) * 64] = st.l_run;
   }
+  __syncthreads();
+  if (kh || myq >= p.seq) return;
+  const float m2 = xs[NB * 16 * 64], l2 = xs[(NB * 16 + 1) * 64];
+  const float m = fmaxf(st.m_run, m2);  // finite: key myq is in one of the two halves
+  const float f1 = st.m_run == -INFINITY ? 0.f : fexp2(st.m_run - m);
+  const float f2 = m2 == -INFINITY ? 0.f : fexp2(m2 - m);
+  const float lsum = st.l_run * f1 + l2 * f2;
+  const float inv = 1.0f / lsum;
+  bf16* dst = p.ctx + (grow0 + myq) * p.h_l + (long)l * D;
+#pragma unroll
+  for (int db = 0; db < NB; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * q4 + e;
+        v[e] = (bf16)((st.o[db][i] * f1 + xs[(16 * db + i) * 64] * f2) * inv);
+      }
+      *(bf16x4*)(dst + 32 * db + 8 * q4 + 4 * g) = v;
+    }
+  if (g == 0) p.lse[(long)head * p.seq + myq] = (m + __log2f(lsum)) * (1.0f / kLog2e);
 }
 
 // ---- backward: dK, dV ---------------------------------------------------------------
@@ -647,8 +678,8 @@ MP make_mp(const AttnDesc& a) {
 template <int D>
 hipError_t fwd_d(const MP& p, hipStream_t stream) {
   dim3 grid(p.batch * p.n_local, (p.seq + 127) / 128);
-  if (p.alibi) hipLaunchKernelGGL((fwd_mfma<D, true>), grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((fwd_mfma<D, false>), grid, dim3(256), 0, stream, p);
+  if (p.alibi) hipLaunchKernelGGL((fwd_mfma<D, true>), grid, dim3(64 * FWD_WAVES), 0, stream, p);
+  else hipLaunchKernelGGL((fwd_mfma<D, false>), grid, dim3(64 * FWD_WAVES), 0, stream, p);
   return hipGetLastError();
 }
 template <int D>

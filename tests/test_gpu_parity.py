@@ -93,6 +93,9 @@ SMALL = [
     ("d160_tp2_r1", 1, 257, 4, 160, 2, 1, False),
     ("d16_tp2_r1_vector_path", 2, 40, 8, 16, 2, 1, True),
     ("d128_tp4_r3_seq1", 3, 1, 8, 128, 4, 3, True),
+    # longer, ragged sequences: many key tiles per query tile, partial last tiles
+    ("d64_tp1_alibi_long_ragged", 1, 777, 2, 64, 1, 0, True),
+    ("d160_tp2_r0_long_ragged", 2, 1100, 4, 160, 2, 0, False),
 ]
 
 
