@@ -1,6 +1,6 @@
 """fp64 CPU oracle for one tensor-parallel rank's share of a Megatron-style
 Transformer layer (MLP block and causal self-attention block, forward and
-backward).
+backward), and of the residual add + LayerNorm that follows each block.
 
 TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
 baseline leg may import this package. The product path (the HIP library and
@@ -23,3 +23,4 @@ from .tp_layer import (  # noqa: F401
     layer_weight_shapes, mlp_fwd, mlp_bwd, alibi_slope, attn_core_fwd, attn_core_bwd, attn_fwd,
     attn_bwd, sum_partials,
 )
+from .ln_residual import ln_residual_fwd, ln_residual_bwd  # noqa: F401
