@@ -135,6 +135,57 @@ def cpu_baseline(w, inp, target_s: float) -> dict:
                       f"in {t:.2f} s)"}
 
 
+def ln_residual_measure(w, reps: int = 20) -> dict:
+    """The residual add + LayerNorm after a block (outside the layer-shard step
+    and its metric): one forward + backward per repetition at the workload's
+    T x hidden, bf16, one block output (after g), replicated bias, residual
+    gradient. HBM-bound: achieved = algorithmic bytes / average launch-sequence
+    time (HIP events on the library's stream)."""
+    import torch
+    import synth
+    import tensor_transformer_layer_tp_amd as tp
+
+    inp = synth.draw_ln(w, seed=0, n_parts=1, bias_std=0.02)
+    dev = {k: (v.cuda() if torch.is_tensor(v) else [p.cuda() for p in v]) for k, v in inp.items()}
+    s = tp.TpShape.make(batch=w.batch, seq=w.seq, hidden=w.hidden, ffn=w.ffn, n_heads=w.n_heads,
+                        head_dim=w.head_dim, tp_rank=0, tp_size=w.tp_size, dtype=w.dtype, alibi=int(w.alibi))
+    T, h = w.tokens, w.hidden
+    bf = torch.bfloat16
+    r, y, dr = (torch.empty((T, h), dtype=bf, device="cuda") for _ in range(3))
+    mean, rstd = (torch.empty(T, dtype=torch.float32, device="cuda") for _ in range(2))
+    dg, db, dbias = (torch.empty(h, dtype=bf, device="cuda") for _ in range(3))
+    ws = torch.empty(tp.tp_ln_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+
+    def once():
+        tp.tp_ln_residual_fwd(s, dev["resid_in"], dev["parts"], dev["bias"], dev["gamma"], dev["beta"], 1e-5, r, y,
+                              mean, rstd)
+        tp.tp_ln_residual_bwd(s, r, mean, rstd, dev["gamma"], dev["d_ln_out"], dev["d_resid_out"], dr, dg, db,
+                              dbias, workspace=ws)
+
+    for _ in range(3):
+        once()
+    torch.cuda.synchronize()
+    tp.tp_profile_enable((1 << tp.STEPS["ln_fwd"]) | (1 << tp.STEPS["ln_bwd"]))
+    for _ in range(reps):
+        once()
+    torch.cuda.synchronize()
+    res = {}
+    # algorithmic bytes: every tensor once (bf16), statistics fp32
+    nbytes = {"fwd": 2 * (3 * T * h + 3 * h) + 2 * T * h + 8 * T,   # resid_in, part, bias, gamma, beta -> r, y, stats
+              "bwd": 2 * (3 * T * h + h) + 2 * (T * h + 3 * h) + 8 * T}  # r, dy, dr_in, gamma, stats -> dr, 3 sums
+    for name in ("fwd", "bwd"):
+        n, ms = tp.tp_profile_collect(tp.STEPS["ln_" + name])
+        avg = ms / max(n, 1)
+        gbs = nbytes[name] / (avg / 1e3) / 1e9
+        res[name] = {"avg_launch_ms": round(avg, 4), "launches": n, "algorithmic_bytes": nbytes[name],
+                     "achieved": round(gbs, 1), "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                     "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"  ln_residual {name}: {avg * 1e3:.1f} us, {gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of HBM)")
+    tp.tp_profile_enable(0)
+    return {"bound": "hbm", "workload": f"{w.name}: T={T}, hidden={h}, bf16, 1 block output, bias, residual grad",
+            **res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +193,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mtnlg_530b_tp8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ln", action="store_true", help="skip the residual + LayerNorm measurement")
     ap.add_argument("--cpu-target-s", type=float, default=15.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run device-to-device copies of this many MiB (calibrates byte counters)")
@@ -231,6 +283,11 @@ def main():
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": kernel,
             "flops_per_launch": sf[dom], "avg_launch_ms": round(avg_dom_ms, 4), "launches": n_dom}
 
+    ln = None
+    if not a.no_ln:
+        log("residual add + LayerNorm (measured apart from the step)")
+        ln = ln_residual_measure(w)
+
     cpu = None
     if not a.no_cpu_baseline:
         log("cpu baseline (fp64 oracle on a bounded sample)")
@@ -249,6 +306,7 @@ def main():
         "breakdown_ms": {k: round(v, 4) for k, v in breakdown.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "ln_residual": ln,
     }
     print(json.dumps(out), flush=True)
 

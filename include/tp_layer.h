@@ -149,6 +149,48 @@ tp_status tp_attn_bwd(const tp_shape* shape, const void* X, const void* Wqkv_i, 
 tp_status tp_sum_partials(const tp_shape* shape, const void* const* parts, int32_t n_parts,
                           const void* bias_or_null, void* out, void* stream);
 
+/* Residual add + LayerNorm after a block (Megatron-LM deep dive, Fig. 2: the
+ * layer's residual connections and layer normalizations around the attention
+ * and MLP blocks; Fig. 4: g completes the block output before the residual
+ * add; Megatron-DeepSpeed blog, section 4.3: the residual add fused into the
+ * LayerNorm kernel). Per token row t of h = hidden elements:
+ *   resid_out = resid_in + sum_{k < n_parts} parts[k] + bias   (the new
+ *               residual stream; with the ranks' partial block outputs as
+ *               parts this is also g's sum, emulated on one device)
+ *   mean, rstd: mean and 1/sqrt(biased variance + eps) of the row of
+ *               resid_out as stored (fp32 [T] each, saved for the backward)
+ *   ln_out    = (resid_out - mean) * rstd * gamma + beta   (the next block's input)
+ * resid_in, parts[k], resid_out, ln_out [T,h]; bias_or_null, gamma, beta [h]
+ * in shape->dtype (only batch, seq, hidden and dtype of shape are used, the
+ * rest is validated as for every call). parts is a HOST array of n_parts
+ * (0..64) device pointers (may be NULL when n_parts = 0). eps > 0 (the pages
+ * give no value). Needs hidden % 8 == 0 (else TP_ERR_ALIGN) and hidden <=
+ * 24576 (else TP_ERR_SHAPE). Outputs must not alias inputs. */
+tp_status tp_ln_residual_fwd(const tp_shape* shape, const void* resid_in, const void* const* parts,
+                             int32_t n_parts, const void* bias_or_null, const void* gamma,
+                             const void* beta, float eps, void* resid_out, void* ln_out, float* mean,
+                             float* rstd, void* stream);
+
+/* Workspace bytes of tp_ln_residual_bwd (0 when none is needed, i.e. an empty
+ * batch, or on an invalid shape). Host-only; no HIP call. */
+size_t tp_ln_workspace_bytes(const tp_shape* shape);
+
+/* Backward of tp_ln_residual_fwd: gradients of <ln_out, d_ln_out> +
+ * <resid_out, d_resid_out> (d_resid_out_or_null: the gradient reaching
+ * resid_out along the residual stream from later in the network; NULL = 0),
+ * from the saved resid_out, mean, rstd:
+ *   xhat = (resid_out - mean) * rstd,  g = d_ln_out * gamma
+ *   d_resid = d_resid_out + rstd * (g - mean_j g - xhat * mean_j (g * xhat))   [T,h]
+ *             (the gradient of resid_in, of every part and of the block output)
+ *   dgamma = sum_t d_ln_out * xhat,  dbeta = sum_t d_ln_out   [h]
+ *   dbias  = sum_t d_resid [h], written only if dbias_or_null != NULL
+ * Column sums are formed from fixed-order fp32 partials (deterministic). */
+tp_status tp_ln_residual_bwd(const tp_shape* shape, const void* resid_out, const float* mean,
+                             const float* rstd, const void* gamma, const void* d_ln_out,
+                             const void* d_resid_out_or_null, void* d_resid, void* dgamma,
+                             void* dbeta, void* dbias_or_null, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* Steps of the path, for per-step timing. The id doubles as the bit position
  * in tp_profile_enable's mask. */
 enum {
@@ -166,7 +208,9 @@ enum {
   TP_STEP_ATTN_BWD = 12,  /* per-head causal attention, backward             */
   TP_STEP_QKV_WGRAD = 13, /* dWqkv_i = X^T dqkv                              */
   TP_STEP_QKV_DGRAD = 14, /* dX_i = dqkv Wqkv_i^T                            */
-  TP_STEP_BIAS_GRADS = 15 /* column sums db1_i, db2, dbo, dbqkv_i            */
+  TP_STEP_BIAS_GRADS = 15, /* column sums db1_i, db2, dbo, dbqkv_i           */
+  TP_STEP_LN_FWD = 16,     /* residual add + LayerNorm, forward              */
+  TP_STEP_LN_BWD = 17      /* residual add + LayerNorm, backward             */
 };
 
 /* Measurement aid (no passage of the pages; for benchmarks): while bit k of

@@ -26,7 +26,7 @@ from dataclasses import dataclass, replace
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "draw_shard", "draw_full", "DRAW_ORDER"]
+__all__ = ["Workload", "WORKLOADS", "draw_shard", "draw_full", "DRAW_ORDER", "draw_ln", "LN_DRAW_ORDER"]
 
 
 @dataclass(frozen=True)
@@ -127,3 +127,28 @@ def draw_full(w: Workload, seed: int = 0) -> dict:
     gen = torch.Generator().manual_seed(seed)
     dt = _TORCH_DTYPE[w.dtype]
     return {name: _normal(gen, shape, std, dt) for name, (shape, std) in _shapes(w, 1).items()}
+
+
+# Residual add + LayerNorm after a block: fixed order of the draws.
+LN_DRAW_ORDER = ("resid_in", "parts", "bias", "gamma", "beta", "d_ln_out", "d_resid_out")
+
+
+def draw_ln(w: Workload, seed: int = 0, n_parts: int = 1, bias_std: float = 0.0) -> dict:
+    """Inputs of the residual add + LayerNorm that follows a block, at w's
+    token count and hidden size, from their own generator: the residual
+    stream and each partial block output N(0, 1); gamma N(1, 0.1^2) and beta
+    N(0, 0.1^2) (LayerNorm weights start at 1 and 0; the spread makes every
+    term of the backward matter); the replicated bias N(0, bias_std^2) (None
+    when bias_std is 0); the gradients arriving at the LayerNorm output and
+    along the residual stream N(0, 1). CPU tensors in the storage dtype."""
+    gen = torch.Generator().manual_seed(seed)
+    dt = _TORCH_DTYPE[w.dtype]
+    T, h = w.tokens, w.hidden
+    out = {"resid_in": _normal(gen, (T, h), 1.0, dt),
+           "parts": [_normal(gen, (T, h), 1.0, dt) for _ in range(n_parts)]}
+    out["bias"] = _normal(gen, (h,), bias_std, dt) if bias_std > 0 else None
+    out["gamma"] = (1.0 + _normal(gen, (h,), 0.1, torch.float32)).to(dt)
+    out["beta"] = _normal(gen, (h,), 0.1, dt)
+    out["d_ln_out"] = _normal(gen, (T, h), 1.0, dt)
+    out["d_resid_out"] = _normal(gen, (T, h), 1.0, dt)
+    return out

@@ -21,7 +21,7 @@ __all__ = [
     "TpShape", "TPError", "TP_FP32", "TP_BF16", "STATUS", "library_path", "load_library",
     "exported_symbols", "tp_mlp_workspace_bytes", "tp_attn_workspace_bytes", "tp_mlp_fwd",
     "tp_mlp_bwd", "tp_attn_fwd", "tp_attn_bwd", "tp_sum_partials", "tp_last_error", "tp_profile_enable",
-    "tp_profile_collect", "STEPS",
+    "tp_profile_collect", "STEPS", "tp_ln_workspace_bytes", "tp_ln_residual_fwd", "tp_ln_residual_bwd",
 ]
 
 TP_FP32, TP_BF16 = 0, 1
@@ -68,6 +68,10 @@ _SIGS = {
     "tp_attn_fwd": (_st, [ctypes.POINTER(TpShape)] + [_vp] * 8 + [_vp, _sz, _vp]),
     "tp_attn_bwd": (_st, [ctypes.POINTER(TpShape)] + [_vp] * 12 + [_vp, _sz, _vp]),
     "tp_sum_partials": (_st, [ctypes.POINTER(TpShape), ctypes.POINTER(_vp), ctypes.c_int32, _vp, _vp, _vp]),
+    "tp_ln_workspace_bytes": (_sz, [ctypes.POINTER(TpShape)]),
+    "tp_ln_residual_fwd": (_st, [ctypes.POINTER(TpShape), _vp, ctypes.POINTER(_vp), ctypes.c_int32, _vp, _vp, _vp,
+                                 ctypes.c_float, _vp, _vp, _vp, _vp, _vp]),
+    "tp_ln_residual_bwd": (_st, [ctypes.POINTER(TpShape)] + [_vp] * 10 + [_vp, _sz, _vp]),
     "tp_profile_enable": (_st, [ctypes.c_uint32]),
     "tp_profile_collect": (_st, [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)]),
     "tp_last_error": (ctypes.c_char_p, []),
@@ -77,7 +81,7 @@ _SIGS = {
 STEPS = {
     "qkv_proj": 1, "attn_fwd": 2, "out_proj": 3, "fc1": 4, "fc2": 5, "fc2_dgrad": 6, "fc2_wgrad": 7,
     "fc1_wgrad": 8, "fc1_dgrad": 9, "out_dgrad": 10, "out_wgrad": 11, "attn_bwd": 12, "qkv_wgrad": 13,
-    "qkv_dgrad": 14, "bias_grads": 15,
+    "qkv_dgrad": 14, "bias_grads": 15, "ln_fwd": 16, "ln_bwd": 17,
 }
 
 
@@ -189,3 +193,25 @@ def tp_sum_partials(shape, parts, bias_or_null, out, stream=None):
     arr = (_vp * len(parts))(*[_ptr(p) for p in parts])
     _check(load_library().tp_sum_partials(ctypes.byref(shape), arr, len(parts), _ptr(bias_or_null), _ptr(out),
                                           _stream(stream)))
+
+
+def tp_ln_workspace_bytes(shape: TpShape) -> int:
+    return load_library().tp_ln_workspace_bytes(ctypes.byref(shape))
+
+
+def tp_ln_residual_fwd(shape, resid_in, parts, bias_or_null, gamma, beta, eps, resid_out, ln_out, mean, rstd,
+                       stream=None):
+    """resid_out = resid_in + sum(parts) + bias; ln_out = LayerNorm(resid_out) (see the header)."""
+    arr = (_vp * max(len(parts), 1))(*[_ptr(p) for p in parts])
+    _check(load_library().tp_ln_residual_fwd(ctypes.byref(shape), _ptr(resid_in), arr, len(parts),
+                                             _ptr(bias_or_null), _ptr(gamma), _ptr(beta), float(eps),
+                                             _ptr(resid_out), _ptr(ln_out), _ptr(mean), _ptr(rstd), _stream(stream)))
+
+
+def tp_ln_residual_bwd(shape, resid_out, mean, rstd, gamma, d_ln_out, d_resid_out_or_null, d_resid, dgamma, dbeta,
+                       dbias_or_null=None, workspace=None, stream=None):
+    w, wn = _ws(workspace)
+    _check(load_library().tp_ln_residual_bwd(ctypes.byref(shape), _ptr(resid_out), _ptr(mean), _ptr(rstd),
+                                             _ptr(gamma), _ptr(d_ln_out), _ptr(d_resid_out_or_null), _ptr(d_resid),
+                                             _ptr(dgamma), _ptr(dbeta), _ptr(dbias_or_null), w, wn,
+                                             _stream(stream)))

@@ -79,6 +79,36 @@ hipError_t colsum_launch(int dtype, const void* X, int M, int N, long ld, void* 
 hipError_t sum_partials_launch(int dtype, const void* const* parts, int n_parts, const void* bias,
                                void* out, long long count, int cols, hipStream_t stream);
 
+// Residual add + LayerNorm around a tensor-parallel block (token rows of h
+// elements; h a multiple of 8, at most kLnMaxHidden).
+constexpr int kLnMaxHidden = 24576;
+struct LnDesc {
+  long long T = 0;  // rows
+  int h = 0;
+  float eps = 0.f;
+  // forward: resid_out = resid_in + sum_k parts[k] + bias; y = LayerNorm(resid_out)
+  const void* resid_in = nullptr;
+  const void* const* parts = nullptr;  // host array of n_parts (<= 64) device pointers
+  int n_parts = 0;
+  const void* bias = nullptr;  // [h] or NULL
+  const void* gamma = nullptr;
+  const void* beta = nullptr;
+  void* resid_out = nullptr;  // also the backward's input r
+  void* y = nullptr;
+  float* mean = nullptr;  // [T]
+  float* rstd = nullptr;  // [T]
+  // backward
+  const void* dy = nullptr;
+  const void* dr_in = nullptr;  // [T,h] or NULL
+  void* dr = nullptr;
+  void* dgamma = nullptr;
+  void* dbeta = nullptr;
+  void* dbias = nullptr;  // [h] or NULL
+};
+size_t ln_bwd_workspace_bytes(long long rows, int h);
+hipError_t ln_fwd_launch(int dtype, const LnDesc& d, hipStream_t stream);
+hipError_t ln_bwd_launch(int dtype, const LnDesc& d, void* ws, hipStream_t stream);
+
 // Fill rows x cols (leading dimension ld) of dtype elements with zero.
 hipError_t zero_launch(int dtype, void* p, long long rows, long long cols, long long ld,
                        hipStream_t stream);

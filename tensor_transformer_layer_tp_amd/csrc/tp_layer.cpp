@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -240,6 +241,14 @@ tp_status check_ws(void* ws, size_t have, size_t need) {
   return TP_OK;
 }
 
+// Residual add + LayerNorm: row-vector kernels need 8 | hidden and keep a row
+// (forward) or a thread's column partials (backward) in registers.
+tp_status check_ln(const Dims& dm) {
+  if (dm.h % 8) return fail(TP_ERR_ALIGN, "residual + LayerNorm needs hidden to be a multiple of 8");
+  if (dm.h > kLnMaxHidden) return fail(TP_ERR_SHAPE, "residual + LayerNorm supports hidden <= %d", kLnMaxHidden);
+  return TP_OK;
+}
+
 GemmDesc gd(int role, int M, int N, int K, const void* A, long lda, bool ak, const void* B, long ldb, bool bk,
             int epi, void* C, long ldc) {
   GemmDesc g;
@@ -435,6 +444,70 @@ tp_status tp_sum_partials(const tp_shape* shape, const void* const* parts, int32
   if (e) return TP_OK;
   TP_HIP(sum_partials_launch(dm.dtype, parts, n_parts, bias_or_null, out, dm.T * dm.h, (int)dm.h, (hipStream_t)stream),
          "sum of partials");
+  return TP_OK;
+}
+
+size_t tp_ln_workspace_bytes(const tp_shape* shape) {
+  Dims dm;
+  if (check_shape(shape, dm) != TP_OK || check_ln(dm) != TP_OK) return 0;
+  return ln_bwd_workspace_bytes(dm.T, (int)dm.h);
+}
+
+tp_status tp_ln_residual_fwd(const tp_shape* shape, const void* resid_in, const void* const* parts, int32_t n_parts,
+                             const void* bias_or_null, const void* gamma, const void* beta, float eps, void* resid_out,
+                             void* ln_out, float* mean, float* rstd, void* stream) {
+  Dims dm;
+  TP_CHECK(check_shape(shape, dm));
+  TP_CHECK(check_ln(dm));
+  if (!(eps > 0.f) || !std::isfinite(eps)) return fail(TP_ERR_SHAPE, "eps must be positive and finite");
+  if (n_parts < 0 || n_parts > 64) return fail(TP_ERR_SHAPE, "n_parts %d outside [0, 64]", n_parts);
+  if (n_parts > 0 && !parts) return fail(TP_ERR_NULL, "parts is NULL");
+  const bool e = dm.T == 0;
+  TP_CHECK(check_ptr(resid_in, "resid_in", e));
+  for (int k = 0; k < n_parts; ++k) TP_CHECK(check_ptr(parts[k], "parts[k]", e));
+  TP_CHECK(check_ptr(bias_or_null, "bias", true));
+  TP_CHECK(check_ptr(gamma, "gamma", false));
+  TP_CHECK(check_ptr(beta, "beta", false));
+  TP_CHECK(check_ptr(resid_out, "resid_out", e));
+  TP_CHECK(check_ptr(ln_out, "ln_out", e));
+  TP_CHECK(check_ptr(mean, "mean", e));
+  TP_CHECK(check_ptr(rstd, "rstd", e));
+  if (e) return TP_OK;
+  LnDesc d;
+  d.T = dm.T; d.h = (int)dm.h; d.eps = eps;
+  d.resid_in = resid_in; d.parts = parts; d.n_parts = n_parts; d.bias = bias_or_null;
+  d.gamma = gamma; d.beta = beta; d.resid_out = resid_out; d.y = ln_out; d.mean = mean; d.rstd = rstd;
+  hipStream_t st = (hipStream_t)stream;
+  TP_STEP(TP_STEP_LN_FWD, ln_fwd_launch(dm.dtype, d, st), "residual add + LayerNorm forward");
+  return TP_OK;
+}
+
+tp_status tp_ln_residual_bwd(const tp_shape* shape, const void* resid_out, const float* mean, const float* rstd,
+                             const void* gamma, const void* d_ln_out, const void* d_resid_out_or_null, void* d_resid,
+                             void* dgamma, void* dbeta, void* dbias_or_null, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  Dims dm;
+  TP_CHECK(check_shape(shape, dm));
+  TP_CHECK(check_ln(dm));
+  const bool e = dm.T == 0;
+  TP_CHECK(check_ptr(resid_out, "resid_out", e));
+  TP_CHECK(check_ptr(mean, "mean", e));
+  TP_CHECK(check_ptr(rstd, "rstd", e));
+  TP_CHECK(check_ptr(gamma, "gamma", false));
+  TP_CHECK(check_ptr(d_ln_out, "d_ln_out", e));
+  TP_CHECK(check_ptr(d_resid_out_or_null, "d_resid_out", true));
+  TP_CHECK(check_ptr(d_resid, "d_resid", e));
+  TP_CHECK(check_ptr(dgamma, "dgamma", false));
+  TP_CHECK(check_ptr(dbeta, "dbeta", false));
+  TP_CHECK(check_ptr(dbias_or_null, "dbias", true));
+  TP_CHECK(check_ws(workspace, workspace_bytes, ln_bwd_workspace_bytes(dm.T, (int)dm.h)));
+  LnDesc d;
+  d.T = dm.T; d.h = (int)dm.h;
+  d.resid_out = (void*)resid_out; d.mean = (float*)mean; d.rstd = (float*)rstd; d.gamma = gamma;
+  d.dy = d_ln_out; d.dr_in = d_resid_out_or_null; d.dr = d_resid;
+  d.dgamma = dgamma; d.dbeta = dbeta; d.dbias = dbias_or_null;
+  hipStream_t st = (hipStream_t)stream;
+  TP_STEP(TP_STEP_LN_BWD, ln_bwd_launch(dm.dtype, d, workspace, st), "residual add + LayerNorm backward");
   return TP_OK;
 }
 

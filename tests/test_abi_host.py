@@ -22,7 +22,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     names = tp.exported_symbols()
     assert set(names) == {"tp_mlp_workspace_bytes", "tp_attn_workspace_bytes", "tp_mlp_fwd", "tp_mlp_bwd",
                           "tp_attn_fwd", "tp_attn_bwd", "tp_sum_partials", "tp_last_error", "tp_profile_enable",
-                          "tp_profile_collect"}
+                          "tp_profile_collect", "tp_ln_workspace_bytes", "tp_ln_residual_fwd", "tp_ln_residual_bwd"}
     for n in names:
         assert isinstance(getattr(lib, n), ctypes._CFuncPtr), n
     out = subprocess.run(["nm", "-D", "--defined-only", tp.library_path()], capture_output=True, text=True).stdout
@@ -112,7 +112,7 @@ def test_profile_mask_without_gpu():
     tp.tp_profile_enable(1 << tp.STEPS["fc1"])
     tp.tp_profile_enable(0)
     assert tp.tp_profile_collect(tp.STEPS["fc1"]) == (0, 0.0)
-    assert set(tp.STEPS.values()) == set(range(1, 16))
+    assert set(tp.STEPS.values()) == set(range(1, 18))
 
 
 def test_empty_batch_needs_no_token_pointers():
@@ -120,3 +120,76 @@ def test_empty_batch_needs_no_token_pointers():
     s = shape(batch=0)
     tp.tp_mlp_fwd(s, None, FAKE, FAKE, FAKE, None, None, None, workspace=(FAKE, 1 << 40), stream=0)
     tp.tp_attn_fwd(s, None, FAKE, FAKE, FAKE, None, None, None, None, workspace=(FAKE, 1 << 40), stream=0)
+
+
+# ---------------------------------------------------------------------------
+# residual add + LayerNorm
+# ---------------------------------------------------------------------------
+
+def _ln_fwd(s, parts=(FAKE,), eps=1e-5, **override):
+    args = dict(resid_in=FAKE, bias_or_null=None, gamma=FAKE, beta=FAKE, resid_out=FAKE, ln_out=FAKE, mean=FAKE,
+                rstd=FAKE)
+    args.update(override)
+    tp.tp_ln_residual_fwd(s, args["resid_in"], list(parts), args["bias_or_null"], args["gamma"], args["beta"], eps,
+                          args["resid_out"], args["ln_out"], args["mean"], args["rstd"], stream=0)
+
+
+def _ln_bwd(s, ws=(FAKE, 1 << 40), **override):
+    args = dict(resid_out=FAKE, mean=FAKE, rstd=FAKE, gamma=FAKE, d_ln_out=FAKE, d_resid_out_or_null=None,
+                d_resid=FAKE, dgamma=FAKE, dbeta=FAKE, dbias_or_null=None)
+    args.update(override)
+    tp.tp_ln_residual_bwd(s, workspace=ws, stream=0, **args)
+
+
+def test_ln_workspace_bytes():
+    # one fp32 partial row of (dgamma, dbeta, dbias) per run of rows, at most 256 runs
+    big = shape(batch=1, seq=2048, hidden=20480, ffn=81920, n_heads=128, head_dim=160, tp_size=8, dtype=tp.TP_BF16)
+    assert tp.tp_ln_workspace_bytes(big) == 256 * 3 * 20480 * 4
+    assert tp.tp_ln_workspace_bytes(shape()) == 64 * 3 * 64 * 4  # 64 rows -> 64 runs of one row
+    assert tp.tp_ln_workspace_bytes(shape(batch=0)) == 0
+    wide = shape(hidden=32768, n_heads=256, head_dim=128, ffn=256)
+    assert tp.tp_ln_workspace_bytes(wide) == 0  # hidden above the supported width
+
+
+@pytest.mark.parametrize("kw,override,status", [
+    (dict(hidden=32768, n_heads=256, head_dim=128), {}, "TP_ERR_SHAPE"),
+    (dict(hidden=60, n_heads=6, head_dim=10, ffn=240), {}, "TP_ERR_HEADDIM"),
+    (dict(hidden=72, n_heads=4, head_dim=18, ffn=256), {}, "TP_ERR_HEADDIM"),
+    (dict(hidden=40, n_heads=5, head_dim=8, ffn=240, tp_size=2), {}, "TP_ERR_DIVISIBILITY"),
+    ({}, dict(eps=0.0), "TP_ERR_SHAPE"),
+    ({}, dict(eps=float("inf")), "TP_ERR_SHAPE"),
+    ({}, dict(eps=float("nan")), "TP_ERR_SHAPE"),
+    ({}, dict(gamma=None), "TP_ERR_NULL"),
+    ({}, dict(beta=FAKE + 8), "TP_ERR_ALIGN"),
+    ({}, dict(parts=[FAKE] * 65), "TP_ERR_SHAPE"),
+    ({}, dict(parts=[FAKE, None]), "TP_ERR_NULL"),
+    (dict(tp_rank=3), {}, "TP_ERR_RANK"),
+])
+def test_ln_fwd_validation(kw, override, status):
+    with pytest.raises(tp.TPError) as ei:
+        _ln_fwd(shape(**kw), **override)
+    assert ei.value.name == status, str(ei.value)
+
+
+def test_ln_hidden_multiple_of_8():
+    # hidden = n_heads * head_dim with 8 | head_dim, so a hidden of 100 is already refused by the shape checks
+    s = shape(hidden=100, n_heads=4, head_dim=25, ffn=256)
+    with pytest.raises(tp.TPError) as ei:
+        _ln_fwd(s)
+    assert ei.value.name in ("TP_ERR_ALIGN", "TP_ERR_HEADDIM"), str(ei.value)
+
+
+def test_ln_bwd_validation():
+    with pytest.raises(tp.TPError) as ei:
+        _ln_bwd(shape(), dgamma=None)
+    assert ei.value.name == "TP_ERR_NULL"
+    with pytest.raises(tp.TPError) as ei:
+        _ln_bwd(shape(), ws=(FAKE, 16))
+    assert ei.value.name == "TP_ERR_WORKSPACE"
+    with pytest.raises(tp.TPError) as ei:
+        _ln_bwd(shape(), d_resid_out_or_null=FAKE + 4)
+    assert ei.value.name == "TP_ERR_ALIGN"
+
+
+def test_ln_empty_batch_needs_no_token_pointers():
+    _ln_fwd(shape(batch=0), parts=(None,), resid_in=None, resid_out=None, ln_out=None, mean=None, rstd=None)
