@@ -20,19 +20,26 @@
 // taken over the stored (rounded) r, so the backward pass, which rereads r,
 // sees exactly the values the forward pass normalized.
 //
-// Forward: one workgroup of 1024 threads per row; the row stays in registers
-// between the two reductions (mean, then variance about the mean).
+// Forward: one workgroup of 256 threads per row (several rows in flight per
+// CU); the row stays in registers between the two reductions (mean, then
+// variance about the mean).
 // Backward: one workgroup of 512 threads per run of rows; each thread owns
 // the same columns in every row of its run and keeps fp32 column partials of
-// dy xhat, dy and dr in registers; a second kernel adds the runs' partials in
-// a fixed order (no atomics: results do not depend on scheduling).
+// dy xhat and dy in registers, and loads the next row while it reduces the
+// current one; a second kernel adds the runs' partials in a fixed order (no
+// atomics: results do not depend on scheduling). dbias, when asked for, is a
+// column sum of dr.
+//
+// The workgroup reductions exchange values through LDS behind a barrier that
+// waits only for LDS traffic, so loads and stores to memory stay in flight
+// across it.
 #include "common.h"
 #include "kernels.h"
 
 namespace tpk {
 namespace {
 
-constexpr int FWD_T = 1024;
+constexpr int FWD_T = 256;
 constexpr int BWD_T = 512;
 constexpr int BWD_RUNS = 256;  // target number of row runs (one per CU)
 
@@ -42,6 +49,9 @@ template <> struct V8<bf16> {
   bf16x8 v;
   __device__ __forceinline__ void load(const bf16* p) { v = *(const bf16x8*)p; }
   __device__ __forceinline__ float operator[](int e) const { return (float)v[e]; }
+  // Make the packed value opaque to the compiler here, so that widened copies
+  // made before this point are not kept alive past it (they are recomputed).
+  __device__ __forceinline__ void opaque() { asm volatile("" : "+v"(v)); }
 };
 template <> struct V8<float> {
   f32x4 a, b;
@@ -50,6 +60,7 @@ template <> struct V8<float> {
     b = *(const f32x4*)(p + 4);
   }
   __device__ __forceinline__ float operator[](int e) const { return e < 4 ? a[e] : b[e - 4]; }
+  __device__ __forceinline__ void opaque() {}
 };
 
 template <typename T> __device__ __forceinline__ void load8(const T* p, float (&x)[8]) {
@@ -69,6 +80,11 @@ __device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
   *(f32x4*)(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
 }
 
+// Workgroup barrier for LDS exchanges only: this thread's LDS accesses have
+// completed, then s_barrier. Unlike __syncthreads it does not wait for
+// outstanding global loads and stores.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Sum of K values over the workgroup (NT threads); every thread receives the
 // totals, formed in one fixed order. `red` holds NT/64 * K floats.
 template <int NT, int K>
@@ -82,7 +98,7 @@ __device__ __forceinline__ void block_sum(float (&x)[K], float* red) {
 #pragma unroll
     for (int k = 0; k < K; ++k) red[w * K + k] = x[k];
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     float s = 0.f;
@@ -90,13 +106,17 @@ __device__ __forceinline__ void block_sum(float (&x)[K], float* red) {
     for (int i = 0; i < NT / 64; ++i) s += red[i * K + k];
     x[k] = s;
   }
-  __syncthreads();  // `red` may be written again after this
+  lds_barrier();  // `red` may be written again after this
 }
 
 struct PartPtrs {
   const void* p[64];
 };
 
+// Chunk i of this thread (8 elements at column 8c) is valid if c < nc; the
+// loads use the clamped chunk min(c, nc - 1), always in range, so that no load
+// waits behind a branch; only arithmetic that feeds a sum and the stores
+// depend on validity.
 template <typename T, int NV>
 __global__ __launch_bounds__(FWD_T) void ln_residual_fwd_kernel(const T* __restrict__ resid_in, PartPtrs parts,
                                                                 int n_parts, const T* __restrict__ bias,
@@ -107,28 +127,43 @@ __global__ __launch_bounds__(FWD_T) void ln_residual_fwd_kernel(const T* __restr
   __shared__ float red[FWD_T / 64];
   const long base = (long)blockIdx.x * h;
   const int nc = h >> 3;
-  float v[NV][8];
-  float s[1] = {0.f};
+  int cl[NV];
+  bool ok[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = threadIdx.x + i * FWD_T;
-    if (c >= nc) continue;
-    load8(resid_in + base + 8 * c, v[i]);
-    for (int k = 0; k < n_parts; ++k) {
-      float p[8];
-      load8((const T*)parts.p[k] + base + 8 * c, p);
+    ok[i] = c < nc;
+    cl[i] = 8 * (ok[i] ? c : nc - 1);
+  }
+  float v[NV][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[i][e] += p[e];
-    }
-    if (bias) {
-      float b[8];
-      load8(bias + 8 * c, b);
+  for (int i = 0; i < NV; ++i) load8(resid_in + base + cl[i], v[i]);
+  for (int k = 0; k < n_parts; ++k) {
+    const T* pk = (const T*)parts.p[k];
+    V8<T> pv[NV];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[i][e] += b[e];
-    }
+    for (int i = 0; i < NV; ++i) pv[i].load(pk + base + cl[i]);
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[i][e] += pv[i][e];
+  }
+  if (bias) {
+    V8<T> bv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) bv[i].load(bias + cl[i]);
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[i][e] += bv[i][e];
+  }
+  float s[1] = {0.f};
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[i][e] = to_f(from_f<T>(v[i][e]));  // the value stored
-    store8(resid_out + base + 8 * c, v[i]);
+    if (!ok[i]) continue;
+    store8(resid_out + base + cl[i], v[i]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) s[0] += v[i][e];
   }
@@ -137,25 +172,28 @@ __global__ __launch_bounds__(FWD_T) void ln_residual_fwd_kernel(const T* __restr
   float q[1] = {0.f};
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    if (threadIdx.x + i * FWD_T >= nc) continue;
+    if (!ok[i]) continue;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float d = v[i][e] - mu;
       q[0] += d * d;
     }
   }
+  V8<T> gm[NV], bt[NV];  // loaded before the second reduction, in flight across it
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    gm[i].load(gamma + cl[i]);
+    bt[i].load(beta + cl[i]);
+  }
   block_sum<FWD_T, 1>(q, red);
   const float rs = 1.0f / sqrtf(q[0] / (float)h + eps);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int c = threadIdx.x + i * FWD_T;
-    if (c >= nc) continue;
-    float gm[8], bt[8], o[8];
-    load8(gamma + 8 * c, gm);
-    load8(beta + 8 * c, bt);
+    if (!ok[i]) continue;
+    float o[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (v[i][e] - mu) * rs * gm[e] + bt[e];
-    store8(y + base + 8 * c, o);
+    for (int e = 0; e < 8; ++e) o[e] = (v[i][e] - mu) * rs * gm[i][e] + bt[i][e];
+    store8(y + base + cl[i], o);
   }
   if (threadIdx.x == 0) {
     mean[blockIdx.x] = mu;
@@ -164,7 +202,8 @@ __global__ __launch_bounds__(FWD_T) void ln_residual_fwd_kernel(const T* __restr
 }
 
 // Rows [run * rows_per, ...) of the backward pass; writes dr and this run's
-// column partials part[(3 run + j) h + col], j = 0: dy xhat, 1: dy, 2: dr.
+// column partials part[(2 run + j) h + col], j = 0: dy xhat, 1: dy. Loads use
+// clamped chunks and rows (always in range) as in the forward kernel.
 template <typename T, int NV>
 __global__ __launch_bounds__(BWD_T) void ln_residual_bwd_kernel(const T* __restrict__ r, const float* __restrict__ mean,
                                                                 const float* __restrict__ rstd,
@@ -176,26 +215,31 @@ __global__ __launch_bounds__(BWD_T) void ln_residual_bwd_kernel(const T* __restr
   const int nc = h >> 3;
   const long r0 = (long)blockIdx.x * rows_per;
   const long r1 = r0 + rows_per < rows ? r0 + rows_per : rows;
-  V8<T> gm[NV];
-  float ag[NV][8], ab[NV][8], ar[NV][8];
+  int cl[NV];
+  bool ok[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = threadIdx.x + i * BWD_T;
-    if (c < nc) gm[i].load(gamma + 8 * c);
+    ok[i] = c < nc;
+    cl[i] = 8 * (ok[i] ? c : nc - 1);
+  }
+  V8<T> gm[NV], dyv[NV], rv[NV];
+  float ag[NV][8], ab[NV][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ag[i][e] = ab[i][e] = ar[i][e] = 0.f;
+  for (int i = 0; i < NV; ++i) {
+    gm[i].load(gamma + cl[i]);
+    dyv[i].load(dy + r0 * h + cl[i]);
+    rv[i].load(r + r0 * h + cl[i]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ag[i][e] = ab[i][e] = 0.f;
   }
   for (long t = r0; t < r1; ++t) {
     const long base = t * h;
     const float mu = mean[t], rs = rstd[t];
-    V8<T> dyv[NV], rv[NV];
     float s[2] = {0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int c = threadIdx.x + i * BWD_T;
-      if (c >= nc) continue;
-      dyv[i].load(dy + base + 8 * c);
-      rv[i].load(r + base + 8 * c);
+      if (!ok[i]) continue;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float g = dyv[i][e] * gm[i][e];
@@ -203,63 +247,82 @@ __global__ __launch_bounds__(BWD_T) void ln_residual_bwd_kernel(const T* __restr
         s[1] += g * ((rv[i][e] - mu) * rs);
       }
     }
+    // the next row's dy and r (this row again after the last), and this row's
+    // residual gradient, in flight across the reduction
+    const long nb = (t + 1 < r1 ? t + 1 : t) * h;
+    V8<T> dyn[NV], rn[NV], din[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      dyn[i].load(dy + nb + cl[i]);
+      rn[i].load(r + nb + cl[i]);
+    }
+    if (dr_in) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) din[i].load(dr_in + base + cl[i]);
+    }
     block_sum<BWD_T, 2>(s, red);
     const float a = s[0] / (float)h, b = s[1] / (float)h;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int c = threadIdx.x + i * BWD_T;
-      if (c >= nc) continue;
-      float o[8];
-      if (dr_in) load8(dr_in + base + 8 * c, o);
-      else {
+      gm[i].opaque();
+      dyv[i].opaque();
+      rv[i].opaque();
+      if (ok[i]) {
+        float o[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = 0.f;
+        for (int e = 0; e < 8; ++e) {
+          const float xh = (rv[i][e] - mu) * rs;
+          o[e] = (dr_in ? din[i][e] : 0.f) + rs * (dyv[i][e] * gm[i][e] - a - xh * b);
+          ag[i][e] += dyv[i][e] * xh;
+          ab[i][e] += dyv[i][e];
+        }
+        store8(dr + base + cl[i], o);
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float xh = (rv[i][e] - mu) * rs;
-        o[e] += rs * (dyv[i][e] * gm[i][e] - a - xh * b);
-        ag[i][e] += dyv[i][e] * xh;
-        ab[i][e] += dyv[i][e];
-        ar[i][e] += o[e];
-      }
-      store8(dr + base + 8 * c, o);
+      dyv[i] = dyn[i];
+      rv[i] = rn[i];
     }
   }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int c = threadIdx.x + i * BWD_T;
-    if (c >= nc) continue;
-    float* p = part + (long)3 * blockIdx.x * h + 8 * c;
+    if (!ok[i]) continue;
+    float* p = part + (long)2 * blockIdx.x * h + cl[i];
     store8(p, ag[i]);
     store8(p + h, ab[i]);
-    store8(p + 2 * h, ar[i]);
   }
 }
 
-// out_j[col] = sum over runs of part[(3 run + j) h + col], runs in order;
-// 4 column vectors x 64 threads per workgroup, 4 thread rows split the runs
-// (interleaved) and are added in a fixed order.
+// out_j[col] = sum over runs of part[(2 run + j) h + col]: a workgroup covers
+// 64 columns (16 threads x 4) and its 16 thread rows take the runs
+// interleaved (four loads in flight each); the 16 row sums are then added in
+// a fixed order.
 template <typename T>
 __global__ __launch_bounds__(256) void ln_residual_bwd_final_kernel(const float* __restrict__ part, int runs, int h,
-                                                                    T* dgamma, T* dbeta, T* dbias) {
-  __shared__ f32x4 red[3][64];
+                                                                    T* dgamma, T* dbeta) {
+  __shared__ f32x4 red[16][16];
   const int j = blockIdx.y;
-  T* out = j == 0 ? dgamma : (j == 1 ? dbeta : dbias);
-  if (!out) return;  // uniform over the workgroup
-  const int tc = threadIdx.x & 63, tr = threadIdx.x >> 6;
-  const int col = 4 * (blockIdx.x * 64 + tc);
+  T* out = j == 0 ? dgamma : dbeta;
+  const int tc = threadIdx.x & 15, tr = threadIdx.x >> 4;
+  const int col = 4 * (blockIdx.x * 16 + tc);
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
   if (col < h) {
-    for (int w = tr; w < runs; w += 4) s += *(const f32x4*)(part + ((long)3 * w + j) * h + col);
+    for (int w = tr; w < runs; w += 64) {
+      f32x4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (w + 16 * u < runs) x[u] = *(const f32x4*)(part + ((long)2 * (w + 16 * u) + j) * h + col);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (w + 16 * u < runs) s += x[u];
+    }
   }
-  if (tr > 0) red[tr - 1][tc] = s;
+  red[tr][tc] = s;
   __syncthreads();
   if (tr == 0 && col < h) {
+    f32x4 t = red[0][tc];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) s += red[k][tc];
+    for (int k = 1; k < 16; ++k) t += red[k][tc];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) out[col + e] = from_f<T>(s[e]);
+    for (int e = 0; e < 4; ++e) out[col + e] = from_f<T>(t[e]);
   }
 }
 
@@ -281,12 +344,14 @@ hipError_t fwd_t(const LnDesc& d, hipStream_t st) {
   PartPtrs ps{};
   for (int k = 0; k < d.n_parts; ++k) ps.p[k] = d.parts[k];
   const int nv = (d.h / 8 + FWD_T - 1) / FWD_T;
-  switch (nv) {
-    case 1: fwd_nv<T, 1>(d, ps, st); break;
-    case 2: fwd_nv<T, 2>(d, ps, st); break;
-    case 3: fwd_nv<T, 3>(d, ps, st); break;
-    default: return hipErrorInvalidValue;
-  }
+  if (nv <= 1) fwd_nv<T, 1>(d, ps, st);
+  else if (nv <= 2) fwd_nv<T, 2>(d, ps, st);
+  else if (nv <= 4) fwd_nv<T, 4>(d, ps, st);
+  else if (nv <= 6) fwd_nv<T, 6>(d, ps, st);
+  else if (nv <= 8) fwd_nv<T, 8>(d, ps, st);
+  else if (nv <= 10) fwd_nv<T, 10>(d, ps, st);
+  else if (nv <= 12) fwd_nv<T, 12>(d, ps, st);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -313,18 +378,23 @@ hipError_t bwd_t(const LnDesc& d, float* part, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((d.h / 4 + 63) / 64), 3);
+  const dim3 grid((unsigned)((d.h / 4 + 15) / 16), 2);
   hipLaunchKernelGGL(ln_residual_bwd_final_kernel<T>, grid, dim3(256), 0, st, (const float*)part, runs, d.h,
-                     (T*)d.dgamma, (T*)d.dbeta, (T*)d.dbias);
-  return hipGetLastError();
+                     (T*)d.dgamma, (T*)d.dbeta);
+  e = hipGetLastError();
+  if (e != hipSuccess || !d.dbias) return e;
+  return colsum_launch(sizeof(T) == 2 ? DT_BF16 : DT_F32, d.dr, (int)d.T, d.h, d.h, d.dbias,
+                       part + (size_t)2 * runs * d.h, st);
 }
 
 }  // namespace
 
+// Two fp32 partial rows (dgamma, dbeta) per run, then the column-sum
+// workspace of dbias.
 size_t ln_bwd_workspace_bytes(long long rows, int h) {
   if (rows <= 0) return 0;
   int rows_per = 1;
-  return (size_t)ln_runs(rows, rows_per) * 3 * (size_t)h * sizeof(float);
+  return (size_t)ln_runs(rows, rows_per) * 2 * (size_t)h * sizeof(float) + colsum_workspace_bytes((int)rows, h);
 }
 
 hipError_t ln_fwd_launch(int dtype, const LnDesc& d, hipStream_t stream) {

@@ -34,20 +34,34 @@ __global__ __launch_bounds__(256) void colsum_part_vec_kernel(const T* X, int M,
   const int r1 = min(M, r0 + rows_per);
   float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (n0 < N) {
-    for (int r = r0 + rg; r < r1; r += 4) {
-      const T* src = X + (long)r * ld + n0;
-      if constexpr (sizeof(T) == 2) {
-        const bf16x8 v = *(const bf16x8*)src;
+    // rows r0 + rg, r0 + rg + 4, ... added in that order; eight rows' loads in
+    // flight at a time (a row past the run loads row r1 - 1 again, unused, so
+    // that no load sits behind a branch)
+    for (int r = r0 + rg; r < r1; r += 32) {
+      float x[8][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s[e] += (float)v[e];
-      } else {
-        const f32x4 a = *(const f32x4*)src, b = *(const f32x4*)(src + 4);
+      for (int u = 0; u < 8; ++u) {
+        const int ru = min(r + 4 * u, r1 - 1);
+        const T* src = X + (long)ru * ld + n0;
+        if constexpr (sizeof(T) == 2) {
+          const bf16x8 v = *(const bf16x8*)src;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          s[e] += a[e];
-          s[4 + e] += b[e];
+          for (int e = 0; e < 8; ++e) x[u][e] = (float)v[e];
+        } else {
+          const f32x4 a = *(const f32x4*)src, b = *(const f32x4*)(src + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[u][e] = a[e];
+            x[u][4 + e] = b[e];
+          }
         }
       }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (r + 4 * u < r1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s[e] += x[u][e];
+        }
     }
   }
   if (rg > 0) {
