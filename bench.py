@@ -139,8 +139,10 @@ def ln_residual_measure(w, reps: int = 20) -> dict:
     """The residual add + LayerNorm after a block (outside the layer-shard step
     and its metric): one forward + backward per repetition at the workload's
     T x hidden, bf16, one block output (after g), replicated bias, residual
-    gradient. HBM-bound: achieved = algorithmic bytes / average launch-sequence
-    time (HIP events on the library's stream)."""
+    gradient. The bias gradient is left to the block's own backward (its
+    db2 / dbo column sum of the same gradient), so dbias is not requested.
+    HBM-bound: achieved = algorithmic bytes / average launch-sequence time
+    (HIP events on the library's stream)."""
     import torch
     import synth
     import tensor_transformer_layer_tp_amd as tp
@@ -153,14 +155,14 @@ def ln_residual_measure(w, reps: int = 20) -> dict:
     bf = torch.bfloat16
     r, y, dr = (torch.empty((T, h), dtype=bf, device="cuda") for _ in range(3))
     mean, rstd = (torch.empty(T, dtype=torch.float32, device="cuda") for _ in range(2))
-    dg, db, dbias = (torch.empty(h, dtype=bf, device="cuda") for _ in range(3))
+    dg, db = (torch.empty(h, dtype=bf, device="cuda") for _ in range(2))
     ws = torch.empty(tp.tp_ln_workspace_bytes(s), dtype=torch.uint8, device="cuda")
 
     def once():
         tp.tp_ln_residual_fwd(s, dev["resid_in"], dev["parts"], dev["bias"], dev["gamma"], dev["beta"], 1e-5, r, y,
                               mean, rstd)
         tp.tp_ln_residual_bwd(s, r, mean, rstd, dev["gamma"], dev["d_ln_out"], dev["d_resid_out"], dr, dg, db,
-                              dbias, workspace=ws)
+                              None, workspace=ws)
 
     for _ in range(3):
         once()
@@ -172,7 +174,7 @@ def ln_residual_measure(w, reps: int = 20) -> dict:
     res = {}
     # algorithmic bytes: every tensor once (bf16), statistics fp32
     nbytes = {"fwd": 2 * (3 * T * h + 3 * h) + 2 * T * h + 8 * T,   # resid_in, part, bias, gamma, beta -> r, y, stats
-              "bwd": 2 * (3 * T * h + h) + 2 * (T * h + 3 * h) + 8 * T}  # r, dy, dr_in, gamma, stats -> dr, 3 sums
+              "bwd": 2 * (3 * T * h + h) + 2 * (T * h + 2 * h) + 8 * T}  # r, dy, dr_in, gamma, stats -> dr, 2 sums
     for name in ("fwd", "bwd"):
         n, ms = tp.tp_profile_collect(tp.STEPS["ln_" + name])
         avg = ms / max(n, 1)
