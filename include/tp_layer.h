@@ -191,6 +191,45 @@ tp_status tp_ln_residual_bwd(const tp_shape* shape, const void* resid_out, const
                              void* dbeta, void* dbias_or_null, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Vocabulary-parallel logits + cross-entropy of the output layer
+ * (Megatron-LM deep dive, vocabulary-parallel loss fusion section: the
+ * embedding table is split along the vocabulary, each rank computes the
+ * logits of its slice, and the loss exchanges per-token aggregates instead
+ * of the logits; the training-recipe table pads the GPT-2 vocabulary to
+ * 51,200 so that it splits evenly). V = vocab (padded), n = V / tp_size,
+ * rank r owns token ids [v0, v0 + n), v0 = r n. W_i [n, h] is rows v0.. of
+ * the [V, h] table (tied to the input embedding; no bias). labels [T] int32
+ * global token ids; a label outside [0, V) is owned by no rank (its loss is
+ * the log-sum-exp). Needs V % tp_size == 0 (else TP_ERR_DIVISIBILITY), n a
+ * multiple of 8 (else TP_ERR_ALIGN) and n <= 32768 (else TP_ERR_SHAPE); of
+ * shape, batch, seq, hidden, tp_rank, tp_size and dtype are used (the rest is
+ * validated as for every call). Workspace: tp_vocab_workspace_bytes.
+ *
+ * Forward, per rank:
+ *   logits_i = X W_i^T   [T, n] (shape->dtype)    X [T, h]: final hidden states
+ *   stats_i  [3][T] fp32: m = max_j logits_i[t, j], s = sum_j exp(logits_i - m),
+ *            z = logits_i[t, label_t - v0] if the label is in the slice, else 0 */
+size_t tp_vocab_workspace_bytes(const tp_shape* shape, int32_t vocab);
+tp_status tp_vocab_ce_fwd(const tp_shape* shape, int32_t vocab, const void* X, const void* W_i,
+                          const int32_t* labels, void* logits_i, float* stats_i, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* The exchange of the per-token aggregates, emulated on one device over the
+ * ranks' stats (a HOST array of n_parts (1..64) device pointers to [3][T]
+ * fp32): m = max_k m_k, S = sum_k s_k exp(m_k - m), z = sum_k z_k;
+ * lse [T] = m + log S; loss [T] = lse - z (fp32, per token). */
+tp_status tp_vocab_ce_combine(const tp_shape* shape, const float* const* stats, int32_t n_parts,
+                              float* loss, float* lse, void* stream);
+
+/* Backward for the loss sum_t dloss_t loss_t (dloss [T] fp32; 1/T for a mean):
+ *   dlogits = (exp(logits_i - lse) - onehot(label - v0)) * dloss   (workspace)
+ *   dX_i = dlogits W_i [T, h]   this rank's PARTIAL input gradient (f sums it)
+ *   dW_i = dlogits^T X [n, h] */
+tp_status tp_vocab_ce_bwd(const tp_shape* shape, int32_t vocab, const void* X, const void* W_i,
+                          const int32_t* labels, const void* logits_i, const float* lse,
+                          const float* dloss, void* dX_i, void* dW_i, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 /* Steps of the path, for per-step timing. The id doubles as the bit position
  * in tp_profile_enable's mask. */
 enum {
@@ -210,7 +249,13 @@ enum {
   TP_STEP_QKV_DGRAD = 14, /* dX_i = dqkv Wqkv_i^T                            */
   TP_STEP_BIAS_GRADS = 15, /* column sums db1_i, db2, dbo, dbqkv_i           */
   TP_STEP_LN_FWD = 16,     /* residual add + LayerNorm, forward              */
-  TP_STEP_LN_BWD = 17      /* residual add + LayerNorm, backward             */
+  TP_STEP_LN_BWD = 17,     /* residual add + LayerNorm, backward             */
+  TP_STEP_LOGITS = 18,     /* logits_i = X W_i^T                             */
+  TP_STEP_CE_STATS = 19,   /* per-token aggregates of the vocabulary slice   */
+  TP_STEP_CE_COMBINE = 20, /* exchange of the aggregates (emulated)          */
+  TP_STEP_CE_DLOGITS = 21, /* dlogits = (softmax - onehot) dloss             */
+  TP_STEP_LOGITS_DGRAD = 22, /* dX_i = dlogits W_i                           */
+  TP_STEP_LOGITS_WGRAD = 23  /* dW_i = dlogits^T X                           */
 };
 
 /* Measurement aid (no passage of the pages; for benchmarks): while bit k of

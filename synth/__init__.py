@@ -26,7 +26,7 @@ from dataclasses import dataclass, replace
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "draw_shard", "draw_full", "DRAW_ORDER", "draw_ln", "LN_DRAW_ORDER"]
+__all__ = ["Workload", "WORKLOADS", "draw_shard", "draw_full", "DRAW_ORDER", "draw_ln", "LN_DRAW_ORDER", "draw_vocab", "GPT2_VOCAB", "VOCAB_PADDED"]
 
 
 @dataclass(frozen=True)
@@ -151,4 +151,40 @@ def draw_ln(w: Workload, seed: int = 0, n_parts: int = 1, bias_std: float = 0.0)
     out["beta"] = _normal(gen, (h,), 0.1, dt)
     out["d_ln_out"] = _normal(gen, (T, h), 1.0, dt)
     out["d_resid_out"] = _normal(gen, (T, h), 1.0, dt)
+    return out
+
+
+# Output layer: GPT-2's vocabulary padded so that it splits evenly over up to
+# 8 ranks (Megatron-LM deep dive, training-recipe table).
+GPT2_VOCAB = 50257
+VOCAB_PADDED = 51200
+
+
+def draw_vocab(w: Workload, vocab: int = VOCAB_PADDED, seed: int = 0, ranks=None, label_max: int | None = None,
+               dloss: str = "mean") -> dict:
+    """Inputs of the vocabulary-parallel output layer at w's tokens and hidden
+    size, from their own generator: the final hidden states X N(0, 1) (a
+    LayerNorm output), the embedding table N(0, w.w_std^2) -- only the slices
+    of `ranks` (default: all) are returned, as {rank: [V/p, h]} (the whole
+    table is drawn slice by slice in rank order, so any subset is the same
+    numbers) -- labels uniform over [0, label_max) (default: the real GPT-2
+    vocabulary when it fits, so padded ids are never targets), and the loss
+    gradient: 1/T per token for a mean ("mean") or N(0, 1) ("normal")."""
+    gen = torch.Generator().manual_seed(seed)
+    dt = _TORCH_DTYPE[w.dtype]
+    T, h, p = w.tokens, w.hidden, w.tp_size
+    n = vocab // p
+    out = {"X": _normal(gen, (T, h), 1.0, dt), "W": {}}
+    want = set(range(p)) if ranks is None else set(ranks)
+    for r in range(p):
+        t = _normal(gen, (n, h), w.w_std, dt)
+        if r in want:
+            out["W"][r] = t
+    if label_max is None:
+        label_max = GPT2_VOCAB if vocab >= GPT2_VOCAB else vocab
+    out["labels"] = torch.randint(0, label_max, (T,), generator=gen, dtype=torch.int64).to(torch.int32)
+    if dloss == "mean":
+        out["dloss"] = torch.full((T,), 1.0 / max(T, 1), dtype=torch.float32)
+    else:
+        out["dloss"] = torch.randn((T,), generator=gen, dtype=torch.float32)
     return out

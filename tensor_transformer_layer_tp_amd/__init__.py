@@ -22,6 +22,7 @@ __all__ = [
     "exported_symbols", "tp_mlp_workspace_bytes", "tp_attn_workspace_bytes", "tp_mlp_fwd",
     "tp_mlp_bwd", "tp_attn_fwd", "tp_attn_bwd", "tp_sum_partials", "tp_last_error", "tp_profile_enable",
     "tp_profile_collect", "STEPS", "tp_ln_workspace_bytes", "tp_ln_residual_fwd", "tp_ln_residual_bwd",
+    "tp_vocab_workspace_bytes", "tp_vocab_ce_fwd", "tp_vocab_ce_combine", "tp_vocab_ce_bwd",
 ]
 
 TP_FP32, TP_BF16 = 0, 1
@@ -72,6 +73,10 @@ _SIGS = {
     "tp_ln_residual_fwd": (_st, [ctypes.POINTER(TpShape), _vp, ctypes.POINTER(_vp), ctypes.c_int32, _vp, _vp, _vp,
                                  ctypes.c_float, _vp, _vp, _vp, _vp, _vp]),
     "tp_ln_residual_bwd": (_st, [ctypes.POINTER(TpShape)] + [_vp] * 10 + [_vp, _sz, _vp]),
+    "tp_vocab_workspace_bytes": (_sz, [ctypes.POINTER(TpShape), ctypes.c_int32]),
+    "tp_vocab_ce_fwd": (_st, [ctypes.POINTER(TpShape), ctypes.c_int32] + [_vp] * 5 + [_vp, _sz, _vp]),
+    "tp_vocab_ce_combine": (_st, [ctypes.POINTER(TpShape), ctypes.POINTER(_vp), ctypes.c_int32, _vp, _vp, _vp]),
+    "tp_vocab_ce_bwd": (_st, [ctypes.POINTER(TpShape), ctypes.c_int32] + [_vp] * 8 + [_vp, _sz, _vp]),
     "tp_profile_enable": (_st, [ctypes.c_uint32]),
     "tp_profile_collect": (_st, [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)]),
     "tp_last_error": (ctypes.c_char_p, []),
@@ -81,7 +86,8 @@ _SIGS = {
 STEPS = {
     "qkv_proj": 1, "attn_fwd": 2, "out_proj": 3, "fc1": 4, "fc2": 5, "fc2_dgrad": 6, "fc2_wgrad": 7,
     "fc1_wgrad": 8, "fc1_dgrad": 9, "out_dgrad": 10, "out_wgrad": 11, "attn_bwd": 12, "qkv_wgrad": 13,
-    "qkv_dgrad": 14, "bias_grads": 15, "ln_fwd": 16, "ln_bwd": 17,
+    "qkv_dgrad": 14, "bias_grads": 15, "ln_fwd": 16, "ln_bwd": 17, "logits": 18, "ce_stats": 19,
+    "ce_combine": 20, "ce_dlogits": 21, "logits_dgrad": 22, "logits_wgrad": 23,
 }
 
 
@@ -215,3 +221,27 @@ def tp_ln_residual_bwd(shape, resid_out, mean, rstd, gamma, d_ln_out, d_resid_ou
                                              _ptr(gamma), _ptr(d_ln_out), _ptr(d_resid_out_or_null), _ptr(d_resid),
                                              _ptr(dgamma), _ptr(dbeta), _ptr(dbias_or_null), w, wn,
                                              _stream(stream)))
+
+
+def tp_vocab_workspace_bytes(shape: TpShape, vocab: int) -> int:
+    return load_library().tp_vocab_workspace_bytes(ctypes.byref(shape), int(vocab))
+
+
+def tp_vocab_ce_fwd(shape, vocab, X, W_i, labels, logits_i, stats_i, workspace=None, stream=None):
+    """logits_i = X W_i^T and the slice's per-token aggregates (see the header)."""
+    w, wn = _ws(workspace)
+    _check(load_library().tp_vocab_ce_fwd(ctypes.byref(shape), int(vocab), _ptr(X), _ptr(W_i), _ptr(labels),
+                                          _ptr(logits_i), _ptr(stats_i), w, wn, _stream(stream)))
+
+
+def tp_vocab_ce_combine(shape, stats, loss, lse, stream=None):
+    arr = (_vp * len(stats))(*[_ptr(p) for p in stats])
+    _check(load_library().tp_vocab_ce_combine(ctypes.byref(shape), arr, len(stats), _ptr(loss), _ptr(lse),
+                                              _stream(stream)))
+
+
+def tp_vocab_ce_bwd(shape, vocab, X, W_i, labels, logits_i, lse, dloss, dX_i, dW_i, workspace=None, stream=None):
+    w, wn = _ws(workspace)
+    _check(load_library().tp_vocab_ce_bwd(ctypes.byref(shape), int(vocab), _ptr(X), _ptr(W_i), _ptr(labels),
+                                          _ptr(logits_i), _ptr(lse), _ptr(dloss), _ptr(dX_i), _ptr(dW_i), w, wn,
+                                          _stream(stream)))

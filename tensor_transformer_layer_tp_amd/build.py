@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "lib", "libtp_layer.so")
 SOURCES = ["tp_layer.cpp", "gemm_mfma.hip", "gemm_simt.hip", "attn_mfma.hip", "attn_simt.hip", "reduce.hip",
-           "ln_residual.hip"]
+           "ln_residual.hip", "vocab_ce.hip"]
 ARCH = os.environ.get("TP_LAYER_ARCH", "gfx950")
 
 

@@ -566,6 +566,11 @@ TP_GEMM_KERNELS(gemm_fc2_wgrad, 4, false, false, EPI_STORE)
 TP_GEMM_KERNELS(gemm_fc1_wgrad, 4, false, false, EPI_STORE)
 TP_GEMM_KERNELS(gemm_out_wgrad, 4, false, false, EPI_STORE)
 TP_GEMM_KERNELS(gemm_qkv_wgrad, 4, false, false, EPI_STORE)
+// vocabulary-parallel output layer: logits = X W_i^T (the table slice W_i
+// [V/p, h] is k-inner), dX = dlogits W_i, dW_i = dlogits^T X
+TP_GEMM_KERNELS(gemm_logits, 8, true, true, EPI_STORE)
+TP_GEMM_KERNELS(gemm_logits_dgrad, 8, true, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_logits_wgrad, 4, false, false, EPI_STORE)
 #undef TP_GEMM_KERNELS
 
 namespace {
@@ -687,6 +692,9 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
     TP_ROLE(GR_FC1_WGRAD, gemm_fc1_wgrad, 4, false, false, EPI_STORE)
     TP_ROLE(GR_OUT_WGRAD, gemm_out_wgrad, 4, false, false, EPI_STORE)
     TP_ROLE(GR_QKV_WGRAD, gemm_qkv_wgrad, 4, false, false, EPI_STORE)
+    TP_ROLE(GR_LOGITS, gemm_logits, 8, true, true, EPI_STORE)
+    TP_ROLE(GR_LOGITS_DGRAD, gemm_logits_dgrad, 8, true, false, EPI_STORE)
+    TP_ROLE(GR_LOGITS_WGRAD, gemm_logits_wgrad, 4, false, false, EPI_STORE)
     default: return hipErrorInvalidValue;
   }
 #undef TP_ROLE

@@ -23,7 +23,7 @@ enum Epi : int {
 enum GemmRole : int {
   GR_QKV_PROJ = 1, GR_OUT_PROJ = 3, GR_FC1 = 4, GR_FC2 = 5, GR_FC2_DGRAD = 6, GR_FC2_WGRAD = 7,
   GR_FC1_WGRAD = 8, GR_FC1_DGRAD = 9, GR_OUT_DGRAD = 10, GR_OUT_WGRAD = 11, GR_QKV_WGRAD = 13,
-  GR_QKV_DGRAD = 14,
+  GR_QKV_DGRAD = 14, GR_LOGITS = 18, GR_LOGITS_DGRAD = 22, GR_LOGITS_WGRAD = 23,
 };
 
 // C[M,N] = op(A) op(B) with fp32 accumulation, then an epilogue.
@@ -108,6 +108,23 @@ struct LnDesc {
 size_t ln_bwd_workspace_bytes(long long rows, int h);
 hipError_t ln_fwd_launch(int dtype, const LnDesc& d, hipStream_t stream);
 hipError_t ln_bwd_launch(int dtype, const LnDesc& d, void* ws, hipStream_t stream);
+
+// Vocabulary-parallel cross-entropy of one rank's slice [v0, v0 + n) of the
+// vocabulary (n a multiple of 8, at most kCeMaxSlice).
+constexpr int kCeMaxSlice = 32768;
+struct CeDesc {
+  long long T = 0;  // tokens
+  int n = 0, v0 = 0;
+  const void* logits = nullptr;  // [T, n]
+  const int* labels = nullptr;   // [T] global token ids
+  float* stats = nullptr;        // [3][T]: m, s, z (ce_stats)
+  const float* lse = nullptr;    // [T] (ce_dlogits)
+  const float* dloss = nullptr;  // [T]
+};
+hipError_t ce_stats_launch(int dtype, const CeDesc& d, hipStream_t stream);
+hipError_t ce_combine_launch(const float* const* stats, int n_parts, long long rows, float* loss, float* lse,
+                             hipStream_t stream);
+hipError_t ce_dlogits_launch(int dtype, const CeDesc& d, void* dl, hipStream_t stream);
 
 // Fill rows x cols (leading dimension ld) of dtype elements with zero.
 hipError_t zero_launch(int dtype, void* p, long long rows, long long cols, long long ld,

@@ -249,6 +249,43 @@ tp_status check_ln(const Dims& dm) {
   return TP_OK;
 }
 
+// Vocabulary-parallel output layer: the rank's slice [v0, v0 + n) of a vocab
+// of V = vocab rows, n = V / tp_size.
+struct VocabDims {
+  int n, v0;
+};
+tp_status check_vocab(const tp_shape* s, const Dims& dm, int32_t vocab, VocabDims& vd) {
+  if (vocab <= 0 || vocab > kMaxDim) return fail(TP_ERR_SHAPE, "vocab %d outside [1, 2^22]", vocab);
+  if (vocab % s->tp_size) return fail(TP_ERR_DIVISIBILITY, "vocab %d not divisible by tp_size %d", vocab, s->tp_size);
+  vd.n = vocab / s->tp_size;
+  vd.v0 = s->tp_rank * vd.n;
+  if (vd.n % 8) return fail(TP_ERR_ALIGN, "vocab / tp_size = %d is not a multiple of 8", vd.n);
+  if (vd.n > kCeMaxSlice) return fail(TP_ERR_SHAPE, "vocab / tp_size = %d exceeds %d", vd.n, kCeMaxSlice);
+  if (dm.T * vd.n >= kMaxElems || (long long)vd.n * dm.h >= kMaxElems)
+    return fail(TP_ERR_SHAPE, "a tensor of this shape has >= 2^30 elements");
+  return TP_OK;
+}
+
+struct VocabPlan {
+  void *dl, *gemm_ws;
+  size_t gemm_bytes, total;
+};
+
+VocabPlan plan_vocab(const Dims& dm, const VocabDims& vd, void* ws, bool bwd) {
+  Bump bp(ws);
+  VocabPlan pl{};
+  const int dt = dm.dtype, T = (int)dm.T, h = (int)dm.h, n = vd.n;
+  size_t g = gemm_workspace_bytes(dt, T, n, h);
+  if (bwd) {
+    pl.dl = bp.take((size_t)(dm.T * n) * dm.esz);
+    g = max3(g, gemm_workspace_bytes(dt, T, h, n), gemm_workspace_bytes(dt, n, h, T));
+  }
+  pl.gemm_bytes = g;
+  pl.gemm_ws = bp.take(g);
+  pl.total = bp.off;
+  return pl;
+}
+
 GemmDesc gd(int role, int M, int N, int K, const void* A, long lda, bool ak, const void* B, long ldb, bool bk,
             int epi, void* C, long ldc) {
   GemmDesc g;
@@ -508,6 +545,87 @@ tp_status tp_ln_residual_bwd(const tp_shape* shape, const void* resid_out, const
   d.dgamma = dgamma; d.dbeta = dbeta; d.dbias = dbias_or_null;
   hipStream_t st = (hipStream_t)stream;
   TP_STEP(TP_STEP_LN_BWD, ln_bwd_launch(dm.dtype, d, workspace, st), "residual add + LayerNorm backward");
+  return TP_OK;
+}
+
+size_t tp_vocab_workspace_bytes(const tp_shape* shape, int32_t vocab) {
+  Dims dm;
+  VocabDims vd;
+  if (check_shape(shape, dm) != TP_OK || check_vocab(shape, dm, vocab, vd) != TP_OK) return 0;
+  const VocabPlan a = plan_vocab(dm, vd, nullptr, false), b = plan_vocab(dm, vd, nullptr, true);
+  return a.total > b.total ? a.total : b.total;
+}
+
+tp_status tp_vocab_ce_fwd(const tp_shape* shape, int32_t vocab, const void* X, const void* W_i, const int32_t* labels,
+                          void* logits_i, float* stats_i, void* workspace, size_t workspace_bytes, void* stream) {
+  Dims dm;
+  VocabDims vd;
+  TP_CHECK(check_shape(shape, dm));
+  TP_CHECK(check_vocab(shape, dm, vocab, vd));
+  const bool e = dm.T == 0;
+  TP_CHECK(check_ptr(X, "X", e));
+  TP_CHECK(check_ptr(W_i, "W_i", false));
+  TP_CHECK(check_ptr(labels, "labels", e));
+  TP_CHECK(check_ptr(logits_i, "logits_i", e));
+  TP_CHECK(check_ptr(stats_i, "stats_i", e));
+  TP_CHECK(check_ws(workspace, workspace_bytes, plan_vocab(dm, vd, nullptr, false).total));
+  if (e) return TP_OK;
+  const VocabPlan pl = plan_vocab(dm, vd, workspace, false);
+  hipStream_t st = (hipStream_t)stream;
+  const int dt = dm.dtype, T = (int)dm.T, h = (int)dm.h, n = vd.n;
+  TP_STEP(TP_STEP_LOGITS, gemm_launch(dt, gd(GR_LOGITS, T, n, h, X, h, true, W_i, h, true, EPI_STORE, logits_i, n), pl.gemm_ws, pl.gemm_bytes, st),
+         "vocab logits X W_i^T");
+  CeDesc c;
+  c.T = dm.T; c.n = n; c.v0 = vd.v0; c.logits = logits_i; c.labels = labels; c.stats = stats_i;
+  TP_STEP(TP_STEP_CE_STATS, ce_stats_launch(dt, c, st), "cross-entropy slice aggregates");
+  return TP_OK;
+}
+
+tp_status tp_vocab_ce_combine(const tp_shape* shape, const float* const* stats, int32_t n_parts, float* loss,
+                              float* lse, void* stream) {
+  Dims dm;
+  TP_CHECK(check_shape(shape, dm));
+  const bool e = dm.T == 0;
+  if (!stats) return fail(TP_ERR_NULL, "stats is NULL");
+  if (n_parts < 1 || n_parts > 64) return fail(TP_ERR_SHAPE, "n_parts %d outside [1, 64]", n_parts);
+  for (int k = 0; k < n_parts; ++k) TP_CHECK(check_ptr(stats[k], "stats[k]", e));
+  TP_CHECK(check_ptr(loss, "loss", e));
+  TP_CHECK(check_ptr(lse, "lse", e));
+  if (e) return TP_OK;
+  hipStream_t st = (hipStream_t)stream;
+  TP_STEP(TP_STEP_CE_COMBINE, ce_combine_launch(stats, n_parts, dm.T, loss, lse, st), "cross-entropy exchange (emulated)");
+  return TP_OK;
+}
+
+tp_status tp_vocab_ce_bwd(const tp_shape* shape, int32_t vocab, const void* X, const void* W_i, const int32_t* labels,
+                          const void* logits_i, const float* lse, const float* dloss, void* dX_i, void* dW_i,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  Dims dm;
+  VocabDims vd;
+  TP_CHECK(check_shape(shape, dm));
+  TP_CHECK(check_vocab(shape, dm, vocab, vd));
+  const bool e = dm.T == 0;
+  TP_CHECK(check_ptr(X, "X", e));
+  TP_CHECK(check_ptr(W_i, "W_i", false));
+  TP_CHECK(check_ptr(labels, "labels", e));
+  TP_CHECK(check_ptr(logits_i, "logits_i", e));
+  TP_CHECK(check_ptr(lse, "lse", e));
+  TP_CHECK(check_ptr(dloss, "dloss", e));
+  TP_CHECK(check_ptr(dX_i, "dX_i", e));
+  TP_CHECK(check_ptr(dW_i, "dW_i", false));
+  TP_CHECK(check_ws(workspace, workspace_bytes, plan_vocab(dm, vd, nullptr, true).total));
+  const VocabPlan pl = plan_vocab(dm, vd, workspace, true);
+  hipStream_t st = (hipStream_t)stream;
+  const int dt = dm.dtype, T = (int)dm.T, h = (int)dm.h, n = vd.n;
+  if (T > 0) {
+    CeDesc c;
+    c.T = dm.T; c.n = n; c.v0 = vd.v0; c.logits = logits_i; c.labels = labels; c.lse = lse; c.dloss = dloss;
+    TP_STEP(TP_STEP_CE_DLOGITS, ce_dlogits_launch(dt, c, pl.dl, st), "cross-entropy dlogits");
+    TP_STEP(TP_STEP_LOGITS_DGRAD, gemm_launch(dt, gd(GR_LOGITS_DGRAD, T, h, n, pl.dl, n, true, W_i, h, false, EPI_STORE, dX_i, h), pl.gemm_ws, pl.gemm_bytes, st),
+           "vocab dgrad dX_i = dlogits W_i");
+  }
+  TP_STEP(TP_STEP_LOGITS_WGRAD, gemm_launch(dt, gd(GR_LOGITS_WGRAD, n, h, T, pl.dl, n, false, X, h, false, EPI_STORE, dW_i, h), pl.gemm_ws, pl.gemm_bytes, st),
+         "vocab wgrad dW_i = dlogits^T X");
   return TP_OK;
 }
 
