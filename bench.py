@@ -188,6 +188,74 @@ def ln_residual_measure(w, reps: int = 20) -> dict:
             **res}
 
 
+def vocab_ce_measure(reps: int = 10) -> dict:
+    """The vocabulary-parallel output layer (outside the layer-shard step and
+    its metric), at the 8.3B-like shard (16384 tokens, hidden 3072) with the
+    padded GPT-2 vocabulary of 51,200 over 8 ranks, rank 0 (6,400 vocabulary
+    rows): logits GEMM + slice aggregates, the emulated exchange over 8
+    ranks' aggregates (rank 0's stand in for all: timing only), dlogits, and
+    the input- and table-gradient GEMMs. GEMMs against the MFMA peak (2 T n h
+    flops each), the row kernels against HBM (algorithmic bytes)."""
+    import torch
+    import synth
+    import tensor_transformer_layer_tp_amd as tp
+
+    w = synth.WORKLOADS["gpt_8p3b_tp8"]
+    V = synth.VOCAB_PADDED
+    T, h, n = w.tokens, w.hidden, V // w.tp_size
+    inp = synth.draw_vocab(w, V, seed=0, ranks=(0,), dloss="mean")
+    s = tp.TpShape.make(batch=w.batch, seq=w.seq, hidden=w.hidden, ffn=w.ffn, n_heads=w.n_heads,
+                        head_dim=w.head_dim, tp_rank=0, tp_size=w.tp_size, dtype=w.dtype)
+    X, W0 = inp["X"].cuda(), inp["W"][0].cuda()
+    labels, dloss = inp["labels"].cuda(), inp["dloss"].cuda()
+    bf = torch.bfloat16
+    logits = torch.empty((T, n), dtype=bf, device="cuda")
+    stats = torch.empty(3 * T, dtype=torch.float32, device="cuda")
+    loss, lse = (torch.empty(T, dtype=torch.float32, device="cuda") for _ in range(2))
+    dX = torch.empty((T, h), dtype=bf, device="cuda")
+    dW = torch.empty((n, h), dtype=bf, device="cuda")
+    ws = torch.empty(tp.tp_vocab_workspace_bytes(s, V), dtype=torch.uint8, device="cuda")
+
+    def once():
+        tp.tp_vocab_ce_fwd(s, V, X, W0, labels, logits, stats, workspace=ws)
+        tp.tp_vocab_ce_combine(s, [stats] * w.tp_size, loss, lse)
+        tp.tp_vocab_ce_bwd(s, V, X, W0, labels, logits, lse, dloss, dX, dW, workspace=ws)
+
+    for _ in range(2):
+        once()
+    torch.cuda.synchronize()
+    names = ("logits", "ce_stats", "ce_combine", "ce_dlogits", "logits_dgrad", "logits_wgrad")
+    tp.tp_profile_enable(sum(1 << tp.STEPS[k] for k in names))
+    for _ in range(reps):
+        once()
+    torch.cuda.synchronize()
+    gemm = 2.0 * T * n * h
+    work = {"logits": ("mfma", gemm), "logits_dgrad": ("mfma", gemm), "logits_wgrad": ("mfma", gemm),
+            "ce_stats": ("hbm", 2 * T * n + 4 * T + 12 * T),                 # logits, labels -> 3 aggregates
+            "ce_combine": ("hbm", 12 * T * w.tp_size + 8 * T),             # every rank's aggregates -> loss, lse
+            "ce_dlogits": ("hbm", 2 * T * n * 2 + 12 * T)}                 # logits -> dlogits (+ labels, lse, dloss)
+    res, fwd_ms, bwd_ms = {}, 0.0, 0.0
+    for k in names:
+        cnt, ms = tp.tp_profile_collect(tp.STEPS[k])
+        avg = ms / max(cnt, 1)
+        bound, amount = work[k]
+        if bound == "mfma":
+            ach, unit, peak = amount / (avg / 1e3) / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS
+        else:
+            ach, unit, peak = amount / (avg / 1e3) / 1e9, "GB/s", PEAK_HBM_GBS
+        res[k] = {"avg_launch_ms": round(avg, 4), "bound": bound, "achieved": round(ach, 1), "unit": unit,
+                  "frac": round(ach / peak, 4)}
+        if k in ("logits", "ce_stats", "ce_combine"):
+            fwd_ms += avg
+        else:
+            bwd_ms += avg
+        log(f"  vocab {k:12s} {avg * 1e3:8.1f} us  {ach:8.1f} {unit} ({100 * ach / peak:.1f}% of peak)")
+    tp.tp_profile_enable(0)
+    return {"workload": f"gpt_8p3b_tp8 output layer: T={T}, hidden={h}, vocab {V} over {w.tp_size} ranks "
+                        f"(rank 0: {n} rows), bf16", "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+            "steps": res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,6 +264,7 @@ def main():
     ap.add_argument("--workload", default="mtnlg_530b_tp8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ln", action="store_true", help="skip the residual + LayerNorm measurement")
+    ap.add_argument("--no-vocab", action="store_true", help="skip the vocabulary-parallel output-layer measurement")
     ap.add_argument("--cpu-target-s", type=float, default=15.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run device-to-device copies of this many MiB (calibrates byte counters)")
@@ -290,6 +359,11 @@ def main():
         log("residual add + LayerNorm (measured apart from the step)")
         ln = ln_residual_measure(w)
 
+    vocab = None
+    if not a.no_vocab:
+        log("vocabulary-parallel logits + cross-entropy (measured apart from the step)")
+        vocab = vocab_ce_measure()
+
     cpu = None
     if not a.no_cpu_baseline:
         log("cpu baseline (fp64 oracle on a bounded sample)")
@@ -309,6 +383,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "ln_residual": ln,
+        "vocab_ce": vocab,
     }
     print(json.dumps(out), flush=True)
 
