@@ -1,7 +1,8 @@
 """fp64 CPU oracle for one tensor-parallel rank's share of a Megatron-style
 Transformer layer (MLP block and causal self-attention block, forward and
 backward), of the residual add + LayerNorm that follows each block, and of the
-vocabulary-parallel logits + cross-entropy of the output layer.
+vocabulary-parallel logits + cross-entropy of the output layer; attention
+dropout masks from a counter-based generator.
 
 TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
 baseline leg may import this package. The product path (the HIP library and
@@ -26,3 +27,4 @@ from .tp_layer import (  # noqa: F401
 )
 from .ln_residual import ln_residual_fwd, ln_residual_bwd  # noqa: F401
 from .vocab_ce import vocab_shard, logits_fwd, ce_partial_stats, ce_combine, ce_bwd  # noqa: F401
+from .dropout import philox4x64_10, keep_threshold, keep_scale, attention_multipliers  # noqa: F401

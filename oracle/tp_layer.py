@@ -139,9 +139,12 @@ def _softmax_rows(S):
     return E / den, (mx + np.log(den))[:, 0]
 
 
-def attn_core_fwd(qkv, *, batch, seq, n_local, head_dim, head0, n_heads, causal=True, alibi=False):
+def attn_core_fwd(qkv, *, batch, seq, n_local, head_dim, head0, n_heads, causal=True, alibi=False, dropout=None):
     """Per batch element and local head l (global head k = head0 + l + 1):
     ctx = softmax(q k^T / sqrt(d) + bias) v, lse = log-sum-exp of each score row.
+    With dropout multipliers D [batch, n_local, seq, seq] (keep * scale, see
+    oracle.dropout), the probabilities are multiplied by D before the value
+    aggregation (the softmax and lse are those of the undropped scores).
     qkv [T, 3h_l] -> ctx [T, h_l], lse [batch, n_local, seq]."""
     h_l = n_local * head_dim
     ctx = np.zeros((batch * seq, h_l))
@@ -153,15 +156,19 @@ def attn_core_fwd(qkv, *, batch, seq, n_local, head_dim, head0, n_heads, causal=
             slope = alibi_slope(head0 + l + 1, n_heads) if alibi else None
             S = _scores(qkv[rows, cq], qkv[rows, ck], head_dim, causal, slope)
             P, lse_h = _softmax_rows(S)
+            if dropout is not None:
+                P = P * dropout[bi, l]
             ctx[rows, cq] = P @ qkv[rows, cv]
             lse[bi, l] = lse_h
     return ctx, lse
 
 
-def attn_core_bwd(qkv, dctx, *, batch, seq, n_local, head_dim, head0, n_heads, causal=True, alibi=False):
+def attn_core_bwd(qkv, dctx, *, batch, seq, n_local, head_dim, head0, n_heads, causal=True, alibi=False,
+                  dropout=None):
     """Gradient of <ctx, dctx> with respect to qkv, per head:
     dv = P^T dc, dP = dc v^T, dS = P * (dP - rowsum(P * dP)),
-    dq = dS k / sqrt(d), dk = dS^T q / sqrt(d)."""
+    dq = dS k / sqrt(d), dk = dS^T q / sqrt(d).
+    With dropout multipliers D: dv = (P D)^T dc and dP = D * (dc v^T)."""
     h_l = n_local * head_dim
     dqkv = np.zeros_like(qkv)
     for bi in range(batch):
@@ -171,26 +178,28 @@ def attn_core_bwd(qkv, dctx, *, batch, seq, n_local, head_dim, head0, n_heads, c
             slope = alibi_slope(head0 + l + 1, n_heads) if alibi else None
             q, k, v = qkv[rows, cq], qkv[rows, ck], qkv[rows, cv]
             P, _ = _softmax_rows(_scores(q, k, head_dim, causal, slope))
+            Dm = 1.0 if dropout is None else dropout[bi, l]
             dc = dctx[rows, cq]
-            dP = dc @ v.T
+            dP = (dc @ v.T) * Dm
             dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
             dqkv[rows, cq] = (dS @ k) / math.sqrt(head_dim)
             dqkv[rows, ck] = (dS.T @ q) / math.sqrt(head_dim)
-            dqkv[rows, cv] = P.T @ dc
+            dqkv[rows, cv] = (P * Dm).T @ dc
     return dqkv
 
 
-def _core_kw(Wqkv_r, batch, seq, n_heads, tp_size, tp_rank, causal, alibi):
+def _core_kw(Wqkv_r, batch, seq, n_heads, tp_size, tp_rank, causal, alibi, dropout=None):
     h_l = Wqkv_r.shape[1] // 3
     n_l = n_heads // tp_size
     return dict(batch=batch, seq=seq, n_local=n_l, head_dim=h_l // n_l, head0=tp_rank * n_l,
-                n_heads=n_heads, causal=causal, alibi=alibi)
+                n_heads=n_heads, causal=causal, alibi=alibi, dropout=dropout)
 
 
 def attn_fwd(X, Wqkv_r, bqkv_r, Wo_r, *, batch, seq, n_heads, tp_size, tp_rank,
-             causal=True, alibi=False):
-    """Returns qkv_r [T, 3h_l], ctx_r [T, h_l], lse_r [batch, n_l, seq], O_r [T, h] (partial)."""
-    kw = _core_kw(Wqkv_r, batch, seq, n_heads, tp_size, tp_rank, causal, alibi)
+             causal=True, alibi=False, dropout=None):
+    """Returns qkv_r [T, 3h_l], ctx_r [T, h_l], lse_r [batch, n_l, seq], O_r [T, h] (partial).
+    dropout: optional multipliers [batch, n_l, seq, seq] on the attention probabilities."""
+    kw = _core_kw(Wqkv_r, batch, seq, n_heads, tp_size, tp_rank, causal, alibi, dropout)
     qkv = X @ Wqkv_r + bqkv_r
     ctx, lse = attn_core_fwd(qkv, **kw)
     O_r = ctx @ Wo_r
@@ -198,10 +207,10 @@ def attn_fwd(X, Wqkv_r, bqkv_r, Wo_r, *, batch, seq, n_heads, tp_size, tp_rank,
 
 
 def attn_bwd(X, Wqkv_r, bqkv_r, Wo_r, dO, *, batch, seq, n_heads, tp_size, tp_rank,
-             causal=True, alibi=False):
+             causal=True, alibi=False, dropout=None):
     """Gradients of <O_r + bo, dO>. Recomputes the forward from X.
     Returns dX_r (partial), dWqkv_r, dbqkv_r, dWo_r, dbo (replicated, once)."""
-    kw = _core_kw(Wqkv_r, batch, seq, n_heads, tp_size, tp_rank, causal, alibi)
+    kw = _core_kw(Wqkv_r, batch, seq, n_heads, tp_size, tp_rank, causal, alibi, dropout)
     qkv = X @ Wqkv_r + bqkv_r
     ctx, _ = attn_core_fwd(qkv, **kw)
     dC = dO @ Wo_r.T
