@@ -142,6 +142,39 @@ tp_status tp_attn_bwd(const tp_shape* shape, const void* X, const void* Wqkv_i, 
                       void* dX_i, void* dWqkv_i, void* dbqkv_i, void* dWo_i, void* dbo_or_null,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* Attention-probability dropout (Megatron-LM deep dive: dropout 0.1 in the
+ * training setup; inside the model-parallel region each rank draws independent
+ * random numbers). The variants below apply it inside the flash-style kernels
+ * (bf16 matrix-core path only: shape->dtype TP_BF16 and head_dim 64, 96, 128
+ * or 160, else TP_ERR_DTYPE / TP_ERR_HEADDIM):
+ *   ctx = (softmax(S) * keep * scale) v,  lse as without dropout,
+ * with keep drawn by Philox4x64-10 (Salmon et al., SC 2011) for element
+ * (batch b, global head k, query i, key j) at counter
+ * (i, j / 32, b * 2^32 + k, ((j % 32) / 4) % 2) with key (seed, offset): its
+ * 16-bit lane 4 ((j % 32) / 8) + j % 4 is kept iff >= thr = round(65536 p),
+ * scale = 65536 / (65536 - thr). Ranks own different global heads, so one
+ * seed gives each rank independent numbers. The forward stores the keep bits
+ * in mask_i (tp_attn_dropout_mask_bytes bytes, device memory, 16-byte
+ * aligned; layout [batch][n_l][ceil(seq/32)][2][seq rounded up to 8] of
+ * 16-bit words); the backward reads them (pass the same p). p = 0 gives the
+ * results of tp_attn_fwd / tp_attn_bwd. p outside [0, 1) is TP_ERR_SHAPE. */
+typedef struct {
+  float p;          /* drop probability, 0 <= p < 1 */
+  uint64_t seed;    /* Philox key word 0 */
+  uint64_t offset;  /* Philox key word 1 (e.g. a step or layer counter) */
+} tp_dropout;
+
+size_t tp_attn_dropout_mask_bytes(const tp_shape* shape);
+tp_status tp_attn_fwd_dropout(const tp_shape* shape, const tp_dropout* dropout, const void* X,
+                              const void* Wqkv_i, const void* bqkv_i, const void* Wo_i, float* qkv_i,
+                              void* ctx_i, float* lse_i, uint16_t* mask_i, void* O_i, void* workspace,
+                              size_t workspace_bytes, void* stream);
+tp_status tp_attn_bwd_dropout(const tp_shape* shape, const tp_dropout* dropout, const void* X,
+                              const void* Wqkv_i, const void* Wo_i, const float* qkv_i,
+                              const void* ctx_i, const float* lse_i, const uint16_t* mask_i,
+                              const void* dO, void* dX_i, void* dWqkv_i, void* dbqkv_i, void* dWo_i,
+                              void* dbo_or_null, void* workspace, size_t workspace_bytes, void* stream);
+
 /* The f / g all-reduce emulated on one device (Megatron-LM deep dive, Fig. 4):
  *   out [T,h] = sum_{k < n_parts} parts[k] + bias   (fp32 accumulation, rounded
  * once). parts is a HOST array of n_parts (1..64) device pointers to [T,h]

@@ -22,7 +22,8 @@ __all__ = [
     "exported_symbols", "tp_mlp_workspace_bytes", "tp_attn_workspace_bytes", "tp_mlp_fwd",
     "tp_mlp_bwd", "tp_attn_fwd", "tp_attn_bwd", "tp_sum_partials", "tp_last_error", "tp_profile_enable",
     "tp_profile_collect", "STEPS", "tp_ln_workspace_bytes", "tp_ln_residual_fwd", "tp_ln_residual_bwd",
-    "tp_vocab_workspace_bytes", "tp_vocab_ce_fwd", "tp_vocab_ce_combine", "tp_vocab_ce_bwd",
+    "tp_vocab_workspace_bytes", "tp_vocab_ce_fwd", "tp_vocab_ce_combine", "tp_vocab_ce_bwd", "TpDropout",
+    "tp_attn_dropout_mask_bytes", "tp_attn_fwd_dropout", "tp_attn_bwd_dropout",
 ]
 
 TP_FP32, TP_BF16 = 0, 1
@@ -59,6 +60,11 @@ class TpShape(ctypes.Structure):
         return cls(batch, seq, hidden, ffn, n_heads, head_dim, tp_rank, tp_size, dtype, int(causal), int(alibi))
 
 
+class TpDropout(ctypes.Structure):
+    """Mirror of tp_dropout: drop probability and the Philox key (seed, offset)."""
+    _fields_ = [("p", ctypes.c_float), ("seed", ctypes.c_uint64), ("offset", ctypes.c_uint64)]
+
+
 _lib = None
 _vp, _sz, _st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
 _SIGS = {
@@ -77,6 +83,9 @@ _SIGS = {
     "tp_vocab_ce_fwd": (_st, [ctypes.POINTER(TpShape), ctypes.c_int32] + [_vp] * 5 + [_vp, _sz, _vp]),
     "tp_vocab_ce_combine": (_st, [ctypes.POINTER(TpShape), ctypes.POINTER(_vp), ctypes.c_int32, _vp, _vp, _vp]),
     "tp_vocab_ce_bwd": (_st, [ctypes.POINTER(TpShape), ctypes.c_int32] + [_vp] * 8 + [_vp, _sz, _vp]),
+    "tp_attn_dropout_mask_bytes": (_sz, [ctypes.POINTER(TpShape)]),
+    "tp_attn_fwd_dropout": (_st, [ctypes.POINTER(TpShape), ctypes.POINTER(TpDropout)] + [_vp] * 9 + [_vp, _sz, _vp]),
+    "tp_attn_bwd_dropout": (_st, [ctypes.POINTER(TpShape), ctypes.POINTER(TpDropout)] + [_vp] * 13 + [_vp, _sz, _vp]),
     "tp_profile_enable": (_st, [ctypes.c_uint32]),
     "tp_profile_collect": (_st, [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)]),
     "tp_last_error": (ctypes.c_char_p, []),
@@ -245,3 +254,29 @@ def tp_vocab_ce_bwd(shape, vocab, X, W_i, labels, logits_i, lse, dloss, dX_i, dW
     _check(load_library().tp_vocab_ce_bwd(ctypes.byref(shape), int(vocab), _ptr(X), _ptr(W_i), _ptr(labels),
                                           _ptr(logits_i), _ptr(lse), _ptr(dloss), _ptr(dX_i), _ptr(dW_i), w, wn,
                                           _stream(stream)))
+
+
+def tp_attn_dropout_mask_bytes(shape: TpShape) -> int:
+    return load_library().tp_attn_dropout_mask_bytes(ctypes.byref(shape))
+
+
+def _drop(dropout):
+    return None if dropout is None else ctypes.byref(dropout)
+
+
+def tp_attn_fwd_dropout(shape, dropout, X, Wqkv_i, bqkv_i, Wo_i, qkv_i, ctx_i, lse_i, mask_i, O_i, workspace=None,
+                        stream=None):
+    """tp_attn_fwd with attention-probability dropout; mask_i receives the keep bits."""
+    w, wn = _ws(workspace)
+    _check(load_library().tp_attn_fwd_dropout(ctypes.byref(shape), _drop(dropout), _ptr(X), _ptr(Wqkv_i),
+                                              _ptr(bqkv_i), _ptr(Wo_i), _ptr(qkv_i), _ptr(ctx_i), _ptr(lse_i),
+                                              _ptr(mask_i), _ptr(O_i), w, wn, _stream(stream)))
+
+
+def tp_attn_bwd_dropout(shape, dropout, X, Wqkv_i, Wo_i, qkv_i, ctx_i, lse_i, mask_i, dO, dX_i, dWqkv_i, dbqkv_i,
+                        dWo_i, dbo_or_null=None, workspace=None, stream=None):
+    w, wn = _ws(workspace)
+    _check(load_library().tp_attn_bwd_dropout(ctypes.byref(shape), _drop(dropout), _ptr(X), _ptr(Wqkv_i),
+                                              _ptr(Wo_i), _ptr(qkv_i), _ptr(ctx_i), _ptr(lse_i), _ptr(mask_i),
+                                              _ptr(dO), _ptr(dX_i), _ptr(dWqkv_i), _ptr(dbqkv_i), _ptr(dWo_i),
+                                              _ptr(dbo_or_null), w, wn, _stream(stream)))

@@ -34,6 +34,16 @@
 // Backward: dK/dV per 32-key wave (workgroup = 128 keys, looping over 64-query
 // tiles), dQ per 32-query wave (looping over 64-key tiles); both recompute P
 // from lse, dS = P (dP - delta) with delta = rowsum(dctx * ctx). No atomics.
+//
+// Dropout variants (DO): the forward draws, per lane and 32-key block, one
+// Philox4x64-10 block at counter (query, key block, batch << 32 | global head,
+// g) with key (seed, offset): 16 uniforms of 16 bits for the lane's 16 keys
+// (key k0 + 8(q>>2) + 4g + (q&3) takes lane q), kept iff >= thr. It zeroes
+// the dropped probabilities before the value product (the row sum keeps them
+// all), scales the output by 65536 / (65536 - thr), and stores the 16 keep
+// bits as one 16-bit word mask[batch][head][key block][g][query] (rows padded
+// to a multiple of 8). The backward kernels read those words: dP and (for dV)
+// P are multiplied by keep * scale.
 #include "common.h"
 #include "kernels.h"
 
@@ -59,7 +69,45 @@ struct MP {
   bf16* dqkv;          // [T, 3*h_l]
   float scale_log2;    // log2(e) / sqrt(D)
   float scale;         // 1 / sqrt(D)
+  // dropout (DO kernels)
+  uint16_t* mask;      // [batch][n_local][nkb][2][mstride] keep bits
+  int nkb, mstride;    // ceil(seq / 32); seq rounded up to a multiple of 8
+  uint32_t drop_thr;   // keep iff the 16-bit uniform >= drop_thr
+  float drop_scale;    // 65536 / (65536 - drop_thr)
+  uint64_t seed, offset;
 };
+
+// Philox4x64-10 (Salmon et al., SC 2011): ten rounds of two 64x64 -> 128-bit
+// products on words 0 and 2, the key advanced by two Weyl constants between
+// rounds.
+__device__ __forceinline__ void philox4x64_10(uint64_t& x0, uint64_t& x1, uint64_t& x2, uint64_t& x3, uint64_t k0,
+                                              uint64_t k1) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B97F4A7C15ull;
+      k1 += 0xBB67AE8584CAA73Bull;
+    }
+    const uint64_t lo0 = M0 * x0, hi0 = __umul64hi(M0, x0);
+    const uint64_t lo1 = M1 * x2, hi1 = __umul64hi(M1, x2);
+    x0 = hi1 ^ x1 ^ k0;
+    x1 = lo1;
+    x2 = hi0 ^ x3 ^ k1;
+    x3 = lo0;
+  }
+}
+
+// Keep bits (bit q = lane q's key) of query i, key block kb, half g.
+__device__ __forceinline__ uint32_t keep_bits(const MP& p, int b, int hk, int i, int kb, int g) {
+  uint64_t x0 = (uint64_t)i, x1 = (uint64_t)kb, x2 = ((uint64_t)b << 32) | (uint64_t)hk, x3 = (uint64_t)g;
+  philox4x64_10(x0, x1, x2, x3, p.seed, p.offset);
+  const uint64_t w[4] = {x0, x1, x2, x3};
+  uint32_t bits = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) bits |= (uint32_t)(((w[q >> 2] >> (16 * (q & 3))) & 0xFFFFull) >= p.drop_thr) << q;
+  return bits;
+}
 
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ const void* uni_ptr(const void* p) {
@@ -193,10 +241,10 @@ constexpr float kLazy = 8.0f;
 
 // One 32-key block (keys k0 .. k0 + 31, block sb of the 64-key tile in `cur`:
 // K hi, K lo, V at 0, TB, 2TB) for this wave's 32 queries.
-template <int D, bool AL>
+template <int D, bool AL, bool DO>
 __device__ __forceinline__ void fwd_block(const MP& p, const char* __restrict__ cur, int k0, int sb, int g,
                                           int q0w, int myq, float slope2, const TrOff& tro, const RowOff& ro,
-                                          FwdState<D>& st) {
+                                          int b, int head, int hk, FwdState<D>& st) {
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
   f32x16 sa = f32x16{}, sc = f32x16{};
 #pragma unroll
@@ -232,6 +280,13 @@ __device__ __forceinline__ void fwd_block(const MP& p, const char* __restrict__ 
     lloc += x[q];
   }
   st.l_run += lloc + __shfl_xor(lloc, 32);
+  if (DO) {
+    const int kb = k0 >> 5;
+    const uint32_t bits = keep_bits(p, b, hk, myq, kb, g);
+    if (myq < p.seq) p.mask[((long)(head * p.nkb + kb) * 2 + g) * p.mstride + myq] = (uint16_t)bits;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) x[q] = ((bits >> q) & 1u) ? x[q] : 0.f;
+  }
   const bf16x8 pf0 = pack8(x), pf1 = pack8(x + 8);
   const char* vt = cur + 2 * TB;
 #pragma unroll
@@ -249,7 +304,7 @@ __device__ __forceinline__ void fwd_block(const MP& p, const char* __restrict__ 
 // arithmetic overlap the other's matrix products.
 constexpr int FWD_WAVES = 8;
 
-template <int D, bool AL>
+template <int D, bool AL, bool DO>
 __global__ __launch_bounds__(64 * FWD_WAVES) void fwd_mfma(MP p) {
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
   constexpr int NX = NB * 16 + 2;  // floats a wave hands to its partner, per lane
@@ -302,7 +357,7 @@ __global__ __launch_bounds__(64 * FWD_WAVES) void fwd_mfma(MP p) {
     }
     const int k0 = kv0 + 32 * kh;
     if (k0 <= q0w + 31 && k0 < p.seq)  // wave-uniform; otherwise every key is masked
-      fwd_block<D, AL>(p, cur, k0, kh, g, q0w, myq, slope2, tro, ro, st);
+      fwd_block<D, AL, DO>(p, cur, k0, kh, g, q0w, myq, slope2, tro, ro, b, head, p.head0 + l, st);
   }
   // Pair merge. The last tile issued no loads, so after this barrier no wave
   // reads or writes the stages any more.
@@ -323,7 +378,7 @@ __global__ __launch_bounds__(64 * FWD_WAVES) void fwd_mfma(MP p) {
   const float f1 = st.m_run == -INFINITY ? 0.f : fexp2(st.m_run - m);
   const float f2 = m2 == -INFINITY ? 0.f : fexp2(m2 - m);
   const float lsum = st.l_run * f1 + l2 * f2;
-  const float inv = 1.0f / lsum;
+  const float inv = (DO ? p.drop_scale : 1.0f) / lsum;
   bf16* dst = p.ctx + (grow0 + myq) * p.h_l + (long)l * D;
 #pragma unroll
   for (int db = 0; db < NB; ++db)
@@ -358,10 +413,14 @@ __device__ __forceinline__ void dma_stats(const MP& p, char* stage_stats, int he
 }
 
 // P and dS of one 32-query block for this lane's key (MASK as in fwd_scores).
-template <bool MASK, bool AL>
+// DO: kw[q4] holds the keep words of queries qs0 + 8 q4 + 4g + 0..3 (16 bits
+// each); this key is bit qk; pv becomes P * keep * scale (for dV) and dP is
+// multiplied by keep * scale.
+template <bool MASK, bool AL, bool DO>
 __device__ __forceinline__ void kv_probs(const f32x16& sa, const f32x16& sc, const f32x16& dp, const float* sL,
                                          const float* sDl, float (&pv)[16], float (&dsv)[16], float scale_log2,
-                                         float slope2, int qs0, int g, int myk, int seq) {
+                                         float slope2, int qs0, int g, int myk, int seq, const uint64_t (&kw)[4],
+                                         int qk, float dscale) {
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
     const f32x4 L = *(const f32x4*)(sL + 8 * q4 + 4 * g);
@@ -374,14 +433,20 @@ __device__ __forceinline__ void kv_probs(const f32x16& sa, const f32x16& sc, con
       if (AL) v -= slope2 * (float)(query - myk);
       float pp = fexp2(v);
       if (MASK && (query < myk || query >= seq)) pp = 0.f;
-      pv[q] = pp;
-      dsv[q] = pp * (dp[q] - Dl[e]);
+      if (DO) {
+        const float kd = ((kw[q4] >> (16 * e + qk)) & 1ull) ? dscale : 0.f;
+        pv[q] = pp * kd;
+        dsv[q] = pp * (dp[q] * kd - Dl[e]);
+      } else {
+        pv[q] = pp;
+        dsv[q] = pp * (dp[q] - Dl[e]);
+      }
     }
   }
 }
 
 // One 64-query tile from stage `cur` (Q hi, Q lo, dctx, then lse, delta).
-template <int D, bool AL>
+template <int D, bool AL, bool DO>
 __device__ __forceinline__ void dkdv_tile(const MP& p, const char* __restrict__ cur, char* __restrict__ nxt,
                                           bool issue, int q0, int head, int l, long grow0, int w, int lane, int k0w,
                                           int myk, float slope2, const TrOff& tro, const RowOff& ro,
@@ -413,11 +478,25 @@ __device__ __forceinline__ void dkdv_tile(const MP& p, const char* __restrict__ 
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(cur + 2 * TB, qs, c, ro), st.vf[c], dp, 0, 0, 0);
     }
     // s[q], dp[q]: query qs0 + 8(q>>2) + 4g + (q&3), key myk
+    uint64_t kw[4] = {0, 0, 0, 0};
+    int qk = 0;
+    if (DO) {  // keep words of this key's block and half for the lane's 16 queries (rows padded: 8-byte loads stay in the row)
+      const int l32 = lane & 31;
+      qk = 4 * (l32 >> 3) + (l32 & 3);
+      const uint16_t* mrow = p.mask + ((long)(head * p.nkb + (k0w >> 5)) * 2 + ((l32 >> 2) & 1)) * p.mstride;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int i0 = qs0 + 8 * q4 + 4 * g;
+        if (i0 < p.seq) kw[q4] = *(const uint64_t*)(mrow + i0);
+      }
+    }
     float pv[16], dsv[16];
     if ((qs0 < k0w + 31) || (qs0 + 32 > p.seq))
-      kv_probs<true, AL>(sa, sc, dp, sL + 32 * qs, sDl + 32 * qs, pv, dsv, p.scale_log2, slope2, qs0, g, myk, p.seq);
+      kv_probs<true, AL, DO>(sa, sc, dp, sL + 32 * qs, sDl + 32 * qs, pv, dsv, p.scale_log2, slope2, qs0, g, myk,
+                             p.seq, kw, qk, p.drop_scale);
     else
-      kv_probs<false, AL>(sa, sc, dp, sL + 32 * qs, sDl + 32 * qs, pv, dsv, p.scale_log2, slope2, qs0, g, myk, p.seq);
+      kv_probs<false, AL, DO>(sa, sc, dp, sL + 32 * qs, sDl + 32 * qs, pv, dsv, p.scale_log2, slope2, qs0, g, myk,
+                              p.seq, kw, qk, p.drop_scale);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const bf16x8 pf = pack8(pv + 8 * h), df = pack8(dsv + 8 * h);
@@ -432,7 +511,7 @@ __device__ __forceinline__ void dkdv_tile(const MP& p, const char* __restrict__ 
   }
 }
 
-template <int D, bool AL>
+template <int D, bool AL, bool DO>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dkdv_mfma(MP p) {
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2, SB = 3 * TB + 512;
   __shared__ __attribute__((aligned(16))) char st0[SB];
@@ -476,7 +555,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int qt = qt0; qt < nqt; ++qt) {
     loads_landed_barrier();
     const bool odd = (qt - qt0) & 1;
-    dkdv_tile<D, AL>(p, odd ? st1 : st0, odd ? st0 : st1, qt + 1 < nqt, qt * TROWS, head, l, grow0, w, lane, k0w,
+    dkdv_tile<D, AL, DO>(p, odd ? st1 : st0, odd ? st0 : st1, qt + 1 < nqt, qt * TROWS, head, l, grow0, w, lane, k0w,
                      myk, slope2, tro, ro, st);
   }
   if (myk < p.seq) {
@@ -508,10 +587,11 @@ struct QState {
 };
 
 // dS of one 32-key block for this lane's query (MASK as in fwd_scores).
-template <bool MASK, bool AL>
+// DO: bit q of `bits` keeps lane q's key; dP is multiplied by keep * scale.
+template <bool MASK, bool AL, bool DO>
 __device__ __forceinline__ void q_dscores(const f32x16& sa, const f32x16& sc, const f32x16& dp, float (&ds)[16],
                                           float scale_log2, float slope2, float L, float Dl, int k0, int g, int myq,
-                                          int seq) {
+                                          int seq, uint32_t bits, float dscale) {
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int key = k0 + 8 * (q >> 2) + 4 * g + (q & 3);
@@ -519,15 +599,16 @@ __device__ __forceinline__ void q_dscores(const f32x16& sa, const f32x16& sc, co
     if (AL) v -= slope2 * (float)(myq - key);
     float pp = fexp2(v);
     if (MASK && (key > myq || key >= seq)) pp = 0.f;
-    ds[q] = pp * (dp[q] - Dl);
+    const float dpq = DO ? (((bits >> q) & 1u) ? dp[q] * dscale : 0.f) : dp[q];
+    ds[q] = pp * (dpq - Dl);
   }
 }
 
 // One 64-key tile from stage `cur` (K hi, K lo, V).
-template <int D, bool AL>
+template <int D, bool AL, bool DO>
 __device__ __forceinline__ void dq_tile(const MP& p, const char* __restrict__ cur, char* __restrict__ nxt, bool issue,
                                         int kv0, int l, long grow0, int w, int lane, int q0w, int myq, float slope2,
-                                        const TrOff& tro, const RowOff& ro, QState<D>& st) {
+                                        const TrOff& tro, const RowOff& ro, int head, QState<D>& st) {
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
   const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
   if (issue) {
@@ -550,11 +631,16 @@ __device__ __forceinline__ void dq_tile(const MP& p, const char* __restrict__ cu
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(cur + 2 * TB, sb, c, ro), st.cf[c], dp, 0, 0, 0);
     }
     // s[q]: key k0 + 8(q>>2) + 4g + (q&3), query myq
+    uint32_t bits = 0;
+    if (DO)  // this query's keep word of the block (a query past seq reads row seq - 1's, unused)
+      bits = p.mask[((long)(head * p.nkb + (k0 >> 5)) * 2 + g) * p.mstride + min(myq, p.seq - 1)];
     float ds[16];
     if ((k0 + 31 > q0w) || (k0 + 32 > p.seq))
-      q_dscores<true, AL>(sa, sc, dp, ds, p.scale_log2, slope2, st.L, st.Dl, k0, g, myq, p.seq);
+      q_dscores<true, AL, DO>(sa, sc, dp, ds, p.scale_log2, slope2, st.L, st.Dl, k0, g, myq, p.seq, bits,
+                              p.drop_scale);
     else
-      q_dscores<false, AL>(sa, sc, dp, ds, p.scale_log2, slope2, st.L, st.Dl, k0, g, myq, p.seq);
+      q_dscores<false, AL, DO>(sa, sc, dp, ds, p.scale_log2, slope2, st.L, st.Dl, k0, g, myq, p.seq, bits,
+                               p.drop_scale);
     const bf16x8 df0 = pack8(ds), df1 = pack8(ds + 8);
 #pragma unroll
     for (int db = 0; db < NB; ++db) {
@@ -564,7 +650,7 @@ __device__ __forceinline__ void dq_tile(const MP& p, const char* __restrict__ cu
   }
 }
 
-template <int D, bool AL>
+template <int D, bool AL, bool DO>
 __global__ __launch_bounds__(256) void dq_mfma(MP p) {
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
   __shared__ __attribute__((aligned(16))) char st0[3 * TB];
@@ -607,8 +693,8 @@ __global__ __launch_bounds__(256) void dq_mfma(MP p) {
   for (int kt = 0; kt < nkt; ++kt) {
     loads_landed_barrier();
     const bool odd = kt & 1;
-    dq_tile<D, AL>(p, odd ? st1 : st0, odd ? st0 : st1, kt + 1 < nkt, kt * TROWS, l, grow0, w, lane, q0w, myq, slope2,
-                   tro, ro, st);
+    dq_tile<D, AL, DO>(p, odd ? st1 : st0, odd ? st0 : st1, kt + 1 < nkt, kt * TROWS, l, grow0, w, lane, q0w, myq,
+                       slope2, tro, ro, head, st);
   }
   if (myq < p.seq) {
     bf16* dQ = p.dqkv + (grow0 + myq) * (3L * p.h_l) + (long)l * D;
@@ -672,25 +758,32 @@ MP make_mp(const AttnDesc& a) {
   p.dctx = (const bf16*)a.dctx; p.delta = a.delta; p.dqkv = (bf16*)a.dqkv;
   p.scale = 1.0f / sqrtf((float)a.head_dim);
   p.scale_log2 = p.scale * kLog2e;
+  p.mask = a.mask;
+  p.nkb = (a.seq + 31) / 32;
+  p.mstride = (a.seq + 7) & ~7;
+  p.drop_thr = (uint32_t)floorf(a.drop_p * 65536.0f + 0.5f);
+  p.drop_scale = 65536.0f / (65536.0f - (float)p.drop_thr);
+  p.seed = a.seed;
+  p.offset = a.offset;
   return p;
 }
 
-template <int D>
+template <int D, bool DO>
 hipError_t fwd_d(const MP& p, hipStream_t stream) {
   dim3 grid(p.batch * p.n_local, (p.seq + 127) / 128);
-  if (p.alibi) hipLaunchKernelGGL((fwd_mfma<D, true>), grid, dim3(64 * FWD_WAVES), 0, stream, p);
-  else hipLaunchKernelGGL((fwd_mfma<D, false>), grid, dim3(64 * FWD_WAVES), 0, stream, p);
+  if (p.alibi) hipLaunchKernelGGL((fwd_mfma<D, true, DO>), grid, dim3(64 * FWD_WAVES), 0, stream, p);
+  else hipLaunchKernelGGL((fwd_mfma<D, false, DO>), grid, dim3(64 * FWD_WAVES), 0, stream, p);
   return hipGetLastError();
 }
-template <int D>
+template <int D, bool DO>
 hipError_t bwd_d(const MP& p, hipStream_t stream) {
   dim3 grid(p.batch * p.n_local, (p.seq + 127) / 128);
-  if (p.alibi) hipLaunchKernelGGL((dkdv_mfma<D, true>), grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((dkdv_mfma<D, false>), grid, dim3(256), 0, stream, p);
+  if (p.alibi) hipLaunchKernelGGL((dkdv_mfma<D, true, DO>), grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((dkdv_mfma<D, false, DO>), grid, dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.alibi) hipLaunchKernelGGL((dq_mfma<D, true>), grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((dq_mfma<D, false>), grid, dim3(256), 0, stream, p);
+  if (p.alibi) hipLaunchKernelGGL((dq_mfma<D, true, DO>), grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((dq_mfma<D, false, DO>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -704,30 +797,43 @@ size_t attn_split_bytes(int dtype, int head_dim, long long T, long long h_l) {
   return attn_mfma_supported(dtype, head_dim) ? (size_t)(5 * T * h_l * 2) : 0;
 }
 
+size_t attn_dropout_mask_bytes(int batch, int seq, int n_local) {
+  return (size_t)batch * n_local * ((seq + 31) / 32) * 2 * ((seq + 7) & ~7) * sizeof(uint16_t);
+}
+
+template <bool DO>
+hipError_t fwd_dispatch(const MP& p, int head_dim, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return fwd_d<64, DO>(p, stream);
+    case 96: return fwd_d<96, DO>(p, stream);
+    case 128: return fwd_d<128, DO>(p, stream);
+    case 160: return fwd_d<160, DO>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+template <bool DO>
+hipError_t bwd_dispatch(const MP& p, int head_dim, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return bwd_d<64, DO>(p, stream);
+    case 96: return bwd_d<96, DO>(p, stream);
+    case 128: return bwd_d<128, DO>(p, stream);
+    case 160: return bwd_d<160, DO>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t attn_mfma_fwd(const AttnDesc& a, hipStream_t stream) {
   hipError_t e = split_launch(a, stream);
   if (e != hipSuccess) return e;
   const MP p = make_mp(a);
-  switch (a.head_dim) {
-    case 64: return fwd_d<64>(p, stream);
-    case 96: return fwd_d<96>(p, stream);
-    case 128: return fwd_d<128>(p, stream);
-    case 160: return fwd_d<160>(p, stream);
-  }
-  return hipErrorInvalidValue;
+  return a.mask ? fwd_dispatch<true>(p, a.head_dim, stream) : fwd_dispatch<false>(p, a.head_dim, stream);
 }
 
 hipError_t attn_mfma_bwd(const AttnDesc& a, hipStream_t stream) {
   hipError_t e = split_launch(a, stream);
   if (e != hipSuccess) return e;
   const MP p = make_mp(a);
-  switch (a.head_dim) {
-    case 64: return bwd_d<64>(p, stream);
-    case 96: return bwd_d<96>(p, stream);
-    case 128: return bwd_d<128>(p, stream);
-    case 160: return bwd_d<160>(p, stream);
-  }
-  return hipErrorInvalidValue;
+  return a.mask ? bwd_dispatch<true>(p, a.head_dim, stream) : bwd_dispatch<false>(p, a.head_dim, stream);
 }
 
 }  // namespace tpk

@@ -268,6 +268,7 @@ hipError_t delta_launch(int dtype, const AttnDesc& a, hipStream_t stream) {
 hipError_t attn_fwd_launch(int dtype, const AttnDesc& a, hipStream_t stream) {
   if (a.batch == 0 || a.seq == 0 || a.n_local == 0) return hipSuccess;
   if (attn_mfma_supported(dtype, a.head_dim)) return attn_mfma_fwd(a, stream);
+  if (a.mask) return hipErrorInvalidValue;  // dropout runs on the matrix-core path only
   SP p = make_sp(a);
   dim3 grid(a.seq, a.n_local, a.batch);
   if (dtype == DT_BF16) hipLaunchKernelGGL(fwd_kernel<bf16>, grid, dim3(NT), 0, stream, p);
@@ -277,6 +278,7 @@ hipError_t attn_fwd_launch(int dtype, const AttnDesc& a, hipStream_t stream) {
 
 hipError_t attn_bwd_launch(int dtype, const AttnDesc& a, hipStream_t stream) {
   if (a.batch == 0 || a.seq == 0 || a.n_local == 0) return hipSuccess;
+  if (a.mask && !attn_mfma_supported(dtype, a.head_dim)) return hipErrorInvalidValue;
   hipError_t e = delta_launch(dtype, a, stream);
   if (e != hipSuccess) return e;
   if (attn_mfma_supported(dtype, a.head_dim)) return attn_mfma_bwd(a, stream);

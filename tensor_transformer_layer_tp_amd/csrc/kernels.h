@@ -64,7 +64,14 @@ struct AttnDesc {
   // matrix-core path only: workspace for q/k/v split into bf16 hi/lo parts,
   // attn_split_bytes() bytes (5 arrays [T, h_l] bf16)
   void* split = nullptr;
+  // attention-probability dropout (matrix-core path only; enabled when mask is
+  // set): keep bits [batch][n_local][ceil(seq/32)][2][seq rounded up to 8],
+  // written by the forward, read by the backward
+  uint16_t* mask = nullptr;
+  float drop_p = 0.f;
+  uint64_t seed = 0, offset = 0;
 };
+size_t attn_dropout_mask_bytes(int batch, int seq, int n_local);
 bool attn_mfma_supported(int dtype, int head_dim);
 size_t attn_split_bytes(int dtype, int head_dim, long long T, long long h_l);
 hipError_t attn_fwd_launch(int dtype, const AttnDesc& a, hipStream_t stream);

@@ -385,11 +385,27 @@ tp_status tp_mlp_bwd(const tp_shape* shape, const void* X, const void* A_i, cons
   return TP_OK;
 }
 
-tp_status tp_attn_fwd(const tp_shape* shape, const void* X, const void* Wqkv_i, const void* bqkv_i, const void* Wo_i,
-                      float* qkv_i, void* ctx_i, float* lse_i, void* O_i, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Dropout arguments: bf16 matrix-core attention only, 0 <= p < 1.
+tp_status check_dropout(const tp_shape* s, const tp_dropout* dr) {
+  if (!dr) return fail(TP_ERR_NULL, "dropout is NULL");
+  if (!(dr->p >= 0.f && dr->p < 1.f)) return fail(TP_ERR_SHAPE, "dropout p must be in [0, 1)");
+  if (s->dtype != TP_BF16) return fail(TP_ERR_DTYPE, "attention dropout runs in bf16 only");
+  if (!attn_mfma_supported(s->dtype, s->head_dim))
+    return fail(TP_ERR_HEADDIM, "attention dropout supports head_dim 64, 96, 128, 160");
+  return TP_OK;
+}
+
+tp_status attn_fwd_impl(const tp_shape* shape, const tp_dropout* dr, uint16_t* mask, const void* X,
+                        const void* Wqkv_i, const void* bqkv_i, const void* Wo_i, float* qkv_i, void* ctx_i,
+                        float* lse_i, void* O_i, void* workspace, size_t workspace_bytes, void* stream) {
   Dims dm;
   TP_CHECK(check_shape(shape, dm));
+  if (dr) TP_CHECK(check_dropout(shape, dr));
+  if (dr) TP_CHECK(check_ptr(mask, "mask_i", dm.T == 0));
   const bool e = dm.T == 0;
   TP_CHECK(check_ptr(X, "X", e));
   TP_CHECK(check_ptr(Wqkv_i, "Wqkv_i", false));
@@ -413,17 +429,23 @@ tp_status tp_attn_fwd(const tp_shape* shape, const void* X, const void* Wqkv_i, 
   a.batch = shape->batch; a.seq = shape->seq; a.n_local = (int)dm.nl; a.head_dim = (int)dm.d;
   a.head0 = shape->tp_rank * (int)dm.nl; a.n_heads = shape->n_heads; a.alibi = shape->alibi;
   a.qkv = qkv_i; a.ctx = ctx_i; a.lse = lse_i; a.split = pl.split;
+  if (dr) {
+    a.mask = mask; a.drop_p = dr->p; a.seed = dr->seed; a.offset = dr->offset;
+  }
   TP_STEP(TP_STEP_ATTN_FWD, attn_fwd_launch(dt, a, st), "attn forward");
   TP_STEP(TP_STEP_OUT_PROJ, gemm_launch(dt, gd(GR_OUT_PROJ, T, h, hl, ctx_i, hl, true, Wo_i, h, false, EPI_STORE, O_i, h), pl.gemm_ws, pl.gemm_bytes, st),
          "attn output projection");
   return TP_OK;
 }
 
-tp_status tp_attn_bwd(const tp_shape* shape, const void* X, const void* Wqkv_i, const void* Wo_i, const float* qkv_i,
-                      const void* ctx_i, const float* lse_i, const void* dO, void* dX_i, void* dWqkv_i, void* dbqkv_i,
-                      void* dWo_i, void* dbo_or_null, void* workspace, size_t workspace_bytes, void* stream) {
+tp_status attn_bwd_impl(const tp_shape* shape, const tp_dropout* dr, const uint16_t* mask, const void* X,
+                        const void* Wqkv_i, const void* Wo_i, const float* qkv_i, const void* ctx_i,
+                        const float* lse_i, const void* dO, void* dX_i, void* dWqkv_i, void* dbqkv_i, void* dWo_i,
+                        void* dbo_or_null, void* workspace, size_t workspace_bytes, void* stream) {
   Dims dm;
   TP_CHECK(check_shape(shape, dm));
+  if (dr) TP_CHECK(check_dropout(shape, dr));
+  if (dr) TP_CHECK(check_ptr(mask, "mask_i", dm.T == 0));
   const bool e = dm.T == 0;
   TP_CHECK(check_ptr(X, "X", e));
   TP_CHECK(check_ptr(Wqkv_i, "Wqkv_i", false));
@@ -455,6 +477,9 @@ tp_status tp_attn_bwd(const tp_shape* shape, const void* X, const void* Wqkv_i, 
     a.head0 = shape->tp_rank * (int)dm.nl; a.n_heads = shape->n_heads; a.alibi = shape->alibi;
     a.qkv = qkv_i; a.ctx = (void*)ctx_i; a.lse = (float*)lse_i;
     a.dctx = pl.dctx; a.delta = (float*)pl.delta; a.dqkv = pl.dqkv; a.split = pl.split;
+    if (dr) {
+      a.mask = (uint16_t*)mask; a.drop_p = dr->p; a.seed = dr->seed; a.offset = dr->offset;
+    }
     TP_STEP(TP_STEP_ATTN_BWD, attn_bwd_launch(dt, a, st), "attn backward");
   }
   TP_STEP(TP_STEP_QKV_WGRAD, gemm_launch(dt, gd(GR_QKV_WGRAD, h, 3 * hl, T, X, h, false, pl.dqkv, 3 * hl, false, EPI_STORE, dWqkv_i, 3 * hl), pl.gemm_ws,
@@ -466,6 +491,47 @@ tp_status tp_attn_bwd(const tp_shape* shape, const void* X, const void* Wqkv_i, 
                        pl.gemm_bytes, st),
            "attn dgrad dX_i = dqkv Wqkv_i^T");
   return TP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tp_status tp_attn_fwd(const tp_shape* shape, const void* X, const void* Wqkv_i, const void* bqkv_i, const void* Wo_i,
+                      float* qkv_i, void* ctx_i, float* lse_i, void* O_i, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return attn_fwd_impl(shape, nullptr, nullptr, X, Wqkv_i, bqkv_i, Wo_i, qkv_i, ctx_i, lse_i, O_i, workspace,
+                       workspace_bytes, stream);
+}
+
+tp_status tp_attn_bwd(const tp_shape* shape, const void* X, const void* Wqkv_i, const void* Wo_i, const float* qkv_i,
+                      const void* ctx_i, const float* lse_i, const void* dO, void* dX_i, void* dWqkv_i, void* dbqkv_i,
+                      void* dWo_i, void* dbo_or_null, void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_bwd_impl(shape, nullptr, nullptr, X, Wqkv_i, Wo_i, qkv_i, ctx_i, lse_i, dO, dX_i, dWqkv_i, dbqkv_i,
+                       dWo_i, dbo_or_null, workspace, workspace_bytes, stream);
+}
+
+size_t tp_attn_dropout_mask_bytes(const tp_shape* shape) {
+  Dims dm;
+  if (check_shape(shape, dm) != TP_OK) return 0;
+  return attn_dropout_mask_bytes(shape->batch, shape->seq, (int)dm.nl);
+}
+
+tp_status tp_attn_fwd_dropout(const tp_shape* shape, const tp_dropout* dropout, const void* X, const void* Wqkv_i,
+                              const void* bqkv_i, const void* Wo_i, float* qkv_i, void* ctx_i, float* lse_i,
+                              uint16_t* mask_i, void* O_i, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dropout) return fail(TP_ERR_NULL, "dropout is NULL");
+  return attn_fwd_impl(shape, dropout, mask_i, X, Wqkv_i, bqkv_i, Wo_i, qkv_i, ctx_i, lse_i, O_i, workspace,
+                       workspace_bytes, stream);
+}
+
+tp_status tp_attn_bwd_dropout(const tp_shape* shape, const tp_dropout* dropout, const void* X, const void* Wqkv_i,
+                              const void* Wo_i, const float* qkv_i, const void* ctx_i, const float* lse_i,
+                              const uint16_t* mask_i, const void* dO, void* dX_i, void* dWqkv_i, void* dbqkv_i,
+                              void* dWo_i, void* dbo_or_null, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dropout) return fail(TP_ERR_NULL, "dropout is NULL");
+  return attn_bwd_impl(shape, dropout, mask_i, X, Wqkv_i, Wo_i, qkv_i, ctx_i, lse_i, dO, dX_i, dWqkv_i, dbqkv_i,
+                       dWo_i, dbo_or_null, workspace, workspace_bytes, stream);
 }
 
 tp_status tp_sum_partials(const tp_shape* shape, const void* const* parts, int32_t n_parts, const void* bias_or_null,

@@ -37,7 +37,8 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(names) == {"tp_mlp_workspace_bytes", "tp_attn_workspace_bytes", "tp_mlp_fwd", "tp_mlp_bwd",
                           "tp_attn_fwd", "tp_attn_bwd", "tp_sum_partials", "tp_last_error", "tp_profile_enable",
                           "tp_profile_collect", "tp_ln_workspace_bytes", "tp_ln_residual_fwd", "tp_ln_residual_bwd",
-                          "tp_vocab_workspace_bytes", "tp_vocab_ce_fwd", "tp_vocab_ce_combine", "tp_vocab_ce_bwd"}
+                          "tp_vocab_workspace_bytes", "tp_vocab_ce_fwd", "tp_vocab_ce_combine", "tp_vocab_ce_bwd",
+                          "tp_attn_dropout_mask_bytes", "tp_attn_fwd_dropout", "tp_attn_bwd_dropout"}
     for n in names:
         assert isinstance(getattr(lib, n), ctypes._CFuncPtr), n
     out = subprocess.run(["nm", "-D", "--defined-only", tp.library_path()], capture_output=True, text=True).stdout
@@ -268,3 +269,57 @@ def test_vocab_empty_batch_forward_needs_no_token_pointers():
     s = shape(batch=0)
     tp.tp_vocab_ce_fwd(s, 512, None, FAKE, None, None, None, workspace=(FAKE, 1 << 40), stream=0)
     tp.tp_vocab_ce_combine(s, [None, None], None, None, stream=0)
+
+
+# ---------------------------------------------------------------------------
+# attention dropout
+# ---------------------------------------------------------------------------
+
+def _bf16_attn(**kw):
+    base = dict(dtype=tp.TP_BF16, hidden=512, ffn=2048, n_heads=4, head_dim=128)
+    base.update(kw)
+    return shape(**base)
+
+
+def test_dropout_mask_bytes():
+    # [batch][n_l][ceil(seq/32)][2][seq rounded up to 8] 16-bit words
+    s = _bf16_attn(batch=2, seq=130)
+    assert tp.tp_attn_dropout_mask_bytes(s) == 2 * 2 * 5 * 2 * 136 * 2
+    c4 = shape(batch=1, seq=2048, hidden=20480, ffn=81920, n_heads=128, head_dim=160, tp_size=8, dtype=tp.TP_BF16)
+    assert tp.tp_attn_dropout_mask_bytes(c4) == 16 * 64 * 2 * 2048 * 2
+
+
+@pytest.mark.parametrize("kw,p,status", [
+    ({}, 1.0, "TP_ERR_SHAPE"),
+    ({}, -0.1, "TP_ERR_SHAPE"),
+    ({}, float("nan"), "TP_ERR_SHAPE"),
+    (dict(dtype=tp.TP_FP32), 0.1, "TP_ERR_DTYPE"),
+    (dict(hidden=128, n_heads=4, head_dim=32), 0.1, "TP_ERR_HEADDIM"),
+    (dict(tp_rank=3), 0.1, "TP_ERR_RANK"),
+])
+def test_dropout_validation(kw, p, status):
+    s = _bf16_attn(**kw)
+    d = tp.TpDropout(p, 1, 2)
+    with pytest.raises(tp.TPError) as ei:
+        tp.tp_attn_fwd_dropout(s, d, *([FAKE] * 9), workspace=(FAKE, 1 << 40), stream=0)
+    assert ei.value.name == status, str(ei.value)
+    with pytest.raises(tp.TPError) as ei:
+        tp.tp_attn_bwd_dropout(s, d, *([FAKE] * 13), workspace=(FAKE, 1 << 40), stream=0)
+    assert ei.value.name == status, str(ei.value)
+
+
+def test_dropout_null_arguments():
+    s = _bf16_attn()
+    with pytest.raises(tp.TPError) as ei:
+        tp.tp_attn_fwd_dropout(s, None, *([FAKE] * 9), workspace=(FAKE, 1 << 40), stream=0)
+    assert ei.value.name == "TP_ERR_NULL"
+    args = [FAKE] * 9
+    args[7] = None  # mask_i
+    with pytest.raises(tp.TPError) as ei:
+        tp.tp_attn_fwd_dropout(s, tp.TpDropout(0.1, 1, 2), *args, workspace=(FAKE, 1 << 40), stream=0)
+    assert ei.value.name == "TP_ERR_NULL"
+    args = [FAKE] * 13
+    args[6] = FAKE + 2  # mask_i misaligned
+    with pytest.raises(tp.TPError) as ei:
+        tp.tp_attn_bwd_dropout(s, tp.TpDropout(0.1, 1, 2), *args, workspace=(FAKE, 1 << 40), stream=0)
+    assert ei.value.name == "TP_ERR_ALIGN"
