@@ -256,6 +256,48 @@ def vocab_ce_measure(reps: int = 10) -> dict:
             "steps": res}
 
 
+def attn_dropout_measure(w, ls, reps: int = 10) -> dict:
+    """Attention-probability dropout variant (outside the step and its metric):
+    the attention block's forward and backward at the workload's shape with
+    p = 0.1, next to the same calls without dropout, timed over the attention
+    steps only (HIP events)."""
+    import torch
+    import tensor_transformer_layer_tp_amd as tp
+
+    s, i, o = ls.shape, ls.inp, ls.out
+    mask = torch.empty(tp.tp_attn_dropout_mask_bytes(s) // 2, dtype=torch.int16, device="cuda")
+    drop = tp.TpDropout(0.1, 1234, 0)
+
+    def once(dr):
+        if dr is None:
+            tp.tp_attn_fwd(s, i["X_attn"], i["Wqkv"], i["bqkv"], i["Wo"], o["qkv"], o["ctx"], o["lse"], o["O"],
+                           ls.workspace)
+            tp.tp_attn_bwd(s, i["X_attn"], i["Wqkv"], i["Wo"], o["qkv"], o["ctx"], o["lse"], i["dO"], o["dX_attn"],
+                           o["dWqkv"], o["dbqkv"], o["dWo"], o.get("dbo"), ls.workspace)
+        else:
+            tp.tp_attn_fwd_dropout(s, dr, i["X_attn"], i["Wqkv"], i["bqkv"], i["Wo"], o["qkv"], o["ctx"], o["lse"],
+                                   mask, o["O"], ls.workspace)
+            tp.tp_attn_bwd_dropout(s, dr, i["X_attn"], i["Wqkv"], i["Wo"], o["qkv"], o["ctx"], o["lse"], mask,
+                                   i["dO"], o["dX_attn"], o["dWqkv"], o["dbqkv"], o["dWo"], o.get("dbo"),
+                                   ls.workspace)
+
+    res = {}
+    for name, dr in (("p0_plain", None), ("p0.1", drop)):
+        for _ in range(2):
+            once(dr)
+        torch.cuda.synchronize()
+        tp.tp_profile_enable((1 << tp.STEPS["attn_fwd"]) | (1 << tp.STEPS["attn_bwd"]))
+        for _ in range(reps):
+            once(dr)
+        torch.cuda.synchronize()
+        nf, msf = tp.tp_profile_collect(tp.STEPS["attn_fwd"])
+        nb, msb = tp.tp_profile_collect(tp.STEPS["attn_bwd"])
+        tp.tp_profile_enable(0)
+        res[name] = {"attn_fwd_ms": round(msf / max(nf, 1), 4), "attn_bwd_ms": round(msb / max(nb, 1), 4)}
+        log(f"  attention {name:8s}: fwd {res[name]['attn_fwd_ms']:.3f} ms, bwd {res[name]['attn_bwd_ms']:.3f} ms")
+    return {"workload": f"{w.name} attention block, bf16, p = 0.1 (Philox4x64-10 keep bits)", **res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,6 +307,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ln", action="store_true", help="skip the residual + LayerNorm measurement")
     ap.add_argument("--no-vocab", action="store_true", help="skip the vocabulary-parallel output-layer measurement")
+    ap.add_argument("--no-dropout", action="store_true", help="skip the attention-dropout measurement")
     ap.add_argument("--cpu-target-s", type=float, default=15.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run device-to-device copies of this many MiB (calibrates byte counters)")
@@ -359,6 +402,11 @@ def main():
         log("residual add + LayerNorm (measured apart from the step)")
         ln = ln_residual_measure(w)
 
+    adrop = None
+    if not a.no_dropout:
+        log("attention-probability dropout (measured apart from the step)")
+        adrop = attn_dropout_measure(w, ls)
+
     vocab = None
     if not a.no_vocab:
         log("vocabulary-parallel logits + cross-entropy (measured apart from the step)")
@@ -384,6 +432,7 @@ def main():
         "cpu_baseline": cpu,
         "ln_residual": ln,
         "vocab_ce": vocab,
+        "attn_dropout": adrop,
     }
     print(json.dumps(out), flush=True)
 
