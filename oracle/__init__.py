@@ -25,6 +25,6 @@ from .tp_layer import (  # noqa: F401
     layer_weight_shapes, mlp_fwd, mlp_bwd, alibi_slope, attn_core_fwd, attn_core_bwd, attn_fwd,
     attn_bwd, sum_partials,
 )
-from .ln_residual import ln_residual_fwd, ln_residual_bwd  # noqa: F401
+from .ln_residual import ln_residual_fwd, ln_residual_bwd, ln_residual_bwd_dropout  # noqa: F401
 from .vocab_ce import vocab_shard, logits_fwd, ce_partial_stats, ce_combine, ce_bwd  # noqa: F401
-from .dropout import philox4x64_10, keep_threshold, keep_scale, attention_multipliers  # noqa: F401
+from .dropout import philox4x64_10, keep_threshold, keep_scale, attention_multipliers, residual_multipliers  # noqa: F401

@@ -16,6 +16,12 @@ constants into 128-bit products, then
     (x0, x1, x2, x3) <- (hi(M1 x2) ^ x1 ^ k0, lo(M1 x2), hi(M0 x0) ^ x3 ^ k1, lo(M0 x0)),
 with the key advanced by two Weyl constants between rounds.
 
+Residual mask (dropout on a block's output before the residual add, outside
+the model-parallel region, so identical on every rank): for token t and
+column j the counter is (t, j // 16, 0, 2) -- no rank or head in it, and the
+last word 2 keeps it apart from every attention counter -- with the same key;
+the uniform is 16-bit lane j % 16, kept and scaled as below.
+
 Attention mask (readings, the pages fix none of this): for batch b, global
 head k (0-based), query i and key j, the counter is
     (i, j // 32, (b << 32) | k, g)   with g = ((j % 32) >> 2) & 1,
@@ -94,3 +100,18 @@ def attention_multipliers(*, batch, seq, n_local, head0, p, seed, offset):
                     ok = j < seq
                     D[b, l][:, j[ok]] = keep[:, ok, gg]
     return D
+
+
+def residual_multipliers(*, tokens, hidden, p, seed, offset):
+    """Dropout multipliers R[t, j] = keep * scale on a block output before the
+    residual add (the same on every rank)."""
+    thr = keep_threshold(p)
+    scale = keep_scale(p)
+    t = np.arange(tokens, dtype=np.uint64)[:, None]
+    c = np.arange((hidden + 15) // 16, dtype=np.uint64)[None, :]
+    words = philox4x64_10(t, c, np.uint64(0), np.uint64(2), seed, offset)  # each [T, ceil(h/16)]
+    R = np.zeros((tokens, (hidden + 15) // 16 * 16))
+    for q in range(16):
+        u = (words[q >> 2] >> np.uint64(16 * (q & 3))) & np.uint64(0xFFFF)
+        R[:, q::16] = (u >= np.uint64(thr)).astype(np.float64) * scale
+    return R[:, :hidden]

@@ -15,9 +15,12 @@ definition of layer normalization:
     rstd  = 1 / sqrt(var + eps)
     y     = (r - mu) * rstd * gamma + beta          (the next block's input)
 
-Readings where the pages are silent: dropout is off; eps is the caller's
-argument (the pages give no value; 1e-5 in the tests); the variance is the
-biased one.
+Readings where the pages are silent: eps is the caller's argument (the pages
+give no value; 1e-5 in the tests); the variance is the biased one. Dropout
+on the block output (before the residual add; identical on every rank) is
+optional: with multipliers R = keep * scale (oracle.dropout),
+    r = resid_in + R * (sum_k parts[k] + bias),
+and the block output, every part and the bias then receive dr * R.
 
 Backward, for the loss <y, dy> + <r, dr_in> (dr_in: the gradient reaching r
 along the residual stream from later in the network):
@@ -34,14 +37,18 @@ from __future__ import annotations
 import numpy as np
 
 
-def ln_residual_fwd(resid_in, parts, bias, gamma, beta, eps):
+def ln_residual_fwd(resid_in, parts, bias, gamma, beta, eps, dropout=None):
     """-> r [T,h], y [T,h], mu [T], rstd [T]. `parts` is a list of [T,h]
-    arrays (one per emulated rank); bias may be None."""
-    r = np.array(resid_in, dtype=np.float64)
+    arrays (one per emulated rank); bias may be None; dropout: optional
+    multipliers [T,h] on the block output (sum of parts + bias)."""
+    blk = np.zeros_like(np.asarray(resid_in, dtype=np.float64))
     for p in parts:
-        r = r + p
+        blk = blk + p
     if bias is not None:
-        r = r + bias
+        blk = blk + bias
+    if dropout is not None:
+        blk = blk * dropout
+    r = np.array(resid_in, dtype=np.float64) + blk
     mu = r.mean(axis=1)
     cen = r - mu[:, None]
     var = (cen * cen).mean(axis=1)
@@ -68,3 +75,12 @@ def ln_residual_bwd(r, gamma, eps, dy, dr_in=None):
     dbeta = dy.sum(axis=0)
     dbias = dr.sum(axis=0)
     return dr, dgamma, dbeta, dbias
+
+
+def ln_residual_bwd_dropout(r, gamma, eps, dy, dr_in, dropout):
+    """With residual dropout multipliers R: -> dr (gradient of resid_in),
+    d_block = dr * R (gradient of the block output, every part and the bias),
+    dgamma, dbeta, dbias = sum_t d_block."""
+    dr, dgamma, dbeta, _ = ln_residual_bwd(r, gamma, eps, dy, dr_in)
+    d_block = dr * dropout
+    return dr, d_block, dgamma, dbeta, d_block.sum(axis=0)

@@ -154,3 +154,53 @@ def test_documented_element_mapping():
         q = 4 * ((j % 32) >> 3) + (j % 4)
         u = (int(words[q >> 2]) >> (16 * (q & 3))) & 0xFFFF
         assert (D[b, l, i, j] > 0) == (u >= thr)
+
+
+# ----------------------------------------------------------------------------
+# residual dropout (before the residual add; identical on every rank)
+# ----------------------------------------------------------------------------
+
+def test_residual_mask_mapping_and_statistics():
+    T, h, p, seed, offset = 37, 100, 0.25, 77, 3
+    R = oracle.residual_multipliers(tokens=T, hidden=h, p=p, seed=seed, offset=offset)
+    thr = oracle.keep_threshold(p)
+    for t, j in ((0, 0), (5, 15), (5, 16), (36, 99), (17, 42)):
+        w = oracle.philox4x64_10(np.uint64(t), np.uint64(j // 16), np.uint64(0), np.uint64(2), seed, offset)
+        u = (int(w[(j % 16) >> 2]) >> (16 * (j % 4))) & 0xFFFF
+        assert (R[t, j] > 0) == (u >= thr)
+    kept = (R > 0).mean()
+    assert abs(kept - (1 - thr / 65536)) < 6 * math.sqrt(p * (1 - p) / R.size)
+    # the residual counter space (last word 2) never meets the attention one (last word 0 or 1)
+    A = oracle.attention_multipliers(batch=1, seq=T, n_local=1, head0=0, p=p, seed=seed, offset=offset)
+    assert not np.array_equal((A[0, 0, :, :T] > 0), (R[:, :T] > 0))
+
+
+def test_residual_dropout_ln_matches_torch_autograd():
+    g = np.random.default_rng(6)
+    T, h = 7, 40
+    resid, parts = g.normal(size=(T, h)), [g.normal(size=(T, h)) for _ in range(2)]
+    bias, gamma, beta = g.normal(size=h), 1 + 0.1 * g.normal(size=h), 0.1 * g.normal(size=h)
+    dy, dr_in = g.normal(size=(T, h)), g.normal(size=(T, h))
+    R = oracle.residual_multipliers(tokens=T, hidden=h, p=0.3, seed=1, offset=2)
+    r, y, _, _ = oracle.ln_residual_fwd(resid, parts, bias, gamma, beta, 1e-5, dropout=R)
+    dr, d_block, dg, db, dbias = oracle.ln_residual_bwd_dropout(r, gamma, 1e-5, dy, dr_in, R)
+    tr, tparts = torch.tensor(resid, requires_grad=True), [torch.tensor(q, requires_grad=True) for q in parts]
+    tb, tg, tbe = (torch.tensor(a, requires_grad=True) for a in (bias, gamma, beta))
+    rt = tr + (sum(tparts) + tb) * torch.tensor(R)
+    yt = torch.nn.functional.layer_norm(rt, (h,), tg, tbe, 1e-5)
+    np.testing.assert_allclose(r, rt.detach().numpy(), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(y, yt.detach().numpy(), rtol=1e-12, atol=1e-12)
+    ((yt * torch.tensor(dy)).sum() + (rt * torch.tensor(dr_in)).sum()).backward()
+    tol = dict(rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dr, tr.grad.numpy(), **tol)
+    for q in tparts:
+        np.testing.assert_allclose(d_block, q.grad.numpy(), **tol)
+    np.testing.assert_allclose(dbias, tb.grad.numpy(), **tol)
+    np.testing.assert_allclose(dg, tg.grad.numpy(), **tol)
+    np.testing.assert_allclose(db, tbe.grad.numpy(), **tol)
+    # p = 0 is the step without dropout
+    R0 = oracle.residual_multipliers(tokens=T, hidden=h, p=0.0, seed=1, offset=2)
+    a = oracle.ln_residual_fwd(resid, parts, bias, gamma, beta, 1e-5, dropout=R0)
+    b = oracle.ln_residual_fwd(resid, parts, bias, gamma, beta, 1e-5)
+    for x, z in zip(a, b):
+        np.testing.assert_array_equal(x, z)
