@@ -263,6 +263,36 @@ tp_status tp_vocab_ce_bwd(const tp_shape* shape, int32_t vocab, const void* X, c
                           const float* dloss, void* dX_i, void* dW_i, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* Residual add + LayerNorm with dropout on the block output (Megatron-LM deep
+ * dive: dropout before the residual add lies outside the model-parallel
+ * region and must be identical on the ranks of a model replica):
+ *   resid_out = resid_in + keep * scale * (sum_k parts[k] + bias), then as in
+ *   tp_ln_residual_fwd; element (t, j) is kept iff 16-bit lane j % 16 of the
+ *   Philox4x64-10 block at counter (t, j / 16, 0, 2) with key (seed, offset)
+ *   is >= thr = round(65536 p); scale = 65536 / (65536 - thr). No rank enters
+ *   the counter, so every rank draws the same mask from the same (seed,
+ *   offset). mask [T][hidden/8] bytes (bit e of byte c: element 8c + e,
+ *   tp_ln_dropout_mask_bytes bytes) receives the keep bits. p outside [0, 1)
+ *   is TP_ERR_SHAPE; other arguments as in tp_ln_residual_fwd. */
+size_t tp_ln_dropout_mask_bytes(const tp_shape* shape);
+tp_status tp_ln_residual_fwd_dropout(const tp_shape* shape, const tp_dropout* dropout,
+                                     const void* resid_in, const void* const* parts, int32_t n_parts,
+                                     const void* bias_or_null, const void* gamma, const void* beta,
+                                     float eps, void* resid_out, void* ln_out, float* mean, float* rstd,
+                                     uint8_t* mask, void* stream);
+
+/* Backward of tp_ln_residual_fwd_dropout: d_resid as in tp_ln_residual_bwd
+ * (the gradient of resid_in), and d_block [T,h] = d_resid * keep * scale, the
+ * gradient of the block output, of every part and (summed over tokens, into
+ * dbias_or_null) of the bias. mask as written by the forward. */
+tp_status tp_ln_residual_bwd_dropout(const tp_shape* shape, const tp_dropout* dropout,
+                                     const void* resid_out, const float* mean, const float* rstd,
+                                     const void* gamma, const void* d_ln_out,
+                                     const void* d_resid_out_or_null, const uint8_t* mask,
+                                     void* d_resid, void* d_block, void* dgamma, void* dbeta,
+                                     void* dbias_or_null, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
 /* Steps of the path, for per-step timing. The id doubles as the bit position
  * in tp_profile_enable's mask. */
 enum {

@@ -23,7 +23,8 @@ __all__ = [
     "tp_mlp_bwd", "tp_attn_fwd", "tp_attn_bwd", "tp_sum_partials", "tp_last_error", "tp_profile_enable",
     "tp_profile_collect", "STEPS", "tp_ln_workspace_bytes", "tp_ln_residual_fwd", "tp_ln_residual_bwd",
     "tp_vocab_workspace_bytes", "tp_vocab_ce_fwd", "tp_vocab_ce_combine", "tp_vocab_ce_bwd", "TpDropout",
-    "tp_attn_dropout_mask_bytes", "tp_attn_fwd_dropout", "tp_attn_bwd_dropout",
+    "tp_attn_dropout_mask_bytes", "tp_attn_fwd_dropout", "tp_attn_bwd_dropout", "tp_ln_dropout_mask_bytes",
+    "tp_ln_residual_fwd_dropout", "tp_ln_residual_bwd_dropout",
 ]
 
 TP_FP32, TP_BF16 = 0, 1
@@ -86,6 +87,11 @@ _SIGS = {
     "tp_attn_dropout_mask_bytes": (_sz, [ctypes.POINTER(TpShape)]),
     "tp_attn_fwd_dropout": (_st, [ctypes.POINTER(TpShape), ctypes.POINTER(TpDropout)] + [_vp] * 9 + [_vp, _sz, _vp]),
     "tp_attn_bwd_dropout": (_st, [ctypes.POINTER(TpShape), ctypes.POINTER(TpDropout)] + [_vp] * 13 + [_vp, _sz, _vp]),
+    "tp_ln_dropout_mask_bytes": (_sz, [ctypes.POINTER(TpShape)]),
+    "tp_ln_residual_fwd_dropout": (_st, [ctypes.POINTER(TpShape), ctypes.POINTER(TpDropout), _vp, ctypes.POINTER(_vp),
+                                         ctypes.c_int32, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "tp_ln_residual_bwd_dropout": (_st, [ctypes.POINTER(TpShape), ctypes.POINTER(TpDropout)] + [_vp] * 12
+                                   + [_vp, _sz, _vp]),
     "tp_profile_enable": (_st, [ctypes.c_uint32]),
     "tp_profile_collect": (_st, [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)]),
     "tp_last_error": (ctypes.c_char_p, []),
@@ -280,3 +286,27 @@ def tp_attn_bwd_dropout(shape, dropout, X, Wqkv_i, Wo_i, qkv_i, ctx_i, lse_i, ma
                                               _ptr(Wo_i), _ptr(qkv_i), _ptr(ctx_i), _ptr(lse_i), _ptr(mask_i),
                                               _ptr(dO), _ptr(dX_i), _ptr(dWqkv_i), _ptr(dbqkv_i), _ptr(dWo_i),
                                               _ptr(dbo_or_null), w, wn, _stream(stream)))
+
+
+def tp_ln_dropout_mask_bytes(shape: TpShape) -> int:
+    return load_library().tp_ln_dropout_mask_bytes(ctypes.byref(shape))
+
+
+def tp_ln_residual_fwd_dropout(shape, dropout, resid_in, parts, bias_or_null, gamma, beta, eps, resid_out, ln_out,
+                               mean, rstd, mask, stream=None):
+    """tp_ln_residual_fwd with dropout on the block output; mask receives the keep bits."""
+    arr = (_vp * max(len(parts), 1))(*[_ptr(p) for p in parts])
+    _check(load_library().tp_ln_residual_fwd_dropout(ctypes.byref(shape), _drop(dropout), _ptr(resid_in), arr,
+                                                     len(parts), _ptr(bias_or_null), _ptr(gamma), _ptr(beta),
+                                                     float(eps), _ptr(resid_out), _ptr(ln_out), _ptr(mean), _ptr(rstd),
+                                                     _ptr(mask), _stream(stream)))
+
+
+def tp_ln_residual_bwd_dropout(shape, dropout, resid_out, mean, rstd, gamma, d_ln_out, d_resid_out_or_null, mask,
+                               d_resid, d_block, dgamma, dbeta, dbias_or_null=None, workspace=None, stream=None):
+    w, wn = _ws(workspace)
+    _check(load_library().tp_ln_residual_bwd_dropout(ctypes.byref(shape), _drop(dropout), _ptr(resid_out),
+                                                     _ptr(mean), _ptr(rstd), _ptr(gamma), _ptr(d_ln_out),
+                                                     _ptr(d_resid_out_or_null), _ptr(mask), _ptr(d_resid),
+                                                     _ptr(d_block), _ptr(dgamma), _ptr(dbeta), _ptr(dbias_or_null),
+                                                     w, wn, _stream(stream)))

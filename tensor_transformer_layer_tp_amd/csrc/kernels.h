@@ -111,6 +111,13 @@ struct LnDesc {
   void* dgamma = nullptr;
   void* dbeta = nullptr;
   void* dbias = nullptr;  // [h] or NULL
+  // dropout on the block output before the residual add (enabled by mask):
+  // keep bits [T][h/8] (bit e of byte c: element 8c + e); the backward also
+  // writes d_block = dr * keep * scale and forms dbias from it
+  uint8_t* mask = nullptr;
+  void* d_block = nullptr;
+  float drop_p = 0.f;
+  uint64_t seed = 0, offset = 0;
 };
 size_t ln_bwd_workspace_bytes(long long rows, int h);
 hipError_t ln_fwd_launch(int dtype, const LnDesc& d, hipStream_t stream);

@@ -6,7 +6,7 @@
 // Megatron-DeepSpeed blog (section 4.3) fuses the residual add into the
 // LayerNorm kernel. Definitions (h = hidden, per token row t):
 //
-//   r    = resid_in + sum_k parts[k] + bias      stored in the storage type
+//   r    = resid_in + (sum_k parts[k] + bias)    stored in the storage type
 //   mu   = mean_j r,  var = mean_j (r - mu)^2,   rstd = 1 / sqrt(var + eps)
 //   y    = (r - mu) rstd gamma + beta
 //
@@ -33,8 +33,17 @@
 // The workgroup reductions exchange values through LDS behind a barrier that
 // waits only for LDS traffic, so loads and stores to memory stay in flight
 // across it.
+//
+// Dropout variants (DO): the block output (sum of parts + bias) is multiplied
+// by keep * scale before the residual add; element (t, j) draws 16-bit lane
+// j % 16 of the Philox4x64-10 block at counter (t, j / 16, 0, 2) with key
+// (seed, offset) -- no rank in it, so every rank draws the same mask -- and is
+// kept iff that lane >= thr. The forward stores the 8 keep bits of each
+// 8-element chunk as one byte; the backward also writes the gradient of the
+// block output, d_block = dr * keep * scale.
 #include "common.h"
 #include "kernels.h"
+#include "philox.h"
 #include "rowops.h"
 
 namespace tpk {
@@ -48,17 +57,36 @@ struct PartPtrs {
   const void* p[64];
 };
 
+struct DropArgs {
+  uint8_t* mask;  // [rows][h/8]
+  uint32_t thr;
+  float scale;
+  uint64_t seed, offset;
+};
+
+// Keep bits (bit e = element 8c + e) of chunk c of row t.
+__device__ __forceinline__ uint32_t residual_keep_byte(const DropArgs& d, long t, int c) {
+  uint64_t x0 = (uint64_t)t, x1 = (uint64_t)(c >> 1), x2 = 0, x3 = 2;
+  philox4x64_10(x0, x1, x2, x3, d.seed, d.offset);
+  const uint64_t w[4] = {x0, x1, x2, x3};
+  uint32_t bits = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) bits |= (uint32_t)(philox_lane16(w, 8 * (c & 1) + e) >= d.thr) << e;
+  return bits;
+}
+
 // Chunk i of this thread (8 elements at column 8c) is valid if c < nc; the
 // loads use the clamped chunk min(c, nc - 1), always in range, so that no load
 // waits behind a branch; only arithmetic that feeds a sum and the stores
 // depend on validity.
-template <typename T, int NV>
+template <typename T, int NV, bool DO>
 __global__ __launch_bounds__(FWD_T) void ln_residual_fwd_kernel(const T* __restrict__ resid_in, PartPtrs parts,
                                                                 int n_parts, const T* __restrict__ bias,
                                                                 const T* __restrict__ gamma,
                                                                 const T* __restrict__ beta, float eps, int h,
                                                                 T* __restrict__ resid_out, T* __restrict__ y,
-                                                                float* __restrict__ mean, float* __restrict__ rstd) {
+                                                                float* __restrict__ mean, float* __restrict__ rstd,
+                                                                DropArgs da) {
   __shared__ float red[FWD_T / 64];
   const long base = (long)blockIdx.x * h;
   const int nc = h >> 3;
@@ -70,9 +98,16 @@ __global__ __launch_bounds__(FWD_T) void ln_residual_fwd_kernel(const T* __restr
     ok[i] = c < nc;
     cl[i] = 8 * (ok[i] ? c : nc - 1);
   }
+  // the block output (sum of parts + bias) first, then the residual input
+  // (after dropout in the DO variant; at p = 0 both variants add identically)
+  V8<T> rv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) rv[i].load(resid_in + base + cl[i]);
   float v[NV][8];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) load8(resid_in + base + cl[i], v[i]);
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
   for (int k = 0; k < n_parts; ++k) {
     const T* pk = (const T*)parts.p[k];
     V8<T> pv[NV];
@@ -91,6 +126,18 @@ __global__ __launch_bounds__(FWD_T) void ln_residual_fwd_kernel(const T* __restr
     for (int i = 0; i < NV; ++i)
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[i][e] += bv[i][e];
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    if (DO) {
+      const uint32_t bits = residual_keep_byte(da, blockIdx.x, cl[i] >> 3);
+      if (ok[i]) da.mask[(long)blockIdx.x * (h >> 3) + (cl[i] >> 3)] = (uint8_t)bits;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[i][e] = rv[i][e] + (((bits >> e) & 1u) ? v[i][e] * da.scale : 0.f);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[i][e] = rv[i][e] + v[i][e];
+    }
   }
   float s[1] = {0.f};
 #pragma unroll
@@ -139,13 +186,14 @@ __global__ __launch_bounds__(FWD_T) void ln_residual_fwd_kernel(const T* __restr
 // Rows [run * rows_per, ...) of the backward pass; writes dr and this run's
 // column partials part[(2 run + j) h + col], j = 0: dy xhat, 1: dy. Loads use
 // clamped chunks and rows (always in range) as in the forward kernel.
-template <typename T, int NV>
+template <typename T, int NV, bool DO>
 __global__ __launch_bounds__(BWD_T) void ln_residual_bwd_kernel(const T* __restrict__ r, const float* __restrict__ mean,
                                                                 const float* __restrict__ rstd,
                                                                 const T* __restrict__ gamma, const T* __restrict__ dy,
                                                                 const T* __restrict__ dr_in, int h, long rows,
                                                                 int rows_per, T* __restrict__ dr,
-                                                                float* __restrict__ part) {
+                                                                float* __restrict__ part, const uint8_t* __restrict__ mask,
+                                                                T* __restrict__ d_block, float dscale) {
   __shared__ float red[2 * BWD_T / 64];
   const int nc = h >> 3;
   const long r0 = (long)blockIdx.x * rows_per;
@@ -195,6 +243,11 @@ __global__ __launch_bounds__(BWD_T) void ln_residual_bwd_kernel(const T* __restr
 #pragma unroll
       for (int i = 0; i < NV; ++i) din[i].load(dr_in + base + cl[i]);
     }
+    uint32_t mb[NV];
+    if (DO) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) mb[i] = mask[t * (h >> 3) + (cl[i] >> 3)];
+    }
     block_sum<BWD_T, 2>(s, red);
     const float a = s[0] / (float)h, b = s[1] / (float)h;
 #pragma unroll
@@ -212,6 +265,11 @@ __global__ __launch_bounds__(BWD_T) void ln_residual_bwd_kernel(const T* __restr
           ab[i][e] += dyv[i][e];
         }
         store8(dr + base + cl[i], o);
+        if (DO) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = ((mb[i] >> e) & 1u) ? o[e] * dscale : 0.f;
+          store8(d_block + base + cl[i], o);
+        }
       }
       dyv[i] = dyn[i];
       rv[i] = rn[i];
@@ -267,11 +325,27 @@ int ln_runs(long long rows, int& rows_per) {
   return (int)((rows + rows_per - 1) / rows_per);
 }
 
+DropArgs drop_args(const LnDesc& d) {
+  DropArgs a{};
+  a.mask = d.mask;
+  a.thr = (uint32_t)floorf(d.drop_p * 65536.0f + 0.5f);
+  a.scale = 65536.0f / (65536.0f - (float)a.thr);
+  a.seed = d.seed;
+  a.offset = d.offset;
+  return a;
+}
+
 template <typename T, int NV>
 void fwd_nv(const LnDesc& d, const PartPtrs& ps, hipStream_t st) {
-  hipLaunchKernelGGL((ln_residual_fwd_kernel<T, NV>), dim3((unsigned)d.T), dim3(FWD_T), 0, st,
-                     (const T*)d.resid_in, ps, d.n_parts, (const T*)d.bias, (const T*)d.gamma, (const T*)d.beta,
-                     d.eps, d.h, (T*)d.resid_out, (T*)d.y, d.mean, d.rstd);
+  const DropArgs da = drop_args(d);
+  if (d.mask)
+    hipLaunchKernelGGL((ln_residual_fwd_kernel<T, NV, true>), dim3((unsigned)d.T), dim3(FWD_T), 0, st,
+                       (const T*)d.resid_in, ps, d.n_parts, (const T*)d.bias, (const T*)d.gamma, (const T*)d.beta,
+                       d.eps, d.h, (T*)d.resid_out, (T*)d.y, d.mean, d.rstd, da);
+  else
+    hipLaunchKernelGGL((ln_residual_fwd_kernel<T, NV, false>), dim3((unsigned)d.T), dim3(FWD_T), 0, st,
+                       (const T*)d.resid_in, ps, d.n_parts, (const T*)d.bias, (const T*)d.gamma, (const T*)d.beta,
+                       d.eps, d.h, (T*)d.resid_out, (T*)d.y, d.mean, d.rstd, da);
 }
 
 template <typename T>
@@ -292,9 +366,17 @@ hipError_t fwd_t(const LnDesc& d, hipStream_t st) {
 
 template <typename T, int NV>
 void bwd_nv(const LnDesc& d, int runs, int rows_per, float* part, hipStream_t st) {
-  hipLaunchKernelGGL((ln_residual_bwd_kernel<T, NV>), dim3(runs), dim3(BWD_T), 0, st, (const T*)d.resid_out,
-                     (const float*)d.mean, (const float*)d.rstd, (const T*)d.gamma, (const T*)d.dy,
-                     (const T*)d.dr_in, d.h, (long)d.T, rows_per, (T*)d.dr, part);
+  const DropArgs da = drop_args(d);
+  if (d.mask)
+    hipLaunchKernelGGL((ln_residual_bwd_kernel<T, NV, true>), dim3(runs), dim3(BWD_T), 0, st, (const T*)d.resid_out,
+                       (const float*)d.mean, (const float*)d.rstd, (const T*)d.gamma, (const T*)d.dy,
+                       (const T*)d.dr_in, d.h, (long)d.T, rows_per, (T*)d.dr, part, (const uint8_t*)d.mask,
+                       (T*)d.d_block, da.scale);
+  else
+    hipLaunchKernelGGL((ln_residual_bwd_kernel<T, NV, false>), dim3(runs), dim3(BWD_T), 0, st, (const T*)d.resid_out,
+                       (const float*)d.mean, (const float*)d.rstd, (const T*)d.gamma, (const T*)d.dy,
+                       (const T*)d.dr_in, d.h, (long)d.T, rows_per, (T*)d.dr, part, (const uint8_t*)nullptr,
+                       (T*)nullptr, da.scale);
 }
 
 template <typename T>
@@ -318,7 +400,7 @@ hipError_t bwd_t(const LnDesc& d, float* part, hipStream_t st) {
                      (T*)d.dgamma, (T*)d.dbeta);
   e = hipGetLastError();
   if (e != hipSuccess || !d.dbias) return e;
-  return colsum_launch(sizeof(T) == 2 ? DT_BF16 : DT_F32, d.dr, (int)d.T, d.h, d.h, d.dbias,
+  return colsum_launch(sizeof(T) == 2 ? DT_BF16 : DT_F32, d.mask ? d.d_block : d.dr, (int)d.T, d.h, d.h, d.dbias,
                        part + (size_t)2 * runs * d.h, st);
 }
 

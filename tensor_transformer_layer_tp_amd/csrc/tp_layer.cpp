@@ -556,12 +556,25 @@ size_t tp_ln_workspace_bytes(const tp_shape* shape) {
   return ln_bwd_workspace_bytes(dm.T, (int)dm.h);
 }
 
-tp_status tp_ln_residual_fwd(const tp_shape* shape, const void* resid_in, const void* const* parts, int32_t n_parts,
-                             const void* bias_or_null, const void* gamma, const void* beta, float eps, void* resid_out,
-                             void* ln_out, float* mean, float* rstd, void* stream) {
+}  // extern "C"
+
+namespace {
+
+tp_status check_p(const tp_dropout* dr) {
+  if (!dr) return fail(TP_ERR_NULL, "dropout is NULL");
+  if (!(dr->p >= 0.f && dr->p < 1.f)) return fail(TP_ERR_SHAPE, "dropout p must be in [0, 1)");
+  return TP_OK;
+}
+
+tp_status ln_fwd_impl(const tp_shape* shape, const tp_dropout* dr, uint8_t* mask, const void* resid_in,
+                      const void* const* parts, int32_t n_parts, const void* bias_or_null, const void* gamma,
+                      const void* beta, float eps, void* resid_out, void* ln_out, float* mean, float* rstd,
+                      void* stream) {
   Dims dm;
   TP_CHECK(check_shape(shape, dm));
   TP_CHECK(check_ln(dm));
+  if (dr) TP_CHECK(check_p(dr));
+  if (dr) TP_CHECK(check_ptr(mask, "mask", dm.T == 0));
   if (!(eps > 0.f) || !std::isfinite(eps)) return fail(TP_ERR_SHAPE, "eps must be positive and finite");
   if (n_parts < 0 || n_parts > 64) return fail(TP_ERR_SHAPE, "n_parts %d outside [0, 64]", n_parts);
   if (n_parts > 0 && !parts) return fail(TP_ERR_NULL, "parts is NULL");
@@ -580,18 +593,24 @@ tp_status tp_ln_residual_fwd(const tp_shape* shape, const void* resid_in, const 
   d.T = dm.T; d.h = (int)dm.h; d.eps = eps;
   d.resid_in = resid_in; d.parts = parts; d.n_parts = n_parts; d.bias = bias_or_null;
   d.gamma = gamma; d.beta = beta; d.resid_out = resid_out; d.y = ln_out; d.mean = mean; d.rstd = rstd;
+  if (dr) {
+    d.mask = mask; d.drop_p = dr->p; d.seed = dr->seed; d.offset = dr->offset;
+  }
   hipStream_t st = (hipStream_t)stream;
   TP_STEP(TP_STEP_LN_FWD, ln_fwd_launch(dm.dtype, d, st), "residual add + LayerNorm forward");
   return TP_OK;
 }
 
-tp_status tp_ln_residual_bwd(const tp_shape* shape, const void* resid_out, const float* mean, const float* rstd,
-                             const void* gamma, const void* d_ln_out, const void* d_resid_out_or_null, void* d_resid,
-                             void* dgamma, void* dbeta, void* dbias_or_null, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+tp_status ln_bwd_impl(const tp_shape* shape, const tp_dropout* dr, const uint8_t* mask, void* d_block,
+                      const void* resid_out, const float* mean, const float* rstd, const void* gamma,
+                      const void* d_ln_out, const void* d_resid_out_or_null, void* d_resid, void* dgamma, void* dbeta,
+                      void* dbias_or_null, void* workspace, size_t workspace_bytes, void* stream) {
   Dims dm;
   TP_CHECK(check_shape(shape, dm));
   TP_CHECK(check_ln(dm));
+  if (dr) TP_CHECK(check_p(dr));
+  if (dr) TP_CHECK(check_ptr(mask, "mask", dm.T == 0));
+  if (dr) TP_CHECK(check_ptr(d_block, "d_block", dm.T == 0));
   const bool e = dm.T == 0;
   TP_CHECK(check_ptr(resid_out, "resid_out", e));
   TP_CHECK(check_ptr(mean, "mean", e));
@@ -609,9 +628,56 @@ tp_status tp_ln_residual_bwd(const tp_shape* shape, const void* resid_out, const
   d.resid_out = (void*)resid_out; d.mean = (float*)mean; d.rstd = (float*)rstd; d.gamma = gamma;
   d.dy = d_ln_out; d.dr_in = d_resid_out_or_null; d.dr = d_resid;
   d.dgamma = dgamma; d.dbeta = dbeta; d.dbias = dbias_or_null;
+  if (dr) {
+    d.mask = (uint8_t*)mask; d.d_block = d_block; d.drop_p = dr->p; d.seed = dr->seed; d.offset = dr->offset;
+  }
   hipStream_t st = (hipStream_t)stream;
   TP_STEP(TP_STEP_LN_BWD, ln_bwd_launch(dm.dtype, d, workspace, st), "residual add + LayerNorm backward");
   return TP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tp_status tp_ln_residual_fwd(const tp_shape* shape, const void* resid_in, const void* const* parts, int32_t n_parts,
+                             const void* bias_or_null, const void* gamma, const void* beta, float eps, void* resid_out,
+                             void* ln_out, float* mean, float* rstd, void* stream) {
+  return ln_fwd_impl(shape, nullptr, nullptr, resid_in, parts, n_parts, bias_or_null, gamma, beta, eps, resid_out,
+                     ln_out, mean, rstd, stream);
+}
+
+tp_status tp_ln_residual_bwd(const tp_shape* shape, const void* resid_out, const float* mean, const float* rstd,
+                             const void* gamma, const void* d_ln_out, const void* d_resid_out_or_null, void* d_resid,
+                             void* dgamma, void* dbeta, void* dbias_or_null, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return ln_bwd_impl(shape, nullptr, nullptr, nullptr, resid_out, mean, rstd, gamma, d_ln_out, d_resid_out_or_null,
+                     d_resid, dgamma, dbeta, dbias_or_null, workspace, workspace_bytes, stream);
+}
+
+size_t tp_ln_dropout_mask_bytes(const tp_shape* shape) {
+  Dims dm;
+  if (check_shape(shape, dm) != TP_OK || check_ln(dm) != TP_OK) return 0;
+  return (size_t)(dm.T * (dm.h / 8));
+}
+
+tp_status tp_ln_residual_fwd_dropout(const tp_shape* shape, const tp_dropout* dropout, const void* resid_in,
+                                     const void* const* parts, int32_t n_parts, const void* bias_or_null,
+                                     const void* gamma, const void* beta, float eps, void* resid_out, void* ln_out,
+                                     float* mean, float* rstd, uint8_t* mask, void* stream) {
+  if (!dropout) return fail(TP_ERR_NULL, "dropout is NULL");
+  return ln_fwd_impl(shape, dropout, mask, resid_in, parts, n_parts, bias_or_null, gamma, beta, eps, resid_out,
+                     ln_out, mean, rstd, stream);
+}
+
+tp_status tp_ln_residual_bwd_dropout(const tp_shape* shape, const tp_dropout* dropout, const void* resid_out,
+                                     const float* mean, const float* rstd, const void* gamma, const void* d_ln_out,
+                                     const void* d_resid_out_or_null, const uint8_t* mask, void* d_resid,
+                                     void* d_block, void* dgamma, void* dbeta, void* dbias_or_null, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (!dropout) return fail(TP_ERR_NULL, "dropout is NULL");
+  return ln_bwd_impl(shape, dropout, mask, d_block, resid_out, mean, rstd, gamma, d_ln_out, d_resid_out_or_null,
+                     d_resid, dgamma, dbeta, dbias_or_null, workspace, workspace_bytes, stream);
 }
 
 size_t tp_vocab_workspace_bytes(const tp_shape* shape, int32_t vocab) {

@@ -38,7 +38,8 @@ def test_library_loads_and_exports_every_declared_symbol():
                           "tp_attn_fwd", "tp_attn_bwd", "tp_sum_partials", "tp_last_error", "tp_profile_enable",
                           "tp_profile_collect", "tp_ln_workspace_bytes", "tp_ln_residual_fwd", "tp_ln_residual_bwd",
                           "tp_vocab_workspace_bytes", "tp_vocab_ce_fwd", "tp_vocab_ce_combine", "tp_vocab_ce_bwd",
-                          "tp_attn_dropout_mask_bytes", "tp_attn_fwd_dropout", "tp_attn_bwd_dropout"}
+                          "tp_attn_dropout_mask_bytes", "tp_attn_fwd_dropout", "tp_attn_bwd_dropout",
+                          "tp_ln_dropout_mask_bytes", "tp_ln_residual_fwd_dropout", "tp_ln_residual_bwd_dropout"}
     for n in names:
         assert isinstance(getattr(lib, n), ctypes._CFuncPtr), n
     out = subprocess.run(["nm", "-D", "--defined-only", tp.library_path()], capture_output=True, text=True).stdout
@@ -323,3 +324,26 @@ def test_dropout_null_arguments():
     with pytest.raises(tp.TPError) as ei:
         tp.tp_attn_bwd_dropout(s, tp.TpDropout(0.1, 1, 2), *args, workspace=(FAKE, 1 << 40), stream=0)
     assert ei.value.name == "TP_ERR_ALIGN"
+
+
+
+def test_ln_dropout_validation():
+    s = shape()
+    assert tp.tp_ln_dropout_mask_bytes(s) == 64 * 64 // 8
+    for p, status in ((1.0, "TP_ERR_SHAPE"), (-1.0, "TP_ERR_SHAPE")):
+        with pytest.raises(tp.TPError) as ei:
+            tp.tp_ln_residual_fwd_dropout(s, tp.TpDropout(p, 1, 2), FAKE, [FAKE], None, FAKE, FAKE, 1e-5, FAKE, FAKE,
+                                          FAKE, FAKE, FAKE, stream=0)
+        assert ei.value.name == status
+    with pytest.raises(tp.TPError) as ei:
+        tp.tp_ln_residual_fwd_dropout(s, tp.TpDropout(0.1, 1, 2), FAKE, [FAKE], None, FAKE, FAKE, 1e-5, FAKE, FAKE,
+                                      FAKE, FAKE, None, stream=0)
+    assert ei.value.name == "TP_ERR_NULL"  # mask
+    with pytest.raises(tp.TPError) as ei:
+        tp.tp_ln_residual_fwd_dropout(s, None, FAKE, [FAKE], None, FAKE, FAKE, 1e-5, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      stream=0)
+    assert ei.value.name == "TP_ERR_NULL"  # dropout
+    with pytest.raises(tp.TPError) as ei:
+        tp.tp_ln_residual_bwd_dropout(s, tp.TpDropout(0.1, 1, 2), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                      None, FAKE, FAKE, workspace=(FAKE, 1 << 40), stream=0)
+    assert ei.value.name == "TP_ERR_NULL"  # d_block

@@ -126,3 +126,68 @@ def test_ln_residual_deterministic():
     b = run_gpu(w, inp)
     for k in OUTS:
         assert torch.equal(a[k], b[k]), k
+
+
+# ---------------------------------------------------------------------------
+# dropout on the block output before the residual add (identical on every rank)
+# ---------------------------------------------------------------------------
+
+def run_gpu_dropout(w, inp, drop):
+    s = tp_shape(w)
+    T, h, dt = w.tokens, w.hidden, _DT[w.dtype]
+    dev = lambda t: None if t is None else t.cuda().contiguous()  # noqa: E731
+    nan = float("nan")
+    o = {k: torch.full((T, h), nan, dtype=dt, device="cuda") for k in ("resid_out", "ln_out", "d_resid", "d_block")}
+    o.update({k: torch.full((T,), nan, dtype=torch.float32, device="cuda") for k in ("mean", "rstd")})
+    o.update({k: torch.full((h,), nan, dtype=dt, device="cuda") for k in ("dgamma", "dbeta", "dbias")})
+    mask = torch.zeros(max(tp.tp_ln_dropout_mask_bytes(s), 1), dtype=torch.uint8, device="cuda")
+    gamma = dev(inp["gamma"])
+    tp.tp_ln_residual_fwd_dropout(s, drop, dev(inp["resid_in"]), [dev(p) for p in inp["parts"]], dev(inp["bias"]),
+                                  gamma, dev(inp["beta"]), EPS, o["resid_out"], o["ln_out"], o["mean"], o["rstd"],
+                                  mask)
+    ws = torch.empty(max(tp.tp_ln_workspace_bytes(s), 1), dtype=torch.uint8, device="cuda")
+    tp.tp_ln_residual_bwd_dropout(s, drop, o["resid_out"], o["mean"], o["rstd"], gamma, dev(inp["d_ln_out"]),
+                                  dev(inp["d_resid_out"]), mask, o["d_resid"], o["d_block"], o["dgamma"], o["dbeta"],
+                                  o["dbias"], workspace=ws)
+    torch.cuda.synchronize()
+    o["mask"] = mask
+    return o
+
+
+DROP_CASES = [
+    ("c1_fp32_h64_two_ranks_p03", "tiny_fp32_tp2", 64, 2, 0.5, 0.3),
+    ("c4_h20480_37_rows_p01", "mtnlg_530b_tp8", 37, 1, 0.02, 0.1),
+    ("c2_h1536_ragged_p05", "gpt2_1p2b_tp1", 300, 1, 0.5, 0.5),
+]
+
+
+@pytest.mark.parametrize("case", DROP_CASES, ids=[c[0] for c in DROP_CASES])
+def test_ln_residual_dropout_matches_oracle(case):
+    name, wname, rows, n_parts, bias_std, p = case
+    w = synth.WORKLOADS[wname].with_(batch=1, seq=rows)
+    print(f"\n  [ln dropout case {name}]", flush=True)
+    inp = synth.draw_ln(w, seed=9, n_parts=n_parts, bias_std=bias_std)
+    got = run_gpu_dropout(w, inp, tp.TpDropout(p, 99, 5))
+    R = oracle.residual_multipliers(tokens=w.tokens, hidden=w.hidden, p=p, seed=99, offset=5)
+    # keep bits, bit-exact
+    bits = got["mask"].cpu().numpy()[:w.tokens * w.hidden // 8].reshape(w.tokens, w.hidden // 8)
+    keep = np.unpackbits(bits[:, :, None], axis=2, bitorder="little").reshape(w.tokens, w.hidden).astype(bool)
+    assert np.array_equal(keep, R > 0)
+    a = {k: (None if v is None else (f64(v) if not isinstance(v, list) else [f64(q) for q in v]))
+         for k, v in inp.items()}
+    r, y, mu, rstd = oracle.ln_residual_fwd(a["resid_in"], a["parts"], a["bias"], a["gamma"], a["beta"], EPS,
+                                            dropout=R)
+    dr, dblk, dg, db, dbias = oracle.ln_residual_bwd_dropout(r, a["gamma"], EPS, a["d_ln_out"], a["d_resid_out"], R)
+    for k, ref in (("resid_out", r), ("ln_out", y), ("mean", mu), ("rstd", rstd), ("d_resid", dr),
+                   ("d_block", dblk), ("dgamma", dg), ("dbeta", db), ("dbias", dbias)):
+        compare(k, got[k], ref, w.dtype)
+
+
+def test_ln_residual_dropout_p0_equals_plain():
+    w = synth.WORKLOADS["bloom_176b_tp8"].with_(batch=1, seq=50)
+    inp = synth.draw_ln(w, seed=4, n_parts=2, bias_std=0.02)
+    a = run_gpu_dropout(w, inp, tp.TpDropout(0.0, 1, 1))
+    b = run_gpu(w, inp)
+    for k in ("resid_out", "ln_out", "mean", "rstd", "d_resid", "dgamma", "dbeta"):
+        assert torch.equal(a[k], b[k]), k
+    assert torch.equal(a["d_block"], b["d_resid"])
