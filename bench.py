@@ -184,6 +184,34 @@ def ln_residual_measure(w, reps: int = 20) -> dict:
                      "frac": round(gbs / PEAK_HBM_GBS, 4)}
         log(f"  ln_residual {name}: {avg * 1e3:.1f} us, {gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of HBM)")
     tp.tp_profile_enable(0)
+    # the variant with dropout (p = 0.1) on the block output: same tensors plus the
+    # keep bytes (T h / 8) written / read and the block-output gradient written
+    drop = tp.TpDropout(0.1, 7, 0)
+    mask = torch.empty(tp.tp_ln_dropout_mask_bytes(s), dtype=torch.uint8, device="cuda")
+    dblk = torch.empty((T, h), dtype=bf, device="cuda")
+
+    def once_do():
+        tp.tp_ln_residual_fwd_dropout(s, drop, dev["resid_in"], dev["parts"], dev["bias"], dev["gamma"], dev["beta"],
+                                      1e-5, r, y, mean, rstd, mask)
+        tp.tp_ln_residual_bwd_dropout(s, drop, r, mean, rstd, dev["gamma"], dev["d_ln_out"], dev["d_resid_out"], mask,
+                                      dr, dblk, dg, db, None, workspace=ws)
+
+    for _ in range(3):
+        once_do()
+    torch.cuda.synchronize()
+    tp.tp_profile_enable((1 << tp.STEPS["ln_fwd"]) | (1 << tp.STEPS["ln_bwd"]))
+    for _ in range(reps):
+        once_do()
+    torch.cuda.synchronize()
+    extra = {"fwd": T * h // 8, "bwd": T * h // 8 + 2 * T * h}
+    for name in ("fwd", "bwd"):
+        n, ms = tp.tp_profile_collect(tp.STEPS["ln_" + name])
+        avg = ms / max(n, 1)
+        gbs = (nbytes[name] + extra[name]) / (avg / 1e3) / 1e9
+        res[name + "_dropout_p0.1"] = {"avg_launch_ms": round(avg, 4), "achieved": round(gbs, 1), "unit": "GB/s",
+                                       "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"  ln_residual {name} (dropout 0.1): {avg * 1e3:.1f} us, {gbs:.0f} GB/s")
+    tp.tp_profile_enable(0)
     return {"bound": "hbm", "workload": f"{w.name}: T={T}, hidden={h}, bf16, 1 block output, bias, residual grad",
             **res}
 
