@@ -6,7 +6,9 @@
 // per lane, one wave per SIMD); with 8 waves (2x4) each owns 128x64 (128
 // accumulators, two waves per SIMD, so one wave's barrier and load waits are
 // covered by the other's MFMAs, and twice as many loads are in flight per CU).
-// K advances 64 at a time through two LDS stages (2 x 64 KiB).
+// Products with a k-inner B may take a 256x320 tile instead (8 waves, 4x2,
+// 64x160 each, 160 accumulators). K advances 64 at a time through two LDS
+// stages (2 x 64 KiB, or 2 x 72 KiB for the 320-wide tile).
 //
 // Global -> LDS: buffer loads that write LDS directly (16 bytes per lane; one
 // instruction fills 1 KiB in lane order), so no VGPRs stage the tiles. Each
@@ -38,19 +40,27 @@
 namespace tpk {
 namespace {
 
-constexpr int BM = 256, BN = 256, BKK = 64;
-// Wave layout of a workgroup of NW waves (4: one per SIMD, 8: two per SIMD):
-// 2 waves along m (128 rows each) x NW/2 along n.
-template <int NW>
+constexpr int BM = 256, BKK = 64;
+// Wave layout of a workgroup of NW waves over a BM x BNV tile. 256 wide: 2
+// waves along m (128 rows each) x NW/2 along n (4 waves: one per SIMD, 128x128
+// each; 8 waves: two per SIMD, 128x64 each). 320 wide (8 waves, k-inner B
+// only): 4 waves along m x 2 along n, 64x160 each -- a fifth more flops per
+// byte staged than 256x256, and 2048 x 10240 / 20480 products fill 256 CUs in
+// whole rounds.
+template <int NW, int BNV>
 struct WC {
-  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert((NW == 4 && BNV == 256) || (NW == 8 && (BNV == 256 || BNV == 320)), "tile shape");
   static constexpr int NTHR = 64 * NW;
-  static constexpr int WNG = NW / 2;      // waves along n
-  static constexpr int WNW = BN / WNG;    // columns per wave
-  static constexpr int NJ = WNW / 32;     // 32-column MFMA blocks per wave
-  static constexpr int NLI = 32 / NW;     // loads per operand per wave per k-step
+  static constexpr int WMG = BNV == 320 ? 4 : 2;  // waves along m
+  static constexpr int WNG = NW / WMG;            // waves along n
+  static constexpr int WMW = BM / WMG;            // rows per wave
+  static constexpr int MI = WMW / 32;             // 32-row MFMA blocks per wave
+  static constexpr int WNW = BNV / WNG;           // columns per wave
+  static constexpr int NJ = WNW / 32;             // 32-column MFMA blocks per wave
+  static constexpr int NLA = BM * BKK * 2 / 1024 / NW;   // A loads (1 KiB each) per wave per k-step
+  static constexpr int NLB = BNV * BKK * 2 / 1024 / NW;  // B loads per wave per k-step
 };
-constexpr int STAGE = BM * BKK;  // bf16 elements per operand per stage
+constexpr int BN_MAX = 320;      // widest tile (workspace sizing)
 constexpr int GMAX = 256;        // largest persistent grid (workspace sizing)
 constexpr int GROUP_M = 8;       // tiles along M per raster group
 
@@ -69,7 +79,7 @@ struct KParams {
   bf16* C2; long ldc2;
   const bf16* bias;
   const bf16* aux; long ldaux;
-  float* partials;    // [2*sk_grid][BM*BN] (split tail: [splits*split_tiles][BM*BN])
+  float* partials;    // [2*sk_grid][BM*BNV] (split tail: [splits*split_tiles][BM*BNV])
   // Split tail (splits > 1, instead of stream-K): after the data-parallel
   // rounds, workgroup lw < splits*split_tiles takes k-range lw / split_tiles of
   // tile split_first + lw % split_tiles.
@@ -104,24 +114,24 @@ __device__ __forceinline__ const bf16* uni_ptr(const bf16* p) {
 
 // One operand panel of a tile: a buffer resource based at the panel's first
 // row (k-inner) or first column (k-outer), and this lane's byte offsets for its
-// 8 load instructions (nrec = out of range: the load writes zeros).
-template <int NW>
+// NL load instructions (nrec = out of range: the load writes zeros).
+template <int NL>
 struct Panel {
   const bf16* base;  // workgroup-uniform
   uint32_t nrec;     // workgroup-uniform buffer size in bytes
   uint32_t kstep;    // workgroup-uniform bytes the panel advances per k-step
-  uint32_t voff[WC<NW>::NLI];
+  uint32_t voff[NL];
 };
 
-// k-inner X[r*ld + k], rows r0g.. of `rows`. Load i of wave w fills LDS block
-// b = NLI*w + i = rows 8b .. 8b+7; lane l lands in row 8b+(l>>3), physical
-// chunk l&7, so it loads logical chunk (l&7) ^ swz(row) = (l&7) ^ (l>>3) ^ (b&7).
-template <int NW>
-__device__ __forceinline__ Panel<NW> panel_kinner(const bf16* X, long ld, int rows, int r0g, int wave, int lane) {
-  constexpr int NLI = WC<NW>::NLI;
-  Panel<NW> pn;
+// k-inner X[r*ld + k], rows r0g .. r0g+PR-1 of `rows`. Load i of wave w fills
+// LDS block b = NLI*w + i = rows 8b .. 8b+7; lane l lands in row 8b+(l>>3),
+// physical chunk l&7, so it loads logical chunk (l&7) ^ swz(row) =
+// (l&7) ^ (l>>3) ^ (b&7).
+template <int NLI, int PR>
+__device__ __forceinline__ Panel<NLI> panel_kinner(const bf16* X, long ld, int rows, int r0g, int wave, int lane) {
+  Panel<NLI> pn;
   int nrows = rows - r0g;
-  nrows = nrows < 256 ? nrows : 256;
+  nrows = nrows < PR ? nrows : PR;
   pn.base = uni_ptr(X + (long)r0g * ld);
   pn.nrec = uni((uint32_t)((long)nrows * ld * 2));
   pn.kstep = BKK * 2;
@@ -138,11 +148,10 @@ __device__ __forceinline__ Panel<NW> panel_kinner(const bf16* X, long ld, int ro
 // block b = NLI*w + i = k-rows 2b, 2b+1; lane l lands in k-row 2b+(l>>5),
 // physical chunk l&31, so it loads logical chunk (l&31) ^ 4(krow&3). Rows at
 // or past K fall beyond nrec and load zeros.
-template <int NW>
-__device__ __forceinline__ Panel<NW> panel_kouter(const bf16* X, long ld, int rows, int K, int r0g, int wave,
-                                                  int lane) {
-  constexpr int NLI = WC<NW>::NLI;
-  Panel<NW> pn;
+template <int NLI>
+__device__ __forceinline__ Panel<NLI> panel_kouter(const bf16* X, long ld, int rows, int K, int r0g, int wave,
+                                                   int lane) {
+  Panel<NLI> pn;
   pn.base = uni_ptr(X + r0g);
   pn.nrec = uni((uint32_t)(((long)K * ld - r0g) * 2));
   pn.kstep = uni((uint32_t)(BKK * ld * 2));
@@ -156,9 +165,8 @@ __device__ __forceinline__ Panel<NW> panel_kouter(const bf16* X, long ld, int ro
 }
 
 // Issue the NLI loads of one operand for k-step kt into LDS stage `dst`.
-template <int NW, bool KIN>
-__device__ __forceinline__ void issue_panel(const Panel<NW>& pn, int kt, int K, bf16* dst, int wave, int lane) {
-  constexpr int NLI = WC<NW>::NLI;
+template <int NLI, bool KIN>
+__device__ __forceinline__ void issue_panel(const Panel<NLI>& pn, int kt, int K, bf16* dst, int wave, int lane) {
   const int soff = (int)uni((uint32_t)kt * pn.kstep);
   __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)pn.base, (short)0, (int)pn.nrec, 0x00020000);
   // k tail (k-inner only): chunks at or past K must read zeros, not the next row
@@ -179,10 +187,11 @@ __device__ __forceinline__ void issue_panel(const Panel<NW>& pn, int kt, int K, 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ---- fragment reads ------------------------------------------------------------
-// k-inner: 32-row block i of this wave's 128 rows; lane owns row base+32i+(l&31)
-// and k = 16kk + 8(l>>5) .. +7.
-__device__ __forceinline__ bf16x8 frag_kin(const bf16* s, int rowbase, int s1, int g, int kk, int i) {
-  const int e = (2 * kk) ^ g ^ s1 ^ (4 * (i & 1));
+// k-inner: 32-row block i of this wave's rows; lane owns row base+32i+(l&31)
+// and k = 16kk + 8(l>>5) .. +7. The wave's first row `base` is a multiple of
+// 32; pb = (base/32) & 1 is its contribution to bit 2 of the row swizzle.
+__device__ __forceinline__ bf16x8 frag_kin(const bf16* s, int rowbase, int s1, int g, int kk, int i, int pb) {
+  const int e = (2 * kk) ^ g ^ s1 ^ (4 * ((i + pb) & 1));
   return *(const bf16x8*)(s + rowbase + i * 32 * BKK + (e << 3));
 }
 // k-outer: per-lane byte offset of 32-column block jb inside a stage (see the
@@ -212,39 +221,42 @@ __device__ __forceinline__ bf16x8 frag_kout(const bf16* s, int lane_off, int kk)
 // information lets the compiler's wait-count pass leave the in-flight LDS
 // writes (other stage) outstanding while the fragment reads (this stage)
 // proceed.
-template <int NW, bool AK, bool BKM>
-__device__ __forceinline__ void kstep(const KParams& p, const Panel<NW>& pa, const Panel<NW>& pb, int kt,
-                                      const bf16* __restrict__ a, const bf16* __restrict__ b,
-                                      bf16* __restrict__ na, bf16* __restrict__ nb, int wave, int lane, int rowA,
-                                      int rowB, const int (&offA)[4], const int (&offB)[WC<NW>::NJ], int s1, int g,
-                                      f32x16 (&acc)[4][WC<NW>::NJ]) {
-  constexpr int NJ = WC<NW>::NJ, NLI = WC<NW>::NLI;
+template <int NW, int BNV, bool AK, bool BKM>
+__device__ __forceinline__ void kstep(const KParams& p, const Panel<WC<NW, BNV>::NLA>& pa,
+                                      const Panel<WC<NW, BNV>::NLB>& pb, int kt, const bf16* __restrict__ a,
+                                      const bf16* __restrict__ b, bf16* __restrict__ na, bf16* __restrict__ nb,
+                                      int wave, int lane, int rowA, int rowB, const int (&offA)[WC<NW, BNV>::MI],
+                                      const int (&offB)[WC<NW, BNV>::NJ], int s1, int g, int pbA, int pbB,
+                                      f32x16 (&acc)[WC<NW, BNV>::MI][WC<NW, BNV>::NJ]) {
+  constexpr int MI = WC<NW, BNV>::MI, NJ = WC<NW, BNV>::NJ;
+  constexpr int NLA = WC<NW, BNV>::NLA, NLB = WC<NW, BNV>::NLB;
+  constexpr int NF = MI > NJ ? MI : NJ;
   wait_vmem();
   __syncthreads();
   // Next k-step's loads, unconditionally so that the whole step is one
   // scheduling region: past the last k-step of the tile they read either zeros
   // (k beyond K is out of the buffer's range) or in-range data nobody uses.
-  issue_panel<NW, AK>(pa, kt + 1, p.K, na, wave, lane);
-  issue_panel<NW, BKM>(pb, kt + 1, p.K, nb, wave, lane);
+  issue_panel<NLA, AK>(pa, kt + 1, p.K, na, wave, lane);
+  issue_panel<NLB, BKM>(pb, kt + 1, p.K, nb, wave, lane);
   // fragments read in the order a0, b0, a1, b1, ...
-  bf16x8 af[2][4], bfg[2][NJ];
+  bf16x8 af[2][MI], bfg[2][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    af[0][i] = AK ? frag_kin(a, rowA, s1, g, 0, i) : frag_kout(a, offA[i], 0);
-    if (i < NJ) bfg[0][i] = BKM ? frag_kin(b, rowB, s1, g, 0, i) : frag_kout(b, offB[i], 0);
+  for (int i = 0; i < NF; ++i) {
+    if (i < MI) af[0][i] = AK ? frag_kin(a, rowA, s1, g, 0, i, pbA) : frag_kout(a, offA[i], 0);
+    if (i < NJ) bfg[0][i] = BKM ? frag_kin(b, rowB, s1, g, 0, i, pbB) : frag_kout(b, offB[i], 0);
   }
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     const int c = kk & 1, n = c ^ 1;
     if (kk < 3) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        af[n][i] = AK ? frag_kin(a, rowA, s1, g, kk + 1, i) : frag_kout(a, offA[i], kk + 1);
-        if (i < NJ) bfg[n][i] = BKM ? frag_kin(b, rowB, s1, g, kk + 1, i) : frag_kout(b, offB[i], kk + 1);
+      for (int i = 0; i < NF; ++i) {
+        if (i < MI) af[n][i] = AK ? frag_kin(a, rowA, s1, g, kk + 1, i, pbA) : frag_kout(a, offA[i], kk + 1);
+        if (i < NJ) bfg[n][i] = BKM ? frag_kin(b, rowB, s1, g, kk + 1, i, pbB) : frag_kout(b, offB[i], kk + 1);
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
         // operands swapped: D[n][m], so each lane ends up owning one m and
@@ -253,9 +265,10 @@ __device__ __forceinline__ void kstep(const KParams& p, const Panel<NW>& pa, con
   }
   // Instruction order for the step: the first sub-step's fragment reads, then
   // the MFMAs with the next sub-step's fragment reads spread evenly between
-  // them and (in the first sub-step) the next k-step's 2*NLI loads.
-  constexpr int R = (AK ? 4 : 8) + (BKM ? NJ : 2 * NJ);  // LDS reads per sub-step
-  constexpr int NM = 4 * NJ;                              // MFMAs per sub-step
+  // them and (in the first sub-step) the next k-step's NLA+NLB loads.
+  constexpr int R = (AK ? MI : 2 * MI) + (BKM ? NJ : 2 * NJ);  // LDS reads per sub-step
+  constexpr int NM = MI * NJ;                                  // MFMAs per sub-step
+  constexpr int NL = NLA + NLB;                                // global->LDS loads per k-step
   __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
@@ -266,39 +279,44 @@ __device__ __forceinline__ void kstep(const KParams& p, const Panel<NW>& pa, con
       if (kk < 3)
 #pragma unroll
         for (int t = 0; t < nr; ++t) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      const int nv = (2 * NLI * (m + 1)) / NM - (2 * NLI * m) / NM;
+      const int nv = (NL * (m + 1)) / NM - (NL * m) / NM;
       if (kk == 0)
 #pragma unroll
         for (int t = 0; t < nv; ++t) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
 }
 
-template <int NW, bool AK, bool BKM>
+template <int NW, int BNV, bool AK, bool BKM>
 __device__ __forceinline__ void mainloop(const KParams& p, int tm, int tn, int kb, int ke,
-                                         f32x16 (&acc)[4][WC<NW>::NJ], bf16* sA0, bf16* sA1, bf16* sB0, bf16* sB1) {
-  constexpr int NJ = WC<NW>::NJ, WNG = WC<NW>::WNG, WNW = WC<NW>::WNW;
+                                         f32x16 (&acc)[WC<NW, BNV>::MI][WC<NW, BNV>::NJ], bf16* sA0, bf16* sA1,
+                                         bf16* sB0, bf16* sB1) {
+  using C = WC<NW, BNV>;
+  constexpr int MI = C::MI, NJ = C::NJ, WNG = C::WNG, WMW = C::WMW, WNW = C::WNW;
+  static_assert(BKM || BNV == 256, "k-outer B panels are 256 columns wide");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = (int)uni((uint32_t)(tid >> 6));
   const int wm = wave / WNG, wn = wave % WNG;
   const int g = lane >> 5, l32 = lane & 31;
   const int s1 = (l32 & 7) ^ (l32 >> 3);
-  Panel<NW> pa, pb;
-  if (AK) pa = panel_kinner<NW>(p.A, p.lda, p.M, tm * BM, wave, lane);
-  else pa = panel_kouter<NW>(p.A, p.lda, p.M, p.K, tm * BM, wave, lane);
-  if (BKM) pb = panel_kinner<NW>(p.B, p.ldb, p.N, tn * BN, wave, lane);
-  else pb = panel_kouter<NW>(p.B, p.ldb, p.N, p.K, tn * BN, wave, lane);
-  const int rowA = (wm * 128 + l32) * BKK, rowB = (wn * WNW + l32) * BKK;
-  int offA[4], offB[NJ];
+  Panel<C::NLA> pa;
+  Panel<C::NLB> pb;
+  if (AK) pa = panel_kinner<C::NLA, BM>(p.A, p.lda, p.M, tm * BM, wave, lane);
+  else pa = panel_kouter<C::NLA>(p.A, p.lda, p.M, p.K, tm * BM, wave, lane);
+  if (BKM) pb = panel_kinner<C::NLB, BNV>(p.B, p.ldb, p.N, tn * BNV, wave, lane);
+  else pb = panel_kouter<C::NLB>(p.B, p.ldb, p.N, p.K, tn * BNV, wave, lane);
+  const int rowA = (wm * WMW + l32) * BKK, rowB = (wn * WNW + l32) * BKK;
+  const int pbA = (wm * WMW / 32) & 1, pbB = (wn * WNW / 32) & 1;
+  int offA[MI], offB[NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) offA[i] = AK ? 0 : kout_lane_off(wm * 128, i, lane);
+  for (int i = 0; i < MI; ++i) offA[i] = AK ? 0 : kout_lane_off(wm * WMW, i, lane);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) offB[j] = BKM ? 0 : kout_lane_off(wn * WNW, j, lane);
-  issue_panel<NW, AK>(pa, kb, p.K, sA0, wave, lane);
-  issue_panel<NW, BKM>(pb, kb, p.K, sB0, wave, lane);
+  issue_panel<C::NLA, AK>(pa, kb, p.K, sA0, wave, lane);
+  issue_panel<C::NLB, BKM>(pb, kb, p.K, sB0, wave, lane);
   for (int kt = kb; kt < ke; ++kt) {
     const bool odd = (kt - kb) & 1;
-    kstep<NW, AK, BKM>(p, pa, pb, kt, odd ? sA1 : sA0, odd ? sB1 : sB0, odd ? sA0 : sA1, odd ? sB0 : sB1, wave, lane,
-                   rowA, rowB, offA, offB, s1, g, acc);
+    kstep<NW, BNV, AK, BKM>(p, pa, pb, kt, odd ? sA1 : sA0, odd ? sB1 : sB0, odd ? sA0 : sA1, odd ? sB0 : sB1, wave,
+                            lane, rowA, rowB, offA, offB, s1, g, pbA, pbB, acc);
   }
   wait_vmem();      // the last step's read-ahead loads have landed
   __syncthreads();  // LDS is reused by the next work item
@@ -312,21 +330,21 @@ __device__ __forceinline__ void store_bf16x4(bf16* dst, const float (&v)[4]) {
   *(bf16x4*)dst = o;
 }
 
-// Row block i (rows 32i..32i+31 of each wave's 128) of a tile.
-template <int NW, int EPI>
+// Row block i (rows 32i..32i+31 of each wave's rows) of a tile.
+template <int NW, int BNV, int EPI>
 __device__ __forceinline__ void epilogue_rows(const KParams& p, int tm, int tn, int i,
-                                              const f32x16 (&acc)[WC<NW>::NJ]) {
-  constexpr int NJ = WC<NW>::NJ, WNG = WC<NW>::WNG, WNW = WC<NW>::WNW;
+                                              const f32x16 (&acc)[WC<NW, BNV>::NJ]) {
+  constexpr int NJ = WC<NW, BNV>::NJ, WNG = WC<NW, BNV>::WNG, WMW = WC<NW, BNV>::WMW, WNW = WC<NW, BNV>::WNW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WNG, wn = wave % WNG;
   {
-    const int m = tm * BM + wm * 128 + i * 32 + (lane & 31);
+    const int m = tm * BM + wm * WMW + i * 32 + (lane & 31);
     if (m >= p.M) return;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int n = tn * BN + wn * WNW + j * 32 + q4 * 8 + (lane >> 5) * 4;
+        const int n = tn * BNV + wn * WNW + j * 32 + q4 * 8 + (lane >> 5) * 4;
         if (n >= p.N) continue;
         float v[4] = {acc[j][4 * q4], acc[j][4 * q4 + 1], acc[j][4 * q4 + 2], acc[j][4 * q4 + 3]};
         if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_F32) {
@@ -355,10 +373,80 @@ __device__ __forceinline__ void epilogue_rows(const KParams& p, int tm, int tn, 
   }
 }
 
-template <int NW, int EPI>
-__device__ __forceinline__ void epilogue(const KParams& p, int tm, int tn, const f32x16 (&acc)[4][WC<NW>::NJ]) {
+template <int NW, int BNV, int EPI>
+__device__ __forceinline__ void epilogue(const KParams& p, int tm, int tn,
+                                         const f32x16 (&acc)[WC<NW, BNV>::MI][WC<NW, BNV>::NJ]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) epilogue_rows<NW, EPI>(p, tm, tn, i, acc[i]);
+  for (int i = 0; i < WC<NW, BNV>::MI; ++i) epilogue_rows<NW, BNV, EPI>(p, tm, tn, i, acc[i]);
+}
+
+// Whole-tile epilogue of a plain store through LDS (the stages are free once
+// the main loop has ended): each wave writes its bf16 results into a
+// [256 rows][256 cols] image -- rows 64q .. 64q+63 in stage array q, 16-byte
+// chunk c of row m at c ^ (m & 31), so that neither the row-per-lane writes
+// nor the row-major reads conflict on banks -- and the workgroup then stores
+// whole rows, 1 KiB (two rows) per instruction. Storing straight from the
+// accumulator layout writes 16 bytes into each of 32 rows per instruction;
+// with K short (the weight gradients) that epilogue is a visible share of the
+// tile. The LDS-only barriers leave the global stores in flight.
+__device__ __forceinline__ void lds_only_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int NW, int BNV>
+__device__ __forceinline__ void epilogue_store_lds(const KParams& p, int tm, int tn,
+                                                   const f32x16 (&acc)[WC<NW, BNV>::MI][WC<NW, BNV>::NJ],
+                                                   bf16* q0, bf16* q1, bf16* q2, bf16* q3) {
+  using C = WC<NW, BNV>;
+  static_assert(BNV == 256 && BM == 256 && BKK == 64 && C::WMW == 128, "one 64-row quarter per stage array");
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+  // an opaque copy of the thread id keeps the ~60 per-lane addresses below
+  // from being hoisted out of the tile loop (they would be held, or spilled,
+  // across the main loop)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = (int)uni((uint32_t)(tid >> 6));
+  const int wm = wave / C::WNG, wn = wave % C::WNG;
+  const int l32 = lane & 31;
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i) {
+    // rows wm*128 + 32i + l32: quarter 2wm + i/2, row (32i + l32) & 63 in it
+    bf16* qa = (i < 2) ? q0 : q1;
+    bf16* qb = (i < 2) ? q2 : q3;
+    bf16* row = (wm ? qb : qa) + ((32 * i + l32) & 63) * 256;
+    const int sw = (32 * i + l32) & 31;  // = m & 31
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int c = (wn * C::WNW + j * 32 + q4 * 8) >> 3;
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (bf16)acc[i][j][4 * q4 + e];
+        *(lds_bf16x4*)(row + ((c ^ sw) << 3) + (lane >> 5) * 4) = o;
+      }
+  }
+  lds_only_barrier();
+  constexpr int ITERS = BM * 32 / C::NTHR;  // 16-byte chunks per thread
+  constexpr int PER_Q = ITERS / 4;          // iterations per 64-row quarter
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    bf16* q = it < PER_Q ? q0 : it < 2 * PER_Q ? q1 : it < 3 * PER_Q ? q2 : q3;
+    const int lin = it * C::NTHR + tid, m = lin >> 5, c = lin & 31;
+    const bf16x8 v = *(lds_bf16x8*)(q + (m & 63) * 256 + ((c ^ (m & 31)) << 3));
+    const int gm = tm * BM + m, gn = tn * BNV + 8 * c;
+    if (gm < p.M && gn < p.N) *(bf16x8*)(p.C + (long)gm * p.ldc + gn) = v;
+  }
+  lds_only_barrier();  // the next tile's loads overwrite the stages
+}
+
+// Whole-tile epilogue: the LDS-staged store for plain stores of 4-wave tiles,
+// else straight from the accumulators.
+template <int NW, int BNV, int EPI>
+__device__ __forceinline__ void epilogue_tile(const KParams& p, int tm, int tn,
+                                              const f32x16 (&acc)[WC<NW, BNV>::MI][WC<NW, BNV>::NJ], bf16* sA0,
+                                              bf16* sA1, bf16* sB0, bf16* sB1) {
+  if constexpr (NW == 4 && EPI == EPI_STORE) epilogue_store_lds<NW, BNV>(p, tm, tn, acc, sA0, sA1, sB0, sB1);
+  else epilogue<NW, BNV, EPI>(p, tm, tn, acc);
 }
 
 // ---- stream-K bookkeeping -----------------------------------------------------
@@ -375,12 +463,12 @@ __device__ __forceinline__ long long sk_owner(long long x, long long base, long 
 // Partial tiles are stored in accumulator order: float4 f4 of thread tid at
 // (f4*NTHR + tid)*4, so each store/load instruction covers NTHR*16 bytes
 // contiguously.
-template <int NW>
-__device__ __forceinline__ void store_partial(float* slot, const f32x16 (&acc)[4][WC<NW>::NJ]) {
-  constexpr int NJ = WC<NW>::NJ, NTHR = WC<NW>::NTHR;
+template <int NW, int BNV>
+__device__ __forceinline__ void store_partial(float* slot, const f32x16 (&acc)[WC<NW, BNV>::MI][WC<NW, BNV>::NJ]) {
+  constexpr int MI = WC<NW, BNV>::MI, NJ = WC<NW, BNV>::NJ, NTHR = WC<NW, BNV>::NTHR;
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -394,9 +482,9 @@ __device__ __forceinline__ void store_partial(float* slot, const f32x16 (&acc)[4
 // One loop over this workgroup's work items: first its data-parallel tiles,
 // then its run of stream-K iterations (whole tiles in the run are stored
 // directly, partial tiles go to the workspace).
-template <int NW, bool AK, bool BKM, int EPI>
+template <int NW, int BNV, bool AK, bool BKM, int EPI>
 __device__ __forceinline__ void gemm_body(const KParams& p, bf16* sA0, bf16* sA1, bf16* sB0, bf16* sB1) {
-  constexpr int NJ = WC<NW>::NJ;
+  constexpr int MI = WC<NW, BNV>::MI, NJ = WC<NW, BNV>::NJ;
   const int lw = logical_wg(blockIdx.x, p.grid);
   if (p.splits > 1) {
     // data-parallel rounds, then the split tail: consecutive workgroups (one
@@ -406,13 +494,13 @@ __device__ __forceinline__ void gemm_body(const KParams& p, bf16* sA0, bf16* sA1
       const int t = r * p.grid + lw;
       int tm, tn;
       tile_coords(p, t, tm, tn);
-      f32x16 acc[4][NJ];
+      f32x16 acc[MI][NJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
-      mainloop<NW, AK, BKM>(p, tm, tn, 0, p.iters, acc, sA0, sA1, sB0, sB1);
-      epilogue<NW, EPI>(p, tm, tn, acc);
+      mainloop<NW, BNV, AK, BKM>(p, tm, tn, 0, p.iters, acc, sA0, sA1, sB0, sB1);
+      epilogue_tile<NW, BNV, EPI>(p, tm, tn, acc, sA0, sA1, sB0, sB1);
     }
     if (lw >= p.splits * p.split_tiles) return;
     const int t = p.split_first + lw % p.split_tiles, sidx = lw / p.split_tiles;
@@ -420,13 +508,13 @@ __device__ __forceinline__ void gemm_body(const KParams& p, bf16* sA0, bf16* sA1
     const int ke = (int)((long long)(sidx + 1) * p.iters / p.splits);
     int tm, tn;
     tile_coords(p, t, tm, tn);
-    f32x16 acc[4][NJ];
+    f32x16 acc[MI][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
-    mainloop<NW, AK, BKM>(p, tm, tn, kb, ke, acc, sA0, sA1, sB0, sB1);
-    store_partial<NW>(p.partials + (long)lw * BM * BN, acc);
+    mainloop<NW, BNV, AK, BKM>(p, tm, tn, kb, ke, acc, sA0, sA1, sB0, sB1);
+    store_partial<NW, BNV>(p.partials + (long)lw * BM * BNV, acc);
     return;
   }
   const bool in_sk = p.sk_total > 0 && lw < p.sk_grid;
@@ -457,36 +545,36 @@ __device__ __forceinline__ void gemm_body(const KParams& p, bf16* sA0, bf16* sA1
     }
     int tm, tn;
     tile_coords(p, t, tm, tn);
-    f32x16 acc[4][NJ];
+    f32x16 acc[MI][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
-    mainloop<NW, AK, BKM>(p, tm, tn, kb, ke, acc, sA0, sA1, sB0, sB1);
+    mainloop<NW, BNV, AK, BKM>(p, tm, tn, kb, ke, acc, sA0, sA1, sB0, sB1);
     if (kb == 0 && ke == p.iters) {
-      epilogue<NW, EPI>(p, tm, tn, acc);
+      epilogue_tile<NW, BNV, EPI>(p, tm, tn, acc, sA0, sA1, sB0, sB1);
     } else {
       const long long t0 = (long long)t * p.iters - p.sk_begin;  // tile start, SK-relative
       const int slot = 2 * lw + (s >= t0 ? 0 : 1);
-      store_partial<NW>(p.partials + (long)slot * BM * BN, acc);
+      store_partial<NW, BNV>(p.partials + (long)slot * BM * BNV, acc);
     }
   }
 }
 
 // Stream-K fix-up: sum each split tile's partials in contributor order and
 // apply the epilogue.
-template <int NW, int EPI>
+template <int NW, int BNV, int EPI>
 __device__ __forceinline__ void fixup_body(const KParams& p, int first_tile) {
-  constexpr int NJ = WC<NW>::NJ, NTHR = WC<NW>::NTHR;
-  // four workgroups per tile, one per row block i of the waves' sub-tiles
-  const int t = first_tile + blockIdx.x / 4, i = blockIdx.x % 4;
+  constexpr int MI = WC<NW, BNV>::MI, NJ = WC<NW, BNV>::NJ, NTHR = WC<NW, BNV>::NTHR;
+  // MI workgroups per tile, one per row block i of the waves' sub-tiles
+  const int t = first_tile + blockIdx.x / MI, i = blockIdx.x % MI;
   const int tid = threadIdx.x;
   if (p.splits > 1) {  // split tail: tile t's partials are slots (t - first) + s*split_tiles
     f32x16 acc[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[j] = f32x16{};
     for (int sidx = 0; sidx < p.splits; ++sidx) {
-      const float* src = p.partials + (long)(sidx * p.split_tiles + t - p.split_first) * BM * BN;
+      const float* src = p.partials + (long)(sidx * p.split_tiles + t - p.split_first) * BM * BNV;
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -501,7 +589,7 @@ __device__ __forceinline__ void fixup_body(const KParams& p, int first_tile) {
     }
     int tm, tn;
     tile_coords(p, t, tm, tn);
-    epilogue_rows<NW, EPI>(p, tm, tn, i, acc);
+    epilogue_rows<NW, BNV, EPI>(p, tm, tn, i, acc);
     return;
   }
   const long long base = p.sk_total / p.sk_grid, rem = p.sk_total % p.sk_grid;
@@ -513,7 +601,7 @@ __device__ __forceinline__ void fixup_body(const KParams& p, int first_tile) {
   for (int j = 0; j < NJ; ++j) acc[j] = f32x16{};
   for (long long c = c0; c <= c1; ++c) {
     const int slot = (int)(2 * c + (sk_start(c, base, rem) >= t0 ? 0 : 1));
-    const float* src = p.partials + (long)slot * BM * BN;
+    const float* src = p.partials + (long)slot * BM * BNV;
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -528,49 +616,56 @@ __device__ __forceinline__ void fixup_body(const KParams& p, int first_tile) {
   }
   int tm, tn;
   tile_coords(p, t, tm, tn);
-  epilogue_rows<NW, EPI>(p, tm, tn, i, acc);
+  epilogue_rows<NW, BNV, EPI>(p, tm, tn, i, acc);
 }
 
 }  // namespace
 
 // One kernel (and its stream-K fix-up kernel) per product of the layer, so
 // that a trace attributes time to each step by name.
-#define TP_GEMM_KERNELS(NAME, NWV, AKV, BKV, EV)                                      \
-  __global__ __launch_bounds__(64 * NWV)                                              \
-  __attribute__((amdgpu_waves_per_eu(NWV / 4, NWV / 4))) void NAME(KParams p) {       \
-    __shared__ __attribute__((aligned(16))) bf16 sA0[STAGE];                          \
-    __shared__ __attribute__((aligned(16))) bf16 sA1[STAGE];                          \
-    __shared__ __attribute__((aligned(16))) bf16 sB0[STAGE];                          \
-    __shared__ __attribute__((aligned(16))) bf16 sB1[STAGE];                          \
-    gemm_body<NWV, AKV, BKV, EV>(p, sA0, sA1, sB0, sB1);                              \
-  }                                                                                   \
-  __global__ __launch_bounds__(64 * NWV) void NAME##_fixup(KParams p, int first_tile) { \
-    fixup_body<NWV, EV>(p, first_tile);                                               \
+#define TP_GEMM_KERNELS(NAME, NWV, BNV, AKV, BKV, EV)                                      \
+  __global__ __launch_bounds__(64 * NWV)                                                   \
+  __attribute__((amdgpu_waves_per_eu(NWV / 4, NWV / 4))) void NAME(KParams p) {            \
+    __shared__ __attribute__((aligned(16))) bf16 sA0[BM * BKK];                            \
+    __shared__ __attribute__((aligned(16))) bf16 sA1[BM * BKK];                            \
+    __shared__ __attribute__((aligned(16))) bf16 sB0[BNV * BKK];                           \
+    __shared__ __attribute__((aligned(16))) bf16 sB1[BNV * BKK];                           \
+    gemm_body<NWV, BNV, AKV, BKV, EV>(p, sA0, sA1, sB0, sB1);                              \
+  }                                                                                        \
+  __global__ __launch_bounds__(64 * NWV) void NAME##_fixup(KParams p, int first_tile) {    \
+    fixup_body<NWV, BNV, EV>(p, first_tile);                                               \
   }
 
 // Products with a k-inner A (activations of the forward products, input
 // gradients) run 8 waves per workgroup (two per SIMD); the weight gradients
-// (both operands read through transposing LDS loads) run 4.
+// (both operands read through transposing LDS loads) run 4. Products with a
+// k-inner B also have a 256x320-tile kernel (suffix _n320), taken when N is a
+// multiple of 320.
 // forward products: A k-inner (activations), B k-outer (weights)
-TP_GEMM_KERNELS(gemm_qkv_proj, 8, true, false, EPI_BIAS_F32)
-TP_GEMM_KERNELS(gemm_out_proj, 8, true, false, EPI_STORE)
-TP_GEMM_KERNELS(gemm_fc1_bias_gelu, 8, true, false, EPI_BIAS_GELU)
-TP_GEMM_KERNELS(gemm_fc2, 8, true, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_qkv_proj, 8, 256, true, false, EPI_BIAS_F32)
+TP_GEMM_KERNELS(gemm_out_proj, 8, 256, true, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_fc1_bias_gelu, 8, 256, true, false, EPI_BIAS_GELU)
+TP_GEMM_KERNELS(gemm_fc2, 8, 256, true, false, EPI_STORE)
 // input gradients: both k-inner (weights read transposed)
-TP_GEMM_KERNELS(gemm_fc2_dgrad_gelu, 8, true, true, EPI_DGELU)
-TP_GEMM_KERNELS(gemm_fc1_dgrad, 8, true, true, EPI_STORE)
-TP_GEMM_KERNELS(gemm_out_dgrad, 8, true, true, EPI_STORE)
-TP_GEMM_KERNELS(gemm_qkv_dgrad, 8, true, true, EPI_STORE)
+TP_GEMM_KERNELS(gemm_fc2_dgrad_gelu, 8, 256, true, true, EPI_DGELU)
+TP_GEMM_KERNELS(gemm_fc1_dgrad, 8, 256, true, true, EPI_STORE)
+TP_GEMM_KERNELS(gemm_out_dgrad, 8, 256, true, true, EPI_STORE)
+TP_GEMM_KERNELS(gemm_qkv_dgrad, 8, 256, true, true, EPI_STORE)
+TP_GEMM_KERNELS(gemm_fc2_dgrad_gelu_n320, 8, 320, true, true, EPI_DGELU)
+TP_GEMM_KERNELS(gemm_fc1_dgrad_n320, 8, 320, true, true, EPI_STORE)
+TP_GEMM_KERNELS(gemm_out_dgrad_n320, 8, 320, true, true, EPI_STORE)
+TP_GEMM_KERNELS(gemm_qkv_dgrad_n320, 8, 320, true, true, EPI_STORE)
 // weight gradients: both k-outer (K = tokens)
-TP_GEMM_KERNELS(gemm_fc2_wgrad, 4, false, false, EPI_STORE)
-TP_GEMM_KERNELS(gemm_fc1_wgrad, 4, false, false, EPI_STORE)
-TP_GEMM_KERNELS(gemm_out_wgrad, 4, false, false, EPI_STORE)
-TP_GEMM_KERNELS(gemm_qkv_wgrad, 4, false, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_fc2_wgrad, 4, 256, false, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_fc1_wgrad, 4, 256, false, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_out_wgrad, 4, 256, false, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_qkv_wgrad, 4, 256, false, false, EPI_STORE)
 // vocabulary-parallel output layer: logits = X W_i^T (the table slice W_i
 // [V/p, h] is k-inner), dX = dlogits W_i, dW_i = dlogits^T X
-TP_GEMM_KERNELS(gemm_logits, 8, true, true, EPI_STORE)
-TP_GEMM_KERNELS(gemm_logits_dgrad, 8, true, false, EPI_STORE)
-TP_GEMM_KERNELS(gemm_logits_wgrad, 4, false, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_logits, 8, 256, true, true, EPI_STORE)
+TP_GEMM_KERNELS(gemm_logits_n320, 8, 320, true, true, EPI_STORE)
+TP_GEMM_KERNELS(gemm_logits_dgrad, 8, 256, true, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_logits_wgrad, 4, 256, false, false, EPI_STORE)
 #undef TP_GEMM_KERNELS
 
 namespace {
@@ -634,22 +729,68 @@ int device_cus() {
 
 }  // namespace
 
+// Upper bound over the tile widths a product may run with.
 size_t gemm_mfma_workspace_bytes(int M, int N, int K) {
-  const long long tiles = (long long)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const long long iters = (K + BKK - 1) / BKK;
-  if (iters < 8 || tiles <= 0) return 0;
-  long long slots = 2LL * GMAX;
-  if (slots > 2 * tiles * iters) slots = 2 * tiles * iters;
-  return (size_t)slots * BM * BN * sizeof(float);
+  size_t best = 0;
+  for (int bn : {256, BN_MAX}) {
+    const long long tiles = (long long)((M + BM - 1) / BM) * ((N + bn - 1) / bn);
+    if (iters < 8 || tiles <= 0) continue;
+    long long slots = 2LL * GMAX;
+    if (slots > 2 * tiles * iters) slots = 2 * tiles * iters;
+    const size_t b = (size_t)slots * BM * bn * sizeof(float);
+    best = b > best ? b : best;
+  }
+  return best;
 }
 
 hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStream_t stream) {
+  typedef void (*MainK)(KParams);
+  typedef void (*FixK)(KParams, int);
+  MainK mk = nullptr, mkw = nullptr;
+  FixK fk = nullptr, fkw = nullptr;
+  bool ak = true, bk = false;
+  int ep = EPI_STORE, nw = 4;
+#define TP_ROLE(R, NAME, NWV, AKV, BKV, EV) \
+  case R: mk = NAME; fk = NAME##_fixup; nw = NWV; ak = AKV; bk = BKV; ep = EV; break;
+#define TP_ROLE_W(R, NAME, NWV, AKV, BKV, EV)                                                    \
+  case R: mk = NAME; fk = NAME##_fixup; mkw = NAME##_n320; fkw = NAME##_n320_fixup; nw = NWV; ak = AKV; \
+    bk = BKV; ep = EV; break;
+  switch (g.role) {
+    TP_ROLE(GR_QKV_PROJ, gemm_qkv_proj, 8, true, false, EPI_BIAS_F32)
+    TP_ROLE(GR_OUT_PROJ, gemm_out_proj, 8, true, false, EPI_STORE)
+    TP_ROLE(GR_FC1, gemm_fc1_bias_gelu, 8, true, false, EPI_BIAS_GELU)
+    TP_ROLE(GR_FC2, gemm_fc2, 8, true, false, EPI_STORE)
+    TP_ROLE_W(GR_FC2_DGRAD, gemm_fc2_dgrad_gelu, 8, true, true, EPI_DGELU)
+    TP_ROLE_W(GR_FC1_DGRAD, gemm_fc1_dgrad, 8, true, true, EPI_STORE)
+    TP_ROLE_W(GR_OUT_DGRAD, gemm_out_dgrad, 8, true, true, EPI_STORE)
+    TP_ROLE_W(GR_QKV_DGRAD, gemm_qkv_dgrad, 8, true, true, EPI_STORE)
+    TP_ROLE(GR_FC2_WGRAD, gemm_fc2_wgrad, 4, false, false, EPI_STORE)
+    TP_ROLE(GR_FC1_WGRAD, gemm_fc1_wgrad, 4, false, false, EPI_STORE)
+    TP_ROLE(GR_OUT_WGRAD, gemm_out_wgrad, 4, false, false, EPI_STORE)
+    TP_ROLE(GR_QKV_WGRAD, gemm_qkv_wgrad, 4, false, false, EPI_STORE)
+    TP_ROLE_W(GR_LOGITS, gemm_logits, 8, true, true, EPI_STORE)
+    TP_ROLE(GR_LOGITS_DGRAD, gemm_logits_dgrad, 8, true, false, EPI_STORE)
+    TP_ROLE(GR_LOGITS_WGRAD, gemm_logits_wgrad, 4, false, false, EPI_STORE)
+    default: return hipErrorInvalidValue;
+  }
+#undef TP_ROLE
+#undef TP_ROLE_W
+  if (g.a_kmajor != ak || g.b_kmajor != bk || g.epi != ep) return hipErrorInvalidValue;
+  // the wide tile when N is a whole number of them and they fill the CUs at
+  // least once (with fewer tiles the k-split tail is better balanced at 256)
+  const int ncu = device_cus();
+  const bool wide = mkw != nullptr && g.N % BN_MAX == 0 &&
+                    (long long)((g.M + BM - 1) / BM) * (g.N / BN_MAX) >= (ncu < GMAX ? ncu : GMAX);
+  const int bn = wide ? BN_MAX : 256;
+  if (bn == BN_MAX) { mk = mkw; fk = fkw; }
+  const int mi = bn == BN_MAX ? WC<8, BN_MAX>::MI : 4;  // fix-up workgroups per tile
   KParams p{};
   p.A = (const bf16*)g.A; p.B = (const bf16*)g.B;
   p.lda = g.lda; p.ldb = g.ldb;
   p.M = g.M; p.N = g.N; p.K = g.K;
   p.tiles_m = (g.M + BM - 1) / BM;
-  p.tiles_n = (g.N + BN - 1) / BN;
+  p.tiles_n = (g.N + bn - 1) / bn;
   p.iters = (g.K + BKK - 1) / BKK;
   p.epi = g.epi;
   p.C = (bf16*)g.C; p.ldc = g.ldc;
@@ -659,51 +800,22 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
   p.partials = (float*)ws;
   p.splits = 1;
   const int tiles = p.tiles_m * p.tiles_n;
-  Plan pl = make_plan(tiles, p.iters, device_cus());
+  Plan pl = make_plan(tiles, p.iters, ncu);
   if (pl.sk_total > 0 || pl.splits > 1) {
     const size_t slots = pl.splits > 1 ? (size_t)pl.splits * pl.sk_tiles : (size_t)2 * pl.sk_grid;
-    if (ws == nullptr || ws_bytes < slots * BM * BN * sizeof(float))
+    if (ws == nullptr || ws_bytes < slots * BM * bn * sizeof(float))
       pl = Plan{tiles, 1, 0, 0, 0, 0, 0, 1};  // data-parallel only
   }
   p.grid = pl.grid; p.dp_rounds = pl.dp_rounds; p.sk_grid = pl.sk_grid;
   p.sk_begin = pl.sk_begin; p.sk_total = pl.sk_total; p.splits = pl.splits;
   p.split_first = pl.sk_first_tile; p.split_tiles = pl.sk_tiles;
-  dim3 grid(pl.grid);
   const int first = pl.sk_first_tile, nsk = pl.sk_tiles;
   const bool sk = pl.sk_total > 0 || pl.splits > 1;
-  typedef void (*MainK)(KParams);
-  typedef void (*FixK)(KParams, int);
-  MainK mk = nullptr;
-  FixK fk = nullptr;
-  bool ak = true, bk = false;
-  int ep = EPI_STORE, nw = 4;
-#define TP_ROLE(R, NAME, NWV, AKV, BKV, EV) \
-  case R: mk = NAME; fk = NAME##_fixup; nw = NWV; ak = AKV; bk = BKV; ep = EV; break;
-  switch (g.role) {
-    TP_ROLE(GR_QKV_PROJ, gemm_qkv_proj, 8, true, false, EPI_BIAS_F32)
-    TP_ROLE(GR_OUT_PROJ, gemm_out_proj, 8, true, false, EPI_STORE)
-    TP_ROLE(GR_FC1, gemm_fc1_bias_gelu, 8, true, false, EPI_BIAS_GELU)
-    TP_ROLE(GR_FC2, gemm_fc2, 8, true, false, EPI_STORE)
-    TP_ROLE(GR_FC2_DGRAD, gemm_fc2_dgrad_gelu, 8, true, true, EPI_DGELU)
-    TP_ROLE(GR_FC1_DGRAD, gemm_fc1_dgrad, 8, true, true, EPI_STORE)
-    TP_ROLE(GR_OUT_DGRAD, gemm_out_dgrad, 8, true, true, EPI_STORE)
-    TP_ROLE(GR_QKV_DGRAD, gemm_qkv_dgrad, 8, true, true, EPI_STORE)
-    TP_ROLE(GR_FC2_WGRAD, gemm_fc2_wgrad, 4, false, false, EPI_STORE)
-    TP_ROLE(GR_FC1_WGRAD, gemm_fc1_wgrad, 4, false, false, EPI_STORE)
-    TP_ROLE(GR_OUT_WGRAD, gemm_out_wgrad, 4, false, false, EPI_STORE)
-    TP_ROLE(GR_QKV_WGRAD, gemm_qkv_wgrad, 4, false, false, EPI_STORE)
-    TP_ROLE(GR_LOGITS, gemm_logits, 8, true, true, EPI_STORE)
-    TP_ROLE(GR_LOGITS_DGRAD, gemm_logits_dgrad, 8, true, false, EPI_STORE)
-    TP_ROLE(GR_LOGITS_WGRAD, gemm_logits_wgrad, 4, false, false, EPI_STORE)
-    default: return hipErrorInvalidValue;
-  }
-#undef TP_ROLE
-  if (g.a_kmajor != ak || g.b_kmajor != bk || g.epi != ep) return hipErrorInvalidValue;
   const dim3 block(64 * nw);
-  hipLaunchKernelGGL(mk, grid, block, 0, stream, p);
+  hipLaunchKernelGGL(mk, dim3(pl.grid), block, 0, stream, p);
   hipError_t e1 = hipGetLastError();
   if (e1 != hipSuccess || !sk) return e1;
-  hipLaunchKernelGGL(fk, dim3(4 * nsk), block, 0, stream, p, first);
+  hipLaunchKernelGGL(fk, dim3(mi * nsk), block, 0, stream, p, first);
   return hipGetLastError();
 }
 
