@@ -44,8 +44,8 @@ constexpr int BM = 256, BKK = 64;
 // Wave layout of a workgroup of NW waves over a BM x BNV tile. 256 wide: 2
 // waves along m (128 rows each) x NW/2 along n (4 waves: one per SIMD, 128x128
 // each; 8 waves: two per SIMD, 128x64 each). 320 wide (8 waves, k-inner B
-// only): 4 waves along m x 2 along n, 64x160 each -- a fifth more flops per
-// byte staged than 256x256, and 2048 x 10240 / 20480 products fill 256 CUs in
+// only): 4 waves along m x 2 along n, 64x160 each -- 11% more flops per byte
+// staged than 256x256, and 2048 x 10240 / 20480 products fill 256 CUs in
 // whole rounds.
 template <int NW, int BNV>
 struct WC {
@@ -373,80 +373,111 @@ __device__ __forceinline__ void epilogue_rows(const KParams& p, int tm, int tn, 
   }
 }
 
-template <int NW, int BNV, int EPI>
-__device__ __forceinline__ void epilogue(const KParams& p, int tm, int tn,
-                                         const f32x16 (&acc)[WC<NW, BNV>::MI][WC<NW, BNV>::NJ]) {
-#pragma unroll
-  for (int i = 0; i < WC<NW, BNV>::MI; ++i) epilogue_rows<NW, BNV, EPI>(p, tm, tn, i, acc[i]);
-}
-
-// Whole-tile epilogue of a plain store through LDS (the stages are free once
-// the main loop has ended): each wave writes its bf16 results into a
-// [256 rows][256 cols] image -- rows 64q .. 64q+63 in stage array q, 16-byte
-// chunk c of row m at c ^ (m & 31), so that neither the row-per-lane writes
-// nor the row-major reads conflict on banks -- and the workgroup then stores
-// whole rows, 1 KiB (two rows) per instruction. Storing straight from the
-// accumulator layout writes 16 bytes into each of 32 rows per instruction;
-// with K short (the weight gradients) that epilogue is a visible share of the
-// tile. The LDS-only barriers leave the global stores in flight.
+// Whole-tile epilogue through LDS (the stages are free once the main loop has
+// ended). Storing straight from the accumulator layout writes 8 or 16 bytes
+// into each of 32 rows per instruction; instead each wave applies the
+// epilogue in registers and writes its results into a row-major image of the
+// tile in LDS, and the workgroup then stores whole rows, NTHR*16 bytes per
+// instruction. Image rows of RB bytes hold NCH 16-byte chunks, chunk c of
+// image row r at (c + r) mod NCH, so the row-per-lane writes spread over the
+// banks and the row-major reads do not conflict. An image larger than the
+// stage memory (fp32 out, or 320 columns) goes in passes of PR rows; GeLU's
+// two outputs go one after the other. The LDS-only barriers leave the global
+// stores in flight.
 __device__ __forceinline__ void lds_only_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int NW, int BNV>
-__device__ __forceinline__ void epilogue_store_lds(const KParams& p, int tm, int tn,
-                                                   const f32x16 (&acc)[WC<NW, BNV>::MI][WC<NW, BNV>::NJ],
-                                                   bf16* q0, bf16* q1, bf16* q2, bf16* q3) {
+template <int NW, int BNV, int EPI>
+__device__ __forceinline__ void epilogue_staged(const KParams& p, int tm, int tn,
+                                                const f32x16 (&acc)[WC<NW, BNV>::MI][WC<NW, BNV>::NJ],
+                                                bf16* smem) {
   using C = WC<NW, BNV>;
-  static_assert(BNV == 256 && BM == 256 && BKK == 64 && C::WMW == 128, "one 64-row quarter per stage array");
-  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-  typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
-  // an opaque copy of the thread id keeps the ~60 per-lane addresses below
-  // from being hoisted out of the tile loop (they would be held, or spilled,
+  constexpr int ES = EPI == EPI_BIAS_F32 ? 4 : 2;  // bytes per output element
+  constexpr int RB = BNV * ES, NCH = RB / 16;
+  constexpr int LDS_BYTES = 2 * (BM + BNV) * BKK * 2;
+  constexpr int PR = 256 * RB <= LDS_BYTES ? 256 : 128 * RB <= LDS_BYTES ? 128 : 64;
+  constexpr int NPASS = BM / PR, NIMG = EPI == EPI_BIAS_GELU ? 2 : 1;
+  constexpr int ITERS = PR * NCH / C::NTHR;
+  static_assert(PR * NCH % C::NTHR == 0 && NCH >= 32 && PR % 32 == 0, "image layout");
+  typedef __attribute__((address_space(3))) char lds_char;
+  lds_char* img = (lds_char*)smem;
+  // an opaque copy of the thread id keeps the per-lane addresses below from
+  // being hoisted out of the tile loop (they would be held, or spilled,
   // across the main loop)
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   const int lane = tid & 63, wave = (int)uni((uint32_t)(tid >> 6));
   const int wm = wave / C::WNG, wn = wave % C::WNG;
-  const int l32 = lane & 31;
+  const int l32 = lane & 31, hh = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i) {
-    // rows wm*128 + 32i + l32: quarter 2wm + i/2, row (32i + l32) & 63 in it
-    bf16* qa = (i < 2) ? q0 : q1;
-    bf16* qb = (i < 2) ? q2 : q3;
-    bf16* row = (wm ? qb : qa) + ((32 * i + l32) & 63) * 256;
-    const int sw = (32 * i + l32) & 31;  // = m & 31
+  for (int im = 0; im < NIMG; ++im) {
 #pragma unroll
-    for (int j = 0; j < C::NJ; ++j)
+    for (int ps = 0; ps < NPASS; ++ps) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int c = (wn * C::WNW + j * 32 + q4 * 8) >> 3;
-        bf16x4 o;
+      for (int i = 0; i < C::MI; ++i) {
+        const int r0 = wm * C::WMW + 32 * i - ps * PR;  // wave-uniform
+        if (NPASS > 1 && (r0 < 0 || r0 >= PR)) continue;
+        const unsigned rl = (unsigned)(r0 + l32);
+        const int m = tm * BM + ps * PR + (int)rl;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (bf16)acc[i][j][4 * q4 + e];
-        *(lds_bf16x4*)(row + ((c ^ sw) << 3) + (lane >> 5) * 4) = o;
+        for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int nt = wn * C::WNW + j * 32 + q4 * 8 + 4 * hh, n = tn * BNV + nt;
+            float v[4] = {acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]};
+            if (n < p.N) {
+              if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_F32) {
+                const bf16x4 bb = *(const bf16x4*)(p.bias + n);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] += (float)bb[e];
+              }
+              if (EPI == EPI_DGELU && m < p.M) {
+                const bf16x4 pa = *(const bf16x4*)(p.aux + (long)m * p.ldaux + n);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f((float)pa[e]);
+              }
+            }
+            if (EPI == EPI_BIAS_GELU && im == 1) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = gelu_f(v[e]);
+            }
+            const unsigned c = (unsigned)(nt * ES / 16), pc = (c + rl) % NCH;
+            lds_char* dst = img + rl * RB + pc * 16 + (nt * ES) % 16;
+            if constexpr (ES == 4) {
+              *(__attribute__((address_space(3))) f32x4*)dst = f32x4{v[0], v[1], v[2], v[3]};
+            } else {
+              bf16x4 o;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
+              *(__attribute__((address_space(3))) bf16x4*)dst = o;
+            }
+          }
       }
-  }
-  lds_only_barrier();
-  constexpr int ITERS = BM * 32 / C::NTHR;  // 16-byte chunks per thread
-  constexpr int PER_Q = ITERS / 4;          // iterations per 64-row quarter
+      lds_only_barrier();
+      char* out = im == 0 ? (char*)p.C : (char*)p.C2;
+      const long ld = im == 0 ? p.ldc : p.ldc2;
 #pragma unroll
-  for (int it = 0; it < ITERS; ++it) {
-    bf16* q = it < PER_Q ? q0 : it < 2 * PER_Q ? q1 : it < 3 * PER_Q ? q2 : q3;
-    const int lin = it * C::NTHR + tid, m = lin >> 5, c = lin & 31;
-    const bf16x8 v = *(lds_bf16x8*)(q + (m & 63) * 256 + ((c ^ (m & 31)) << 3));
-    const int gm = tm * BM + m, gn = tn * BNV + 8 * c;
-    if (gm < p.M && gn < p.N) *(bf16x8*)(p.C + (long)gm * p.ldc + gn) = v;
+      for (int it = 0; it < ITERS; ++it) {
+        const unsigned lin = (unsigned)(it * C::NTHR + tid), rl = lin / NCH, c = lin - rl * NCH;
+        const u32x4 v = *(__attribute__((address_space(3))) const u32x4*)(img + rl * RB + ((c + rl) % NCH) * 16);
+        const int gm = tm * BM + ps * PR + (int)rl, gn = tn * BNV + (int)c * (16 / ES);
+        if (gm < p.M && gn < p.N) *(u32x4*)(out + ((long)gm * ld + gn) * ES) = v;
+      }
+      lds_only_barrier();  // the image (or the next tile's loads) overwrites this pass
+    }
   }
-  lds_only_barrier();  // the next tile's loads overwrite the stages
 }
 
-// Whole-tile epilogue: the LDS-staged store for plain stores of 4-wave tiles,
-// else straight from the accumulators.
+// Whole-tile epilogue: through LDS, except the fp32 output (its direct stores
+// already write 16 bytes per lane, and its image would take two passes).
 template <int NW, int BNV, int EPI>
 __device__ __forceinline__ void epilogue_tile(const KParams& p, int tm, int tn,
-                                              const f32x16 (&acc)[WC<NW, BNV>::MI][WC<NW, BNV>::NJ], bf16* sA0,
-                                              bf16* sA1, bf16* sB0, bf16* sB1) {
-  if constexpr (NW == 4 && EPI == EPI_STORE) epilogue_store_lds<NW, BNV>(p, tm, tn, acc, sA0, sA1, sB0, sB1);
-  else epilogue<NW, BNV, EPI>(p, tm, tn, acc);
+                                              const f32x16 (&acc)[WC<NW, BNV>::MI][WC<NW, BNV>::NJ], bf16* smem) {
+  if constexpr (EPI == EPI_BIAS_F32) {
+#pragma unroll
+    for (int i = 0; i < WC<NW, BNV>::MI; ++i) epilogue_rows<NW, BNV, EPI>(p, tm, tn, i, acc[i]);
+  } else {
+    epilogue_staged<NW, BNV, EPI>(p, tm, tn, acc, smem);
+  }
 }
 
 // ---- stream-K bookkeeping -----------------------------------------------------
@@ -483,8 +514,13 @@ __device__ __forceinline__ void store_partial(float* slot, const f32x16 (&acc)[W
 // then its run of stream-K iterations (whole tiles in the run are stored
 // directly, partial tiles go to the workspace).
 template <int NW, int BNV, bool AK, bool BKM, int EPI>
-__device__ __forceinline__ void gemm_body(const KParams& p, bf16* sA0, bf16* sA1, bf16* sB0, bf16* sB1) {
+__device__ __forceinline__ void gemm_body(const KParams& p, bf16* smem) {
   constexpr int MI = WC<NW, BNV>::MI, NJ = WC<NW, BNV>::NJ;
+  // two stages of each operand, contiguous (the epilogue reuses all of it)
+  bf16* sA0 = smem;
+  bf16* sA1 = smem + BM * BKK;
+  bf16* sB0 = smem + 2 * BM * BKK;
+  bf16* sB1 = sB0 + BNV * BKK;
   const int lw = logical_wg(blockIdx.x, p.grid);
   if (p.splits > 1) {
     // data-parallel rounds, then the split tail: consecutive workgroups (one
@@ -500,7 +536,7 @@ __device__ __forceinline__ void gemm_body(const KParams& p, bf16* sA0, bf16* sA1
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
       mainloop<NW, BNV, AK, BKM>(p, tm, tn, 0, p.iters, acc, sA0, sA1, sB0, sB1);
-      epilogue_tile<NW, BNV, EPI>(p, tm, tn, acc, sA0, sA1, sB0, sB1);
+      epilogue_tile<NW, BNV, EPI>(p, tm, tn, acc, smem);
     }
     if (lw >= p.splits * p.split_tiles) return;
     const int t = p.split_first + lw % p.split_tiles, sidx = lw / p.split_tiles;
@@ -552,7 +588,7 @@ __device__ __forceinline__ void gemm_body(const KParams& p, bf16* sA0, bf16* sA1
       for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
     mainloop<NW, BNV, AK, BKM>(p, tm, tn, kb, ke, acc, sA0, sA1, sB0, sB1);
     if (kb == 0 && ke == p.iters) {
-      epilogue_tile<NW, BNV, EPI>(p, tm, tn, acc, sA0, sA1, sB0, sB1);
+      epilogue_tile<NW, BNV, EPI>(p, tm, tn, acc, smem);
     } else {
       const long long t0 = (long long)t * p.iters - p.sk_begin;  // tile start, SK-relative
       const int slot = 2 * lw + (s >= t0 ? 0 : 1);
@@ -626,11 +662,8 @@ __device__ __forceinline__ void fixup_body(const KParams& p, int first_tile) {
 #define TP_GEMM_KERNELS(NAME, NWV, BNV, AKV, BKV, EV)                                      \
   __global__ __launch_bounds__(64 * NWV)                                                   \
   __attribute__((amdgpu_waves_per_eu(NWV / 4, NWV / 4))) void NAME(KParams p) {            \
-    __shared__ __attribute__((aligned(16))) bf16 sA0[BM * BKK];                            \
-    __shared__ __attribute__((aligned(16))) bf16 sA1[BM * BKK];                            \
-    __shared__ __attribute__((aligned(16))) bf16 sB0[BNV * BKK];                           \
-    __shared__ __attribute__((aligned(16))) bf16 sB1[BNV * BKK];                           \
-    gemm_body<NWV, BNV, AKV, BKV, EV>(p, sA0, sA1, sB0, sB1);                              \
+    __shared__ __attribute__((aligned(16))) bf16 smem[2 * (BM + BNV) * BKK];               \
+    gemm_body<NWV, BNV, AKV, BKV, EV>(p, smem);                                            \
   }                                                                                        \
   __global__ __launch_bounds__(64 * NWV) void NAME##_fixup(KParams p, int first_tile) {    \
     fixup_body<NWV, BNV, EV>(p, first_tile);                                               \

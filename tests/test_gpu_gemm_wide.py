@@ -1,0 +1,84 @@
+"""GPU parity of the 256x320-tile products against the fp64 oracle. The library
+takes that tile for products with a k-inner B (the input gradients) when N is
+a multiple of 320 and the tiles fill the CUs at least once, which the small
+parity shapes never reach; these MLP shapes do, with a ragged token count (a
+partial last row of tiles) and a stream-K tail:
+  * h = 3200, f = 9600: the GEMM2 input gradient (+ GeLU' epilogue) runs 320
+    wide (N = f);
+  * h = 9600, f = 3200: the GEMM1 input gradient runs 320 wide (N = h).
+The oracle recomputes column sub-shards and sampled token rows exactly."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity_util import compare, f64, shape_of
+
+pytestmark = pytest.mark.gpu
+
+tp = pytest.importorskip("tensor_transformer_layer_tp_amd")
+
+MLP_IN = ("X_mlp", "A", "b1", "B", "dZ")
+ATTN_IN = ("X_attn", "Wqkv", "bqkv", "Wo", "dO")
+TOKENS = 2100  # 9 row tiles of 256, the last one 52 rows
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tp.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def workload(h, ffn):
+    return synth.Workload(f"wide_h{h}_f{ffn}", batch=1, seq=TOKENS, hidden=h, n_heads=h // 160, head_dim=160,
+                          ffn=ffn, tp_size=1, dtype="bf16", bias_std=0.5)
+
+
+def samples(n, k, rng):
+    return np.unique(np.concatenate([[0, 1, n // 2, n - 1], rng.choice(n, k, replace=False)]))
+
+
+@pytest.mark.parametrize("h,ffn", [(3200, 9600), (9600, 3200)], ids=["fc2_dgrad_wide", "fc1_dgrad_wide"])
+def test_mlp_wide_tiles_ragged_tokens(h, ffn):
+    w = workload(h, ffn)
+    print(f"\n  [wide MLP] T={TOKENS} h={h} f={ffn}", flush=True)
+    inp = synth.draw_shard(w, seed=21, skip=ATTN_IN)
+    s = shape_of(w, 0)
+    T, bf, nan = w.tokens, torch.bfloat16, float("nan")
+    d = {k: inp[k].cuda().contiguous() for k in MLP_IN}
+    o = {"pre": torch.full((T, ffn), nan, dtype=bf, device="cuda"),
+         "y": torch.full((T, ffn), nan, dtype=bf, device="cuda"),
+         "Z": torch.full((T, h), nan, dtype=bf, device="cuda"),
+         "dX": torch.full((T, h), nan, dtype=bf, device="cuda"),
+         "dA": torch.full((h, ffn), nan, dtype=bf, device="cuda"),
+         "db1": torch.full((ffn,), nan, dtype=bf, device="cuda"),
+         "dB": torch.full((ffn, h), nan, dtype=bf, device="cuda"),
+         "db2": torch.full((h,), nan, dtype=bf, device="cuda")}
+    ws = torch.empty(max(tp.tp_mlp_workspace_bytes(s), 1), dtype=torch.uint8, device="cuda")
+    tp.tp_mlp_fwd(s, d["X_mlp"], d["A"], d["b1"], d["B"], o["pre"], o["y"], o["Z"], workspace=ws)
+    tp.tp_mlp_bwd(s, d["X_mlp"], d["A"], d["B"], o["pre"], o["y"], d["dZ"], o["dX"], o["dA"], o["db1"], o["dB"],
+                  o["db2"], workspace=ws)
+    torch.cuda.synchronize()
+    a = {k: f64(inp[k]) for k in MLP_IN}
+    rng = np.random.default_rng(3)
+    # a column sub-shard C of the FFN columns is itself a valid shard
+    C = samples(ffn, 60, rng)
+    pre_C, y_C, _ = oracle.mlp_fwd(a["X_mlp"], a["A"][:, C], a["b1"][C], a["B"][C, :])
+    compare("pre[:,C]", o["pre"][:, C], pre_C, "bf16")
+    compare("y[:,C]", o["y"][:, C], y_C, "bf16")
+    _, dA_C, db1_C, dB_C, db2 = oracle.mlp_bwd(a["X_mlp"], a["A"][:, C], a["B"][C, :], pre_C, y_C, a["dZ"])
+    compare("dA[:,C]", o["dA"][:, C], dA_C, "bf16")
+    compare("db1[C]", o["db1"][C], db1_C, "bf16")
+    compare("dB[C,:]", o["dB"][C, :], dB_C, "bf16")
+    compare("db2", o["db2"], db2, "bf16")
+    # token rows R, including the ragged last row tile
+    R = np.unique(np.concatenate([samples(T, 12, rng), np.arange(T - 8, T)]))
+    pre_R, y_R, Z_R = oracle.mlp_fwd(a["X_mlp"][R], a["A"], a["b1"], a["B"])
+    compare("pre[R]", o["pre"][R], pre_R, "bf16")
+    compare("Z[R]", o["Z"][R], Z_R, "bf16")
+    dX_R = oracle.mlp_bwd(a["X_mlp"][R], a["A"], a["B"], pre_R, y_R, a["dZ"][R])[0]
+    compare("dX_mlp[R]", o["dX"][R], dX_R, "bf16")
