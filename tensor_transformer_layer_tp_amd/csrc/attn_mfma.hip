@@ -491,14 +491,13 @@ __device__ __forceinline__ void dkdv_tile(const MP& p, const char* __restrict__ 
   }
 }
 
+// dK and dV of the 128 keys of tile kvt of one head (4 waves of 32 keys),
+// looping over the 64-query tiles from the diagonal on.
 template <int D, bool AL, bool DO>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dkdv_mfma(MP p) {
-  constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2, SB = 3 * TB + 512;
-  __shared__ __attribute__((aligned(16))) char st0[SB];
-  __shared__ __attribute__((aligned(16))) char st1[SB];
-  const int head = blockIdx.x;
+__device__ __forceinline__ void dkdv_item(const MP& p, int head, int kvt, char* __restrict__ st0,
+                                          char* __restrict__ st1) {
+  constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
   const int b = head / p.n_local, l = head - b * p.n_local;
-  const int kvt = blockIdx.y;  // 128-key tile; tile 0 sees the most queries
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = (int)uni((uint32_t)(tid >> 6));
   const long grow0 = (long)b * p.seq;
@@ -630,15 +629,13 @@ __device__ __forceinline__ void dq_tile(const MP& p, const char* __restrict__ cu
   }
 }
 
+// dQ of the 128 queries of tile qt of one head (4 waves of 32 queries),
+// looping over the 64-key tiles up to the diagonal.
 template <int D, bool AL, bool DO>
-__global__ __launch_bounds__(256) void dq_mfma(MP p) {
+__device__ __forceinline__ void dq_item(const MP& p, int head, int qt, char* __restrict__ st0,
+                                        char* __restrict__ st1) {
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
-  __shared__ __attribute__((aligned(16))) char st0[3 * TB];
-  __shared__ __attribute__((aligned(16))) char st1[3 * TB];
-  const int head = blockIdx.x;
   const int b = head / p.n_local, l = head - b * p.n_local;
-  const int nqt = (p.seq + 127) / 128;
-  const int qt = nqt - 1 - blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = (int)uni((uint32_t)(tid >> 6));
   const long grow0 = (long)b * p.seq;
@@ -688,6 +685,25 @@ __global__ __launch_bounds__(256) void dq_mfma(MP p) {
         *(bf16x4*)(dQ + 32 * db + 8 * q4 + 4 * g) = a;
       }
   }
+}
+
+// The backward's two kinds of work item in one launch. The dK/dV item of key
+// tile r and the dQ item of query tile nt-1-r both cover nt-r query/key tile
+// pairs (the causal triangle makes tile costs range from 1 to nt); items are
+// numbered heaviest first -- rank r's dK/dV items, then its dQ items, for
+// every head -- so workgroups freed by light items pick up the remaining
+// ones instead of waiting, as two separate launches would, for each launch's
+// heaviest tile.
+template <int D, bool AL, bool DO>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_mfma(MP p) {
+  constexpr int SB = 3 * TROWS * D * 2 + 512;  // three tiles + lse and delta of 64 queries
+  __shared__ __attribute__((aligned(16))) char st0[SB];
+  __shared__ __attribute__((aligned(16))) char st1[SB];
+  const int nh = p.batch * p.n_local, nt = (p.seq + 127) / 128;
+  const int head = (int)(blockIdx.x % (unsigned)nh), rk = (int)(blockIdx.x / (unsigned)nh);
+  const int r = rk >> 1;
+  if (rk & 1) dq_item<D, AL, DO>(p, head, nt - 1 - r, st0, st1);
+  else dkdv_item<D, AL, DO>(p, head, r, st0, st1);
 }
 
 // ---- q/k/v split ------------------------------------------------------------------
@@ -757,13 +773,9 @@ hipError_t fwd_d(const MP& p, hipStream_t stream) {
 }
 template <int D, bool DO>
 hipError_t bwd_d(const MP& p, hipStream_t stream) {
-  dim3 grid(p.batch * p.n_local, (p.seq + 127) / 128);
-  if (p.alibi) hipLaunchKernelGGL((dkdv_mfma<D, true, DO>), grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((dkdv_mfma<D, false, DO>), grid, dim3(256), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (p.alibi) hipLaunchKernelGGL((dq_mfma<D, true, DO>), grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((dq_mfma<D, false, DO>), grid, dim3(256), 0, stream, p);
+  const dim3 grid((unsigned)(2 * ((p.seq + 127) / 128) * p.batch * p.n_local));
+  if (p.alibi) hipLaunchKernelGGL((bwd_mfma<D, true, DO>), grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((bwd_mfma<D, false, DO>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
