@@ -85,11 +85,17 @@ def stored_traffic(kernel: str, workload: str):
     return float(m_b.group(1))
 
 
-def cpu_baseline(w, inp, target_s: float) -> dict:
+PARITY_OUTS = ("qkv", "ctx", "lse", "O", "pre", "y", "Z", "dX_mlp", "dA", "db1", "dB", "db2", "dX_attn", "dWqkv",
+               "dbqkv", "dWo", "dbo")
+
+
+def cpu_baseline(w, inp, target_s: float, gpu_out=None) -> dict:
     """The fp64 oracle, as it stands, on a bounded sample of the same workload:
     a sub-shard of this rank (its first n_sub heads and first f_sub FFN
     columns; a column block of a column-parallel shard is itself a shard), on
-    the same tokens. Rate = algorithmic flops of the sample / wall time."""
+    the same tokens. Rate = algorithmic flops of the sample / wall time. When
+    the sample is the whole shard and the GPU step's outputs are given (host
+    copies, same inputs), also the relative Frobenius error of every output."""
     import numpy as np
     import oracle
     try:
@@ -111,11 +117,18 @@ def cpu_baseline(w, inp, target_s: float) -> dict:
         kw = dict(batch=w.batch, seq=w.seq, n_heads=w.n_heads, tp_size=w.n_heads // n_sub, tp_rank=0,
                   alibi=w.alibi)
         t0 = time.perf_counter()
-        oracle.attn_fwd(X_attn, Wqkv, bqkv, Wo, **kw)
-        oracle.attn_bwd(X_attn, Wqkv, bqkv, Wo, dO, **kw)
-        pre, y, _ = oracle.mlp_fwd(X_mlp, A, b1, B)
-        oracle.mlp_bwd(X_mlp, A, B, pre, y, dZ)
-        return time.perf_counter() - t0
+        qkv, ctx, lse, O = oracle.attn_fwd(X_attn, Wqkv, bqkv, Wo, **kw)
+        dXa, dWqkv, dbqkv, dWo, dbo = oracle.attn_bwd(X_attn, Wqkv, bqkv, Wo, dO, **kw)
+        pre, y, Z = oracle.mlp_fwd(X_mlp, A, b1, B)
+        dXm, dA, db1, dB, db2 = oracle.mlp_bwd(X_mlp, A, B, pre, y, dZ)
+        t = time.perf_counter() - t0
+        outs.clear()
+        if n_sub == n_l and f_sub == f_l:
+            outs.update(qkv=qkv, ctx=ctx, lse=lse, O=O, pre=pre, y=y, Z=Z, dX_mlp=dXm, dA=dA, db1=db1, dB=dB,
+                        db2=db2, dX_attn=dXa, dWqkv=dWqkv, dbqkv=dbqkv, dWo=dWo, dbo=dbo)
+        return t
+
+    outs = {}
 
     k = n_l  # start at 1/n_l of the shard (one head, f_l/n_l FFN columns)
     while True:
@@ -129,10 +142,22 @@ def cpu_baseline(w, inp, target_s: float) -> dict:
         while n_l % k:
             k -= 1
     fl = layer_flops(w, n_l=n_sub, f_l=f_sub)
-    return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"fp64 NumPy oracle, fwd+bwd of a sub-shard of rank 0: {n_sub} of {n_l} heads and "
-                      f"{f_sub} of {f_l} FFN columns on all {w.tokens} tokens ({fl:.3e} algorithmic flops "
-                      f"in {t:.2f} s)"}
+    res = {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"fp64 NumPy oracle, fwd+bwd of a sub-shard of rank 0: {n_sub} of {n_l} heads and "
+                     f"{f_sub} of {f_l} FFN columns on all {w.tokens} tokens ({fl:.3e} algorithmic flops "
+                     f"in {t:.2f} s)"}
+    if gpu_out is not None and outs:
+        err = {}
+        for k in PARITY_OUTS:
+            if k in gpu_out and k in outs:
+                g, r = f64(gpu_out[k]).reshape(outs[k].shape), outs[k]
+                nr = float(np.linalg.norm(r))
+                err[k] = float(np.linalg.norm(g - r)) / (nr if nr > 0 else 1.0)
+        worst = max(err, key=err.get)
+        log(f"parity of the timed step's outputs vs the oracle: worst {worst} rel_fro {err[worst]:.3e}")
+        res["parity"] = {"rel_fro": {k: float(f"{v:.3e}") for k, v in err.items()}, "bar": 1e-2,
+                         "pass": all(v <= 1e-2 for v in err.values())}
+    return res
 
 
 def ln_residual_measure(w, reps: int = 20) -> dict:
@@ -402,15 +427,22 @@ def main():
     tp.tp_profile_enable(1 << tp.STEPS[dom])
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps - 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     e0.record(stream)
-    for _ in range(a.steps):
+    for k in range(a.steps):
         ls.step()
-    e1.record(stream)
+        (ev[k] if k < a.steps - 1 else e1).record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = e0.elapsed_time(e1) / a.steps
+    marks = [e0, *ev, e1]
+    per_step = sorted(marks[k].elapsed_time(marks[k + 1]) for k in range(a.steps))
+    step_stats = {"median": round(per_step[len(per_step) // 2], 4), "min": round(per_step[0], 4),
+                  "p90": round(per_step[min(len(per_step) - 1, int(math.ceil(0.9 * len(per_step))) - 1)], 4)}
+    # host copies of the timed step's outputs (later measurements reuse the buffers)
+    gpu_out = None if a.no_cpu_baseline else {k: v.cpu() for k, v in ls.out.items()}
     n_dom, ms_dom = tp.tp_profile_collect(tp.STEPS[dom])
     tp.tp_profile_enable(0)
     avg_dom_ms = ms_dom / max(n_dom, 1)
@@ -443,12 +475,14 @@ def main():
     cpu = None
     if not a.no_cpu_baseline:
         log("cpu baseline (fp64 oracle on a bounded sample)")
-        cpu = cpu_baseline(w, inp, a.cpu_target_s)
+        cpu = cpu_baseline(w, inp, a.cpu_target_s, gpu_out)
+        gpu_out = None
 
     out = {
         "metric": "layer-shard fwd+bwd TFLOP/s (bf16) on 1 MI355X; % of MFMA peak",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
-        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "ms_per_step": round(ms_step, 4), "step_ms": step_stats, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded N(0,1) activations and gradients, N(0,0.02) weights)",
         "pct_of_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq, "hidden": w.hidden,
@@ -456,6 +490,7 @@ def main():
                    "ffn_shard": f"{w.ffn_local} of {w.ffn}", "tp_rank": 0, "tp_size": w.tp_size,
                    "alibi": w.alibi, "flops_per_step": F},
         "breakdown_ms": {k: round(v, 4) for k, v in breakdown.items()},
+        "breakdown_tflops": {k: round(sf[k] / (v / 1e3) / 1e12, 1) for k, v in breakdown.items() if sf[k] > 0},
         "roofline": roof,
         "cpu_baseline": cpu,
         "ln_residual": ln,
