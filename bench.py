@@ -366,8 +366,8 @@ def main():
                     help="only run device-to-device copies of this many MiB (calibrates byte counters)")
     a = ap.parse_args()
     if a.gpus != 1:
-        print(f"bench.py measures one GPU only (--gpus {a.gpus} requested): this build runs one tensor-parallel "
-              "rank's shard on one device; multi-GPU runs are not part of it.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (--gpus {a.gpus} requested): it runs one tensor-parallel "
+              "rank's shard on one device; runs on several GPUs are not supported.", file=sys.stderr)
         sys.exit(2)
 
     import torch
