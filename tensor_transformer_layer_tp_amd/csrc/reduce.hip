@@ -79,12 +79,21 @@ __global__ __launch_bounds__(256) void colsum_part_vec_kernel(const T* X, int M,
   }
 }
 
+// The R partial rows added in order r = 0, 1, ..; eight rows' loads in
+// flight at a time (rows past R load row R - 1 again, unused).
 template <typename T>
 __global__ __launch_bounds__(CB) void colsum_final_kernel(const float* part, int R, int N, T* out) {
   const int n = blockIdx.x * CB + threadIdx.x;
   if (n >= N) return;
   float s = 0.f;
-  for (int r = 0; r < R; ++r) s += part[(long)r * N + n];
+  for (int r = 0; r < R; r += 8) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = part[(long)min(r + u, R - 1) * N + n];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (r + u < R) s += x[u];
+  }
   out[n] = from_f<T>(s);
 }
 
