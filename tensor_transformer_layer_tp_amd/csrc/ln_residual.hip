@@ -198,21 +198,28 @@ __global__ __launch_bounds__(BWD_T) void ln_residual_bwd_kernel(const T* __restr
   const int nc = h >> 3;
   const long r0 = (long)blockIdx.x * rows_per;
   const long r1 = r0 + rows_per < rows ? r0 + rows_per : rows;
-  int cl[NV];
+  uint32_t cl[NV];  // byte offset of this thread's chunk i in a row
   bool ok[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = threadIdx.x + i * BWD_T;
     ok[i] = c < nc;
-    cl[i] = 8 * (ok[i] ? c : nc - 1);
+    cl[i] = (uint32_t)(8 * (ok[i] ? c : nc - 1) * sizeof(T));
   }
+  const uint32_t hb = (uint32_t)(h * sizeof(T));  // bytes per row
   V8<T> gm[NV], dyv[NV], rv[NV];
   float ag[NV][8], ab[NV][8];
+  {
+    const auto rg = row_rsrc(gamma, hb), rd = row_rsrc(dy + r0 * h, hb), rr = row_rsrc(r + r0 * h, hb);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      load8_buf(gm[i], rg, cl[i]);
+      load8_buf(dyv[i], rd, cl[i]);
+      load8_buf(rv[i], rr, cl[i]);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    gm[i].load(gamma + cl[i]);
-    dyv[i].load(dy + r0 * h + cl[i]);
-    rv[i].load(r + r0 * h + cl[i]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) ag[i][e] = ab[i][e] = 0.f;
   }
@@ -234,22 +241,30 @@ __global__ __launch_bounds__(BWD_T) void ln_residual_bwd_kernel(const T* __restr
     // residual gradient, in flight across the reduction
     const long nb = (t + 1 < r1 ? t + 1 : t) * h;
     V8<T> dyn[NV], rn[NV], din[NV];
+    {
+      const auto rd = row_rsrc(dy + nb, hb), rr = row_rsrc(r + nb, hb);
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      dyn[i].load(dy + nb + cl[i]);
-      rn[i].load(r + nb + cl[i]);
+      for (int i = 0; i < NV; ++i) {
+        load8_buf(dyn[i], rd, cl[i]);
+        load8_buf(rn[i], rr, cl[i]);
+      }
     }
     if (dr_in) {
+      const auto ri = row_rsrc(dr_in + base, hb);
 #pragma unroll
-      for (int i = 0; i < NV; ++i) din[i].load(dr_in + base + cl[i]);
+      for (int i = 0; i < NV; ++i) load8_buf(din[i], ri, cl[i]);
     }
     uint32_t mb[NV];
     if (DO) {
+      const auto rm = row_rsrc(mask + t * (h >> 3), (uint32_t)(h >> 3));
 #pragma unroll
-      for (int i = 0; i < NV; ++i) mb[i] = mask[t * (h >> 3) + (cl[i] >> 3)];
+      for (int i = 0; i < NV; ++i)
+        mb[i] = __builtin_amdgcn_raw_buffer_load_b8(rm, (int)(cl[i] / (8 * (uint32_t)sizeof(T))), 0, 0);
     }
     block_sum<BWD_T, 2>(s, red);
     const float a = s[0] / (float)h, b = s[1] / (float)h;
+    const auto ro = row_rsrc(dr + base, hb);
+    const auto rob = row_rsrc(DO ? d_block + base : dr + base, hb);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       gm[i].opaque();
@@ -264,11 +279,11 @@ __global__ __launch_bounds__(BWD_T) void ln_residual_bwd_kernel(const T* __restr
           ag[i][e] += dyv[i][e] * xh;
           ab[i][e] += dyv[i][e];
         }
-        store8(dr + base + cl[i], o);
+        store8_buf(T{}, ro, cl[i], o);
         if (DO) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) o[e] = ((mb[i] >> e) & 1u) ? o[e] * dscale : 0.f;
-          store8(d_block + base + cl[i], o);
+          store8_buf(T{}, rob, cl[i], o);
         }
       }
       dyv[i] = dyn[i];
@@ -278,7 +293,7 @@ __global__ __launch_bounds__(BWD_T) void ln_residual_bwd_kernel(const T* __restr
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     if (!ok[i]) continue;
-    float* p = part + (long)2 * blockIdx.x * h + cl[i];
+    float* p = part + (long)2 * blockIdx.x * h + cl[i] / sizeof(T);
     store8(p, ag[i]);
     store8(p + h, ab[i]);
   }

@@ -25,6 +25,33 @@ template <> struct V8<float> {
   __device__ __forceinline__ void opaque() {}
 };
 
+// Buffer access to one row: a resource based at the row (workgroup-uniform,
+// in scalar registers; `bytes` bounds it) and a per-lane byte offset, so one
+// offset register per column chunk serves every row and array instead of a
+// 64-bit address per chunk, row and array.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* row, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), (short)0, (int)bytes, 0x00020000);
+}
+template <typename T> __device__ __forceinline__ void load8_buf(V8<T>& v, __amdgpu_buffer_rsrc_t rs, uint32_t off);
+template <> __device__ __forceinline__ void load8_buf<bf16>(V8<bf16>& v, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  v.v = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+}
+template <> __device__ __forceinline__ void load8_buf<float>(V8<float>& v, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  v.a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+  v.b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off + 16, 0, 0));
+}
+__device__ __forceinline__ void store8_buf(bf16, __amdgpu_buffer_rsrc_t rs, uint32_t off, const float (&x)[8]) {
+  bf16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (bf16)x[e];
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, (int)off, 0, 0);
+}
+__device__ __forceinline__ void store8_buf(float, __amdgpu_buffer_rsrc_t rs, uint32_t off, const float (&x)[8]) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{x[0], x[1], x[2], x[3]}), rs, (int)off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{x[4], x[5], x[6], x[7]}), rs, (int)off + 16,
+                                         0, 0);
+}
+
 template <typename T> __device__ __forceinline__ void load8(const T* p, float (&x)[8]) {
   V8<T> v;
   v.load(p);
