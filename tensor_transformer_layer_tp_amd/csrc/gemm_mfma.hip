@@ -286,10 +286,15 @@ __device__ __forceinline__ void kstep(const KParams& p, const Panel<WC<NW, BNV>:
     }
 }
 
+// Stage s (0, 1) of the two: A at smem + s*BM*BKK, B after both A stages.
+template <int BNV>
+__device__ __forceinline__ bf16* stage_a(bf16* smem, int s) { return smem + s * BM * BKK; }
+template <int BNV>
+__device__ __forceinline__ bf16* stage_b(bf16* smem, int s) { return smem + 2 * BM * BKK + s * BNV * BKK; }
+
 template <int NW, int BNV, bool AK, bool BKM>
 __device__ __forceinline__ void mainloop(const KParams& p, int tm, int tn, int kb, int ke,
-                                         f32x16 (&acc)[WC<NW, BNV>::MI][WC<NW, BNV>::NJ], bf16* sA0, bf16* sA1,
-                                         bf16* sB0, bf16* sB1) {
+                                         f32x16 (&acc)[WC<NW, BNV>::MI][WC<NW, BNV>::NJ], bf16* smem) {
   using C = WC<NW, BNV>;
   constexpr int MI = C::MI, NJ = C::NJ, WNG = C::WNG, WMW = C::WMW, WNW = C::WNW;
   static_assert(BKM || BNV == 256, "k-outer B panels are 256 columns wide");
@@ -311,12 +316,16 @@ __device__ __forceinline__ void mainloop(const KParams& p, int tm, int tn, int k
   for (int i = 0; i < MI; ++i) offA[i] = AK ? 0 : kout_lane_off(wm * WMW, i, lane);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) offB[j] = BKM ? 0 : kout_lane_off(wn * WNW, j, lane);
-  issue_panel<C::NLA, AK>(pa, kb, p.K, sA0, wave, lane);
-  issue_panel<C::NLB, BKM>(pb, kb, p.K, sB0, wave, lane);
+  issue_panel<C::NLA, AK>(pa, kb, p.K, stage_a<BNV>(smem, 0), wave, lane);
+  issue_panel<C::NLB, BKM>(pb, kb, p.K, stage_b<BNV>(smem, 0), wave, lane);
+  // stage addresses from the step's parity (a select between four pointers
+  // measured a little slower in the weight gradients' loop)
+  int cur = 0;
   for (int kt = kb; kt < ke; ++kt) {
-    const bool odd = (kt - kb) & 1;
-    kstep<NW, BNV, AK, BKM>(p, pa, pb, kt, odd ? sA1 : sA0, odd ? sB1 : sB0, odd ? sA0 : sA1, odd ? sB0 : sB1, wave,
-                            lane, rowA, rowB, offA, offB, s1, g, pbA, pbB, acc);
+    kstep<NW, BNV, AK, BKM>(p, pa, pb, kt, stage_a<BNV>(smem, cur), stage_b<BNV>(smem, cur),
+                            stage_a<BNV>(smem, cur ^ 1), stage_b<BNV>(smem, cur ^ 1), wave, lane, rowA, rowB, offA,
+                            offB, s1, g, pbA, pbB, acc);
+    cur ^= 1;
   }
   wait_vmem();      // the last step's read-ahead loads have landed
   __syncthreads();  // LDS is reused by the next work item
@@ -516,11 +525,6 @@ __device__ __forceinline__ void store_partial(float* slot, const f32x16 (&acc)[W
 template <int NW, int BNV, bool AK, bool BKM, int EPI>
 __device__ __forceinline__ void gemm_body(const KParams& p, bf16* smem) {
   constexpr int MI = WC<NW, BNV>::MI, NJ = WC<NW, BNV>::NJ;
-  // two stages of each operand, contiguous (the epilogue reuses all of it)
-  bf16* sA0 = smem;
-  bf16* sA1 = smem + BM * BKK;
-  bf16* sB0 = smem + 2 * BM * BKK;
-  bf16* sB1 = sB0 + BNV * BKK;
   const int lw = logical_wg(blockIdx.x, p.grid);
   if (p.splits > 1) {
     // data-parallel rounds, then the split tail: consecutive workgroups (one
@@ -535,7 +539,7 @@ __device__ __forceinline__ void gemm_body(const KParams& p, bf16* smem) {
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
-      mainloop<NW, BNV, AK, BKM>(p, tm, tn, 0, p.iters, acc, sA0, sA1, sB0, sB1);
+      mainloop<NW, BNV, AK, BKM>(p, tm, tn, 0, p.iters, acc, smem);
       epilogue_tile<NW, BNV, EPI>(p, tm, tn, acc, smem);
     }
     if (lw >= p.splits * p.split_tiles) return;
@@ -549,7 +553,7 @@ __device__ __forceinline__ void gemm_body(const KParams& p, bf16* smem) {
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
-    mainloop<NW, BNV, AK, BKM>(p, tm, tn, kb, ke, acc, sA0, sA1, sB0, sB1);
+    mainloop<NW, BNV, AK, BKM>(p, tm, tn, kb, ke, acc, smem);
     store_partial<NW, BNV>(p.partials + (long)lw * BM * BNV, acc);
     return;
   }
@@ -586,7 +590,7 @@ __device__ __forceinline__ void gemm_body(const KParams& p, bf16* smem) {
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
-    mainloop<NW, BNV, AK, BKM>(p, tm, tn, kb, ke, acc, sA0, sA1, sB0, sB1);
+    mainloop<NW, BNV, AK, BKM>(p, tm, tn, kb, ke, acc, smem);
     if (kb == 0 && ke == p.iters) {
       epilogue_tile<NW, BNV, EPI>(p, tm, tn, acc, smem);
     } else {
