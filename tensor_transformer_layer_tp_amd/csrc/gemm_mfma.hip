@@ -165,12 +165,14 @@ __device__ __forceinline__ Panel<NLI> panel_kouter(const bf16* X, long ld, int r
 }
 
 // Issue the NLI loads of one operand for k-step kt into LDS stage `dst`.
-template <int NLI, bool KIN>
+// TAIL: k-step kt may be a partial one (k-inner chunks at or past K must
+// read zeros, not the next row); the caller passes false for every k-step
+// that is full or past the tile's end (whose data nobody uses).
+template <int NLI, bool KIN, bool TAIL>
 __device__ __forceinline__ void issue_panel(const Panel<NLI>& pn, int kt, int K, bf16* dst, int wave, int lane) {
   const int soff = (int)uni((uint32_t)kt * pn.kstep);
   __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)pn.base, (short)0, (int)pn.nrec, 0x00020000);
-  // k tail (k-inner only): chunks at or past K must read zeros, not the next row
-  const bool tail = KIN && (kt + 1) * BKK > K;
+  const bool tail = KIN && TAIL && (kt + 1) * BKK > K;
 #pragma unroll
   for (int i = 0; i < NLI; ++i) {
     const int b = NLI * wave + i;
@@ -221,7 +223,7 @@ __device__ __forceinline__ bf16x8 frag_kout(const bf16* s, int lane_off, int kk)
 // information lets the compiler's wait-count pass leave the in-flight LDS
 // writes (other stage) outstanding while the fragment reads (this stage)
 // proceed.
-template <int NW, int BNV, bool AK, bool BKM>
+template <int NW, int BNV, bool AK, bool BKM, bool TAIL>
 __device__ __forceinline__ void kstep(const KParams& p, const Panel<WC<NW, BNV>::NLA>& pa,
                                       const Panel<WC<NW, BNV>::NLB>& pb, int kt, const bf16* __restrict__ a,
                                       const bf16* __restrict__ b, bf16* __restrict__ na, bf16* __restrict__ nb,
@@ -236,8 +238,8 @@ __device__ __forceinline__ void kstep(const KParams& p, const Panel<WC<NW, BNV>:
   // Next k-step's loads, unconditionally so that the whole step is one
   // scheduling region: past the last k-step of the tile they read either zeros
   // (k beyond K is out of the buffer's range) or in-range data nobody uses.
-  issue_panel<NLA, AK>(pa, kt + 1, p.K, na, wave, lane);
-  issue_panel<NLB, BKM>(pb, kt + 1, p.K, nb, wave, lane);
+  issue_panel<NLA, AK, TAIL>(pa, kt + 1, p.K, na, wave, lane);
+  issue_panel<NLB, BKM, TAIL>(pb, kt + 1, p.K, nb, wave, lane);
   // fragments read in the order a0, b0, a1, b1, ...
   bf16x8 af[2][MI], bfg[2][NJ];
 #pragma unroll
@@ -316,15 +318,33 @@ __device__ __forceinline__ void mainloop(const KParams& p, int tm, int tn, int k
   for (int i = 0; i < MI; ++i) offA[i] = AK ? 0 : kout_lane_off(wm * WMW, i, lane);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) offB[j] = BKM ? 0 : kout_lane_off(wn * WNW, j, lane);
-  issue_panel<C::NLA, AK>(pa, kb, p.K, stage_a<BNV>(smem, 0), wave, lane);
-  issue_panel<C::NLB, BKM>(pb, kb, p.K, stage_b<BNV>(smem, 0), wave, lane);
+  issue_panel<C::NLA, AK, true>(pa, kb, p.K, stage_a<BNV>(smem, 0), wave, lane);
+  issue_panel<C::NLB, BKM, true>(pb, kb, p.K, stage_b<BNV>(smem, 0), wave, lane);
+  // the one k-step that may be partial (none if K is a multiple of BKK); only
+  // the step that loads it checks its chunks against K: the loop is split
+  // around that step
+  const int ktail = p.K % BKK ? p.iters - 1 : -1;
+  const int kmid = ktail > kb && ktail - 1 < ke ? ktail - 1 : ke;
   // stage addresses from the step's parity (a select between four pointers
   // measured a little slower in the weight gradients' loop)
-  int cur = 0;
-  for (int kt = kb; kt < ke; ++kt) {
-    kstep<NW, BNV, AK, BKM>(p, pa, pb, kt, stage_a<BNV>(smem, cur), stage_b<BNV>(smem, cur),
-                            stage_a<BNV>(smem, cur ^ 1), stage_b<BNV>(smem, cur ^ 1), wave, lane, rowA, rowB, offA,
-                            offB, s1, g, pbA, pbB, acc);
+  int cur = 0, kt = kb;
+  for (; kt < kmid; ++kt) {
+    kstep<NW, BNV, AK, BKM, false>(p, pa, pb, kt, stage_a<BNV>(smem, cur), stage_b<BNV>(smem, cur),
+                                   stage_a<BNV>(smem, cur ^ 1), stage_b<BNV>(smem, cur ^ 1), wave, lane, rowA, rowB,
+                                   offA, offB, s1, g, pbA, pbB, acc);
+    cur ^= 1;
+  }
+  if (kt < ke) {
+    kstep<NW, BNV, AK, BKM, true>(p, pa, pb, kt, stage_a<BNV>(smem, cur), stage_b<BNV>(smem, cur),
+                                  stage_a<BNV>(smem, cur ^ 1), stage_b<BNV>(smem, cur ^ 1), wave, lane, rowA, rowB,
+                                  offA, offB, s1, g, pbA, pbB, acc);
+    cur ^= 1;
+    ++kt;
+  }
+  for (; kt < ke; ++kt) {
+    kstep<NW, BNV, AK, BKM, false>(p, pa, pb, kt, stage_a<BNV>(smem, cur), stage_b<BNV>(smem, cur),
+                                   stage_a<BNV>(smem, cur ^ 1), stage_b<BNV>(smem, cur ^ 1), wave, lane, rowA, rowB,
+                                   offA, offB, s1, g, pbA, pbB, acc);
     cur ^= 1;
   }
   wait_vmem();      // the last step's read-ahead loads have landed
