@@ -50,7 +50,7 @@ def step_flops(w) -> dict:
         "qkv_proj": g(T, 3 * hl, h), "attn_fwd": att, "out_proj": g(T, h, hl), "fc1": g(T, fl, h),
         "fc2": g(T, h, fl), "fc2_dgrad": g(T, fl, h), "fc2_wgrad": g(fl, h, T), "fc1_wgrad": g(h, fl, T),
         "fc1_dgrad": g(T, h, fl), "out_dgrad": g(T, hl, h), "out_wgrad": g(hl, h, T), "attn_bwd": 2 * att,
-        "qkv_wgrad": g(h, 3 * hl, T), "qkv_dgrad": g(T, h, 3 * hl), "bias_grads": 0.0,
+        "qkv_wgrad": g(h, 3 * hl, T), "qkv_dgrad": g(T, h, 3 * hl), "bias_grads": 0.0, "transposes": 0.0,
     }
 
 

@@ -318,7 +318,11 @@ enum {
   TP_STEP_CE_COMBINE = 20, /* exchange of the aggregates (emulated)          */
   TP_STEP_CE_DLOGITS = 21, /* dlogits = (softmax - onehot) dloss             */
   TP_STEP_LOGITS_DGRAD = 22, /* dX_i = dlogits W_i                           */
-  TP_STEP_LOGITS_WGRAD = 23  /* dW_i = dlogits^T X                           */
+  TP_STEP_LOGITS_WGRAD = 23, /* dW_i = dlogits^T X                           */
+  TP_STEP_TRANSPOSE = 24     /* bf16 backward: token-contiguous copies y_i^T,
+                                dPre^T, ctx_i^T, dqkv^T read by the weight
+                                gradients (the dPre^T and dqkv^T copies also
+                                form db1_i's and dbqkv_i's column partials) */
 };
 
 /* Measurement aid (no passage of the pages; for benchmarks): while bit k of

@@ -102,7 +102,7 @@ STEPS = {
     "qkv_proj": 1, "attn_fwd": 2, "out_proj": 3, "fc1": 4, "fc2": 5, "fc2_dgrad": 6, "fc2_wgrad": 7,
     "fc1_wgrad": 8, "fc1_dgrad": 9, "out_dgrad": 10, "out_wgrad": 11, "attn_bwd": 12, "qkv_wgrad": 13,
     "qkv_dgrad": 14, "bias_grads": 15, "ln_fwd": 16, "ln_bwd": 17, "logits": 18, "ce_stats": 19,
-    "ce_combine": 20, "ce_dlogits": 21, "logits_dgrad": 22, "logits_wgrad": 23,
+    "ce_combine": 20, "ce_dlogits": 21, "logits_dgrad": 22, "logits_wgrad": 23, "transposes": 24,
 }
 
 

@@ -693,11 +693,16 @@ __device__ __forceinline__ void fixup_body(const KParams& p, int first_tile) {
     fixup_body<NWV, BNV, EV>(p, first_tile);                                               \
   }
 
-// Products with a k-inner A (activations of the forward products, input
-// gradients) run 8 waves per workgroup (two per SIMD); the weight gradients
-// (both operands read through transposing LDS loads) run 4. Products with a
-// k-inner B also have a 256x320-tile kernel (suffix _n320), taken when N is a
-// multiple of 320.
+// Every layer product runs 8 waves per workgroup (two per SIMD). The weight
+// gradients (K = tokens) take one operand as a transposed copy made just
+// before them (k-inner, read by ds_read_b128) and the other as stored
+// (k-outer, read through transposing LDS loads): with both operands k-outer
+// the 8-wave tile reads 1.5x more LDS bytes-equivalent per flop than the
+// forward products, and 4 waves (one per SIMD) left the matrix cores idle at
+// every wait; the copies cost less than they save. Products with a k-inner B
+// also have a 256x320-tile kernel (suffix _n320), taken when N is a multiple
+// of 320. Only the vocabulary-parallel weight gradient keeps 4 waves with
+// both operands k-outer.
 // forward products: A k-inner (activations), B k-outer (weights)
 TP_GEMM_KERNELS(gemm_qkv_proj, 8, 256, true, false, EPI_BIAS_F32)
 TP_GEMM_KERNELS(gemm_out_proj, 8, 256, true, false, EPI_STORE)
@@ -712,11 +717,16 @@ TP_GEMM_KERNELS(gemm_fc2_dgrad_gelu_n320, 8, 320, true, true, EPI_DGELU)
 TP_GEMM_KERNELS(gemm_fc1_dgrad_n320, 8, 320, true, true, EPI_STORE)
 TP_GEMM_KERNELS(gemm_out_dgrad_n320, 8, 320, true, true, EPI_STORE)
 TP_GEMM_KERNELS(gemm_qkv_dgrad_n320, 8, 320, true, true, EPI_STORE)
-// weight gradients: both k-outer (K = tokens)
-TP_GEMM_KERNELS(gemm_fc2_wgrad, 4, 256, false, false, EPI_STORE)
-TP_GEMM_KERNELS(gemm_fc1_wgrad, 4, 256, false, false, EPI_STORE)
-TP_GEMM_KERNELS(gemm_out_wgrad, 4, 256, false, false, EPI_STORE)
-TP_GEMM_KERNELS(gemm_qkv_wgrad, 4, 256, false, false, EPI_STORE)
+// weight gradients (K = tokens): dB_i = (y_i^T copy) dZ and dWo_i = (ctx_i^T
+// copy) dO take a k-inner A and the stored gradient as a k-outer B; dA_i = X^T
+// (dPre^T copy) and dWqkv_i = X^T (dqkv^T copy) take X as stored (k-outer A)
+// and a k-inner B
+TP_GEMM_KERNELS(gemm_fc2_wgrad, 8, 256, true, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_out_wgrad, 8, 256, true, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_fc1_wgrad, 8, 256, false, true, EPI_STORE)
+TP_GEMM_KERNELS(gemm_qkv_wgrad, 8, 256, false, true, EPI_STORE)
+TP_GEMM_KERNELS(gemm_fc1_wgrad_n320, 8, 320, false, true, EPI_STORE)
+TP_GEMM_KERNELS(gemm_qkv_wgrad_n320, 8, 320, false, true, EPI_STORE)
 // vocabulary-parallel output layer: logits = X W_i^T (the table slice W_i
 // [V/p, h] is k-inner), dX = dlogits W_i, dW_i = dlogits^T X
 TP_GEMM_KERNELS(gemm_logits, 8, 256, true, true, EPI_STORE)
@@ -822,10 +832,10 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
     TP_ROLE_W(GR_FC1_DGRAD, gemm_fc1_dgrad, 8, true, true, EPI_STORE)
     TP_ROLE_W(GR_OUT_DGRAD, gemm_out_dgrad, 8, true, true, EPI_STORE)
     TP_ROLE_W(GR_QKV_DGRAD, gemm_qkv_dgrad, 8, true, true, EPI_STORE)
-    TP_ROLE(GR_FC2_WGRAD, gemm_fc2_wgrad, 4, false, false, EPI_STORE)
-    TP_ROLE(GR_FC1_WGRAD, gemm_fc1_wgrad, 4, false, false, EPI_STORE)
-    TP_ROLE(GR_OUT_WGRAD, gemm_out_wgrad, 4, false, false, EPI_STORE)
-    TP_ROLE(GR_QKV_WGRAD, gemm_qkv_wgrad, 4, false, false, EPI_STORE)
+    TP_ROLE(GR_FC2_WGRAD, gemm_fc2_wgrad, 8, true, false, EPI_STORE)
+    TP_ROLE_W(GR_FC1_WGRAD, gemm_fc1_wgrad, 8, false, true, EPI_STORE)
+    TP_ROLE(GR_OUT_WGRAD, gemm_out_wgrad, 8, true, false, EPI_STORE)
+    TP_ROLE_W(GR_QKV_WGRAD, gemm_qkv_wgrad, 8, false, true, EPI_STORE)
     TP_ROLE_W(GR_LOGITS, gemm_logits, 8, true, true, EPI_STORE)
     TP_ROLE(GR_LOGITS_DGRAD, gemm_logits_dgrad, 8, true, false, EPI_STORE)
     TP_ROLE(GR_LOGITS_WGRAD, gemm_logits_wgrad, 4, false, false, EPI_STORE)

@@ -82,6 +82,17 @@ size_t colsum_workspace_bytes(int M, int N);
 hipError_t colsum_launch(int dtype, const void* X, int M, int N, long ld, void* out, float* ws,
                          hipStream_t stream);
 
+// bf16 XT[c*ldt + r] = X[r*ldx + c] (r < R, c < C; the 8-row group holding
+// row R-1 is written whole, zeros past R, so ldt must be a multiple of 8 and
+// >= R), and, when part is not null, part[b*C + c] = sum of X[r][c] over rows
+// 64b .. 64b+63 (fixed order) for b < transpose_part_rows(R). Needs C % 8 == 0,
+// ldx % 8 == 0, 16-byte aligned X and XT.
+int transpose_part_rows(int R);
+hipError_t transpose_colsum_launch(const void* X, int R, int C, long ldx, void* XT, long ldt, float* part,
+                                   hipStream_t stream);
+// out[n] = sum over r < R of part[r*N + n], added in the order r = 0, 1, ...
+hipError_t colsum_final_launch(int dtype, const float* part, int R, int N, void* out, hipStream_t stream);
+
 // out[i] = sum_k parts[k][i] + bias[i % cols] over count elements.
 hipError_t sum_partials_launch(int dtype, const void* const* parts, int n_parts, const void* bias,
                                void* out, long long count, int cols, hipStream_t stream);

@@ -179,8 +179,18 @@ struct Bump {
 
 size_t max3(size_t a, size_t b, size_t c) { return a > b ? (a > c ? a : c) : (b > c ? b : c); }
 
+// Row length of a transposed [*, T] copy: T rounded up to a multiple of 8
+// (at least 8), so that every row starts 16-byte aligned.
+long long t_ld(long long T) { return T < 8 ? 8 : (T + 7) / 8 * 8; }
+
+// bf16 weight gradients read one operand as a transposed copy (k = tokens
+// contiguous); the fp32 path reads both as stored.
+bool wgrad_copies(const Dims& dm) { return dm.dtype == DT_BF16; }
+
 struct MlpPlan {
   void *dpre, *gemm_ws, *col_ws;
+  void *yT, *dpreT;  // [fl, t_ld(T)] transposed copies (bf16 backward)
+  float* tpart;      // [transpose_part_rows(T), fl] column partials of dPre
   size_t gemm_bytes, col_bytes, total;
 };
 
@@ -189,6 +199,12 @@ MlpPlan plan_mlp(const Dims& dm, void* ws, bool bwd) {
   MlpPlan pl{};
   const int dt = dm.dtype;
   if (bwd) pl.dpre = bp.take((size_t)(dm.T * dm.fl) * dm.esz);
+  if (bwd && wgrad_copies(dm) && dm.T > 0) {
+    const size_t tbytes = (size_t)(dm.fl * t_ld(dm.T)) * dm.esz;
+    pl.yT = bp.take(tbytes);
+    pl.dpreT = bp.take(tbytes);
+    pl.tpart = (float*)bp.take((size_t)transpose_part_rows((int)dm.T) * dm.fl * sizeof(float));
+  }
   size_t g = gemm_workspace_bytes(dt, (int)dm.T, (int)dm.fl, (int)dm.h);
   g = max3(g, gemm_workspace_bytes(dt, (int)dm.T, (int)dm.h, (int)dm.fl), 0);
   if (bwd) {
@@ -205,6 +221,8 @@ MlpPlan plan_mlp(const Dims& dm, void* ws, bool bwd) {
 
 struct AttnPlan {
   void *dctx, *dqkv, *delta, *gemm_ws, *col_ws, *split;
+  void *ctxT, *dqkvT;  // [hl, t_ld(T)], [3hl, t_ld(T)] transposed copies (bf16 backward)
+  float* tpart;        // [transpose_part_rows(T), 3hl] column partials of dqkv
   size_t gemm_bytes, col_bytes, total;
 };
 
@@ -221,6 +239,11 @@ AttnPlan plan_attn(const Dims& dm, void* ws, bool bwd) {
     pl.dctx = bp.take((size_t)(dm.T * dm.hl) * dm.esz);
     pl.dqkv = bp.take((size_t)(dm.T * 3 * dm.hl) * dm.esz);
     pl.delta = bp.take((size_t)(dm.T * dm.nl) * sizeof(float));
+    if (wgrad_copies(dm) && dm.T > 0) {
+      pl.ctxT = bp.take((size_t)(dm.hl * t_ld(dm.T)) * dm.esz);
+      pl.dqkvT = bp.take((size_t)(3 * dm.hl * t_ld(dm.T)) * dm.esz);
+      pl.tpart = (float*)bp.take((size_t)transpose_part_rows((int)dm.T) * 3 * dm.hl * sizeof(float));
+    }
     g = max3(g, gemm_workspace_bytes(dt, (int)B, (int)dm.hl, (int)dm.h),
              gemm_workspace_bytes(dt, (int)dm.hl, (int)dm.h, (int)B));
     g = max3(g, gemm_workspace_bytes(dt, (int)dm.h, (int)(3 * dm.hl), (int)B), 0);
@@ -373,11 +396,23 @@ tp_status tp_mlp_bwd(const tp_shape* shape, const void* X, const void* A_i, cons
     TP_STEP(TP_STEP_FC2_DGRAD, gemm_launch(dt, g, pl.gemm_ws, pl.gemm_bytes, st), "mlp dgrad (dZ B_i^T * GeLU'(pre_i))");
   }
   // weight gradients (K = T; T == 0 gives zeros)
-  TP_STEP(TP_STEP_FC2_WGRAD, gemm_launch(dt, gd(GR_FC2_WGRAD, fl, h, T, y_i, fl, false, dZ, h, false, EPI_STORE, dB_i, h), pl.gemm_ws, pl.gemm_bytes, st),
-         "mlp wgrad dB_i = y_i^T dZ");
-  TP_STEP(TP_STEP_FC1_WGRAD, gemm_launch(dt, gd(GR_FC1_WGRAD, h, fl, T, X, h, false, pl.dpre, fl, false, EPI_STORE, dA_i, fl), pl.gemm_ws, pl.gemm_bytes, st),
-         "mlp wgrad dA_i = X^T dPre");
-  TP_STEP(TP_STEP_BIAS_GRADS, colsum_launch(dt, pl.dpre, T, fl, fl, db1_i, (float*)pl.col_ws, st), "mlp db1_i");
+  if (wgrad_copies(dm)) {
+    // y_i^T and dPre^T copies (the latter with db1_i's column partials)
+    const long ldt = (long)t_ld(T);
+    TP_STEP(TP_STEP_TRANSPOSE, transpose_colsum_launch(y_i, T, fl, fl, pl.yT, ldt, nullptr, st), "mlp y_i^T copy");
+    TP_STEP(TP_STEP_FC2_WGRAD, gemm_launch(dt, gd(GR_FC2_WGRAD, fl, h, T, pl.yT, ldt, true, dZ, h, false, EPI_STORE, dB_i, h), pl.gemm_ws, pl.gemm_bytes, st),
+           "mlp wgrad dB_i = y_i^T dZ");
+    TP_STEP(TP_STEP_TRANSPOSE, transpose_colsum_launch(pl.dpre, T, fl, fl, pl.dpreT, ldt, pl.tpart, st), "mlp dPre^T copy");
+    TP_STEP(TP_STEP_FC1_WGRAD, gemm_launch(dt, gd(GR_FC1_WGRAD, h, fl, T, X, h, false, pl.dpreT, ldt, true, EPI_STORE, dA_i, fl), pl.gemm_ws, pl.gemm_bytes, st),
+           "mlp wgrad dA_i = X^T dPre");
+    TP_STEP(TP_STEP_BIAS_GRADS, colsum_final_launch(dt, pl.tpart, transpose_part_rows(T), fl, db1_i, st), "mlp db1_i");
+  } else {
+    TP_STEP(TP_STEP_FC2_WGRAD, gemm_launch(dt, gd(GR_FC2_WGRAD, fl, h, T, y_i, fl, false, dZ, h, false, EPI_STORE, dB_i, h), pl.gemm_ws, pl.gemm_bytes, st),
+           "mlp wgrad dB_i = y_i^T dZ");
+    TP_STEP(TP_STEP_FC1_WGRAD, gemm_launch(dt, gd(GR_FC1_WGRAD, h, fl, T, X, h, false, pl.dpre, fl, false, EPI_STORE, dA_i, fl), pl.gemm_ws, pl.gemm_bytes, st),
+           "mlp wgrad dA_i = X^T dPre");
+    TP_STEP(TP_STEP_BIAS_GRADS, colsum_launch(dt, pl.dpre, T, fl, fl, db1_i, (float*)pl.col_ws, st), "mlp db1_i");
+  }
   if (T > 0)
     TP_STEP(TP_STEP_FC1_DGRAD, gemm_launch(dt, gd(GR_FC1_DGRAD, T, h, fl, pl.dpre, fl, true, A_i, fl, true, EPI_STORE, dX_i, h), pl.gemm_ws, pl.gemm_bytes, st),
            "mlp dgrad dX_i = dPre A_i^T");
@@ -468,8 +503,16 @@ tp_status attn_bwd_impl(const tp_shape* shape, const tp_dropout* dr, const uint1
   if (T > 0)
     TP_STEP(TP_STEP_OUT_DGRAD, gemm_launch(dt, gd(GR_OUT_DGRAD, T, hl, h, dO, h, true, Wo_i, h, true, EPI_STORE, pl.dctx, hl), pl.gemm_ws, pl.gemm_bytes, st),
            "attn dgrad dC = dO Wo_i^T");
-  TP_STEP(TP_STEP_OUT_WGRAD, gemm_launch(dt, gd(GR_OUT_WGRAD, hl, h, T, ctx_i, hl, false, dO, h, false, EPI_STORE, dWo_i, h), pl.gemm_ws, pl.gemm_bytes, st),
-         "attn wgrad dWo_i = ctx_i^T dO");
+  const bool copies = wgrad_copies(dm);
+  const long ldt = (long)t_ld(T);
+  if (copies) {
+    TP_STEP(TP_STEP_TRANSPOSE, transpose_colsum_launch(ctx_i, T, hl, hl, pl.ctxT, ldt, nullptr, st), "attn ctx_i^T copy");
+    TP_STEP(TP_STEP_OUT_WGRAD, gemm_launch(dt, gd(GR_OUT_WGRAD, hl, h, T, pl.ctxT, ldt, true, dO, h, false, EPI_STORE, dWo_i, h), pl.gemm_ws, pl.gemm_bytes, st),
+           "attn wgrad dWo_i = ctx_i^T dO");
+  } else {
+    TP_STEP(TP_STEP_OUT_WGRAD, gemm_launch(dt, gd(GR_OUT_WGRAD, hl, h, T, ctx_i, hl, false, dO, h, false, EPI_STORE, dWo_i, h), pl.gemm_ws, pl.gemm_bytes, st),
+           "attn wgrad dWo_i = ctx_i^T dO");
+  }
   if (dbo_or_null) TP_STEP(TP_STEP_BIAS_GRADS, colsum_launch(dt, dO, T, h, h, dbo_or_null, (float*)pl.col_ws, st), "attn dbo");
   if (T > 0) {
     AttnDesc a;
@@ -482,10 +525,19 @@ tp_status attn_bwd_impl(const tp_shape* shape, const tp_dropout* dr, const uint1
     }
     TP_STEP(TP_STEP_ATTN_BWD, attn_bwd_launch(dt, a, st), "attn backward");
   }
-  TP_STEP(TP_STEP_QKV_WGRAD, gemm_launch(dt, gd(GR_QKV_WGRAD, h, 3 * hl, T, X, h, false, pl.dqkv, 3 * hl, false, EPI_STORE, dWqkv_i, 3 * hl), pl.gemm_ws,
-                     pl.gemm_bytes, st),
-         "attn wgrad dWqkv_i = X^T dqkv");
-  TP_STEP(TP_STEP_BIAS_GRADS, colsum_launch(dt, pl.dqkv, T, 3 * hl, 3 * hl, dbqkv_i, (float*)pl.col_ws, st), "attn dbqkv_i");
+  if (copies) {
+    // dqkv^T copy with dbqkv_i's column partials
+    TP_STEP(TP_STEP_TRANSPOSE, transpose_colsum_launch(pl.dqkv, T, 3 * hl, 3 * hl, pl.dqkvT, ldt, pl.tpart, st), "attn dqkv^T copy");
+    TP_STEP(TP_STEP_QKV_WGRAD, gemm_launch(dt, gd(GR_QKV_WGRAD, h, 3 * hl, T, X, h, false, pl.dqkvT, ldt, true, EPI_STORE, dWqkv_i, 3 * hl), pl.gemm_ws,
+                       pl.gemm_bytes, st),
+           "attn wgrad dWqkv_i = X^T dqkv");
+    TP_STEP(TP_STEP_BIAS_GRADS, colsum_final_launch(dt, pl.tpart, transpose_part_rows(T), 3 * hl, dbqkv_i, st), "attn dbqkv_i");
+  } else {
+    TP_STEP(TP_STEP_QKV_WGRAD, gemm_launch(dt, gd(GR_QKV_WGRAD, h, 3 * hl, T, X, h, false, pl.dqkv, 3 * hl, false, EPI_STORE, dWqkv_i, 3 * hl), pl.gemm_ws,
+                       pl.gemm_bytes, st),
+           "attn wgrad dWqkv_i = X^T dqkv");
+    TP_STEP(TP_STEP_BIAS_GRADS, colsum_launch(dt, pl.dqkv, T, 3 * hl, 3 * hl, dbqkv_i, (float*)pl.col_ws, st), "attn dbqkv_i");
+  }
   if (T > 0)
     TP_STEP(TP_STEP_QKV_DGRAD, gemm_launch(dt, gd(GR_QKV_DGRAD, T, h, 3 * hl, pl.dqkv, 3 * hl, true, Wqkv_i, 3 * hl, true, EPI_STORE, dX_i, h), pl.gemm_ws,
                        pl.gemm_bytes, st),

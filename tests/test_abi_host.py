@@ -4,6 +4,8 @@ before touching the device (every call here returns before any HIP call)."""
 import ctypes
 import subprocess
 
+import os
+
 import pytest
 
 import tensor_transformer_layer_tp_amd as tp
@@ -129,7 +131,11 @@ def test_profile_mask_without_gpu():
     tp.tp_profile_enable(1 << tp.STEPS["fc1"])
     tp.tp_profile_enable(0)
     assert tp.tp_profile_collect(tp.STEPS["fc1"]) == (0, 0.0)
-    assert set(tp.STEPS.values()) == set(range(1, 24))
+    # the binding's step ids are exactly the header's TP_STEP_* values
+    import re
+    with open(os.path.join(os.path.dirname(__file__), "..", "include", "tp_layer.h")) as fh:
+        ids = {int(v) for v in re.findall(r"TP_STEP_\w+ = (\d+)", fh.read())}
+    assert set(tp.STEPS.values()) == ids == set(range(1, 25))
 
 
 def test_empty_batch_needs_no_token_pointers():

@@ -6,6 +6,8 @@ partial last row of tiles) and a stream-K tail:
   * h = 3200, f = 9600: the GEMM2 input gradient (+ GeLU' epilogue) runs 320
     wide (N = f);
   * h = 9600, f = 3200: the GEMM1 input gradient runs 320 wide (N = h).
+The GEMM1 weight gradient (X^T times a transposed dPre copy) runs 320 wide in
+both shapes, with K = 2100 tokens (a partial last k-step).
 The oracle recomputes column sub-shards and sampled token rows exactly."""
 import numpy as np
 import pytest
