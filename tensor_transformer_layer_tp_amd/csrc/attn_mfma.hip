@@ -76,6 +76,20 @@ struct MP {
   uint32_t drop_thr;   // keep iff the 16-bit uniform >= drop_thr
   float drop_scale;    // 65536 / (65536 - drop_thr)
   uint64_t seed, offset;
+  // forward key-split items: partial (output, max, sum) of each half,
+  // [2][batch * n_local][seq][D] and [2][batch * n_local][seq]
+  float* part_o;
+  float* part_ml;
+};
+
+// Forward work items, heaviest first: item = qt << 2 | part, where part 0 is
+// a whole 128-query tile and parts 1, 2 are the two halves of its key tiles.
+// n == 0: no table, blockIdx.y = nqt - 1 - qt.
+constexpr int kMaxFwdItems = 512;
+struct FwdItems {
+  int n;
+  int qsplit;  // query tiles >= qsplit are split (== nqt: none)
+  uint16_t it[kMaxFwdItems];
 };
 
 // Keep bits (bit q = lane q's key) of query i, key block kb, half g.
@@ -285,7 +299,7 @@ __device__ __forceinline__ void fwd_block(const MP& p, const char* __restrict__ 
 constexpr int FWD_WAVES = 8;
 
 template <int D, bool AL, bool DO>
-__global__ __launch_bounds__(64 * FWD_WAVES) void fwd_mfma(MP p) {
+__global__ __launch_bounds__(64 * FWD_WAVES) void fwd_mfma(MP p, FwdItems items) {
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
   constexpr int NX = NB * 16 + 2;  // floats a wave hands to its partner, per lane
   static_assert(4 * NX * 64 * 4 <= 6 * TB, "merge buffer exceeds the tile stages");
@@ -293,7 +307,12 @@ __global__ __launch_bounds__(64 * FWD_WAVES) void fwd_mfma(MP p) {
   const int head = blockIdx.x;
   const int b = head / p.n_local, l = head - b * p.n_local;
   const int nqt = (p.seq + 127) / 128;
-  const int qt = nqt - 1 - blockIdx.y;  // heaviest (longest causal prefix) first
+  int qt = nqt - 1 - (int)blockIdx.y, part = 0;  // heaviest (longest causal prefix) first
+  if (items.n) {
+    const int it = items.it[blockIdx.y];
+    qt = it >> 2;
+    part = it & 3;
+  }
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = (int)uni((uint32_t)(tid >> 6));
   const int qw = w & 3, kh = w >> 2;
@@ -303,9 +322,12 @@ __global__ __launch_bounds__(64 * FWD_WAVES) void fwd_mfma(MP p) {
   const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
   const int kv_end = min(p.seq, qt * 128 + 128);
   const int nkt = (kv_end + TROWS - 1) / TROWS;
-  dma_tile<D, FWD_WAVES>(p.kh, nrec, stage, grow0, l * D, 0, p.seq, p.h_l, w, lane);
-  dma_tile<D, FWD_WAVES>(p.kl, nrec, stage + TB, grow0, l * D, 0, p.seq, p.h_l, w, lane);
-  dma_tile<D, FWD_WAVES>(p.vh, nrec, stage + 2 * TB, grow0, l * D, 0, p.seq, p.h_l, w, lane);
+  // key tiles [ktb, kte): all of them, or one half of a split item (every
+  // query of a split tile has keys in both halves)
+  const int ktb = part == 2 ? nkt / 2 : 0, kte = part == 1 ? nkt / 2 : nkt;
+  dma_tile<D, FWD_WAVES>(p.kh, nrec, stage, grow0, l * D, ktb * TROWS, p.seq, p.h_l, w, lane);
+  dma_tile<D, FWD_WAVES>(p.kl, nrec, stage + TB, grow0, l * D, ktb * TROWS, p.seq, p.h_l, w, lane);
+  dma_tile<D, FWD_WAVES>(p.vh, nrec, stage + 2 * TB, grow0, l * D, ktb * TROWS, p.seq, p.h_l, w, lane);
   FwdState<D> st;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -324,13 +346,13 @@ __global__ __launch_bounds__(64 * FWD_WAVES) void fwd_mfma(MP p) {
   const float slope2 = alibi_slope_log2(p, l);
   const TrOff tro = tr_offsets(lane);
   const RowOff ro = row_offsets(lane);
-  for (int kt = 0; kt < nkt; ++kt) {
+  for (int kt = ktb; kt < kte; ++kt) {
     loads_landed_barrier();  // tile kt is in LDS; tile kt-1 is no longer read
-    const bool odd = kt & 1;
+    const bool odd = (kt - ktb) & 1;
     const char* cur = odd ? stage + 3 * TB : stage;
     char* nxt = odd ? stage : stage + 3 * TB;
     const int kv0 = kt * TROWS;
-    if (kt + 1 < nkt) {
+    if (kt + 1 < kte) {
       dma_tile<D, FWD_WAVES>(p.kh, nrec, nxt, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
       dma_tile<D, FWD_WAVES>(p.kl, nrec, nxt + TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
       dma_tile<D, FWD_WAVES>(p.vh, nrec, nxt + 2 * TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
@@ -358,6 +380,29 @@ __global__ __launch_bounds__(64 * FWD_WAVES) void fwd_mfma(MP p) {
   const float f1 = st.m_run == -INFINITY ? 0.f : fexp2(st.m_run - m);
   const float f2 = m2 == -INFINITY ? 0.f : fexp2(m2 - m);
   const float lsum = st.l_run * f1 + l2 * f2;
+  if (part) {
+    // this half's output relative to its max m, with its sum; the merge
+    // kernel combines the two halves
+    const long row = ((long)(part - 1) * p.batch * p.n_local + head) * p.seq + myq;
+    float* po = p.part_o + row * D;
+#pragma unroll
+    for (int db = 0; db < NB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * q4 + e;
+          v[e] = st.o[db][i] * f1 + xs[(16 * db + i) * 64] * f2;
+        }
+        *(f32x4*)(po + 32 * db + 8 * q4 + 4 * g) = v;
+      }
+    if (g == 0) {
+      p.part_ml[2 * row] = m;
+      p.part_ml[2 * row + 1] = lsum;
+    }
+    return;
+  }
   const float inv = (DO ? p.drop_scale : 1.0f) / lsum;
   bf16* dst = p.ctx + (grow0 + myq) * p.h_l + (long)l * D;
 #pragma unroll
@@ -373,6 +418,42 @@ __global__ __launch_bounds__(64 * FWD_WAVES) void fwd_mfma(MP p) {
       *(bf16x4*)(dst + 32 * db + 8 * q4 + 4 * g) = v;
     }
   if (g == 0) p.lse[(long)head * p.seq + myq] = (m + __log2f(lsum)) * (1.0f / kLog2e);
+}
+
+// Merge of the two key halves of each split query tile: per query, with
+// m = max(m1, m2), ctx = (o1 2^(m1-m) + o2 2^(m2-m)) / (l1 2^(m1-m) + l2 2^(m2-m))
+// (times the dropout scale) and lse = m + log2(sum), in natural log. One
+// thread per query and 8 output columns.
+template <int D, bool DO>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(MP p, int q_first) {
+  constexpr int CH = D / 8;
+  const int nq = p.seq - q_first, nh = p.batch * p.n_local;
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)nh * nq * CH) return;
+  const int ch = (int)(idx % CH);
+  const long hq = idx / CH;
+  const int head = (int)(hq / nq), q = q_first + (int)(hq % nq);
+  const long r1 = (long)head * p.seq + q, r2 = ((long)nh + head) * p.seq + q;
+  const float m1 = p.part_ml[2 * r1], l1 = p.part_ml[2 * r1 + 1];
+  const float m2 = p.part_ml[2 * r2], l2 = p.part_ml[2 * r2 + 1];
+  const float m = fmaxf(m1, m2);
+  const float f1 = m1 == -INFINITY ? 0.f : fexp2(m1 - m);
+  const float f2 = m2 == -INFINITY ? 0.f : fexp2(m2 - m);
+  const float lsum = l1 * f1 + l2 * f2;
+  const float inv = (DO ? p.drop_scale : 1.0f) / lsum;
+  const float* o1 = p.part_o + r1 * D + 8 * ch;
+  const float* o2 = p.part_o + r2 * D + 8 * ch;
+  const f32x4 a0 = *(const f32x4*)o1, a1 = *(const f32x4*)(o1 + 4);
+  const f32x4 b0 = *(const f32x4*)o2, b1 = *(const f32x4*)(o2 + 4);
+  bf16x8 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[e] = (bf16)((a0[e] * f1 + b0[e] * f2) * inv);
+    v[4 + e] = (bf16)((a1[e] * f1 + b1[e] * f2) * inv);
+  }
+  const int b = head / p.n_local, l = head - b * p.n_local;
+  *(bf16x8*)(p.ctx + ((long)b * p.seq + q) * p.h_l + (long)l * D + 8 * ch) = v;
+  if (ch == 0) p.lse[(long)head * p.seq + q] = (m + __log2f(lsum)) * (1.0f / kLog2e);
 }
 
 // ---- backward: dK, dV ---------------------------------------------------------------
@@ -761,14 +842,71 @@ MP make_mp(const AttnDesc& a) {
   p.drop_scale = 65536.0f / (65536.0f - (float)p.drop_thr);
   p.seed = a.seed;
   p.offset = a.offset;
+  p.part_o = a.fwd_part;
+  p.part_ml = a.fwd_part ? a.fwd_part + 2L * a.batch * a.n_local * a.seq * a.head_dim : nullptr;
   return p;
+}
+
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Forward items. With fewer than two 128-query tiles per CU the longest
+// causal tiles decide the kernel's time (one workgroup per CU fits), so a
+// tile with more than half the longest tile's key tiles (and at least 4) is
+// split into two halves of its key tiles, merged afterwards; the items are
+// dealt heaviest first (ties: later query tile first).
+FwdItems fwd_items(const MP& p) {
+  FwdItems fi{};
+  const int nqt = (p.seq + 127) / 128, nh = p.batch * p.n_local;
+  auto nkt = [&](int qt) { return ((p.seq < qt * 128 + 128 ? p.seq : qt * 128 + 128) + TROWS - 1) / TROWS; };
+  fi.qsplit = nqt;
+  if (p.part_o == nullptr || 2 * nqt > kMaxFwdItems || (long)nh * nqt >= 2L * device_cus()) return fi;
+  const int kmax = nkt(nqt - 1);
+  while (fi.qsplit > 0 && nkt(fi.qsplit - 1) >= 4 && 2 * nkt(fi.qsplit - 1) > kmax) --fi.qsplit;
+  if (fi.qsplit == nqt) return fi;
+  int wt[kMaxFwdItems];
+  for (int qt = nqt - 1; qt >= 0; --qt) {
+    const int k = nkt(qt);
+    if (qt >= fi.qsplit) {
+      fi.it[fi.n] = (uint16_t)(qt << 2 | 2); wt[fi.n++] = k - k / 2;
+      fi.it[fi.n] = (uint16_t)(qt << 2 | 1); wt[fi.n++] = k / 2;
+    } else {
+      fi.it[fi.n] = (uint16_t)(qt << 2); wt[fi.n++] = k;
+    }
+  }
+  // stable insertion sort by weight, descending
+  for (int i = 1; i < fi.n; ++i) {
+    const int w = wt[i];
+    const uint16_t v = fi.it[i];
+    int j = i - 1;
+    while (j >= 0 && wt[j] < w) { wt[j + 1] = wt[j]; fi.it[j + 1] = fi.it[j]; --j; }
+    wt[j + 1] = w;
+    fi.it[j + 1] = v;
+  }
+  return fi;
 }
 
 template <int D, bool DO>
 hipError_t fwd_d(const MP& p, hipStream_t stream) {
-  dim3 grid(p.batch * p.n_local, (p.seq + 127) / 128);
-  if (p.alibi) hipLaunchKernelGGL((fwd_mfma<D, true, DO>), grid, dim3(64 * FWD_WAVES), 0, stream, p);
-  else hipLaunchKernelGGL((fwd_mfma<D, false, DO>), grid, dim3(64 * FWD_WAVES), 0, stream, p);
+  const FwdItems fi = fwd_items(p);
+  const int nqt = (p.seq + 127) / 128;
+  dim3 grid(p.batch * p.n_local, fi.n ? fi.n : nqt);
+  if (p.alibi) hipLaunchKernelGGL((fwd_mfma<D, true, DO>), grid, dim3(64 * FWD_WAVES), 0, stream, p, fi);
+  else hipLaunchKernelGGL((fwd_mfma<D, false, DO>), grid, dim3(64 * FWD_WAVES), 0, stream, p, fi);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || fi.qsplit >= nqt) return e;
+  const int q_first = fi.qsplit * 128;
+  const long n = (long)p.batch * p.n_local * (p.seq - q_first) * (D / 8);
+  hipLaunchKernelGGL((fwd_merge_kernel<D, DO>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, q_first);
   return hipGetLastError();
 }
 template <int D, bool DO>
@@ -787,6 +925,11 @@ bool attn_mfma_supported(int dtype, int head_dim) {
 
 size_t attn_split_bytes(int dtype, int head_dim, long long T, long long h_l) {
   return attn_mfma_supported(dtype, head_dim) ? (size_t)(5 * T * h_l * 2) : 0;
+}
+
+size_t attn_fwd_part_bytes(int dtype, int head_dim, int batch, int seq, int n_local) {
+  if (!attn_mfma_supported(dtype, head_dim)) return 0;
+  return (size_t)2 * batch * n_local * seq * (head_dim + 2) * sizeof(float);
 }
 
 size_t attn_dropout_mask_bytes(int batch, int seq, int n_local) {

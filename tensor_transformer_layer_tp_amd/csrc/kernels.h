@@ -70,8 +70,13 @@ struct AttnDesc {
   uint16_t* mask = nullptr;
   float drop_p = 0.f;
   uint64_t seed = 0, offset = 0;
+  // matrix-core forward only: attn_fwd_part_bytes() bytes for the partial
+  // results of query tiles whose keys are split over two workgroups (null:
+  // no split)
+  float* fwd_part = nullptr;
 };
 size_t attn_dropout_mask_bytes(int batch, int seq, int n_local);
+size_t attn_fwd_part_bytes(int dtype, int head_dim, int batch, int seq, int n_local);
 bool attn_mfma_supported(int dtype, int head_dim);
 size_t attn_split_bytes(int dtype, int head_dim, long long T, long long h_l);
 hipError_t attn_fwd_launch(int dtype, const AttnDesc& a, hipStream_t stream);
@@ -84,8 +89,8 @@ hipError_t colsum_launch(int dtype, const void* X, int M, int N, long ld, void* 
 
 // bf16 XT[c*ldt + r] = X[r*ldx + c] (r < R, c < C; the 8-row group holding
 // row R-1 is written whole, zeros past R, so ldt must be a multiple of 8 and
-// >= R), and, when part is not null, part[b*C + c] = sum of X[r][c] over rows
-// 64b .. 64b+63 (fixed order) for b < transpose_part_rows(R). Needs C % 8 == 0,
+// >= R), and, when part is not null, part[b*C + c] = sum of X[r][c] over the
+// b-th run of 32 rows (fixed order) for b < transpose_part_rows(R). Needs C % 8 == 0,
 // ldx % 8 == 0, 16-byte aligned X and XT.
 int transpose_part_rows(int R);
 hipError_t transpose_colsum_launch(const void* X, int R, int C, long ldx, void* XT, long ldt, float* part,

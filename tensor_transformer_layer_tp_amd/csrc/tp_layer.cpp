@@ -96,6 +96,7 @@ constexpr int kMaxDim = 1 << 22;
 
 struct Dims {
   long long T, h, hl, fl, nl, d;
+  long long batch, seq;
   int dtype;
   size_t esz;
 };
@@ -118,6 +119,8 @@ tp_status check_shape(const tp_shape* s, Dims& dm) {
   if (s->head_dim < 8 || s->head_dim > 256 || s->head_dim % 8 != 0)
     return fail(TP_ERR_HEADDIM, "head_dim %d not a multiple of 8 in [8, 256]", s->head_dim);
   dm.T = (long long)s->batch * s->seq;
+  dm.batch = s->batch;
+  dm.seq = s->seq;
   dm.h = s->hidden;
   dm.nl = s->n_heads / s->tp_size;
   dm.d = s->head_dim;
@@ -221,6 +224,7 @@ MlpPlan plan_mlp(const Dims& dm, void* ws, bool bwd) {
 
 struct AttnPlan {
   void *dctx, *dqkv, *delta, *gemm_ws, *col_ws, *split;
+  void* fwd_part;      // forward: partials of key-split query tiles
   void *ctxT, *dqkvT;  // [hl, t_ld(T)], [3hl, t_ld(T)] transposed copies (bf16 backward)
   float* tpart;        // [transpose_part_rows(T), 3hl] column partials of dqkv
   size_t gemm_bytes, col_bytes, total;
@@ -233,6 +237,10 @@ AttnPlan plan_attn(const Dims& dm, void* ws, bool bwd) {
   const long long B = dm.T;
   const size_t split = attn_split_bytes(dt, (int)dm.d, dm.T, dm.hl);
   pl.split = split ? bp.take(split) : nullptr;
+  if (!bwd) {
+    const size_t fp = attn_fwd_part_bytes(dt, (int)dm.d, (int)dm.batch, (int)dm.seq, (int)dm.nl);
+    pl.fwd_part = fp ? bp.take(fp) : nullptr;
+  }
   size_t g = max3(gemm_workspace_bytes(dt, (int)B, (int)(3 * dm.hl), (int)dm.h),
                   gemm_workspace_bytes(dt, (int)B, (int)dm.h, (int)dm.hl), 0);
   if (bwd) {
@@ -463,7 +471,7 @@ tp_status attn_fwd_impl(const tp_shape* shape, const tp_dropout* dr, uint16_t* m
   AttnDesc a;
   a.batch = shape->batch; a.seq = shape->seq; a.n_local = (int)dm.nl; a.head_dim = (int)dm.d;
   a.head0 = shape->tp_rank * (int)dm.nl; a.n_heads = shape->n_heads; a.alibi = shape->alibi;
-  a.qkv = qkv_i; a.ctx = ctx_i; a.lse = lse_i; a.split = pl.split;
+  a.qkv = qkv_i; a.ctx = ctx_i; a.lse = lse_i; a.split = pl.split; a.fwd_part = (float*)pl.fwd_part;
   if (dr) {
     a.mask = mask; a.drop_p = dr->p; a.seed = dr->seed; a.offset = dr->offset;
   }
