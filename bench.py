@@ -71,12 +71,30 @@ def wide_mn(step, w):
             "fc1_wgrad": (h, fl), "qkv_wgrad": (h, 3 * hl)}.get(step)
 
 
+# Forward products with a 256x320-tile kernel (GEMM2, output projection), with
+# (M, N, K): taken when N is
+# a multiple of 320, K of 64, and the tiles run in data-parallel rounds (they
+# fill >= 90% of the CUs' last round).
+def fwd_mnk(step, w):
+    T, h, hl, fl = w.tokens, w.hidden, w.h_local, w.ffn_local
+    return {"fc2": (T, h, fl), "out_proj": (T, h, hl)}.get(step)
+
+
 def kernel_of(step, w, ncu) -> str:
     """Name of the kernel the library launches for a step's product."""
     base = KERNEL_OF_STEP[step]
+    if w.dtype != "bf16":
+        return base
+    ncu = min(ncu, 256)
     mn = wide_mn(step, w)
-    if mn and w.dtype == "bf16" and mn[1] % 320 == 0 and ((mn[0] + 255) // 256) * (mn[1] // 320) >= min(ncu, 256):
+    if mn and mn[1] % 320 == 0 and ((mn[0] + 255) // 256) * (mn[1] // 320) >= ncu:
         return base + "_n320"
+    mnk = fwd_mnk(step, w)
+    if mnk and mnk[1] % 320 == 0 and mnk[2] % 64 == 0:
+        tiles = ((mnk[0] + 255) // 256) * (mnk[1] // 320)
+        rounds = (tiles + ncu - 1) // ncu
+        if tiles >= 0.9 * rounds * ncu or mnk[2] // 64 < 8:
+            return base + "_n320"
     return base
 
 

@@ -7,8 +7,10 @@
 // accumulators, two waves per SIMD, so one wave's barrier and load waits are
 // covered by the other's MFMAs, and twice as many loads are in flight per CU).
 // Products with a k-inner B may take a 256x320 tile instead (8 waves, 4x2,
-// 64x160 each, 160 accumulators). K advances 64 at a time through two LDS
-// stages (2 x 64 KiB, or 2 x 72 KiB for the 320-wide tile).
+// 64x160 each, 160 accumulators); GEMM2 and the output projection (k-outer
+// B) take a 256x320 tile on v_mfma_f32_16x16x32_bf16 (8 waves, 2x4, 128x80
+// each) when its tiles run in whole data-parallel rounds. K advances 64 at a time
+// through two LDS stages (2 x 64 KiB, or 2 x 72 KiB for the 320-wide tiles).
 //
 // Global -> LDS: buffer loads that write LDS directly (16 bytes per lane; one
 // instruction fills 1 KiB in lane order), so no VGPRs stage the tiles. Each
@@ -679,6 +681,174 @@ __device__ __forceinline__ void fixup_body(const KParams& p, int first_tile) {
   epilogue_rows<NW, BNV, EPI>(p, tm, tn, i, acc);
 }
 
+// ---- 256x320 tiles for the forward products (k-outer B) ----------------------
+// 8 waves, 2 along m x 4 along n (128 x 80 each) on v_mfma_f32_16x16x32_bf16:
+// each wave reads its A rows (k-inner, the panel above) through ds_read_b128
+// and its 80 B columns (k-outer: the weight) through the transposing reads,
+// so the weight goes through the transposing reads twice per k-step (the 4x2
+// layout of the 32x32 tile needs four). The B stage is [64 k-rows][40 chunks]
+// (640 bytes per k-row); logical chunk lc of k-row kr sits at physical chunk
+// 8(lc/8) + ((lc%8) ^ 2((kr + kr/8) % 4)), so the four k-rows one 16-lane group
+// of a transposing read touches land in four different 32-byte bank groups
+// (and two such groups served together differ in k-row parity). Operands are
+// swapped in the MFMA as in the 32x32 kernels: each lane owns one m and four
+// consecutive n of a 16x16 block. Data-parallel plans only (N a multiple of
+// 320, K of 64, whole rounds of tiles); other shapes take the 256-wide tile.
+struct PanelB320 { const bf16* base; uint32_t nrec, kstep; uint32_t voff[5]; };
+__device__ __forceinline__ int b320_swz(int kr) { return 2 * ((kr + (kr >> 3)) & 3); }
+// physical chunk q of the stage (64 k-rows x 40 chunks) holds logical chunk lc of k-row kr
+__device__ __forceinline__ PanelB320 panel_b320(const bf16* B, long ld, int N, int K, int n0, int wave, int lane) {
+  PanelB320 pn;
+  pn.base = uni_ptr(B + n0);
+  pn.nrec = uni((uint32_t)(((long)K * ld - n0) * 2));
+  pn.kstep = uni((uint32_t)(BKK * ld * 2));
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int q = 64 * (5 * wave + i) + lane;
+    const int kr = q / 40, pc = q - kr * 40;
+    const int lc = 8 * (pc >> 3) + ((pc & 7) ^ b320_swz(kr));
+    pn.voff[i] = (n0 + 8 * lc < N) ? (uint32_t)(((long)kr * ld + 8 * lc) * 2) : pn.nrec;
+  }
+  return pn;
+}
+__device__ __forceinline__ void issue_b320(const PanelB320& pn, int kt, bf16* dst, int wave) {
+  const int soff = (int)uni((uint32_t)kt * pn.kstep);
+  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)pn.base, (short)0, (int)pn.nrec, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    bf16* blk = dst + (5 * wave + i) * 512;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)blk, 16, pn.voff[i], soff, 0, 0);
+  }
+}
+
+// One k-step: wait for this wave's loads, barrier, issue the next k-step's
+// loads, then two 32-deep sub-steps: the wave's five B fragments (two
+// transposing reads each), and for each of its eight 16-row A blocks one
+// ds_read_b128 and five MFMAs.
+__device__ __forceinline__ void fwd320_kstep(const KParams& p, const Panel<4>& pa, const PanelB320& pb, int kt,
+                                             const bf16* __restrict__ a, const bf16* __restrict__ b,
+                                             bf16* __restrict__ na, bf16* __restrict__ nb, int wave, int lane,
+                                             int aoff0, int abase, const int (&boff)[5], f32x4 (&acc)[8][5]) {
+  wait_vmem();
+  __syncthreads();
+  issue_panel<4, true, false>(pa, kt + 1, p.K, na, wave, lane);
+  issue_b320(pb, kt + 1, nb, wave);
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    bf16x8 bfr[5];
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const char* bb = (const char*)b + boff[j];
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(bb + (32 * kk) * 640));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(bb + (32 * kk + 4) * 640));
+      typedef short i16x8 __attribute__((ext_vector_type(8)));
+      const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      bfr[j] = __builtin_bit_cast(bf16x8, v);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int ch = abase ^ (4 * kk) ^ (2 * (i & 3));
+      const bf16x8 af = *(const bf16x8*)((const char*)a + aoff0 + 2048 * i + (ch << 4));
+#pragma unroll
+      for (int j = 0; j < 5; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af, acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
+// bf16 output (EPI_STORE, EPI_BIAS) through a row-major LDS image, two passes
+// of 128 rows (one per wave row), chunk c of image row r at (c + r) mod 40.
+template <int EPI>
+__device__ __forceinline__ void fwd320_epilogue(const KParams& p, int tm, int tn, const f32x4 (&acc)[8][5], bf16* smem) {
+  static_assert(EPI == EPI_STORE || EPI == EPI_BIAS, "bf16 single-output epilogues");
+  constexpr int RB = 640, NCH = 40, PR = 128, ITERS = PR * NCH / 512;
+  typedef __attribute__((address_space(3))) char lds_char;
+  lds_char* img = (lds_char*)smem;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = (int)uni((uint32_t)(tid >> 6));
+  const int wm = wave >> 2, wn = wave & 3, l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps) {
+    if (wm == ps) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const unsigned rl = (unsigned)(16 * i + l16);
+#pragma unroll
+        for (int j = 0; j < 5; ++j) {
+          const int nt = wn * 80 + 16 * j + 4 * g, n = tn * 320 + nt;
+          float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+          if (EPI == EPI_BIAS && n < p.N) {
+            const bf16x4 bb = *(const bf16x4*)(p.bias + n);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += (float)bb[e];
+          }
+          const unsigned c = (unsigned)(nt >> 3), pc = (c + rl) % NCH;
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
+          *(__attribute__((address_space(3))) bf16x4*)(img + rl * RB + pc * 16 + (nt * 2) % 16) = o;
+        }
+      }
+    }
+    lds_only_barrier();
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const unsigned lin = (unsigned)(it * 512 + tid), rl = lin / NCH, c = lin - rl * NCH;
+      const u32x4 v = *(__attribute__((address_space(3))) const u32x4*)(img + rl * RB + ((c + rl) % NCH) * 16);
+      const int gm = tm * BM + ps * PR + (int)rl, gn = tn * 320 + (int)c * 8;
+      if (gm < p.M && gn < p.N) *(u32x4*)((char*)p.C + ((long)gm * p.ldc + gn) * 2) = v;
+    }
+    lds_only_barrier();  // the next pass (or the next tile's loads) overwrites the image
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ void fwd320_body(const KParams& p, bf16* smem) {
+  const int lw = logical_wg(blockIdx.x, p.grid);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = (int)uni((uint32_t)(tid >> 6));
+  const int wm = wave >> 2, wn = wave & 3, l16 = lane & 15, g = lane >> 4;
+  // A fragment of block i, sub-step kk: row wm*128 + 16i + l16, k chunk 4kk + g,
+  // stored at chunk (4kk + g) ^ swz(row) = abase ^ 4kk ^ 2(i & 3) (the k-inner
+  // swizzle (r ^ r>>3) & 7 restricted to these rows)
+  const int aoff0 = (wm * 128 + l16) * 128;
+  const int abase = g ^ ((l16 & 7) ^ (l16 >> 3));
+  // B fragment of block j: this lane addresses k-row 8g + r' (+ 32kk, + 4 for
+  // the second read) and column quad c' = l16 & 3, i.e. logical chunk
+  // lc = wn*10 + 2j + c'/2 at physical 8(lc/8) + ((lc%8) ^ f), f = b320_swz of
+  // that k-row = 2((r' + g) % 4) for every kk and read
+  const int rp = l16 >> 2, cq = l16 & 3, f = 2 * ((rp + g) & 3);
+  for (int r = 0; r < p.dp_rounds; ++r) {
+    const int t = r * p.grid + lw;
+    int tm, tn;
+    tile_coords(p, t, tm, tn);
+    f32x4 acc[8][5];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 5; ++j) acc[i][j] = f32x4{};
+    const Panel<4> pa = panel_kinner<4, BM>(p.A, p.lda, p.M, tm * BM, wave, lane);
+    const PanelB320 pb = panel_b320(p.B, p.ldb, p.N, p.K, tn * 320, wave, lane);
+    issue_panel<4, true, false>(pa, 0, p.K, smem, wave, lane);
+    issue_b320(pb, 0, smem + 2 * BM * BKK, wave);
+    int boff[5];
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const int lc = wn * 10 + 2 * j + (cq >> 1);
+      boff[j] = (8 * g + rp) * 640 + (8 * (lc >> 3) + ((lc & 7) ^ f)) * 16 + 8 * (cq & 1);
+    }
+    int cur = 0;
+    for (int kt = 0; kt < p.iters; ++kt) {
+      fwd320_kstep(p, pa, pb, kt, smem + cur * BM * BKK, smem + 2 * BM * BKK + cur * 320 * BKK,
+                       smem + (cur ^ 1) * BM * BKK, smem + 2 * BM * BKK + (cur ^ 1) * 320 * BKK, wave, lane, aoff0,
+                       abase, boff, acc);
+      cur ^= 1;
+    }
+    wait_vmem();
+    __syncthreads();
+    fwd320_epilogue<EPI>(p, tm, tn, acc, smem);
+  }
+}
 }  // namespace
 
 // One kernel (and its stream-K fix-up kernel) per product of the layer, so
@@ -727,6 +897,18 @@ TP_GEMM_KERNELS(gemm_fc1_wgrad, 8, 256, false, true, EPI_STORE)
 TP_GEMM_KERNELS(gemm_qkv_wgrad, 8, 256, false, true, EPI_STORE)
 TP_GEMM_KERNELS(gemm_fc1_wgrad_n320, 8, 320, false, true, EPI_STORE)
 TP_GEMM_KERNELS(gemm_qkv_wgrad_n320, 8, 320, false, true, EPI_STORE)
+// forward products with a plain bf16 output on 256x320 tiles (16x16x32
+// MFMAs, data-parallel plans only, so no fix-up kernel). GEMM1 (bias + GeLU,
+// two outputs) keeps the 256-wide tile: on that tile its step time was 30 us
+// longer although the kernel alone ran 3% faster.
+#define TP_GEMM_FWD320(NAME, EV)                                                                \
+  __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void NAME(KParams p) { \
+    __shared__ __attribute__((aligned(16))) bf16 smem[2 * (BM + BN_MAX) * BKK];                 \
+    fwd320_body<EV>(p, smem);                                                                   \
+  }
+TP_GEMM_FWD320(gemm_out_proj_n320, EPI_STORE)
+TP_GEMM_FWD320(gemm_fc2_n320, EPI_STORE)
+#undef TP_GEMM_FWD320
 // vocabulary-parallel output layer: logits = X W_i^T (the table slice W_i
 // [V/p, h] is k-inner), dX = dlogits W_i, dW_i = dlogits^T X
 TP_GEMM_KERNELS(gemm_logits, 8, 256, true, true, EPI_STORE)
@@ -814,7 +996,7 @@ size_t gemm_mfma_workspace_bytes(int M, int N, int K) {
 hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStream_t stream) {
   typedef void (*MainK)(KParams);
   typedef void (*FixK)(KParams, int);
-  MainK mk = nullptr, mkw = nullptr;
+  MainK mk = nullptr, mkw = nullptr, mkf = nullptr;  // mkf: forward product on 256x320 tiles
   FixK fk = nullptr, fkw = nullptr;
   bool ak = true, bk = false;
   int ep = EPI_STORE, nw = 4;
@@ -825,9 +1007,9 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
     bk = BKV; ep = EV; break;
   switch (g.role) {
     TP_ROLE(GR_QKV_PROJ, gemm_qkv_proj, 8, true, false, EPI_BIAS_F32)
-    TP_ROLE(GR_OUT_PROJ, gemm_out_proj, 8, true, false, EPI_STORE)
+    case GR_OUT_PROJ: mk = gemm_out_proj; fk = gemm_out_proj_fixup; mkf = gemm_out_proj_n320; nw = 8; ep = EPI_STORE; break;
     TP_ROLE(GR_FC1, gemm_fc1_bias_gelu, 8, true, false, EPI_BIAS_GELU)
-    TP_ROLE(GR_FC2, gemm_fc2, 8, true, false, EPI_STORE)
+    case GR_FC2: mk = gemm_fc2; fk = gemm_fc2_fixup; mkf = gemm_fc2_n320; nw = 8; ep = EPI_STORE; break;
     TP_ROLE_W(GR_FC2_DGRAD, gemm_fc2_dgrad_gelu, 8, true, true, EPI_DGELU)
     TP_ROLE_W(GR_FC1_DGRAD, gemm_fc1_dgrad, 8, true, true, EPI_STORE)
     TP_ROLE_W(GR_OUT_DGRAD, gemm_out_dgrad, 8, true, true, EPI_STORE)
@@ -844,9 +1026,32 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
 #undef TP_ROLE
 #undef TP_ROLE_W
   if (g.a_kmajor != ak || g.b_kmajor != bk || g.epi != ep) return hipErrorInvalidValue;
+  const int ncu = device_cus();
+  // forward products: 256x320 tiles when N is a whole number of them, K of
+  // k-steps, and the tiles run in data-parallel rounds (no k-split tail)
+  if (mkf != nullptr && g.N % BN_MAX == 0 && g.K % BKK == 0) {
+    const int tiles = ((g.M + BM - 1) / BM) * (g.N / BN_MAX);
+    const Plan pl = make_plan(tiles, g.K / BKK, ncu);
+    if (pl.splits == 1 && pl.sk_total == 0) {
+      KParams p{};
+      p.A = (const bf16*)g.A; p.B = (const bf16*)g.B;
+      p.lda = g.lda; p.ldb = g.ldb;
+      p.M = g.M; p.N = g.N; p.K = g.K;
+      p.tiles_m = (g.M + BM - 1) / BM;
+      p.tiles_n = g.N / BN_MAX;
+      p.iters = g.K / BKK;
+      p.epi = g.epi;
+      p.C = (bf16*)g.C; p.ldc = g.ldc;
+      p.C2 = (bf16*)g.C2; p.ldc2 = g.ldc2;
+      p.bias = (const bf16*)g.bias;
+      p.grid = pl.grid; p.dp_rounds = pl.dp_rounds;
+      p.splits = 1;
+      hipLaunchKernelGGL(mkf, dim3(pl.grid), dim3(512), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
   // the wide tile when N is a whole number of them and they fill the CUs at
   // least once (with fewer tiles the k-split tail is better balanced at 256)
-  const int ncu = device_cus();
   const bool wide = mkw != nullptr && g.N % BN_MAX == 0 &&
                     (long long)((g.M + BM - 1) / BM) * (g.N / BN_MAX) >= (ncu < GMAX ? ncu : GMAX);
   const int bn = wide ? BN_MAX : 256;

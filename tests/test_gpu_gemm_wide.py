@@ -8,6 +8,9 @@ partial last row of tiles) and a stream-K tail:
   * h = 9600, f = 3200: the GEMM1 input gradient runs 320 wide (N = h).
 The GEMM1 weight gradient (X^T times a transposed dPre copy) runs 320 wide in
 both shapes, with K = 2100 tokens (a partial last k-step).
+  * h = f = 8960: the forward GEMM2 runs its 256x320 tile (16x16x32 MFMAs):
+    9 x 28 = 252 tiles, one data-parallel round on 256 CUs, the last row of
+    tiles 52 rows.
 The oracle recomputes column sub-shards and sampled token rows exactly."""
 import numpy as np
 import pytest
@@ -44,7 +47,8 @@ def samples(n, k, rng):
     return np.unique(np.concatenate([[0, 1, n // 2, n - 1], rng.choice(n, k, replace=False)]))
 
 
-@pytest.mark.parametrize("h,ffn", [(3200, 9600), (9600, 3200)], ids=["fc2_dgrad_wide", "fc1_dgrad_wide"])
+@pytest.mark.parametrize("h,ffn", [(3200, 9600), (9600, 3200), (8960, 8960)],
+                         ids=["fc2_dgrad_wide", "fc1_dgrad_wide", "fwd_wide"])
 def test_mlp_wide_tiles_ragged_tokens(h, ffn):
     w = workload(h, ffn)
     print(f"\n  [wide MLP] T={TOKENS} h={h} f={ffn}", flush=True)
