@@ -71,13 +71,13 @@ def wide_mn(step, w):
             "fc1_wgrad": (h, fl), "qkv_wgrad": (h, 3 * hl)}.get(step)
 
 
-# Forward products with a 256x320-tile kernel (GEMM2, output projection), with
-# (M, N, K): taken when N is
-# a multiple of 320, K of 64, and the tiles run in data-parallel rounds (they
-# fill >= 90% of the CUs' last round).
+# k-outer-B products with a 256x320-tile kernel (GEMM2, output projection,
+# GEMM2 weight gradient), with (M, N, K): taken when N is a multiple of 320
+# and the tiles run in data-parallel rounds (they fill >= 90% of the CUs'
+# last round).
 def fwd_mnk(step, w):
     T, h, hl, fl = w.tokens, w.hidden, w.h_local, w.ffn_local
-    return {"fc2": (T, h, fl), "out_proj": (T, h, hl)}.get(step)
+    return {"fc2": (T, h, fl), "out_proj": (T, h, hl), "fc2_wgrad": (fl, h, T)}.get(step)
 
 
 def kernel_of(step, w, ncu) -> str:
@@ -90,10 +90,10 @@ def kernel_of(step, w, ncu) -> str:
     if mn and mn[1] % 320 == 0 and ((mn[0] + 255) // 256) * (mn[1] // 320) >= ncu:
         return base + "_n320"
     mnk = fwd_mnk(step, w)
-    if mnk and mnk[1] % 320 == 0 and mnk[2] % 64 == 0:
+    if mnk and mnk[1] % 320 == 0 and mnk[2] > 0:
         tiles = ((mnk[0] + 255) // 256) * (mnk[1] // 320)
         rounds = (tiles + ncu - 1) // ncu
-        if tiles >= 0.9 * rounds * ncu or mnk[2] // 64 < 8:
+        if tiles >= 0.9 * rounds * ncu or (mnk[2] + 63) // 64 < 8:
             return base + "_n320"
     return base
 

@@ -36,6 +36,8 @@
 // split evenly over all workgroups, each split tile's fp32 partials go to the
 // workspace and a second kernel sums them in a fixed order and applies the
 // epilogue (no inter-workgroup waiting inside a kernel).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -725,13 +727,14 @@ __device__ __forceinline__ void issue_b320(const PanelB320& pn, int kt, bf16* ds
 // loads, then two 32-deep sub-steps: the wave's five B fragments (two
 // transposing reads each), and for each of its eight 16-row A blocks one
 // ds_read_b128 and five MFMAs.
+template <bool TAIL>
 __device__ __forceinline__ void fwd320_kstep(const KParams& p, const Panel<4>& pa, const PanelB320& pb, int kt,
                                              const bf16* __restrict__ a, const bf16* __restrict__ b,
                                              bf16* __restrict__ na, bf16* __restrict__ nb, int wave, int lane,
                                              int aoff0, int abase, const int (&boff)[5], f32x4 (&acc)[8][5]) {
   wait_vmem();
   __syncthreads();
-  issue_panel<4, true, false>(pa, kt + 1, p.K, na, wave, lane);
+  issue_panel<4, true, TAIL>(pa, kt + 1, p.K, na, wave, lane);  // B rows past K read zeros
   issue_b320(pb, kt + 1, nb, wave);
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
@@ -829,7 +832,7 @@ __device__ __forceinline__ void fwd320_body(const KParams& p, bf16* smem) {
       for (int j = 0; j < 5; ++j) acc[i][j] = f32x4{};
     const Panel<4> pa = panel_kinner<4, BM>(p.A, p.lda, p.M, tm * BM, wave, lane);
     const PanelB320 pb = panel_b320(p.B, p.ldb, p.N, p.K, tn * 320, wave, lane);
-    issue_panel<4, true, false>(pa, 0, p.K, smem, wave, lane);
+    issue_panel<4, true, true>(pa, 0, p.K, smem, wave, lane);
     issue_b320(pb, 0, smem + 2 * BM * BKK, wave);
     int boff[5];
 #pragma unroll
@@ -837,13 +840,21 @@ __device__ __forceinline__ void fwd320_body(const KParams& p, bf16* smem) {
       const int lc = wn * 10 + 2 * j + (cq >> 1);
       boff[j] = (8 * g + rp) * 640 + (8 * (lc >> 3) + ((lc & 7) ^ f)) * 16 + 8 * (cq & 1);
     }
-    int cur = 0;
-    for (int kt = 0; kt < p.iters; ++kt) {
-      fwd320_kstep(p, pa, pb, kt, smem + cur * BM * BKK, smem + 2 * BM * BKK + cur * 320 * BKK,
-                       smem + (cur ^ 1) * BM * BKK, smem + 2 * BM * BKK + (cur ^ 1) * 320 * BKK, wave, lane, aoff0,
-                       abase, boff, acc);
+    // only the k-step that loads a partial last k-step (K not a multiple of
+    // 64) checks the A chunks against K: the loop is split around it
+    const int kload = p.K % BKK ? p.iters - 2 : -1;  // k-step whose loads are the partial one
+    int cur = 0, kt = 0;
+    auto step = [&](auto tail) {
+      fwd320_kstep<decltype(tail)::value>(p, pa, pb, kt, smem + cur * BM * BKK, smem + 2 * BM * BKK + cur * 320 * BKK,
+                                          smem + (cur ^ 1) * BM * BKK, smem + 2 * BM * BKK + (cur ^ 1) * 320 * BKK,
+                                          wave, lane, aoff0, abase, boff, acc);
       cur ^= 1;
-    }
+      ++kt;
+    };
+    const int kmid = kload >= 0 ? kload : p.iters;
+    while (kt < kmid) step(std::false_type{});
+    if (kt < p.iters && kt == kload) step(std::true_type{});
+    while (kt < p.iters) step(std::false_type{});
     wait_vmem();
     __syncthreads();
     fwd320_epilogue<EPI>(p, tm, tn, acc, smem);
@@ -908,6 +919,7 @@ TP_GEMM_KERNELS(gemm_qkv_wgrad_n320, 8, 320, false, true, EPI_STORE)
   }
 TP_GEMM_FWD320(gemm_out_proj_n320, EPI_STORE)
 TP_GEMM_FWD320(gemm_fc2_n320, EPI_STORE)
+TP_GEMM_FWD320(gemm_fc2_wgrad_n320, EPI_STORE)
 #undef TP_GEMM_FWD320
 // vocabulary-parallel output layer: logits = X W_i^T (the table slice W_i
 // [V/p, h] is k-inner), dX = dlogits W_i, dW_i = dlogits^T X
@@ -1014,7 +1026,8 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
     TP_ROLE_W(GR_FC1_DGRAD, gemm_fc1_dgrad, 8, true, true, EPI_STORE)
     TP_ROLE_W(GR_OUT_DGRAD, gemm_out_dgrad, 8, true, true, EPI_STORE)
     TP_ROLE_W(GR_QKV_DGRAD, gemm_qkv_dgrad, 8, true, true, EPI_STORE)
-    TP_ROLE(GR_FC2_WGRAD, gemm_fc2_wgrad, 8, true, false, EPI_STORE)
+    case GR_FC2_WGRAD: mk = gemm_fc2_wgrad; fk = gemm_fc2_wgrad_fixup; mkf = gemm_fc2_wgrad_n320; nw = 8; ep = EPI_STORE;
+      break;
     TP_ROLE_W(GR_FC1_WGRAD, gemm_fc1_wgrad, 8, false, true, EPI_STORE)
     TP_ROLE(GR_OUT_WGRAD, gemm_out_wgrad, 8, true, false, EPI_STORE)
     TP_ROLE_W(GR_QKV_WGRAD, gemm_qkv_wgrad, 8, false, true, EPI_STORE)
@@ -1027,11 +1040,12 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
 #undef TP_ROLE_W
   if (g.a_kmajor != ak || g.b_kmajor != bk || g.epi != ep) return hipErrorInvalidValue;
   const int ncu = device_cus();
-  // forward products: 256x320 tiles when N is a whole number of them, K of
-  // k-steps, and the tiles run in data-parallel rounds (no k-split tail)
-  if (mkf != nullptr && g.N % BN_MAX == 0 && g.K % BKK == 0) {
+  // k-outer-B products (GEMM2, output projection, GEMM2 weight gradient):
+  // 256x320 tiles when N is a whole number of them and the tiles run in
+  // data-parallel rounds (no k-split tail)
+  if (mkf != nullptr && g.N % BN_MAX == 0) {
     const int tiles = ((g.M + BM - 1) / BM) * (g.N / BN_MAX);
-    const Plan pl = make_plan(tiles, g.K / BKK, ncu);
+    const Plan pl = make_plan(tiles, (g.K + BKK - 1) / BKK, ncu);
     if (pl.splits == 1 && pl.sk_total == 0) {
       KParams p{};
       p.A = (const bf16*)g.A; p.B = (const bf16*)g.B;
@@ -1039,7 +1053,7 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
       p.M = g.M; p.N = g.N; p.K = g.K;
       p.tiles_m = (g.M + BM - 1) / BM;
       p.tiles_n = g.N / BN_MAX;
-      p.iters = g.K / BKK;
+      p.iters = (g.K + BKK - 1) / BKK;
       p.epi = g.epi;
       p.C = (bf16*)g.C; p.ldc = g.ldc;
       p.C2 = (bf16*)g.C2; p.ldc2 = g.ldc2;

@@ -10,7 +10,8 @@ The GEMM1 weight gradient (X^T times a transposed dPre copy) runs 320 wide in
 both shapes, with K = 2100 tokens (a partial last k-step).
   * h = f = 8960: the forward GEMM2 runs its 256x320 tile (16x16x32 MFMAs):
     9 x 28 = 252 tiles, one data-parallel round on 256 CUs, the last row of
-    tiles 52 rows.
+    tiles 52 rows; so does the GEMM2 weight gradient (35 x 28 tiles in four
+    rounds, K = 2100: a partial last k-step).
 The oracle recomputes column sub-shards and sampled token rows exactly."""
 import numpy as np
 import pytest
