@@ -85,6 +85,8 @@ def kernel_of(step, w, ncu) -> str:
     base = KERNEL_OF_STEP[step]
     if w.dtype != "bf16":
         return base
+    if step.endswith("_wgrad") and w.hidden < 8192:  # no transposed copy: both operands k-outer
+        return base + "_ko"
     ncu = min(ncu, 256)
     mn = wide_mn(step, w)
     if mn and mn[1] % 320 == 0 and ((mn[0] + 255) // 256) * (mn[1] // 320) >= ncu:

@@ -908,6 +908,13 @@ TP_GEMM_KERNELS(gemm_fc1_wgrad, 8, 256, false, true, EPI_STORE)
 TP_GEMM_KERNELS(gemm_qkv_wgrad, 8, 256, false, true, EPI_STORE)
 TP_GEMM_KERNELS(gemm_fc1_wgrad_n320, 8, 320, false, true, EPI_STORE)
 TP_GEMM_KERNELS(gemm_qkv_wgrad_n320, 8, 320, false, true, EPI_STORE)
+// weight gradients of narrow layers, both operands read as stored (k-outer,
+// 4 waves: with both through the transposing loads 8 waves measured slower);
+// there a transposed copy costs more than the product gains
+TP_GEMM_KERNELS(gemm_fc2_wgrad_ko, 4, 256, false, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_out_wgrad_ko, 4, 256, false, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_fc1_wgrad_ko, 4, 256, false, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_qkv_wgrad_ko, 4, 256, false, false, EPI_STORE)
 // forward products with a plain bf16 output on 256x320 tiles (16x16x32
 // MFMAs, data-parallel plans only, so no fix-up kernel). GEMM1 (bias + GeLU,
 // two outputs) keeps the 256-wide tile: on that tile its step time was 30 us
@@ -1009,6 +1016,8 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
   typedef void (*MainK)(KParams);
   typedef void (*FixK)(KParams, int);
   MainK mk = nullptr, mkw = nullptr, mkf = nullptr;  // mkf: forward product on 256x320 tiles
+  MainK mko = nullptr;                               // weight gradient with both operands k-outer
+  FixK fko = nullptr;
   FixK fk = nullptr, fkw = nullptr;
   bool ak = true, bk = false;
   int ep = EPI_STORE, nw = 4;
@@ -1027,10 +1036,15 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
     TP_ROLE_W(GR_OUT_DGRAD, gemm_out_dgrad, 8, true, true, EPI_STORE)
     TP_ROLE_W(GR_QKV_DGRAD, gemm_qkv_dgrad, 8, true, true, EPI_STORE)
     case GR_FC2_WGRAD: mk = gemm_fc2_wgrad; fk = gemm_fc2_wgrad_fixup; mkf = gemm_fc2_wgrad_n320; nw = 8; ep = EPI_STORE;
-      break;
-    TP_ROLE_W(GR_FC1_WGRAD, gemm_fc1_wgrad, 8, false, true, EPI_STORE)
-    TP_ROLE(GR_OUT_WGRAD, gemm_out_wgrad, 8, true, false, EPI_STORE)
-    TP_ROLE_W(GR_QKV_WGRAD, gemm_qkv_wgrad, 8, false, true, EPI_STORE)
+      mko = gemm_fc2_wgrad_ko; fko = gemm_fc2_wgrad_ko_fixup; break;
+    case GR_FC1_WGRAD: mk = gemm_fc1_wgrad; fk = gemm_fc1_wgrad_fixup; mkw = gemm_fc1_wgrad_n320;
+      fkw = gemm_fc1_wgrad_n320_fixup; nw = 8; ak = false; bk = true; ep = EPI_STORE;
+      mko = gemm_fc1_wgrad_ko; fko = gemm_fc1_wgrad_ko_fixup; break;
+    case GR_OUT_WGRAD: mk = gemm_out_wgrad; fk = gemm_out_wgrad_fixup; nw = 8; ep = EPI_STORE;
+      mko = gemm_out_wgrad_ko; fko = gemm_out_wgrad_ko_fixup; break;
+    case GR_QKV_WGRAD: mk = gemm_qkv_wgrad; fk = gemm_qkv_wgrad_fixup; mkw = gemm_qkv_wgrad_n320;
+      fkw = gemm_qkv_wgrad_n320_fixup; nw = 8; ak = false; bk = true; ep = EPI_STORE;
+      mko = gemm_qkv_wgrad_ko; fko = gemm_qkv_wgrad_ko_fixup; break;
     TP_ROLE_W(GR_LOGITS, gemm_logits, 8, true, true, EPI_STORE)
     TP_ROLE(GR_LOGITS_DGRAD, gemm_logits_dgrad, 8, true, false, EPI_STORE)
     TP_ROLE(GR_LOGITS_WGRAD, gemm_logits_wgrad, 4, false, false, EPI_STORE)
@@ -1038,6 +1052,9 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
   }
 #undef TP_ROLE
 #undef TP_ROLE_W
+  if (mko != nullptr && !g.a_kmajor && !g.b_kmajor) {  // weight gradient without a transposed copy
+    mk = mko; fk = fko; mkw = nullptr; mkf = nullptr; nw = 4; ak = false; bk = false;
+  }
   if (g.a_kmajor != ak || g.b_kmajor != bk || g.epi != ep) return hipErrorInvalidValue;
   const int ncu = device_cus();
   // k-outer-B products (GEMM2, output projection, GEMM2 weight gradient):

@@ -80,24 +80,36 @@ __global__ __launch_bounds__(256) void colsum_part_vec_kernel(const T* X, int M,
   }
 }
 
-// The R partial rows added in order r = 0, 1, ..; eight rows' loads in
-// flight at a time (rows past R load row R - 1 again, unused). 64 columns per
-// workgroup, so that a few thousand columns still spread over many CUs.
-constexpr int FB = 64;
+// out[n] = sum of the R partial rows part[r][n]. A workgroup takes 32 columns
+// and 8 row groups; group q adds rows q, q + 8, q + 16, ... in that order
+// with eight rows' loads in flight (rows past R load row R - 1 again,
+// unused), and the 8 group sums are added in group order: a fixed order for
+// any R, and R / 8 dependent steps per thread instead of R (thousands of
+// partial rows at 16384 tokens).
+constexpr int FC = 32, FG = 8;
 template <typename T>
-__global__ __launch_bounds__(FB) void colsum_final_kernel(const float* part, int R, int N, T* out) {
-  const int n = blockIdx.x * FB + threadIdx.x;
-  if (n >= N) return;
+__global__ __launch_bounds__(FC * FG) void colsum_final_kernel(const float* part, int R, int N, T* out) {
+  __shared__ float red[FG][FC];
+  const int c = threadIdx.x % FC, q = threadIdx.x / FC;
+  const int n = blockIdx.x * FC + c;
+  const int nn = n < N ? n : N - 1;  // clamped: every thread loads in range
   float s = 0.f;
-  for (int r = 0; r < R; r += 8) {
+  for (int r = q; r < R; r += 8 * FG) {
     float x[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) x[u] = part[(long)min(r + u, R - 1) * N + n];
+    for (int u = 0; u < 8; ++u) x[u] = part[(long)min(r + u * FG, R - 1) * N + nn];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (r + u < R) s += x[u];
+      if (r + u * FG < R) s += x[u];
   }
-  out[n] = from_f<T>(s);
+  red[q][c] = s;
+  __syncthreads();
+  if (q == 0 && n < N) {
+    float t = red[0][c];
+#pragma unroll
+    for (int k = 1; k < FG; ++k) t += red[k][c];
+    out[n] = from_f<T>(t);
+  }
 }
 
 void colsum_split(int M, int N, int& R, int& rows_per) {
@@ -255,11 +267,11 @@ hipError_t transpose_colsum_launch(const void* X, int R, int C, long ldx, void* 
 
 hipError_t colsum_final_launch(int dtype, const float* part, int R, int N, void* out, hipStream_t stream) {
   if (N <= 0) return hipSuccess;
-  const unsigned fblocks = (N + FB - 1) / FB;
+  const unsigned fblocks = (N + FC - 1) / FC;
   if (dtype == DT_BF16)
-    hipLaunchKernelGGL(colsum_final_kernel<bf16>, dim3(fblocks), dim3(FB), 0, stream, part, R, N, (bf16*)out);
+    hipLaunchKernelGGL(colsum_final_kernel<bf16>, dim3(fblocks), dim3(FC * FG), 0, stream, part, R, N, (bf16*)out);
   else
-    hipLaunchKernelGGL(colsum_final_kernel<float>, dim3(fblocks), dim3(FB), 0, stream, part, R, N, (float*)out);
+    hipLaunchKernelGGL(colsum_final_kernel<float>, dim3(fblocks), dim3(FC * FG), 0, stream, part, R, N, (float*)out);
   return hipGetLastError();
 }
 

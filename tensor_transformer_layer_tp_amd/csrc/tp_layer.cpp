@@ -186,9 +186,13 @@ size_t max3(size_t a, size_t b, size_t c) { return a > b ? (a > c ? a : c) : (b 
 // (at least 8), so that every row starts 16-byte aligned.
 long long t_ld(long long T) { return T < 8 ? 8 : (T + 7) / 8 * 8; }
 
-// bf16 weight gradients read one operand as a transposed copy (k = tokens
-// contiguous); the fp32 path reads both as stored.
-bool wgrad_copies(const Dims& dm) { return dm.dtype == DT_BF16; }
+// bf16 weight gradients of wide layers read one operand as a transposed copy
+// (k = tokens contiguous). A weight gradient does h/2 flops per byte of its
+// copied operand (M or N is h), and the copy moves each byte twice: below
+// h = 8192 the copy costs more than the product gains (about 10%), and both
+// operands are read as stored, as on the fp32 path.
+constexpr long long kCopyMinHidden = 8192;
+bool wgrad_copies(const Dims& dm) { return dm.dtype == DT_BF16 && dm.h >= kCopyMinHidden; }
 
 struct MlpPlan {
   void *dpre, *gemm_ws, *col_ws;
