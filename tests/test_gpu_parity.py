@@ -99,6 +99,19 @@ SMALL = [
 ]
 
 
+# Wide layers (hidden >= 8192) give the weight gradients transposed copies of
+# one operand (y^T, dPre^T, ctx^T, dqkv^T, with the bias gradients' column
+# partials); these token counts make the copies mostly padding (T < 8, a
+# ragged 8-row group, a partial 32-row run) and K = T a single partial k-step.
+@pytest.mark.parametrize("batch,seq", [(3, 1), (1, 77)], ids=["T3", "T77"])
+def test_wide_layer_weight_gradient_copies_few_tokens(batch, seq):
+    w = synth.Workload(f"wide_copies_T{batch * seq}", batch=batch, seq=seq, hidden=8192, n_heads=64, head_dim=128,
+                       ffn=8192, tp_size=8, dtype="bf16", alibi=False, bias_std=0.5)
+    inp = synth.draw_shard(w, seed=5)
+    ls = run_shard(w, inp, 5)
+    check_all(ls, oracle_rank(w, inp, 5), "bf16")
+
+
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_small_bf16_shard_matches_oracle(case):
     name, batch, seq, nh, d, tps, rank, alibi = case
@@ -153,10 +166,13 @@ def test_emulated_tp_bf16_equals_unsharded(tps):
 # Edge cases: empty batch, every output written, determinism.
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-def test_empty_batch_gives_zero_weight_grads(dtype):
-    w = synth.Workload("empty", batch=0, seq=64, hidden=256, n_heads=2, head_dim=128, ffn=1024, tp_size=2,
-                       dtype=dtype)
+@pytest.mark.parametrize("dtype,hidden", [("fp32", 256), ("bf16", 256), ("bf16", 8192)],
+                         ids=["fp32", "bf16", "bf16_wide_copies"])
+def test_empty_batch_gives_zero_weight_grads(dtype, hidden):
+    # hidden 8192: the weight gradients' copy path (no copies are made; the
+    # bias-gradient final passes see zero partial rows)
+    w = synth.Workload("empty", batch=0, seq=64, hidden=hidden, n_heads=hidden // 128, head_dim=128, ffn=1024,
+                       tp_size=2, dtype=dtype)
     inp = synth.draw_shard(w, seed=4)
     ls = run_shard(w, inp, 1)
     for k in ("dA", "db1", "dB", "db2", "dWqkv", "dbqkv", "dWo", "dbo"):
