@@ -63,12 +63,24 @@ KERNEL_OF_STEP = {
 }
 
 
-# Steps whose product has a 256x320-tile kernel (suffix _n320), with its (M, N):
-# the library takes it when N is a multiple of 320 and the tiles fill the CUs.
-def wide_mn(step, w):
+# Steps whose product has a 256x320-tile kernel (suffix _n320), with its
+# (M, N, K): the library takes it when N is a multiple of 320 and the tiles
+# fill the CUs, or when their k-split covers every CU exactly.
+def wide_mnk(step, w):
     T, h, hl, fl = w.tokens, w.hidden, w.h_local, w.ffn_local
-    return {"fc2_dgrad": (T, fl), "fc1_dgrad": (T, h), "out_dgrad": (T, hl), "qkv_dgrad": (T, h),
-            "fc1_wgrad": (h, fl), "qkv_wgrad": (h, 3 * hl)}.get(step)
+    return {"fc2_dgrad": (T, fl, h), "fc1_dgrad": (T, h, fl), "out_dgrad": (T, hl, h), "qkv_dgrad": (T, h, 3 * hl),
+            "fc1_wgrad": (h, fl, T), "qkv_wgrad": (h, 3 * hl, T)}.get(step)
+
+
+def exact_split(tiles, iters, ncu) -> bool:
+    """The library's plan for fewer tiles than CUs: a k-split of every tile
+    into sp = min(ncu // tiles, iters // 8) parts; true when those parts cover
+    every CU exactly."""
+    waves = (tiles + ncu - 1) // ncu
+    if iters < 16 or tiles >= ncu or tiles / (waves * ncu) >= 0.9:
+        return False
+    sp = min(ncu // tiles, iters // 8)
+    return sp >= 2 and sp * tiles == ncu
 
 
 # k-outer-B products with a 256x320-tile kernel (GEMM2, output projection,
@@ -88,9 +100,11 @@ def kernel_of(step, w, ncu) -> str:
     if step.endswith("_wgrad") and w.hidden < 8192:  # no transposed copy: both operands k-outer
         return base + "_ko"
     ncu = min(ncu, 256)
-    mn = wide_mn(step, w)
-    if mn and mn[1] % 320 == 0 and ((mn[0] + 255) // 256) * (mn[1] // 320) >= ncu:
-        return base + "_n320"
+    mnk = wide_mnk(step, w)
+    if mnk and mnk[1] % 320 == 0:
+        tiles = ((mnk[0] + 255) // 256) * (mnk[1] // 320)
+        if tiles >= ncu or exact_split(tiles, (mnk[2] + 63) // 64, ncu):
+            return base + "_n320"
     mnk = fwd_mnk(step, w)
     if mnk and mnk[1] % 320 == 0 and mnk[2] > 0:
         tiles = ((mnk[0] + 255) // 256) * (mnk[1] // 320)

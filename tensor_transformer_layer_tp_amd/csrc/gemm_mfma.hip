@@ -1082,9 +1082,15 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
     }
   }
   // the wide tile when N is a whole number of them and they fill the CUs at
-  // least once (with fewer tiles the k-split tail is better balanced at 256)
-  const bool wide = mkw != nullptr && g.N % BN_MAX == 0 &&
-                    (long long)((g.M + BM - 1) / BM) * (g.N / BN_MAX) >= (ncu < GMAX ? ncu : GMAX);
+  // least once, or, fewer, when their k-split covers every CU exactly (with
+  // other counts the k-split tail is better balanced at 256)
+  bool wide = false;
+  if (mkw != nullptr && g.N % BN_MAX == 0) {
+    const int cus = ncu < GMAX ? ncu : GMAX;
+    const int t320 = ((g.M + BM - 1) / BM) * (g.N / BN_MAX);
+    const Plan p320 = make_plan(t320, (g.K + BKK - 1) / BKK, ncu);
+    wide = t320 >= cus || (p320.splits > 1 && p320.dp_rounds == 0 && p320.splits * t320 == cus);
+  }
   const int bn = wide ? BN_MAX : 256;
   if (bn == BN_MAX) { mk = mkw; fk = fkw; }
   const int mi = bn == BN_MAX ? WC<8, BN_MAX>::MI : 4;  // fix-up workgroups per tile
