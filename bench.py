@@ -149,11 +149,7 @@ def cpu_baseline(w, inp, target_s: float, gpu_out=None) -> dict:
     copies, same inputs), also the relative Frobenius error of every output."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    cores = blas_threads()
     f64 = lambda t: t.double().numpy()  # noqa: E731
     X_attn, X_mlp, dO, dZ = f64(inp["X_attn"]), f64(inp["X_mlp"]), f64(inp["dO"]), f64(inp["dZ"])
     n_l, f_l, d = w.heads_local, w.ffn_local, w.head_dim
@@ -402,6 +398,149 @@ def attn_dropout_measure(w, ls, reps: int = 10) -> dict:
     return {"workload": f"{w.name} attention block, bf16, p = 0.1 (Philox4x64-10 keep bits)", **res}
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def cpu_baseline_tiny(reps: int = 100) -> dict:
+    """The fp64 oracle on the tiny fp32 workload (both emulated ranks' shards,
+    fwd + bwd), averaged over `reps` runs."""
+    import oracle
+    import synth
+    w = synth.WORKLOADS["tiny_fp32_tp2"]
+    full = synth.draw_full(w, seed=0)
+    a = {k: v.double().numpy() for k, v in full.items()}
+    shards = []
+    for r in range(w.tp_size):
+        shards.append(dict(Wqkv=oracle.qkv_weight_shard(a["Wqkv"], r, w.tp_size),
+                           bqkv=oracle.qkv_bias_shard(a["bqkv"], r, w.tp_size),
+                           Wo=oracle.row_shard(a["Wo"], r, w.tp_size), A=oracle.column_shard(a["A"], r, w.tp_size),
+                           b1=oracle.column_shard(a["b1"], r, w.tp_size), B=oracle.row_shard(a["B"], r, w.tp_size)))
+
+    def once():
+        for r, sh in enumerate(shards):
+            kw = dict(batch=w.batch, seq=w.seq, n_heads=w.n_heads, tp_size=w.tp_size, tp_rank=r, alibi=w.alibi)
+            oracle.attn_fwd(a["X_attn"], sh["Wqkv"], sh["bqkv"], sh["Wo"], **kw)
+            oracle.attn_bwd(a["X_attn"], sh["Wqkv"], sh["bqkv"], sh["Wo"], a["dO"], **kw)
+            pre, y, _ = oracle.mlp_fwd(a["X_mlp"], sh["A"], sh["b1"], sh["B"])
+            oracle.mlp_bwd(a["X_mlp"], sh["A"], sh["B"], pre, y, a["dZ"])
+
+    once()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        once()
+    t = (time.perf_counter() - t0) / reps
+    fl = w.tp_size * layer_flops(w)
+    return {"workload": w.name, "runs": reps, "avg_s": t, "flops_per_run": fl, "value": fl / t / 1e12,
+            "unit": "TFLOP/s", "sample": f"fp64 NumPy oracle, fwd+bwd of both emulated ranks' shards, mean of {reps} runs"}
+
+
+def time_steps(ls, steps: int, dom_step=None):
+    """Run `steps` layer steps on the library's stream bracketed by events:
+    -> (ms per step, per-step stats, host wall s, dominant-kernel record).
+    With dom_step, every launch sequence of that step is also bracketed by
+    events (a separate pass: those events are not in the headline timing)."""
+    import torch
+    import tensor_transformer_layer_tp_amd as tp
+    if dom_step is not None:
+        tp.tp_profile_enable(1 << tp.STEPS[dom_step])
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps - 1)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for k in range(steps):
+        ls.step()
+        (ev[k] if k < steps - 1 else e1).record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = e0.elapsed_time(e1) / steps
+    marks = [e0, *ev, e1]
+    per_step = sorted(marks[k].elapsed_time(marks[k + 1]) for k in range(steps))
+    stats = {"median": round(per_step[len(per_step) // 2], 4), "min": round(per_step[0], 4),
+             "p90": round(per_step[min(len(per_step) - 1, int(math.ceil(0.9 * len(per_step))) - 1)], 4)}
+    dom = None
+    if dom_step is not None:
+        n, ms = tp.tp_profile_collect(tp.STEPS[dom_step])
+        tp.tp_profile_enable(0)
+        dom = (n, ms / max(n, 1))
+    return ms_step, stats, wall, dom
+
+
+def breakdown_pass(ls, reps: int = 3) -> dict:
+    """Per-step GPU time (ms per step) from a pass with events around every step."""
+    import torch
+    import tensor_transformer_layer_tp_amd as tp
+    tp.tp_profile_enable(sum(1 << v for v in tp.STEPS.values()))
+    for _ in range(reps):
+        ls.step()
+    torch.cuda.synchronize()
+    out = {}
+    for name, sid in tp.STEPS.items():
+        n, ms = tp.tp_profile_collect(sid)
+        if n:
+            out[name] = ms / reps
+    tp.tp_profile_enable(0)
+    return out
+
+
+def other_workload(name: str, steps: int, warmup: int) -> dict:
+    """One more configuration, timed like the headline one (reported under
+    `configs`, not in `value`)."""
+    import torch
+    import synth
+    import tensor_transformer_layer_tp_amd as tp
+    from tensor_transformer_layer_tp_amd.shard import INPUTS, LayerShard
+    w = synth.WORKLOADS[name]
+    log(f"workload {name}: drawing seeded inputs")
+    inp = synth.draw_shard(w, seed=0)
+    shape = tp.TpShape.make(batch=w.batch, seq=w.seq, hidden=w.hidden, ffn=w.ffn, n_heads=w.n_heads,
+                            head_dim=w.head_dim, tp_rank=0, tp_size=w.tp_size, dtype=w.dtype, alibi=int(w.alibi))
+    ls = LayerShard(shape, {k: inp[k].cuda() for k in INPUTS})
+    del inp
+    for _ in range(warmup):
+        ls.step()
+    torch.cuda.synchronize()
+    bd = breakdown_pass(ls)
+    ms, stats, _, _ = time_steps(ls, steps)
+    F = layer_flops(w)
+    tf = F / (ms / 1e3) / 1e12
+    sf = step_flops(w)
+    tot = sum(bd.values())
+    attn = bd.get("attn_fwd", 0.0) + bd.get("attn_bwd", 0.0)
+    log(f"  {name}: {ms:.3f} ms/step, {tf:.1f} TFLOP/s ({100 * tf / PEAK_BF16_TFLOPS:.1f}% of peak), "
+        f"attention {100 * attn / tot:.1f}% of the step")
+    del ls
+    torch.cuda.empty_cache()
+    return {"ms_per_step": round(ms, 4), "step_ms": stats, "tflops": round(tf, 2),
+            "pct_of_mfma_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2), "flops_per_step": F,
+            "attention_share_of_step": round(attn / tot, 4),
+            "breakdown_ms": {k: round(v, 4) for k, v in bd.items()},
+            "breakdown_tflops": {k: round(sf[k] / (v / 1e3) / 1e12, 1) for k, v in bd.items() if sf.get(k)},
+            "config": {"batch": w.batch, "seq_len": w.seq, "hidden": w.hidden,
+                       "heads": f"{w.heads_local} of {w.n_heads}", "head_dim": w.head_dim,
+                       "ffn_shard": f"{w.ffn_local} of {w.ffn}", "tp_rank": 0, "tp_size": w.tp_size,
+                       "alibi": w.alibi}}
+
+
+OTHER_WORKLOADS = ("gpt2_1p2b_tp1", "gpt_8p3b_tp8", "bloom_176b_tp8")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -412,6 +551,7 @@ def main():
     ap.add_argument("--no-ln", action="store_true", help="skip the residual + LayerNorm measurement")
     ap.add_argument("--no-vocab", action="store_true", help="skip the vocabulary-parallel output-layer measurement")
     ap.add_argument("--no-dropout", action="store_true", help="skip the attention-dropout measurement")
+    ap.add_argument("--no-configs", action="store_true", help="skip timing the other bf16 workloads")
     ap.add_argument("--cpu-target-s", type=float, default=15.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run device-to-device copies of this many MiB (calibrates byte counters)")
@@ -455,59 +595,51 @@ def main():
 
     # per-step breakdown (separate pass, every step bracketed by events)
     sf = step_flops(w)
-    tp.tp_profile_enable(sum(1 << v for v in tp.STEPS.values()))
-    nb = 3
-    for _ in range(nb):
-        ls.step()
-    torch.cuda.synchronize()
-    breakdown = {}
-    for name, sid in tp.STEPS.items():
-        n, ms = tp.tp_profile_collect(sid)
-        if n:
-            breakdown[name] = ms / nb
-    tp.tp_profile_enable(0)
+    breakdown = breakdown_pass(ls)
     tot = sum(breakdown.values())
     for name, ms in sorted(breakdown.items(), key=lambda kv: -kv[1]):
         tf = sf[name] / (ms / 1e3) / 1e12 if ms > 0 else 0.0
         log(f"  {name:11s} {ms:8.3f} ms  {100 * ms / tot:5.1f}%  {tf:7.1f} TFLOP/s  {100 * tf / PEAK_BF16_TFLOPS:5.1f}% peak")
     gemm_steps = {k: v for k, v in breakdown.items() if k in KERNEL_OF_STEP}
     dom = max(gemm_steps, key=gemm_steps.get)
-
-    # timed region; the dominant kernel's launches are bracketed by events on the same stream
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
-    log(f"timing {a.steps} steps (dominant kernel: {kernel_of(dom, w, ncu)})")
-    tp.tp_profile_enable(1 << tp.STEPS[dom])
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps - 1)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    e0.record(stream)
-    for k in range(a.steps):
-        ls.step()
-        (ev[k] if k < a.steps - 1 else e1).record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = e0.elapsed_time(e1) / a.steps
-    marks = [e0, *ev, e1]
-    per_step = sorted(marks[k].elapsed_time(marks[k + 1]) for k in range(a.steps))
-    step_stats = {"median": round(per_step[len(per_step) // 2], 4), "min": round(per_step[0], 4),
-                  "p90": round(per_step[min(len(per_step) - 1, int(math.ceil(0.9 * len(per_step))) - 1)], 4)}
+    kernel = kernel_of(dom, w, ncu)
+
+    # the timed region: K steps, events only between steps
+    log(f"timing {a.steps} steps")
+    ms_step, step_stats, wall, _ = time_steps(ls, a.steps)
     # host copies of the timed step's outputs (later measurements reuse the buffers)
     gpu_out = None if a.no_cpu_baseline else {k: v.cpu() for k, v in ls.out.items()}
-    n_dom, ms_dom = tp.tp_profile_collect(tp.STEPS[dom])
-    tp.tp_profile_enable(0)
-    avg_dom_ms = ms_dom / max(n_dom, 1)
     F = layer_flops(w)
     value = F / (ms_step / 1e3) / 1e12
     log(f"{ms_step:.3f} ms/step, {value:.1f} TFLOP/s ({100 * value / PEAK_BF16_TFLOPS:.1f}% of peak); "
         f"host wall {wall:.3f} s for {a.steps} steps")
+    # the same K steps again with the dominant kernel's launches bracketed by
+    # events on the library's stream (its average launch time for the roofline)
+    log(f"timing {a.steps} steps again with events around the dominant kernel ({kernel})")
+    ms_step2, _, _, (n_dom, avg_dom_ms) = time_steps(ls, a.steps, dom_step=dom)
     achieved = sf[dom] / (avg_dom_ms / 1e3) / 1e12
-    kernel = kernel_of(dom, w, ncu)
     traffic = stored_traffic(kernel, w.name)
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": kernel,
-            "flops_per_launch": sf[dom], "avg_launch_ms": round(avg_dom_ms, 4), "launches": n_dom}
+            "flops_per_launch": sf[dom], "avg_launch_ms": round(avg_dom_ms, 4), "launches": n_dom,
+            "ms_per_step_of_that_pass": round(ms_step2, 4)}
+
+    configs = {}
+    if not a.no_configs:
+        del ls, dev
+        torch.cuda.empty_cache()
+        log("the other bf16 configurations (timed like the headline one)")
+        configs[w.name] = {"ms_per_step": round(ms_step, 4), "tflops": round(value, 2),
+                           "pct_of_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+                           "attention_share_of_step": round((breakdown.get("attn_fwd", 0) + breakdown.get("attn_bwd", 0)) / tot, 4)}
+        for name in OTHER_WORKLOADS:
+            if name != w.name:
+                configs[name] = other_workload(name, a.steps, a.warmup)
+        dev = {k: inp[k].cuda() for k in INPUTS}
+        ls = LayerShard(shape, dev)
+        ls.step()
+        torch.cuda.synchronize()
 
     ln = None
     if not a.no_ln:
@@ -529,6 +661,9 @@ def main():
         log("cpu baseline (fp64 oracle on a bounded sample)")
         cpu = cpu_baseline(w, inp, a.cpu_target_s, gpu_out)
         gpu_out = None
+        cpu["cpu_model"] = cpu_model()
+        log("cpu baseline on the tiny fp32 workload (mean of 100 runs)")
+        cpu["tiny_fp32_tp2"] = cpu_baseline_tiny()
 
     out = {
         "metric": "layer-shard fwd+bwd TFLOP/s (bf16) on 1 MI355X; % of MFMA peak",
@@ -545,6 +680,7 @@ def main():
         "breakdown_tflops": {k: round(sf[k] / (v / 1e3) / 1e12, 1) for k, v in breakdown.items() if sf[k] > 0},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "configs": configs or None,
         "ln_residual": ln,
         "vocab_ce": vocab,
         "attn_dropout": adrop,

@@ -99,8 +99,10 @@ tp_status tp_mlp_fwd(const tp_shape* shape, const void* X, const void* A_i, cons
                      const void* B_i, void* pre_i, void* y_i, void* Z_i, void* workspace,
                      size_t workspace_bytes, void* stream);
 
-/* MLP backward: gradients of <Z_i + b2, dZ> with dZ [T,h] replicated (g's
- * backward is the identity):
+/* MLP backward (Megatron-LM deep dive, Fig. 3a for the column / row split
+ * and Fig. 4 for the conjugate operators: g's backward passes dZ through
+ * unchanged, f's backward sums the ranks' input gradients): gradients of
+ * <Z_i + b2, dZ> with dZ [T,h] replicated:
  *   dPre = (dZ B_i^T) * GeLU'(pre_i)
  *   dB_i = y_i^T dZ [f_l,h];  dA_i = X^T dPre [h,f_l];  db1_i = sum_t dPre [f_l]
  *   dX_i = dPre A_i^T [T,h]   this rank's PARTIAL input gradient (f's backward
@@ -130,7 +132,10 @@ tp_status tp_attn_fwd(const tp_shape* shape, const void* X, const void* Wqkv_i, 
                       const void* Wo_i, float* qkv_i, void* ctx_i, float* lse_i, void* O_i,
                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* Attention backward: gradients of <O_i + bo, dO>, dO [T,h] replicated.
+/* Attention backward (Megatron-LM deep dive, Fig. 3b for the per-head split
+ * and Fig. 4 for f and g in the backward pass: dO reaches every rank whole,
+ * and the ranks' partial input gradients are summed by f's backward):
+ * gradients of <O_i + bo, dO>, dO [T,h] replicated.
  *   dC = dO Wo_i^T;  dWo_i = ctx_i^T dO [h_l,h]
  *   per head: dV = P^T dC, dP = dC V^T, dS = P*(dP - rowsum(dC*ctx)),
  *             dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d)   (P recomputed from lse)
@@ -157,9 +162,11 @@ tp_status tp_attn_bwd(const tp_shape* shape, const void* X, const void* Wqkv_i, 
  * in mask_i (tp_attn_dropout_mask_bytes bytes, device memory, 16-byte
  * aligned; layout [batch][n_l][ceil(seq/32)][2][seq rounded up to 8] of
  * 16-bit words); the backward reads them (pass the same p). p = 0 gives the
- * results of tp_attn_fwd / tp_attn_bwd. p outside [0, 1) is TP_ERR_SHAPE. */
+ * results of tp_attn_fwd / tp_attn_bwd. p must keep thr below 65536 (at
+ * least one 16-bit value kept, a finite scale): p outside [0, 1 - 2^-17) is
+ * TP_ERR_SHAPE. */
 typedef struct {
-  float p;          /* drop probability, 0 <= p < 1 */
+  float p;          /* drop probability, 0 <= p < 1 - 2^-17 */
   uint64_t seed;    /* Philox key word 0 */
   uint64_t offset;  /* Philox key word 1 (e.g. a step or layer counter) */
 } tp_dropout;
@@ -272,8 +279,8 @@ tp_status tp_vocab_ce_bwd(const tp_shape* shape, int32_t vocab, const void* X, c
  *   is >= thr = round(65536 p); scale = 65536 / (65536 - thr). No rank enters
  *   the counter, so every rank draws the same mask from the same (seed,
  *   offset). mask [T][hidden/8] bytes (bit e of byte c: element 8c + e,
- *   tp_ln_dropout_mask_bytes bytes) receives the keep bits. p outside [0, 1)
- *   is TP_ERR_SHAPE; other arguments as in tp_ln_residual_fwd. */
+ *   tp_ln_dropout_mask_bytes bytes) receives the keep bits. p outside
+ *   [0, 1 - 2^-17) is TP_ERR_SHAPE; other arguments as in tp_ln_residual_fwd. */
 size_t tp_ln_dropout_mask_bytes(const tp_shape* shape);
 tp_status tp_ln_residual_fwd_dropout(const tp_shape* shape, const tp_dropout* dropout,
                                      const void* resid_in, const void* const* parts, int32_t n_parts,
@@ -325,7 +332,12 @@ enum {
                                 form db1_i's and dbqkv_i's column partials) */
 };
 
-/* Measurement aid (no passage of the pages; for benchmarks): while bit k of
+/* Measurement aid (no passage of the pages; for benchmarks). This timing
+ * state -- the step mask, the recorded events and the event pool, guarded by
+ * one mutex -- is the library's only process-global state besides the
+ * thread-local error message and a per-device cache of the compute-unit
+ * count (read once, used to plan launches); the compute calls above keep no
+ * data between calls. While bit k of
  * step_mask is set, every launch sequence of step k is bracketed by a pair of
  * hipEvents recorded on the caller's stream (the events are created on first
  * use and pooled). tp_profile_enable discards what was recorded and sets the

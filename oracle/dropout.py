@@ -70,7 +70,12 @@ def philox4x64_10(c0, c1, c2, c3, k0, k1):
 
 
 def keep_threshold(p: float) -> int:
-    return int(np.floor(p * 65536.0 + 0.5))
+    thr = int(np.floor(p * 65536.0 + 0.5))
+    if not 0 <= thr < 65536:
+        # every 16-bit uniform would be dropped and the scale 65536 / (65536 - thr)
+        # would not exist: such p cannot be realized in steps of 2^-16
+        raise ValueError(f"drop probability {p} rounds to a keep threshold of {thr} (needs 0 <= thr < 65536)")
+    return thr
 
 
 def keep_scale(p: float) -> float:

@@ -129,11 +129,22 @@ def exported_symbols() -> list[str]:
     return re.findall(r"^\s*(?:size_t|tp_status|const char\*)\s+(tp_\w+)\s*\(", text, flags=re.M)
 
 
+def _device_tensor(t, what: str = "tensor"):
+    """Refuse a tensor the library cannot read as the header requires: host
+    memory (a kernel would fault on its address) or a non-contiguous view
+    (the library reads dense row-major storage)."""
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be in device memory (got a tensor on {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous (row-major); call .contiguous() first")
+
+
 def _ptr(t):
     if t is None:
         return None
     if isinstance(t, int):
         return t or None
+    _device_tensor(t)
     return t.data_ptr() or None
 
 
@@ -151,6 +162,7 @@ def _ws(ws):
         return None, 0
     if isinstance(ws, tuple):
         return ws
+    _device_tensor(ws, "workspace")
     return ws.data_ptr(), ws.numel() * ws.element_size()
 
 

@@ -695,7 +695,9 @@ __device__ __forceinline__ void fixup_body(const KParams& p, int first_tile) {
 // (and two such groups served together differ in k-row parity). Operands are
 // swapped in the MFMA as in the 32x32 kernels: each lane owns one m and four
 // consecutive n of a 16x16 block. Data-parallel plans only (N a multiple of
-// 320, K of 64, whole rounds of tiles); other shapes take the 256-wide tile.
+// 320, whole rounds of tiles); a K that is not a multiple of 64 ends in a
+// partial k-step whose A chunks past K read zeros (the one k-step that loads
+// it checks them). Other shapes take the 256-wide tile.
 struct PanelB320 { const bf16* base; uint32_t nrec, kstep; uint32_t voff[5]; };
 __device__ __forceinline__ int b320_swz(int kr) { return 2 * ((kr + (kr >> 3)) & 3); }
 // physical chunk q of the stage (64 k-rows x 40 chunks) holds logical chunk lc of k-row kr

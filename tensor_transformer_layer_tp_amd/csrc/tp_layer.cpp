@@ -436,10 +436,19 @@ tp_status tp_mlp_bwd(const tp_shape* shape, const void* X, const void* A_i, cons
 
 namespace {
 
-// Dropout arguments: bf16 matrix-core attention only, 0 <= p < 1.
+// A drop probability the kernels can realize: p >= 0 and a keep threshold
+// thr = round(65536 p) (computed as the kernels do) below 65536, so that at
+// least one of the 65536 16-bit values is kept and the keep scale
+// 65536 / (65536 - thr) is finite (p < 1 - 2^-17).
+bool valid_drop_p(float p) {
+  if (!(p >= 0.f && p < 1.f)) return false;
+  return floorf(p * 65536.0f + 0.5f) < 65536.0f;
+}
+
+// Dropout arguments: bf16 matrix-core attention only, a realizable p.
 tp_status check_dropout(const tp_shape* s, const tp_dropout* dr) {
   if (!dr) return fail(TP_ERR_NULL, "dropout is NULL");
-  if (!(dr->p >= 0.f && dr->p < 1.f)) return fail(TP_ERR_SHAPE, "dropout p must be in [0, 1)");
+  if (!valid_drop_p(dr->p)) return fail(TP_ERR_SHAPE, "dropout p must be in [0, 1 - 2^-17)");
   if (s->dtype != TP_BF16) return fail(TP_ERR_DTYPE, "attention dropout runs in bf16 only");
   if (!attn_mfma_supported(s->dtype, s->head_dim))
     return fail(TP_ERR_HEADDIM, "attention dropout supports head_dim 64, 96, 128, 160");
@@ -626,7 +635,7 @@ namespace {
 
 tp_status check_p(const tp_dropout* dr) {
   if (!dr) return fail(TP_ERR_NULL, "dropout is NULL");
-  if (!(dr->p >= 0.f && dr->p < 1.f)) return fail(TP_ERR_SHAPE, "dropout p must be in [0, 1)");
+  if (!valid_drop_p(dr->p)) return fail(TP_ERR_SHAPE, "dropout p must be in [0, 1 - 2^-17)");
   return TP_OK;
 }
 

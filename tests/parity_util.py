@@ -7,15 +7,27 @@ import torch
 import oracle
 
 # Relative Frobenius bound per storage type (the stated bar); the element-wise
-# bound catches a localized error (a wrong tile errs by ~rms) that a norm over
-# millions of elements hides. Outputs downstream of the softmax get a wider
-# element band: with bf16 storage of qkv, near-tied large scores move the
-# softmax weights by more than the rounding of any one element (sharp rows at
-# the 530B-like shape: score gaps of ~0.1 at |score| ~ 20).
+# bound |gpu - ref| <= a * scale + b * |ref| catches a localized error (a wrong
+# tile errs by ~rms) that a norm over millions of elements hides. One band for
+# every output (qkv is kept in fp32 and the scores are formed from split-bf16 q
+# and k, good to ~2^-16, so the outputs downstream of the softmax need no wider
+# band). `scale` is the larger of the output's rms and the rms of the
+# element's own row: the rounding of a bf16 intermediate errs in proportion to
+# the magnitudes of its row, and some rows are far above the average (the first
+# token's key and value gradients collect every query's contribution; in a
+# d = 160 shard its input-gradient row is 13x the global rms, and the bf16
+# rounding of dqkv alone puts one of its elements at 1.1x a band scaled by the
+# global rms, 0.10x one scaled by the row's).
 FRO_TOL = {"fp32": 1e-5, "bf16": 1e-2}
-ELEM_TOL = {"fp32": (2e-5, 1e-5), "bf16": (0.08, 0.02)}  # (x rms(ref), x |ref|)
-ELEM_TOL_SOFTMAX = {"fp32": (2e-5, 1e-5), "bf16": (0.3, 0.05)}
-SOFTMAX_DOWNSTREAM = ("ctx", "lse", "O", "dX_attn", "dWqkv", "dbqkv", "dWo")
+ELEM_TOL = {"fp32": (2e-5, 1e-5), "bf16": (0.08, 0.02)}  # (x scale, x |ref|)
+
+
+def band_scale(r: np.ndarray):
+    """max(rms of r, rms of each row of r) for matrices; rms of r otherwise."""
+    rms = np.sqrt(np.mean(r * r)) if r.size else 0.0
+    if r.ndim == 2 and r.shape[1] > 1 and r.size:
+        return np.maximum(rms, np.sqrt(np.mean(r * r, axis=1, keepdims=True)))
+    return rms
 
 
 def f64(t) -> np.ndarray:
@@ -30,21 +42,22 @@ def compare(name: str, gpu, ref, dtype: str, report: dict | None = None, verbose
     assert np.all(np.isfinite(g)), f"{name}: non-finite values in the HIP output"
     nr = np.linalg.norm(r)
     err = np.linalg.norm(g - r) / (nr if nr > 0 else 1.0)
+    a, b = ELEM_TOL[dtype]
+    scale = band_scale(r)
+    worst = float(np.max(np.abs(g - r) / (a * scale + b * np.abs(r) + 1e-300))) if r.size else 0.0
     if report is not None:
-        report[name] = err
-    soft = name.split("[")[0].split("(")[-1].rstrip(")") in SOFTMAX_DOWNSTREAM
-    a, b = (ELEM_TOL_SOFTMAX if soft else ELEM_TOL)[dtype]
-    rms = np.sqrt(np.mean(r * r)) if r.size else 0.0
-    worst = float(np.max(np.abs(g - r) / (a * rms + b * np.abs(r) + 1e-300))) if r.size else 0.0
+        report[name] = {"rel_fro": float(err), "worst_over_band": worst}
     if verbose:
-        print(f"    {name:14s} rel_fro {err:.3e} (bar {FRO_TOL[dtype]:.0e})  worst element / band {worst:.3f}", flush=True)
+        print(f"    {name:14s} rel_fro {err:.3e} (bar {FRO_TOL[dtype]:.0e})  worst element / band {worst:.3f}",
+              flush=True)
     assert err <= FRO_TOL[dtype], f"{name}: relative Frobenius error {err:.3e} > {FRO_TOL[dtype]:.0e}"
     if r.size:
-        bad = np.abs(g - r) > a * rms + b * np.abs(r)
+        bad = np.abs(g - r) > a * scale + b * np.abs(r)
         if np.any(bad):
             idx = np.argwhere(bad)[0]
+            sc = float(np.broadcast_to(scale, r.shape)[tuple(idx)])
             raise AssertionError(f"{name}: {int(bad.sum())} elements out of bound, first at {tuple(idx)}: "
-                                 f"gpu {g[tuple(idx)]:.6g} ref {r[tuple(idx)]:.6g} rms {rms:.3g}")
+                                 f"gpu {g[tuple(idx)]:.6g} ref {r[tuple(idx)]:.6g} scale {sc:.3g}")
     return err
 
 

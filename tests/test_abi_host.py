@@ -353,3 +353,52 @@ def test_ln_dropout_validation():
         tp.tp_ln_residual_bwd_dropout(s, tp.TpDropout(0.1, 1, 2), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
                                       None, FAKE, FAKE, workspace=(FAKE, 1 << 40), stream=0)
     assert ei.value.name == "TP_ERR_NULL"  # d_block
+
+
+def test_binding_refuses_host_and_strided_tensors():
+    # The header wants contiguous device memory; the binding refuses a host
+    # tensor or a strided view before the library sees its address.
+    import torch
+    s = shape()
+    host = torch.zeros(64, 64)
+    with pytest.raises(ValueError, match="device memory"):
+        tp.tp_mlp_fwd(s, host, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, workspace=(FAKE, 1 << 40), stream=0)
+    with pytest.raises(ValueError, match="device memory"):
+        tp.tp_mlp_fwd(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, workspace=torch.zeros(16, dtype=torch.uint8),
+                      stream=0)
+    strided = torch.zeros(64, 128)[:, :64]
+
+    class _View:  # a strided "device" tensor: is_cuda true, not contiguous
+        is_cuda = True
+        def is_contiguous(self):
+            return strided.is_contiguous()
+        def data_ptr(self):
+            return FAKE
+    with pytest.raises(ValueError, match="contiguous"):
+        tp.tp_mlp_fwd(s, _View(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, workspace=(FAKE, 1 << 40), stream=0)
+
+
+@pytest.mark.parametrize("p", [1.0 - 2.0 ** -17, 1.0 - 2.0 ** -20, 1.0 - 2.0 ** -24])
+def test_dropout_p_with_nothing_kept_is_refused(p):
+    # round(65536 p) = 65536 would keep nothing and make the scale infinite
+    import numpy as np
+    assert np.floor(np.float32(p) * np.float32(65536.0) + np.float32(0.5)) >= 65536
+    s = _bf16_attn()
+    with pytest.raises(tp.TPError) as ei:
+        tp.tp_attn_fwd_dropout(s, tp.TpDropout(p, 1, 2), *([FAKE] * 9), workspace=(FAKE, 1 << 40), stream=0)
+    assert ei.value.name == "TP_ERR_SHAPE"
+    with pytest.raises(tp.TPError) as ei:
+        tp.tp_ln_residual_fwd_dropout(shape(), tp.TpDropout(p, 1, 2), FAKE, [FAKE], None, FAKE, FAKE, 1e-5, FAKE,
+                                      FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert ei.value.name == "TP_ERR_SHAPE"
+
+
+def test_dropout_largest_realizable_p_passes_validation():
+    # p = 65535/65536 (thr 65535) is valid: the call then fails only on the
+    # workspace check that follows, proving p itself was accepted
+    s = _bf16_attn()
+    with pytest.raises(tp.TPError) as ei:
+        tp.tp_attn_fwd_dropout(s, tp.TpDropout(65535.0 / 65536.0, 1, 2), *([FAKE] * 9), workspace=(FAKE, 0),
+                               stream=0)
+    assert ei.value.name == "TP_ERR_WORKSPACE", str(ei.value)
+

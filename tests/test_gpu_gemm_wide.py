@@ -12,6 +12,12 @@ both shapes, with K = 2100 tokens (a partial last k-step).
     9 x 28 = 252 tiles, one data-parallel round on 256 CUs, the last row of
     tiles 52 rows; so does the GEMM2 weight gradient (35 x 28 tiles in four
     rounds, K = 2100: a partial last k-step).
+With fewer 320-wide tiles than CUs the input gradients take that tile when
+its k-split covers every CU exactly; at T = 1900 (8 row tiles, the last one
+108 rows) on a 256-CU device:
+  * h = 2720, f = 2560: the GEMM2 input gradient (+ GeLU' epilogue), 8 x 8 =
+    64 tiles in 4 k-parts, K = 2720 (the last part ends in a partial k-step);
+  * h = 2560, f = 2720: the GEMM1 input gradient, the same split over K = 2720.
 The oracle recomputes column sub-shards and sampled token rows exactly."""
 import numpy as np
 import pytest
@@ -39,8 +45,8 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def workload(h, ffn):
-    return synth.Workload(f"wide_h{h}_f{ffn}", batch=1, seq=TOKENS, hidden=h, n_heads=h // 160, head_dim=160,
+def workload(h, ffn, tokens=TOKENS):
+    return synth.Workload(f"wide_h{h}_f{ffn}", batch=1, seq=tokens, hidden=h, n_heads=h // 160, head_dim=160,
                           ffn=ffn, tp_size=1, dtype="bf16", bias_std=0.5)
 
 
@@ -48,11 +54,15 @@ def samples(n, k, rng):
     return np.unique(np.concatenate([[0, 1, n // 2, n - 1], rng.choice(n, k, replace=False)]))
 
 
-@pytest.mark.parametrize("h,ffn", [(3200, 9600), (9600, 3200), (8960, 8960)],
-                         ids=["fc2_dgrad_wide", "fc1_dgrad_wide", "fwd_wide"])
-def test_mlp_wide_tiles_ragged_tokens(h, ffn):
-    w = workload(h, ffn)
-    print(f"\n  [wide MLP] T={TOKENS} h={h} f={ffn}", flush=True)
+@pytest.mark.parametrize("h,ffn,tokens,exact_split", [
+    (3200, 9600, TOKENS, False), (9600, 3200, TOKENS, False), (8960, 8960, TOKENS, False),
+    (2720, 2560, 1900, True), (2560, 2720, 1900, True)],
+    ids=["fc2_dgrad_wide", "fc1_dgrad_wide", "fwd_wide", "fc2_dgrad_exact_ksplit", "fc1_dgrad_exact_ksplit"])
+def test_mlp_wide_tiles_ragged_tokens(h, ffn, tokens, exact_split):
+    if exact_split and torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the exact k-split of 64 tiles in 4 parts is planned for a 256-CU device only")
+    w = workload(h, ffn, tokens)
+    print(f"\n  [wide MLP] T={tokens} h={h} f={ffn}", flush=True)
     inp = synth.draw_shard(w, seed=21, skip=ATTN_IN)
     s = shape_of(w, 0)
     T, bf, nan = w.tokens, torch.bfloat16, float("nan")

@@ -40,6 +40,26 @@ def run_shard(w, inp, rank, fill=float("nan"), alibi=None):
     return ls
 
 
+def _recording(rep: dict):
+    """compare() that also keeps each output's errors in rep."""
+    def cmp(name, gpu, ref, dtype):
+        return compare(name, gpu, ref, dtype, rep)
+    return cmp
+
+
+def _write_report(case: str, rep: dict):
+    """Per-output errors of a full-size case, as JSON under the directory named
+    by TP_PARITY_REPORT_DIR (nothing is written when it is unset)."""
+    import json
+    import os
+    out = os.environ.get("TP_PARITY_REPORT_DIR")
+    if not out:
+        return
+    os.makedirs(out, exist_ok=True)
+    with open(os.path.join(out, f"{case}.json"), "w") as fh:
+        json.dump(rep, fh, indent=1)
+
+
 def check_all(ls, ref, dtype, names=OUTS):
     rep = {}
     for k in names:
@@ -196,22 +216,27 @@ def test_deterministic_repeat():
 # benchmark times (rank 0 of the shard; every output sampled or complete).
 # ---------------------------------------------------------------------------
 
-FULL = ["gpt2_1p2b_tp1", "gpt_8p3b_tp8", "mtnlg_530b_tp8", "bloom_176b_tp8"]
+# (workload, rank): rank 0 of each, and the last rank of the ALiBi workload,
+# whose heads (global 99..112 of 112) carry the smallest slopes, down to 2^-8.
+FULL = [("gpt2_1p2b_tp1", 0), ("gpt_8p3b_tp8", 0), ("mtnlg_530b_tp8", 0), ("bloom_176b_tp8", 0),
+        ("bloom_176b_tp8", 7)]
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_workload(name):
+@pytest.mark.parametrize("name,rank", FULL, ids=[f"{n}_r{r}" for n, r in FULL])
+def test_full_size_workload(name, rank):
     w = synth.WORKLOADS[name]
-    print(f"[full-size] {name}: drawing inputs", flush=True)
+    print(f"[full-size] {name} rank {rank}: drawing inputs", flush=True)
     inp = synth.draw_shard(w, seed=0)
-    print(f"[full-size] {name}: running the HIP path", flush=True)
-    ls = run_shard(w, inp, 0)
+    print(f"[full-size] {name} rank {rank}: running the HIP path", flush=True)
+    ls = run_shard(w, inp, rank)
     out = ls.out
+    rep = {}
+    compare = _recording(rep)
     rng = np.random.default_rng(7)
     T, h, fl = w.tokens, w.hidden, w.ffn_local
     hl, nl, d = w.h_local, w.heads_local, w.head_dim
     a = {k: f64(inp[k]) for k in INPUTS}
-    print(f"[full-size] {name}: oracle on sampled outputs", flush=True)
+    print(f"[full-size] {name} rank {rank}: oracle on sampled outputs", flush=True)
     # MLP: a column sub-shard C of the rank's FFN columns is itself a valid shard
     C = np.unique(np.concatenate([[0, 1, fl // 2, fl - 1], rng.choice(fl, 60, replace=False)]))
     pre_C, y_C, _ = oracle.mlp_fwd(a["X_mlp"], a["A"][:, C], a["b1"][C], a["B"][C, :])
@@ -229,7 +254,7 @@ def test_full_size_workload(name):
     dX_R = oracle.mlp_bwd(a["X_mlp"][R], a["A"], a["B"], pre_R, y_R, a["dZ"][R])[0]
     compare("dX_mlp[R]", out["dX_mlp"][R], dX_R, "bf16")
     # attention: the complete per-head core, projections sampled
-    kw = dict(batch=w.batch, seq=w.seq, n_local=nl, head_dim=d, head0=0, n_heads=w.n_heads, alibi=w.alibi)
+    kw = dict(batch=w.batch, seq=w.seq, n_local=nl, head_dim=d, head0=rank * nl, n_heads=w.n_heads, alibi=w.alibi)
     qkv = a["X_attn"] @ a["Wqkv"] + a["bqkv"]
     compare("qkv", out["qkv"], qkv, "bf16")
     ctx, lse = oracle.attn_core_fwd(qkv, **kw)
@@ -245,4 +270,5 @@ def test_full_size_workload(name):
     compare("dbqkv", out["dbqkv"], dqkv.sum(axis=0), "bf16")
     compare("dbo", out["dbo"], a["dO"].sum(axis=0), "bf16")
     compare("dX_attn[R]", out["dX_attn"][R], dqkv[R] @ a["Wqkv"].T, "bf16")
-    print(f"[full-size] {name}: done", flush=True)
+    _write_report(f"{name}_r{rank}", rep)
+    print(f"[full-size] {name} rank {rank}: done", flush=True)
