@@ -231,6 +231,25 @@ tp_status tp_ln_residual_bwd(const tp_shape* shape, const void* resid_out, const
                              void* dbeta, void* dbias_or_null, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* tp_ln_residual_bwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments, results and errors as
+ * tp_ln_residual_bwd (bit-identical outputs), but the fp32 run partials live
+ * in a scratch array of tp_ln_residual_bwd_noalloc_max_scratch_bytes() bytes
+ * (48 MiB) that the library holds on each device it runs on until the
+ * process ends; the call itself allocates nothing. A shape whose
+ * tp_ln_workspace_bytes exceeds that size is TP_ERR_SHAPE (e.g. hidden 24576
+ * with 256 or more rows; hidden 20480 fits). Every call on a device shares
+ * that device's array: calls that overlap on one device (several streams or
+ * threads) race and give undefined results; calls ordered on one stream are
+ * safe. The first call on a device looks up the array's address
+ * (hipGetSymbolAddress) and keeps it. */
+size_t tp_ln_residual_bwd_noalloc_max_scratch_bytes(void);
+tp_status tp_ln_residual_bwd_noalloc(const tp_shape* shape, const void* resid_out, const float* mean,
+                                     const float* rstd, const void* gamma, const void* d_ln_out,
+                                     const void* d_resid_out_or_null, void* d_resid, void* dgamma,
+                                     void* dbeta, void* dbias_or_null, void* stream);
+
 /* Vocabulary-parallel logits + cross-entropy of the output layer
  * (Megatron-LM deep dive, vocabulary-parallel loss fusion section: the
  * embedding table is split along the vocabulary, each rank computes the

@@ -24,7 +24,8 @@ __all__ = [
     "tp_profile_collect", "STEPS", "tp_ln_workspace_bytes", "tp_ln_residual_fwd", "tp_ln_residual_bwd",
     "tp_vocab_workspace_bytes", "tp_vocab_ce_fwd", "tp_vocab_ce_combine", "tp_vocab_ce_bwd", "TpDropout",
     "tp_attn_dropout_mask_bytes", "tp_attn_fwd_dropout", "tp_attn_bwd_dropout", "tp_ln_dropout_mask_bytes",
-    "tp_ln_residual_fwd_dropout", "tp_ln_residual_bwd_dropout",
+    "tp_ln_residual_fwd_dropout", "tp_ln_residual_bwd_dropout", "tp_ln_residual_bwd_noalloc",
+    "tp_ln_residual_bwd_noalloc_max_scratch_bytes",
 ]
 
 TP_FP32, TP_BF16 = 0, 1
@@ -92,6 +93,8 @@ _SIGS = {
                                          ctypes.c_int32, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp]),
     "tp_ln_residual_bwd_dropout": (_st, [ctypes.POINTER(TpShape), ctypes.POINTER(TpDropout)] + [_vp] * 12
                                    + [_vp, _sz, _vp]),
+    "tp_ln_residual_bwd_noalloc": (_st, [ctypes.POINTER(TpShape)] + [_vp] * 10 + [_vp]),
+    "tp_ln_residual_bwd_noalloc_max_scratch_bytes": (_sz, []),
     "tp_profile_enable": (_st, [ctypes.c_uint32]),
     "tp_profile_collect": (_st, [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)]),
     "tp_last_error": (ctypes.c_char_p, []),
@@ -248,6 +251,19 @@ def tp_ln_residual_bwd(shape, resid_out, mean, rstd, gamma, d_ln_out, d_resid_ou
                                              _ptr(gamma), _ptr(d_ln_out), _ptr(d_resid_out_or_null), _ptr(d_resid),
                                              _ptr(dgamma), _ptr(dbeta), _ptr(dbias_or_null), w, wn,
                                              _stream(stream)))
+
+
+def tp_ln_residual_bwd_noalloc_max_scratch_bytes() -> int:
+    return load_library().tp_ln_residual_bwd_noalloc_max_scratch_bytes()
+
+
+def tp_ln_residual_bwd_noalloc(shape, resid_out, mean, rstd, gamma, d_ln_out, d_resid_out_or_null, d_resid, dgamma,
+                               dbeta, dbias_or_null=None, stream=None):
+    """tp_ln_residual_bwd with the library's own scratch instead of a workspace."""
+    _check(load_library().tp_ln_residual_bwd_noalloc(ctypes.byref(shape), _ptr(resid_out), _ptr(mean), _ptr(rstd),
+                                                     _ptr(gamma), _ptr(d_ln_out), _ptr(d_resid_out_or_null),
+                                                     _ptr(d_resid), _ptr(dgamma), _ptr(dbeta), _ptr(dbias_or_null),
+                                                     _stream(stream)))
 
 
 def tp_vocab_workspace_bytes(shape: TpShape, vocab: int) -> int:

@@ -674,10 +674,42 @@ tp_status ln_fwd_impl(const tp_shape* shape, const tp_dropout* dr, uint8_t* mask
   return TP_OK;
 }
 
+// ---- scratch of the entry point that allocates nothing ---------------------
+// tp_ln_residual_bwd_noalloc keeps the backward's fp32 run partials in this
+// array instead of a caller workspace. Each device holds its own copy for the
+// life of the process; host code uses only the device address that
+// hipGetSymbolAddress returns for the current device (looked up on the first
+// call on that device and kept per device), never the array's name.
+constexpr size_t kNoallocScratchBytes = (size_t)48 << 20;
+__device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+tp_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(TP_ERR_HIP, "device %d outside the %d devices the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(TP_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL on device %d", dev);
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return TP_OK;
+}
+
+// use_scratch: take the workspace from the library's scratch array (after all
+// argument checks) instead of the caller's.
 tp_status ln_bwd_impl(const tp_shape* shape, const tp_dropout* dr, const uint8_t* mask, void* d_block,
                       const void* resid_out, const float* mean, const float* rstd, const void* gamma,
                       const void* d_ln_out, const void* d_resid_out_or_null, void* d_resid, void* dgamma, void* dbeta,
-                      void* dbias_or_null, void* workspace, size_t workspace_bytes, void* stream) {
+                      void* dbias_or_null, void* workspace, size_t workspace_bytes, void* stream,
+                      bool use_scratch = false) {
   Dims dm;
   TP_CHECK(check_shape(shape, dm));
   TP_CHECK(check_ln(dm));
@@ -695,7 +727,16 @@ tp_status ln_bwd_impl(const tp_shape* shape, const tp_dropout* dr, const uint8_t
   TP_CHECK(check_ptr(dgamma, "dgamma", false));
   TP_CHECK(check_ptr(dbeta, "dbeta", false));
   TP_CHECK(check_ptr(dbias_or_null, "dbias", true));
-  TP_CHECK(check_ws(workspace, workspace_bytes, ln_bwd_workspace_bytes(dm.T, (int)dm.h)));
+  const size_t need = ln_bwd_workspace_bytes(dm.T, (int)dm.h);
+  if (use_scratch) {
+    if (need > kNoallocScratchBytes)
+      return fail(TP_ERR_SHAPE, "this shape needs %zu bytes of scratch; the allocation-free entry point holds %zu "
+                  "(use tp_ln_residual_bwd with a workspace)", need, kNoallocScratchBytes);
+    workspace = nullptr;
+    workspace_bytes = kNoallocScratchBytes;
+    if (need) TP_CHECK(scratch_address(&workspace));
+  }
+  TP_CHECK(check_ws(workspace, workspace_bytes, need));
   LnDesc d;
   d.T = dm.T; d.h = (int)dm.h;
   d.resid_out = (void*)resid_out; d.mean = (float*)mean; d.rstd = (float*)rstd; d.gamma = gamma;
@@ -726,6 +767,16 @@ tp_status tp_ln_residual_bwd(const tp_shape* shape, const void* resid_out, const
                              void* stream) {
   return ln_bwd_impl(shape, nullptr, nullptr, nullptr, resid_out, mean, rstd, gamma, d_ln_out, d_resid_out_or_null,
                      d_resid, dgamma, dbeta, dbias_or_null, workspace, workspace_bytes, stream);
+}
+
+size_t tp_ln_residual_bwd_noalloc_max_scratch_bytes(void) { return kNoallocScratchBytes; }
+
+tp_status tp_ln_residual_bwd_noalloc(const tp_shape* shape, const void* resid_out, const float* mean,
+                                     const float* rstd, const void* gamma, const void* d_ln_out,
+                                     const void* d_resid_out_or_null, void* d_resid, void* dgamma, void* dbeta,
+                                     void* dbias_or_null, void* stream) {
+  return ln_bwd_impl(shape, nullptr, nullptr, nullptr, resid_out, mean, rstd, gamma, d_ln_out, d_resid_out_or_null,
+                     d_resid, dgamma, dbeta, dbias_or_null, nullptr, 0, stream, /*use_scratch=*/true);
 }
 
 size_t tp_ln_dropout_mask_bytes(const tp_shape* shape) {

@@ -41,7 +41,8 @@ def test_library_loads_and_exports_every_declared_symbol():
                           "tp_profile_collect", "tp_ln_workspace_bytes", "tp_ln_residual_fwd", "tp_ln_residual_bwd",
                           "tp_vocab_workspace_bytes", "tp_vocab_ce_fwd", "tp_vocab_ce_combine", "tp_vocab_ce_bwd",
                           "tp_attn_dropout_mask_bytes", "tp_attn_fwd_dropout", "tp_attn_bwd_dropout",
-                          "tp_ln_dropout_mask_bytes", "tp_ln_residual_fwd_dropout", "tp_ln_residual_bwd_dropout"}
+                          "tp_ln_dropout_mask_bytes", "tp_ln_residual_fwd_dropout", "tp_ln_residual_bwd_dropout",
+                          "tp_ln_residual_bwd_noalloc", "tp_ln_residual_bwd_noalloc_max_scratch_bytes"}
     for n in names:
         assert isinstance(getattr(lib, n), ctypes._CFuncPtr), n
     out = subprocess.run(["nm", "-D", "--defined-only", tp.library_path()], capture_output=True, text=True).stdout
@@ -402,3 +403,20 @@ def test_dropout_largest_realizable_p_passes_validation():
                                stream=0)
     assert ei.value.name == "TP_ERR_WORKSPACE", str(ei.value)
 
+
+def test_noalloc_ln_backward_refuses_shapes_beyond_its_scratch():
+    assert tp.tp_ln_residual_bwd_noalloc_max_scratch_bytes() == 48 << 20
+    # hidden 24576 with 256 rows needs 256 runs x 2 x 24576 fp32 partials (48 MiB) plus the
+    # bias column sums: more than the scratch; refused before any device call
+    s = shape(batch=1, seq=256, hidden=24576, ffn=4 * 24576, n_heads=192, head_dim=128, tp_size=8, dtype=tp.TP_BF16)
+    assert tp.tp_ln_workspace_bytes(s) > 48 << 20
+    with pytest.raises(tp.TPError) as ei:
+        tp.tp_ln_residual_bwd_noalloc(s, *([FAKE] * 10), stream=0)
+    assert ei.value.name == "TP_ERR_SHAPE" and "scratch" in str(ei.value)
+    # its other argument checks are those of tp_ln_residual_bwd
+    with pytest.raises(tp.TPError) as ei:
+        tp.tp_ln_residual_bwd_noalloc(shape(), None, *([FAKE] * 9), stream=0)
+    assert ei.value.name == "TP_ERR_NULL"
+    # the 530B-like shard's hidden size fits
+    c4 = shape(batch=1, seq=2048, hidden=20480, ffn=81920, n_heads=128, head_dim=160, tp_size=8, dtype=tp.TP_BF16)
+    assert 0 < tp.tp_ln_workspace_bytes(c4) <= 48 << 20
