@@ -2,6 +2,7 @@
 
     python -m tensor_transformer_layer_tp_amd.profsum stats  <dir>            # per-kernel durations
     python -m tensor_transformer_layer_tp_amd.profsum counters <dir> [filter] # per-kernel counter means
+    python -m tensor_transformer_layer_tp_amd.profsum util <sq_dir> <mem_dir>  # MFMA busy, LDS, TA, L2, DRAM
     python -m tensor_transformer_layer_tp_amd.profsum traffic <fetch_dir> <write_dir> \
         <copy_fetch_dir> <copy_write_dir> <copy_bytes> <kernel>                # HBM bytes per launch
 
@@ -55,6 +56,49 @@ def counters(d: str, filt: str = "") -> str:
     return "\n".join(out)
 
 
+XCDS, CUS, SIMDS = 8, 256, 1024  # MI355X: GRBM_GUI_ACTIVE is summed over its 8 XCDs
+
+
+def _per_kernel(d: str):
+    acc = defaultdict(lambda: defaultdict(list))
+    dur = defaultdict(list)
+    for r in _rows(d, "counter_collection.csv"):
+        k = short(r["Kernel_Name"])
+        acc[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+            dur[k].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    mean = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
+    return mean, {k: sum(v) / len(v) for k, v in dur.items()}, {k: len(v) for k, v in dur.items()}
+
+
+def util(sq_dir: str, mem_dir: str, top: int = 16) -> str:
+    """Per kernel, from a pass of SQ counters and a pass of memory counters
+    (each with GRBM_GUI_ACTIVE): the shader clock it ran at (busy cycles per
+    XCD over the dispatch's duration), MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES over
+    1024 SIMDs x those cycles, the MfmaUtil definition), LDS active and
+    bank-conflict cycles per CU, TA busy and TCP pending-data stall per CU, the
+    L2 hit rate and the L2's DRAM-side read and write requests (x 64 bytes)."""
+    A, dA, nA = _per_kernel(sq_dir)
+    B, _, _ = _per_kernel(mem_dir)
+    out = ["| kernel | dispatches | avg us | clock GHz | MFMA busy % | LDS active % | LDS bank-conflict % | "
+           "TA busy % | TCP pending stall % | L2 hit % | DRAM read GB | DRAM write GB |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for k in sorted(A, key=lambda k: -dA.get(k, 0))[:top]:
+        a, b = A[k], B.get(k, {})
+        cyc = a["GRBM_GUI_ACTIVE"] / XCDS
+        bc = b.get("GRBM_GUI_ACTIVE", 0) / XCDS or 1.0
+        hit, miss = b.get("TCC_HIT_sum", 0.0), b.get("TCC_MISS_sum", 0.0)
+        out.append(
+            f"| {k} | {nA[k]} | {dA[k] / 1e3:.1f} | {cyc / dA[k]:.2f} | "
+            f"{100 * a['SQ_VALU_MFMA_BUSY_CYCLES'] / (SIMDS * cyc):.1f} | "
+            f"{100 * a['SQ_LDS_IDX_ACTIVE'] / (CUS * cyc):.1f} | {100 * a['SQ_LDS_BANK_CONFLICT'] / (CUS * cyc):.1f} | "
+            f"{100 * b.get('TA_TA_BUSY_sum', 0) / (CUS * bc):.1f} | "
+            f"{100 * b.get('TCP_PENDING_STALL_CYCLES_sum', 0) / (CUS * bc):.1f} | "
+            f"{100 * hit / max(hit + miss, 1):.1f} | {b.get('TCC_EA0_RDREQ_DRAM_sum', 0) * 64 / 1e9:.3f} | "
+            f"{b.get('TCC_EA0_WRREQ_DRAM_sum', 0) * 64 / 1e9:.3f} |")
+    return "\n".join(out)
+
+
 def _mean(d: str, counter: str, kernel: str) -> float:
     v = [float(r["Counter_Value"]) for r in _rows(d, "counter_collection.csv")
          if r["Counter_Name"] == counter and short(r["Kernel_Name"]) == kernel]
@@ -89,6 +133,8 @@ if __name__ == "__main__":
         print(stats(d))
     elif mode == "counters":
         print(counters(d, sys.argv[3] if len(sys.argv) > 3 else ""))
+    elif mode == "util":
+        print(util(d, sys.argv[3]))
     elif mode == "traffic":
         print(traffic(d, sys.argv[3], sys.argv[4], sys.argv[5], int(sys.argv[6]), sys.argv[7]))
     else:
