@@ -126,8 +126,9 @@ tp_status tp_mlp_bwd(const tp_shape* shape, const void* X, const void* A_i, cons
  * Saved for backward: qkv_i [T,3h_l] fp32, ctx_i [T,h_l] (heads side by
  * side), lse_i [batch, n_l, seq] fp32. qkv_i is kept in fp32 because the
  * scores q.k/sqrt(d) can be large and nearly tied (rows sharper than bf16 can
- * resolve); the bf16 path forms them from q and k split into bf16 high and
- * low parts (three matrix-core products), accurate to about 2^-16. */
+ * resolve); the bf16 path forms them in one matrix-core product of fp16
+ * copies of q and k (11-bit significands; values beyond the fp16 range,
+ * |q log2(e)/sqrt(d)| or |k| above 65504, saturate). */
 tp_status tp_attn_fwd(const tp_shape* shape, const void* X, const void* Wqkv_i, const void* bqkv_i,
                       const void* Wo_i, float* qkv_i, void* ctx_i, float* lse_i, void* O_i,
                       void* workspace, size_t workspace_bytes, void* stream);

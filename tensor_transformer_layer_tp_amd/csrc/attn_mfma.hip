@@ -3,14 +3,21 @@
 //
 // Inputs: per rank, qkv [T, 3*h_l] = [Q | K | V] in fp32; local head l uses
 // columns l*D.. of each third; row t = b*seq + position. A split kernel first
-// writes five bf16 arrays [T, h_l] to the workspace: q_hi, q_lo, k_hi, k_lo,
-// v (x = hi + lo to ~2^-16 relative). Outputs: ctx [T, h_l] bf16, lse
-// [batch, n_local, seq] fp32 (natural log); backward dqkv [T, 3*h_l] bf16.
+// writes five 16-bit arrays [T, h_l] to the workspace: q16 = fp16(q log2(e) /
+// sqrt(D)), k16 = fp16(k) for the scores, and qb = bf16(q), kb = bf16(k),
+// v = bf16(v) for the gradient and value products. Outputs: ctx [T, h_l]
+// bf16, lse [batch, n_local, seq] fp32 (natural log); backward dqkv
+// [T, 3*h_l] bf16.
 //
-// Precision: scores are S = q_hi k_hi + q_hi k_lo + q_lo k_hi (three
-// products), because rows of large, nearly tied scores amplify bf16 rounding
-// of q and k far beyond the rounding of the output. V, P, dS and dctx enter
-// the products as bf16 (their rounding is not amplified).
+// Precision: the scores are one fp16 product q16 k16^T (fp32 accumulation),
+// already in log2 units. Rows of large, nearly tied scores amplify the
+// rounding of q and k far beyond the rounding of the output: with bf16 q and
+// k (8-bit significands) the 530B-like shard's input gradients move by 1.2e-2
+// relative, with fp16 (11 bits) by 1.5e-3. fp16 holds the scaled q and k of
+// these layers with room to spare (|q log2(e)/sqrt(D)|, |k| far below 65504;
+// larger values saturate to +-65504 in the split). V, P, dS and dctx enter
+// the products as bf16 (their rounding is not amplified, and bf16 keeps the
+// gradients' fp32 range).
 //
 // Tiles of 64 rows x D columns are staged in LDS by buffer loads that write
 // LDS directly, double-buffered (the next tile's loads are in flight while
@@ -54,6 +61,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int TROWS = 64;  // rows per staged tile
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -62,14 +70,14 @@ typedef __attribute__((address_space(3))) i16x4* lds_i16x4;
 struct MP {
   int batch, seq, n_local, h_l, head0, n_heads, alibi;
   long T;
-  const bf16* qh; const bf16* ql; const bf16* kh; const bf16* kl; const bf16* vh;  // [T, h_l] each
+  // [T, h_l] each: scaled fp16 q and fp16 k (scores), bf16 q, k, v
+  const bf16* q16; const bf16* qb; const bf16* k16; const bf16* kb; const bf16* vh;
   bf16* ctx;
   float* lse;
   const bf16* dctx;    // [T, h_l]
   const float* delta;  // [batch, n_local, seq]
   bf16* dqkv;          // [T, 3*h_l]
-  float scale_log2;    // log2(e) / sqrt(D)
-  float scale;         // 1 / sqrt(D)
+  float scale;         // 1 / sqrt(D) (q16 carries log2(e) / sqrt(D) already)
   // dropout (DO kernels)
   uint16_t* mask;      // [batch][n_local][nkb][2][mstride] keep bits
   int nkb, mstride;    // ceil(seq / 32); seq rounded up to a multiple of 8
@@ -183,6 +191,12 @@ __device__ __forceinline__ bf16x8 frag_tr(const char* tile, int db, int kc, cons
   return __builtin_bit_cast(bf16x8, v);
 }
 
+__device__ __forceinline__ f16x8 as_f16(bf16x8 v) { return __builtin_bit_cast(f16x8, v); }
+// score product of fp16 fragments (stored in 16-bit slots typed bf16x8)
+__device__ __forceinline__ f32x16 mfma_f16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16(a), as_f16(b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ bf16x8 pack8(const float* x) {
   bf16x8 v;
 #pragma unroll
@@ -203,7 +217,7 @@ __device__ __forceinline__ void loads_landed_barrier() {
 // ---- forward ---------------------------------------------------------------------
 template <int D>
 struct FwdState {
-  bf16x8 qf[D / 16], qfl[D / 16];
+  bf16x8 qf[D / 16];  // q16 fragments (fp16 bits)
   f32x16 o[D / 32];
   float m_run, l_run;
 };
@@ -212,13 +226,13 @@ struct FwdState {
 // after the query or past the sequence (MASK: only blocks on the diagonal or
 // at the end need it).
 template <bool MASK, bool AL>
-__device__ __forceinline__ float fwd_scores(const f32x16& sa, const f32x16& sc, float (&x)[16], float scale_log2,
-                                            float slope2, int k0, int g, int myq, int seq) {
+__device__ __forceinline__ float fwd_scores(const f32x16& sa, float (&x)[16], float slope2, int k0, int g, int myq,
+                                            int seq) {
   float mloc = -INFINITY;
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int key = k0 + 8 * (q >> 2) + 4 * g + (q & 3);
-    float v = (sc[q] + sa[q]) * scale_log2;
+    float v = sa[q];
     if (AL) v -= slope2 * (float)(myq - key);
     if (MASK && (key > myq || key >= seq)) v = -INFINITY;
     x[q] = v;
@@ -234,28 +248,22 @@ __device__ __forceinline__ float fwd_scores(const f32x16& sa, const f32x16& sc, 
 constexpr float kLazy = 8.0f;
 
 // One 32-key block (keys k0 .. k0 + 31, block sb of the 64-key tile in `cur`:
-// K hi, K lo, V at 0, TB, 2TB) for this wave's 32 queries.
+// K16 and V at 0 and TB) for this wave's 32 queries.
 template <int D, bool AL, bool DO>
 __device__ __forceinline__ void fwd_block(const MP& p, const char* __restrict__ cur, int k0, int sb, int g,
                                           int q0w, int myq, float slope2, const TrOff& tro, const RowOff& ro,
                                           int b, int head, int hk, FwdState<D>& st) {
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
-  f32x16 sa = f32x16{}, sc = f32x16{};
+  f32x16 sa = f32x16{};
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const bf16x8 kh = frag_row(cur, sb, c, ro);
-    const bf16x8 kl = frag_row(cur + TB, sb, c, ro);
-    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, st.qf[c], sc, 0, 0, 0);
-    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, st.qfl[c], sc, 0, 0, 0);
-    sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, st.qf[c], sa, 0, 0, 0);
-  }
-  // s[q]: key k0 + 8(q>>2) + 4g + (q&3), query myq
+  for (int c = 0; c < NC; ++c) sa = mfma_f16(frag_row(cur, sb, c, ro), st.qf[c], sa);
+  // s[q]: key k0 + 8(q>>2) + 4g + (q&3), query myq, in log2 units
   float x[16];
   float mloc;
   if ((k0 + 31 > q0w) || (k0 + 32 > p.seq))
-    mloc = fwd_scores<true, AL>(sa, sc, x, p.scale_log2, slope2, k0, g, myq, p.seq);
+    mloc = fwd_scores<true, AL>(sa, x, slope2, k0, g, myq, p.seq);
   else
-    mloc = fwd_scores<false, AL>(sa, sc, x, p.scale_log2, slope2, k0, g, myq, p.seq);
+    mloc = fwd_scores<false, AL>(sa, x, slope2, k0, g, myq, p.seq);
   mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
   const bool move = mloc > st.m_run + kLazy;  // also true on a row's first unmasked keys
   if (__ballot(move)) {                        // wave-uniform
@@ -282,7 +290,7 @@ __device__ __forceinline__ void fwd_block(const MP& p, const char* __restrict__ 
     for (int q = 0; q < 16; ++q) x[q] = ((bits >> q) & 1u) ? x[q] : 0.f;
   }
   const bf16x8 pf0 = pack8(x), pf1 = pack8(x + 8);
-  const char* vt = cur + 2 * TB;
+  const char* vt = cur + TB;
 #pragma unroll
   for (int db = 0; db < NB; ++db) {
     st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(vt, db, 2 * sb, tro), pf0, st.o[db], 0, 0, 0);
@@ -302,8 +310,9 @@ template <int D, bool AL, bool DO>
 __global__ __launch_bounds__(64 * FWD_WAVES) void fwd_mfma(MP p, FwdItems items) {
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
   constexpr int NX = NB * 16 + 2;  // floats a wave hands to its partner, per lane
-  static_assert(4 * NX * 64 * 4 <= 6 * TB, "merge buffer exceeds the tile stages");
-  __shared__ __attribute__((aligned(16))) char stage[6 * TB];
+  // two stages of (K16, V) tiles; the pair merge at the end reuses the memory
+  constexpr int SZ = 4 * TB > 4 * NX * 64 * 4 ? 4 * TB : 4 * NX * 64 * 4;
+  __shared__ __attribute__((aligned(16))) char stage[SZ];
   const int head = blockIdx.x;
   const int b = head / p.n_local, l = head - b * p.n_local;
   const int nqt = (p.seq + 127) / 128;
@@ -325,19 +334,13 @@ __global__ __launch_bounds__(64 * FWD_WAVES) void fwd_mfma(MP p, FwdItems items)
   // key tiles [ktb, kte): all of them, or one half of a split item (every
   // query of a split tile has keys in both halves)
   const int ktb = part == 2 ? nkt / 2 : 0, kte = part == 1 ? nkt / 2 : nkt;
-  dma_tile<D, FWD_WAVES>(p.kh, nrec, stage, grow0, l * D, ktb * TROWS, p.seq, p.h_l, w, lane);
-  dma_tile<D, FWD_WAVES>(p.kl, nrec, stage + TB, grow0, l * D, ktb * TROWS, p.seq, p.h_l, w, lane);
-  dma_tile<D, FWD_WAVES>(p.vh, nrec, stage + 2 * TB, grow0, l * D, ktb * TROWS, p.seq, p.h_l, w, lane);
+  dma_tile<D, FWD_WAVES>(p.k16, nrec, stage, grow0, l * D, ktb * TROWS, p.seq, p.h_l, w, lane);
+  dma_tile<D, FWD_WAVES>(p.vh, nrec, stage + TB, grow0, l * D, ktb * TROWS, p.seq, p.h_l, w, lane);
   FwdState<D> st;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     st.qf[c] = bf16x8{};
-    st.qfl[c] = bf16x8{};
-    if (myq < p.seq) {
-      const long off = (grow0 + myq) * p.h_l + (long)l * D + 16 * c + 8 * g;
-      st.qf[c] = ld8(p.qh + off);
-      st.qfl[c] = ld8(p.ql + off);
-    }
+    if (myq < p.seq) st.qf[c] = ld8(p.q16 + (grow0 + myq) * p.h_l + (long)l * D + 16 * c + 8 * g);
   }
 #pragma unroll
   for (int db = 0; db < NB; ++db) st.o[db] = f32x16{};
@@ -349,13 +352,12 @@ __global__ __launch_bounds__(64 * FWD_WAVES) void fwd_mfma(MP p, FwdItems items)
   for (int kt = ktb; kt < kte; ++kt) {
     loads_landed_barrier();  // tile kt is in LDS; tile kt-1 is no longer read
     const bool odd = (kt - ktb) & 1;
-    const char* cur = odd ? stage + 3 * TB : stage;
-    char* nxt = odd ? stage : stage + 3 * TB;
+    const char* cur = odd ? stage + 2 * TB : stage;
+    char* nxt = odd ? stage : stage + 2 * TB;
     const int kv0 = kt * TROWS;
     if (kt + 1 < kte) {
-      dma_tile<D, FWD_WAVES>(p.kh, nrec, nxt, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
-      dma_tile<D, FWD_WAVES>(p.kl, nrec, nxt + TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
-      dma_tile<D, FWD_WAVES>(p.vh, nrec, nxt + 2 * TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
+      dma_tile<D, FWD_WAVES>(p.k16, nrec, nxt, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
+      dma_tile<D, FWD_WAVES>(p.vh, nrec, nxt + TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
     }
     const int k0 = kv0 + 32 * kh;
     if (k0 <= q0w + 31 && k0 < p.seq)  // wave-uniform; otherwise every key is masked
@@ -459,7 +461,7 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(MP p, int q_first) {
 // ---- backward: dK, dV ---------------------------------------------------------------
 template <int D>
 struct KvState {
-  bf16x8 kf[D / 16], kfl[D / 16], vf[D / 16];
+  bf16x8 kf[D / 16], vf[D / 16];  // k16 (fp16 bits), v
   f32x16 dv[D / 32], dk[D / 32];
 };
 
@@ -478,10 +480,9 @@ __device__ __forceinline__ void dma_stats(const MP& p, char* stage_stats, int he
 // each); this key is bit qk; pv becomes P * keep * scale (for dV) and dP is
 // multiplied by keep * scale.
 template <bool MASK, bool AL, bool DO>
-__device__ __forceinline__ void kv_probs(const f32x16& sa, const f32x16& sc, const f32x16& dp, const float* sL,
-                                         const float* sDl, float (&pv)[16], float (&dsv)[16], float scale_log2,
-                                         float slope2, int qs0, int g, int myk, int seq, const uint64_t (&kw)[4],
-                                         int qk, float dscale) {
+__device__ __forceinline__ void kv_probs(const f32x16& sa, const f32x16& dp, const float* sL, const float* sDl,
+                                         float (&pv)[16], float (&dsv)[16], float slope2, int qs0, int g, int myk,
+                                         int seq, const uint64_t (&kw)[4], int qk, float dscale) {
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
     const f32x4 L = *(const f32x4*)(sL + 8 * q4 + 4 * g);
@@ -490,7 +491,7 @@ __device__ __forceinline__ void kv_probs(const f32x16& sa, const f32x16& sc, con
     for (int e = 0; e < 4; ++e) {
       const int q = 4 * q4 + e;
       const int query = qs0 + 8 * q4 + 4 * g + e;
-      float v = (sc[q] + sa[q]) * scale_log2 - L[e] * kLog2e;
+      float v = sa[q] - L[e] * kLog2e;
       if (AL) v -= slope2 * (float)(query - myk);
       float pp = fexp2(v);
       if (MASK && (query < myk || query >= seq)) pp = 0.f;
@@ -506,7 +507,7 @@ __device__ __forceinline__ void kv_probs(const f32x16& sa, const f32x16& sc, con
   }
 }
 
-// One 64-query tile from stage `cur` (Q hi, Q lo, dctx, then lse, delta).
+// One 64-query tile from stage `cur` (Q16, Q bf16, dctx, then lse, delta).
 template <int D, bool AL, bool DO>
 __device__ __forceinline__ void dkdv_tile(const MP& p, const char* __restrict__ cur, char* __restrict__ nxt,
                                           bool issue, int q0, int head, int l, long grow0, int w, int lane, int k0w,
@@ -516,8 +517,8 @@ __device__ __forceinline__ void dkdv_tile(const MP& p, const char* __restrict__ 
   const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
   if (issue) {
     const int qn = q0 + TROWS;
-    dma_tile<D>(p.qh, nrec, nxt, grow0, l * D, qn, p.seq, p.h_l, w, lane);
-    dma_tile<D>(p.ql, nrec, nxt + TB, grow0, l * D, qn, p.seq, p.h_l, w, lane);
+    dma_tile<D>(p.q16, nrec, nxt, grow0, l * D, qn, p.seq, p.h_l, w, lane);
+    dma_tile<D>(p.qb, nrec, nxt + TB, grow0, l * D, qn, p.seq, p.h_l, w, lane);
     dma_tile<D>(p.dctx, nrec, nxt + 2 * TB, grow0, l * D, qn, p.seq, p.h_l, w, lane);
     dma_stats(p, nxt + 3 * TB, head, qn, w, lane);
   }
@@ -529,13 +530,10 @@ __device__ __forceinline__ void dkdv_tile(const MP& p, const char* __restrict__ 
   for (int qs = 0; qs < 2; ++qs) {
     const int qs0 = q0 + 32 * qs;
     if (qs0 + 31 < k0w || qs0 >= p.seq) continue;  // wave-uniform: all masked
-    f32x16 sa = f32x16{}, sc = f32x16{}, dp = f32x16{};
+    f32x16 sa = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const bf16x8 qh = frag_row(cur, qs, c, ro), ql = frag_row(cur + TB, qs, c, ro);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql, st.kf[c], sc, 0, 0, 0);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, st.kfl[c], sc, 0, 0, 0);
-      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, st.kf[c], sa, 0, 0, 0);
+      sa = mfma_f16(frag_row(cur, qs, c, ro), st.kf[c], sa);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(cur + 2 * TB, qs, c, ro), st.vf[c], dp, 0, 0, 0);
     }
     // s[q], dp[q]: query qs0 + 8(q>>2) + 4g + (q&3), key myk
@@ -553,11 +551,11 @@ __device__ __forceinline__ void dkdv_tile(const MP& p, const char* __restrict__ 
     }
     float pv[16], dsv[16];
     if ((qs0 < k0w + 31) || (qs0 + 32 > p.seq))
-      kv_probs<true, AL, DO>(sa, sc, dp, sL + 32 * qs, sDl + 32 * qs, pv, dsv, p.scale_log2, slope2, qs0, g, myk,
-                             p.seq, kw, qk, p.drop_scale);
+      kv_probs<true, AL, DO>(sa, dp, sL + 32 * qs, sDl + 32 * qs, pv, dsv, slope2, qs0, g, myk, p.seq, kw, qk,
+                             p.drop_scale);
     else
-      kv_probs<false, AL, DO>(sa, sc, dp, sL + 32 * qs, sDl + 32 * qs, pv, dsv, p.scale_log2, slope2, qs0, g, myk,
-                              p.seq, kw, qk, p.drop_scale);
+      kv_probs<false, AL, DO>(sa, dp, sL + 32 * qs, sDl + 32 * qs, pv, dsv, slope2, qs0, g, myk, p.seq, kw, qk,
+                              p.drop_scale);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const bf16x8 pf = pack8(pv + 8 * h), df = pack8(dsv + 8 * h);
@@ -565,8 +563,8 @@ __device__ __forceinline__ void dkdv_tile(const MP& p, const char* __restrict__ 
       for (int db = 0; db < NB; ++db) {
         st.dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(cur + 2 * TB, db, 2 * qs + h, tro), pf,
                                                             st.dv[db], 0, 0, 0);
-        st.dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(cur, db, 2 * qs + h, tro), df, st.dk[db], 0,
-                                                            0, 0);
+        st.dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(cur + TB, db, 2 * qs + h, tro), df, st.dk[db],
+                                                            0, 0, 0);
       }
     }
   }
@@ -587,20 +585,18 @@ __device__ __forceinline__ void dkdv_item(const MP& p, int head, int kvt, char* 
   const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
   const int nqt = (p.seq + TROWS - 1) / TROWS;
   const int qt0 = (kvt * 128) / TROWS;
-  dma_tile<D>(p.qh, nrec, st0, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, lane);
-  dma_tile<D>(p.ql, nrec, st0 + TB, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, lane);
+  dma_tile<D>(p.q16, nrec, st0, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, lane);
+  dma_tile<D>(p.qb, nrec, st0 + TB, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, lane);
   dma_tile<D>(p.dctx, nrec, st0 + 2 * TB, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, lane);
   dma_stats(p, st0 + 3 * TB, head, qt0 * TROWS, w, lane);
   KvState<D> st;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     st.kf[c] = bf16x8{};
-    st.kfl[c] = bf16x8{};
     st.vf[c] = bf16x8{};
     if (myk < p.seq) {
       const long off = (grow0 + myk) * p.h_l + (long)l * D + 16 * c + 8 * g;
-      st.kf[c] = ld8(p.kh + off);
-      st.kfl[c] = ld8(p.kl + off);
+      st.kf[c] = ld8(p.k16 + off);
       st.vf[c] = ld8(p.vh + off);
     }
   }
@@ -641,7 +637,7 @@ __device__ __forceinline__ void dkdv_item(const MP& p, int head, int kvt, char* 
 // ---- backward: dQ ----------------------------------------------------------------
 template <int D>
 struct QState {
-  bf16x8 qf[D / 16], qfl[D / 16], cf[D / 16];
+  bf16x8 qf[D / 16], cf[D / 16];  // q16 (fp16 bits), dctx
   f32x16 dq[D / 32];
   float L, Dl;
 };
@@ -649,13 +645,12 @@ struct QState {
 // dS of one 32-key block for this lane's query (MASK as in fwd_scores).
 // DO: bit q of `bits` keeps lane q's key; dP is multiplied by keep * scale.
 template <bool MASK, bool AL, bool DO>
-__device__ __forceinline__ void q_dscores(const f32x16& sa, const f32x16& sc, const f32x16& dp, float (&ds)[16],
-                                          float scale_log2, float slope2, float L, float Dl, int k0, int g, int myq,
-                                          int seq, uint32_t bits, float dscale) {
+__device__ __forceinline__ void q_dscores(const f32x16& sa, const f32x16& dp, float (&ds)[16], float slope2, float L,
+                                          float Dl, int k0, int g, int myq, int seq, uint32_t bits, float dscale) {
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int key = k0 + 8 * (q >> 2) + 4 * g + (q & 3);
-    float v = (sc[q] + sa[q]) * scale_log2 - L;
+    float v = sa[q] - L;
     if (AL) v -= slope2 * (float)(myq - key);
     float pp = fexp2(v);
     if (MASK && (key > myq || key >= seq)) pp = 0.f;
@@ -664,7 +659,7 @@ __device__ __forceinline__ void q_dscores(const f32x16& sa, const f32x16& sc, co
   }
 }
 
-// One 64-key tile from stage `cur` (K hi, K lo, V).
+// One 64-key tile from stage `cur` (K16, K bf16, V).
 template <int D, bool AL, bool DO>
 __device__ __forceinline__ void dq_tile(const MP& p, const char* __restrict__ cur, char* __restrict__ nxt, bool issue,
                                         int kv0, int l, long grow0, int w, int lane, int q0w, int myq, float slope2,
@@ -672,8 +667,8 @@ __device__ __forceinline__ void dq_tile(const MP& p, const char* __restrict__ cu
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
   const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
   if (issue) {
-    dma_tile<D>(p.kh, nrec, nxt, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
-    dma_tile<D>(p.kl, nrec, nxt + TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
+    dma_tile<D>(p.k16, nrec, nxt, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
+    dma_tile<D>(p.kb, nrec, nxt + TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
     dma_tile<D>(p.vh, nrec, nxt + 2 * TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
   }
   const int g = lane >> 5;
@@ -681,13 +676,10 @@ __device__ __forceinline__ void dq_tile(const MP& p, const char* __restrict__ cu
   for (int sb = 0; sb < 2; ++sb) {
     const int k0 = kv0 + 32 * sb;
     if (k0 > q0w + 31 || k0 >= p.seq) continue;
-    f32x16 sa = f32x16{}, sc = f32x16{}, dp = f32x16{};
+    f32x16 sa = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const bf16x8 kh = frag_row(cur, sb, c, ro), kl = frag_row(cur + TB, sb, c, ro);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, st.qf[c], sc, 0, 0, 0);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, st.qfl[c], sc, 0, 0, 0);
-      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, st.qf[c], sa, 0, 0, 0);
+      sa = mfma_f16(frag_row(cur, sb, c, ro), st.qf[c], sa);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(cur + 2 * TB, sb, c, ro), st.cf[c], dp, 0, 0, 0);
     }
     // s[q]: key k0 + 8(q>>2) + 4g + (q&3), query myq
@@ -696,16 +688,15 @@ __device__ __forceinline__ void dq_tile(const MP& p, const char* __restrict__ cu
       bits = p.mask[((long)(head * p.nkb + (k0 >> 5)) * 2 + g) * p.mstride + min(myq, p.seq - 1)];
     float ds[16];
     if ((k0 + 31 > q0w) || (k0 + 32 > p.seq))
-      q_dscores<true, AL, DO>(sa, sc, dp, ds, p.scale_log2, slope2, st.L, st.Dl, k0, g, myq, p.seq, bits,
-                              p.drop_scale);
+      q_dscores<true, AL, DO>(sa, dp, ds, slope2, st.L, st.Dl, k0, g, myq, p.seq, bits, p.drop_scale);
     else
-      q_dscores<false, AL, DO>(sa, sc, dp, ds, p.scale_log2, slope2, st.L, st.Dl, k0, g, myq, p.seq, bits,
-                               p.drop_scale);
+      q_dscores<false, AL, DO>(sa, dp, ds, slope2, st.L, st.Dl, k0, g, myq, p.seq, bits, p.drop_scale);
     const bf16x8 df0 = pack8(ds), df1 = pack8(ds + 8);
+    const char* kbt = cur + TB;
 #pragma unroll
     for (int db = 0; db < NB; ++db) {
-      st.dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(cur, db, 2 * sb, tro), df0, st.dq[db], 0, 0, 0);
-      st.dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(cur, db, 2 * sb + 1, tro), df1, st.dq[db], 0, 0, 0);
+      st.dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(kbt, db, 2 * sb, tro), df0, st.dq[db], 0, 0, 0);
+      st.dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(kbt, db, 2 * sb + 1, tro), df1, st.dq[db], 0, 0, 0);
     }
   }
 }
@@ -725,19 +716,17 @@ __device__ __forceinline__ void dq_item(const MP& p, int head, int qt, char* __r
   const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
   const int kv_end = min(p.seq, qt * 128 + 128);
   const int nkt = (kv_end + TROWS - 1) / TROWS;
-  dma_tile<D>(p.kh, nrec, st0, grow0, l * D, 0, p.seq, p.h_l, w, lane);
-  dma_tile<D>(p.kl, nrec, st0 + TB, grow0, l * D, 0, p.seq, p.h_l, w, lane);
+  dma_tile<D>(p.k16, nrec, st0, grow0, l * D, 0, p.seq, p.h_l, w, lane);
+  dma_tile<D>(p.kb, nrec, st0 + TB, grow0, l * D, 0, p.seq, p.h_l, w, lane);
   dma_tile<D>(p.vh, nrec, st0 + 2 * TB, grow0, l * D, 0, p.seq, p.h_l, w, lane);
   QState<D> st;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     st.qf[c] = bf16x8{};
-    st.qfl[c] = bf16x8{};
     st.cf[c] = bf16x8{};
     if (myq < p.seq) {
       const long off = (grow0 + myq) * p.h_l + (long)l * D + 16 * c + 8 * g;
-      st.qf[c] = ld8(p.qh + off);
-      st.qfl[c] = ld8(p.ql + off);
+      st.qf[c] = ld8(p.q16 + off);
       st.cf[c] = ld8(p.dctx + off);
     }
   }
@@ -788,9 +777,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ---- q/k/v split ------------------------------------------------------------------
-// out = [q_hi | q_lo | k_hi | k_lo | v] as five [T, h_l] bf16 arrays; hi is the
-// round-to-nearest bf16 of x, lo that of x - hi.
-__global__ __launch_bounds__(256) void split_qkv_kernel(const float* qkv, bf16* out, long T, int h_l) {
+// out = [q16 | qb | k16 | kb | v] as five [T, h_l] 16-bit arrays: q16 =
+// fp16(q qscale) with qscale = log2(e) / sqrt(D), k16 = fp16(k) (both rounded
+// to nearest and saturated to +-65504), qb, kb, v the round-to-nearest bf16
+// of q, k, v.
+__device__ __forceinline__ bf16 f16_bits(float x) {
+  x = fminf(fmaxf(x, -65504.0f), 65504.0f);
+  return __builtin_bit_cast(bf16, (_Float16)x);
+}
+__global__ __launch_bounds__(256) void split_qkv_kernel(const float* qkv, bf16* out, long T, int h_l, float qscale) {
   const long n8 = T * 3L * h_l / 8;
   const long plane = T * (long)h_l;
   const long stride = (long)gridDim.x * 256;
@@ -801,14 +796,14 @@ __global__ __launch_bounds__(256) void split_qkv_kernel(const float* qkv, bf16* 
     const int part = col / h_l, c = col - part * h_l;
     const f32x4 a = *(const f32x4*)(qkv + e0), b = *(const f32x4*)(qkv + e0 + 4);
     const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    bf16x8 hi, lo;
+    bf16x8 h16, hb;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      hi[e] = (bf16)x[e];
-      lo[e] = (bf16)(x[e] - (float)hi[e]);
+      h16[e] = f16_bits(part == 0 ? x[e] * qscale : x[e]);
+      hb[e] = (bf16)x[e];
     }
-    *(bf16x8*)(out + 2 * part * plane + t * h_l + c) = hi;
-    if (part < 2) *(bf16x8*)(out + (2 * part + 1) * plane + t * h_l + c) = lo;
+    if (part < 2) *(bf16x8*)(out + 2 * part * plane + t * h_l + c) = h16;
+    *(bf16x8*)(out + (part < 2 ? 2 * part + 1 : 4) * plane + t * h_l + c) = hb;
   }
 }
 
@@ -819,7 +814,9 @@ hipError_t split_launch(const AttnDesc& a, hipStream_t stream) {
   long grid = (n8 + 255) / 256;
   if (grid > 8192) grid = 8192;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(split_qkv_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a.qkv, (bf16*)a.split, T, h_l);
+  const float qscale = kLog2e / sqrtf((float)a.head_dim);
+  hipLaunchKernelGGL(split_qkv_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a.qkv, (bf16*)a.split, T, h_l,
+                     qscale);
   return hipGetLastError();
 }
 
@@ -830,11 +827,10 @@ MP make_mp(const AttnDesc& a) {
   p.T = (long)a.batch * a.seq;
   const bf16* sp = (const bf16*)a.split;
   const long plane = p.T * p.h_l;
-  p.qh = sp; p.ql = sp + plane; p.kh = sp + 2 * plane; p.kl = sp + 3 * plane; p.vh = sp + 4 * plane;
+  p.q16 = sp; p.qb = sp + plane; p.k16 = sp + 2 * plane; p.kb = sp + 3 * plane; p.vh = sp + 4 * plane;
   p.ctx = (bf16*)a.ctx; p.lse = a.lse;
   p.dctx = (const bf16*)a.dctx; p.delta = a.delta; p.dqkv = (bf16*)a.dqkv;
   p.scale = 1.0f / sqrtf((float)a.head_dim);
-  p.scale_log2 = p.scale * kLog2e;
   p.mask = a.mask;
   p.nkb = (a.seq + 31) / 32;
   p.mstride = (a.seq + 7) & ~7;

@@ -47,8 +47,8 @@ size_t gemm_workspace_bytes(int dtype, int M, int N, int K);
 hipError_t gemm_launch(int dtype, const GemmDesc& g, void* ws, size_t ws_bytes, hipStream_t stream);
 
 // Attention on the packed per-rank qkv [T, 3*h_l] = [Q | K | V].
-// qkv is fp32 for both storage types (scores are formed from split-bf16
-// q and k on the matrix cores); ctx, dctx and dqkv use the storage type.
+// qkv is fp32 for both storage types (the matrix-core path forms the scores
+// from fp16 copies of q and k); ctx, dctx and dqkv use the storage type.
 struct AttnDesc {
   int batch = 0, seq = 0, n_local = 0, head_dim = 0;
   int head0 = 0;       // 0-based global index of local head 0 (rank * n_local)
@@ -61,8 +61,9 @@ struct AttnDesc {
   const void* dctx = nullptr;  // [T, h_l]
   float* delta = nullptr;      // [batch, n_local, seq] scratch: rowsum(dctx * ctx)
   void* dqkv = nullptr;        // [T, 3*h_l]
-  // matrix-core path only: workspace for q/k/v split into bf16 hi/lo parts,
-  // attn_split_bytes() bytes (5 arrays [T, h_l] bf16)
+  // matrix-core path only: workspace for the 16-bit copies of q, k, v
+  // (fp16 q and k for the scores, bf16 q, k, v), attn_split_bytes() bytes
+  // (5 arrays [T, h_l])
   void* split = nullptr;
   // attention-probability dropout (matrix-core path only; enabled when mask is
   // set): keep bits [batch][n_local][ceil(seq/32)][2][seq rounded up to 8],

@@ -9,9 +9,8 @@ import oracle
 # Relative Frobenius bound per storage type (the stated bar); the element-wise
 # bound |gpu - ref| <= a * scale + b * |ref| catches a localized error (a wrong
 # tile errs by ~rms) that a norm over millions of elements hides. One band for
-# every output (qkv is kept in fp32 and the scores are formed from split-bf16 q
-# and k, good to ~2^-16, so the outputs downstream of the softmax need no wider
-# band). `scale` is the larger of the output's rms and the rms of the
+# every output (qkv is kept in fp32 and the scores are formed from fp16 q and
+# k, so the outputs downstream of the softmax need no wider band). `scale` is the larger of the output's rms and the rms of the
 # element's own row: the rounding of a bf16 intermediate errs in proportion to
 # the magnitudes of its row, and some rows are far above the average (the first
 # token's key and value gradients collect every query's contribution; in a
