@@ -690,16 +690,28 @@ __device__ __forceinline__ void fixup_body(const KParams& p, int first_tile) {
 // so the weight goes through the transposing reads twice per k-step (the 4x2
 // layout of the 32x32 tile needs four). The B stage is [64 k-rows][40 chunks]
 // (640 bytes per k-row); logical chunk lc of k-row kr sits at physical chunk
-// 8(lc/8) + ((lc%8) ^ 2((kr + kr/8) % 4)), so the four k-rows one 16-lane group
-// of a transposing read touches land in four different 32-byte bank groups
-// (and two such groups served together differ in k-row parity). Operands are
+// 8(lc/8) + ((lc%8) ^ f(kr)), f(kr) = 2(((kr%8) + s(kr/8)) % 4) with
+// s(G) = (G%4) ^ ((G%4)/2), so the four k-rows one 16-lane group of a
+// transposing read touches land in four different 32-byte bank groups, and
+// the k-rows of lane groups served together differ in f or in parity.
+// Permuted k slots: lane group g of the 16x16x32 MFMA holds the 8 k of
+// logical chunk 4kk + t(g) of the sub-step, t = (0, 2, 1, 3), in both
+// operands (the sum over k is unchanged). A 128-bit LDS read serves lanes
+// {s..s+7} and {s+32..s+39} together; with t(g) = g those lanes read the same
+// eight A rows at chunks c and c ^ 2, which share banks (measured: 4 conflict
+// cycles per read, twice the cycles of the 32x32 kernels' reads), with t they
+// read chunks of opposite parity and do not conflict. Operands are
 // swapped in the MFMA as in the 32x32 kernels: each lane owns one m and four
 // consecutive n of a 16x16 block. Data-parallel plans only (N a multiple of
 // 320, whole rounds of tiles); a K that is not a multiple of 64 ends in a
 // partial k-step whose A chunks past K read zeros (the one k-step that loads
 // it checks them). Other shapes take the 256-wide tile.
 struct PanelB320 { const bf16* base; uint32_t nrec, kstep; uint32_t voff[5]; };
-__device__ __forceinline__ int b320_swz(int kr) { return 2 * ((kr + (kr >> 3)) & 3); }
+__device__ __forceinline__ int b320_swz(int kr) {
+  const int G = (kr >> 3) & 3;
+  return 2 * (((kr & 7) + (G ^ (G >> 1))) & 3);
+}
+__device__ __forceinline__ int kslot16(int g) { return ((g & 1) << 1) | (g >> 1); }  // t(g)
 // physical chunk q of the stage (64 k-rows x 40 chunks) holds logical chunk lc of k-row kr
 __device__ __forceinline__ PanelB320 panel_b320(const bf16* B, long ld, int N, int K, int n0, int wave, int lane) {
   PanelB320 pn;
@@ -813,16 +825,17 @@ __device__ __forceinline__ void fwd320_body(const KParams& p, bf16* smem) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = (int)uni((uint32_t)(tid >> 6));
   const int wm = wave >> 2, wn = wave & 3, l16 = lane & 15, g = lane >> 4;
-  // A fragment of block i, sub-step kk: row wm*128 + 16i + l16, k chunk 4kk + g,
-  // stored at chunk (4kk + g) ^ swz(row) = abase ^ 4kk ^ 2(i & 3) (the k-inner
-  // swizzle (r ^ r>>3) & 7 restricted to these rows)
+  // A fragment of block i, sub-step kk: row wm*128 + 16i + l16, k chunk
+  // 4kk + t(g), stored at chunk (4kk + t(g)) ^ swz(row) = abase ^ 4kk ^ 2(i & 3)
+  // (the k-inner swizzle (r ^ r>>3) & 7 restricted to these rows)
+  const int tg = kslot16(g);
   const int aoff0 = (wm * 128 + l16) * 128;
-  const int abase = g ^ ((l16 & 7) ^ (l16 >> 3));
-  // B fragment of block j: this lane addresses k-row 8g + r' (+ 32kk, + 4 for
-  // the second read) and column quad c' = l16 & 3, i.e. logical chunk
+  const int abase = tg ^ ((l16 & 7) ^ (l16 >> 3));
+  // B fragment of block j: this lane addresses k-row 8t(g) + r' (+ 32kk, + 4
+  // for the second read) and column quad c' = l16 & 3, i.e. logical chunk
   // lc = wn*10 + 2j + c'/2 at physical 8(lc/8) + ((lc%8) ^ f), f = b320_swz of
-  // that k-row = 2((r' + g) % 4) for every kk and read
-  const int rp = l16 >> 2, cq = l16 & 3, f = 2 * ((rp + g) & 3);
+  // that k-row, the same for every kk and read
+  const int rp = l16 >> 2, cq = l16 & 3, f = b320_swz(8 * tg + rp);
   for (int r = 0; r < p.dp_rounds; ++r) {
     const int t = r * p.grid + lw;
     int tm, tn;
@@ -840,7 +853,7 @@ __device__ __forceinline__ void fwd320_body(const KParams& p, bf16* smem) {
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
       const int lc = wn * 10 + 2 * j + (cq >> 1);
-      boff[j] = (8 * g + rp) * 640 + (8 * (lc >> 3) + ((lc & 7) ^ f)) * 16 + 8 * (cq & 1);
+      boff[j] = (8 * tg + rp) * 640 + (8 * (lc >> 3) + ((lc & 7) ^ f)) * 16 + 8 * (cq & 1);
     }
     // only the k-step that loads a partial last k-step (K not a multiple of
     // 64) checks the A chunks against K: the loop is split around it
