@@ -140,6 +140,21 @@ PARITY_OUTS = ("qkv", "ctx", "lse", "O", "pre", "y", "Z", "dX_mlp", "dA", "db1",
                "dbqkv", "dWo", "dbo")
 
 
+def saved_qkv_f64(buf, w):
+    """q | k | v [T, 3h_l] from the saved projection tp_attn_fwd wrote: the
+    bf16 planes 1, 3, 4 of the matrix-core layout, or the fp32 layout."""
+    import numpy as np
+    import torch
+    T, hl = w.tokens, w.h_local
+    b = buf.contiguous()
+    if w.dtype == "bf16" and w.head_dim in (64, 96, 128, 160):
+        n = T * hl
+        h16 = b[: 10 * n].view(torch.int16)
+        return np.concatenate([h16[k * n:(k + 1) * n].view(torch.bfloat16).double().reshape(T, hl).numpy()
+                               for k in (1, 3, 4)], axis=1)
+    return b[: 12 * T * hl].view(torch.float32).double().reshape(T, 3 * hl).numpy()
+
+
 def cpu_baseline(w, inp, target_s: float, gpu_out=None) -> dict:
     """The fp64 oracle, as it stands, on a bounded sample of the same workload:
     a sub-shard of this rank (its first n_sub heads and first f_sub FFN
@@ -197,7 +212,10 @@ def cpu_baseline(w, inp, target_s: float, gpu_out=None) -> dict:
         err = {}
         for k in PARITY_OUTS:
             if k in gpu_out and k in outs:
-                g, r = f64(gpu_out[k]).reshape(outs[k].shape), outs[k]
+                if k == "qkv":  # the saved projection's bf16 planes (q, k, v), or fp32
+                    g, r = saved_qkv_f64(gpu_out[k], w), outs[k]
+                else:
+                    g, r = f64(gpu_out[k]).reshape(outs[k].shape), outs[k]
                 nr = float(np.linalg.norm(r))
                 err[k] = float(np.linalg.norm(g - r)) / (nr if nr > 0 else 1.0)
         worst = max(err, key=err.get)

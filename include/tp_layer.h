@@ -114,7 +114,7 @@ tp_status tp_mlp_bwd(const tp_shape* shape, const void* X, const void* A_i, cons
                      size_t workspace_bytes, void* stream);
 
 /* Attention forward (Megatron-LM deep dive, Fig. 3b):
- *   qkv_i = X Wqkv_i + bqkv_i    (fp32 for both storage types, see below)
+ *   qkv_i = X Wqkv_i + bqkv_i    (saved in the form described below)
  *                                Wqkv_i [h,3h_l] = [Wq_i | Wk_i | Wv_i] (the
  *                                columns of this rank's heads), bqkv_i [3h_l];
  *                                local head l uses columns l*d..l*d+d-1 of each
@@ -123,14 +123,22 @@ tp_status tp_mlp_bwd(const tp_shape* shape, const void* X, const void* A_i, cons
  *   mask, row softmax, ctx = softmax(S) v; lse = log-sum-exp of each row of S
  *   O_i = ctx_i Wo_i             Wo_i [h_l,h] (row shard); O_i [T,h] is this
  *                                rank's PARTIAL sum; bo is not added.
- * Saved for backward: qkv_i [T,3h_l] fp32, ctx_i [T,h_l] (heads side by
- * side), lse_i [batch, n_l, seq] fp32. qkv_i is kept in fp32 because the
- * scores q.k/sqrt(d) can be large and nearly tied (rows sharper than bf16 can
- * resolve); the bf16 path forms them in one matrix-core product of fp16
- * copies of q and k (11-bit significands; values beyond the fp16 range,
- * |q log2(e)/sqrt(d)| or |k| above 65504, saturate). */
+ * Saved for backward: qkv_i (tp_attn_qkv_bytes bytes), ctx_i [T,h_l] (heads
+ * side by side), lse_i [batch, n_l, seq] fp32. The projection is saved at
+ * more than storage precision, because the scores q.k/sqrt(d) can be large and
+ * nearly tied (rows sharper than bf16 can resolve):
+ *   - dtype TP_BF16 with head_dim 64, 96, 128 or 160 (the matrix-core path):
+ *     five 16-bit planes [T,h_l] (x = the fp32 projection, rounded to
+ *     nearest), plane k at byte offset 2*k*T*h_l: 0 fp16(q log2(e)/sqrt(d)),
+ *     1 bf16(q), 2 fp16(k), 3 bf16(k), 4 bf16(v), where q, k, v are the three
+ *     thirds of qkv_i; the scores are one matrix-core product of the fp16
+ *     planes (11-bit significands; fp16 values saturate at +-65504), the
+ *     bf16 planes feed the gradient and value products;
+ *   - otherwise [T,3h_l] fp32.
+ * The backward reads the buffer as the forward wrote it. */
+size_t tp_attn_qkv_bytes(const tp_shape* shape);
 tp_status tp_attn_fwd(const tp_shape* shape, const void* X, const void* Wqkv_i, const void* bqkv_i,
-                      const void* Wo_i, float* qkv_i, void* ctx_i, float* lse_i, void* O_i,
+                      const void* Wo_i, void* qkv_i, void* ctx_i, float* lse_i, void* O_i,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Attention backward (Megatron-LM deep dive, Fig. 3b for the per-head split
@@ -144,7 +152,7 @@ tp_status tp_attn_fwd(const tp_shape* shape, const void* X, const void* Wqkv_i, 
  *   dX_i = dqkv Wqkv_i^T [T,h]   PARTIAL input gradient
  *   dbo = sum_t dO [h]           replicated bias; written only if dbo_or_null != NULL */
 tp_status tp_attn_bwd(const tp_shape* shape, const void* X, const void* Wqkv_i, const void* Wo_i,
-                      const float* qkv_i, const void* ctx_i, const float* lse_i, const void* dO,
+                      const void* qkv_i, const void* ctx_i, const float* lse_i, const void* dO,
                       void* dX_i, void* dWqkv_i, void* dbqkv_i, void* dWo_i, void* dbo_or_null,
                       void* workspace, size_t workspace_bytes, void* stream);
 
@@ -174,11 +182,11 @@ typedef struct {
 
 size_t tp_attn_dropout_mask_bytes(const tp_shape* shape);
 tp_status tp_attn_fwd_dropout(const tp_shape* shape, const tp_dropout* dropout, const void* X,
-                              const void* Wqkv_i, const void* bqkv_i, const void* Wo_i, float* qkv_i,
+                              const void* Wqkv_i, const void* bqkv_i, const void* Wo_i, void* qkv_i,
                               void* ctx_i, float* lse_i, uint16_t* mask_i, void* O_i, void* workspace,
                               size_t workspace_bytes, void* stream);
 tp_status tp_attn_bwd_dropout(const tp_shape* shape, const tp_dropout* dropout, const void* X,
-                              const void* Wqkv_i, const void* Wo_i, const float* qkv_i,
+                              const void* Wqkv_i, const void* Wo_i, const void* qkv_i,
                               const void* ctx_i, const float* lse_i, const uint16_t* mask_i,
                               const void* dO, void* dX_i, void* dWqkv_i, void* dbqkv_i, void* dWo_i,
                               void* dbo_or_null, void* workspace, size_t workspace_bytes, void* stream);

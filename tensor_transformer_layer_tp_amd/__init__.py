@@ -24,7 +24,7 @@ __all__ = [
     "tp_profile_collect", "STEPS", "tp_ln_workspace_bytes", "tp_ln_residual_fwd", "tp_ln_residual_bwd",
     "tp_vocab_workspace_bytes", "tp_vocab_ce_fwd", "tp_vocab_ce_combine", "tp_vocab_ce_bwd", "TpDropout",
     "tp_attn_dropout_mask_bytes", "tp_attn_fwd_dropout", "tp_attn_bwd_dropout", "tp_ln_dropout_mask_bytes",
-    "tp_ln_residual_fwd_dropout", "tp_ln_residual_bwd_dropout", "tp_ln_residual_bwd_noalloc",
+    "tp_ln_residual_fwd_dropout", "tp_ln_residual_bwd_dropout", "tp_ln_residual_bwd_noalloc", "tp_attn_qkv_bytes",
     "tp_ln_residual_bwd_noalloc_max_scratch_bytes",
 ]
 
@@ -72,6 +72,7 @@ _vp, _sz, _st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
 _SIGS = {
     "tp_mlp_workspace_bytes": (_sz, [ctypes.POINTER(TpShape)]),
     "tp_attn_workspace_bytes": (_sz, [ctypes.POINTER(TpShape)]),
+    "tp_attn_qkv_bytes": (_sz, [ctypes.POINTER(TpShape)]),
     "tp_mlp_fwd": (_st, [ctypes.POINTER(TpShape)] + [_vp] * 7 + [_vp, _sz, _vp]),
     "tp_mlp_bwd": (_st, [ctypes.POINTER(TpShape)] + [_vp] * 11 + [_vp, _sz, _vp]),
     "tp_attn_fwd": (_st, [ctypes.POINTER(TpShape)] + [_vp] * 8 + [_vp, _sz, _vp]),
@@ -184,6 +185,11 @@ def tp_mlp_workspace_bytes(shape: TpShape) -> int:
 
 def tp_attn_workspace_bytes(shape: TpShape) -> int:
     return load_library().tp_attn_workspace_bytes(ctypes.byref(shape))
+
+
+def tp_attn_qkv_bytes(shape: TpShape) -> int:
+    """Bytes of the saved projection qkv_i (five 16-bit planes on the matrix-core path, else fp32)."""
+    return load_library().tp_attn_qkv_bytes(ctypes.byref(shape))
 
 
 def tp_mlp_fwd(shape, X, A_i, b1_i, B_i, pre_i, y_i, Z_i, workspace=None, stream=None):

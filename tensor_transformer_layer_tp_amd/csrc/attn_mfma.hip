@@ -1,13 +1,12 @@
 // Flash-style causal attention for bf16 on CDNA4 matrix cores
 // (v_mfma_f32_32x32x16_bf16), head widths D in {64, 96, 128, 160}.
 //
-// Inputs: per rank, qkv [T, 3*h_l] = [Q | K | V] in fp32; local head l uses
-// columns l*D.. of each third; row t = b*seq + position. A split kernel first
-// writes five 16-bit arrays [T, h_l] to the workspace: q16 = fp16(q log2(e) /
-// sqrt(D)), k16 = fp16(k) for the scores, and qb = bf16(q), kb = bf16(k),
-// v = bf16(v) for the gradient and value products. Outputs: ctx [T, h_l]
-// bf16, lse [batch, n_local, seq] fp32 (natural log); backward dqkv
-// [T, 3*h_l] bf16.
+// Inputs: per rank, the QKV projection's five 16-bit planes [T, h_l] (written
+// by its GEMM epilogue; local head l uses columns l*D..; row t = b*seq +
+// position): q16 = fp16(q log2(e) / sqrt(D)), k16 = fp16(k) for the scores,
+// and qb = bf16(q), kb = bf16(k), v = bf16(v) for the gradient and value
+// products. Outputs: ctx [T, h_l] bf16, lse [batch, n_local, seq] fp32
+// (natural log); backward dqkv [T, 3*h_l] bf16.
 //
 // Precision: the scores are one fp16 product q16 k16^T (fp32 accumulation),
 // already in log2 units. Rows of large, nearly tied scores amplify the
@@ -15,7 +14,7 @@
 // k (8-bit significands) the 530B-like shard's input gradients move by 1.2e-2
 // relative, with fp16 (11 bits) by 1.5e-3. fp16 holds the scaled q and k of
 // these layers with room to spare (|q log2(e)/sqrt(D)|, |k| far below 65504;
-// larger values saturate to +-65504 in the split). V, P, dS and dctx enter
+// larger values saturate to +-65504). V, P, dS and dctx enter
 // the products as bf16 (their rounding is not amplified, and bf16 keeps the
 // gradients' fp32 range).
 //
@@ -776,56 +775,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   else dkdv_item<D, AL, DO>(p, head, r, st0, st1);
 }
 
-// ---- q/k/v split ------------------------------------------------------------------
-// out = [q16 | qb | k16 | kb | v] as five [T, h_l] 16-bit arrays: q16 =
-// fp16(q qscale) with qscale = log2(e) / sqrt(D), k16 = fp16(k) (both rounded
-// to nearest and saturated to +-65504), qb, kb, v the round-to-nearest bf16
-// of q, k, v.
-__device__ __forceinline__ bf16 f16_bits(float x) {
-  x = fminf(fmaxf(x, -65504.0f), 65504.0f);
-  return __builtin_bit_cast(bf16, (_Float16)x);
-}
-__global__ __launch_bounds__(256) void split_qkv_kernel(const float* qkv, bf16* out, long T, int h_l, float qscale) {
-  const long n8 = T * 3L * h_l / 8;
-  const long plane = T * (long)h_l;
-  const long stride = (long)gridDim.x * 256;
-  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
-    const long e0 = 8 * i;
-    const long t = e0 / (3L * h_l);
-    const int col = (int)(e0 - t * 3L * h_l);
-    const int part = col / h_l, c = col - part * h_l;
-    const f32x4 a = *(const f32x4*)(qkv + e0), b = *(const f32x4*)(qkv + e0 + 4);
-    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    bf16x8 h16, hb;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      h16[e] = f16_bits(part == 0 ? x[e] * qscale : x[e]);
-      hb[e] = (bf16)x[e];
-    }
-    if (part < 2) *(bf16x8*)(out + 2 * part * plane + t * h_l + c) = h16;
-    *(bf16x8*)(out + (part < 2 ? 2 * part + 1 : 4) * plane + t * h_l + c) = hb;
-  }
-}
-
-hipError_t split_launch(const AttnDesc& a, hipStream_t stream) {
-  const long T = (long)a.batch * a.seq;
-  const int h_l = a.n_local * a.head_dim;
-  const long n8 = T * 3L * h_l / 8;
-  long grid = (n8 + 255) / 256;
-  if (grid > 8192) grid = 8192;
-  if (grid < 1) grid = 1;
-  const float qscale = kLog2e / sqrtf((float)a.head_dim);
-  hipLaunchKernelGGL(split_qkv_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a.qkv, (bf16*)a.split, T, h_l,
-                     qscale);
-  return hipGetLastError();
-}
-
 MP make_mp(const AttnDesc& a) {
   MP p{};
   p.batch = a.batch; p.seq = a.seq; p.n_local = a.n_local;
   p.h_l = a.n_local * a.head_dim; p.head0 = a.head0; p.n_heads = a.n_heads; p.alibi = a.alibi;
   p.T = (long)a.batch * a.seq;
-  const bf16* sp = (const bf16*)a.split;
+  const bf16* sp = (const bf16*)a.qkv;  // the five planes the QKV projection wrote
   const long plane = p.T * p.h_l;
   p.q16 = sp; p.qb = sp + plane; p.k16 = sp + 2 * plane; p.kb = sp + 3 * plane; p.vh = sp + 4 * plane;
   p.ctx = (bf16*)a.ctx; p.lse = a.lse;
@@ -919,10 +874,6 @@ bool attn_mfma_supported(int dtype, int head_dim) {
   return dtype == DT_BF16 && (head_dim == 64 || head_dim == 96 || head_dim == 128 || head_dim == 160);
 }
 
-size_t attn_split_bytes(int dtype, int head_dim, long long T, long long h_l) {
-  return attn_mfma_supported(dtype, head_dim) ? (size_t)(5 * T * h_l * 2) : 0;
-}
-
 size_t attn_fwd_part_bytes(int dtype, int head_dim, int batch, int seq, int n_local) {
   if (!attn_mfma_supported(dtype, head_dim)) return 0;
   return (size_t)2 * batch * n_local * seq * (head_dim + 2) * sizeof(float);
@@ -954,15 +905,11 @@ hipError_t bwd_dispatch(const MP& p, int head_dim, hipStream_t stream) {
 }
 
 hipError_t attn_mfma_fwd(const AttnDesc& a, hipStream_t stream) {
-  hipError_t e = split_launch(a, stream);
-  if (e != hipSuccess) return e;
   const MP p = make_mp(a);
   return a.mask ? fwd_dispatch<true>(p, a.head_dim, stream) : fwd_dispatch<false>(p, a.head_dim, stream);
 }
 
 hipError_t attn_mfma_bwd(const AttnDesc& a, hipStream_t stream) {
-  hipError_t e = split_launch(a, stream);
-  if (e != hipSuccess) return e;
   const MP p = make_mp(a);
   return a.mask ? bwd_dispatch<true>(p, a.head_dim, stream) : bwd_dispatch<false>(p, a.head_dim, stream);
 }

@@ -245,7 +245,7 @@ SP make_sp(const AttnDesc& a) {
   SP p{};
   p.batch = a.batch; p.seq = a.seq; p.n_local = a.n_local; p.d = a.head_dim;
   p.h_l = a.n_local * a.head_dim; p.head0 = a.head0; p.n_heads = a.n_heads; p.alibi = a.alibi;
-  p.qkv = a.qkv; p.ctx = a.ctx; p.lse = a.lse; p.dctx = a.dctx; p.delta = a.delta; p.dqkv = a.dqkv;
+  p.qkv = (const float*)a.qkv; p.ctx = a.ctx; p.lse = a.lse; p.dctx = a.dctx; p.delta = a.delta; p.dqkv = a.dqkv;
   return p;
 }
 

@@ -83,6 +83,7 @@ struct KParams {
   bf16* C2; long ldc2;
   const bf16* bias;
   const bf16* aux; long ldaux;
+  int qkv_hl; float qscale;  // EPI_QKV_PLANES
   float* partials;    // [2*sk_grid][BM*BNV] (split tail: [splits*split_tiles][BM*BNV])
   // Split tail (splits > 1, instead of stream-K): after the data-parallel
   // rounds, workgroup lw < splits*split_tiles takes k-range lw / split_tiles of
@@ -380,10 +381,27 @@ __device__ __forceinline__ void epilogue_rows(const KParams& p, int tm, int tn, 
         const int n = tn * BNV + wn * WNW + j * 32 + q4 * 8 + (lane >> 5) * 4;
         if (n >= p.N) continue;
         float v[4] = {acc[j][4 * q4], acc[j][4 * q4 + 1], acc[j][4 * q4 + 2], acc[j][4 * q4 + 3]};
-        if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_F32) {
+        if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_F32 || EPI == EPI_QKV_PLANES) {
           bf16x4 bb = *(const bf16x4*)(p.bias + n);
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] += (float)bb[e];
+        }
+        if (EPI == EPI_QKV_PLANES) {
+          // the 4 columns lie in one third (hl is a multiple of 8)
+          const int part = n / p.qkv_hl, c = n - part * p.qkv_hl;
+          const long plane = (long)p.M * p.qkv_hl, off = (long)m * p.qkv_hl + c;
+          bf16x4 hb;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hb[e] = (bf16)v[e];
+          *(bf16x4*)(p.C + (part == 2 ? 4 * plane : (2 * part + 1) * plane) + off) = hb;
+          if (part < 2) {
+            const float sc = part == 0 ? p.qscale : 1.0f;
+            _Float16 h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = (_Float16)fminf(fmaxf(v[e] * sc, -65504.0f), 65504.0f);
+            *(bf16x4*)(p.C + 2 * part * plane + off) = __builtin_bit_cast(bf16x4, h);
+          }
+          continue;
         }
         if (EPI == EPI_DGELU) {
           bf16x4 pa = *(const bf16x4*)(p.aux + (long)m * p.ldaux + n);
@@ -428,7 +446,9 @@ __device__ __forceinline__ void epilogue_staged(const KParams& p, int tm, int tn
   constexpr int RB = BNV * ES, NCH = RB / 16;
   constexpr int LDS_BYTES = 2 * (BM + BNV) * BKK * 2;
   constexpr int PR = 256 * RB <= LDS_BYTES ? 256 : 128 * RB <= LDS_BYTES ? 128 : 64;
-  constexpr int NPASS = BM / PR, NIMG = EPI == EPI_BIAS_GELU ? 2 : 1;
+  // two images: GeLU's pre and y; the projection planes' fp16 score copies
+  // (and v) and then their bf16 copies
+  constexpr int NPASS = BM / PR, NIMG = (EPI == EPI_BIAS_GELU || EPI == EPI_QKV_PLANES) ? 2 : 1;
   constexpr int ITERS = PR * NCH / C::NTHR;
   static_assert(PR * NCH % C::NTHR == 0 && NCH >= 32 && PR % 32 == 0, "image layout");
   typedef __attribute__((address_space(3))) char lds_char;
@@ -458,7 +478,7 @@ __device__ __forceinline__ void epilogue_staged(const KParams& p, int tm, int tn
             const int nt = wn * C::WNW + j * 32 + q4 * 8 + 4 * hh, n = tn * BNV + nt;
             float v[4] = {acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]};
             if (n < p.N) {
-              if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_F32) {
+              if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_F32 || EPI == EPI_QKV_PLANES) {
                 const bf16x4 bb = *(const bf16x4*)(p.bias + n);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] += (float)bb[e];
@@ -477,6 +497,13 @@ __device__ __forceinline__ void epilogue_staged(const KParams& p, int tm, int tn
             lds_char* dst = img + rl * RB + pc * 16 + (nt * ES) % 16;
             if constexpr (ES == 4) {
               *(__attribute__((address_space(3))) f32x4*)dst = f32x4{v[0], v[1], v[2], v[3]};
+            } else if (EPI == EPI_QKV_PLANES && im == 0 && n < 2 * p.qkv_hl) {
+              // q and k columns, first image: fp16 score copies (q scaled)
+              const float sc = n < p.qkv_hl ? p.qscale : 1.0f;
+              _Float16 hv[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) hv[e] = (_Float16)fminf(fmaxf(v[e] * sc, -65504.0f), 65504.0f);
+              *(__attribute__((address_space(3))) bf16x4*)dst = __builtin_bit_cast(bf16x4, hv);
             } else {
               bf16x4 o;
 #pragma unroll
@@ -493,6 +520,14 @@ __device__ __forceinline__ void epilogue_staged(const KParams& p, int tm, int tn
         const unsigned lin = (unsigned)(it * C::NTHR + tid), rl = lin / NCH, c = lin - rl * NCH;
         const u32x4 v = *(__attribute__((address_space(3))) const u32x4*)(img + rl * RB + ((c + rl) % NCH) * 16);
         const int gm = tm * BM + ps * PR + (int)rl, gn = tn * BNV + (int)c * (16 / ES);
+        if (EPI == EPI_QKV_PLANES) {
+          // 8 columns of one third: its plane for this image (v has none in the second)
+          const int part = gn / p.qkv_hl, cc = gn - part * p.qkv_hl;
+          const int pl = part < 2 ? 2 * part + im : (im == 0 ? 4 : -1);
+          if (gm < p.M && gn < p.N && pl >= 0)
+            *(u32x4*)(p.C + (long)pl * p.M * p.qkv_hl + (long)gm * p.qkv_hl + cc) = v;
+          continue;
+        }
         if (gm < p.M && gn < p.N) *(u32x4*)(out + ((long)gm * ld + gn) * ES) = v;
       }
       lds_only_barrier();  // the image (or the next tile's loads) overwrites this pass
@@ -501,7 +536,10 @@ __device__ __forceinline__ void epilogue_staged(const KParams& p, int tm, int tn
 }
 
 // Whole-tile epilogue: through LDS, except the fp32 output (its direct stores
-// already write 16 bytes per lane, and its image would take two passes).
+// already write 16 bytes per lane, and its image would take two passes). The
+// projection's 16-bit planes go through LDS: stored straight from the
+// accumulators they took 8-byte stores into five planes (+20% on the
+// GPT-2-like projection).
 template <int NW, int BNV, int EPI>
 __device__ __forceinline__ void epilogue_tile(const KParams& p, int tm, int tn,
                                               const f32x16 (&acc)[WC<NW, BNV>::MI][WC<NW, BNV>::NJ], bf16* smem) {
@@ -900,7 +938,10 @@ __device__ __forceinline__ void fwd320_body(const KParams& p, bf16* smem) {
 // of 320. Only the vocabulary-parallel weight gradient keeps 4 waves with
 // both operands k-outer.
 // forward products: A k-inner (activations), B k-outer (weights)
-TP_GEMM_KERNELS(gemm_qkv_proj, 8, 256, true, false, EPI_BIAS_F32)
+// the QKV projection writes the attention's 16-bit operand planes (matrix-core
+// attention) or fp32 q, k, v (the vector-ALU attention)
+TP_GEMM_KERNELS(gemm_qkv_proj, 8, 256, true, false, EPI_QKV_PLANES)
+TP_GEMM_KERNELS(gemm_qkv_proj_f32, 8, 256, true, false, EPI_BIAS_F32)
 TP_GEMM_KERNELS(gemm_out_proj, 8, 256, true, false, EPI_STORE)
 TP_GEMM_KERNELS(gemm_fc1_bias_gelu, 8, 256, true, false, EPI_BIAS_GELU)
 TP_GEMM_KERNELS(gemm_fc2, 8, 256, true, false, EPI_STORE)
@@ -1042,7 +1083,10 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
   case R: mk = NAME; fk = NAME##_fixup; mkw = NAME##_n320; fkw = NAME##_n320_fixup; nw = NWV; ak = AKV; \
     bk = BKV; ep = EV; break;
   switch (g.role) {
-    TP_ROLE(GR_QKV_PROJ, gemm_qkv_proj, 8, true, false, EPI_BIAS_F32)
+    case GR_QKV_PROJ:
+      if (g.epi == EPI_QKV_PLANES) { mk = gemm_qkv_proj; fk = gemm_qkv_proj_fixup; }
+      else { mk = gemm_qkv_proj_f32; fk = gemm_qkv_proj_f32_fixup; }
+      nw = 8; ep = g.epi == EPI_QKV_PLANES ? EPI_QKV_PLANES : EPI_BIAS_F32; break;
     case GR_OUT_PROJ: mk = gemm_out_proj; fk = gemm_out_proj_fixup; mkf = gemm_out_proj_n320; nw = 8; ep = EPI_STORE; break;
     TP_ROLE(GR_FC1, gemm_fc1_bias_gelu, 8, true, false, EPI_BIAS_GELU)
     case GR_FC2: mk = gemm_fc2; fk = gemm_fc2_fixup; mkf = gemm_fc2_n320; nw = 8; ep = EPI_STORE; break;
@@ -1121,6 +1165,7 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
   p.C2 = (bf16*)g.C2; p.ldc2 = g.ldc2;
   p.bias = (const bf16*)g.bias;
   p.aux = (const bf16*)g.aux; p.ldaux = g.ldaux;
+  p.qkv_hl = g.qkv_hl; p.qscale = g.qscale;
   p.partials = (float*)ws;
   p.splits = 1;
   const int tiles = p.tiles_m * p.tiles_n;

@@ -17,6 +17,10 @@ enum Epi : int {
   EPI_DGELU = 2,      // out = acc * gelu'(aux[m][n])
   EPI_BIAS = 3,       // out = acc + bias[n]
   EPI_BIAS_F32 = 4,   // out (fp32) = acc + bias[n]
+  // x = acc + bias[n] of a [M, 3 h] projection [q | k | v] (h = qkv_hl) as
+  // five 16-bit planes [M, h] at out + p*M*h: 0 fp16(q qscale), 1 bf16(q),
+  // 2 fp16(k), 3 bf16(k), 4 bf16(v); fp16 values saturate at +-65504
+  EPI_QKV_PLANES = 5,
 };
 
 // The layer's products; the numbers match the TP_STEP_* ids of the C ABI.
@@ -40,31 +44,29 @@ struct GemmDesc {
   void* C2 = nullptr; long ldc2 = 0;
   const void* bias = nullptr;
   const void* aux = nullptr; long ldaux = 0;
+  int qkv_hl = 0; float qscale = 0.f;  // EPI_QKV_PLANES only
 };
 
 // Workspace bytes gemm_launch needs for this problem (host only).
 size_t gemm_workspace_bytes(int dtype, int M, int N, int K);
 hipError_t gemm_launch(int dtype, const GemmDesc& g, void* ws, size_t ws_bytes, hipStream_t stream);
 
-// Attention on the packed per-rank qkv [T, 3*h_l] = [Q | K | V].
-// qkv is fp32 for both storage types (the matrix-core path forms the scores
-// from fp16 copies of q and k); ctx, dctx and dqkv use the storage type.
+// Attention on the per-rank projection [T, 3*h_l] = [Q | K | V]: qkv holds
+// it in fp32 for the vector-ALU path, or as the five 16-bit planes of
+// EPI_QKV_PLANES (T*h_l elements each) for the matrix-core path
+// (attn_mfma_supported); ctx, dctx and dqkv use the storage type.
 struct AttnDesc {
   int batch = 0, seq = 0, n_local = 0, head_dim = 0;
   int head0 = 0;       // 0-based global index of local head 0 (rank * n_local)
   int n_heads = 1;     // global head count (ALiBi slopes)
   int alibi = 0;
-  const float* qkv = nullptr;  // [T, 3*h_l] fp32
+  const void* qkv = nullptr;  // fp32 [T, 3*h_l], or the five planes
   void* ctx = nullptr;        // [T, h_l]
   float* lse = nullptr;       // [batch, n_local, seq]
   // backward only
   const void* dctx = nullptr;  // [T, h_l]
   float* delta = nullptr;      // [batch, n_local, seq] scratch: rowsum(dctx * ctx)
   void* dqkv = nullptr;        // [T, 3*h_l]
-  // matrix-core path only: workspace for the 16-bit copies of q, k, v
-  // (fp16 q and k for the scores, bf16 q, k, v), attn_split_bytes() bytes
-  // (5 arrays [T, h_l])
-  void* split = nullptr;
   // attention-probability dropout (matrix-core path only; enabled when mask is
   // set): keep bits [batch][n_local][ceil(seq/32)][2][seq rounded up to 8],
   // written by the forward, read by the backward
@@ -79,7 +81,6 @@ struct AttnDesc {
 size_t attn_dropout_mask_bytes(int batch, int seq, int n_local);
 size_t attn_fwd_part_bytes(int dtype, int head_dim, int batch, int seq, int n_local);
 bool attn_mfma_supported(int dtype, int head_dim);
-size_t attn_split_bytes(int dtype, int head_dim, long long T, long long h_l);
 hipError_t attn_fwd_launch(int dtype, const AttnDesc& a, hipStream_t stream);
 hipError_t attn_bwd_launch(int dtype, const AttnDesc& a, hipStream_t stream);
 

@@ -227,7 +227,7 @@ MlpPlan plan_mlp(const Dims& dm, void* ws, bool bwd) {
 }
 
 struct AttnPlan {
-  void *dctx, *dqkv, *delta, *gemm_ws, *col_ws, *split;
+  void *dctx, *dqkv, *delta, *gemm_ws, *col_ws;
   void* fwd_part;      // forward: partials of key-split query tiles
   void *ctxT, *dqkvT;  // [hl, t_ld(T)], [3hl, t_ld(T)] transposed copies (bf16 backward)
   float* tpart;        // [transpose_part_rows(T), 3hl] column partials of dqkv
@@ -239,8 +239,6 @@ AttnPlan plan_attn(const Dims& dm, void* ws, bool bwd) {
   AttnPlan pl{};
   const int dt = dm.dtype;
   const long long B = dm.T;
-  const size_t split = attn_split_bytes(dt, (int)dm.d, dm.T, dm.hl);
-  pl.split = split ? bp.take(split) : nullptr;
   if (!bwd) {
     const size_t fp = attn_fwd_part_bytes(dt, (int)dm.d, (int)dm.batch, (int)dm.seq, (int)dm.nl);
     pl.fwd_part = fp ? bp.take(fp) : nullptr;
@@ -456,7 +454,7 @@ tp_status check_dropout(const tp_shape* s, const tp_dropout* dr) {
 }
 
 tp_status attn_fwd_impl(const tp_shape* shape, const tp_dropout* dr, uint16_t* mask, const void* X,
-                        const void* Wqkv_i, const void* bqkv_i, const void* Wo_i, float* qkv_i, void* ctx_i,
+                        const void* Wqkv_i, const void* bqkv_i, const void* Wo_i, void* qkv_i, void* ctx_i,
                         float* lse_i, void* O_i, void* workspace, size_t workspace_bytes, void* stream) {
   Dims dm;
   TP_CHECK(check_shape(shape, dm));
@@ -478,13 +476,19 @@ tp_status attn_fwd_impl(const tp_shape* shape, const tp_dropout* dr, uint16_t* m
   hipStream_t st = (hipStream_t)stream;
   const int dt = dm.dtype;
   const int T = (int)dm.T, h = (int)dm.h, hl = (int)dm.hl;
-  GemmDesc g = gd(GR_QKV_PROJ, T, 3 * hl, h, X, h, true, Wqkv_i, 3 * hl, false, EPI_BIAS_F32, qkv_i, 3 * hl);
+  // the matrix-core attention takes the projection as its five 16-bit
+  // operand planes, written by the GEMM epilogue; the vector-ALU path fp32
+  const bool planes = attn_mfma_supported(dt, (int)dm.d);
+  GemmDesc g = gd(GR_QKV_PROJ, T, 3 * hl, h, X, h, true, Wqkv_i, 3 * hl, false,
+                  planes ? EPI_QKV_PLANES : EPI_BIAS_F32, qkv_i, planes ? hl : 3 * hl);
   g.bias = bqkv_i;
+  g.qkv_hl = hl;
+  g.qscale = (float)(1.4426950408889634 / std::sqrt((double)dm.d));
   TP_STEP(TP_STEP_QKV_PROJ, gemm_launch(dt, g, pl.gemm_ws, pl.gemm_bytes, st), "attn QKV projection");
   AttnDesc a;
   a.batch = shape->batch; a.seq = shape->seq; a.n_local = (int)dm.nl; a.head_dim = (int)dm.d;
   a.head0 = shape->tp_rank * (int)dm.nl; a.n_heads = shape->n_heads; a.alibi = shape->alibi;
-  a.qkv = qkv_i; a.ctx = ctx_i; a.lse = lse_i; a.split = pl.split; a.fwd_part = (float*)pl.fwd_part;
+  a.qkv = qkv_i; a.ctx = ctx_i; a.lse = lse_i; a.fwd_part = (float*)pl.fwd_part;
   if (dr) {
     a.mask = mask; a.drop_p = dr->p; a.seed = dr->seed; a.offset = dr->offset;
   }
@@ -495,7 +499,7 @@ tp_status attn_fwd_impl(const tp_shape* shape, const tp_dropout* dr, uint16_t* m
 }
 
 tp_status attn_bwd_impl(const tp_shape* shape, const tp_dropout* dr, const uint16_t* mask, const void* X,
-                        const void* Wqkv_i, const void* Wo_i, const float* qkv_i, const void* ctx_i,
+                        const void* Wqkv_i, const void* Wo_i, const void* qkv_i, const void* ctx_i,
                         const float* lse_i, const void* dO, void* dX_i, void* dWqkv_i, void* dbqkv_i, void* dWo_i,
                         void* dbo_or_null, void* workspace, size_t workspace_bytes, void* stream) {
   Dims dm;
@@ -540,7 +544,7 @@ tp_status attn_bwd_impl(const tp_shape* shape, const tp_dropout* dr, const uint1
     a.batch = shape->batch; a.seq = shape->seq; a.n_local = (int)dm.nl; a.head_dim = (int)dm.d;
     a.head0 = shape->tp_rank * (int)dm.nl; a.n_heads = shape->n_heads; a.alibi = shape->alibi;
     a.qkv = qkv_i; a.ctx = (void*)ctx_i; a.lse = (float*)lse_i;
-    a.dctx = pl.dctx; a.delta = (float*)pl.delta; a.dqkv = pl.dqkv; a.split = pl.split;
+    a.dctx = pl.dctx; a.delta = (float*)pl.delta; a.dqkv = pl.dqkv;
     if (dr) {
       a.mask = (uint16_t*)mask; a.drop_p = dr->p; a.seed = dr->seed; a.offset = dr->offset;
     }
@@ -571,17 +575,24 @@ tp_status attn_bwd_impl(const tp_shape* shape, const tp_dropout* dr, const uint1
 extern "C" {
 
 tp_status tp_attn_fwd(const tp_shape* shape, const void* X, const void* Wqkv_i, const void* bqkv_i, const void* Wo_i,
-                      float* qkv_i, void* ctx_i, float* lse_i, void* O_i, void* workspace, size_t workspace_bytes,
+                      void* qkv_i, void* ctx_i, float* lse_i, void* O_i, void* workspace, size_t workspace_bytes,
                       void* stream) {
   return attn_fwd_impl(shape, nullptr, nullptr, X, Wqkv_i, bqkv_i, Wo_i, qkv_i, ctx_i, lse_i, O_i, workspace,
                        workspace_bytes, stream);
 }
 
-tp_status tp_attn_bwd(const tp_shape* shape, const void* X, const void* Wqkv_i, const void* Wo_i, const float* qkv_i,
+tp_status tp_attn_bwd(const tp_shape* shape, const void* X, const void* Wqkv_i, const void* Wo_i, const void* qkv_i,
                       const void* ctx_i, const float* lse_i, const void* dO, void* dX_i, void* dWqkv_i, void* dbqkv_i,
                       void* dWo_i, void* dbo_or_null, void* workspace, size_t workspace_bytes, void* stream) {
   return attn_bwd_impl(shape, nullptr, nullptr, X, Wqkv_i, Wo_i, qkv_i, ctx_i, lse_i, dO, dX_i, dWqkv_i, dbqkv_i,
                        dWo_i, dbo_or_null, workspace, workspace_bytes, stream);
+}
+
+size_t tp_attn_qkv_bytes(const tp_shape* shape) {
+  Dims dm;
+  if (check_shape(shape, dm) != TP_OK) return 0;
+  const size_t per = attn_mfma_supported(dm.dtype, (int)dm.d) ? 5 * 2 : 3 * 4;  // planes, or fp32 q | k | v
+  return (size_t)(dm.T * dm.hl) * per;
 }
 
 size_t tp_attn_dropout_mask_bytes(const tp_shape* shape) {
@@ -591,7 +602,7 @@ size_t tp_attn_dropout_mask_bytes(const tp_shape* shape) {
 }
 
 tp_status tp_attn_fwd_dropout(const tp_shape* shape, const tp_dropout* dropout, const void* X, const void* Wqkv_i,
-                              const void* bqkv_i, const void* Wo_i, float* qkv_i, void* ctx_i, float* lse_i,
+                              const void* bqkv_i, const void* Wo_i, void* qkv_i, void* ctx_i, float* lse_i,
                               uint16_t* mask_i, void* O_i, void* workspace, size_t workspace_bytes, void* stream) {
   if (!dropout) return fail(TP_ERR_NULL, "dropout is NULL");
   return attn_fwd_impl(shape, dropout, mask_i, X, Wqkv_i, bqkv_i, Wo_i, qkv_i, ctx_i, lse_i, O_i, workspace,
@@ -599,7 +610,7 @@ tp_status tp_attn_fwd_dropout(const tp_shape* shape, const tp_dropout* dropout, 
 }
 
 tp_status tp_attn_bwd_dropout(const tp_shape* shape, const tp_dropout* dropout, const void* X, const void* Wqkv_i,
-                              const void* Wo_i, const float* qkv_i, const void* ctx_i, const float* lse_i,
+                              const void* Wo_i, const void* qkv_i, const void* ctx_i, const float* lse_i,
                               const uint16_t* mask_i, const void* dO, void* dX_i, void* dWqkv_i, void* dbqkv_i,
                               void* dWo_i, void* dbo_or_null, void* workspace, size_t workspace_bytes, void* stream) {
   if (!dropout) return fail(TP_ERR_NULL, "dropout is NULL");

@@ -10,8 +10,8 @@ from __future__ import annotations
 
 import torch
 
-from . import TP_BF16, TP_FP32, TpShape, tp_attn_bwd, tp_attn_fwd, tp_attn_workspace_bytes, tp_mlp_bwd, \
-    tp_mlp_fwd, tp_mlp_workspace_bytes
+from . import TP_BF16, TP_FP32, TpShape, tp_attn_bwd, tp_attn_fwd, tp_attn_qkv_bytes, tp_attn_workspace_bytes, \
+    tp_mlp_bwd, tp_mlp_fwd, tp_mlp_workspace_bytes
 
 _DT = {TP_FP32: torch.float32, TP_BF16: torch.bfloat16}
 INPUTS = ("X_attn", "Wqkv", "bqkv", "Wo", "dO", "X_mlp", "A", "b1", "B", "dZ")
@@ -37,11 +37,13 @@ class LayerShard:
         def buf(*s, dtype=dt):
             t = torch.empty(*s, dtype=dtype, device=self.dev)
             if fill is not None:
-                t.fill_(fill)
+                # a byte buffer takes all-ones bytes: NaN in every float format it holds
+                t.fill_(255 if dtype == torch.uint8 else fill)
             return t
 
         self.out = {
-            "qkv": buf(T, 3 * hl, dtype=torch.float32), "ctx": buf(T, hl), "lse": buf(shape.batch, nl, shape.seq, dtype=torch.float32),
+            # the saved projection, in the form tp_attn_qkv_bytes describes
+            "qkv": buf(max(tp_attn_qkv_bytes(shape), 1), dtype=torch.uint8), "ctx": buf(T, hl), "lse": buf(shape.batch, nl, shape.seq, dtype=torch.float32),
             "O": buf(T, h), "pre": buf(T, fl), "y": buf(T, fl), "Z": buf(T, h),
             "dX_mlp": buf(T, h), "dA": buf(h, fl), "db1": buf(fl), "dB": buf(fl, h),
             "dX_attn": buf(T, h), "dWqkv": buf(h, 3 * hl), "dbqkv": buf(3 * hl), "dWo": buf(hl, h),

@@ -60,6 +60,35 @@ def compare(name: str, gpu, ref, dtype: str, report: dict | None = None, verbose
     return err
 
 
+MFMA_HEAD_DIMS = (64, 96, 128, 160)
+
+
+def saved_qkv(buf, T: int, hl: int, head_dim: int, dtype: str):
+    """The saved projection qkv_i as written by tp_attn_fwd, decoded for
+    comparison: -> (qkv [T, 3hl] float64 from the bf16 planes (or the fp32
+    buffer), q16 and k16 [T, hl] float64 from the fp16 planes with q16's
+    log2(e)/sqrt(d) factor divided out (None on the fp32 layout))."""
+    b = buf.detach().to("cpu").contiguous()
+    if dtype == "bf16" and head_dim in MFMA_HEAD_DIMS:
+        n = T * hl
+        h16 = b[: 10 * n].view(torch.int16)
+        plane = lambda k, dt: h16[k * n:(k + 1) * n].view(dt).to(torch.float64).reshape(T, hl).numpy()  # noqa: E731
+        qkv = np.concatenate([plane(1, torch.bfloat16), plane(3, torch.bfloat16), plane(4, torch.bfloat16)], axis=1)
+        qscale = 1.4426950408889634 / np.sqrt(head_dim)
+        return qkv, plane(0, torch.float16) / qscale, plane(2, torch.float16)
+    return b[: 12 * T * hl].view(torch.float32).to(torch.float64).reshape(T, 3 * hl).numpy(), None, None
+
+
+def compare_saved_qkv(buf, ref_qkv, T, hl, head_dim, dtype, report=None):
+    """The bf16 (or fp32) copy of the projection against the oracle's, and the
+    fp16 score copies of q and k against its q and k."""
+    qkv, q16, k16 = saved_qkv(buf, T, hl, head_dim, dtype)
+    compare("qkv", qkv, ref_qkv, dtype, report)
+    if q16 is not None:
+        compare("qkv(q fp16)", q16, ref_qkv[:, :hl], "bf16", report)
+        compare("qkv(k fp16)", k16, ref_qkv[:, hl:2 * hl], "bf16", report)
+
+
 def oracle_rank(w, inp: dict, rank: int, alibi=None) -> dict:
     """Full oracle for one rank's shard (small shapes)."""
     a = {k: f64(v) for k, v in inp.items()}

@@ -42,7 +42,8 @@ def test_library_loads_and_exports_every_declared_symbol():
                           "tp_vocab_workspace_bytes", "tp_vocab_ce_fwd", "tp_vocab_ce_combine", "tp_vocab_ce_bwd",
                           "tp_attn_dropout_mask_bytes", "tp_attn_fwd_dropout", "tp_attn_bwd_dropout",
                           "tp_ln_dropout_mask_bytes", "tp_ln_residual_fwd_dropout", "tp_ln_residual_bwd_dropout",
-                          "tp_ln_residual_bwd_noalloc", "tp_ln_residual_bwd_noalloc_max_scratch_bytes"}
+                          "tp_ln_residual_bwd_noalloc", "tp_ln_residual_bwd_noalloc_max_scratch_bytes",
+                          "tp_attn_qkv_bytes"}
     for n in names:
         assert isinstance(getattr(lib, n), ctypes._CFuncPtr), n
     out = subprocess.run(["nm", "-D", "--defined-only", tp.library_path()], capture_output=True, text=True).stdout
@@ -59,6 +60,17 @@ def test_workspace_sizes():
     # dctx + dqkv + delta
     assert tp.tp_attn_workspace_bytes(big) >= 2048 * 2560 * 2 * 4 + 2048 * 16 * 4
     assert tp.tp_mlp_workspace_bytes(shape(tp_rank=2)) == 0  # invalid shape -> 0
+
+
+def test_saved_projection_bytes():
+    # matrix-core path (bf16, head_dim 64/96/128/160): five 16-bit planes [T, h_l];
+    # otherwise fp32 [T, 3 h_l]
+    big = shape(batch=1, seq=2048, hidden=20480, ffn=81920, n_heads=128, head_dim=160, tp_size=8, dtype=tp.TP_BF16)
+    assert tp.tp_attn_qkv_bytes(big) == 5 * 2 * 2048 * 2560
+    assert tp.tp_attn_qkv_bytes(shape()) == 12 * 64 * 32  # fp32 tiny shard: T = 64, h_l = 32
+    d16 = shape(batch=2, seq=40, hidden=128, ffn=512, n_heads=8, head_dim=16, tp_size=2, dtype=tp.TP_BF16)
+    assert tp.tp_attn_qkv_bytes(d16) == 12 * 80 * 64  # bf16 with head_dim 16: vector-ALU path, fp32
+    assert tp.tp_attn_qkv_bytes(shape(tp_rank=2)) == 0
 
 
 def _mlp_fwd(s, ws=(FAKE, 1 << 40), **override):

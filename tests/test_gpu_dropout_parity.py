@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synth
-from parity_util import compare, f64, shape_of
+from parity_util import compare, compare_saved_qkv, f64, shape_of
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +34,7 @@ def run_gpu(w, inp, rank, drop):
     T, h, hl, nl = w.tokens, w.hidden, w.h_local, w.heads_local
     dev = {k: inp[k].cuda().contiguous() for k in ATTN_IN}
     bf, nan = torch.bfloat16, float("nan")
-    o = {"qkv": torch.full((T, 3 * hl), nan, dtype=torch.float32, device="cuda"),
+    o = {"qkv": torch.full((max(tp.tp_attn_qkv_bytes(s), 1),), 255, dtype=torch.uint8, device="cuda"),
          "ctx": torch.full((T, hl), nan, dtype=bf, device="cuda"),
          "lse": torch.full((w.batch, nl, w.seq), nan, dtype=torch.float32, device="cuda"),
          "O": torch.full((T, h), nan, dtype=bf, device="cuda"),
@@ -115,7 +115,8 @@ def test_dropout_attention_matches_oracle(case):
               dropout=D)
     qkv, ctx, lse, O = oracle.attn_fwd(a["X_attn"], a["Wqkv"], a["bqkv"], a["Wo"], **kw)
     dX, dWqkv, dbqkv, dWo, dbo = oracle.attn_bwd(a["X_attn"], a["Wqkv"], a["bqkv"], a["Wo"], a["dO"], **kw)
-    for k, ref in (("qkv", qkv), ("ctx", ctx), ("lse", lse), ("O", O), ("dX_attn", dX), ("dWqkv", dWqkv),
+    compare_saved_qkv(got["qkv"], qkv, w.tokens, w.h_local, w.head_dim, "bf16")
+    for k, ref in (("ctx", ctx), ("lse", lse), ("O", O), ("dX_attn", dX), ("dWqkv", dWqkv),
                    ("dbqkv", dbqkv), ("dWo", dWo), ("dbo", dbo)):
         compare(k, got[k], ref, "bf16")
 

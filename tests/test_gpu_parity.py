@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import synth
-from parity_util import compare, f64, oracle_rank, shape_of, shard_of_full
+from parity_util import compare, compare_saved_qkv, f64, oracle_rank, shape_of, shard_of_full
 
 pytestmark = pytest.mark.gpu
 
@@ -62,8 +62,13 @@ def _write_report(case: str, rep: dict):
 
 def check_all(ls, ref, dtype, names=OUTS):
     rep = {}
+    s = ls.shape
+    T, hl = s.batch * s.seq, s.n_heads // s.tp_size * s.head_dim
     for k in names:
-        compare(k, ls.out[k], ref[k], dtype, rep)
+        if k == "qkv":
+            compare_saved_qkv(ls.out[k], ref[k], T, hl, s.head_dim, dtype, rep)
+        else:
+            compare(k, ls.out[k], ref[k], dtype, rep)
     return rep
 
 
@@ -256,7 +261,7 @@ def test_full_size_workload(name, rank):
     # attention: the complete per-head core, projections sampled
     kw = dict(batch=w.batch, seq=w.seq, n_local=nl, head_dim=d, head0=rank * nl, n_heads=w.n_heads, alibi=w.alibi)
     qkv = a["X_attn"] @ a["Wqkv"] + a["bqkv"]
-    compare("qkv", out["qkv"], qkv, "bf16")
+    compare_saved_qkv(out["qkv"], qkv, T, hl, d, "bf16", rep)
     ctx, lse = oracle.attn_core_fwd(qkv, **kw)
     compare("ctx", out["ctx"], ctx, "bf16")
     compare("lse", out["lse"], lse, "bf16")
