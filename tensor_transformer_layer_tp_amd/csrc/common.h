@@ -15,26 +15,27 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// tanh-form GeLU and its derivative in fp32.
+// tanh-form GeLU and its derivative in fp32:
 // gelu(x) = 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3).
-// tanh(u) is evaluated as 1 - 2 / (exp(2u) + 1), which saturates correctly
-// for large |u| (exp overflow to inf gives 1, underflow to 0 gives -1).
-__device__ __forceinline__ float tanh_via_exp(float u) {
-  float e = __expf(2.0f * u);
-  return 1.0f - 2.0f / (e + 1.0f);
+// With s = (1 + tanh(u)) / 2 = 1 / (1 + exp(-2u)) (the logistic function of
+// 2u): gelu(x) = x s, and gelu'(x) = s + 2 x s (1 - s) u'(x),
+// u'(x) = sqrt(2/pi) (1 + 3 * 0.044715 x^2). exp(-2u) is one hardware 2^w
+// (w = -2u log2(e)) and 1 / (1 + exp(-2u)) one hardware reciprocal (both
+// within a few ulp, far below the outputs' bf16 rounding; an IEEE division
+// costs about ten instructions). Saturates correctly: 2^w overflows to inf
+// for very negative x (s = 0) and underflows to 0 for large x (s = 1).
+constexpr float kGeluK0 = 0.7978845608028654f;                    // sqrt(2/pi)
+constexpr float kGeluW = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+__device__ __forceinline__ float gelu_logistic(float x, float x2) {
+  const float w = (kGeluW * x) * fmaf(0.044715f, x2, 1.0f);
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(w));
 }
-__device__ __forceinline__ float gelu_f(float x) {
-  const float k0 = 0.7978845608028654f;
-  float u = k0 * (x + 0.044715f * x * x * x);
-  return 0.5f * x * (1.0f + tanh_via_exp(u));
-}
+__device__ __forceinline__ float gelu_f(float x) { return x * gelu_logistic(x, x * x); }
 __device__ __forceinline__ float gelu_grad_f(float x) {
-  const float k0 = 0.7978845608028654f;
-  float x2 = x * x;
-  float u = k0 * (x + 0.044715f * x2 * x);
-  float t = tanh_via_exp(u);
-  float du = k0 * (1.0f + 3.0f * 0.044715f * x2);
-  return 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * du;
+  const float x2 = x * x;
+  const float s = gelu_logistic(x, x2);
+  const float du = fmaf(3.0f * 0.044715f * kGeluK0, x2, kGeluK0);
+  return fmaf(2.0f * x * du, fmaf(-s, s, s), s);
 }
 
 template <typename T> __device__ __forceinline__ float to_f(T v);
