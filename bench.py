@@ -54,64 +54,19 @@ def step_flops(w) -> dict:
     }
 
 
-# Kernel names per step (as the trace shows them) for the roofline record.
-KERNEL_OF_STEP = {
-    "qkv_proj": "gemm_qkv_proj", "out_proj": "gemm_out_proj", "fc1": "gemm_fc1_bias_gelu", "fc2": "gemm_fc2",
-    "fc2_dgrad": "gemm_fc2_dgrad_gelu", "fc2_wgrad": "gemm_fc2_wgrad", "fc1_wgrad": "gemm_fc1_wgrad",
-    "fc1_dgrad": "gemm_fc1_dgrad", "out_dgrad": "gemm_out_dgrad", "out_wgrad": "gemm_out_wgrad",
-    "qkv_wgrad": "gemm_qkv_wgrad", "qkv_dgrad": "gemm_qkv_dgrad",
-}
+# The GEMM steps (products) of the layer; the library names the kernel each
+# one launches for a shape (tp_step_kernel), for the roofline record.
+GEMM_STEPS = ("qkv_proj", "out_proj", "fc1", "fc2", "fc2_dgrad", "fc2_wgrad", "fc1_wgrad", "fc1_dgrad", "out_dgrad",
+              "out_wgrad", "qkv_wgrad", "qkv_dgrad")
 
 
-# Steps whose product has a 256x320-tile kernel (suffix _n320), with its
-# (M, N, K): the library takes it when N is a multiple of 320 and the tiles
-# fill the CUs, or when their k-split covers every CU exactly.
-def wide_mnk(step, w):
-    T, h, hl, fl = w.tokens, w.hidden, w.h_local, w.ffn_local
-    return {"fc2_dgrad": (T, fl, h), "fc1_dgrad": (T, h, fl), "out_dgrad": (T, hl, h), "qkv_dgrad": (T, h, 3 * hl),
-            "fc1_wgrad": (h, fl, T), "qkv_wgrad": (h, 3 * hl, T)}.get(step)
-
-
-def exact_split(tiles, iters, ncu) -> bool:
-    """The library's plan for fewer tiles than CUs: a k-split of every tile
-    into sp = min(ncu // tiles, iters // 8) parts; true when those parts cover
-    every CU exactly."""
-    waves = (tiles + ncu - 1) // ncu
-    if iters < 16 or tiles >= ncu or tiles / (waves * ncu) >= 0.9:
-        return False
-    sp = min(ncu // tiles, iters // 8)
-    return sp >= 2 and sp * tiles == ncu
-
-
-# k-outer-B products with a 256x320-tile kernel (GEMM2, output projection,
-# GEMM2 weight gradient), with (M, N, K): taken when N is a multiple of 320
-# and the tiles run in data-parallel rounds (they fill >= 90% of the CUs'
-# last round).
-def fwd_mnk(step, w):
-    T, h, hl, fl = w.tokens, w.hidden, w.h_local, w.ffn_local
-    return {"fc2": (T, h, fl), "out_proj": (T, h, hl), "fc2_wgrad": (fl, h, T)}.get(step)
-
-
-def kernel_of(step, w, ncu) -> str:
+def kernel_of(step, shape) -> str:
     """Name of the kernel the library launches for a step's product."""
-    base = KERNEL_OF_STEP[step]
-    if w.dtype != "bf16":
-        return base
-    if step.endswith("_wgrad") and w.hidden < 8192:  # no transposed copy: both operands k-outer
-        return base + "_ko"
-    ncu = min(ncu, 256)
-    mnk = wide_mnk(step, w)
-    if mnk and mnk[1] % 320 == 0:
-        tiles = ((mnk[0] + 255) // 256) * (mnk[1] // 320)
-        if tiles >= ncu or exact_split(tiles, (mnk[2] + 63) // 64, ncu):
-            return base + "_n320"
-    mnk = fwd_mnk(step, w)
-    if mnk and mnk[1] % 320 == 0 and mnk[2] > 0:
-        tiles = ((mnk[0] + 255) // 256) * (mnk[1] // 320)
-        rounds = (tiles + ncu - 1) // ncu
-        if tiles >= 0.9 * rounds * ncu or (mnk[2] + 63) // 64 < 8:
-            return base + "_n320"
-    return base
+    import tensor_transformer_layer_tp_amd as tp
+    name = tp.tp_step_kernel(shape, step)
+    if name is None:
+        raise SystemExit(f"the library names no kernel for step {step}")
+    return name
 
 
 def gemm_source_hash() -> str:
@@ -618,10 +573,9 @@ def main():
     for name, ms in sorted(breakdown.items(), key=lambda kv: -kv[1]):
         tf = sf[name] / (ms / 1e3) / 1e12 if ms > 0 else 0.0
         log(f"  {name:11s} {ms:8.3f} ms  {100 * ms / tot:5.1f}%  {tf:7.1f} TFLOP/s  {100 * tf / PEAK_BF16_TFLOPS:5.1f}% peak")
-    gemm_steps = {k: v for k, v in breakdown.items() if k in KERNEL_OF_STEP}
+    gemm_steps = {k: v for k, v in breakdown.items() if k in GEMM_STEPS}
     dom = max(gemm_steps, key=gemm_steps.get)
-    ncu = torch.cuda.get_device_properties(0).multi_processor_count
-    kernel = kernel_of(dom, w, ncu)
+    kernel = kernel_of(dom, shape)
 
     # the timed region: K steps, events only between steps
     log(f"timing {a.steps} steps")

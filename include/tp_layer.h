@@ -375,6 +375,17 @@ enum {
 tp_status tp_profile_enable(uint32_t step_mask);
 tp_status tp_profile_collect(int32_t step, int32_t* launches, double* total_ms);
 
+/* Measurement aid (no passage of the pages; for traces and roofline
+ * records): the name of the main kernel that the GEMM step `step` (a
+ * TP_STEP_* id of a product: QKV_PROJ, OUT_PROJ, FC1, FC2, the input and
+ * weight gradients) launches for this shape on the current device, as a
+ * kernel trace shows it (e.g. "gemm_fc1_bias_gelu"); a k-split or stream-K
+ * plan adds the kernel of that name with the suffix "_fixup". The choice
+ * depends on the shape and the device's compute-unit count only. Returns NULL
+ * for an invalid shape, a step that is not a product, or an empty product
+ * (no launch). The string is static; the call touches no device memory. */
+const char* tp_step_kernel(const tp_shape* shape, int32_t step);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* tp_last_error(void);
 

@@ -25,7 +25,7 @@ __all__ = [
     "tp_vocab_workspace_bytes", "tp_vocab_ce_fwd", "tp_vocab_ce_combine", "tp_vocab_ce_bwd", "TpDropout",
     "tp_attn_dropout_mask_bytes", "tp_attn_fwd_dropout", "tp_attn_bwd_dropout", "tp_ln_dropout_mask_bytes",
     "tp_ln_residual_fwd_dropout", "tp_ln_residual_bwd_dropout", "tp_ln_residual_bwd_noalloc", "tp_attn_qkv_bytes",
-    "tp_ln_residual_bwd_noalloc_max_scratch_bytes",
+    "tp_ln_residual_bwd_noalloc_max_scratch_bytes", "tp_step_kernel",
 ]
 
 TP_FP32, TP_BF16 = 0, 1
@@ -99,6 +99,7 @@ _SIGS = {
     "tp_profile_enable": (_st, [ctypes.c_uint32]),
     "tp_profile_collect": (_st, [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)]),
     "tp_last_error": (ctypes.c_char_p, []),
+    "tp_step_kernel": (ctypes.c_char_p, [ctypes.POINTER(TpShape), ctypes.c_int32]),
 }
 
 # Step ids of tp_profile_enable / tp_profile_collect (TP_STEP_* in the header).
@@ -177,6 +178,13 @@ def _check(status: int):
 
 def tp_last_error() -> str:
     return load_library().tp_last_error().decode()
+
+
+def tp_step_kernel(shape: TpShape, step) -> str | None:
+    """Name of the main kernel a GEMM step (a STEPS name or id) launches for
+    this shape, or None (invalid shape, not a product, or no launch)."""
+    r = load_library().tp_step_kernel(ctypes.byref(shape), STEPS[step] if isinstance(step, str) else int(step))
+    return r.decode() if r is not None else None
 
 
 def tp_mlp_workspace_bytes(shape: TpShape) -> int:

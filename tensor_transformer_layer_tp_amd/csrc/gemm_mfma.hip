@@ -47,15 +47,17 @@ namespace {
 constexpr int BM = 256, BKK = 64;
 // Wave layout of a workgroup of NW waves over a BM x BNV tile. 256 wide: 2
 // waves along m (128 rows each) x NW/2 along n (4 waves: one per SIMD, 128x128
-// each; 8 waves: two per SIMD, 128x64 each). 320 wide (8 waves, k-inner B
-// only): 4 waves along m x 2 along n, 64x160 each -- 11% more flops per byte
-// staged than 256x256, and 2048 x 10240 / 20480 products fill 256 CUs in
-// whole rounds.
+// each; 8 waves: two per SIMD, 128x64 each). 320 and 192 wide (8 waves,
+// k-inner B only): 4 waves along m x 2 along n, 64x160 or 64x96 each. 320:
+// 11% more flops per byte staged than 256x256, and 2048 x 10240 / 20480
+// products fill 256 CUs in whole rounds; 192: 12% fewer, but products with
+// N = 1536 or 384 (narrow layers) then fill the CUs in whole rounds (or an
+// exact k-split) instead of a stream-K tail.
 template <int NW, int BNV>
 struct WC {
-  static_assert((NW == 4 && BNV == 256) || (NW == 8 && (BNV == 256 || BNV == 320)), "tile shape");
+  static_assert((NW == 4 && BNV == 256) || (NW == 8 && (BNV == 192 || BNV == 256 || BNV == 320)), "tile shape");
   static constexpr int NTHR = 64 * NW;
-  static constexpr int WMG = BNV == 320 ? 4 : 2;  // waves along m
+  static constexpr int WMG = BNV == 256 ? 2 : 4;  // waves along m
   static constexpr int WNG = NW / WMG;            // waves along n
   static constexpr int WMW = BM / WMG;            // rows per wave
   static constexpr int MI = WMW / 32;             // 32-row MFMA blocks per wave
@@ -450,7 +452,7 @@ __device__ __forceinline__ void epilogue_staged(const KParams& p, int tm, int tn
   // (and v) and then their bf16 copies
   constexpr int NPASS = BM / PR, NIMG = (EPI == EPI_BIAS_GELU || EPI == EPI_QKV_PLANES) ? 2 : 1;
   constexpr int ITERS = PR * NCH / C::NTHR;
-  static_assert(PR * NCH % C::NTHR == 0 && NCH >= 32 && PR % 32 == 0, "image layout");
+  static_assert(PR * NCH % C::NTHR == 0 && NCH >= 24 && PR % 32 == 0, "image layout");
   typedef __attribute__((address_space(3))) char lds_char;
   lds_char* img = (lds_char*)smem;
   // an opaque copy of the thread id keeps the per-lane addresses below from
@@ -954,6 +956,10 @@ TP_GEMM_KERNELS(gemm_fc2_dgrad_gelu_n320, 8, 320, true, true, EPI_DGELU)
 TP_GEMM_KERNELS(gemm_fc1_dgrad_n320, 8, 320, true, true, EPI_STORE)
 TP_GEMM_KERNELS(gemm_out_dgrad_n320, 8, 320, true, true, EPI_STORE)
 TP_GEMM_KERNELS(gemm_qkv_dgrad_n320, 8, 320, true, true, EPI_STORE)
+TP_GEMM_KERNELS(gemm_fc2_dgrad_gelu_n192, 8, 192, true, true, EPI_DGELU)
+TP_GEMM_KERNELS(gemm_fc1_dgrad_n192, 8, 192, true, true, EPI_STORE)
+TP_GEMM_KERNELS(gemm_out_dgrad_n192, 8, 192, true, true, EPI_STORE)
+TP_GEMM_KERNELS(gemm_qkv_dgrad_n192, 8, 192, true, true, EPI_STORE)
 // weight gradients (K = tokens): dB_i = (y_i^T copy) dZ and dWo_i = (ctx_i^T
 // copy) dO take a k-inner A and the stored gradient as a k-outer B; dA_i = X^T
 // (dPre^T copy) and dWqkv_i = X^T (dqkv^T copy) take X as stored (k-outer A)
@@ -1057,7 +1063,7 @@ int device_cus() {
 size_t gemm_mfma_workspace_bytes(int M, int N, int K) {
   const long long iters = (K + BKK - 1) / BKK;
   size_t best = 0;
-  for (int bn : {256, BN_MAX}) {
+  for (int bn : {192, 256, BN_MAX}) {
     const long long tiles = (long long)((M + BM - 1) / BM) * ((N + bn - 1) / bn);
     if (iters < 8 || tiles <= 0) continue;
     long long slots = 2LL * GMAX;
@@ -1068,97 +1074,166 @@ size_t gemm_mfma_workspace_bytes(int M, int N, int K) {
   return best;
 }
 
-hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStream_t stream) {
-  typedef void (*MainK)(KParams);
-  typedef void (*FixK)(KParams, int);
-  MainK mk = nullptr, mkw = nullptr, mkf = nullptr;  // mkf: forward product on 256x320 tiles
-  MainK mko = nullptr;                               // weight gradient with both operands k-outer
-  FixK fko = nullptr;
-  FixK fk = nullptr, fkw = nullptr;
+namespace {
+
+typedef void (*MainK)(KParams);
+typedef void (*FixK)(KParams, int);
+struct KRef {
+  MainK mk = nullptr;
+  FixK fk = nullptr;  // stream-K / k-split fix-up (none for the forward 320-wide kernels)
+  const char* name = nullptr;
+};
+#define TP_K(NAME) KRef{NAME, NAME##_fixup, #NAME}
+#define TP_KF(NAME) KRef{NAME, nullptr, #NAME}
+
+// The kernels of one product: the 256-wide tile and the alternatives its
+// role has (k-inner B on 320- or 192-wide tiles, the forward products'
+// 16x16x32 320-wide tile, both operands k-outer on 4 waves), with the
+// operand layouts and epilogue the kernels are compiled for.
+struct RoleKernels {
+  KRef base, w320, w192, f320, ko;
+  int nw = 8;
   bool ak = true, bk = false;
-  int ep = EPI_STORE, nw = 4;
-#define TP_ROLE(R, NAME, NWV, AKV, BKV, EV) \
-  case R: mk = NAME; fk = NAME##_fixup; nw = NWV; ak = AKV; bk = BKV; ep = EV; break;
-#define TP_ROLE_W(R, NAME, NWV, AKV, BKV, EV)                                                    \
-  case R: mk = NAME; fk = NAME##_fixup; mkw = NAME##_n320; fkw = NAME##_n320_fixup; nw = NWV; ak = AKV; \
-    bk = BKV; ep = EV; break;
+  int ep = EPI_STORE;
+};
+
+bool role_kernels(const GemmDesc& g, RoleKernels& r) {
   switch (g.role) {
     case GR_QKV_PROJ:
-      if (g.epi == EPI_QKV_PLANES) { mk = gemm_qkv_proj; fk = gemm_qkv_proj_fixup; }
-      else { mk = gemm_qkv_proj_f32; fk = gemm_qkv_proj_f32_fixup; }
-      nw = 8; ep = g.epi == EPI_QKV_PLANES ? EPI_QKV_PLANES : EPI_BIAS_F32; break;
-    case GR_OUT_PROJ: mk = gemm_out_proj; fk = gemm_out_proj_fixup; mkf = gemm_out_proj_n320; nw = 8; ep = EPI_STORE; break;
-    TP_ROLE(GR_FC1, gemm_fc1_bias_gelu, 8, true, false, EPI_BIAS_GELU)
-    case GR_FC2: mk = gemm_fc2; fk = gemm_fc2_fixup; mkf = gemm_fc2_n320; nw = 8; ep = EPI_STORE; break;
-    TP_ROLE_W(GR_FC2_DGRAD, gemm_fc2_dgrad_gelu, 8, true, true, EPI_DGELU)
-    TP_ROLE_W(GR_FC1_DGRAD, gemm_fc1_dgrad, 8, true, true, EPI_STORE)
-    TP_ROLE_W(GR_OUT_DGRAD, gemm_out_dgrad, 8, true, true, EPI_STORE)
-    TP_ROLE_W(GR_QKV_DGRAD, gemm_qkv_dgrad, 8, true, true, EPI_STORE)
-    case GR_FC2_WGRAD: mk = gemm_fc2_wgrad; fk = gemm_fc2_wgrad_fixup; mkf = gemm_fc2_wgrad_n320; nw = 8; ep = EPI_STORE;
-      mko = gemm_fc2_wgrad_ko; fko = gemm_fc2_wgrad_ko_fixup; break;
-    case GR_FC1_WGRAD: mk = gemm_fc1_wgrad; fk = gemm_fc1_wgrad_fixup; mkw = gemm_fc1_wgrad_n320;
-      fkw = gemm_fc1_wgrad_n320_fixup; nw = 8; ak = false; bk = true; ep = EPI_STORE;
-      mko = gemm_fc1_wgrad_ko; fko = gemm_fc1_wgrad_ko_fixup; break;
-    case GR_OUT_WGRAD: mk = gemm_out_wgrad; fk = gemm_out_wgrad_fixup; nw = 8; ep = EPI_STORE;
-      mko = gemm_out_wgrad_ko; fko = gemm_out_wgrad_ko_fixup; break;
-    case GR_QKV_WGRAD: mk = gemm_qkv_wgrad; fk = gemm_qkv_wgrad_fixup; mkw = gemm_qkv_wgrad_n320;
-      fkw = gemm_qkv_wgrad_n320_fixup; nw = 8; ak = false; bk = true; ep = EPI_STORE;
-      mko = gemm_qkv_wgrad_ko; fko = gemm_qkv_wgrad_ko_fixup; break;
-    TP_ROLE_W(GR_LOGITS, gemm_logits, 8, true, true, EPI_STORE)
-    TP_ROLE(GR_LOGITS_DGRAD, gemm_logits_dgrad, 8, true, false, EPI_STORE)
-    TP_ROLE(GR_LOGITS_WGRAD, gemm_logits_wgrad, 4, false, false, EPI_STORE)
-    default: return hipErrorInvalidValue;
+      if (g.epi == EPI_QKV_PLANES) { r.base = TP_K(gemm_qkv_proj); r.ep = EPI_QKV_PLANES; }
+      else { r.base = TP_K(gemm_qkv_proj_f32); r.ep = EPI_BIAS_F32; }
+      return true;
+    case GR_OUT_PROJ: r.base = TP_K(gemm_out_proj); r.f320 = TP_KF(gemm_out_proj_n320); return true;
+    case GR_FC1: r.base = TP_K(gemm_fc1_bias_gelu); r.ep = EPI_BIAS_GELU; return true;
+    case GR_FC2: r.base = TP_K(gemm_fc2); r.f320 = TP_KF(gemm_fc2_n320); return true;
+    case GR_FC2_DGRAD:
+      r.base = TP_K(gemm_fc2_dgrad_gelu); r.w320 = TP_K(gemm_fc2_dgrad_gelu_n320);
+      r.w192 = TP_K(gemm_fc2_dgrad_gelu_n192); r.bk = true; r.ep = EPI_DGELU; return true;
+    case GR_FC1_DGRAD:
+      r.base = TP_K(gemm_fc1_dgrad); r.w320 = TP_K(gemm_fc1_dgrad_n320); r.w192 = TP_K(gemm_fc1_dgrad_n192);
+      r.bk = true; return true;
+    case GR_OUT_DGRAD:
+      r.base = TP_K(gemm_out_dgrad); r.w320 = TP_K(gemm_out_dgrad_n320); r.w192 = TP_K(gemm_out_dgrad_n192);
+      r.bk = true; return true;
+    case GR_QKV_DGRAD:
+      r.base = TP_K(gemm_qkv_dgrad); r.w320 = TP_K(gemm_qkv_dgrad_n320); r.w192 = TP_K(gemm_qkv_dgrad_n192);
+      r.bk = true; return true;
+    case GR_FC2_WGRAD:
+      r.base = TP_K(gemm_fc2_wgrad); r.f320 = TP_KF(gemm_fc2_wgrad_n320); r.ko = TP_K(gemm_fc2_wgrad_ko); return true;
+    case GR_FC1_WGRAD:
+      r.base = TP_K(gemm_fc1_wgrad); r.w320 = TP_K(gemm_fc1_wgrad_n320); r.ko = TP_K(gemm_fc1_wgrad_ko);
+      r.ak = false; r.bk = true; return true;
+    case GR_OUT_WGRAD: r.base = TP_K(gemm_out_wgrad); r.ko = TP_K(gemm_out_wgrad_ko); return true;
+    case GR_QKV_WGRAD:
+      r.base = TP_K(gemm_qkv_wgrad); r.w320 = TP_K(gemm_qkv_wgrad_n320); r.ko = TP_K(gemm_qkv_wgrad_ko);
+      r.ak = false; r.bk = true; return true;
+    case GR_LOGITS: r.base = TP_K(gemm_logits); r.w320 = TP_K(gemm_logits_n320); r.bk = true; return true;
+    case GR_LOGITS_DGRAD: r.base = TP_K(gemm_logits_dgrad); return true;
+    case GR_LOGITS_WGRAD: r.base = TP_K(gemm_logits_wgrad); r.nw = 4; r.ak = false; return true;
   }
-#undef TP_ROLE
-#undef TP_ROLE_W
-  if (mko != nullptr && !g.a_kmajor && !g.b_kmajor) {  // weight gradient without a transposed copy
-    mk = mko; fk = fko; mkw = nullptr; mkf = nullptr; nw = 4; ak = false; bk = false;
+  return false;
+}
+#undef TP_K
+#undef TP_KF
+
+// Critical-path length of a plan, in k-steps of the plan's tile: data-parallel
+// rounds, plus the longest k-split piece or stream-K run; a plan with a
+// fix-up launch pays kFixSteps more (the fp32 partial tiles are written,
+// read back and reduced: 16-38 us measured, 10-20 k-steps of a 256x256 tile).
+// A 256x192 k-step takes about kStep192 of a 256x256 one (0.75 of the flops,
+// 0.875 of the bytes staged through LDS).
+constexpr double kStep192 = 0.85, kFixSteps = 20.0;
+double plan_cost(const Plan& pl, int tiles, int iters, int ncu, double per_step) {
+  ncu = ncu < GMAX ? ncu : GMAX;
+  double steps;
+  if (pl.splits > 1) steps = (double)pl.dp_rounds * iters + (iters + pl.splits - 1) / pl.splits;
+  else if (pl.sk_total > 0) steps = (double)pl.dp_rounds * iters + (double)((pl.sk_total + pl.sk_grid - 1) / pl.sk_grid);
+  else steps = (double)((tiles + ncu - 1) / ncu) * iters;
+  return per_step * steps + ((pl.splits > 1 || pl.sk_total > 0) ? kFixSteps : 0.0);
+}
+
+// The kernel and schedule of one product.
+struct Pick {
+  KRef k;
+  int bn = 256, nw = 8;
+  int mi = 4;           // fix-up workgroups per tile (one per row block of the waves' sub-tiles)
+  bool fwd320 = false;  // the forward products' 16x16x32 320-wide kernel (data-parallel only)
+  Plan pl{};
+};
+
+// Kernel choice, given ws_bytes of workspace for stream-K / k-split
+// partials (too little: data-parallel only). False when the role, operand
+// layouts and epilogue match no kernel.
+bool pick(const GemmDesc& g, size_t ws_bytes, Pick& out) {
+  RoleKernels r;
+  if (!role_kernels(g, r)) return false;
+  if (r.ko.mk != nullptr && !g.a_kmajor && !g.b_kmajor) {  // weight gradient without a transposed copy
+    r.base = r.ko;
+    r.w320 = r.w192 = r.f320 = KRef{};
+    r.nw = 4; r.ak = false; r.bk = false;
   }
-  if (g.a_kmajor != ak || g.b_kmajor != bk || g.epi != ep) return hipErrorInvalidValue;
-  const int ncu = device_cus();
+  if (g.a_kmajor != r.ak || g.b_kmajor != r.bk || g.epi != r.ep) return false;
+  const int ncu = device_cus(), cus = ncu < GMAX ? ncu : GMAX;
+  const int iters = (g.K + BKK - 1) / BKK, tm = (g.M + BM - 1) / BM;
   // k-outer-B products (GEMM2, output projection, GEMM2 weight gradient):
   // 256x320 tiles when N is a whole number of them and the tiles run in
   // data-parallel rounds (no k-split tail)
-  if (mkf != nullptr && g.N % BN_MAX == 0) {
-    const int tiles = ((g.M + BM - 1) / BM) * (g.N / BN_MAX);
-    const Plan pl = make_plan(tiles, (g.K + BKK - 1) / BKK, ncu);
+  if (r.f320.mk != nullptr && g.N % BN_MAX == 0) {
+    const int tiles = tm * (g.N / BN_MAX);
+    const Plan pl = make_plan(tiles, iters, ncu);
     if (pl.splits == 1 && pl.sk_total == 0) {
-      KParams p{};
-      p.A = (const bf16*)g.A; p.B = (const bf16*)g.B;
-      p.lda = g.lda; p.ldb = g.ldb;
-      p.M = g.M; p.N = g.N; p.K = g.K;
-      p.tiles_m = (g.M + BM - 1) / BM;
-      p.tiles_n = g.N / BN_MAX;
-      p.iters = (g.K + BKK - 1) / BKK;
-      p.epi = g.epi;
-      p.C = (bf16*)g.C; p.ldc = g.ldc;
-      p.C2 = (bf16*)g.C2; p.ldc2 = g.ldc2;
-      p.bias = (const bf16*)g.bias;
-      p.grid = pl.grid; p.dp_rounds = pl.dp_rounds;
-      p.splits = 1;
-      hipLaunchKernelGGL(mkf, dim3(pl.grid), dim3(512), 0, stream, p);
-      return hipGetLastError();
+      out.k = r.f320; out.bn = BN_MAX; out.nw = 8; out.fwd320 = true; out.pl = pl;
+      return true;
     }
   }
-  // the wide tile when N is a whole number of them and they fill the CUs at
-  // least once, or, fewer, when their k-split covers every CU exactly (with
-  // other counts the k-split tail is better balanced at 256)
-  bool wide = false;
-  if (mkw != nullptr && g.N % BN_MAX == 0) {
-    const int cus = ncu < GMAX ? ncu : GMAX;
-    const int t320 = ((g.M + BM - 1) / BM) * (g.N / BN_MAX);
-    const Plan p320 = make_plan(t320, (g.K + BKK - 1) / BKK, ncu);
-    wide = t320 >= cus || (p320.splits > 1 && p320.dp_rounds == 0 && p320.splits * t320 == cus);
+  // k-inner B: the 320-wide tile when N is a whole number of them and they
+  // fill the CUs at least once, or, fewer, when their k-split covers every CU
+  // exactly; else the 192-wide tile when its plan is shorter than the
+  // 256-wide one's (whole rounds or an exact k-split instead of a stream-K
+  // tail and its fix-up)
+  int bn = 256;
+  if (r.w320.mk != nullptr && g.N % BN_MAX == 0) {
+    const int t320 = tm * (g.N / BN_MAX);
+    const Plan p320 = make_plan(t320, iters, ncu);
+    if (t320 >= cus || (p320.splits > 1 && p320.dp_rounds == 0 && p320.splits * t320 == cus)) bn = BN_MAX;
   }
-  const int bn = wide ? BN_MAX : 256;
-  if (bn == BN_MAX) { mk = mkw; fk = fkw; }
-  const int mi = bn == BN_MAX ? WC<8, BN_MAX>::MI : 4;  // fix-up workgroups per tile
+  if (bn == 256 && r.w192.mk != nullptr) {
+    const int t256 = tm * ((g.N + 255) / 256), t192 = tm * ((g.N + 191) / 192);
+    if (plan_cost(make_plan(t192, iters, ncu), t192, iters, ncu, kStep192) <
+        plan_cost(make_plan(t256, iters, ncu), t256, iters, ncu, 1.0))
+      bn = 192;
+  }
+  out.k = bn == BN_MAX ? r.w320 : bn == 192 ? r.w192 : r.base;
+  out.bn = bn;
+  out.nw = r.nw;
+  out.mi = bn == BN_MAX ? WC<8, BN_MAX>::MI : bn == 192 ? WC<8, 192>::MI : 4;
+  const int tiles = tm * ((g.N + bn - 1) / bn);
+  Plan pl = make_plan(tiles, iters, ncu);
+  if (pl.sk_total > 0 || pl.splits > 1) {
+    const size_t slots = pl.splits > 1 ? (size_t)pl.splits * pl.sk_tiles : (size_t)2 * pl.sk_grid;
+    if (ws_bytes < slots * BM * bn * sizeof(float)) pl = Plan{tiles, 1, 0, 0, 0, 0, 0, 1};  // data-parallel only
+  }
+  out.pl = pl;
+  return true;
+}
+
+}  // namespace
+
+const char* gemm_mfma_kernel_name(const GemmDesc& g) {
+  Pick pk;
+  return pick(g, (size_t)-1, pk) ? pk.k.name : nullptr;
+}
+
+hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Pick pk;
+  if (!pick(g, ws != nullptr ? ws_bytes : 0, pk)) return hipErrorInvalidValue;
+  const Plan& pl = pk.pl;
   KParams p{};
   p.A = (const bf16*)g.A; p.B = (const bf16*)g.B;
   p.lda = g.lda; p.ldb = g.ldb;
   p.M = g.M; p.N = g.N; p.K = g.K;
   p.tiles_m = (g.M + BM - 1) / BM;
-  p.tiles_n = (g.N + bn - 1) / bn;
+  p.tiles_n = (g.N + pk.bn - 1) / pk.bn;
   p.iters = (g.K + BKK - 1) / BKK;
   p.epi = g.epi;
   p.C = (bf16*)g.C; p.ldc = g.ldc;
@@ -1167,24 +1242,15 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
   p.aux = (const bf16*)g.aux; p.ldaux = g.ldaux;
   p.qkv_hl = g.qkv_hl; p.qscale = g.qscale;
   p.partials = (float*)ws;
-  p.splits = 1;
-  const int tiles = p.tiles_m * p.tiles_n;
-  Plan pl = make_plan(tiles, p.iters, ncu);
-  if (pl.sk_total > 0 || pl.splits > 1) {
-    const size_t slots = pl.splits > 1 ? (size_t)pl.splits * pl.sk_tiles : (size_t)2 * pl.sk_grid;
-    if (ws == nullptr || ws_bytes < slots * BM * bn * sizeof(float))
-      pl = Plan{tiles, 1, 0, 0, 0, 0, 0, 1};  // data-parallel only
-  }
   p.grid = pl.grid; p.dp_rounds = pl.dp_rounds; p.sk_grid = pl.sk_grid;
   p.sk_begin = pl.sk_begin; p.sk_total = pl.sk_total; p.splits = pl.splits;
   p.split_first = pl.sk_first_tile; p.split_tiles = pl.sk_tiles;
-  const int first = pl.sk_first_tile, nsk = pl.sk_tiles;
-  const bool sk = pl.sk_total > 0 || pl.splits > 1;
-  const dim3 block(64 * nw);
-  hipLaunchKernelGGL(mk, dim3(pl.grid), block, 0, stream, p);
+  const dim3 block(64 * pk.nw);
+  hipLaunchKernelGGL(pk.k.mk, dim3(pl.grid), block, 0, stream, p);
   hipError_t e1 = hipGetLastError();
-  if (e1 != hipSuccess || !sk) return e1;
-  hipLaunchKernelGGL(fk, dim3(mi * nsk), block, 0, stream, p, first);
+  const bool sk = pl.sk_total > 0 || pl.splits > 1;
+  if (e1 != hipSuccess || !sk || pk.fwd320) return e1;
+  hipLaunchKernelGGL(pk.k.fk, dim3(pk.mi * pl.sk_tiles), block, 0, stream, p, pl.sk_first_tile);
   return hipGetLastError();
 }
 

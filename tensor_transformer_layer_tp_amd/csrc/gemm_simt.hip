@@ -9,6 +9,7 @@ namespace tpk {
 
 size_t gemm_mfma_workspace_bytes(int M, int N, int K);
 hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStream_t stream);
+const char* gemm_mfma_kernel_name(const GemmDesc& g);
 
 namespace {
 
@@ -85,6 +86,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(SParams p) {
 
 size_t gemm_workspace_bytes(int dtype, int M, int N, int K) {
   return dtype == DT_BF16 ? gemm_mfma_workspace_bytes(M, N, K) : 0;
+}
+
+const char* gemm_kernel_name(int dtype, const GemmDesc& g) {
+  if (g.M <= 0 || g.N <= 0 || g.K <= 0) return nullptr;
+  return dtype == DT_BF16 ? gemm_mfma_kernel_name(g) : "gemm_f32_kernel";
 }
 
 hipError_t gemm_launch(int dtype, const GemmDesc& g, void* ws, size_t ws_bytes, hipStream_t stream) {

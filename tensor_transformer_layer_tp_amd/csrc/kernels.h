@@ -50,6 +50,9 @@ struct GemmDesc {
 // Workspace bytes gemm_launch needs for this problem (host only).
 size_t gemm_workspace_bytes(int dtype, int M, int N, int K);
 hipError_t gemm_launch(int dtype, const GemmDesc& g, void* ws, size_t ws_bytes, hipStream_t stream);
+// Name of the main kernel gemm_launch runs for g (host only; null when it
+// launches none: an empty product, or no kernel for g's layouts).
+const char* gemm_kernel_name(int dtype, const GemmDesc& g);
 
 // Attention on the per-rank projection [T, 3*h_l] = [Q | K | V]: qkv holds
 // it in fp32 for the vector-ALU path, or as the five 16-bit planes of

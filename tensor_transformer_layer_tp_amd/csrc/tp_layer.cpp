@@ -319,6 +319,66 @@ VocabPlan plan_vocab(const Dims& dm, const VocabDims& vd, void* ws, bool bwd) {
   return pl;
 }
 
+// Shape, operand layouts and epilogue of a GEMM step's product (the caller
+// fills in the pointers): the wrappers below launch exactly these, and
+// tp_step_kernel names the kernel each one runs. Weight gradients of wide
+// layers read a transposed, token-contiguous copy of one operand (leading
+// dimension t_ld(T)).
+GemmDesc step_gemm(const Dims& dm, int step) {
+  GemmDesc g;
+  const int T = (int)dm.T, h = (int)dm.h, hl = (int)dm.hl, fl = (int)dm.fl;
+  const bool cp = wgrad_copies(dm);
+  const long ldt = (long)t_ld(T);
+  auto set = [&](int role, int M, int N, int K, long lda, bool ak, long ldb, bool bk, int epi, long ldc) {
+    g.role = role;
+    g.M = M; g.N = N; g.K = K;
+    g.lda = lda; g.a_kmajor = ak;
+    g.ldb = ldb; g.b_kmajor = bk;
+    g.epi = epi;
+    g.ldc = ldc;
+  };
+  switch (step) {
+    case TP_STEP_QKV_PROJ: {
+      const bool planes = attn_mfma_supported(dm.dtype, (int)dm.d);
+      set(GR_QKV_PROJ, T, 3 * hl, h, h, true, 3 * hl, false, planes ? EPI_QKV_PLANES : EPI_BIAS_F32,
+          planes ? hl : 3 * hl);
+      g.qkv_hl = hl;
+      g.qscale = (float)(1.4426950408889634 / std::sqrt((double)dm.d));
+      break;
+    }
+    case TP_STEP_OUT_PROJ: set(GR_OUT_PROJ, T, h, hl, hl, true, h, false, EPI_STORE, h); break;
+    case TP_STEP_FC1: set(GR_FC1, T, fl, h, h, true, fl, false, EPI_BIAS_GELU, fl); g.ldc2 = fl; break;
+    case TP_STEP_FC2: set(GR_FC2, T, h, fl, fl, true, h, false, EPI_STORE, h); break;
+    case TP_STEP_FC2_DGRAD: set(GR_FC2_DGRAD, T, fl, h, h, true, h, true, EPI_DGELU, fl); g.ldaux = fl; break;
+    case TP_STEP_FC2_WGRAD:
+      if (cp) set(GR_FC2_WGRAD, fl, h, T, ldt, true, h, false, EPI_STORE, h);
+      else set(GR_FC2_WGRAD, fl, h, T, fl, false, h, false, EPI_STORE, h);
+      break;
+    case TP_STEP_FC1_WGRAD:
+      if (cp) set(GR_FC1_WGRAD, h, fl, T, h, false, ldt, true, EPI_STORE, fl);
+      else set(GR_FC1_WGRAD, h, fl, T, h, false, fl, false, EPI_STORE, fl);
+      break;
+    case TP_STEP_FC1_DGRAD: set(GR_FC1_DGRAD, T, h, fl, fl, true, fl, true, EPI_STORE, h); break;
+    case TP_STEP_OUT_DGRAD: set(GR_OUT_DGRAD, T, hl, h, h, true, h, true, EPI_STORE, hl); break;
+    case TP_STEP_OUT_WGRAD:
+      if (cp) set(GR_OUT_WGRAD, hl, h, T, ldt, true, h, false, EPI_STORE, h);
+      else set(GR_OUT_WGRAD, hl, h, T, hl, false, h, false, EPI_STORE, h);
+      break;
+    case TP_STEP_QKV_WGRAD:
+      if (cp) set(GR_QKV_WGRAD, h, 3 * hl, T, h, false, ldt, true, EPI_STORE, 3 * hl);
+      else set(GR_QKV_WGRAD, h, 3 * hl, T, h, false, 3 * hl, false, EPI_STORE, 3 * hl);
+      break;
+    case TP_STEP_QKV_DGRAD: set(GR_QKV_DGRAD, T, h, 3 * hl, 3 * hl, true, 3 * hl, true, EPI_STORE, h); break;
+    default: break;  // role 0: not a GEMM step
+  }
+  return g;
+}
+
+GemmDesc with_ptrs(GemmDesc g, const void* A, const void* B, void* C) {
+  g.A = A; g.B = B; g.C = C;
+  return g;
+}
+
 GemmDesc gd(int role, int M, int N, int K, const void* A, long lda, bool ak, const void* B, long ldb, bool bk,
             int epi, void* C, long ldc) {
   GemmDesc g;
@@ -336,6 +396,14 @@ GemmDesc gd(int role, int M, int N, int K, const void* A, long lda, bool ak, con
 extern "C" {
 
 const char* tp_last_error(void) { return g_last_error.c_str(); }
+
+const char* tp_step_kernel(const tp_shape* shape, int32_t step) {
+  Dims dm;
+  if (check_shape(shape, dm) != TP_OK) return nullptr;
+  const GemmDesc g = step_gemm(dm, step);
+  if (g.role == 0) return nullptr;
+  return gemm_kernel_name(dm.dtype, g);
+}
 
 size_t tp_mlp_workspace_bytes(const tp_shape* shape) {
   Dims dm;
@@ -369,10 +437,10 @@ tp_status tp_mlp_fwd(const tp_shape* shape, const void* X, const void* A_i, cons
   const MlpPlan pl = plan_mlp(dm, workspace, false);
   hipStream_t st = (hipStream_t)stream;
   const int dt = dm.dtype;
-  GemmDesc g1 = gd(GR_FC1, (int)dm.T, (int)dm.fl, (int)dm.h, X, dm.h, true, A_i, dm.fl, false, EPI_BIAS_GELU, pre_i, dm.fl);
-  g1.C2 = y_i; g1.ldc2 = dm.fl; g1.bias = b1_i;
+  GemmDesc g1 = with_ptrs(step_gemm(dm, TP_STEP_FC1), X, A_i, pre_i);
+  g1.C2 = y_i; g1.bias = b1_i;
   TP_STEP(TP_STEP_FC1, gemm_launch(dt, g1, pl.gemm_ws, pl.gemm_bytes, st), "mlp GEMM1 (X A_i + b1_i, GeLU)");
-  GemmDesc g2 = gd(GR_FC2, (int)dm.T, (int)dm.h, (int)dm.fl, y_i, dm.fl, true, B_i, dm.h, false, EPI_STORE, Z_i, dm.h);
+  GemmDesc g2 = with_ptrs(step_gemm(dm, TP_STEP_FC2), y_i, B_i, Z_i);
   TP_STEP(TP_STEP_FC2, gemm_launch(dt, g2, pl.gemm_ws, pl.gemm_bytes, st), "mlp GEMM2 (y_i B_i)");
   return TP_OK;
 }
@@ -401,8 +469,8 @@ tp_status tp_mlp_bwd(const tp_shape* shape, const void* X, const void* A_i, cons
   const int dt = dm.dtype;
   const int T = (int)dm.T, h = (int)dm.h, fl = (int)dm.fl;
   if (T > 0) {
-    GemmDesc g = gd(GR_FC2_DGRAD, T, fl, h, dZ, h, true, B_i, h, true, EPI_DGELU, pl.dpre, fl);
-    g.aux = pre_i; g.ldaux = fl;
+    GemmDesc g = with_ptrs(step_gemm(dm, TP_STEP_FC2_DGRAD), dZ, B_i, pl.dpre);
+    g.aux = pre_i;
     TP_STEP(TP_STEP_FC2_DGRAD, gemm_launch(dt, g, pl.gemm_ws, pl.gemm_bytes, st), "mlp dgrad (dZ B_i^T * GeLU'(pre_i))");
   }
   // weight gradients (K = T; T == 0 gives zeros)
@@ -410,21 +478,21 @@ tp_status tp_mlp_bwd(const tp_shape* shape, const void* X, const void* A_i, cons
     // y_i^T and dPre^T copies (the latter with db1_i's column partials)
     const long ldt = (long)t_ld(T);
     TP_STEP(TP_STEP_TRANSPOSE, transpose_colsum_launch(y_i, T, fl, fl, pl.yT, ldt, nullptr, st), "mlp y_i^T copy");
-    TP_STEP(TP_STEP_FC2_WGRAD, gemm_launch(dt, gd(GR_FC2_WGRAD, fl, h, T, pl.yT, ldt, true, dZ, h, false, EPI_STORE, dB_i, h), pl.gemm_ws, pl.gemm_bytes, st),
+    TP_STEP(TP_STEP_FC2_WGRAD, gemm_launch(dt, with_ptrs(step_gemm(dm, TP_STEP_FC2_WGRAD), pl.yT, dZ, dB_i), pl.gemm_ws, pl.gemm_bytes, st),
            "mlp wgrad dB_i = y_i^T dZ");
     TP_STEP(TP_STEP_TRANSPOSE, transpose_colsum_launch(pl.dpre, T, fl, fl, pl.dpreT, ldt, pl.tpart, st), "mlp dPre^T copy");
-    TP_STEP(TP_STEP_FC1_WGRAD, gemm_launch(dt, gd(GR_FC1_WGRAD, h, fl, T, X, h, false, pl.dpreT, ldt, true, EPI_STORE, dA_i, fl), pl.gemm_ws, pl.gemm_bytes, st),
+    TP_STEP(TP_STEP_FC1_WGRAD, gemm_launch(dt, with_ptrs(step_gemm(dm, TP_STEP_FC1_WGRAD), X, pl.dpreT, dA_i), pl.gemm_ws, pl.gemm_bytes, st),
            "mlp wgrad dA_i = X^T dPre");
     TP_STEP(TP_STEP_BIAS_GRADS, colsum_final_launch(dt, pl.tpart, transpose_part_rows(T), fl, db1_i, st), "mlp db1_i");
   } else {
-    TP_STEP(TP_STEP_FC2_WGRAD, gemm_launch(dt, gd(GR_FC2_WGRAD, fl, h, T, y_i, fl, false, dZ, h, false, EPI_STORE, dB_i, h), pl.gemm_ws, pl.gemm_bytes, st),
+    TP_STEP(TP_STEP_FC2_WGRAD, gemm_launch(dt, with_ptrs(step_gemm(dm, TP_STEP_FC2_WGRAD), y_i, dZ, dB_i), pl.gemm_ws, pl.gemm_bytes, st),
            "mlp wgrad dB_i = y_i^T dZ");
-    TP_STEP(TP_STEP_FC1_WGRAD, gemm_launch(dt, gd(GR_FC1_WGRAD, h, fl, T, X, h, false, pl.dpre, fl, false, EPI_STORE, dA_i, fl), pl.gemm_ws, pl.gemm_bytes, st),
+    TP_STEP(TP_STEP_FC1_WGRAD, gemm_launch(dt, with_ptrs(step_gemm(dm, TP_STEP_FC1_WGRAD), X, pl.dpre, dA_i), pl.gemm_ws, pl.gemm_bytes, st),
            "mlp wgrad dA_i = X^T dPre");
     TP_STEP(TP_STEP_BIAS_GRADS, colsum_launch(dt, pl.dpre, T, fl, fl, db1_i, (float*)pl.col_ws, st), "mlp db1_i");
   }
   if (T > 0)
-    TP_STEP(TP_STEP_FC1_DGRAD, gemm_launch(dt, gd(GR_FC1_DGRAD, T, h, fl, pl.dpre, fl, true, A_i, fl, true, EPI_STORE, dX_i, h), pl.gemm_ws, pl.gemm_bytes, st),
+    TP_STEP(TP_STEP_FC1_DGRAD, gemm_launch(dt, with_ptrs(step_gemm(dm, TP_STEP_FC1_DGRAD), pl.dpre, A_i, dX_i), pl.gemm_ws, pl.gemm_bytes, st),
            "mlp dgrad dX_i = dPre A_i^T");
   if (db2_or_null) TP_STEP(TP_STEP_BIAS_GRADS, colsum_launch(dt, dZ, T, h, h, db2_or_null, (float*)pl.col_ws, st), "mlp db2");
   return TP_OK;
@@ -475,15 +543,10 @@ tp_status attn_fwd_impl(const tp_shape* shape, const tp_dropout* dr, uint16_t* m
   const AttnPlan pl = plan_attn(dm, workspace, false);
   hipStream_t st = (hipStream_t)stream;
   const int dt = dm.dtype;
-  const int T = (int)dm.T, h = (int)dm.h, hl = (int)dm.hl;
   // the matrix-core attention takes the projection as its five 16-bit
   // operand planes, written by the GEMM epilogue; the vector-ALU path fp32
-  const bool planes = attn_mfma_supported(dt, (int)dm.d);
-  GemmDesc g = gd(GR_QKV_PROJ, T, 3 * hl, h, X, h, true, Wqkv_i, 3 * hl, false,
-                  planes ? EPI_QKV_PLANES : EPI_BIAS_F32, qkv_i, planes ? hl : 3 * hl);
+  GemmDesc g = with_ptrs(step_gemm(dm, TP_STEP_QKV_PROJ), X, Wqkv_i, qkv_i);
   g.bias = bqkv_i;
-  g.qkv_hl = hl;
-  g.qscale = (float)(1.4426950408889634 / std::sqrt((double)dm.d));
   TP_STEP(TP_STEP_QKV_PROJ, gemm_launch(dt, g, pl.gemm_ws, pl.gemm_bytes, st), "attn QKV projection");
   AttnDesc a;
   a.batch = shape->batch; a.seq = shape->seq; a.n_local = (int)dm.nl; a.head_dim = (int)dm.d;
@@ -493,7 +556,7 @@ tp_status attn_fwd_impl(const tp_shape* shape, const tp_dropout* dr, uint16_t* m
     a.mask = mask; a.drop_p = dr->p; a.seed = dr->seed; a.offset = dr->offset;
   }
   TP_STEP(TP_STEP_ATTN_FWD, attn_fwd_launch(dt, a, st), "attn forward");
-  TP_STEP(TP_STEP_OUT_PROJ, gemm_launch(dt, gd(GR_OUT_PROJ, T, h, hl, ctx_i, hl, true, Wo_i, h, false, EPI_STORE, O_i, h), pl.gemm_ws, pl.gemm_bytes, st),
+  TP_STEP(TP_STEP_OUT_PROJ, gemm_launch(dt, with_ptrs(step_gemm(dm, TP_STEP_OUT_PROJ), ctx_i, Wo_i, O_i), pl.gemm_ws, pl.gemm_bytes, st),
          "attn output projection");
   return TP_OK;
 }
@@ -526,16 +589,16 @@ tp_status attn_bwd_impl(const tp_shape* shape, const tp_dropout* dr, const uint1
   const int dt = dm.dtype;
   const int T = (int)dm.T, h = (int)dm.h, hl = (int)dm.hl;
   if (T > 0)
-    TP_STEP(TP_STEP_OUT_DGRAD, gemm_launch(dt, gd(GR_OUT_DGRAD, T, hl, h, dO, h, true, Wo_i, h, true, EPI_STORE, pl.dctx, hl), pl.gemm_ws, pl.gemm_bytes, st),
+    TP_STEP(TP_STEP_OUT_DGRAD, gemm_launch(dt, with_ptrs(step_gemm(dm, TP_STEP_OUT_DGRAD), dO, Wo_i, pl.dctx), pl.gemm_ws, pl.gemm_bytes, st),
            "attn dgrad dC = dO Wo_i^T");
   const bool copies = wgrad_copies(dm);
   const long ldt = (long)t_ld(T);
   if (copies) {
     TP_STEP(TP_STEP_TRANSPOSE, transpose_colsum_launch(ctx_i, T, hl, hl, pl.ctxT, ldt, nullptr, st), "attn ctx_i^T copy");
-    TP_STEP(TP_STEP_OUT_WGRAD, gemm_launch(dt, gd(GR_OUT_WGRAD, hl, h, T, pl.ctxT, ldt, true, dO, h, false, EPI_STORE, dWo_i, h), pl.gemm_ws, pl.gemm_bytes, st),
+    TP_STEP(TP_STEP_OUT_WGRAD, gemm_launch(dt, with_ptrs(step_gemm(dm, TP_STEP_OUT_WGRAD), pl.ctxT, dO, dWo_i), pl.gemm_ws, pl.gemm_bytes, st),
            "attn wgrad dWo_i = ctx_i^T dO");
   } else {
-    TP_STEP(TP_STEP_OUT_WGRAD, gemm_launch(dt, gd(GR_OUT_WGRAD, hl, h, T, ctx_i, hl, false, dO, h, false, EPI_STORE, dWo_i, h), pl.gemm_ws, pl.gemm_bytes, st),
+    TP_STEP(TP_STEP_OUT_WGRAD, gemm_launch(dt, with_ptrs(step_gemm(dm, TP_STEP_OUT_WGRAD), ctx_i, dO, dWo_i), pl.gemm_ws, pl.gemm_bytes, st),
            "attn wgrad dWo_i = ctx_i^T dO");
   }
   if (dbo_or_null) TP_STEP(TP_STEP_BIAS_GRADS, colsum_launch(dt, dO, T, h, h, dbo_or_null, (float*)pl.col_ws, st), "attn dbo");
@@ -553,18 +616,18 @@ tp_status attn_bwd_impl(const tp_shape* shape, const tp_dropout* dr, const uint1
   if (copies) {
     // dqkv^T copy with dbqkv_i's column partials
     TP_STEP(TP_STEP_TRANSPOSE, transpose_colsum_launch(pl.dqkv, T, 3 * hl, 3 * hl, pl.dqkvT, ldt, pl.tpart, st), "attn dqkv^T copy");
-    TP_STEP(TP_STEP_QKV_WGRAD, gemm_launch(dt, gd(GR_QKV_WGRAD, h, 3 * hl, T, X, h, false, pl.dqkvT, ldt, true, EPI_STORE, dWqkv_i, 3 * hl), pl.gemm_ws,
+    TP_STEP(TP_STEP_QKV_WGRAD, gemm_launch(dt, with_ptrs(step_gemm(dm, TP_STEP_QKV_WGRAD), X, pl.dqkvT, dWqkv_i), pl.gemm_ws,
                        pl.gemm_bytes, st),
            "attn wgrad dWqkv_i = X^T dqkv");
     TP_STEP(TP_STEP_BIAS_GRADS, colsum_final_launch(dt, pl.tpart, transpose_part_rows(T), 3 * hl, dbqkv_i, st), "attn dbqkv_i");
   } else {
-    TP_STEP(TP_STEP_QKV_WGRAD, gemm_launch(dt, gd(GR_QKV_WGRAD, h, 3 * hl, T, X, h, false, pl.dqkv, 3 * hl, false, EPI_STORE, dWqkv_i, 3 * hl), pl.gemm_ws,
+    TP_STEP(TP_STEP_QKV_WGRAD, gemm_launch(dt, with_ptrs(step_gemm(dm, TP_STEP_QKV_WGRAD), X, pl.dqkv, dWqkv_i), pl.gemm_ws,
                        pl.gemm_bytes, st),
            "attn wgrad dWqkv_i = X^T dqkv");
     TP_STEP(TP_STEP_BIAS_GRADS, colsum_launch(dt, pl.dqkv, T, 3 * hl, 3 * hl, dbqkv_i, (float*)pl.col_ws, st), "attn dbqkv_i");
   }
   if (T > 0)
-    TP_STEP(TP_STEP_QKV_DGRAD, gemm_launch(dt, gd(GR_QKV_DGRAD, T, h, 3 * hl, pl.dqkv, 3 * hl, true, Wqkv_i, 3 * hl, true, EPI_STORE, dX_i, h), pl.gemm_ws,
+    TP_STEP(TP_STEP_QKV_DGRAD, gemm_launch(dt, with_ptrs(step_gemm(dm, TP_STEP_QKV_DGRAD), pl.dqkv, Wqkv_i, dX_i), pl.gemm_ws,
                        pl.gemm_bytes, st),
            "attn dgrad dX_i = dqkv Wqkv_i^T");
   return TP_OK;

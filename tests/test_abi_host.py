@@ -42,7 +42,7 @@ def test_library_loads_and_exports_every_declared_symbol():
                           "tp_vocab_workspace_bytes", "tp_vocab_ce_fwd", "tp_vocab_ce_combine", "tp_vocab_ce_bwd",
                           "tp_attn_dropout_mask_bytes", "tp_attn_fwd_dropout", "tp_attn_bwd_dropout",
                           "tp_ln_dropout_mask_bytes", "tp_ln_residual_fwd_dropout", "tp_ln_residual_bwd_dropout",
-                          "tp_ln_residual_bwd_noalloc", "tp_ln_residual_bwd_noalloc_max_scratch_bytes",
+                          "tp_ln_residual_bwd_noalloc", "tp_ln_residual_bwd_noalloc_max_scratch_bytes", "tp_step_kernel",
                           "tp_attn_qkv_bytes"}
     for n in names:
         assert isinstance(getattr(lib, n), ctypes._CFuncPtr), n

@@ -18,6 +18,12 @@ its k-split covers every CU exactly; at T = 1900 (8 row tiles, the last one
   * h = 2720, f = 2560: the GEMM2 input gradient (+ GeLU' epilogue), 8 x 8 =
     64 tiles in 4 k-parts, K = 2720 (the last part ends in a partial k-step);
   * h = 2560, f = 2720: the GEMM1 input gradient, the same split over K = 2720.
+Narrow layers take 256x192 tiles for the input gradients where their plan is
+shorter; at h = 384, f = 3000, T = 2100 (9 row tiles, the last one 52 rows):
+  * the GEMM2 input gradient (N = f = 3000, K = 384) runs 9 x 16 data-parallel
+    tiles, the last column of tiles 120 wide;
+  * the GEMM1 input gradient (N = h = 384, K = 3000: a partial last k-step)
+    runs 18 tiles dealt out stream-K over the CUs, with the fix-up.
 The oracle recomputes column sub-shards and sampled token rows exactly."""
 import numpy as np
 import pytest
@@ -46,7 +52,8 @@ def _gpu():
 
 
 def workload(h, ffn, tokens=TOKENS):
-    return synth.Workload(f"wide_h{h}_f{ffn}", batch=1, seq=tokens, hidden=h, n_heads=h // 160, head_dim=160,
+    d = 160 if h % 160 == 0 else 128
+    return synth.Workload(f"wide_h{h}_f{ffn}", batch=1, seq=tokens, hidden=h, n_heads=h // d, head_dim=d,
                           ffn=ffn, tp_size=1, dtype="bf16", bias_std=0.5)
 
 
@@ -56,15 +63,20 @@ def samples(n, k, rng):
 
 @pytest.mark.parametrize("h,ffn,tokens,exact_split", [
     (3200, 9600, TOKENS, False), (9600, 3200, TOKENS, False), (8960, 8960, TOKENS, False),
-    (2720, 2560, 1900, True), (2560, 2720, 1900, True)],
-    ids=["fc2_dgrad_wide", "fc1_dgrad_wide", "fwd_wide", "fc2_dgrad_exact_ksplit", "fc1_dgrad_exact_ksplit"])
+    (2720, 2560, 1900, True), (2560, 2720, 1900, True), (384, 3000, TOKENS, False)],
+    ids=["fc2_dgrad_wide", "fc1_dgrad_wide", "fwd_wide", "fc2_dgrad_exact_ksplit", "fc1_dgrad_exact_ksplit",
+         "dgrads_192_wide"])
 def test_mlp_wide_tiles_ragged_tokens(h, ffn, tokens, exact_split):
     if exact_split and torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("the exact k-split of 64 tiles in 4 parts is planned for a 256-CU device only")
     w = workload(h, ffn, tokens)
-    print(f"\n  [wide MLP] T={tokens} h={h} f={ffn}", flush=True)
-    inp = synth.draw_shard(w, seed=21, skip=ATTN_IN)
     s = shape_of(w, 0)
+    print(f"\n  [wide MLP] T={tokens} h={h} f={ffn}: {tp.tp_step_kernel(s, 'fc2_dgrad')}, "
+          f"{tp.tp_step_kernel(s, 'fc1_dgrad')}", flush=True)
+    if h == 384 and torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert tp.tp_step_kernel(s, "fc2_dgrad").endswith("_n192")
+        assert tp.tp_step_kernel(s, "fc1_dgrad").endswith("_n192")
+    inp = synth.draw_shard(w, seed=21, skip=ATTN_IN)
     T, bf, nan = w.tokens, torch.bfloat16, float("nan")
     d = {k: inp[k].cuda().contiguous() for k in MLP_IN}
     o = {"pre": torch.full((T, ffn), nan, dtype=bf, device="cuda"),
