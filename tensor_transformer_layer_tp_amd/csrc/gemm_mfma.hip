@@ -9,8 +9,11 @@
 // Products with a k-inner B may take a 256x320 tile instead (8 waves, 4x2,
 // 64x160 each, 160 accumulators); GEMM2 and the output projection (k-outer
 // B) take a 256x320 tile on v_mfma_f32_16x16x32_bf16 (8 waves, 2x4, 128x80
-// each) when its tiles run in whole data-parallel rounds. K advances 64 at a time
-// through two LDS stages (2 x 64 KiB, or 2 x 72 KiB for the 320-wide tiles).
+// each) when its tiles run in whole data-parallel rounds. Narrow layers' products
+// may take a 256x192 tile (8 waves, 4x2, 64x96 each, either B layout) when it
+// fills the CUs in whole rounds where 256-wide tiles would leave a stream-K
+// tail. K advances 64 at a time through two LDS stages (2 x 64 KiB; 2 x 72
+// KiB for the 320-wide tiles, 2 x 56 KiB for the 192-wide ones).
 //
 // Global -> LDS: buffer loads that write LDS directly (16 bytes per lane; one
 // instruction fills 1 KiB in lane order), so no VGPRs stage the tiles. Each
@@ -25,7 +28,8 @@
 //    an MFMA fragment is one ds_read_b128 per lane.
 //  * k-outer operand (memory holds k-rows with the m/n index contiguous: the
 //    weight of a forward product, both operands of a weight gradient): kept in
-//    memory order, [64 k][256 cols], chunk c of k-row q at c ^ 4(q & 3); an
+//    memory order, [64 k][256 cols], chunk c of k-row q at c ^ 4(q & 3) (192
+//    cols: [64 k][24 chunks], the swizzle of panel_kouter192); an
 //    MFMA fragment is two ds_read_b64_tr_b16 per lane (the transposing LDS
 //    read of gfx950: lane 4r+c of each 16-lane group fetches 4 columns of
 //    k-row r, and lane i receives column i of the 4 rows).
@@ -171,6 +175,32 @@ __device__ __forceinline__ Panel<NLI> panel_kouter(const bf16* X, long ld, int r
   return pn;
 }
 
+// k-outer X[k*ld + c], the 192 columns c0g.. of `cols` (a 192-wide tile's
+// B): the stage holds 64 k-rows of 24 chunks (384 bytes). Load i of wave w
+// fills linear chunk q = 64(NLI*w + i) + lane, i.e. k-row q / 24, physical
+// chunk q % 24, which holds logical chunk (q % 24) ^ kout192_swz(k-row). The
+// XOR stays inside aligned groups of 8 chunks; with 384-byte rows it puts the
+// 8 (k-row, 32-byte column pair) reads that one transposing read serves
+// together (lanes 0-31, or lanes 0-15 with 32-47) in 8 different 32-byte
+// bank groups (checked exhaustively on the CPU for both groupings).
+__device__ __forceinline__ int kout192_swz(int kr) { return 4 * ((kr >> 1) & 1) + 2 * ((kr >> 3) & 1); }
+template <int NLI>
+__device__ __forceinline__ Panel<NLI> panel_kouter192(const bf16* X, long ld, int cols, int K, int c0g, int wave,
+                                                      int lane) {
+  Panel<NLI> pn;
+  pn.base = uni_ptr(X + c0g);
+  pn.nrec = uni((uint32_t)(((long)K * ld - c0g) * 2));
+  pn.kstep = uni((uint32_t)(BKK * ld * 2));
+#pragma unroll
+  for (int i = 0; i < NLI; ++i) {
+    const int q = 64 * (NLI * wave + i) + lane;
+    const int kr = q / 24, pc = q - 24 * kr;
+    const int lc = pc ^ kout192_swz(kr);
+    pn.voff[i] = (c0g + 8 * lc < cols) ? (uint32_t)(((long)kr * ld + 8 * lc) * 2) : pn.nrec;
+  }
+  return pn;
+}
+
 // Issue the NLI loads of one operand for k-step kt into LDS stage `dst`.
 // TAIL: k-step kt may be a partial one (k-inner chunks at or past K must
 // read zeros, not the next row); the caller passes false for every k-step
@@ -212,10 +242,21 @@ __device__ __forceinline__ int kout_lane_off(int colbase, int jb, int lane) {
   const int chunk = (col >> 3) ^ (4 * (j >> 2));
   return (8 * v + (j >> 2)) * 512 + chunk * 16 + 8 * (j & 1);
 }
+// 192-wide k-outer stage (384-byte k-rows, swizzle kout192_swz): the same
+// lane roles; the swizzle depends on bits 1 and 3 of the k-row, which the
+// +16kk and +4 steps of the reads leave unchanged.
+__device__ __forceinline__ int kout192_lane_off(int colbase, int jb, int lane) {
+  const int j = lane & 15, h = (lane >> 4) & 1, v = lane >> 5;
+  const int col = colbase + 32 * jb + 16 * h + 4 * (j & 3);
+  const int kr = 8 * v + (j >> 2);
+  return kr * 384 + ((col >> 3) ^ kout192_swz(kr)) * 16 + 8 * (j & 1);
+}
+// RS: bytes per k-row of the stage (512 for 256 columns, 384 for 192)
+template <int RS>
 __device__ __forceinline__ bf16x8 frag_kout(const bf16* s, int lane_off, int kk) {
-  const char* b = (const char*)s + lane_off + kk * 16 * 512;
+  const char* b = (const char*)s + lane_off + kk * 16 * RS;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(b));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(b + 4 * 512));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(b + 4 * RS));
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v);
@@ -251,8 +292,8 @@ __device__ __forceinline__ void kstep(const KParams& p, const Panel<WC<NW, BNV>:
   bf16x8 af[2][MI], bfg[2][NJ];
 #pragma unroll
   for (int i = 0; i < NF; ++i) {
-    if (i < MI) af[0][i] = AK ? frag_kin(a, rowA, s1, g, 0, i, pbA) : frag_kout(a, offA[i], 0);
-    if (i < NJ) bfg[0][i] = BKM ? frag_kin(b, rowB, s1, g, 0, i, pbB) : frag_kout(b, offB[i], 0);
+    if (i < MI) af[0][i] = AK ? frag_kin(a, rowA, s1, g, 0, i, pbA) : frag_kout<2 * BM>(a, offA[i], 0);
+    if (i < NJ) bfg[0][i] = BKM ? frag_kin(b, rowB, s1, g, 0, i, pbB) : frag_kout<2 * BNV>(b, offB[i], 0);
   }
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -260,8 +301,9 @@ __device__ __forceinline__ void kstep(const KParams& p, const Panel<WC<NW, BNV>:
     if (kk < 3) {
 #pragma unroll
       for (int i = 0; i < NF; ++i) {
-        if (i < MI) af[n][i] = AK ? frag_kin(a, rowA, s1, g, kk + 1, i, pbA) : frag_kout(a, offA[i], kk + 1);
-        if (i < NJ) bfg[n][i] = BKM ? frag_kin(b, rowB, s1, g, kk + 1, i, pbB) : frag_kout(b, offB[i], kk + 1);
+        if (i < MI) af[n][i] = AK ? frag_kin(a, rowA, s1, g, kk + 1, i, pbA) : frag_kout<2 * BM>(a, offA[i], kk + 1);
+        if (i < NJ)
+          bfg[n][i] = BKM ? frag_kin(b, rowB, s1, g, kk + 1, i, pbB) : frag_kout<2 * BNV>(b, offB[i], kk + 1);
       }
     }
 #pragma unroll
@@ -306,7 +348,7 @@ __device__ __forceinline__ void mainloop(const KParams& p, int tm, int tn, int k
                                          f32x16 (&acc)[WC<NW, BNV>::MI][WC<NW, BNV>::NJ], bf16* smem) {
   using C = WC<NW, BNV>;
   constexpr int MI = C::MI, NJ = C::NJ, WNG = C::WNG, WMW = C::WMW, WNW = C::WNW;
-  static_assert(BKM || BNV == 256, "k-outer B panels are 256 columns wide");
+  static_assert(BKM || BNV == 256 || BNV == 192, "k-outer B panels are 256 or 192 columns wide");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = (int)uni((uint32_t)(tid >> 6));
   const int wm = wave / WNG, wn = wave % WNG;
@@ -317,6 +359,7 @@ __device__ __forceinline__ void mainloop(const KParams& p, int tm, int tn, int k
   if (AK) pa = panel_kinner<C::NLA, BM>(p.A, p.lda, p.M, tm * BM, wave, lane);
   else pa = panel_kouter<C::NLA>(p.A, p.lda, p.M, p.K, tm * BM, wave, lane);
   if (BKM) pb = panel_kinner<C::NLB, BNV>(p.B, p.ldb, p.N, tn * BNV, wave, lane);
+  else if (BNV == 192) pb = panel_kouter192<C::NLB>(p.B, p.ldb, p.N, p.K, tn * BNV, wave, lane);
   else pb = panel_kouter<C::NLB>(p.B, p.ldb, p.N, p.K, tn * BNV, wave, lane);
   const int rowA = (wm * WMW + l32) * BKK, rowB = (wn * WNW + l32) * BKK;
   const int pbA = (wm * WMW / 32) & 1, pbB = (wn * WNW / 32) & 1;
@@ -324,7 +367,8 @@ __device__ __forceinline__ void mainloop(const KParams& p, int tm, int tn, int k
 #pragma unroll
   for (int i = 0; i < MI; ++i) offA[i] = AK ? 0 : kout_lane_off(wm * WMW, i, lane);
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) offB[j] = BKM ? 0 : kout_lane_off(wn * WNW, j, lane);
+  for (int j = 0; j < NJ; ++j)
+    offB[j] = BKM ? 0 : BNV == 192 ? kout192_lane_off(wn * WNW, j, lane) : kout_lane_off(wn * WNW, j, lane);
   issue_panel<C::NLA, AK, true>(pa, kb, p.K, stage_a<BNV>(smem, 0), wave, lane);
   issue_panel<C::NLB, BKM, true>(pb, kb, p.K, stage_b<BNV>(smem, 0), wave, lane);
   // the one k-step that may be partial (none if K is a multiple of BKK); only
@@ -947,6 +991,10 @@ TP_GEMM_KERNELS(gemm_qkv_proj_f32, 8, 256, true, false, EPI_BIAS_F32)
 TP_GEMM_KERNELS(gemm_out_proj, 8, 256, true, false, EPI_STORE)
 TP_GEMM_KERNELS(gemm_fc1_bias_gelu, 8, 256, true, false, EPI_BIAS_GELU)
 TP_GEMM_KERNELS(gemm_fc2, 8, 256, true, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_qkv_proj_n192, 8, 192, true, false, EPI_QKV_PLANES)
+TP_GEMM_KERNELS(gemm_out_proj_n192, 8, 192, true, false, EPI_STORE)
+TP_GEMM_KERNELS(gemm_fc1_bias_gelu_n192, 8, 192, true, false, EPI_BIAS_GELU)
+TP_GEMM_KERNELS(gemm_fc2_n192, 8, 192, true, false, EPI_STORE)
 // input gradients: both k-inner (weights read transposed)
 TP_GEMM_KERNELS(gemm_fc2_dgrad_gelu, 8, 256, true, true, EPI_DGELU)
 TP_GEMM_KERNELS(gemm_fc1_dgrad, 8, 256, true, true, EPI_STORE)
@@ -1100,12 +1148,14 @@ struct RoleKernels {
 bool role_kernels(const GemmDesc& g, RoleKernels& r) {
   switch (g.role) {
     case GR_QKV_PROJ:
-      if (g.epi == EPI_QKV_PLANES) { r.base = TP_K(gemm_qkv_proj); r.ep = EPI_QKV_PLANES; }
+      if (g.epi == EPI_QKV_PLANES) { r.base = TP_K(gemm_qkv_proj); r.w192 = TP_K(gemm_qkv_proj_n192); r.ep = EPI_QKV_PLANES; }
       else { r.base = TP_K(gemm_qkv_proj_f32); r.ep = EPI_BIAS_F32; }
       return true;
-    case GR_OUT_PROJ: r.base = TP_K(gemm_out_proj); r.f320 = TP_KF(gemm_out_proj_n320); return true;
-    case GR_FC1: r.base = TP_K(gemm_fc1_bias_gelu); r.ep = EPI_BIAS_GELU; return true;
-    case GR_FC2: r.base = TP_K(gemm_fc2); r.f320 = TP_KF(gemm_fc2_n320); return true;
+    case GR_OUT_PROJ:
+      r.base = TP_K(gemm_out_proj); r.f320 = TP_KF(gemm_out_proj_n320); r.w192 = TP_K(gemm_out_proj_n192); return true;
+    case GR_FC1:
+      r.base = TP_K(gemm_fc1_bias_gelu); r.w192 = TP_K(gemm_fc1_bias_gelu_n192); r.ep = EPI_BIAS_GELU; return true;
+    case GR_FC2: r.base = TP_K(gemm_fc2); r.f320 = TP_KF(gemm_fc2_n320); r.w192 = TP_K(gemm_fc2_n192); return true;
     case GR_FC2_DGRAD:
       r.base = TP_K(gemm_fc2_dgrad_gelu); r.w320 = TP_K(gemm_fc2_dgrad_gelu_n320);
       r.w192 = TP_K(gemm_fc2_dgrad_gelu_n192); r.bk = true; r.ep = EPI_DGELU; return true;
@@ -1188,9 +1238,9 @@ bool pick(const GemmDesc& g, size_t ws_bytes, Pick& out) {
   }
   // k-inner B: the 320-wide tile when N is a whole number of them and they
   // fill the CUs at least once, or, fewer, when their k-split covers every CU
-  // exactly; else the 192-wide tile when its plan is shorter than the
-  // 256-wide one's (whole rounds or an exact k-split instead of a stream-K
-  // tail and its fix-up)
+  // exactly. Then (either B layout) the 192-wide tile when its plan is
+  // shorter than the 256-wide one's (whole rounds or an exact k-split instead
+  // of a stream-K tail and its fix-up)
   int bn = 256;
   if (r.w320.mk != nullptr && g.N % BN_MAX == 0) {
     const int t320 = tm * (g.N / BN_MAX);
