@@ -95,6 +95,10 @@ struct KParams {
   // rounds, workgroup lw < splits*split_tiles takes k-range lw / split_tiles of
   // tile split_first + lw % split_tiles.
   int splits, split_first, split_tiles;
+  // Phase-block tile numbering of a stream-K plan (blk_s > 0; see
+  // phase_blocks): tile t is position t / blk_s of block t % blk_s, blocks of
+  // blk_m x blk_n tiles; workgroups keep their hardware order
+  int blk_s, blk_m, blk_n;
 };
 
 __device__ __forceinline__ int logical_wg(int w, int g) {
@@ -104,6 +108,12 @@ __device__ __forceinline__ int logical_wg(int w, int g) {
 }
 
 __device__ __forceinline__ void tile_coords(const KParams& p, int t, int& tm, int& tn) {
+  if (p.blk_s > 0) {
+    const int rho = t % p.blk_s, i = t / p.blk_s, nbn = p.tiles_n / p.blk_n;
+    tm = (rho / nbn) * p.blk_m + i % p.blk_m;
+    tn = (rho % nbn) * p.blk_n + i / p.blk_m;
+    return;
+  }
   int group = GROUP_M * p.tiles_n;
   int g = t / group;
   int first_m = g * GROUP_M;
@@ -633,7 +643,7 @@ __device__ __forceinline__ void store_partial(float* slot, const f32x16 (&acc)[W
 template <int NW, int BNV, bool AK, bool BKM, int EPI>
 __device__ __forceinline__ void gemm_body(const KParams& p, bf16* smem) {
   constexpr int MI = WC<NW, BNV>::MI, NJ = WC<NW, BNV>::NJ;
-  const int lw = logical_wg(blockIdx.x, p.grid);
+  const int lw = p.blk_s > 0 ? (int)blockIdx.x : logical_wg(blockIdx.x, p.grid);
   if (p.splits > 1) {
     // data-parallel rounds, then the split tail: consecutive workgroups (one
     // XCD) take the same k-range of neighbouring tiles, so they share panels
@@ -1052,6 +1062,7 @@ struct Plan {
   int grid, dp_rounds, sk_grid, sk_first_tile, sk_tiles;
   long long sk_begin, sk_total;
   int splits;
+  int blk_s, blk_m, blk_n;  // phase blocks (0: raster order)
 };
 
 // Data-parallel rounds of ncu tiles; the remaining R tiles, if a partial
@@ -1091,6 +1102,45 @@ Plan make_plan(int tiles, int iters, int ncu) {
   pl.sk_total = (long long)pl.sk_tiles * iters;
   pl.sk_grid = (int)(pl.sk_total < ncu ? pl.sk_total : ncu);
   return pl;
+}
+
+// Stream-K over all tiles with the same whole number q of k-steps per
+// workgroup: workgroup w starts at k-step (q w) mod iters of tile q w / iters,
+// so the workgroups w = r (mod P), P = iters / gcd(q, iters), run in step
+// (the same k-step at the same time) on tiles t_r + s i, i = 0 .. c-1, with
+// c = grid / P and s = tiles / c. Workgroups are dealt round-robin to the 8
+// XCDs: with P a multiple of 8 each such class sits on one XCD. Numbering the
+// tiles so that each class's c tiles form a compact bm x bn block of the tile
+// grid (tile t = position t / s of block t % s) lets the class share its
+// operand panels in that XCD's L2: bm + bn panel loads per k-step instead of
+// 2c. (In the raster order the workgroups of one XCD sit at up to 16
+// different k-steps of their tiles, and the panels come from the
+// memory-side cache at a lower rate.)
+void phase_blocks(Plan& pl, int tiles_m, int tiles_n, int iters) {
+  if (pl.sk_total == 0 || pl.splits > 1 || pl.dp_rounds > 0 || pl.sk_total % pl.sk_grid) return;
+  const long long q = pl.sk_total / pl.sk_grid;
+  long long a = q, b = iters;
+  while (b) {
+    const long long r = a % b;
+    a = b;
+    b = r;
+  }
+  const long long P = iters / a;
+  if (P % 8 || pl.sk_grid % P) return;
+  const int c = (int)(pl.sk_grid / P), tiles = tiles_m * tiles_n;
+  if (tiles % c) return;
+  int bm_best = 0, bn_best = 0;
+  for (int bm = 1; bm <= c; ++bm) {
+    if (c % bm || tiles_m % bm || tiles_n % (c / bm)) continue;
+    if (bm_best == 0 || bm + c / bm < bm_best + bn_best) {
+      bm_best = bm;
+      bn_best = c / bm;
+    }
+  }
+  if (bm_best == 0) return;
+  pl.blk_s = tiles / c;
+  pl.blk_m = bm_best;
+  pl.blk_n = bn_best;
 }
 
 int device_cus() {
@@ -1257,12 +1307,13 @@ bool pick(const GemmDesc& g, size_t ws_bytes, Pick& out) {
   out.bn = bn;
   out.nw = r.nw;
   out.mi = bn == BN_MAX ? WC<8, BN_MAX>::MI : bn == 192 ? WC<8, 192>::MI : 4;
-  const int tiles = tm * ((g.N + bn - 1) / bn);
+  const int tn = (g.N + bn - 1) / bn, tiles = tm * tn;
   Plan pl = make_plan(tiles, iters, ncu);
   if (pl.sk_total > 0 || pl.splits > 1) {
     const size_t slots = pl.splits > 1 ? (size_t)pl.splits * pl.sk_tiles : (size_t)2 * pl.sk_grid;
     if (ws_bytes < slots * BM * bn * sizeof(float)) pl = Plan{tiles, 1, 0, 0, 0, 0, 0, 1};  // data-parallel only
   }
+  phase_blocks(pl, tm, tn, iters);
   out.pl = pl;
   return true;
 }
@@ -1295,6 +1346,7 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
   p.grid = pl.grid; p.dp_rounds = pl.dp_rounds; p.sk_grid = pl.sk_grid;
   p.sk_begin = pl.sk_begin; p.sk_total = pl.sk_total; p.splits = pl.splits;
   p.split_first = pl.sk_first_tile; p.split_tiles = pl.sk_tiles;
+  p.blk_s = pl.blk_s; p.blk_m = pl.blk_m; p.blk_n = pl.blk_n;
   const dim3 block(64 * pk.nw);
   hipLaunchKernelGGL(pk.k.mk, dim3(pl.grid), block, 0, stream, p);
   hipError_t e1 = hipGetLastError();
