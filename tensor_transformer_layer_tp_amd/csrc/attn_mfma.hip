@@ -37,9 +37,12 @@
 // query column and the softmax statistics (max, sum) are per lane, combined
 // with the partner lane 32 away; ctx^T += V^T P^T; the pair merges at the end.
 //
-// Backward: dK/dV per 32-key wave (workgroup = 128 keys, looping over 64-query
-// tiles), dQ per 32-query wave (looping over 64-key tiles); both recompute P
-// from lse, dS = P (dP - delta) with delta = rowsum(dctx * ctx). No atomics.
+// Backward (workgroup = 8 waves, two per SIMD): dK/dV of 128 keys looping
+// over 64-query tiles, each 32-key pair of waves split into a role that
+// recomputes P from lse and accumulates dV and a role that forms dP and
+// dS = P (dP - delta) (delta = rowsum(dctx * ctx)) and accumulates dK; dQ of
+// 128 queries looping over 64-key tiles, each 32-query pair splitting the key
+// tiles' halves. No atomics.
 //
 // Dropout variants (DO): the forward draws, per lane and 32-key block, one
 // Philox4x64-10 block at counter (query, key block, batch << 32 | global head,
@@ -204,6 +207,10 @@ __device__ __forceinline__ bf16x8 pack8(const float* x) {
 }
 
 __device__ __forceinline__ bf16x8 ld8(const bf16* p) { return *(const bf16x8*)p; }
+
+// This wave's LDS reads and writes have completed, then the workgroup
+// barrier (the LDS-only form: loads into LDS stay in flight).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // This wave's loads into LDS have landed, then the workgroup barrier: after it
 // every wave's loads have landed. (The barrier's own fence does not wait for
@@ -457,12 +464,25 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(MP p, int q_first) {
   if (ch == 0) p.lse[(long)head * p.seq + q] = (m + __log2f(lsum)) * (1.0f / kLog2e);
 }
 
-// ---- backward: dK, dV ---------------------------------------------------------------
-template <int D>
-struct KvState {
-  bf16x8 kf[D / 16], vf[D / 16];  // k16 (fp16 bits), v
-  f32x16 dv[D / 32], dk[D / 32];
-};
+// ---- backward ---------------------------------------------------------------------
+// One launch, 8 waves (two per SIMD) per workgroup, two kinds of work item:
+//  * dK/dV of 128 keys (tile kvt), looping over the 64-query tiles from the
+//    diagonal on. Four key pairs of 32 keys; each pair is two waves with
+//    split roles (waves p and p + 4, on one SIMD): role A holds K (fp16) and
+//    the dV accumulator, forms S^T = K Q^T and P = 2^(S - lse), hands P to
+//    role B through LDS and adds P^T dO into dV; role B holds V and the dK
+//    accumulator, forms dP^T = V dO^T and, with A's P, dS = P (dP - delta),
+//    and adds dS^T Q into dK. Each role keeps half the registers of a wave
+//    that did all four products (which fit 256 only up to D = 96), so two
+//    waves share each SIMD and one's softmax arithmetic overlaps the other's
+//    matrix products.
+//  * dQ of 128 queries (tile qt), looping over the 64-key tiles up to the
+//    diagonal. Four query blocks of 32; each is two waves that take the two
+//    32-key halves of every key tile and merge their dQ through LDS at the
+//    end (as the forward's pairs do).
+// P goes through LDS in fp32, so dS is formed from the same unrounded P as
+// in a single wave. No atomics. Narrow heads (D <= 96) take bwd4_mfma below
+// instead.
 
 // lse and delta of a 64-query tile: 64 floats each, after the three tiles.
 __device__ __forceinline__ void dma_stats(const MP& p, char* stage_stats, int head, int q0, int w, int lane) {
@@ -473,6 +493,353 @@ __device__ __forceinline__ void dma_stats(const MP& p, char* stage_stats, int he
   const uint32_t vo = q0 + lane < p.seq ? (uint32_t)((q0 + lane) * 4) : nrec;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(stage_stats + 256 * w), 4, vo, 0, 0, 0);
 }
+
+constexpr int BWD_WAVES = 8;
+// P hand-over: [key pair][query block][quad][lane][4] floats
+constexpr int PBUF_BYTES = 4 * 2 * 4 * 64 * 4 * 4;
+template <int D>
+constexpr int bwd_stage_bytes() { return 3 * TROWS * D * 2 + 512; }  // three tiles + lse and delta of 64 queries
+template <int D>
+constexpr int bwd_lds_bytes() {
+  // two stages and the P buffer; the dQ pairs' merge (4 x NB x 16 floats per
+  // lane) reuses the stages
+  return 2 * bwd_stage_bytes<D>() + PBUF_BYTES;
+}
+static_assert(2 * 3 * TROWS * 160 * 2 + 1024 + PBUF_BYTES <= 160 * 1024, "LDS budget at D = 160");
+
+// Keep bits of this lane's key for the 16 queries of a 32-query block: bit
+// 4 q4 + e for query qs0 + 8 q4 + 4g + e (the order of the score
+// accumulators), taken from the stored 16-bit words (rows padded: the 8-byte
+// loads stay in the row; the key is bit qk of each word).
+__device__ __forceinline__ uint32_t key_keep_bits(const MP& p, int head, int k0w, int qs0, int lane) {
+  const int l32 = lane & 31, g = lane >> 5;
+  const int qk = 4 * (l32 >> 3) + (l32 & 3);
+  const uint16_t* mrow = p.mask + ((long)(head * p.nkb + (k0w >> 5)) * 2 + ((l32 >> 2) & 1)) * p.mstride;
+  uint32_t bits = 0;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int i0 = qs0 + 8 * q4 + 4 * g;
+    const uint64_t wd = i0 < p.seq ? *(const uint64_t*)(mrow + i0) : 0ull;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bits |= (uint32_t)((wd >> (16 * e + qk)) & 1ull) << (4 * q4 + e);
+  }
+  return bits;
+}
+
+// Role A: P of one 32-query block for this lane's key (MASK as in
+// fwd_scores).
+template <bool MASK, bool AL>
+__device__ __forceinline__ void a_probs(const f32x16& sa, const float* sL, float (&pr)[16], float slope2, int qs0,
+                                        int g, int myk, int seq) {
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const f32x4 L = *(const f32x4*)(sL + 8 * q4 + 4 * g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int q = 4 * q4 + e;
+      const int query = qs0 + 8 * q4 + 4 * g + e;
+      float v = sa[q] - L[e] * kLog2e;
+      if (AL) v -= slope2 * (float)(query - myk);
+      float pp = fexp2(v);
+      if (MASK && (query < myk || query >= seq)) pp = 0.f;
+      pr[q] = pp;
+    }
+  }
+}
+
+// 8 values packed to bf16, each times `scale` where its keep bit (bits >> q0) is set, else 0.
+__device__ __forceinline__ bf16x8 pack8_keep(const float* x, uint32_t bits, int q0, float scale) {
+  bf16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (bf16)(((bits >> (q0 + e)) & 1u) ? x[e] * scale : 0.f);
+  return v;
+}
+
+// dK/dV of the 128 keys of tile kvt of one head.
+template <int D, bool AL, bool DO>
+__device__ __forceinline__ void dkdv_item(const MP& p, int head, int kvt, char* __restrict__ st0,
+                                          char* __restrict__ st1, float* __restrict__ pbuf) {
+  constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
+  const int b = head / p.n_local, l = head - b * p.n_local;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = (int)uni((uint32_t)(tid >> 6));
+  const int kp = w & 3;         // key pair
+  const bool roleA = w < 4;     // wave-uniform
+  const long grow0 = (long)b * p.seq;
+  const int k0w = kvt * 128 + 32 * kp;
+  const int myk = k0w + l32;
+  const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
+  const int nqt = (p.seq + TROWS - 1) / TROWS;
+  const int qt0 = (kvt * 128) / TROWS;
+  dma_tile<D, BWD_WAVES>(p.q16, nrec, st0, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, lane);
+  dma_tile<D, BWD_WAVES>(p.qb, nrec, st0 + TB, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, lane);
+  dma_tile<D, BWD_WAVES>(p.dctx, nrec, st0 + 2 * TB, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, lane);
+  dma_stats(p, st0 + 3 * TB, head, qt0 * TROWS, w, lane);
+  // A: K (fp16 bits) and dV; B: V and dK
+  bf16x8 kv[NC];
+  f32x16 acc[NB];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    kv[c] = bf16x8{};
+    if (myk < p.seq) kv[c] = ld8((roleA ? p.k16 : p.vh) + (grow0 + myk) * p.h_l + (long)l * D + 16 * c + 8 * g);
+  }
+#pragma unroll
+  for (int db = 0; db < NB; ++db) acc[db] = f32x16{};
+  const float slope2 = alibi_slope_log2(p, l);
+  const TrOff tro = tr_offsets(lane);
+  const RowOff ro = row_offsets(lane);
+  float* pb = pbuf + kp * (2 * 4 * 64 * 4) + 4 * lane;  // + (qs*4 + q4)*256
+  for (int qt = qt0; qt < nqt; ++qt) {
+    loads_landed_barrier();  // tile qt is in LDS; the other stage and the P buffer are free
+    const bool odd = (qt - qt0) & 1;
+    const char* cur = odd ? st1 : st0;
+    char* nxt = odd ? st0 : st1;
+    if (qt + 1 < nqt) {
+      const int qn = (qt + 1) * TROWS;
+      dma_tile<D, BWD_WAVES>(p.q16, nrec, nxt, grow0, l * D, qn, p.seq, p.h_l, w, lane);
+      dma_tile<D, BWD_WAVES>(p.qb, nrec, nxt + TB, grow0, l * D, qn, p.seq, p.h_l, w, lane);
+      dma_tile<D, BWD_WAVES>(p.dctx, nrec, nxt + 2 * TB, grow0, l * D, qn, p.seq, p.h_l, w, lane);
+      dma_stats(p, nxt + 3 * TB, head, qn, w, lane);
+    }
+    const float* sL = (const float*)(cur + 3 * TB);
+    const float* sDl = sL + 64;
+    const int q0 = qt * TROWS;
+    bf16x8 pf[2][2];  // A: P * keep * scale of both query blocks, packed
+    f32x16 dp[2];     // B: dP^T of both query blocks
+    // phase 1: A scores -> P (to LDS); B dP
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const int qs0 = q0 + 32 * qs;
+      if (qs0 + 31 < k0w || qs0 >= p.seq || k0w >= p.seq) continue;  // wave-uniform: all masked
+      if (roleA) {
+        f32x16 sa = f32x16{};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) sa = mfma_f16(frag_row(cur, qs, c, ro), kv[c], sa);
+        float pr[16];
+        if ((qs0 < k0w + 31) || (qs0 + 32 > p.seq))
+          a_probs<true, AL>(sa, sL + 32 * qs, pr, slope2, qs0, g, myk, p.seq);
+        else
+          a_probs<false, AL>(sa, sL + 32 * qs, pr, slope2, qs0, g, myk, p.seq);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *(__attribute__((address_space(3))) f32x4*)(pb + (qs * 4 + q4) * 256) =
+              f32x4{pr[4 * q4], pr[4 * q4 + 1], pr[4 * q4 + 2], pr[4 * q4 + 3]};
+        if (DO) {  // the value product takes P * keep * scale
+          const uint32_t bits = key_keep_bits(p, head, k0w, qs0, lane);
+          pf[qs][0] = pack8_keep(pr, bits, 0, p.drop_scale);
+          pf[qs][1] = pack8_keep(pr + 8, bits, 8, p.drop_scale);
+        } else {
+          pf[qs][0] = pack8(pr);
+          pf[qs][1] = pack8(pr + 8);
+        }
+      } else {
+        f32x16 d = f32x16{};
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(cur + 2 * TB, qs, c, ro), kv[c], d, 0, 0, 0);
+        dp[qs] = d;
+      }
+    }
+    lds_barrier();  // A's P of both blocks is in LDS
+    // phase 2: A dV += P^T dO; B dS = P (dP - delta), dK += dS^T Q
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const int qs0 = q0 + 32 * qs;
+      if (qs0 + 31 < k0w || qs0 >= p.seq || k0w >= p.seq) continue;
+      bf16x8 f0, f1;
+      const char* tt;
+      if (roleA) {
+        f0 = pf[qs][0];
+        f1 = pf[qs][1];
+        tt = cur + 2 * TB;
+      } else {
+        const uint32_t bits = DO ? key_keep_bits(p, head, k0w, qs0, lane) : 0u;
+        float ds[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 P = *(__attribute__((address_space(3))) const f32x4*)(pb + (qs * 4 + q4) * 256);
+          const f32x4 Dl = *(const f32x4*)(sDl + 32 * qs + 8 * q4 + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int q = 4 * q4 + e;
+            const float dpq = DO ? (((bits >> q) & 1u) ? dp[qs][q] * p.drop_scale : 0.f) : dp[qs][q];
+            ds[q] = P[e] * (dpq - Dl[e]);
+          }
+        }
+        f0 = pack8(ds);
+        f1 = pack8(ds + 8);
+        tt = cur + TB;
+      }
+#pragma unroll
+      for (int db = 0; db < NB; ++db) {
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(tt, db, 2 * qs, tro), f0, acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(tt, db, 2 * qs + 1, tro), f1, acc[db], 0, 0, 0);
+      }
+    }
+  }
+  if (myk < p.seq) {
+    // A: dV; B: dK (times 1 / sqrt(D): the scores' scale)
+    bf16* dst = p.dqkv + (grow0 + myk) * (3L * p.h_l) + (roleA ? 2L : 1L) * p.h_l + (long)l * D;
+    const float sc = roleA ? 1.0f : p.scale;
+#pragma unroll
+    for (int db = 0; db < NB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = (bf16)(acc[db][4 * q4 + e] * sc);
+        *(bf16x4*)(dst + 32 * db + 8 * q4 + 4 * g) = a;
+      }
+  }
+}
+
+// dS of one 32-key block for this lane's query (MASK as in fwd_scores).
+// DO: bit q of `bits` keeps lane q's key; dP is multiplied by keep * scale.
+template <bool MASK, bool AL, bool DO>
+__device__ __forceinline__ void q_dscores(const f32x16& sa, const f32x16& dp, float (&ds)[16], float slope2, float L,
+                                          float Dl, int k0, int g, int myq, int seq, uint32_t bits, float dscale) {
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int key = k0 + 8 * (q >> 2) + 4 * g + (q & 3);
+    float v = sa[q] - L;
+    if (AL) v -= slope2 * (float)(myq - key);
+    float pp = fexp2(v);
+    if (MASK && (key > myq || key >= seq)) pp = 0.f;
+    const float dpq = DO ? (((bits >> q) & 1u) ? dp[q] * dscale : 0.f) : dp[q];
+    ds[q] = pp * (dpq - Dl);
+  }
+}
+
+// dQ of the 128 queries of tile qt of one head: wave w takes queries
+// qt*128 + 32(w & 3) .. +31 and the 32-key half w >> 2 of every 64-key tile.
+template <int D, bool AL, bool DO>
+__device__ __forceinline__ void dq_item(const MP& p, int head, int qt, char* __restrict__ st0,
+                                        char* __restrict__ st1) {
+  constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
+  const int b = head / p.n_local, l = head - b * p.n_local;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = (int)uni((uint32_t)(tid >> 6));
+  const int qw = w & 3, kh = w >> 2;
+  const long grow0 = (long)b * p.seq;
+  const int q0w = qt * 128 + 32 * qw;
+  const int myq = q0w + l32;
+  const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
+  const int kv_end = min(p.seq, qt * 128 + 128);
+  const int nkt = (kv_end + TROWS - 1) / TROWS;
+  dma_tile<D, BWD_WAVES>(p.k16, nrec, st0, grow0, l * D, 0, p.seq, p.h_l, w, lane);
+  dma_tile<D, BWD_WAVES>(p.kb, nrec, st0 + TB, grow0, l * D, 0, p.seq, p.h_l, w, lane);
+  dma_tile<D, BWD_WAVES>(p.vh, nrec, st0 + 2 * TB, grow0, l * D, 0, p.seq, p.h_l, w, lane);
+  bf16x8 qf[NC], cf[NC];  // q16 (fp16 bits), dctx
+  f32x16 dq[NB];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    qf[c] = bf16x8{};
+    cf[c] = bf16x8{};
+    if (myq < p.seq) {
+      const long off = (grow0 + myq) * p.h_l + (long)l * D + 16 * c + 8 * g;
+      qf[c] = ld8(p.q16 + off);
+      cf[c] = ld8(p.dctx + off);
+    }
+  }
+  const float L = myq < p.seq ? p.lse[(long)head * p.seq + myq] * kLog2e : 0.f;
+  const float Dl = myq < p.seq ? p.delta[(long)head * p.seq + myq] : 0.f;
+#pragma unroll
+  for (int db = 0; db < NB; ++db) dq[db] = f32x16{};
+  const float slope2 = alibi_slope_log2(p, l);
+  const TrOff tro = tr_offsets(lane);
+  const RowOff ro = row_offsets(lane);
+  for (int kt = 0; kt < nkt; ++kt) {
+    loads_landed_barrier();
+    const bool odd = kt & 1;
+    const char* cur = odd ? st1 : st0;
+    char* nxt = odd ? st0 : st1;
+    if (kt + 1 < nkt) {
+      const int kn = (kt + 1) * TROWS;
+      dma_tile<D, BWD_WAVES>(p.k16, nrec, nxt, grow0, l * D, kn, p.seq, p.h_l, w, lane);
+      dma_tile<D, BWD_WAVES>(p.kb, nrec, nxt + TB, grow0, l * D, kn, p.seq, p.h_l, w, lane);
+      dma_tile<D, BWD_WAVES>(p.vh, nrec, nxt + 2 * TB, grow0, l * D, kn, p.seq, p.h_l, w, lane);
+    }
+    const int k0 = kt * TROWS + 32 * kh;
+    if (k0 > q0w + 31 || k0 >= p.seq) continue;  // wave-uniform: every key masked
+    f32x16 sa = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      sa = mfma_f16(frag_row(cur, kh, c, ro), qf[c], sa);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(cur + 2 * TB, kh, c, ro), cf[c], dp, 0, 0, 0);
+    }
+    // s[q]: key k0 + 8(q>>2) + 4g + (q&3), query myq
+    uint32_t bits = 0;
+    if (DO)  // this query's keep word of the block (a query past seq reads row seq - 1's, unused)
+      bits = p.mask[((long)(head * p.nkb + (k0 >> 5)) * 2 + g) * p.mstride + min(myq, p.seq - 1)];
+    float ds[16];
+    if ((k0 + 31 > q0w) || (k0 + 32 > p.seq))
+      q_dscores<true, AL, DO>(sa, dp, ds, slope2, L, Dl, k0, g, myq, p.seq, bits, p.drop_scale);
+    else
+      q_dscores<false, AL, DO>(sa, dp, ds, slope2, L, Dl, k0, g, myq, p.seq, bits, p.drop_scale);
+    const bf16x8 df0 = pack8(ds), df1 = pack8(ds + 8);
+    const char* kbt = cur + TB;
+#pragma unroll
+    for (int db = 0; db < NB; ++db) {
+      dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(kbt, db, 2 * kh, tro), df0, dq[db], 0, 0, 0);
+      dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(kbt, db, 2 * kh + 1, tro), df1, dq[db], 0, 0, 0);
+    }
+  }
+  // pair merge: the last tile issued no loads, so after this barrier no wave
+  // reads or writes the stages any more
+  __syncthreads();
+  float* xs = (float*)st0 + qw * (NB * 16 * 64) + lane;
+  if (kh) {
+#pragma unroll
+    for (int db = 0; db < NB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xs[(16 * db + i) * 64] = dq[db][i];
+  }
+  __syncthreads();
+  if (kh || myq >= p.seq) return;
+  bf16* dQ = p.dqkv + (grow0 + myq) * (3L * p.h_l) + (long)l * D;
+#pragma unroll
+  for (int db = 0; db < NB; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 a;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * q4 + e;
+        a[e] = (bf16)((dq[db][i] + xs[(16 * db + i) * 64]) * p.scale);
+      }
+      *(bf16x4*)(dQ + 32 * db + 8 * q4 + 4 * g) = a;
+    }
+}
+
+// Items are numbered heaviest first: the dK/dV item of key tile r and the dQ
+// item of query tile nt-1-r both cover nt-r query/key tile pairs (the causal
+// triangle makes tile costs range from 1 to nt); rank r's dK/dV items, then
+// its dQ items, for every head, so workgroups freed by light items pick up
+// the remaining ones instead of waiting, as two separate launches would, for
+// each launch's heaviest tile.
+template <int D, bool AL, bool DO>
+__global__ __launch_bounds__(64 * BWD_WAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_mfma(MP p) {
+  constexpr int SB = bwd_stage_bytes<D>();
+  __shared__ __attribute__((aligned(16))) char smem[bwd_lds_bytes<D>()];
+  static_assert(4 * (D / 32) * 16 * 64 * 4 <= 2 * SB, "dQ pair merge fits the stages");
+  const int nh = p.batch * p.n_local, nt = (p.seq + 127) / 128;
+  const int head = (int)(blockIdx.x % (unsigned)nh), rk = (int)(blockIdx.x / (unsigned)nh);
+  const int r = rk >> 1;
+  if (rk & 1) dq_item<D, AL, DO>(p, head, nt - 1 - r, smem, smem + SB);
+  else dkdv_item<D, AL, DO>(p, head, r, smem, smem + SB, (float*)(smem + 2 * SB));
+}
+
+// ---- backward, 4 waves per workgroup (narrow heads) --------------------------------
+// Up to D = 96 a wave that holds K, V and both accumulators of its 32 keys
+// (and does all four dK/dV products itself) fits 256 registers, so two such
+// workgroups share a CU, two waves per SIMD; there this form measured faster
+// than the split roles above (0.215 vs 0.276 ms at the GPT-2-like shard,
+// D = 96): no P hand-over through LDS and one barrier per tile instead of two.
+template <int D>
+struct KvState4 {
+  bf16x8 kf[D / 16], vf[D / 16];  // k16 (fp16 bits), v
+  f32x16 dv[D / 32], dk[D / 32];
+};
 
 // P and dS of one 32-query block for this lane's key (MASK as in fwd_scores).
 // DO: kw[q4] holds the keep words of queries qs0 + 8 q4 + 4g + 0..3 (16 bits
@@ -508,10 +875,10 @@ __device__ __forceinline__ void kv_probs(const f32x16& sa, const f32x16& dp, con
 
 // One 64-query tile from stage `cur` (Q16, Q bf16, dctx, then lse, delta).
 template <int D, bool AL, bool DO>
-__device__ __forceinline__ void dkdv_tile(const MP& p, const char* __restrict__ cur, char* __restrict__ nxt,
+__device__ __forceinline__ void dkdv_tile4(const MP& p, const char* __restrict__ cur, char* __restrict__ nxt,
                                           bool issue, int q0, int head, int l, long grow0, int w, int lane, int k0w,
                                           int myk, float slope2, const TrOff& tro, const RowOff& ro,
-                                          KvState<D>& st) {
+                                          KvState4<D>& st) {
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
   const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
   if (issue) {
@@ -572,7 +939,7 @@ __device__ __forceinline__ void dkdv_tile(const MP& p, const char* __restrict__ 
 // dK and dV of the 128 keys of tile kvt of one head (4 waves of 32 keys),
 // looping over the 64-query tiles from the diagonal on.
 template <int D, bool AL, bool DO>
-__device__ __forceinline__ void dkdv_item(const MP& p, int head, int kvt, char* __restrict__ st0,
+__device__ __forceinline__ void dkdv_item4(const MP& p, int head, int kvt, char* __restrict__ st0,
                                           char* __restrict__ st1) {
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
   const int b = head / p.n_local, l = head - b * p.n_local;
@@ -588,7 +955,7 @@ __device__ __forceinline__ void dkdv_item(const MP& p, int head, int kvt, char* 
   dma_tile<D>(p.qb, nrec, st0 + TB, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, lane);
   dma_tile<D>(p.dctx, nrec, st0 + 2 * TB, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, lane);
   dma_stats(p, st0 + 3 * TB, head, qt0 * TROWS, w, lane);
-  KvState<D> st;
+  KvState4<D> st;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     st.kf[c] = bf16x8{};
@@ -610,7 +977,7 @@ __device__ __forceinline__ void dkdv_item(const MP& p, int head, int kvt, char* 
   for (int qt = qt0; qt < nqt; ++qt) {
     loads_landed_barrier();
     const bool odd = (qt - qt0) & 1;
-    dkdv_tile<D, AL, DO>(p, odd ? st1 : st0, odd ? st0 : st1, qt + 1 < nqt, qt * TROWS, head, l, grow0, w, lane, k0w,
+    dkdv_tile4<D, AL, DO>(p, odd ? st1 : st0, odd ? st0 : st1, qt + 1 < nqt, qt * TROWS, head, l, grow0, w, lane, k0w,
                      myk, slope2, tro, ro, st);
   }
   if (myk < p.seq) {
@@ -635,34 +1002,17 @@ __device__ __forceinline__ void dkdv_item(const MP& p, int head, int kvt, char* 
 
 // ---- backward: dQ ----------------------------------------------------------------
 template <int D>
-struct QState {
+struct QState4 {
   bf16x8 qf[D / 16], cf[D / 16];  // q16 (fp16 bits), dctx
   f32x16 dq[D / 32];
   float L, Dl;
 };
 
-// dS of one 32-key block for this lane's query (MASK as in fwd_scores).
-// DO: bit q of `bits` keeps lane q's key; dP is multiplied by keep * scale.
-template <bool MASK, bool AL, bool DO>
-__device__ __forceinline__ void q_dscores(const f32x16& sa, const f32x16& dp, float (&ds)[16], float slope2, float L,
-                                          float Dl, int k0, int g, int myq, int seq, uint32_t bits, float dscale) {
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int key = k0 + 8 * (q >> 2) + 4 * g + (q & 3);
-    float v = sa[q] - L;
-    if (AL) v -= slope2 * (float)(myq - key);
-    float pp = fexp2(v);
-    if (MASK && (key > myq || key >= seq)) pp = 0.f;
-    const float dpq = DO ? (((bits >> q) & 1u) ? dp[q] * dscale : 0.f) : dp[q];
-    ds[q] = pp * (dpq - Dl);
-  }
-}
-
 // One 64-key tile from stage `cur` (K16, K bf16, V).
 template <int D, bool AL, bool DO>
-__device__ __forceinline__ void dq_tile(const MP& p, const char* __restrict__ cur, char* __restrict__ nxt, bool issue,
+__device__ __forceinline__ void dq_tile4(const MP& p, const char* __restrict__ cur, char* __restrict__ nxt, bool issue,
                                         int kv0, int l, long grow0, int w, int lane, int q0w, int myq, float slope2,
-                                        const TrOff& tro, const RowOff& ro, int head, QState<D>& st) {
+                                        const TrOff& tro, const RowOff& ro, int head, QState4<D>& st) {
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
   const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
   if (issue) {
@@ -703,7 +1053,7 @@ __device__ __forceinline__ void dq_tile(const MP& p, const char* __restrict__ cu
 // dQ of the 128 queries of tile qt of one head (4 waves of 32 queries),
 // looping over the 64-key tiles up to the diagonal.
 template <int D, bool AL, bool DO>
-__device__ __forceinline__ void dq_item(const MP& p, int head, int qt, char* __restrict__ st0,
+__device__ __forceinline__ void dq_item4(const MP& p, int head, int qt, char* __restrict__ st0,
                                         char* __restrict__ st1) {
   constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
   const int b = head / p.n_local, l = head - b * p.n_local;
@@ -718,7 +1068,7 @@ __device__ __forceinline__ void dq_item(const MP& p, int head, int qt, char* __r
   dma_tile<D>(p.k16, nrec, st0, grow0, l * D, 0, p.seq, p.h_l, w, lane);
   dma_tile<D>(p.kb, nrec, st0 + TB, grow0, l * D, 0, p.seq, p.h_l, w, lane);
   dma_tile<D>(p.vh, nrec, st0 + 2 * TB, grow0, l * D, 0, p.seq, p.h_l, w, lane);
-  QState<D> st;
+  QState4<D> st;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     st.qf[c] = bf16x8{};
@@ -739,7 +1089,7 @@ __device__ __forceinline__ void dq_item(const MP& p, int head, int qt, char* __r
   for (int kt = 0; kt < nkt; ++kt) {
     loads_landed_barrier();
     const bool odd = kt & 1;
-    dq_tile<D, AL, DO>(p, odd ? st1 : st0, odd ? st0 : st1, kt + 1 < nkt, kt * TROWS, l, grow0, w, lane, q0w, myq,
+    dq_tile4<D, AL, DO>(p, odd ? st1 : st0, odd ? st0 : st1, kt + 1 < nkt, kt * TROWS, l, grow0, w, lane, q0w, myq,
                        slope2, tro, ro, head, st);
   }
   if (myq < p.seq) {
@@ -756,32 +1106,23 @@ __device__ __forceinline__ void dq_item(const MP& p, int head, int qt, char* __r
   }
 }
 
-// The backward's two kinds of work item in one launch. The dK/dV item of key
-// tile r and the dQ item of query tile nt-1-r both cover nt-r query/key tile
-// pairs (the causal triangle makes tile costs range from 1 to nt); items are
-// numbered heaviest first -- rank r's dK/dV items, then its dQ items, for
-// every head -- so workgroups freed by light items pick up the remaining
-// ones instead of waiting, as two separate launches would, for each launch's
-// heaviest tile.
-// Occupancy: a dK/dV wave holds K and V fragments and both accumulators of
-// its 32 keys. Up to D = 96 (without dropout) that fits 256 registers, so
-// two workgroups share a CU (two waves per SIMD: one wave's softmax
-// arithmetic and waits overlap the other's matrix products; 0.296 -> 0.228
-// ms at the GPT-2-like shard, D = 96); wider heads, and the dropout
-// variants (which would spill), run one wave per SIMD.
+// Same items and order as bwd_mfma, 4 waves of 32 keys (or queries): two
+// workgroups per CU without dropout; the dropout variants (which would
+// spill at 256 registers) one. Both take this kernel for D <= 96, so that
+// dropout with p = 0 repeats the plain path's arithmetic bit for bit.
 template <int D, bool DO>
-constexpr int bwd_waves_per_simd() { return (D <= 96 && !DO) ? 2 : 1; }
+constexpr int bwd4_waves_per_simd() { return DO ? 1 : 2; }
 template <int D, bool AL, bool DO>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D, DO>(),
-                                                                     bwd_waves_per_simd<D, DO>()))) void bwd_mfma(MP p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd4_waves_per_simd<D, DO>(),
+                                                                     bwd4_waves_per_simd<D, DO>()))) void bwd4_mfma(MP p) {
   constexpr int SB = 3 * TROWS * D * 2 + 512;  // three tiles + lse and delta of 64 queries
   __shared__ __attribute__((aligned(16))) char st0[SB];
   __shared__ __attribute__((aligned(16))) char st1[SB];
   const int nh = p.batch * p.n_local, nt = (p.seq + 127) / 128;
   const int head = (int)(blockIdx.x % (unsigned)nh), rk = (int)(blockIdx.x / (unsigned)nh);
   const int r = rk >> 1;
-  if (rk & 1) dq_item<D, AL, DO>(p, head, nt - 1 - r, st0, st1);
-  else dkdv_item<D, AL, DO>(p, head, r, st0, st1);
+  if (rk & 1) dq_item4<D, AL, DO>(p, head, nt - 1 - r, st0, st1);
+  else dkdv_item4<D, AL, DO>(p, head, r, st0, st1);
 }
 
 MP make_mp(const AttnDesc& a) {
@@ -872,8 +1213,13 @@ hipError_t fwd_d(const MP& p, hipStream_t stream) {
 template <int D, bool DO>
 hipError_t bwd_d(const MP& p, hipStream_t stream) {
   const dim3 grid((unsigned)(2 * ((p.seq + 127) / 128) * p.batch * p.n_local));
-  if (p.alibi) hipLaunchKernelGGL((bwd_mfma<D, true, DO>), grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((bwd_mfma<D, false, DO>), grid, dim3(256), 0, stream, p);
+  if constexpr (D <= 96) {
+    if (p.alibi) hipLaunchKernelGGL((bwd4_mfma<D, true, DO>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((bwd4_mfma<D, false, DO>), grid, dim3(256), 0, stream, p);
+  } else {
+    if (p.alibi) hipLaunchKernelGGL((bwd_mfma<D, true, DO>), grid, dim3(64 * BWD_WAVES), 0, stream, p);
+    else hipLaunchKernelGGL((bwd_mfma<D, false, DO>), grid, dim3(64 * BWD_WAVES), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

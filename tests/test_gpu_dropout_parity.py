@@ -121,11 +121,14 @@ def test_dropout_attention_matches_oracle(case):
         compare(k, got[k], ref, "bf16")
 
 
-def test_dropout_p0_equals_no_dropout():
-    w = CASES[0][1]
+@pytest.mark.parametrize("case", [0, 1], ids=["d64_four_wave_backward", "d160_split_role_backward"])
+def test_dropout_p0_equals_no_dropout(case):
+    # D <= 96 runs the 4-wave backward, wider heads the 8-wave split-role one;
+    # with p = 0 each dropout variant repeats its plain kernel bit for bit
+    _, w, rank, _ = CASES[case]
     inp = synth.draw_shard(w, seed=12)
-    a = run_gpu(w, inp, 1, tp.TpDropout(0.0, 5, 6))
-    b = run_gpu(w, inp, 1, None)
+    a = run_gpu(w, inp, rank, tp.TpDropout(0.0, 5, 6))
+    b = run_gpu(w, inp, rank, None)
     for k in b:
         assert torch.equal(a[k], b[k]), k
     causal = np.tril(np.ones((w.seq, w.seq), dtype=bool))
