@@ -15,6 +15,7 @@ from __future__ import annotations
 import csv
 import glob
 import os
+import re
 import sys
 from collections import defaultdict
 
@@ -30,6 +31,23 @@ def _rows(d: str, suffix: str):
 
 def short(name: str) -> str:
     n = name.replace("void ", "").replace("(anonymous namespace)::", "").replace("tpk::", "")
+    m = re.match(r"_ZN3tpk12_GLOBAL__N_1(\d+)", n)  # a mangled name the tracer left as is
+    if m:
+        k = int(m.group(1))
+        base = n[m.end():m.end() + k]
+        rest = n[m.end() + k:]
+        if not rest.startswith("I"):
+            return base
+        args, rest = [], rest[1:]
+        while rest and not rest.startswith("E"):
+            t = re.match(r"DF16b|f|Li(\d+)E|Lb([01])E", rest)
+            if not t:
+                break
+            tok = t.group(0)
+            args.append("bf16" if tok == "DF16b" else "float" if tok == "f" else t.group(1) if t.group(1)
+                        else ("true" if t.group(2) == "1" else "false"))
+            rest = rest[t.end():]
+        return base + ("<" + ", ".join(args) + ">" if args else "")
     return n.split("(")[0]
 
 
