@@ -420,23 +420,22 @@ __device__ __forceinline__ void store_bf16x4(bf16* dst, const float (&v)[4]) {
   *(bf16x4*)dst = o;
 }
 
-// Row block i (rows 32i..32i+31 of each wave's rows) of a tile.
+// Column block j (32 columns) of row block i (rows 32i..32i+31 of each
+// wave's rows) of a tile, from its accumulators a.
 template <int NW, int BNV, int EPI>
-__device__ __forceinline__ void epilogue_rows(const KParams& p, int tm, int tn, int i,
-                                              const f32x16 (&acc)[WC<NW, BNV>::NJ]) {
-  constexpr int NJ = WC<NW, BNV>::NJ, WNG = WC<NW, BNV>::WNG, WMW = WC<NW, BNV>::WMW, WNW = WC<NW, BNV>::WNW;
+__device__ __forceinline__ void epilogue_block(const KParams& p, int tm, int tn, int i, int j, const f32x16& a) {
+  constexpr int WNG = WC<NW, BNV>::WNG, WMW = WC<NW, BNV>::WMW, WNW = WC<NW, BNV>::WNW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WNG, wn = wave % WNG;
   {
     const int m = tm * BM + wm * WMW + i * 32 + (lane & 31);
     if (m >= p.M) return;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
+    {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int n = tn * BNV + wn * WNW + j * 32 + q4 * 8 + (lane >> 5) * 4;
         if (n >= p.N) continue;
-        float v[4] = {acc[j][4 * q4], acc[j][4 * q4 + 1], acc[j][4 * q4 + 2], acc[j][4 * q4 + 3]};
+        float v[4] = {a[4 * q4], a[4 * q4 + 1], a[4 * q4 + 2], a[4 * q4 + 3]};
         if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_F32 || EPI == EPI_QKV_PLANES) {
           bf16x4 bb = *(const bf16x4*)(p.bias + n);
 #pragma unroll
@@ -478,6 +477,14 @@ __device__ __forceinline__ void epilogue_rows(const KParams& p, int tm, int tn, 
       }
     }
   }
+}
+
+// Row block i of a tile (all its column blocks).
+template <int NW, int BNV, int EPI>
+__device__ __forceinline__ void epilogue_rows(const KParams& p, int tm, int tn, int i,
+                                              const f32x16 (&acc)[WC<NW, BNV>::NJ]) {
+#pragma unroll
+  for (int j = 0; j < WC<NW, BNV>::NJ; ++j) epilogue_block<NW, BNV, EPI>(p, tm, tn, i, j, acc[j]);
 }
 
 // Whole-tile epilogue through LDS (the stages are free once the main loop has
@@ -720,61 +727,42 @@ __device__ __forceinline__ void gemm_body(const KParams& p, bf16* smem) {
 }
 
 // Stream-K fix-up: sum each split tile's partials in contributor order and
-// apply the epilogue.
+// apply the epilogue. MI x NJ workgroups per tile, one per (row block i,
+// column block j) of the waves' sub-tiles: each thread adds 4 float4 per
+// contributor (a 320-wide tile split 4 ways over K, or a stream-K tile, is
+// spread over 10 or 8 workgroups instead of 2 or 4, so the few split tiles
+// still fill the CUs).
 template <int NW, int BNV, int EPI>
 __device__ __forceinline__ void fixup_body(const KParams& p, int first_tile) {
   constexpr int MI = WC<NW, BNV>::MI, NJ = WC<NW, BNV>::NJ, NTHR = WC<NW, BNV>::NTHR;
-  // MI workgroups per tile, one per row block i of the waves' sub-tiles
-  const int t = first_tile + blockIdx.x / MI, i = blockIdx.x % MI;
+  const int t = first_tile + blockIdx.x / (MI * NJ), r = blockIdx.x % (MI * NJ), i = r / NJ, j = r % NJ;
   const int tid = threadIdx.x;
-  if (p.splits > 1) {  // split tail: tile t's partials are slots (t - first) + s*split_tiles
-    f32x16 acc[NJ];
+  f32x16 acc = f32x16{};
+  auto add = [&](const float* src) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[j] = f32x16{};
-    for (int sidx = 0; sidx < p.splits; ++sidx) {
-      const float* src = p.partials + (long)(sidx * p.split_tiles + t - p.split_first) * BM * BNV;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int f4 = (i * NJ + j) * 4 + q4;
-          f32x4 v = *(const f32x4*)(src + ((long)f4 * NTHR + tid) * 4);
-          acc[j][4 * q4] += v[0];
-          acc[j][4 * q4 + 1] += v[1];
-          acc[j][4 * q4 + 2] += v[2];
-          acc[j][4 * q4 + 3] += v[3];
-        }
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int f4 = (i * NJ + j) * 4 + q4;
+      const f32x4 v = *(const f32x4*)(src + ((long)f4 * NTHR + tid) * 4);
+      acc[4 * q4] += v[0];
+      acc[4 * q4 + 1] += v[1];
+      acc[4 * q4 + 2] += v[2];
+      acc[4 * q4 + 3] += v[3];
     }
-    int tm, tn;
-    tile_coords(p, t, tm, tn);
-    epilogue_rows<NW, BNV, EPI>(p, tm, tn, i, acc);
-    return;
-  }
-  const long long base = p.sk_total / p.sk_grid, rem = p.sk_total % p.sk_grid;
-  const long long t0 = (long long)t * p.iters - p.sk_begin;
-  const long long c0 = sk_owner(t0, base, rem), c1 = sk_owner(t0 + p.iters - 1, base, rem);
-  if (c0 == c1) return;  // one workgroup covered the whole tile and stored it
-  f32x16 acc[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) acc[j] = f32x16{};
-  for (long long c = c0; c <= c1; ++c) {
-    const int slot = (int)(2 * c + (sk_start(c, base, rem) >= t0 ? 0 : 1));
-    const float* src = p.partials + (long)slot * BM * BNV;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int f4 = (i * NJ + j) * 4 + q4;
-        f32x4 v = *(const f32x4*)(src + ((long)f4 * NTHR + tid) * 4);
-        acc[j][4 * q4] += v[0];
-        acc[j][4 * q4 + 1] += v[1];
-        acc[j][4 * q4 + 2] += v[2];
-        acc[j][4 * q4 + 3] += v[3];
-      }
+  };
+  if (p.splits > 1) {  // split tail: tile t's partials are slots (t - first) + s*split_tiles
+    for (int sidx = 0; sidx < p.splits; ++sidx)
+      add(p.partials + (long)(sidx * p.split_tiles + t - p.split_first) * BM * BNV);
+  } else {
+    const long long base = p.sk_total / p.sk_grid, rem = p.sk_total % p.sk_grid;
+    const long long t0 = (long long)t * p.iters - p.sk_begin;
+    const long long c0 = sk_owner(t0, base, rem), c1 = sk_owner(t0 + p.iters - 1, base, rem);
+    if (c0 == c1) return;  // one workgroup covered the whole tile and stored it
+    for (long long c = c0; c <= c1; ++c)
+      add(p.partials + (long)(2 * c + (sk_start(c, base, rem) >= t0 ? 0 : 1)) * BM * BNV);
   }
   int tm, tn;
   tile_coords(p, t, tm, tn);
-  epilogue_rows<NW, BNV, EPI>(p, tm, tn, i, acc);
+  epilogue_block<NW, BNV, EPI>(p, tm, tn, i, j, acc);
 }
 
 // ---- 256x320 tiles for the forward products (k-outer B) ----------------------
@@ -1256,7 +1244,7 @@ double plan_cost(const Plan& pl, int tiles, int iters, int ncu, double per_step)
 struct Pick {
   KRef k;
   int bn = 256, nw = 8;
-  int mi = 4;           // fix-up workgroups per tile (one per row block of the waves' sub-tiles)
+  int fix_per_tile = 8;  // fix-up workgroups per tile: MI x NJ blocks of the waves' sub-tiles
   bool fwd320 = false;  // the forward products' 16x16x32 320-wide kernel (data-parallel only)
   Plan pl{};
 };
@@ -1306,7 +1294,10 @@ bool pick(const GemmDesc& g, size_t ws_bytes, Pick& out) {
   out.k = bn == BN_MAX ? r.w320 : bn == 192 ? r.w192 : r.base;
   out.bn = bn;
   out.nw = r.nw;
-  out.mi = bn == BN_MAX ? WC<8, BN_MAX>::MI : bn == 192 ? WC<8, 192>::MI : 4;
+  out.fix_per_tile = bn == BN_MAX ? WC<8, BN_MAX>::MI * WC<8, BN_MAX>::NJ
+                     : bn == 192  ? WC<8, 192>::MI * WC<8, 192>::NJ
+                     : r.nw == 4  ? WC<4, 256>::MI * WC<4, 256>::NJ
+                                  : WC<8, 256>::MI * WC<8, 256>::NJ;
   const int tn = (g.N + bn - 1) / bn, tiles = tm * tn;
   Plan pl = make_plan(tiles, iters, ncu);
   if (pl.sk_total > 0 || pl.splits > 1) {
@@ -1352,7 +1343,7 @@ hipError_t gemm_mfma_launch(const GemmDesc& g, void* ws, size_t ws_bytes, hipStr
   hipError_t e1 = hipGetLastError();
   const bool sk = pl.sk_total > 0 || pl.splits > 1;
   if (e1 != hipSuccess || !sk || pk.fwd320) return e1;
-  hipLaunchKernelGGL(pk.k.fk, dim3(pk.mi * pl.sk_tiles), block, 0, stream, p, pl.sk_first_tile);
+  hipLaunchKernelGGL(pk.k.fk, dim3(pk.fix_per_tile * pl.sk_tiles), block, 0, stream, p, pl.sk_first_tile);
   return hipGetLastError();
 }
 
