@@ -199,45 +199,59 @@ __global__ __launch_bounds__(NT) void dkdv_kernel(SP p) {
   if (tid + NT < d) { dk[tid + NT] = from_f<T>(k1 * scale); dv[tid + NT] = from_f<T>(v1); }
 }
 
-// delta[b][l][i] = sum_dd dctx[t][l*d+dd] * ctx[t][l*d+dd], t = b*seq + i.
 // delta[b][l][i] = sum_d dctx[t][l*D + d] * ctx[t][l*D + d], t = b*seq + i.
-// One 32-lane half-wave per (token, head) row: lane c reads 8 adjacent
-// elements (16-byte loads of both tensors), then a fixed butterfly of
-// shuffles sums the D/8 (<= 32) lane products.
+// Row r = t*n_local + l is the run of D/8 16-byte chunks (8 elements each)
+// starting at chunk r*D/8 of the flattened [T, h_l] arrays, so consecutive
+// threads read consecutive chunks whatever D is. A workgroup takes DU groups
+// of G = 256/(D/8) whole rows; thread c multiplies chunk c of every group
+// (all loads issued first, clamped in range), the chunk sums go through LDS,
+// and one thread per row adds its D/8 chunk sums in chunk order.
+constexpr int DU = 4;
 template <typename T>
-__global__ __launch_bounds__(256) void delta_kernel(const T* dctx, const T* ctx, float* delta, int batch,
-                                                    int seq, int n_local, int d, int h_l) {
-  const long row = ((long)blockIdx.x * 256 + threadIdx.x) >> 5;
-  const long total = (long)batch * seq * n_local;
-  const int c = threadIdx.x & 31;
-  float s = 0.f;
-  int l = 0;
-  long t = 0;
-  if (row < total) {
-    l = (int)(row % n_local);
-    t = row / n_local;
-    if (8 * c < d) {
-      const T* x = dctx + t * h_l + (long)l * d + 8 * c;
-      const T* y = ctx + t * h_l + (long)l * d + 8 * c;
-      if constexpr (sizeof(T) == 2) {
-        const bf16x8 a = *(const bf16x8*)x, b = *(const bf16x8*)y;
+__global__ __launch_bounds__(256) void delta_kernel(const T* dctx, const T* ctx, float* delta, int seq,
+                                                    int n_local, int d, long rows) {
+  __shared__ float part[DU][256];
+  const int cpr = d >> 3, G = 256 / cpr, c = threadIdx.x;
+  const long r0 = (long)blockIdx.x * DU * G, chunks = rows * cpr;
+  float x[DU][8], y[DU][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s = fmaf((float)a[e], (float)b[e], s);
-      } else {
-        const f32x4 a0 = *(const f32x4*)x, a1 = *(const f32x4*)(x + 4);
-        const f32x4 b0 = *(const f32x4*)y, b1 = *(const f32x4*)(y + 4);
+  for (int u = 0; u < DU; ++u) {
+    const long q = (r0 + (long)u * G) * cpr + c;
+    const long qq = q < chunks ? q : chunks - 1;
+    const T* a = dctx + 8 * qq;
+    const T* b = ctx + 8 * qq;
+    if constexpr (sizeof(T) == 2) {
+      const bf16x8 va = *(const bf16x8*)a, vb = *(const bf16x8*)b;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s = fmaf(a0[e], b0[e], s);
+      for (int e = 0; e < 8; ++e) { x[u][e] = (float)va[e]; y[u][e] = (float)vb[e]; }
+    } else {
+      const f32x4 a0 = *(const f32x4*)a, a1 = *(const f32x4*)(a + 4);
+      const f32x4 b0 = *(const f32x4*)b, b1 = *(const f32x4*)(b + 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s = fmaf(a1[e], b1[e], s);
+      for (int e = 0; e < 4; ++e) {
+        x[u][e] = a0[e]; x[u][4 + e] = a1[e];
+        y[u][e] = b0[e]; y[u][4 + e] = b1[e];
       }
     }
   }
 #pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) s += __shfl_xor(s, off, 32);
-  if (row < total && c == 0) {
-    const int b = (int)(t / seq), i = (int)(t % seq);
-    delta[((long)b * n_local + l) * seq + i] = s;
+  for (int u = 0; u < DU; ++u) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = fmaf(x[u][e], y[u][e], s);
+    part[u][c] = s;
+  }
+  __syncthreads();
+  for (int k = c; k < DU * G; k += 256) {
+    const int u = k / G, j = k - u * G;
+    const long r = r0 + (long)u * G + j;
+    if (r >= rows) continue;
+    float s = 0.f;
+    for (int m = 0; m < cpr; ++m) s += part[u][j * cpr + m];
+    const long t = r / n_local;
+    const int l = (int)(r - t * n_local);
+    const long b = t / seq, i = t - b * seq;
+    delta[(b * n_local + l) * seq + i] = s;
   }
 }
 
@@ -254,14 +268,15 @@ SP make_sp(const AttnDesc& a) {
 hipError_t delta_launch(int dtype, const AttnDesc& a, hipStream_t stream) {
   const long total = (long)a.batch * a.seq * a.n_local;
   if (total == 0) return hipSuccess;
-  dim3 grid((unsigned)((total + 7) / 8));  // 8 rows per 256-thread workgroup
-  const int h_l = a.n_local * a.head_dim;
+  if (a.head_dim % 8 || a.head_dim < 8 || a.head_dim > 256) return hipErrorInvalidValue;
+  const long per_wg = (long)DU * (256 / (a.head_dim / 8));  // whole rows per workgroup
+  dim3 grid((unsigned)((total + per_wg - 1) / per_wg));
   if (dtype == DT_BF16)
     hipLaunchKernelGGL(delta_kernel<bf16>, grid, dim3(256), 0, stream, (const bf16*)a.dctx, (const bf16*)a.ctx,
-                       a.delta, a.batch, a.seq, a.n_local, a.head_dim, h_l);
+                       a.delta, a.seq, a.n_local, a.head_dim, total);
   else
     hipLaunchKernelGGL(delta_kernel<float>, grid, dim3(256), 0, stream, (const float*)a.dctx, (const float*)a.ctx,
-                       a.delta, a.batch, a.seq, a.n_local, a.head_dim, h_l);
+                       a.delta, a.seq, a.n_local, a.head_dim, total);
   return hipGetLastError();
 }
 

@@ -7,9 +7,9 @@
 // accumulators, two waves per SIMD, so one wave's barrier and load waits are
 // covered by the other's MFMAs, and twice as many loads are in flight per CU).
 // Products with a k-inner B may take a 256x320 tile instead (8 waves, 4x2,
-// 64x160 each, 160 accumulators); GEMM2 and the output projection (k-outer
-// B) take a 256x320 tile on v_mfma_f32_16x16x32_bf16 (8 waves, 2x4, 128x80
-// each) when its tiles run in whole data-parallel rounds. Narrow layers' products
+// 64x160 each, 160 accumulators); the output projection (k-outer B) takes
+// a 256x320 tile on v_mfma_f32_16x16x32_bf16 (8 waves, 2x4, 128x80 each)
+// when its tiles run in whole data-parallel rounds. Narrow layers' products
 // may take a 256x192 tile (8 waves, 4x2, 64x96 each, either B layout) when it
 // fills the CUs in whole rounds where 256-wide tiles would leave a stream-K
 // tail. K advances 64 at a time through two LDS stages (2 x 64 KiB; 2 x 72
@@ -765,7 +765,7 @@ __device__ __forceinline__ void fixup_body(const KParams& p, int first_tile) {
   epilogue_block<NW, BNV, EPI>(p, tm, tn, i, j, acc);
 }
 
-// ---- 256x320 tiles for the forward products (k-outer B) ----------------------
+// ---- 256x320 tiles for the output projection (k-outer B) ----------------------
 // 8 waves, 2 along m x 4 along n (128 x 80 each) on v_mfma_f32_16x16x32_bf16:
 // each wave reads its A rows (k-inner, the panel above) through ds_read_b128
 // and its 80 B columns (k-outer: the weight) through the transposing reads,
@@ -1023,18 +1023,19 @@ TP_GEMM_KERNELS(gemm_fc2_wgrad_ko, 4, 256, false, false, EPI_STORE)
 TP_GEMM_KERNELS(gemm_out_wgrad_ko, 4, 256, false, false, EPI_STORE)
 TP_GEMM_KERNELS(gemm_fc1_wgrad_ko, 4, 256, false, false, EPI_STORE)
 TP_GEMM_KERNELS(gemm_qkv_wgrad_ko, 4, 256, false, false, EPI_STORE)
-// forward products with a plain bf16 output on 256x320 tiles (16x16x32
-// MFMAs, data-parallel plans only, so no fix-up kernel). GEMM1 (bias + GeLU,
-// two outputs) keeps the 256-wide tile: on that tile its step time was 30 us
-// longer although the kernel alone ran 3% faster.
+// the output projection on 256x320 tiles (16x16x32 MFMAs, data-parallel
+// plans only, so no fix-up kernel). GEMM1 (bias + GeLU, two outputs) keeps
+// the 256-wide tile: on that tile its step time was 30 us longer although the
+// kernel alone ran 3% faster. GEMM2 and its weight gradient (same k-outer B)
+// also keep it: on the 32x32x16 256-wide tile with a stream-K tail their
+// kernels ran 0.06-0.09 ms faster each and the step 0.10-0.13 ms shorter on
+// three of four GPUs (equal on the fourth).
 #define TP_GEMM_FWD320(NAME, EV)                                                                \
   __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void NAME(KParams p) { \
     __shared__ __attribute__((aligned(16))) bf16 smem[2 * (BM + BN_MAX) * BKK];                 \
     fwd320_body<EV>(p, smem);                                                                   \
   }
 TP_GEMM_FWD320(gemm_out_proj_n320, EPI_STORE)
-TP_GEMM_FWD320(gemm_fc2_n320, EPI_STORE)
-TP_GEMM_FWD320(gemm_fc2_wgrad_n320, EPI_STORE)
 #undef TP_GEMM_FWD320
 // vocabulary-parallel output layer: logits = X W_i^T (the table slice W_i
 // [V/p, h] is k-inner), dX = dlogits W_i, dW_i = dlogits^T X
@@ -1173,7 +1174,7 @@ struct KRef {
 #define TP_KF(NAME) KRef{NAME, nullptr, #NAME}
 
 // The kernels of one product: the 256-wide tile and the alternatives its
-// role has (k-inner B on 320- or 192-wide tiles, the forward products'
+// role has (k-inner B on 320- or 192-wide tiles, the output projection's
 // 16x16x32 320-wide tile, both operands k-outer on 4 waves), with the
 // operand layouts and epilogue the kernels are compiled for.
 struct RoleKernels {
@@ -1193,7 +1194,7 @@ bool role_kernels(const GemmDesc& g, RoleKernels& r) {
       r.base = TP_K(gemm_out_proj); r.f320 = TP_KF(gemm_out_proj_n320); r.w192 = TP_K(gemm_out_proj_n192); return true;
     case GR_FC1:
       r.base = TP_K(gemm_fc1_bias_gelu); r.w192 = TP_K(gemm_fc1_bias_gelu_n192); r.ep = EPI_BIAS_GELU; return true;
-    case GR_FC2: r.base = TP_K(gemm_fc2); r.f320 = TP_KF(gemm_fc2_n320); r.w192 = TP_K(gemm_fc2_n192); return true;
+    case GR_FC2: r.base = TP_K(gemm_fc2); r.w192 = TP_K(gemm_fc2_n192); return true;
     case GR_FC2_DGRAD:
       r.base = TP_K(gemm_fc2_dgrad_gelu); r.w320 = TP_K(gemm_fc2_dgrad_gelu_n320);
       r.w192 = TP_K(gemm_fc2_dgrad_gelu_n192); r.bk = true; r.ep = EPI_DGELU; return true;
@@ -1207,7 +1208,7 @@ bool role_kernels(const GemmDesc& g, RoleKernels& r) {
       r.base = TP_K(gemm_qkv_dgrad); r.w320 = TP_K(gemm_qkv_dgrad_n320); r.w192 = TP_K(gemm_qkv_dgrad_n192);
       r.bk = true; return true;
     case GR_FC2_WGRAD:
-      r.base = TP_K(gemm_fc2_wgrad); r.f320 = TP_KF(gemm_fc2_wgrad_n320); r.ko = TP_K(gemm_fc2_wgrad_ko); return true;
+      r.base = TP_K(gemm_fc2_wgrad); r.ko = TP_K(gemm_fc2_wgrad_ko); return true;
     case GR_FC1_WGRAD:
       r.base = TP_K(gemm_fc1_wgrad); r.w320 = TP_K(gemm_fc1_wgrad_n320); r.ko = TP_K(gemm_fc1_wgrad_ko);
       r.ak = false; r.bk = true; return true;
@@ -1245,7 +1246,7 @@ struct Pick {
   KRef k;
   int bn = 256, nw = 8;
   int fix_per_tile = 8;  // fix-up workgroups per tile: MI x NJ blocks of the waves' sub-tiles
-  bool fwd320 = false;  // the forward products' 16x16x32 320-wide kernel (data-parallel only)
+  bool fwd320 = false;  // the 16x16x32 320-wide kernel (data-parallel only)
   Plan pl{};
 };
 
@@ -1263,9 +1264,8 @@ bool pick(const GemmDesc& g, size_t ws_bytes, Pick& out) {
   if (g.a_kmajor != r.ak || g.b_kmajor != r.bk || g.epi != r.ep) return false;
   const int ncu = device_cus(), cus = ncu < GMAX ? ncu : GMAX;
   const int iters = (g.K + BKK - 1) / BKK, tm = (g.M + BM - 1) / BM;
-  // k-outer-B products (GEMM2, output projection, GEMM2 weight gradient):
-  // 256x320 tiles when N is a whole number of them and the tiles run in
-  // data-parallel rounds (no k-split tail)
+  // the output projection (k-outer B): 256x320 tiles when N is a whole
+  // number of them and the tiles run in data-parallel rounds (no k-split tail)
   if (r.f320.mk != nullptr && g.N % BN_MAX == 0) {
     const int tiles = tm * (g.N / BN_MAX);
     const Plan pl = make_plan(tiles, iters, ncu);

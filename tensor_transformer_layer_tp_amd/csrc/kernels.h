@@ -91,6 +91,11 @@ hipError_t attn_bwd_launch(int dtype, const AttnDesc& a, hipStream_t stream);
 size_t colsum_workspace_bytes(int M, int N);
 hipError_t colsum_launch(int dtype, const void* X, int M, int N, long ld, void* out, float* ws,
                          hipStream_t stream);
+// The same for two matrices with the same row count M (out1 from X1, out2
+// from X2), each pass one launch for both; out2 null: X1 alone.
+size_t colsum_pair_workspace_bytes(int M, int N1, int N2);
+hipError_t colsum_pair_launch(int dtype, int M, const void* X1, int N1, long ld1, void* out1, const void* X2, int N2,
+                              long ld2, void* out2, float* ws, hipStream_t stream);
 
 // bf16 XT[c*ldt + r] = X[r*ldx + c] (r < R, c < C; the 8-row group holding
 // row R-1 is written whole, zeros past R, so ldt must be a multiple of 8 and

@@ -1,6 +1,8 @@
 // Bandwidth-bound helpers: column sums (bias gradients), transposed copies of
 // the weight gradients' token-major operands, the emulated f / g sum over
 // ranks' partials, and zero fill.
+#include <climits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -22,15 +24,36 @@ __global__ __launch_bounds__(CB) void colsum_part_kernel(const T* X, int M, int 
   part[(long)blockIdx.y * N + n] = s;
 }
 
+// Up to two column sums over the same rows, done by one launch of each pass:
+// job q sums the [M, N_q] matrix X_q (leading dimension ld_q) into out_q via
+// the partial rows part_q [R][N_q]; the partial pass gives job 1 the
+// workgroups from blk0 on (x), the final pass those from fblk0 on.
+struct ColJob {
+  const void* X;
+  long ld;
+  int N;
+  int blk0, fblk0;
+  float* part;
+  void* out;
+};
+struct ColJobs {
+  ColJob j[2];
+};
+
 // Same partial sums, 8 adjacent columns per thread (one 16-byte bf16 load or
 // two 16-byte fp32 loads per row): 64 threads span 512 columns and 4 row
 // groups split the run; the row groups are added in a fixed order.
 template <typename T>
-__global__ __launch_bounds__(256) void colsum_part_vec_kernel(const T* X, int M, int N, long ld, int rows_per,
-                                                              float* part) {
+__global__ __launch_bounds__(256) void colsum_part_vec_kernel(ColJobs jobs, int M, int rows_per) {
   __shared__ float red[3][512];
+  const bool q = (int)blockIdx.x >= jobs.j[1].blk0;
+  const T* X = (const T*)(q ? jobs.j[1].X : jobs.j[0].X);
+  const long ld = q ? jobs.j[1].ld : jobs.j[0].ld;
+  const int N = q ? jobs.j[1].N : jobs.j[0].N;
+  float* part = q ? jobs.j[1].part : jobs.j[0].part;
+  const int bx = (int)blockIdx.x - (q ? jobs.j[1].blk0 : 0);
   const int tc = threadIdx.x & 63, rg = threadIdx.x >> 6;
-  const int n0 = blockIdx.x * 512 + 8 * tc;
+  const int n0 = bx * 512 + 8 * tc;
   const int r0 = blockIdx.y * rows_per;
   const int r1 = min(M, r0 + rows_per);
   float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -88,10 +111,15 @@ __global__ __launch_bounds__(256) void colsum_part_vec_kernel(const T* X, int M,
 // partial rows at 16384 tokens).
 constexpr int FC = 32, FG = 8;
 template <typename T>
-__global__ __launch_bounds__(FC * FG) void colsum_final_kernel(const float* part, int R, int N, T* out) {
+__global__ __launch_bounds__(FC * FG) void colsum_final_kernel(ColJobs jobs, int R) {
   __shared__ float red[FG][FC];
+  const bool second = (int)blockIdx.x >= jobs.j[1].fblk0;
+  const float* part = second ? jobs.j[1].part : jobs.j[0].part;
+  const int N = second ? jobs.j[1].N : jobs.j[0].N;
+  T* out = (T*)(second ? jobs.j[1].out : jobs.j[0].out);
+  const int bx = (int)blockIdx.x - (second ? jobs.j[1].fblk0 : 0);
   const int c = threadIdx.x % FC, q = threadIdx.x / FC;
-  const int n = blockIdx.x * FC + c;
+  const int n = bx * FC + c;
   const int nn = n < N ? n : N - 1;  // clamped: every thread loads in range
   float s = 0.f;
   for (int r = q; r < R; r += 8 * FG) {
@@ -213,12 +241,50 @@ unsigned grid_for(long long count) {
 
 }  // namespace
 
-hipError_t colsum_final_launch(int dtype, const float* part, int R, int N, void* out, hipStream_t stream);
+namespace {
+
+bool colsum_vec_ok(const void* X, int N, long ld) { return N % 8 == 0 && ld % 8 == 0 && (uintptr_t)X % 16 == 0; }
+
+ColJobs single_job(const void* X, long ld, int N, float* part, void* out) {
+  ColJobs jobs{};
+  jobs.j[0].X = X; jobs.j[0].ld = ld; jobs.j[0].N = N; jobs.j[0].part = part; jobs.j[0].out = out;
+  jobs.j[1].blk0 = jobs.j[1].fblk0 = INT_MAX;  // no second job
+  return jobs;
+}
+
+hipError_t final_pass(int dtype, const ColJobs& jobs, int R, unsigned fblocks, hipStream_t stream) {
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(colsum_final_kernel<bf16>, dim3(fblocks), dim3(FC * FG), 0, stream, jobs, R);
+  else
+    hipLaunchKernelGGL(colsum_final_kernel<float>, dim3(fblocks), dim3(FC * FG), 0, stream, jobs, R);
+  return hipGetLastError();
+}
+
+hipError_t vec_pass(int dtype, const ColJobs& jobs, unsigned vblocks, int R, int M, int rows_per,
+                    hipStream_t stream) {
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(colsum_part_vec_kernel<bf16>, dim3(vblocks, R), dim3(256), 0, stream, jobs, M, rows_per);
+  else
+    hipLaunchKernelGGL(colsum_part_vec_kernel<float>, dim3(vblocks, R), dim3(256), 0, stream, jobs, M, rows_per);
+  return hipGetLastError();
+}
+
+}  // namespace
 
 size_t colsum_workspace_bytes(int M, int N) {
   int R, rows_per;
   colsum_split(M, N, R, rows_per);
   return (size_t)R * N * sizeof(float);
+}
+
+size_t colsum_pair_workspace_bytes(int M, int N1, int N2) {
+  size_t b = colsum_workspace_bytes(M, N1);
+  const size_t b2 = colsum_workspace_bytes(M, N2);
+  b = b2 > b ? b2 : b;
+  int R, rows_per;
+  colsum_split(M, N1 + N2, R, rows_per);
+  const size_t bp = (size_t)R * (N1 + N2) * sizeof(float);
+  return bp > b ? bp : b;
 }
 
 hipError_t colsum_launch(int dtype, const void* X, int M, int N, long ld, void* out, float* ws,
@@ -227,16 +293,8 @@ hipError_t colsum_launch(int dtype, const void* X, int M, int N, long ld, void* 
   int R, rows_per;
   colsum_split(M, N, R, rows_per);
   const unsigned cblocks = (N + CB - 1) / CB;
-  const bool vec = (N % 8 == 0) && (ld % 8 == 0) && ((uintptr_t)X % 16 == 0);
-  if (M > 0 && vec) {
-    const unsigned vblocks = (N + 511) / 512;
-    if (dtype == DT_BF16)
-      hipLaunchKernelGGL(colsum_part_vec_kernel<bf16>, dim3(vblocks, R), dim3(256), 0, stream, (const bf16*)X, M, N,
-                         ld, rows_per, ws);
-    else
-      hipLaunchKernelGGL(colsum_part_vec_kernel<float>, dim3(vblocks, R), dim3(256), 0, stream, (const float*)X, M,
-                         N, ld, rows_per, ws);
-    hipError_t e = hipGetLastError();
+  if (M > 0 && colsum_vec_ok(X, N, ld)) {
+    const hipError_t e = vec_pass(dtype, single_job(X, ld, N, ws, out), (N + 511) / 512, R, M, rows_per, stream);
     if (e != hipSuccess) return e;
   } else if (M > 0) {
     if (dtype == DT_BF16)
@@ -253,6 +311,27 @@ hipError_t colsum_launch(int dtype, const void* X, int M, int N, long ld, void* 
   return colsum_final_launch(dtype, ws, R, N, out, stream);
 }
 
+hipError_t colsum_pair_launch(int dtype, int M, const void* X1, int N1, long ld1, void* out1, const void* X2, int N2,
+                              long ld2, void* out2, float* ws, hipStream_t stream) {
+  if (out2 == nullptr || N2 <= 0) return colsum_launch(dtype, X1, M, N1, ld1, out1, ws, stream);
+  if (N1 <= 0) return colsum_launch(dtype, X2, M, N2, ld2, out2, ws, stream);
+  if (M <= 0 || !colsum_vec_ok(X1, N1, ld1) || !colsum_vec_ok(X2, N2, ld2)) {  // one after the other
+    const hipError_t e = colsum_launch(dtype, X1, M, N1, ld1, out1, ws, stream);
+    return e != hipSuccess ? e : colsum_launch(dtype, X2, M, N2, ld2, out2, ws, stream);
+  }
+  int R, rows_per;
+  colsum_split(M, N1 + N2, R, rows_per);
+  const unsigned vb1 = (N1 + 511) / 512, vb2 = (N2 + 511) / 512, fb1 = (N1 + FC - 1) / FC,
+                 fb2 = (N2 + FC - 1) / FC;
+  ColJobs jobs = single_job(X1, ld1, N1, ws, out1);
+  jobs.j[1].X = X2; jobs.j[1].ld = ld2; jobs.j[1].N = N2;
+  jobs.j[1].blk0 = (int)vb1; jobs.j[1].fblk0 = (int)fb1;
+  jobs.j[1].part = ws + (size_t)R * N1;
+  jobs.j[1].out = out2;
+  const hipError_t e = vec_pass(dtype, jobs, vb1 + vb2, R, M, rows_per, stream);
+  return e != hipSuccess ? e : final_pass(dtype, jobs, R, fb1 + fb2, stream);
+}
+
 int transpose_part_rows(int R) { return R > 0 ? (R + TR - 1) / TR : 0; }
 
 hipError_t transpose_colsum_launch(const void* X, int R, int C, long ldx, void* XT, long ldt, float* part,
@@ -267,12 +346,7 @@ hipError_t transpose_colsum_launch(const void* X, int R, int C, long ldx, void* 
 
 hipError_t colsum_final_launch(int dtype, const float* part, int R, int N, void* out, hipStream_t stream) {
   if (N <= 0) return hipSuccess;
-  const unsigned fblocks = (N + FC - 1) / FC;
-  if (dtype == DT_BF16)
-    hipLaunchKernelGGL(colsum_final_kernel<bf16>, dim3(fblocks), dim3(FC * FG), 0, stream, part, R, N, (bf16*)out);
-  else
-    hipLaunchKernelGGL(colsum_final_kernel<float>, dim3(fblocks), dim3(FC * FG), 0, stream, part, R, N, (float*)out);
-  return hipGetLastError();
+  return final_pass(dtype, single_job(nullptr, 0, N, (float*)part, out), R, (N + FC - 1) / FC, stream);
 }
 
 hipError_t sum_partials_launch(int dtype, const void* const* parts, int n_parts, const void* bias, void* out,

@@ -217,7 +217,7 @@ MlpPlan plan_mlp(const Dims& dm, void* ws, bool bwd) {
   if (bwd) {
     g = max3(g, gemm_workspace_bytes(dt, (int)dm.fl, (int)dm.h, (int)dm.T),
              gemm_workspace_bytes(dt, (int)dm.h, (int)dm.fl, (int)dm.T));
-    pl.col_bytes = colsum_workspace_bytes((int)dm.T, (int)(dm.fl > dm.h ? dm.fl : dm.h));
+    pl.col_bytes = colsum_pair_workspace_bytes((int)dm.T, (int)dm.fl, (int)dm.h);
     pl.col_ws = bp.take(pl.col_bytes);
   }
   pl.gemm_bytes = g;
@@ -257,7 +257,7 @@ AttnPlan plan_attn(const Dims& dm, void* ws, bool bwd) {
     g = max3(g, gemm_workspace_bytes(dt, (int)B, (int)dm.hl, (int)dm.h),
              gemm_workspace_bytes(dt, (int)dm.hl, (int)dm.h, (int)B));
     g = max3(g, gemm_workspace_bytes(dt, (int)dm.h, (int)(3 * dm.hl), (int)B), 0);
-    pl.col_bytes = colsum_workspace_bytes((int)dm.T, (int)(3 * dm.hl > dm.h ? 3 * dm.hl : dm.h));
+    pl.col_bytes = colsum_pair_workspace_bytes((int)dm.T, (int)(3 * dm.hl), (int)dm.h);
     pl.col_ws = bp.take(pl.col_bytes);
   }
   pl.gemm_bytes = g;
@@ -489,12 +489,17 @@ tp_status tp_mlp_bwd(const tp_shape* shape, const void* X, const void* A_i, cons
            "mlp wgrad dB_i = y_i^T dZ");
     TP_STEP(TP_STEP_FC1_WGRAD, gemm_launch(dt, with_ptrs(step_gemm(dm, TP_STEP_FC1_WGRAD), X, pl.dpre, dA_i), pl.gemm_ws, pl.gemm_bytes, st),
            "mlp wgrad dA_i = X^T dPre");
-    TP_STEP(TP_STEP_BIAS_GRADS, colsum_launch(dt, pl.dpre, T, fl, fl, db1_i, (float*)pl.col_ws, st), "mlp db1_i");
+    // db1_i and db2 in one launch of each column-sum pass
+    TP_STEP(TP_STEP_BIAS_GRADS,
+            colsum_pair_launch(dt, T, pl.dpre, fl, fl, db1_i, dZ, h, h, db2_or_null,
+                               (float*)pl.col_ws, st),
+            "mlp db1_i, db2");
   }
   if (T > 0)
     TP_STEP(TP_STEP_FC1_DGRAD, gemm_launch(dt, with_ptrs(step_gemm(dm, TP_STEP_FC1_DGRAD), pl.dpre, A_i, dX_i), pl.gemm_ws, pl.gemm_bytes, st),
            "mlp dgrad dX_i = dPre A_i^T");
-  if (db2_or_null) TP_STEP(TP_STEP_BIAS_GRADS, colsum_launch(dt, dZ, T, h, h, db2_or_null, (float*)pl.col_ws, st), "mlp db2");
+  if (db2_or_null && wgrad_copies(dm))
+    TP_STEP(TP_STEP_BIAS_GRADS, colsum_launch(dt, dZ, T, h, h, db2_or_null, (float*)pl.col_ws, st), "mlp db2");
   return TP_OK;
 }
 
@@ -601,7 +606,8 @@ tp_status attn_bwd_impl(const tp_shape* shape, const tp_dropout* dr, const uint1
     TP_STEP(TP_STEP_OUT_WGRAD, gemm_launch(dt, with_ptrs(step_gemm(dm, TP_STEP_OUT_WGRAD), ctx_i, dO, dWo_i), pl.gemm_ws, pl.gemm_bytes, st),
            "attn wgrad dWo_i = ctx_i^T dO");
   }
-  if (dbo_or_null) TP_STEP(TP_STEP_BIAS_GRADS, colsum_launch(dt, dO, T, h, h, dbo_or_null, (float*)pl.col_ws, st), "attn dbo");
+  if (dbo_or_null && copies)
+    TP_STEP(TP_STEP_BIAS_GRADS, colsum_launch(dt, dO, T, h, h, dbo_or_null, (float*)pl.col_ws, st), "attn dbo");
   if (T > 0) {
     AttnDesc a;
     a.batch = shape->batch; a.seq = shape->seq; a.n_local = (int)dm.nl; a.head_dim = (int)dm.d;
@@ -624,7 +630,11 @@ tp_status attn_bwd_impl(const tp_shape* shape, const tp_dropout* dr, const uint1
     TP_STEP(TP_STEP_QKV_WGRAD, gemm_launch(dt, with_ptrs(step_gemm(dm, TP_STEP_QKV_WGRAD), X, pl.dqkv, dWqkv_i), pl.gemm_ws,
                        pl.gemm_bytes, st),
            "attn wgrad dWqkv_i = X^T dqkv");
-    TP_STEP(TP_STEP_BIAS_GRADS, colsum_launch(dt, pl.dqkv, T, 3 * hl, 3 * hl, dbqkv_i, (float*)pl.col_ws, st), "attn dbqkv_i");
+    // dbqkv_i and dbo in one launch of each column-sum pass
+    TP_STEP(TP_STEP_BIAS_GRADS,
+            colsum_pair_launch(dt, T, pl.dqkv, 3 * hl, 3 * hl, dbqkv_i, dO, h, h, dbo_or_null,
+                               (float*)pl.col_ws, st),
+            "attn dbqkv_i, dbo");
   }
   if (T > 0)
     TP_STEP(TP_STEP_QKV_DGRAD, gemm_launch(dt, with_ptrs(step_gemm(dm, TP_STEP_QKV_DGRAD), pl.dqkv, Wqkv_i, dX_i), pl.gemm_ws,

@@ -8,10 +8,13 @@ partial last row of tiles) and a stream-K tail:
   * h = 9600, f = 3200: the GEMM1 input gradient runs 320 wide (N = h).
 The GEMM1 weight gradient (X^T times a transposed dPre copy) runs 320 wide in
 both shapes, with K = 2100 tokens (a partial last k-step).
-  * h = f = 8960: the forward GEMM2 runs its 256x320 tile (16x16x32 MFMAs):
-    9 x 28 = 252 tiles, one data-parallel round on 256 CUs, the last row of
-    tiles 52 rows; so does the GEMM2 weight gradient (35 x 28 tiles in four
-    rounds, K = 2100: a partial last k-step).
+  * h = f = 8960: GEMM2 and its weight gradient run 256-wide tiles with a
+    stream-K tail (9 x 35 and 35 x 35 tiles; K = 2100 for the weight
+    gradient: a partial last k-step).
+The output projection takes a 256x320 tile on 16x16x32 MFMAs when its tiles
+run in whole data-parallel rounds; at h = 8960 over 8 ranks (7 heads of 160
+per rank, K = 1120) and T = 2100 that is 9 x 28 = 252 tiles, one round, the
+last row of tiles 52 rows.
 With fewer 320-wide tiles than CUs the input gradients take that tile when
 its k-split covers every CU exactly; at T = 1900 (8 row tiles, the last one
 108 rows) on a 256-CU device:
@@ -111,3 +114,31 @@ def test_mlp_wide_tiles_ragged_tokens(h, ffn, tokens, exact_split):
     compare("Z[R]", o["Z"][R], Z_R, "bf16")
     dX_R = oracle.mlp_bwd(a["X_mlp"][R], a["A"], a["B"], pre_R, y_R, a["dZ"][R])[0]
     compare("dX_mlp[R]", o["dX"][R], dX_R, "bf16")
+
+
+def test_out_projection_wide_tile_ragged_tokens():
+    w = synth.Workload("wide_attn_h8960", batch=1, seq=TOKENS, hidden=8960, n_heads=56, head_dim=160,
+                       ffn=4 * 8960, tp_size=8, dtype="bf16", bias_std=0.5)
+    rank = 3
+    s = shape_of(w, rank)
+    print(f"\n  [wide out-projection] T={TOKENS} h={w.hidden} rank {rank}: {tp.tp_step_kernel(s, 'out_proj')}",
+          flush=True)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert tp.tp_step_kernel(s, "out_proj") == "gemm_out_proj_n320"
+    inp = synth.draw_shard(w, seed=23, skip=MLP_IN)
+    T, h, hl, nl, bf, nan = w.tokens, w.hidden, w.h_local, w.heads_local, torch.bfloat16, float("nan")
+    d = {k: inp[k].cuda().contiguous() for k in ("X_attn", "Wqkv", "bqkv", "Wo")}
+    qkv = torch.full((max(tp.tp_attn_qkv_bytes(s), 1),), 255, dtype=torch.uint8, device="cuda")
+    ctx = torch.full((T, hl), nan, dtype=bf, device="cuda")
+    lse = torch.full((w.batch, nl, w.seq), nan, dtype=torch.float32, device="cuda")
+    O = torch.full((T, h), nan, dtype=bf, device="cuda")
+    ws = torch.empty(max(tp.tp_attn_workspace_bytes(s), 1), dtype=torch.uint8, device="cuda")
+    tp.tp_attn_fwd(s, d["X_attn"], d["Wqkv"], d["bqkv"], d["Wo"], qkv, ctx, lse, O, ws)
+    torch.cuda.synchronize()
+    a = {k: f64(inp[k]) for k in ("X_attn", "Wqkv", "bqkv", "Wo")}
+    ctx_ref, _ = oracle.attn_core_fwd(a["X_attn"] @ a["Wqkv"] + a["bqkv"], batch=w.batch, seq=w.seq, n_local=nl,
+                                      head_dim=w.head_dim, head0=rank * nl, n_heads=w.n_heads, alibi=w.alibi)
+    compare("ctx", ctx, ctx_ref, "bf16")
+    rng = np.random.default_rng(5)
+    R = np.unique(np.concatenate([samples(T, 12, rng), np.arange(T - 8, T)]))
+    compare("O[R]", O[R], ctx_ref[R] @ a["Wo"], "bf16")
