@@ -20,9 +20,14 @@
 //
 // Tiles of 64 rows x D columns are staged in LDS by buffer loads that write
 // LDS directly, double-buffered (the next tile's loads are in flight while
-// the current tile is used), in a chunk-major layout: [D/8 chunks][64 rows]
-// [8 bf16], row r of chunk c stored at slot r ^ 4(c & 3). A tile is read two
-// ways, both free of bank conflicts by that swizzle:
+// the current tile is used), row-major with a row stride of 192 bytes (D <=
+// 96) or 320 (D >= 128; D = 64 and 128 leave 4 unused 16-byte chunks per
+// row), so that each 1 KiB load takes whole row segments of a few rows
+// rather than one 16-byte chunk of 64 rows (64 cache lines per
+// instruction). Logical chunk c of row r sits at physical chunk
+// 4(c/4) + ((c mod 4) xor s(r)), s(r) = 2 bit2(r) + bit3(r). A tile is read
+// two ways, both free of bank conflicts by that swizzle (a CPU simulation of
+// both reads under each lane grouping the hardware may use):
 //  * as rows (MFMA A operand "rows x D"): one ds_read_b128 per lane, lanes
 //    0..31 read 32 consecutive rows of one chunk;
 //  * transposed (A operand "D x rows"): two ds_read_b64_tr_b16 per lane, the
@@ -128,42 +133,78 @@ __device__ __forceinline__ float alibi_slope_log2(const MP& p, int l) {
 }
 
 
+// Row stride and size of a staged tile (see the layout above).
+template <int D>
+constexpr int tile_rs() { return D <= 96 ? 192 : 320; }
+template <int D>
+constexpr int tile_bytes() { return TROWS * tile_rs<D>(); }
+__device__ __forceinline__ int lswz(int r) { return ((r >> 1) & 2) | ((r >> 3) & 1); }
+
+// Per-lane source offsets of the 1 KiB blocks wave w fills in a tile:
+// blocks j = w, w + NW, ... of the tile's tile_rs/16; lane i of block j
+// writes bytes 1024 j + 16 i = row r, physical chunk q, which holds logical
+// chunk c; off[k] = 2 (r h_l + 8 c) bytes from the tile's first element, or
+// ~0 for an unused chunk.
+template <int D, int NW>
+struct TileLanes {
+  static constexpr int S = tile_rs<D>() / 16;
+  static constexpr int K = (S + NW - 1) / NW;
+  uint32_t off[K];
+};
+template <int D, int NW>
+__device__ __forceinline__ TileLanes<D, NW> tile_lanes(int h_l, int w, int lane) {
+  TileLanes<D, NW> t;
+#pragma unroll
+  for (int k = 0; k < TileLanes<D, NW>::K; ++k) {
+    const int o = 1024 * (w + NW * k) + 16 * lane;
+    const int r = o / tile_rs<D>(), q = (o - r * tile_rs<D>()) >> 4;
+    const int c = 4 * (q >> 2) + ((q & 3) ^ lswz(r));
+    t.off[k] = c < D / 8 ? (uint32_t)(2 * (r * h_l + 8 * c)) : 0xffffffffu;
+  }
+  return t;
+}
+
 // Stage rows [row0, row0 + 64) of columns [col0, col0 + D) of a [T, h_l] bf16
-// array into a chunk-major tile. With NW waves, wave w loads the chunks c with
-// c = w (mod 4), every (NW/4)-th of them starting at c = (w & 3) + 4(w >> 2);
-// lane i of a chunk's load lands in slot i, i.e. row i ^ 4(c & 3). Rows at or
-// past seq read zeros (offset beyond the buffer).
+// array into a tile. Rows at or past seq read zeros (offset beyond the
+// buffer): a lane's row r is inside the sequence iff its offset is below
+// 2 (seq - row0) h_l, as 16 c < 2 h_l.
 template <int D, int NW = 4>
 __device__ __forceinline__ void dma_tile(const bf16* arr, uint32_t nrec, char* tile, long grow0, int col0, int row0,
-                                         int seq, int h_l, int w, int lane) {
+                                         int seq, int h_l, int w, const TileLanes<D, NW>& tl) {
   const __amdgpu_buffer_rsrc_t rs = rsrc(arr, nrec);
-  const int w4 = NW == 4 ? w : (w & 3);
-  const int j0 = NW == 4 ? 0 : (w >> 2);
+  const int rows = min(seq - row0, TROWS);
+  const uint32_t lim = rows > 0 ? (uint32_t)(2 * rows * h_l) : 0u;
+  const uint32_t base = (uint32_t)(((grow0 + row0) * h_l + col0) * 2);
 #pragma unroll
-  for (int j = j0; j < D / 32; j += NW / 4) {
-    const int c = w4 + 4 * j;
-    const int pos = row0 + (lane ^ (w4 << 2));  // (c & 3) == w4
-    const uint32_t vo = pos < seq ? (uint32_t)(((grow0 + pos) * h_l + col0 + 8 * c) * 2) : nrec;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(tile + (c << 10)), 16, vo, 0, 0, 0);
+  for (int k = 0; k < TileLanes<D, NW>::K; ++k) {
+    const int j = w + NW * k;
+    if (j < TileLanes<D, NW>::S) {
+      const uint32_t o = tl.off[k];
+      const uint32_t vo = o < lim ? base + o : nrec;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(tile + 1024 * j), 16, vo, 0, 0, 0);
+    }
   }
 }
 
 // Row fragment for MFMA operand "rows x D": lane l reads row 32blk + (l & 31),
-// columns 16c + 8(l >> 5) .. +7, i.e. chunk 2c + g. The swizzle term
-// 4((2c + g) & 3) only depends on the parity of c, so two per-lane offsets
-// (c even, c odd) plus compile-time constants address every fragment.
+// columns 16c + 8(l >> 5) .. +7, i.e. logical chunk 2c + g, at physical chunk
+// 4(c >> 1) + ((2(c & 1) + g) xor s(row)); s(row) = s(l & 31), so two
+// per-lane offsets (c even, c odd) plus compile-time constants address every
+// fragment.
 struct RowOff {
   int e, o;
 };
+template <int D>
 __device__ __forceinline__ RowOff row_offsets(int lane) {
-  const int g = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 5, l32 = lane & 31, f = lswz(l32);
   RowOff r;
-  r.e = (g << 10) + ((l32 ^ (g << 2)) << 4);
-  r.o = (g << 10) + ((l32 ^ ((2 + g) << 2)) << 4);
+  r.e = l32 * tile_rs<D>() + 16 * (g ^ f);
+  r.o = l32 * tile_rs<D>() + 16 * ((2 + g) ^ f);
   return r;
 }
+template <int D>
 __device__ __forceinline__ bf16x8 frag_row(const char* tile, int blk, int c, const RowOff& ro) {
-  return *(const bf16x8*)(tile + ((c & 1) ? ro.o : ro.e) + (c << 11) + (blk << 9));
+  return *(const bf16x8*)(tile + ((c & 1) ? ro.o : ro.e) + 64 * (c >> 1) + blk * 32 * tile_rs<D>());
 }
 
 // 2^x by the hardware instruction (inputs here are <= 2^8 or far below 0;
@@ -177,16 +218,19 @@ __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(
 struct TrOff {
   int a, b;
 };
+template <int D>
 __device__ __forceinline__ TrOff tr_offsets(int lane) {
   const int G = lane >> 4, r = (lane >> 2) & 3, c = lane & 3, g = lane >> 5;
   const int x = 2 * (G & 1) + (c >> 1);  // chunk within the 4-chunk (32-column) block
+  const int ra = 4 * g + r, rb = 8 + ra;
   TrOff o;
-  o.a = (x << 10) + (((4 * g + r) ^ (x << 2)) << 4) + 8 * (c & 1);
-  o.b = (x << 10) + (((8 + 4 * g + r) ^ (x << 2)) << 4) + 8 * (c & 1);
+  o.a = ra * tile_rs<D>() + 16 * (x ^ lswz(ra)) + 8 * (c & 1);
+  o.b = rb * tile_rs<D>() + 16 * (x ^ lswz(rb)) + 8 * (c & 1);
   return o;
 }
+template <int D>
 __device__ __forceinline__ bf16x8 frag_tr(const char* tile, int db, int kc, const TrOff& o) {
-  const char* b = tile + (db << 12) + (kc << 8);
+  const char* b = tile + 64 * db + kc * 16 * tile_rs<D>();
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(b + o.a));
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(b + o.b));
   const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -259,10 +303,10 @@ template <int D, bool AL, bool DO>
 __device__ __forceinline__ void fwd_block(const MP& p, const char* __restrict__ cur, int k0, int sb, int g,
                                           int q0w, int myq, float slope2, const TrOff& tro, const RowOff& ro,
                                           int b, int head, int hk, FwdState<D>& st) {
-  constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
+  constexpr int NC = D / 16, NB = D / 32, TB = tile_bytes<D>();
   f32x16 sa = f32x16{};
 #pragma unroll
-  for (int c = 0; c < NC; ++c) sa = mfma_f16(frag_row(cur, sb, c, ro), st.qf[c], sa);
+  for (int c = 0; c < NC; ++c) sa = mfma_f16(frag_row<D>(cur, sb, c, ro), st.qf[c], sa);
   // s[q]: key k0 + 8(q>>2) + 4g + (q&3), query myq, in log2 units
   float x[16];
   float mloc;
@@ -299,8 +343,8 @@ __device__ __forceinline__ void fwd_block(const MP& p, const char* __restrict__ 
   const char* vt = cur + TB;
 #pragma unroll
   for (int db = 0; db < NB; ++db) {
-    st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(vt, db, 2 * sb, tro), pf0, st.o[db], 0, 0, 0);
-    st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(vt, db, 2 * sb + 1, tro), pf1, st.o[db], 0, 0, 0);
+    st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(vt, db, 2 * sb, tro), pf0, st.o[db], 0, 0, 0);
+    st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(vt, db, 2 * sb + 1, tro), pf1, st.o[db], 0, 0, 0);
   }
 }
 
@@ -314,7 +358,7 @@ constexpr int FWD_WAVES = 8;
 
 template <int D, bool AL, bool DO>
 __global__ __launch_bounds__(64 * FWD_WAVES) void fwd_mfma(MP p, FwdItems items) {
-  constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
+  constexpr int NC = D / 16, NB = D / 32, TB = tile_bytes<D>();
   constexpr int NX = NB * 16 + 2;  // floats a wave hands to its partner, per lane
   // two stages of (K16, V) tiles; the pair merge at the end reuses the memory
   constexpr int SZ = 4 * TB > 4 * NX * 64 * 4 ? 4 * TB : 4 * NX * 64 * 4;
@@ -330,6 +374,7 @@ __global__ __launch_bounds__(64 * FWD_WAVES) void fwd_mfma(MP p, FwdItems items)
   }
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = (int)uni((uint32_t)(tid >> 6));
+  const TileLanes<D, FWD_WAVES> tl = tile_lanes<D, FWD_WAVES>(p.h_l, w, lane);
   const int qw = w & 3, kh = w >> 2;
   const long grow0 = (long)b * p.seq;
   const int q0w = qt * 128 + 32 * qw;
@@ -340,8 +385,8 @@ __global__ __launch_bounds__(64 * FWD_WAVES) void fwd_mfma(MP p, FwdItems items)
   // key tiles [ktb, kte): all of them, or one half of a split item (every
   // query of a split tile has keys in both halves)
   const int ktb = part == 2 ? nkt / 2 : 0, kte = part == 1 ? nkt / 2 : nkt;
-  dma_tile<D, FWD_WAVES>(p.k16, nrec, stage, grow0, l * D, ktb * TROWS, p.seq, p.h_l, w, lane);
-  dma_tile<D, FWD_WAVES>(p.vh, nrec, stage + TB, grow0, l * D, ktb * TROWS, p.seq, p.h_l, w, lane);
+  dma_tile<D, FWD_WAVES>(p.k16, nrec, stage, grow0, l * D, ktb * TROWS, p.seq, p.h_l, w, tl);
+  dma_tile<D, FWD_WAVES>(p.vh, nrec, stage + TB, grow0, l * D, ktb * TROWS, p.seq, p.h_l, w, tl);
   FwdState<D> st;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -353,8 +398,8 @@ __global__ __launch_bounds__(64 * FWD_WAVES) void fwd_mfma(MP p, FwdItems items)
   st.m_run = -INFINITY;
   st.l_run = 0.f;
   const float slope2 = alibi_slope_log2(p, l);
-  const TrOff tro = tr_offsets(lane);
-  const RowOff ro = row_offsets(lane);
+  const TrOff tro = tr_offsets<D>(lane);
+  const RowOff ro = row_offsets<D>(lane);
   for (int kt = ktb; kt < kte; ++kt) {
     loads_landed_barrier();  // tile kt is in LDS; tile kt-1 is no longer read
     const bool odd = (kt - ktb) & 1;
@@ -362,8 +407,8 @@ __global__ __launch_bounds__(64 * FWD_WAVES) void fwd_mfma(MP p, FwdItems items)
     char* nxt = odd ? stage : stage + 2 * TB;
     const int kv0 = kt * TROWS;
     if (kt + 1 < kte) {
-      dma_tile<D, FWD_WAVES>(p.k16, nrec, nxt, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
-      dma_tile<D, FWD_WAVES>(p.vh, nrec, nxt + TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
+      dma_tile<D, FWD_WAVES>(p.k16, nrec, nxt, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, tl);
+      dma_tile<D, FWD_WAVES>(p.vh, nrec, nxt + TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, tl);
     }
     const int k0 = kv0 + 32 * kh;
     if (k0 <= q0w + 31 && k0 < p.seq)  // wave-uniform; otherwise every key is masked
@@ -498,14 +543,14 @@ constexpr int BWD_WAVES = 8;
 // P hand-over: [key pair][query block][quad][lane][4] floats
 constexpr int PBUF_BYTES = 4 * 2 * 4 * 64 * 4 * 4;
 template <int D>
-constexpr int bwd_stage_bytes() { return 3 * TROWS * D * 2 + 512; }  // three tiles + lse and delta of 64 queries
+constexpr int bwd_stage_bytes() { return 3 * tile_bytes<D>() + 512; }  // three tiles + lse and delta of 64 queries
 template <int D>
 constexpr int bwd_lds_bytes() {
   // two stages and the P buffer; the dQ pairs' merge (4 x NB x 16 floats per
   // lane) reuses the stages
   return 2 * bwd_stage_bytes<D>() + PBUF_BYTES;
 }
-static_assert(2 * 3 * TROWS * 160 * 2 + 1024 + PBUF_BYTES <= 160 * 1024, "LDS budget at D = 160");
+static_assert(2 * (3 * TROWS * 320 + 512) + PBUF_BYTES <= 160 * 1024, "LDS budget at D = 128 and 160");
 
 // Keep bits of this lane's key for the 16 queries of a 32-query block: bit
 // 4 q4 + e for query qs0 + 8 q4 + 4g + e (the order of the score
@@ -559,10 +604,11 @@ __device__ __forceinline__ bf16x8 pack8_keep(const float* x, uint32_t bits, int 
 template <int D, bool AL, bool DO>
 __device__ __forceinline__ void dkdv_item(const MP& p, int head, int kvt, char* __restrict__ st0,
                                           char* __restrict__ st1, float* __restrict__ pbuf) {
-  constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
+  constexpr int NC = D / 16, NB = D / 32, TB = tile_bytes<D>();
   const int b = head / p.n_local, l = head - b * p.n_local;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = (int)uni((uint32_t)(tid >> 6));
+  const TileLanes<D, BWD_WAVES> tl = tile_lanes<D, BWD_WAVES>(p.h_l, w, lane);
   const int kp = w & 3;         // key pair
   const bool roleA = w < 4;     // wave-uniform
   const long grow0 = (long)b * p.seq;
@@ -571,9 +617,9 @@ __device__ __forceinline__ void dkdv_item(const MP& p, int head, int kvt, char* 
   const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
   const int nqt = (p.seq + TROWS - 1) / TROWS;
   const int qt0 = (kvt * 128) / TROWS;
-  dma_tile<D, BWD_WAVES>(p.q16, nrec, st0, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, lane);
-  dma_tile<D, BWD_WAVES>(p.qb, nrec, st0 + TB, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, lane);
-  dma_tile<D, BWD_WAVES>(p.dctx, nrec, st0 + 2 * TB, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, lane);
+  dma_tile<D, BWD_WAVES>(p.q16, nrec, st0, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, tl);
+  dma_tile<D, BWD_WAVES>(p.qb, nrec, st0 + TB, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, tl);
+  dma_tile<D, BWD_WAVES>(p.dctx, nrec, st0 + 2 * TB, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, tl);
   dma_stats(p, st0 + 3 * TB, head, qt0 * TROWS, w, lane);
   // A: K (fp16 bits) and dV; B: V and dK
   bf16x8 kv[NC];
@@ -586,8 +632,8 @@ __device__ __forceinline__ void dkdv_item(const MP& p, int head, int kvt, char* 
 #pragma unroll
   for (int db = 0; db < NB; ++db) acc[db] = f32x16{};
   const float slope2 = alibi_slope_log2(p, l);
-  const TrOff tro = tr_offsets(lane);
-  const RowOff ro = row_offsets(lane);
+  const TrOff tro = tr_offsets<D>(lane);
+  const RowOff ro = row_offsets<D>(lane);
   float* pb = pbuf + kp * (2 * 4 * 64 * 4) + 4 * lane;  // + (qs*4 + q4)*256
   for (int qt = qt0; qt < nqt; ++qt) {
     loads_landed_barrier();  // tile qt is in LDS; the other stage and the P buffer are free
@@ -596,9 +642,9 @@ __device__ __forceinline__ void dkdv_item(const MP& p, int head, int kvt, char* 
     char* nxt = odd ? st0 : st1;
     if (qt + 1 < nqt) {
       const int qn = (qt + 1) * TROWS;
-      dma_tile<D, BWD_WAVES>(p.q16, nrec, nxt, grow0, l * D, qn, p.seq, p.h_l, w, lane);
-      dma_tile<D, BWD_WAVES>(p.qb, nrec, nxt + TB, grow0, l * D, qn, p.seq, p.h_l, w, lane);
-      dma_tile<D, BWD_WAVES>(p.dctx, nrec, nxt + 2 * TB, grow0, l * D, qn, p.seq, p.h_l, w, lane);
+      dma_tile<D, BWD_WAVES>(p.q16, nrec, nxt, grow0, l * D, qn, p.seq, p.h_l, w, tl);
+      dma_tile<D, BWD_WAVES>(p.qb, nrec, nxt + TB, grow0, l * D, qn, p.seq, p.h_l, w, tl);
+      dma_tile<D, BWD_WAVES>(p.dctx, nrec, nxt + 2 * TB, grow0, l * D, qn, p.seq, p.h_l, w, tl);
       dma_stats(p, nxt + 3 * TB, head, qn, w, lane);
     }
     const float* sL = (const float*)(cur + 3 * TB);
@@ -614,7 +660,7 @@ __device__ __forceinline__ void dkdv_item(const MP& p, int head, int kvt, char* 
       if (roleA) {
         f32x16 sa = f32x16{};
 #pragma unroll
-        for (int c = 0; c < NC; ++c) sa = mfma_f16(frag_row(cur, qs, c, ro), kv[c], sa);
+        for (int c = 0; c < NC; ++c) sa = mfma_f16(frag_row<D>(cur, qs, c, ro), kv[c], sa);
         float pr[16];
         if ((qs0 < k0w + 31) || (qs0 + 32 > p.seq))
           a_probs<true, AL>(sa, sL + 32 * qs, pr, slope2, qs0, g, myk, p.seq);
@@ -636,7 +682,7 @@ __device__ __forceinline__ void dkdv_item(const MP& p, int head, int kvt, char* 
         f32x16 d = f32x16{};
 #pragma unroll
         for (int c = 0; c < NC; ++c)
-          d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(cur + 2 * TB, qs, c, ro), kv[c], d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row<D>(cur + 2 * TB, qs, c, ro), kv[c], d, 0, 0, 0);
         dp[qs] = d;
       }
     }
@@ -672,8 +718,8 @@ __device__ __forceinline__ void dkdv_item(const MP& p, int head, int kvt, char* 
       }
 #pragma unroll
       for (int db = 0; db < NB; ++db) {
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(tt, db, 2 * qs, tro), f0, acc[db], 0, 0, 0);
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(tt, db, 2 * qs + 1, tro), f1, acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(tt, db, 2 * qs, tro), f0, acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(tt, db, 2 * qs + 1, tro), f1, acc[db], 0, 0, 0);
       }
     }
   }
@@ -715,10 +761,11 @@ __device__ __forceinline__ void q_dscores(const f32x16& sa, const f32x16& dp, fl
 template <int D, bool AL, bool DO>
 __device__ __forceinline__ void dq_item(const MP& p, int head, int qt, char* __restrict__ st0,
                                         char* __restrict__ st1) {
-  constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
+  constexpr int NC = D / 16, NB = D / 32, TB = tile_bytes<D>();
   const int b = head / p.n_local, l = head - b * p.n_local;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = (int)uni((uint32_t)(tid >> 6));
+  const TileLanes<D, BWD_WAVES> tl = tile_lanes<D, BWD_WAVES>(p.h_l, w, lane);
   const int qw = w & 3, kh = w >> 2;
   const long grow0 = (long)b * p.seq;
   const int q0w = qt * 128 + 32 * qw;
@@ -726,9 +773,9 @@ __device__ __forceinline__ void dq_item(const MP& p, int head, int qt, char* __r
   const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
   const int kv_end = min(p.seq, qt * 128 + 128);
   const int nkt = (kv_end + TROWS - 1) / TROWS;
-  dma_tile<D, BWD_WAVES>(p.k16, nrec, st0, grow0, l * D, 0, p.seq, p.h_l, w, lane);
-  dma_tile<D, BWD_WAVES>(p.kb, nrec, st0 + TB, grow0, l * D, 0, p.seq, p.h_l, w, lane);
-  dma_tile<D, BWD_WAVES>(p.vh, nrec, st0 + 2 * TB, grow0, l * D, 0, p.seq, p.h_l, w, lane);
+  dma_tile<D, BWD_WAVES>(p.k16, nrec, st0, grow0, l * D, 0, p.seq, p.h_l, w, tl);
+  dma_tile<D, BWD_WAVES>(p.kb, nrec, st0 + TB, grow0, l * D, 0, p.seq, p.h_l, w, tl);
+  dma_tile<D, BWD_WAVES>(p.vh, nrec, st0 + 2 * TB, grow0, l * D, 0, p.seq, p.h_l, w, tl);
   bf16x8 qf[NC], cf[NC];  // q16 (fp16 bits), dctx
   f32x16 dq[NB];
 #pragma unroll
@@ -746,8 +793,8 @@ __device__ __forceinline__ void dq_item(const MP& p, int head, int qt, char* __r
 #pragma unroll
   for (int db = 0; db < NB; ++db) dq[db] = f32x16{};
   const float slope2 = alibi_slope_log2(p, l);
-  const TrOff tro = tr_offsets(lane);
-  const RowOff ro = row_offsets(lane);
+  const TrOff tro = tr_offsets<D>(lane);
+  const RowOff ro = row_offsets<D>(lane);
   for (int kt = 0; kt < nkt; ++kt) {
     loads_landed_barrier();
     const bool odd = kt & 1;
@@ -755,17 +802,17 @@ __device__ __forceinline__ void dq_item(const MP& p, int head, int qt, char* __r
     char* nxt = odd ? st0 : st1;
     if (kt + 1 < nkt) {
       const int kn = (kt + 1) * TROWS;
-      dma_tile<D, BWD_WAVES>(p.k16, nrec, nxt, grow0, l * D, kn, p.seq, p.h_l, w, lane);
-      dma_tile<D, BWD_WAVES>(p.kb, nrec, nxt + TB, grow0, l * D, kn, p.seq, p.h_l, w, lane);
-      dma_tile<D, BWD_WAVES>(p.vh, nrec, nxt + 2 * TB, grow0, l * D, kn, p.seq, p.h_l, w, lane);
+      dma_tile<D, BWD_WAVES>(p.k16, nrec, nxt, grow0, l * D, kn, p.seq, p.h_l, w, tl);
+      dma_tile<D, BWD_WAVES>(p.kb, nrec, nxt + TB, grow0, l * D, kn, p.seq, p.h_l, w, tl);
+      dma_tile<D, BWD_WAVES>(p.vh, nrec, nxt + 2 * TB, grow0, l * D, kn, p.seq, p.h_l, w, tl);
     }
     const int k0 = kt * TROWS + 32 * kh;
     if (k0 > q0w + 31 || k0 >= p.seq) continue;  // wave-uniform: every key masked
     f32x16 sa = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      sa = mfma_f16(frag_row(cur, kh, c, ro), qf[c], sa);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(cur + 2 * TB, kh, c, ro), cf[c], dp, 0, 0, 0);
+      sa = mfma_f16(frag_row<D>(cur, kh, c, ro), qf[c], sa);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row<D>(cur + 2 * TB, kh, c, ro), cf[c], dp, 0, 0, 0);
     }
     // s[q]: key k0 + 8(q>>2) + 4g + (q&3), query myq
     uint32_t bits = 0;
@@ -780,8 +827,8 @@ __device__ __forceinline__ void dq_item(const MP& p, int head, int qt, char* __r
     const char* kbt = cur + TB;
 #pragma unroll
     for (int db = 0; db < NB; ++db) {
-      dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(kbt, db, 2 * kh, tro), df0, dq[db], 0, 0, 0);
-      dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(kbt, db, 2 * kh + 1, tro), df1, dq[db], 0, 0, 0);
+      dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(kbt, db, 2 * kh, tro), df0, dq[db], 0, 0, 0);
+      dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(kbt, db, 2 * kh + 1, tro), df1, dq[db], 0, 0, 0);
     }
   }
   // pair merge: the last tile issued no loads, so after this barrier no wave
@@ -878,14 +925,14 @@ template <int D, bool AL, bool DO>
 __device__ __forceinline__ void dkdv_tile4(const MP& p, const char* __restrict__ cur, char* __restrict__ nxt,
                                           bool issue, int q0, int head, int l, long grow0, int w, int lane, int k0w,
                                           int myk, float slope2, const TrOff& tro, const RowOff& ro,
-                                          KvState4<D>& st) {
-  constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
+                                          const TileLanes<D, 4>& tl, KvState4<D>& st) {
+  constexpr int NC = D / 16, NB = D / 32, TB = tile_bytes<D>();
   const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
   if (issue) {
     const int qn = q0 + TROWS;
-    dma_tile<D>(p.q16, nrec, nxt, grow0, l * D, qn, p.seq, p.h_l, w, lane);
-    dma_tile<D>(p.qb, nrec, nxt + TB, grow0, l * D, qn, p.seq, p.h_l, w, lane);
-    dma_tile<D>(p.dctx, nrec, nxt + 2 * TB, grow0, l * D, qn, p.seq, p.h_l, w, lane);
+    dma_tile<D>(p.q16, nrec, nxt, grow0, l * D, qn, p.seq, p.h_l, w, tl);
+    dma_tile<D>(p.qb, nrec, nxt + TB, grow0, l * D, qn, p.seq, p.h_l, w, tl);
+    dma_tile<D>(p.dctx, nrec, nxt + 2 * TB, grow0, l * D, qn, p.seq, p.h_l, w, tl);
     dma_stats(p, nxt + 3 * TB, head, qn, w, lane);
   }
   if (k0w >= p.seq) return;
@@ -899,8 +946,8 @@ __device__ __forceinline__ void dkdv_tile4(const MP& p, const char* __restrict__
     f32x16 sa = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      sa = mfma_f16(frag_row(cur, qs, c, ro), st.kf[c], sa);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(cur + 2 * TB, qs, c, ro), st.vf[c], dp, 0, 0, 0);
+      sa = mfma_f16(frag_row<D>(cur, qs, c, ro), st.kf[c], sa);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row<D>(cur + 2 * TB, qs, c, ro), st.vf[c], dp, 0, 0, 0);
     }
     // s[q], dp[q]: query qs0 + 8(q>>2) + 4g + (q&3), key myk
     uint64_t kw[4] = {0, 0, 0, 0};
@@ -927,9 +974,9 @@ __device__ __forceinline__ void dkdv_tile4(const MP& p, const char* __restrict__
       const bf16x8 pf = pack8(pv + 8 * h), df = pack8(dsv + 8 * h);
 #pragma unroll
       for (int db = 0; db < NB; ++db) {
-        st.dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(cur + 2 * TB, db, 2 * qs + h, tro), pf,
+        st.dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(cur + 2 * TB, db, 2 * qs + h, tro), pf,
                                                             st.dv[db], 0, 0, 0);
-        st.dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(cur + TB, db, 2 * qs + h, tro), df, st.dk[db],
+        st.dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(cur + TB, db, 2 * qs + h, tro), df, st.dk[db],
                                                             0, 0, 0);
       }
     }
@@ -941,19 +988,20 @@ __device__ __forceinline__ void dkdv_tile4(const MP& p, const char* __restrict__
 template <int D, bool AL, bool DO>
 __device__ __forceinline__ void dkdv_item4(const MP& p, int head, int kvt, char* __restrict__ st0,
                                           char* __restrict__ st1) {
-  constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
+  constexpr int NC = D / 16, NB = D / 32, TB = tile_bytes<D>();
   const int b = head / p.n_local, l = head - b * p.n_local;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = (int)uni((uint32_t)(tid >> 6));
+  const TileLanes<D, 4> tl = tile_lanes<D, 4>(p.h_l, w, lane);
   const long grow0 = (long)b * p.seq;
   const int k0w = kvt * 128 + 32 * w;
   const int myk = k0w + l32;
   const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
   const int nqt = (p.seq + TROWS - 1) / TROWS;
   const int qt0 = (kvt * 128) / TROWS;
-  dma_tile<D>(p.q16, nrec, st0, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, lane);
-  dma_tile<D>(p.qb, nrec, st0 + TB, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, lane);
-  dma_tile<D>(p.dctx, nrec, st0 + 2 * TB, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, lane);
+  dma_tile<D>(p.q16, nrec, st0, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, tl);
+  dma_tile<D>(p.qb, nrec, st0 + TB, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, tl);
+  dma_tile<D>(p.dctx, nrec, st0 + 2 * TB, grow0, l * D, qt0 * TROWS, p.seq, p.h_l, w, tl);
   dma_stats(p, st0 + 3 * TB, head, qt0 * TROWS, w, lane);
   KvState4<D> st;
 #pragma unroll
@@ -972,13 +1020,13 @@ __device__ __forceinline__ void dkdv_item4(const MP& p, int head, int kvt, char*
     st.dk[db] = f32x16{};
   }
   const float slope2 = alibi_slope_log2(p, l);
-  const TrOff tro = tr_offsets(lane);
-  const RowOff ro = row_offsets(lane);
+  const TrOff tro = tr_offsets<D>(lane);
+  const RowOff ro = row_offsets<D>(lane);
   for (int qt = qt0; qt < nqt; ++qt) {
     loads_landed_barrier();
     const bool odd = (qt - qt0) & 1;
     dkdv_tile4<D, AL, DO>(p, odd ? st1 : st0, odd ? st0 : st1, qt + 1 < nqt, qt * TROWS, head, l, grow0, w, lane, k0w,
-                     myk, slope2, tro, ro, st);
+                     myk, slope2, tro, ro, tl, st);
   }
   if (myk < p.seq) {
     const long ld3 = 3L * p.h_l;
@@ -1012,13 +1060,14 @@ struct QState4 {
 template <int D, bool AL, bool DO>
 __device__ __forceinline__ void dq_tile4(const MP& p, const char* __restrict__ cur, char* __restrict__ nxt, bool issue,
                                         int kv0, int l, long grow0, int w, int lane, int q0w, int myq, float slope2,
-                                        const TrOff& tro, const RowOff& ro, int head, QState4<D>& st) {
-  constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
+                                        const TrOff& tro, const RowOff& ro, int head, const TileLanes<D, 4>& tl,
+                                        QState4<D>& st) {
+  constexpr int NC = D / 16, NB = D / 32, TB = tile_bytes<D>();
   const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
   if (issue) {
-    dma_tile<D>(p.k16, nrec, nxt, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
-    dma_tile<D>(p.kb, nrec, nxt + TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
-    dma_tile<D>(p.vh, nrec, nxt + 2 * TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, lane);
+    dma_tile<D>(p.k16, nrec, nxt, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, tl);
+    dma_tile<D>(p.kb, nrec, nxt + TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, tl);
+    dma_tile<D>(p.vh, nrec, nxt + 2 * TB, grow0, l * D, kv0 + TROWS, p.seq, p.h_l, w, tl);
   }
   const int g = lane >> 5;
 #pragma unroll
@@ -1028,8 +1077,8 @@ __device__ __forceinline__ void dq_tile4(const MP& p, const char* __restrict__ c
     f32x16 sa = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      sa = mfma_f16(frag_row(cur, sb, c, ro), st.qf[c], sa);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(cur + 2 * TB, sb, c, ro), st.cf[c], dp, 0, 0, 0);
+      sa = mfma_f16(frag_row<D>(cur, sb, c, ro), st.qf[c], sa);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row<D>(cur + 2 * TB, sb, c, ro), st.cf[c], dp, 0, 0, 0);
     }
     // s[q]: key k0 + 8(q>>2) + 4g + (q&3), query myq
     uint32_t bits = 0;
@@ -1044,8 +1093,8 @@ __device__ __forceinline__ void dq_tile4(const MP& p, const char* __restrict__ c
     const char* kbt = cur + TB;
 #pragma unroll
     for (int db = 0; db < NB; ++db) {
-      st.dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(kbt, db, 2 * sb, tro), df0, st.dq[db], 0, 0, 0);
-      st.dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(kbt, db, 2 * sb + 1, tro), df1, st.dq[db], 0, 0, 0);
+      st.dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(kbt, db, 2 * sb, tro), df0, st.dq[db], 0, 0, 0);
+      st.dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(kbt, db, 2 * sb + 1, tro), df1, st.dq[db], 0, 0, 0);
     }
   }
 }
@@ -1055,19 +1104,20 @@ __device__ __forceinline__ void dq_tile4(const MP& p, const char* __restrict__ c
 template <int D, bool AL, bool DO>
 __device__ __forceinline__ void dq_item4(const MP& p, int head, int qt, char* __restrict__ st0,
                                         char* __restrict__ st1) {
-  constexpr int NC = D / 16, NB = D / 32, TB = TROWS * D * 2;
+  constexpr int NC = D / 16, NB = D / 32, TB = tile_bytes<D>();
   const int b = head / p.n_local, l = head - b * p.n_local;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = (int)uni((uint32_t)(tid >> 6));
+  const TileLanes<D, 4> tl = tile_lanes<D, 4>(p.h_l, w, lane);
   const long grow0 = (long)b * p.seq;
   const int q0w = qt * 128 + 32 * w;
   const int myq = q0w + l32;
   const uint32_t nrec = (uint32_t)(p.T * p.h_l * 2);
   const int kv_end = min(p.seq, qt * 128 + 128);
   const int nkt = (kv_end + TROWS - 1) / TROWS;
-  dma_tile<D>(p.k16, nrec, st0, grow0, l * D, 0, p.seq, p.h_l, w, lane);
-  dma_tile<D>(p.kb, nrec, st0 + TB, grow0, l * D, 0, p.seq, p.h_l, w, lane);
-  dma_tile<D>(p.vh, nrec, st0 + 2 * TB, grow0, l * D, 0, p.seq, p.h_l, w, lane);
+  dma_tile<D>(p.k16, nrec, st0, grow0, l * D, 0, p.seq, p.h_l, w, tl);
+  dma_tile<D>(p.kb, nrec, st0 + TB, grow0, l * D, 0, p.seq, p.h_l, w, tl);
+  dma_tile<D>(p.vh, nrec, st0 + 2 * TB, grow0, l * D, 0, p.seq, p.h_l, w, tl);
   QState4<D> st;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -1084,13 +1134,13 @@ __device__ __forceinline__ void dq_item4(const MP& p, int head, int qt, char* __
 #pragma unroll
   for (int db = 0; db < NB; ++db) st.dq[db] = f32x16{};
   const float slope2 = alibi_slope_log2(p, l);
-  const TrOff tro = tr_offsets(lane);
-  const RowOff ro = row_offsets(lane);
+  const TrOff tro = tr_offsets<D>(lane);
+  const RowOff ro = row_offsets<D>(lane);
   for (int kt = 0; kt < nkt; ++kt) {
     loads_landed_barrier();
     const bool odd = kt & 1;
     dq_tile4<D, AL, DO>(p, odd ? st1 : st0, odd ? st0 : st1, kt + 1 < nkt, kt * TROWS, l, grow0, w, lane, q0w, myq,
-                       slope2, tro, ro, head, st);
+                       slope2, tro, ro, head, tl, st);
   }
   if (myq < p.seq) {
     bf16* dQ = p.dqkv + (grow0 + myq) * (3L * p.h_l) + (long)l * D;
@@ -1115,7 +1165,7 @@ constexpr int bwd4_waves_per_simd() { return DO ? 1 : 2; }
 template <int D, bool AL, bool DO>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd4_waves_per_simd<D, DO>(),
                                                                      bwd4_waves_per_simd<D, DO>()))) void bwd4_mfma(MP p) {
-  constexpr int SB = 3 * TROWS * D * 2 + 512;  // three tiles + lse and delta of 64 queries
+  constexpr int SB = 3 * tile_bytes<D>() + 512;  // three tiles + lse and delta of 64 queries
   __shared__ __attribute__((aligned(16))) char st0[SB];
   __shared__ __attribute__((aligned(16))) char st1[SB];
   const int nh = p.batch * p.n_local, nt = (p.seq + 127) / 128;
