@@ -75,6 +75,45 @@ __device__ __forceinline__ uint32_t residual_keep_byte(const DropArgs& d, long t
   return bits;
 }
 
+// Keep byte from 8 16-bit lanes held in two Philox words (lanes 4e'..4e'+3
+// in word e').
+__device__ __forceinline__ uint32_t keep_byte_of(uint64_t w0, uint64_t w1, uint32_t thr) {
+  uint32_t bits = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) bits |= (uint32_t)((((e < 4 ? w0 : w1) >> (16 * (e & 3))) & 0xFFFFull) >= thr) << e;
+  return bits;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor1_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, 1), hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), 1);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Keep bytes of this thread's chunks c_i = threadIdx.x + i FWD_T, i < NV.
+// Chunks 2k and 2k+1 take lanes 0-7 and 8-15 of the block at counter
+// (t, k), and all of a thread's chunks have its parity, so two neighbouring
+// threads need the same block for every i. For each pair (i, i+1) the even
+// thread draws the block of its chunk i, the odd thread that of its chunk
+// i+1, and each hands the half it does not use to the other: one block per
+// thread per two chunks instead of one per chunk. Counters come from the
+// unclamped chunk index, so a thread past the row's end still draws the
+// block its neighbour needs.
+template <int NV>
+__device__ __forceinline__ void residual_keep_bytes(const DropArgs& d, long t, uint32_t (&bits)[NV]) {
+  const int odd = threadIdx.x & 1;
+#pragma unroll
+  for (int i = 0; i + 1 < NV; i += 2) {
+    const int c = (int)threadIdx.x + (i + odd) * FWD_T;
+    uint64_t x0 = (uint64_t)t, x1 = (uint64_t)(c >> 1), x2 = 0, x3 = 2;
+    philox4x64_10(x0, x1, x2, x3, d.seed, d.offset);
+    const uint64_t k0 = odd ? x2 : x0, k1 = odd ? x3 : x1;  // the half this thread uses
+    const uint64_t r0 = shfl_xor1_u64(odd ? x0 : x2), r1 = shfl_xor1_u64(odd ? x1 : x3);
+    bits[i] = odd ? keep_byte_of(r0, r1, d.thr) : keep_byte_of(k0, k1, d.thr);
+    bits[i + 1] = odd ? keep_byte_of(k0, k1, d.thr) : keep_byte_of(r0, r1, d.thr);
+  }
+  if (NV & 1) bits[NV - 1] = residual_keep_byte(d, t, (int)threadIdx.x + (NV - 1) * FWD_T);
+}
+
 // Chunk i of this thread (8 elements at column 8c) is valid if c < nc; the
 // loads use the clamped chunk min(c, nc - 1), always in range, so that no load
 // waits behind a branch; only arithmetic that feeds a sum and the stores
@@ -127,10 +166,12 @@ __global__ __launch_bounds__(FWD_T) void ln_residual_fwd_kernel(const T* __restr
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[i][e] += bv[i][e];
   }
+  uint32_t kb[NV];
+  if (DO) residual_keep_bytes<NV>(da, blockIdx.x, kb);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     if (DO) {
-      const uint32_t bits = residual_keep_byte(da, blockIdx.x, cl[i] >> 3);
+      const uint32_t bits = kb[i];
       if (ok[i]) da.mask[(long)blockIdx.x * (h >> 3) + (cl[i] >> 3)] = (uint8_t)bits;
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[i][e] = rv[i][e] + (((bits >> e) & 1u) ? v[i][e] * da.scale : 0.f);
