@@ -145,6 +145,29 @@ def traffic(fetch_dir: str, write_dir: str, copyf_dir: str, copyw_dir: str, copy
     ])
 
 
+def hbm(fetch_dir: str, write_dir: str, copyf_dir: str, copyw_dir: str, copy_bytes: int, *prefixes: str) -> str:
+    """Bandwidth-bound kernels (short names starting with one of `prefixes`):
+    per dispatch, FETCH_SIZE and WRITE_SIZE scaled as in `traffic`, the
+    dispatch's duration (from the GRBM_GUI_ACTIVE rows of the FETCH_SIZE pass)
+    and the rate those bytes give against the 8 TB/s of HBM3E."""
+    cf = copy_bytes / (_mean(copyf_dir, "FETCH_SIZE", "__amd_rocclr_copyBuffer") * 1024)
+    cw = copy_bytes / (_mean(copyw_dir, "WRITE_SIZE", "__amd_rocclr_copyBuffer") * 1024)
+    F, dF, nF = _per_kernel(fetch_dir)
+    W, _, _ = _per_kernel(write_dir)
+    out = [f"calibration: copy of {copy_bytes} bytes -> FETCH_SIZE x {cf:.4f}, WRITE_SIZE x {cw:.4f}", "",
+           "| kernel | dispatches | avg us | fetched MB | written MB | GB/s | % of 8 TB/s |",
+           "|---|---|---|---|---|---|---|"]
+    for k in sorted(F, key=lambda k: -dF.get(k, 0)):
+        if not k.startswith(prefixes) or k not in dF:
+            continue
+        f = F[k].get("FETCH_SIZE", 0.0) * 1024 * cf
+        w = W.get(k, {}).get("WRITE_SIZE", 0.0) * 1024 * cw
+        gbs = (f + w) / dF[k]  # bytes per ns = GB/s
+        out.append(f"| {k} | {nF[k]} | {dF[k] / 1e3:.1f} | {f / 1e6:.1f} | {w / 1e6:.1f} | {gbs:.0f} | "
+                   f"{100 * gbs / 8000:.1f} |")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
     mode, d = sys.argv[1], sys.argv[2]
     if mode == "stats":
@@ -152,7 +175,9 @@ if __name__ == "__main__":
     elif mode == "counters":
         print(counters(d, sys.argv[3] if len(sys.argv) > 3 else ""))
     elif mode == "util":
-        print(util(d, sys.argv[3]))
+        print(util(d, sys.argv[3], int(sys.argv[4]) if len(sys.argv) > 4 else 16))
+    elif mode == "hbm":
+        print(hbm(d, sys.argv[3], sys.argv[4], sys.argv[5], int(sys.argv[6]), *sys.argv[7:]))
     elif mode == "traffic":
         print(traffic(d, sys.argv[3], sys.argv[4], sys.argv[5], int(sys.argv[6]), sys.argv[7]))
     else:
