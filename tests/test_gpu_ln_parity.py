@@ -158,13 +158,24 @@ DROP_CASES = [
     ("c1_fp32_h64_two_ranks_p03", "tiny_fp32_tp2", 64, 2, 0.5, 0.3),
     ("c4_h20480_37_rows_p01", "mtnlg_530b_tp8", 37, 1, 0.02, 0.1),
     ("c2_h1536_ragged_p05", "gpt2_1p2b_tp1", 300, 1, 0.5, 0.5),
+    # the forward draws one Philox block per two neighbouring threads' chunks
+    # and swaps halves: two chunks per thread (h 3072), eight of which the
+    # last is past the row (h 14336), and an odd chunk count (h 4104: 513
+    # chunks, the last one's neighbour past the row)
+    ("c3_h3072_p02", "gpt_8p3b_tp8", 33, 1, 0.5, 0.2),
+    ("c5_h14336_p01", "bloom_176b_tp8", 21, 2, 0.02, 0.1),
+    ("h4104_odd_chunks_p03", "h4104", 19, 1, 0.5, 0.3),
 ]
 
 
 @pytest.mark.parametrize("case", DROP_CASES, ids=[c[0] for c in DROP_CASES])
 def test_ln_residual_dropout_matches_oracle(case):
     name, wname, rows, n_parts, bias_std, p = case
-    w = synth.WORKLOADS[wname].with_(batch=1, seq=rows)
+    if wname == "h4104":
+        w = synth.WORKLOADS["gpt2_1p2b_tp1"].with_(batch=1, seq=rows, hidden=4104, n_heads=27, head_dim=152,
+                                                   ffn=4 * 4104)
+    else:
+        w = synth.WORKLOADS[wname].with_(batch=1, seq=rows)
     print(f"\n  [ln dropout case {name}]", flush=True)
     inp = synth.draw_ln(w, seed=9, n_parts=n_parts, bias_std=bias_std)
     got = run_gpu_dropout(w, inp, tp.TpDropout(p, 99, 5))
