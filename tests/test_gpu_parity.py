@@ -121,6 +121,8 @@ SMALL = [
     # longer, ragged sequences: many key tiles per query tile, partial last tiles
     ("d64_tp1_alibi_long_ragged", 1, 777, 2, 64, 1, 0, True),
     ("d160_tp2_r0_long_ragged", 2, 1100, 4, 160, 2, 0, False),
+    ("d96_tp1_long_ragged", 1, 1025, 2, 96, 1, 0, False),
+    ("d128_tp2_r1_alibi_long_ragged", 2, 1300, 4, 128, 2, 1, True),
 ]
 
 
